@@ -1,0 +1,205 @@
+/*
+ * ds4gen.h -- seeded, counter-based synthetic input generator.
+ *
+ * This module only draws random bits and turns them into input tensors of
+ * the right shape, format and value range (router weights, activations,
+ * quantised expert blocks, lookup tables).  It holds none of the MoE
+ * method's arithmetic: it never decodes a block, never scores a router,
+ * never multiplies a weight by an activation.  Both the CPU oracle tests and
+ * the GPU path consume what it produces; neither shares any other code.
+ *
+ * Random stream: SplitMix64 (Steele, Lea and Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014) used in counter mode.
+ *   mix64(z)          = the SplitMix64 output finaliser
+ *   key(seed, stream) = mix64(seed*G + stream*C + D)
+ *   draw(key, i)      = mix64(key + (i+1)*G),  G = 0x9E3779B97F4A7C15
+ * Every element is a pure function of (seed, stream, index), so any block of
+ * any expert can be regenerated on its own, on the host or on the device,
+ * with identical bits.
+ *
+ * The header compiles as plain C (gcc, host) and as HIP (device and host).
+ * Only integer operations and IEEE double add/multiply appear in the
+ * functions marked GEN_HD; files including it must be compiled with
+ * floating-point contraction disabled so that host and device round alike.
+ * Transcendental draws (normal deviates) are host-only.
+ */
+#ifndef DS4GEN_H
+#define DS4GEN_H
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define GEN_HD __host__ __device__ static inline
+#else
+#define GEN_HD static inline
+#endif
+
+#define DS4GEN_G 0x9E3779B97F4A7C15ULL
+#define DS4GEN_C 0xD1B54A32D192ED03ULL
+#define DS4GEN_D 0x632BE59BD9B4E019ULL
+
+/* Stream kinds; stream id = layer * 64 + kind. */
+enum {
+  DS4GEN_ROUTER_W = 1,  /* router weight [E][H]                         */
+  DS4GEN_ROUTER_B = 2,  /* router selection bias [E]                    */
+  DS4GEN_GATE = 3,      /* routed gate blocks [E][I][H]                 */
+  DS4GEN_UP = 4,        /* routed up blocks [E][I][H]                   */
+  DS4GEN_DOWN = 5,      /* routed down blocks [E][H][I]                 */
+  DS4GEN_SH_GATE = 6,   /* shared-expert gate blocks                    */
+  DS4GEN_SH_UP = 7,     /* shared-expert up blocks                      */
+  DS4GEN_SH_DOWN = 8,   /* shared-expert down blocks                    */
+  DS4GEN_GRID = 9,      /* IQ2_XXS-style 256 x 8 grid                   */
+  DS4GEN_X = 10,        /* token activations                            */
+  DS4GEN_TID2EID = 11,  /* hash-routing table                           */
+  DS4GEN_NORM = 12,     /* RMSNorm weight                               */
+  DS4GEN_ROUTE = 13,    /* caller-given routing (Gumbel keys)           */
+  DS4GEN_GATES = 14,    /* caller-given gate weights                    */
+  DS4GEN_COMMON = 15,   /* shared direction for correlated tokens       */
+  DS4GEN_TOKID = 16,    /* token ids                                    */
+  DS4GEN_RANKPERM = 17  /* expert popularity rank permutation           */
+};
+
+/* Block formats the generator can emit (byte sizes per block). */
+enum { DS4GEN_Q2_K = 0, DS4GEN_IQ2_XXS = 1, DS4GEN_Q8_0 = 2 };
+#define DS4GEN_Q2K_BYTES 84
+#define DS4GEN_IQ2_BYTES 66
+#define DS4GEN_Q80_BYTES 34
+
+GEN_HD uint64_t gen_mix64(uint64_t z) {
+  z ^= z >> 30;
+  z *= 0xBF58476D1CE4E5B9ULL;
+  z ^= z >> 27;
+  z *= 0x94D049BB133111EBULL;
+  z ^= z >> 31;
+  return z;
+}
+
+GEN_HD uint64_t gen_key(uint64_t seed, uint64_t stream) {
+  return gen_mix64(seed * DS4GEN_G + stream * DS4GEN_C + DS4GEN_D);
+}
+
+GEN_HD uint64_t gen_draw(uint64_t key, uint64_t index) {
+  return gen_mix64(key + (index + 1ULL) * DS4GEN_G);
+}
+
+/* Uniform double in [0,1) from the top 53 bits. */
+GEN_HD double gen_u01(uint64_t d) { return (double)(d >> 11) * 0x1.0p-53; }
+
+/* Uniform double in [a,b): a + (b-a)*u with two separately rounded ops. */
+GEN_HD double gen_uniform(uint64_t d, double a, double b) {
+  double span = b - a;
+  double t = span * gen_u01(d);
+  return a + t;
+}
+
+/* Integer in [0, n) from the low 32 bits (multiply-shift, n < 2^32). */
+GEN_HD uint32_t gen_below(uint64_t d, uint32_t n) {
+  return (uint32_t)(((d & 0xFFFFFFFFULL) * (uint64_t)n) >> 32);
+}
+
+GEN_HD uint64_t gen_f64_bits(double v) {
+  union { double d; uint64_t u; } c;
+  c.d = v;
+  return c.u;
+}
+
+/*
+ * Round a double to a narrower binary format with round-to-nearest-even,
+ * done on the integer representation so that every compiler and device gives
+ * the same bits.  mbits = stored mantissa bits, ebits = exponent bits.
+ * Returns the raw bit pattern (sign in the top bit of the 1+ebits+mbits).
+ * Values past the largest finite number become infinity.
+ */
+GEN_HD uint32_t gen_round_narrow(double v, int ebits, int mbits) {
+  uint64_t b = gen_f64_bits(v);
+  uint32_t sign = (uint32_t)(b >> 63) << (ebits + mbits);
+  int e = (int)((b >> 52) & 0x7FF);
+  uint64_t m = b & ((1ULL << 52) - 1);
+  int bias = (1 << (ebits - 1)) - 1;
+  uint32_t inf = ((1u << ebits) - 1) << mbits;
+  if (e == 0x7FF) return sign | inf | (m ? (1u << (mbits - 1)) : 0u);
+  if (e == 0) return sign; /* double subnormals are far below any target */
+  int E = e - 1023;
+  uint64_t mant = m | (1ULL << 52);
+  int emin = 1 - bias;
+  int shift = 52 - mbits;
+  if (E < emin) shift += emin - E;
+  if (E > bias) return sign | inf;
+  if (shift > 62) return sign;
+  uint64_t q = mant >> shift;
+  uint64_t rem = mant & ((1ULL << shift) - 1);
+  uint64_t half = 1ULL << (shift - 1);
+  if (rem > half || (rem == half && (q & 1ULL))) q++;
+  if (E >= emin) {
+    int ee = E + bias;
+    if (q == (2ULL << mbits)) { q >>= 1; ee++; }
+    if (ee >= (1 << ebits) - 1) return sign | inf;
+    return sign | ((uint32_t)ee << mbits) | (uint32_t)(q - (1ULL << mbits));
+  }
+  return sign | (uint32_t)q; /* subnormal; q == 1<<mbits is the least normal */
+}
+
+GEN_HD uint16_t gen_f16(double v) { return (uint16_t)gen_round_narrow(v, 5, 10); }
+GEN_HD uint16_t gen_bf16(double v) { return (uint16_t)gen_round_narrow(v, 8, 7); }
+
+GEN_HD void gen_put_u64(uint8_t* p, uint64_t v) {
+  for (int i = 0; i < 8; i++) p[i] = (uint8_t)(v >> (8 * i));
+}
+GEN_HD void gen_put_u16(uint8_t* p, uint16_t v) {
+  p[0] = (uint8_t)v;
+  p[1] = (uint8_t)(v >> 8);
+}
+
+/*
+ * Q2_K-format block number `blk` of a tensor stream (84 bytes):
+ * bytes 0..15 scale|min nibbles, 16..79 two-bit codes (all uniform random),
+ * 80..81 fp16 d ~ U[1e-3,1e-2], 82..83 fp16 dmin ~ U[0,5e-3].
+ * Draw indices 12*blk + 0..11.
+ */
+GEN_HD void gen_q2k_block(uint64_t key, uint64_t blk, uint8_t* out) {
+  uint64_t base = blk * 12ULL;
+  for (int j = 0; j < 10; j++) gen_put_u64(out + 8 * j, gen_draw(key, base + j));
+  gen_put_u16(out + 80, gen_f16(gen_uniform(gen_draw(key, base + 10), 1e-3, 1e-2)));
+  gen_put_u16(out + 82, gen_f16(gen_uniform(gen_draw(key, base + 11), 0.0, 5e-3)));
+}
+
+/*
+ * IQ2_XXS-style block `blk` (66 bytes): fp16 d ~ U[1e-4,2e-3] at bytes 0..1,
+ * then 8 groups of 8 uniform random bytes (4 grid indices, then a 32-bit word
+ * holding 4x7 sign bits and a 4-bit scale).  Draw indices 9*blk + 0..8.
+ */
+GEN_HD void gen_iq2_block(uint64_t key, uint64_t blk, uint8_t* out) {
+  uint64_t base = blk * 9ULL;
+  gen_put_u16(out, gen_f16(gen_uniform(gen_draw(key, base), 1e-4, 2e-3)));
+  for (int g = 0; g < 8; g++) gen_put_u64(out + 2 + 8 * g, gen_draw(key, base + 1 + g));
+}
+
+/*
+ * Q8_0-format block `blk` (34 bytes, 32 values): fp16 d ~ U[1e-4,1e-3], then
+ * 32 int8 codes uniform in [-127,127].  Draw indices 17*blk + 0..16.
+ */
+GEN_HD void gen_q80_block(uint64_t key, uint64_t blk, uint8_t* out) {
+  uint64_t base = blk * 17ULL;
+  gen_put_u16(out, gen_f16(gen_uniform(gen_draw(key, base), 1e-4, 1e-3)));
+  for (int j = 0; j < 16; j++) {
+    uint64_t d = gen_draw(key, base + 1 + j);
+    out[2 + 2 * j] = (uint8_t)(int8_t)((int)gen_below(d, 255u) - 127);
+    out[3 + 2 * j] = (uint8_t)(int8_t)((int)gen_below(d >> 32, 255u) - 127);
+  }
+}
+
+GEN_HD int gen_block_bytes(int qtype) {
+  return qtype == DS4GEN_Q2_K ? DS4GEN_Q2K_BYTES
+       : qtype == DS4GEN_IQ2_XXS ? DS4GEN_IQ2_BYTES
+       : DS4GEN_Q80_BYTES;
+}
+
+GEN_HD int gen_block_values(int qtype) { return qtype == DS4GEN_Q8_0 ? 32 : 256; }
+
+GEN_HD void gen_block(int qtype, uint64_t key, uint64_t blk, uint8_t* out) {
+  if (qtype == DS4GEN_Q2_K) gen_q2k_block(key, blk, out);
+  else if (qtype == DS4GEN_IQ2_XXS) gen_iq2_block(key, blk, out);
+  else gen_q80_block(key, blk, out);
+}
+
+#endif /* DS4GEN_H */

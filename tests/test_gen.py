@@ -1,0 +1,45 @@
+"""Synthetic input generator: determinism, random access and rounding."""
+import numpy as np
+
+import ds4gen
+import oracle
+
+
+def test_blocks_are_random_access_and_deterministic():
+    for qt in (ds4gen.Q2_K, ds4gen.IQ2_XXS, ds4gen.Q8_0):
+        a = ds4gen.blocks(qt, 7, 3, 100, 20)
+        b = ds4gen.blocks(qt, 7, 3, 110, 5)
+        bb = ds4gen.BLOCK_BYTES[qt]
+        np.testing.assert_array_equal(a[10 * bb:15 * bb], b)
+        assert not np.array_equal(ds4gen.blocks(qt, 8, 3, 100, 1), a[:bb])
+
+
+def test_block_field_ranges():
+    q = ds4gen.blocks(ds4gen.Q2_K, 1, 5, 0, 2000).reshape(2000, 84)
+    d = q[:, 80:82].copy().view(np.float16).astype(np.float64).ravel()
+    dmin = q[:, 82:84].copy().view(np.float16).astype(np.float64).ravel()
+    assert d.min() >= 1e-3 * (1 - 2 ** -10) and d.max() <= 1e-2 * (1 + 2 ** -10)
+    assert dmin.min() >= 0 and dmin.max() <= 5e-3 * (1 + 2 ** -10)
+    iq = ds4gen.blocks(ds4gen.IQ2_XXS, 1, 3, 0, 2000).reshape(2000, 66)
+    d = iq[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
+    assert d.min() >= 1e-4 * (1 - 2 ** -10) and d.max() <= 2e-3 * (1 + 2 ** -10)
+    q8 = ds4gen.blocks(ds4gen.Q8_0, 1, 6, 0, 2000).reshape(2000, 34)
+    codes = q8[:, 2:].view(np.int8)
+    assert codes.min() == -127 and codes.max() == 127
+    g = ds4gen.grid(1)
+    assert set(np.unique(g).tolist()) == {8, 25, 43}
+
+
+def test_rounding_matches_independent_conversions():
+    v = ds4gen.normal(3, 1, 5000, 0.0, 0.02, "f64")
+    f16 = ds4gen.normal(3, 1, 5000, 0.0, 0.02, "f16")
+    np.testing.assert_array_equal(f16, v.astype(np.float16).view(np.uint16))
+    v = ds4gen.normal(3, 10, 3000, 0.0, 1.0, "f64")
+    bf = ds4gen.normal(3, 10, 3000, 0.0, 1.0, "bf16")
+    np.testing.assert_array_equal(bf, [oracle.round_bf16(x) for x in v])
+
+
+def test_tid2eid_rows_distinct():
+    t = ds4gen.tid2eid(4, 11, 0, 5000, 256, 6)
+    assert t.min() >= 0 and t.max() < 256
+    assert all(len(set(r.tolist())) == 6 for r in t)
