@@ -1,0 +1,349 @@
+// ds4moe_api.hip -- C ABI of libds4moe (declared in include/ds4moe.h):
+// argument checks, workspace layout and kernel dispatch.  Built as one
+// translation unit with the kernel sources.
+#include <string.h>
+
+#include "dev_common.h"
+#include "ffn_b1.hip"
+#include "ffn_generic.hip"
+#include "grouped.hip"
+#include "route.hip"
+
+#define DS4_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace ds4;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Byte offsets of the workspace regions for (shape, n_tok).
+struct Layout {
+  size_t status, counters, kbuf, ids, wts, xn, hs, perm, h, y, hb, total;
+};
+
+Layout layout_for(const ds4moe_shape& s, int32_t T) {
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o = align_up(o + bytes, 256);
+    return r;
+  };
+  const size_t E = (size_t)s.n_expert, K = (size_t)s.top_k, H = (size_t)s.hidden,
+               I = (size_t)s.inter, t = (size_t)T;
+  const size_t np = t * K + t;  // routed pairs + shared-expert rows
+  L.status = take(256);
+  L.counters = take(t * 4);
+  L.kbuf = take(t * E * 16);
+  L.ids = take(t * K * 4);
+  L.wts = take(t * K * 4);
+  L.xn = take(t * H * 2);
+  L.hs = take(K * 64 * 16 * 4);
+  L.perm = take((E + (E + 1) + 2 * t * K + 64) * 4);
+  L.h = take(np * I * 4);
+  L.y = take(np * H * 4);
+  L.hb = take(np * I * 2);
+  L.total = o;
+  return L;
+}
+
+bool shape_ok(const ds4moe_shape* s) {
+  return s && s->hidden > 0 && s->hidden % 256 == 0 && s->inter > 0 && s->inter % 32 == 0 &&
+         s->n_expert >= 1 && s->n_expert <= 256 && s->top_k >= 1 && s->top_k <= s->n_expert &&
+         s->top_k <= 64;
+}
+
+bool qtype_ok(int32_t q) { return q == DS4MOE_Q2_K || q == DS4MOE_IQ2_XXS || q == DS4MOE_Q8_0; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool experts_ok(const ds4moe_experts* ex, int32_t H) {
+  if (!ex || !ex->gate || !ex->up || !ex->down) return false;
+  if (!qtype_ok(ex->gate_qtype) || !qtype_ok(ex->up_qtype) || !qtype_ok(ex->down_qtype)) return false;
+  if (ex->inter <= 0 || ex->inter % 32 != 0 || H % 256 != 0) return false;
+  bool need_grid = ex->gate_qtype == DS4MOE_IQ2_XXS || ex->up_qtype == DS4MOE_IQ2_XXS ||
+                   ex->down_qtype == DS4MOE_IQ2_XXS;
+  if (need_grid && !ex->grid) return false;
+  return aligned(ex->gate, 4) && aligned(ex->up, 4) && aligned(ex->down, 4);
+}
+
+ds4moe_status launched() {
+  return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// ---- routing ---------------------------------------------------------------
+ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void* x, int32_t x_dt,
+                       const float* residual, const float* norm_w, float eps, uint16_t* xn_out,
+                       int32_t T, const int32_t* tok, int32_t* ids, float* wts, void* ws,
+                       const Layout& L, hipStream_t st) {
+  uint32_t* status = at<uint32_t>(ws, L.status);
+  if (r.tid2eid) {
+    hipLaunchKernelGGL(k_route_hash, dim3((T + 255) / 256), dim3(256), 0, st, tok, r.tid2eid,
+                       r.vocab, s.n_expert, s.top_k, T, s.routed_scale, ids, wts, status);
+    return launched();
+  }
+  RouteArgs a{};
+  a.x = x;
+  a.x_dt = x_dt;
+  a.residual = residual;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.xn_out = xn_out;
+  a.W = r.w;
+  a.w_dt = r.w_dtype;
+  a.bias = r.bias;
+  a.H = s.hidden;
+  a.E = s.n_expert;
+  a.K = s.top_k;
+  a.T = T;
+  a.scale = s.routed_scale;
+  a.kbuf = at<float4>(ws, L.kbuf);
+  a.counters = at<unsigned>(ws, L.counters);
+  a.ids = ids;
+  a.wts = wts;
+  a.status = status;
+  hipLaunchKernelGGL(k_route, dim3(s.n_expert, T), dim3(256), 0, st, a);
+  return launched();
+}
+
+// RMSNorm only (hash layers): one block per token writes xn.
+__global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, const float* w,
+                                                     float eps, int H, uint16_t* xn) {
+  __shared__ double sh[8];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  double ss = 0.0, dummy = 0.0;
+  for (int c = tid; c < H; c += 256) {
+    double v = (double)residual[(size_t)t * H + c];
+    ss = fma(v, v, ss);
+  }
+  block_sum2(ss, dummy, sh);
+  double ns = 1.0 / sqrt(ss / (double)H + (double)eps);
+  for (int c = tid; c < H; c += 256)
+    xn[(size_t)t * H + c] =
+        (uint16_t)f64_to_bf16_bits((double)residual[(size_t)t * H + c] * ns * (double)w[c]);
+}
+
+// ---- expert FFN dispatch ----------------------------------------------------
+bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_experts* sh,
+             const void* x, int32_t x_dt, int32_t T) {
+  return T == 1 && !sh && x_dt == DS4MOE_BF16 && s.hidden == kH && s.inter == kI && ex.inter == kI &&
+         s.top_k == 6 && ex.gate_qtype == DS4MOE_IQ2_XXS && ex.up_qtype == DS4MOE_IQ2_XXS &&
+         ex.down_qtype == DS4MOE_Q2_K && aligned(x, 16) && aligned(ex.gate, 16) &&
+         aligned(ex.up, 16) && aligned(ex.down, 16);
+}
+
+ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_experts* sh,
+                     const void* x, int32_t x_dt, int32_t T, const int32_t* ids, const float* wts,
+                     float* out, float* residual, int32_t* perm_dbg, void* ws, const Layout& L,
+                     hipStream_t st) {
+  uint32_t* status = at<uint32_t>(ws, L.status);
+  if (fast_b1(s, ex, sh, x, x_dt, T)) {
+    uint16_t* hs = at<uint16_t>(ws, L.hs);
+    hipLaunchKernelGGL((k_gateup_iq2_b1<2>), dim3(kI / 8, 6), dim3(256), 0, st,
+                       (const uint16_t*)x, (const uint8_t*)ex.gate, (const uint8_t*)ex.up,
+                       ex.grid, ids, s.n_expert, hs, status);
+    ds4moe_status rc = launched();
+    if (rc != DS4MOE_OK) return rc;
+    hipLaunchKernelGGL((k_down_q2k_b1<4, 6>), dim3(kH / 16), dim3(256), 0, st, hs,
+                       (const uint8_t*)ex.down, ids, wts, s.n_expert, out, residual, status);
+    return launched();
+  }
+  if (T > 1 && grouped_eligible(s, ex, sh, x, x_dt, T)) {
+    return run_grouped(s, ex, sh, (const uint16_t*)x, T, ids, wts, out, residual, perm_dbg,
+                       at<int32_t>(ws, L.perm), at<uint16_t>(ws, L.hb), at<float>(ws, L.y),
+                       status, st);
+  }
+  GenericArgs a{};
+  a.x = x;
+  a.x_dt = x_dt;
+  a.H = s.hidden;
+  a.I = ex.inter;
+  a.E = s.n_expert;
+  a.K = s.top_k;
+  a.T = T;
+  a.qt_g = ex.gate_qtype;
+  a.qt_u = ex.up_qtype;
+  a.qt_d = ex.down_qtype;
+  a.gate = (const uint8_t*)ex.gate;
+  a.up = (const uint8_t*)ex.up;
+  a.down = (const uint8_t*)ex.down;
+  a.grid = ex.grid;
+  a.sh_I = sh ? sh->inter : 0;
+  if (sh) {
+    a.sh_qt_g = sh->gate_qtype;
+    a.sh_qt_u = sh->up_qtype;
+    a.sh_qt_d = sh->down_qtype;
+    a.sh_gate = (const uint8_t*)sh->gate;
+    a.sh_up = (const uint8_t*)sh->up;
+    a.sh_down = (const uint8_t*)sh->down;
+    a.sh_grid = sh->grid;
+  }
+  a.ids = ids;
+  a.wts = wts;
+  a.h = at<float>(ws, L.h);
+  a.y = at<float>(ws, L.y);
+  a.out = out;
+  a.residual = residual;
+  a.n_sh = sh ? T : 0;
+  a.status = status;
+  const int np = T * s.top_k + a.n_sh;
+  const int imax = a.I > a.sh_I ? a.I : a.sh_I;
+  hipLaunchKernelGGL(k_generic_gateup, dim3((imax + 3) / 4, np), dim3(256), 0, st, a);
+  ds4moe_status rc = launched();
+  if (rc != DS4MOE_OK) return rc;
+  hipLaunchKernelGGL(k_generic_down, dim3((s.hidden + 3) / 4, np), dim3(256), 0, st, a);
+  rc = launched();
+  if (rc != DS4MOE_OK) return rc;
+  size_t n = (size_t)T * s.hidden;
+  hipLaunchKernelGGL(k_generic_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+  return launched();
+}
+
+bool x_dtype_ok(int32_t dt) { return dt == DS4MOE_BF16 || dt == DS4MOE_F32; }
+
+}  // namespace
+
+DS4_EXPORT size_t ds4moe_workspace_size(const ds4moe_shape* shape, int32_t n_tok) {
+  if (!shape_ok(shape) || n_tok < 0) return 0;
+  return layout_for(*shape, n_tok > 0 ? n_tok : 1).total;
+}
+
+DS4_EXPORT ds4moe_status ds4moe_route(const ds4moe_shape* shape, const ds4moe_router* router,
+                                      const void* x, int32_t x_dtype, int32_t n_tok,
+                                      const int32_t* token_ids, int32_t* expert_ids,
+                                      float* weights, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  if (!shape_ok(shape) || !router || n_tok < 0 || !expert_ids || !weights || !ws)
+    return DS4MOE_EINVAL;
+  if (n_tok == 0) return DS4MOE_OK;
+  Layout L = layout_for(*shape, n_tok);
+  if (ws_bytes < L.total) return DS4MOE_EWORKSPACE;
+  if (router->tid2eid) {
+    if (!token_ids || router->vocab <= 0) return DS4MOE_EINVAL;
+  } else {
+    if (!router->w || !router->bias || !x || !x_dtype_ok(x_dtype)) return DS4MOE_EINVAL;
+    if (router->w_dtype != DS4MOE_F16 && router->w_dtype != DS4MOE_F32) return DS4MOE_EINVAL;
+  }
+  return do_route(*shape, *router, x, x_dtype, nullptr, nullptr, 0.0f, nullptr, n_tok, token_ids,
+                  expert_ids, weights, ws, L, stream);
+}
+
+DS4_EXPORT ds4moe_status ds4moe_permute(const ds4moe_shape* shape, const int32_t* expert_ids,
+                                        int32_t n_tok, int32_t* counts, int32_t* offsets,
+                                        int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  if (!shape_ok(shape) || !expert_ids || !counts || !offsets || !perm || !inv || !ws || n_tok < 0)
+    return DS4MOE_EINVAL;
+  if ((int64_t)n_tok * shape->top_k > 32768) return DS4MOE_EUNSUPPORTED;
+  if (n_tok == 0) return DS4MOE_OK;
+  Layout L = layout_for(*shape, n_tok);
+  if (ws_bytes < L.total) return DS4MOE_EWORKSPACE;
+  return launch_permute(expert_ids, n_tok * shape->top_k, shape->n_expert, counts, offsets, perm,
+                        inv, at<uint32_t>(ws, L.status), stream);
+}
+
+DS4_EXPORT ds4moe_status ds4moe_expert_ffn(const ds4moe_shape* shape,
+                                           const ds4moe_experts* routed,
+                                           const ds4moe_experts* shared, const void* x,
+                                           int32_t x_dtype, int32_t n_tok,
+                                           const int32_t* expert_ids, const float* weights,
+                                           float* out, int32_t* perm_dbg, void* ws,
+                                           size_t ws_bytes, hipStream_t stream) {
+  if (!shape_ok(shape) || !experts_ok(routed, shape->hidden) || !x || !x_dtype_ok(x_dtype) ||
+      !expert_ids || !weights || !out || !ws || n_tok < 0)
+    return DS4MOE_EINVAL;
+  if (routed->inter != shape->inter) return DS4MOE_EINVAL;
+  if (shared && (!experts_ok(shared, shape->hidden) || shared->inter > shape->inter))
+    return DS4MOE_EINVAL;
+  if (n_tok == 0) return DS4MOE_OK;
+  Layout L = layout_for(*shape, n_tok);
+  if (ws_bytes < L.total) return DS4MOE_EWORKSPACE;
+  if ((int64_t)n_tok * shape->top_k > 32768) return DS4MOE_EUNSUPPORTED;
+  return do_ffn(*shape, *routed, shared, x, x_dtype, n_tok, expert_ids, weights, out, nullptr,
+                perm_dbg, ws, L, stream);
+}
+
+DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_layer_desc* desc,
+                                      const void* x, int32_t x_dtype, float* residual, float* out,
+                                      const int32_t* token_ids, int32_t n_tok, int32_t* ids_dbg,
+                                      float* w_dbg, uint16_t* xn_dbg, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  if (!shape_ok(shape) || !desc || !experts_ok(&desc->routed, shape->hidden) || !ws || n_tok < 0)
+    return DS4MOE_EINVAL;
+  if (desc->routed.inter != shape->inter) return DS4MOE_EINVAL;
+  const ds4moe_experts* sh = desc->shared;
+  if (sh && (!experts_ok(sh, shape->hidden) || sh->inter > shape->inter)) return DS4MOE_EINVAL;
+  const ds4moe_router& r = desc->router;
+  if (r.tid2eid) {
+    if (!token_ids || r.vocab <= 0) return DS4MOE_EINVAL;
+  } else if (!r.w || !r.bias || (r.w_dtype != DS4MOE_F16 && r.w_dtype != DS4MOE_F32)) {
+    return DS4MOE_EINVAL;
+  }
+  const bool norm = desc->norm_w != nullptr;
+  if (norm) {
+    if (!residual) return DS4MOE_EINVAL;
+  } else {
+    if (!x || !x_dtype_ok(x_dtype) || !out) return DS4MOE_EINVAL;
+  }
+  if (n_tok == 0) return DS4MOE_OK;
+  if ((int64_t)n_tok * shape->top_k > 32768) return DS4MOE_EUNSUPPORTED;
+  Layout L = layout_for(*shape, n_tok);
+  if (ws_bytes < L.total) return DS4MOE_EWORKSPACE;
+  int32_t* ids = at<int32_t>(ws, L.ids);
+  float* wts = at<float>(ws, L.wts);
+  uint16_t* xn = at<uint16_t>(ws, L.xn);
+  ds4moe_status rc;
+  if (norm && r.tid2eid) {
+    hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(n_tok), dim3(256), 0, stream, residual, desc->norm_w,
+                       desc->norm_eps, shape->hidden, xn);
+    if ((rc = launched()) != DS4MOE_OK) return rc;
+  }
+  rc = do_route(*shape, r, x, x_dtype, norm ? residual : nullptr, norm ? desc->norm_w : nullptr,
+                desc->norm_eps, norm ? xn : nullptr, n_tok, token_ids, ids, wts, ws, L, stream);
+  if (rc != DS4MOE_OK) return rc;
+  const void* fx = norm ? (const void*)xn : x;
+  int32_t fdt = norm ? (int32_t)DS4MOE_BF16 : x_dtype;
+  rc = do_ffn(*shape, desc->routed, sh, fx, fdt, n_tok, ids, wts, norm ? nullptr : out,
+              norm ? residual : nullptr, nullptr, ws, L, stream);
+  if (rc != DS4MOE_OK) return rc;
+  if (ids_dbg &&
+      hipMemcpyAsync(ids_dbg, ids, sizeof(int32_t) * n_tok * shape->top_k, hipMemcpyDeviceToDevice,
+                     stream) != hipSuccess)
+    return DS4MOE_EDEVICE;
+  if (w_dbg && hipMemcpyAsync(w_dbg, wts, sizeof(float) * n_tok * shape->top_k,
+                              hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return DS4MOE_EDEVICE;
+  if (xn_dbg && norm &&
+      hipMemcpyAsync(xn_dbg, xn, sizeof(uint16_t) * (size_t)n_tok * shape->hidden,
+                     hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return DS4MOE_EDEVICE;
+  return DS4MOE_OK;
+}
+
+DS4_EXPORT ds4moe_status ds4moe_check(void* ws, hipStream_t stream, uint32_t* faults) {
+  if (!ws) return DS4MOE_EINVAL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return DS4MOE_EDEVICE;
+  uint32_t v = 0, zero = 0;
+  if (hipMemcpy(&v, ws, 4, hipMemcpyDeviceToHost) != hipSuccess) return DS4MOE_EDEVICE;
+  if (v && hipMemcpy(ws, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return DS4MOE_EDEVICE;
+  if (faults) *faults = v;
+  return v ? DS4MOE_EDATA : DS4MOE_OK;
+}
+
+DS4_EXPORT const char* ds4moe_status_string(ds4moe_status s) {
+  switch (s) {
+    case DS4MOE_OK: return "ok";
+    case DS4MOE_EINVAL: return "invalid argument";
+    case DS4MOE_EUNSUPPORTED: return "unsupported shape or type";
+    case DS4MOE_EWORKSPACE: return "workspace too small";
+    case DS4MOE_EDEVICE: return "HIP call failed";
+    case DS4MOE_EDATA: return "device-detected data fault";
+  }
+  return "unknown status";
+}

@@ -1,0 +1,197 @@
+/*
+ * ds4moe.h -- C ABI of libds4moe: the DeepSeek-V4-Flash routed-expert MoE
+ * FFN on block-quantised 2-bit weights, for AMD MI355X (gfx950).
+ *
+ * The method (pages: FLOW = qiita.com/sukimaengineer/items/cd76fec76d49a098abed,
+ * section "MoE FFN 部の中身: router -> top-6 -> expert -> 加重和" and the
+ * config table; DS4C2 = qiita.com/yoshiyakato/items/4678be0e7860ddb444ec,
+ * sections 3 "Q2_K" and 4 "IQ2_XXS"):
+ *   logits   z = x . W_r^T                 (router, f16 weights)
+ *   scores   s = sqrtsoftplus(z) = sqrt(ln(1 + e^z))
+ *   select   the top_k of key = s + bias   (bias for selection only)
+ *   gates    g = routed_scale * s_sel / sum(s_sel)
+ *   experts  E(x) = W_down (SiLU(W_gate x) * W_up x)
+ *   output   y = shared(x) + sum_k g_k E_k(x)
+ * with the first layers routed by a static token-id table instead
+ * (FLOW: hash routing in layers 0-2, no router there).
+ *
+ * Conventions for every entry point:
+ *  - Data pointers are DEVICE pointers (hipMalloc'd or equivalent) unless
+ *    stated; the caller owns all memory.  Calls only enqueue work on
+ *    `stream` and return without waiting; nothing is allocated.
+ *  - Arguments are checked on the host before anything is launched; a
+ *    negative status means nothing was enqueued.
+ *  - Faults in the data that only the device can see (an expert id out of
+ *    range in caller-given routing, a bad hash-table row, a token id out of
+ *    range, a routing decision that could not be certified) set bits of a
+ *    status word in the workspace; ds4moe_check() reports them.  Such data
+ *    never causes an out-of-bounds access: offending ids are replaced by
+ *    valid ones before use.
+ *  - The workspace `ws` (ws_bytes >= ds4moe_workspace_size()) must be
+ *    zero-filled once before its first use; every call leaves its internal
+ *    counters at zero again.  Calls sharing one workspace must be ordered
+ *    on one stream.
+ *  - No exceptions cross the ABI.  NaN or Inf in activations propagate.
+ */
+#ifndef DS4MOE_H
+#define DS4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DS4MOE_OK = 0,
+  DS4MOE_EINVAL = -1,      /* bad argument (null, size, alignment, dtype) */
+  DS4MOE_EUNSUPPORTED = -2,/* valid but not implemented for this shape/type */
+  DS4MOE_EWORKSPACE = -3,  /* workspace smaller than ds4moe_workspace_size */
+  DS4MOE_EDEVICE = -4,     /* a HIP call failed */
+  DS4MOE_EDATA = -5        /* device-detected data fault (ds4moe_check) */
+} ds4moe_status;
+
+typedef enum { DS4MOE_F32 = 0, DS4MOE_F16 = 1, DS4MOE_BF16 = 2 } ds4moe_dtype;
+
+/* Block formats (DS4C2 sections 3 and 4; FLOW quantisation table):
+ *  Q2_K      84 B / 256 values: 16 B scale|min nibbles, 64 B 2-bit codes,
+ *            fp16 d, fp16 dmin;  y = d*sc*q - dmin*m
+ *  IQ2_XXS   66 B / 256 values: fp16 d, 8 groups of (4 grid-index bytes,
+ *            u32 of 4x7 sign bits + 4-bit scale s); y = d*(2s+1)/8*grid*sign
+ *  Q8_0      34 B / 32 values: fp16 d, 32 int8; y = d*c                    */
+typedef enum { DS4MOE_Q2_K = 0, DS4MOE_IQ2_XXS = 1, DS4MOE_Q8_0 = 2 } ds4moe_qtype;
+
+/* Layer shape.  hidden must be a multiple of 256 and inter of 32 (blocks
+ * tile the row-major flattening of each matrix, so a block may span rows);
+ * top_k <= n_expert <= 256, top_k <= 64. */
+typedef struct {
+  int32_t hidden;       /* H (4096)                                    */
+  int32_t inter;        /* routed expert intermediate size I (2048)    */
+  int32_t n_expert;     /* E (256)                                     */
+  int32_t top_k;        /* K (6)                                       */
+  float routed_scale;   /* routed_scaling_factor (1.5)                 */
+} ds4moe_shape;
+
+/* A stacked set of SwiGLU experts.  gate and up are [n][inter][hidden],
+ * down is [n][hidden][inter]; each matrix is the row-major flattening cut
+ * into consecutive blocks of its qtype (all experts of a layer in one
+ * tensor, expert e starting at e * rows * cols / values_per_block blocks).
+ * Pointers must be 4-byte aligned.  `grid` (IQ2_XXS only) is 256 x 8 bytes
+ * of grid values (each < 128). */
+typedef struct {
+  int32_t gate_qtype, up_qtype, down_qtype;
+  const void* gate;
+  const void* up;
+  const void* down;
+  int32_t inter;          /* intermediate size of these experts */
+  const uint8_t* grid;    /* device, required if any qtype is IQ2_XXS */
+} ds4moe_experts;
+
+/* Router of one layer.  Either a learned router (w != NULL: [n_expert][hidden]
+ * of w_dtype F16 or F32, plus fp32 bias[n_expert] used only for selection),
+ * or a hash layer (tid2eid != NULL: int32 [vocab][top_k], expert ids per token
+ * id, equal gates routed_scale / top_k). */
+typedef struct {
+  const void* w;
+  int32_t w_dtype;
+  const float* bias;
+  const int32_t* tid2eid;
+  int32_t vocab;
+} ds4moe_router;
+
+/* One MoE layer for ds4moe_layer(). */
+typedef struct {
+  ds4moe_router router;
+  ds4moe_experts routed;           /* n = n_expert */
+  const ds4moe_experts* shared;    /* host pointer to a descriptor of one
+                                      always-on expert, or NULL */
+  const float* norm_w;             /* fp32 [hidden] RMSNorm weight, or NULL */
+  float norm_eps;
+} ds4moe_layer_desc;
+
+/* Bytes of workspace needed for n_tok tokens of this shape (0 on bad shape). */
+size_t ds4moe_workspace_size(const ds4moe_shape* shape, int32_t n_tok);
+
+/*
+ * Routing (FLOW "MoE FFN" section): for each of n_tok tokens write the top_k
+ * expert ids (int32 [n_tok][top_k], slots ordered by key descending, ties to
+ * the lower expert index) and gate weights (fp32 [n_tok][top_k], summing to
+ * routed_scale).  x: [n_tok][hidden] of x_dtype (BF16 or F32).
+ * Learned router: logits are the exact dot products rounded once to fp32
+ * (accumulated in fp64 and certified against an error bound), scores are
+ * sqrtsoftplus rounded to fp32, keys are fp32 score + bias.  A selection that
+ * the bounds cannot certify sets the status bit DS4MOE_FAULT_UNCERTIFIED.
+ * Hash layer: token_ids (int32 [n_tok], required) index tid2eid; token ids
+ * outside [0, vocab) or table rows with ids out of range or repeated set a
+ * fault bit and route that token to experts 0..top_k-1.
+ */
+ds4moe_status ds4moe_route(const ds4moe_shape* shape, const ds4moe_router* router, const void* x,
+                           int32_t x_dtype, int32_t n_tok, const int32_t* token_ids,
+                           int32_t* expert_ids, float* weights, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
+ * Token -> expert permutation: pair p = t*top_k + k is ordered by
+ * (expert, t, k).  counts int32 [n_expert], offsets int32 [n_expert+1]
+ * (exclusive prefix sum), perm int32 [n_tok*top_k] (pair at each sorted
+ * position), inv int32 [n_tok*top_k] (position of each pair).  Ids outside
+ * [0, n_expert) set DS4MOE_FAULT_BAD_ID and are counted as expert 0.
+ * n_tok * top_k <= 32768.
+ */
+ds4moe_status ds4moe_permute(const ds4moe_shape* shape, const int32_t* expert_ids, int32_t n_tok,
+                             int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Expert FFN and weighted combine (FLOW "MoE FFN" section):
+ *   out[t] = sum_k weights[t][k] * E_{expert_ids[t][k]}(x[t])  + shared(x[t])
+ * x: [n_tok][hidden] BF16 or F32; out: fp32 [n_tok][hidden].  `shared` may
+ * be NULL.  Accumulation is fp32 (decode paths) or bf16 x bf16 MFMA with
+ * fp32 accumulation (prefill path, n_tok > 64).  The permutation used for
+ * n_tok > 1 may be captured: perm_dbg (nullable) receives
+ * offsets[n_expert+1], perm[n_tok*top_k], inv[n_tok*top_k] (int32).
+ */
+ds4moe_status ds4moe_expert_ffn(const ds4moe_shape* shape, const ds4moe_experts* routed,
+                                const ds4moe_experts* shared, const void* x, int32_t x_dtype,
+                                int32_t n_tok, const int32_t* expert_ids, const float* weights,
+                                float* out, int32_t* perm_dbg, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/*
+ * A whole MoE layer.  If desc->norm_w is set: xn = RMSNorm(residual)
+ * (fp32 [n_tok][hidden] in, bf16 out; mean of squares in fp64), the layer
+ * runs on xn and residual += y (fp32), `x` is ignored and `out` may be NULL.
+ * Otherwise it runs on x and writes y to out (residual ignored).
+ * token_ids are required for hash layers.  Debug captures (nullable): ids_dbg
+ * int32 [n_tok][top_k], w_dbg fp32 [n_tok][top_k], xn_dbg bf16 bits
+ * [n_tok][hidden].
+ */
+ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_layer_desc* desc, const void* x,
+                           int32_t x_dtype, float* residual, float* out,
+                           const int32_t* token_ids, int32_t n_tok, int32_t* ids_dbg, float* w_dbg,
+                           uint16_t* xn_dbg, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Status-word bits reported by ds4moe_check(). */
+#define DS4MOE_FAULT_BAD_ID 0x1u       /* caller-given expert id out of range   */
+#define DS4MOE_FAULT_BAD_TOKEN 0x2u    /* token id outside [0, vocab)           */
+#define DS4MOE_FAULT_BAD_TABLE 0x4u    /* tid2eid row out of range / repeated   */
+#define DS4MOE_FAULT_UNCERTIFIED 0x8u  /* routing not certifiable (see route)   */
+#define DS4MOE_FAULT_F16_RANGE 0x10u   /* an intermediate exceeded binary16     */
+
+/*
+ * Waits for `stream`, reads and clears the workspace status word.  Returns
+ * DS4MOE_OK if no fault bit was set, DS4MOE_EDATA otherwise; *faults
+ * (nullable, host) receives the bits.
+ */
+ds4moe_status ds4moe_check(void* ws, hipStream_t stream, uint32_t* faults);
+
+const char* ds4moe_status_string(ds4moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS4MOE_H */

@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.  Expert ids, permutations and hash lookups must match bit
+for bit; outputs within max|err| <= 2e-3 * RMS(out) (fp32 accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_expert_ds4moe_amd as ds4
+import ds4gen as g
+import oracle
+from gpu_util import (TOL_FP32, check_clean, experts_of, max_rel_err, ptr, say, shape_of,
+                      shared_of, stream, workspace, x_dtype, x_fmt)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ds4.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a):
+    from ds4gen.device import to_dev
+    return to_dev(a)
+
+
+# --------------------------------------------------------------------------
+# generator: device fill == host bytes
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("qt", [g.Q2_K, g.IQ2_XXS, g.Q8_0])
+def test_device_fill_matches_host(qt):
+    say("device fill qt", qt)
+    n, first = 1000 + 37, 12345
+    t = torch.empty(n * g.BLOCK_BYTES[qt], dtype=torch.uint8, device="cuda")
+    g.fill_device(qt, 3, 77, first, n, t.data_ptr(), stream())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(t.cpu().numpy(), g.blocks(qt, 3, 77, first, n))
+
+
+# --------------------------------------------------------------------------
+# routing
+# --------------------------------------------------------------------------
+def run_route(w, x, W, bias, T):
+    shp = shape_of(w)
+    ws, nb = workspace(shp, T)
+    wdt = ds4.F32 if w.router_fmt == "f32" else ds4.F16
+    r = ds4.router(w=ptr(W), w_dtype=wdt, bias=ptr(bias))
+    ids = torch.empty((T, w.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, w.K), dtype=torch.float32, device="cuda")
+    ds4.route(shp, r, ptr(x), x_dtype(w), T, None, ptr(ids), ptr(wts), ptr(ws), nb, stream())
+    check_clean(ws)
+    return ids.cpu().numpy(), wts.cpu().numpy()
+
+
+@pytest.mark.parametrize("widx,T", [(0, 4), (1, 16)])
+def test_route_bit_exact(widx, T):
+    w = g.WORKLOADS[widx]
+    say("route", w.name, "T", T)
+    x = g.activations(w, n_tok=T)
+    W = g.router_weight(w, 0)
+    b = g.router_bias(w, 0)
+    ids, wts = run_route(w, dev(x), dev(W), dev(b), T)
+    oids, owts, _, _ = oracle.route(x, x_fmt(w), W, w.router_fmt, b, w.K)
+    np.testing.assert_array_equal(ids, oids)
+    np.testing.assert_allclose(wts, owts, rtol=2e-6, atol=0)
+    assert np.allclose(wts.astype(np.float64).sum(1), 1.5, rtol=2e-6)
+
+
+def test_route_ties_and_bias():
+    # identical router rows give identical keys: the lower index must win,
+    # and a large bias forces an expert in without changing its gate
+    w = g.WORKLOADS[1]
+    T = 4
+    x = g.activations(w, n_tok=T)
+    W = g.router_weight(w, 0).copy()
+    W[200] = W[10]
+    b = g.router_bias(w, 0).copy()
+    b[200] = b[10]
+    b[77] = 50.0
+    ids, wts = run_route(w, dev(x), dev(W), dev(b), T)
+    oids, owts, _, _ = oracle.route(x, "bf16", W, "f16", b, w.K)
+    np.testing.assert_array_equal(ids, oids)
+    assert np.all(ids[:, 0] == 77)
+    np.testing.assert_allclose(wts, owts, rtol=2e-6)
+
+
+def test_hash_route_is_table_lookup():
+    w = g.WORKLOADS[4]
+    say("hash route")
+    table = g.hash_table(w, 1)
+    tok = g.token_ids(w, 64)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, 64)
+    tabd = dev(table)
+    r = ds4.router(tid2eid=ptr(tabd), vocab=w.vocab)
+    tokd = dev(tok)
+    ids = torch.empty((64, 6), dtype=torch.int32, device="cuda")
+    wts = torch.empty((64, 6), dtype=torch.float32, device="cuda")
+    ds4.route(shp, r, None, ds4.BF16, 64, ptr(tokd), ptr(ids), ptr(wts), ptr(ws), nb, stream())
+    check_clean(ws)
+    oids, owts = oracle.route_hash(tok, table, 256, 6)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    np.testing.assert_array_equal(wts.cpu().numpy(), owts)
+    # a token id out of range is reported and routed to experts 0..5
+    bad = dev(np.array([w.vocab + 5, -1], np.int32))
+    ds4.route(shp, r, None, ds4.BF16, 2, ptr(bad), ptr(ids), ptr(wts), ptr(ws), nb, stream())
+    f = ds4.check(ptr(ws), stream())
+    assert f & ds4.FAULT_BAD_TOKEN
+    np.testing.assert_array_equal(ids.cpu().numpy()[:2], [list(range(6))] * 2)
+
+
+# --------------------------------------------------------------------------
+# permutation
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [1, 8, 512, 2000])
+def test_permute_bit_exact(T):
+    say("permute T", T)
+    ids, _ = g.zipf_routing(3, T, 256, 6)
+    shp = ds4.shape(4096, 2048, 256, 6)
+    ws, nb = workspace(shp, T)
+    idd = dev(ids)
+    counts = torch.empty(256, dtype=torch.int32, device="cuda")
+    offs = torch.empty(257, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T * 6, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T * 6, dtype=torch.int32, device="cuda")
+    ds4.permute(shp, ptr(idd), T, ptr(counts), ptr(offs), ptr(perm), ptr(inv), ptr(ws), nb, stream())
+    check_clean(ws)
+    oc, oo, op, oi = oracle.permute(ids, 256)
+    np.testing.assert_array_equal(counts.cpu().numpy(), oc)
+    np.testing.assert_array_equal(offs.cpu().numpy(), oo)
+    np.testing.assert_array_equal(perm.cpu().numpy(), op)
+    np.testing.assert_array_equal(inv.cpu().numpy(), oi)
+
+
+def test_permute_flags_bad_id():
+    shp = ds4.shape(4096, 2048, 256, 6)
+    ws, nb = workspace(shp, 1)
+    idd = dev(np.array([[1, 2, 300, 4, 5, 6]], np.int32))
+    bufs = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (256, 257, 6, 6)]
+    ds4.permute(shp, ptr(idd), 1, *[ptr(b) for b in bufs], ptr(ws), nb, stream())
+    assert ds4.check(ptr(ws), stream()) & ds4.FAULT_BAD_ID
+
+
+# --------------------------------------------------------------------------
+# expert FFN
+# --------------------------------------------------------------------------
+def ffn_case(widx, T, tokens_for_oracle=None, given=None):
+    from ds4gen.device import make_layer, host_experts, host_shared
+    w = g.WORKLOADS[widx]
+    say("ffn", w.name, "T", T)
+    lt = make_layer(w, 0)
+    x = g.activations(w, n_tok=T)
+    if given is None:
+        ids, wts, _, _ = oracle.route(x, x_fmt(w), g.router_weight(w, 0), w.router_fmt,
+                                      g.router_bias(w, 0), w.K)
+    else:
+        ids, wts = given
+    shp = shape_of(w)
+    ws, nb = workspace(shp, T)
+    out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    xd, idd, wd = dev(x), dev(ids), dev(wts)
+    ds4.expert_ffn(shp, experts_of(lt, w), shared_of(lt, w), ptr(xd), x_dtype(w), T, ptr(idd),
+                   ptr(wd), ptr(out), None, ptr(ws), nb, stream())
+    check_clean(ws)
+    got = out.cpu().numpy()
+    toks = np.arange(T) if tokens_for_oracle is None else np.asarray(tokens_for_oracle)
+    used = np.unique(ids[toks])
+    sh = host_shared(w, 0) if w.shared else None
+    want = oracle.moe_ffn(x, x_fmt(w), ids, wts, host_experts(w, 0, used),
+                          (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E,
+                          grid=g.grid(w.seed), tokens=toks, shared=sh, sh_I=w.I)
+    err = max_rel_err(got[toks], want)
+    say("  max|err|/rms =", err)
+    return err
+
+
+def test_ffn_tiny_q2k():
+    assert ffn_case(0, 4) <= TOL_FP32
+
+
+def test_ffn_v4_decode_b1():
+    assert ffn_case(1, 1) <= TOL_FP32
+
+
+@pytest.mark.parametrize("tok", [1, 2, 3])
+def test_ffn_v4_decode_b1_more_tokens(tok):
+    from ds4gen.device import make_layer, host_experts
+    w = g.WORKLOADS[1]
+    lt = make_layer(w, 0)
+    x = g.activations(w, n_tok=1, first_tok=tok)
+    ids, wts, _, _ = oracle.route(x, "bf16", g.router_weight(w, 0), "f16", g.router_bias(w, 0), 6)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, 1)
+    out = torch.empty((1, w.H), dtype=torch.float32, device="cuda")
+    xd, idd, wd = dev(x), dev(ids), dev(wts)
+    ds4.expert_ffn(shp, experts_of(lt, w), None, ptr(xd), ds4.BF16, 1, ptr(idd), ptr(wd), ptr(out),
+                   None, ptr(ws), nb, stream())
+    check_clean(ws)
+    want = oracle.moe_ffn(x, "bf16", ids, wts, host_experts(w, 0, ids[0]),
+                          (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed))
+    err = max_rel_err(out.cpu().numpy(), want)
+    say("  token", tok, "max|err|/rms =", err)
+    assert err <= TOL_FP32
+
+
+def test_ffn_v4_decode_b8_shared_q8():
+    assert ffn_case(2, 8) <= TOL_FP32
+
+
+# --------------------------------------------------------------------------
+# whole layer
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("widx", [0, 1])
+def test_layer_route_and_ffn(widx):
+    from ds4gen.device import make_layer, host_experts
+    w = g.WORKLOADS[widx]
+    say("layer", w.name)
+    T = w.T
+    lt = make_layer(w, 0)
+    x = g.activations(w, n_tok=T)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, T)
+    wdt = ds4.F32 if w.router_fmt == "f32" else ds4.F16
+    d = ds4.layer_desc(ds4.router(w=ptr(lt.router_w), w_dtype=wdt, bias=ptr(lt.bias)),
+                       experts_of(lt, w))
+    out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, w.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, w.K), dtype=torch.float32, device="cuda")
+    xd = dev(x)
+    ds4.layer(shp, d, ptr(xd), x_dtype(w), None, ptr(out), None, T, ptr(ids), ptr(wts), None,
+              ptr(ws), nb, stream())
+    check_clean(ws)
+    oids, owts, _, _ = oracle.route(x, x_fmt(w), g.router_weight(w, 0), w.router_fmt,
+                                    g.router_bias(w, 0), w.K)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    want = oracle.moe_ffn(x, x_fmt(w), oids, owts, host_experts(w, 0, np.unique(oids)),
+                          (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed))
+    err = max_rel_err(out.cpu().numpy(), want)
+    say("  max|err|/rms =", err)
+    assert err <= TOL_FP32
