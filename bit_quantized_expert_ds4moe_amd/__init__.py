@@ -18,7 +18,8 @@ Q2_K, IQ2_XXS, Q8_0 = 0, 1, 2
 FAULT_BAD_ID, FAULT_BAD_TOKEN, FAULT_BAD_TABLE, FAULT_UNCERTIFIED, FAULT_F16_RANGE = 1, 2, 4, 8, 16
 
 EXPORTED = ("ds4moe_workspace_size", "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn",
-            "ds4moe_layer", "ds4moe_check", "ds4moe_status_string")
+            "ds4moe_layer", "ds4moe_profile_events", "ds4moe_check", "ds4moe_status_string")
+K_ROUTE, K_GATEUP, K_DOWN, K_PERMUTE, K_OTHER = range(5)
 
 
 class Ds4moeError(RuntimeError):
@@ -74,6 +75,8 @@ def lib():
         L.ds4moe_layer.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(LayerDesc), vp, i32, vp,
                                    vp, vp, i32, vp, vp, vp, vp, sz, vp]
         L.ds4moe_layer.restype = i32
+        L.ds4moe_profile_events.argtypes = [i32, vp, vp]
+        L.ds4moe_profile_events.restype = i32
         L.ds4moe_check.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
         L.ds4moe_check.restype = i32
         L.ds4moe_status_string.argtypes = [i32]
@@ -138,6 +141,11 @@ def layer(shp, desc, x, x_dtype, residual, out, token_ids, n_tok, ids_dbg, w_dbg
     _ok(lib().ds4moe_layer(ctypes.byref(shp), ctypes.byref(desc), x, x_dtype, residual, out,
                            token_ids, n_tok, ids_dbg, w_dbg, xn_dbg, ws, ws_bytes, stream),
         "ds4moe_layer")
+
+
+def profile_events(cls, begin, end):
+    """begin/end: HIP event handles (int) or None to stop."""
+    _ok(lib().ds4moe_profile_events(cls, begin, end), "ds4moe_profile_events")
 
 
 def check(ws, stream=0):

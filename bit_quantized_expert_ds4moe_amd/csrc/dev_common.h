@@ -38,7 +38,7 @@ __device__ inline uint32_t f32_to_f16_bits(float v) {
 
 // Round a double to the nearest bfloat16 (ties to even) and return its bits.
 // Works on the binary64 encoding so no intermediate binary32 rounding occurs.
-__device__ inline uint32_t f64_to_bf16_bits(double v) {
+__device__ __noinline__ uint32_t f64_to_bf16_bits_general(double v) {
   uint64_t b = __double_as_longlong(v);
   uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
   int e = (int)((b >> 52) & 0x7FF);
@@ -64,6 +64,18 @@ __device__ inline uint32_t f64_to_bf16_bits(double v) {
   return sign | (uint32_t)q;
 }
 
+// Same rounding; inline fast path for results in the normal bfloat16 range
+// (a carry out of the mantissa moves into the exponent by itself), the
+// general routine otherwise.
+__device__ inline uint32_t f64_to_bf16_bits(double v) {
+  uint64_t b = __double_as_longlong(v);
+  uint64_t r = b + 0x00000FFFFFFFFFFFULL + ((b >> 45) & 1);
+  int e8 = (int)((r >> 52) & 0x7FF) - 1023 + 127;
+  if (e8 >= 1 && e8 <= 254 && (b & 0x7FFFFFFFFFFFFFFFULL) != 0)
+    return (uint32_t)((b >> 48) & 0x8000u) | ((uint32_t)e8 << 7) | (uint32_t)((r >> 45) & 0x7Fu);
+  return f64_to_bf16_bits_general(v);
+}
+
 // ---- packed dot products ----------------------------------------------------
 __device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -71,6 +83,11 @@ __device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 __device__ inline float dot2_f16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                false);
+}
+__device__ inline int sdot2(uint32_t a, uint32_t b, int c) {
+  typedef short s16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_sdot2(__builtin_bit_cast(s16x2_t, a), __builtin_bit_cast(s16x2_t, b), c,
                                 false);
 }
 __device__ inline uint32_t vperm(uint32_t hi, uint32_t lo, uint32_t sel) {

@@ -19,7 +19,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Byte offsets of the workspace regions for (shape, n_tok).
 struct Layout {
-  size_t status, counters, kbuf, ids, wts, xn, hs, perm, h, y, hb, total;
+  size_t status, kbuf, ids, wts, xn, hs, perm, h, y, hb, total;
 };
 
 Layout layout_for(const ds4moe_shape& s, int32_t T) {
@@ -34,12 +34,11 @@ Layout layout_for(const ds4moe_shape& s, int32_t T) {
                I = (size_t)s.inter, t = (size_t)T;
   const size_t np = t * K + t;  // routed pairs + shared-expert rows
   L.status = take(256);
-  L.counters = take(t * 4);
   L.kbuf = take(t * E * 16);
   L.ids = take(t * K * 4);
   L.wts = take(t * K * 4);
   L.xn = take(t * H * 2);
-  L.hs = take(K * 64 * 16 * 4);
+  L.hs = take(K * 64 * kHqDwords * 4);
   L.perm = take((E + (E + 1) + 2 * t * K + 64) * 4);
   L.h = take(np * I * 4);
   L.y = take(np * H * 4);
@@ -72,6 +71,20 @@ ds4moe_status launched() {
   return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;
 }
 
+// Profiling events per kernel class (ds4moe_profile_events).
+hipEvent_t g_prof[DS4MOE_K_CLASSES][2] = {};
+
+struct ProfScope {
+  int cls;
+  hipStream_t st;
+  ProfScope(int c, hipStream_t s) : cls(c), st(s) {
+    if (g_prof[cls][0]) (void)hipEventRecord(g_prof[cls][0], st);
+  }
+  ~ProfScope() {
+    if (g_prof[cls][1]) (void)hipEventRecord(g_prof[cls][1], st);
+  }
+};
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -83,6 +96,7 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
                        int32_t T, const int32_t* tok, int32_t* ids, float* wts, void* ws,
                        const Layout& L, hipStream_t st) {
   uint32_t* status = at<uint32_t>(ws, L.status);
+  ProfScope prof(DS4MOE_K_ROUTE, st);
   if (r.tid2eid) {
     hipLaunchKernelGGL(k_route_hash, dim3((T + 255) / 256), dim3(256), 0, st, tok, r.tid2eid,
                        r.vocab, s.n_expert, s.top_k, T, s.routed_scale, ids, wts, status);
@@ -104,11 +118,25 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
   a.T = T;
   a.scale = s.routed_scale;
   a.kbuf = at<float4>(ws, L.kbuf);
-  a.counters = at<unsigned>(ws, L.counters);
   a.ids = ids;
   a.wts = wts;
   a.status = status;
-  hipLaunchKernelGGL(k_route, dim3(s.n_expert, T), dim3(256), 0, st, a);
+  const bool vec = s.hidden % 2048 == 0 && s.hidden <= 4096 && r.w_dtype == DS4MOE_F16 &&
+                   (norm_w || x_dt == DS4MOE_BF16) && ((uintptr_t)r.w % 16 == 0) &&
+                   (norm_w ? ((uintptr_t)residual % 16 == 0 && (uintptr_t)norm_w % 16 == 0)
+                           : (uintptr_t)x % 16 == 0);
+  const dim3 grid(s.n_expert, T);
+  if (vec && norm_w)
+    hipLaunchKernelGGL((k_route_score<true, true>), grid, dim3(256), 0, st, a);
+  else if (vec)
+    hipLaunchKernelGGL((k_route_score<false, true>), grid, dim3(256), 0, st, a);
+  else if (norm_w)
+    hipLaunchKernelGGL((k_route_score<true, false>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_route_score<false, false>), grid, dim3(256), 0, st, a);
+  ds4moe_status rc = launched();
+  if (rc != DS4MOE_OK) return rc;
+  hipLaunchKernelGGL(k_route_select, dim3(T), dim3(64), 0, st, a);
   return launched();
 }
 
@@ -144,14 +172,20 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
                      hipStream_t st) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   if (fast_b1(s, ex, sh, x, x_dt, T)) {
-    uint16_t* hs = at<uint16_t>(ws, L.hs);
-    hipLaunchKernelGGL((k_gateup_iq2_b1<2>), dim3(kI / 8, 6), dim3(256), 0, st,
-                       (const uint16_t*)x, (const uint8_t*)ex.gate, (const uint8_t*)ex.up,
-                       ex.grid, ids, s.n_expert, hs, status);
+    uint32_t* hq = at<uint32_t>(ws, L.hs);
+    {
+      ProfScope prof(DS4MOE_K_GATEUP, st);
+      hipLaunchKernelGGL(k_gateup_iq2_b1, dim3(6 * 64), dim3(512), 0, st, (const uint16_t*)x,
+                         (const uint8_t*)ex.gate, (const uint8_t*)ex.up, ex.grid, ids, s.n_expert,
+                         hq, status);
+    }
     ds4moe_status rc = launched();
     if (rc != DS4MOE_OK) return rc;
-    hipLaunchKernelGGL((k_down_q2k_b1<4, 6>), dim3(kH / 16), dim3(256), 0, st, hs,
-                       (const uint8_t*)ex.down, ids, wts, s.n_expert, out, residual, status);
+    {
+      ProfScope prof(DS4MOE_K_DOWN, st);
+      hipLaunchKernelGGL(k_down_q2k_b1, dim3(kH / 8), dim3(384), 0, st, hq,
+                         (const uint8_t*)ex.down, ids, wts, s.n_expert, out, residual, status);
+    }
     return launched();
   }
   if (T > 1 && grouped_eligible(s, ex, sh, x, x_dt, T)) {
@@ -194,14 +228,23 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
   a.status = status;
   const int np = T * s.top_k + a.n_sh;
   const int imax = a.I > a.sh_I ? a.I : a.sh_I;
-  hipLaunchKernelGGL(k_generic_gateup, dim3((imax + 3) / 4, np), dim3(256), 0, st, a);
+  {
+    ProfScope prof(DS4MOE_K_GATEUP, st);
+    hipLaunchKernelGGL(k_generic_gateup, dim3((imax + 3) / 4, np), dim3(256), 0, st, a);
+  }
   ds4moe_status rc = launched();
   if (rc != DS4MOE_OK) return rc;
-  hipLaunchKernelGGL(k_generic_down, dim3((s.hidden + 3) / 4, np), dim3(256), 0, st, a);
+  {
+    ProfScope prof(DS4MOE_K_DOWN, st);
+    hipLaunchKernelGGL(k_generic_down, dim3((s.hidden + 3) / 4, np), dim3(256), 0, st, a);
+  }
   rc = launched();
   if (rc != DS4MOE_OK) return rc;
   size_t n = (size_t)T * s.hidden;
-  hipLaunchKernelGGL(k_generic_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+  {
+    ProfScope prof(DS4MOE_K_OTHER, st);
+    hipLaunchKernelGGL(k_generic_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+  }
   return launched();
 }
 
@@ -229,6 +272,7 @@ DS4_EXPORT ds4moe_status ds4moe_route(const ds4moe_shape* shape, const ds4moe_ro
   } else {
     if (!router->w || !router->bias || !x || !x_dtype_ok(x_dtype)) return DS4MOE_EINVAL;
     if (router->w_dtype != DS4MOE_F16 && router->w_dtype != DS4MOE_F32) return DS4MOE_EINVAL;
+    if (shape->top_k > kMaxRouteK) return DS4MOE_EUNSUPPORTED;
   }
   return do_route(*shape, *router, x, x_dtype, nullptr, nullptr, 0.0f, nullptr, n_tok, token_ids,
                   expert_ids, weights, ws, L, stream);
@@ -244,6 +288,7 @@ DS4_EXPORT ds4moe_status ds4moe_permute(const ds4moe_shape* shape, const int32_t
   if (n_tok == 0) return DS4MOE_OK;
   Layout L = layout_for(*shape, n_tok);
   if (ws_bytes < L.total) return DS4MOE_EWORKSPACE;
+  ProfScope prof(DS4MOE_K_PERMUTE, stream);
   return launch_permute(expert_ids, n_tok * shape->top_k, shape->n_expert, counts, offsets, perm,
                         inv, at<uint32_t>(ws, L.status), stream);
 }
@@ -284,6 +329,8 @@ DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_la
     if (!token_ids || r.vocab <= 0) return DS4MOE_EINVAL;
   } else if (!r.w || !r.bias || (r.w_dtype != DS4MOE_F16 && r.w_dtype != DS4MOE_F32)) {
     return DS4MOE_EINVAL;
+  } else if (shape->top_k > kMaxRouteK) {
+    return DS4MOE_EUNSUPPORTED;
   }
   const bool norm = desc->norm_w != nullptr;
   if (norm) {
@@ -300,6 +347,7 @@ DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_la
   uint16_t* xn = at<uint16_t>(ws, L.xn);
   ds4moe_status rc;
   if (norm && r.tid2eid) {
+    ProfScope prof(DS4MOE_K_OTHER, stream);
     hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(n_tok), dim3(256), 0, stream, residual, desc->norm_w,
                        desc->norm_eps, shape->hidden, xn);
     if ((rc = launched()) != DS4MOE_OK) return rc;
@@ -323,6 +371,13 @@ DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_la
       hipMemcpyAsync(xn_dbg, xn, sizeof(uint16_t) * (size_t)n_tok * shape->hidden,
                      hipMemcpyDeviceToDevice, stream) != hipSuccess)
     return DS4MOE_EDEVICE;
+  return DS4MOE_OK;
+}
+
+DS4_EXPORT ds4moe_status ds4moe_profile_events(int32_t cls, hipEvent_t begin, hipEvent_t end) {
+  if (cls < 0 || cls >= DS4MOE_K_CLASSES) return DS4MOE_EINVAL;
+  g_prof[cls][0] = begin;
+  g_prof[cls][1] = end;
   return DS4MOE_OK;
 }
 

@@ -16,8 +16,10 @@
 // key interval follows because rounding is monotone.  The selection is
 // accepted when every interval is a single binary32 value, or when the chosen
 // order holds for every value in the intervals; otherwise the status bit
-// DS4MOE_FAULT_UNCERTIFIED is raised.
+// DS4MOE_FAULT_UNCERTIFIED is raised.  Scoring and selection are two kernels:
+// the kernel boundary publishes the scores without any in-kernel fence.
 #include "dev_common.h"
+#include "ssp64.h"
 
 namespace ds4 {
 
@@ -34,7 +36,6 @@ struct RouteArgs {
   int H, E, K, T;
   float scale;
   float4* kbuf;           // [T][E] (key, key_lo, key_hi, score)
-  unsigned* counters;     // [T], zero between calls
   int32_t* ids;           // [T][K]
   float* wts;             // [T][K]
   uint32_t* status;
@@ -54,13 +55,6 @@ __device__ inline double load_w64(const RouteArgs& a, int e, int c) {
   return f16_bits_to_f64(((const uint16_t*)a.W)[(size_t)e * a.H + c]);
 }
 
-// sqrt(ln(1+e^z)) in binary64, written as sqrt(max(z,0) + ln(1+e^-|z|)).
-__device__ inline double sqrtsoftplus64(float zf) {
-  double z = (double)zf;
-  double az = fabs(z);
-  return sqrt(fmax(z, 0.0) + log1p(exp(-az)));
-}
-
 // Block-wide fixed-order sum of two doubles over 256 threads (4 waves).
 __device__ inline void block_sum2(double& a, double& b, double* sh) {
   a = wave_sum_f64(a);
@@ -76,19 +70,67 @@ __device__ inline void block_sum2(double& a, double& b, double* sh) {
   __syncthreads();
 }
 
-__device__ inline bool key_before(float ka, int ea, float kb, int eb) {
-  return ka > kb || (ka == kb && ea < eb);
+// Order-preserving map of a binary32 key to uint32, combined with the expert
+// index so that a larger composite means "earlier in the selection order":
+// higher key first, then lower index.
+__device__ inline uint64_t sel_composite(float key, int e) {
+  uint32_t u = __float_as_uint(key);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(0xFFFF - e);
 }
 
-// Grid (E, T), 256 threads: block (e, t) scores expert e for token t; the
-// last block to finish for token t selects that token's experts.
-__global__ __launch_bounds__(256) void k_route(RouteArgs a) {
-  __shared__ double sh[8];
-  __shared__ int last;
-  const int e = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+  int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ inline uint64_t readlane_u64(uint64_t v, int lane) {
+  uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+  v = umax64(v, dpp_u64<0xB1>(v));
+  v = umax64(v, dpp_u64<0x4E>(v));
+  v = umax64(v, dpp_u64<0x141>(v));
+  v = umax64(v, dpp_u64<0x140>(v));
+  return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+__device__ inline float pick4(const float* a, int j) {
+  return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
+}
+__device__ inline float readlane_f32(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
 
+constexpr int kMaxRouteK = 16;
+
+// Scoring.  Grid (E, T), 256 threads: block (e, t) computes the logit, score
+// and key interval of expert e for token t.  VEC (hidden % 2048 == 0, fp16
+// router, bf16 or normalised input): thread t owns columns 8t..8t+7 of every
+// 2048-column slab and reads them with 16-byte loads; otherwise thread t owns
+// columns t, t+256, ...  Either way each thread sums its products in column
+// order before the fixed reduction tree (depth hidden/256 + 8).  The kernel is
+// specialised so that the batch-1 variant carries no unused code: its blocks
+// run through their code once, and instruction fetch is on the critical path.
+template <bool NORM, bool VEC>
+__global__ __launch_bounds__(256) void k_route_score(RouteArgs a) {
+  __shared__ double sh[8];
+  const int e = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  constexpr int kMaxSlab = 2;  // VEC: hidden <= 4096
+
+  uint4 wv[kMaxSlab];
+  if (VEC) {  // router-weight loads first: their latency overlaps the input
+    const uint4* wp = (const uint4*)((const uint16_t*)a.W + (size_t)e * a.H);
+#pragma unroll
+    for (int j = 0; j < kMaxSlab; j++)
+      if (j < a.H / 2048) wv[j] = wp[256 * j + tid];
+  }
   double nscale = 1.0;
-  if (a.norm_w) {  // RMSNorm scale, recomputed identically by every block
+  if (NORM) {  // RMSNorm scale, recomputed identically by every block
     double ss = 0.0, dummy = 0.0;
     for (int c = tid; c < a.H; c += 256) {
       double v = (double)a.residual[(size_t)t * a.H + c];
@@ -102,113 +144,124 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
             (double)a.residual[(size_t)t * a.H + c] * nscale * (double)a.norm_w[c]);
   }
 
-  // Logit: products are exact in binary64; each thread sums its columns in
-  // order, then a 6-level wave tree and a 2-level cross-wave tree.
   double acc = 0.0, aabs = 0.0;
-  for (int c = tid; c < a.H; c += 256) {
-    double p = load_x64(a, t, c, nscale) * load_w64(a, e, c);
-    acc += p;
-    aabs += fabs(p);
+  if (VEC) {
+#pragma unroll
+    for (int j = 0; j < kMaxSlab; j++) {
+      if (j >= a.H / 2048) break;
+      uint32_t xx[4];
+      float rr[8], nw[8];
+      if (!NORM) {
+        const uint4 xv = ((const uint4*)((const uint16_t*)a.x + (size_t)t * a.H))[256 * j + tid];
+        xx[0] = xv.x; xx[1] = xv.y; xx[2] = xv.z; xx[3] = xv.w;
+      } else {
+        const float4* rp = (const float4*)(a.residual + (size_t)t * a.H) + 512 * j + 2 * tid;
+        const float4* np = (const float4*)a.norm_w + 512 * j + 2 * tid;
+        float4 r0 = rp[0], r1 = rp[1], n0 = np[0], n1 = np[1];
+        rr[0] = r0.x; rr[1] = r0.y; rr[2] = r0.z; rr[3] = r0.w;
+        rr[4] = r1.x; rr[5] = r1.y; rr[6] = r1.z; rr[7] = r1.w;
+        nw[0] = n0.x; nw[1] = n0.y; nw[2] = n0.z; nw[3] = n0.w;
+        nw[4] = n1.x; nw[5] = n1.y; nw[6] = n1.z; nw[7] = n1.w;
+      }
+      const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const uint32_t sh16 = 16 * (u & 1);
+        double xd;
+        if (NORM)
+          xd = bf16_bits_to_f64(f64_to_bf16_bits((double)rr[u] * nscale * (double)nw[u]));
+        else
+          xd = bf16_bits_to_f64((xx[u >> 1] >> sh16) & 0xFFFFu);
+        double p = xd * f16_bits_to_f64((ww[u >> 1] >> sh16) & 0xFFFFu);
+        acc += p;
+        aabs += fabs(p);
+      }
+    }
+  } else {
+    for (int c = tid; c < a.H; c += 256) {
+      double p = load_x64(a, t, c, nscale) * load_w64(a, e, c);
+      acc += p;
+      aabs += fabs(p);
+    }
   }
   block_sum2(acc, aabs, sh);
 
   if (tid == 0) {
     const int depth = (a.H + 255) / 256 + 8;
-    const double u = 0x1p-53;
-    double bound = (double)(depth + 2) * u * aabs * 1.0009765625;
+    double bound = (double)(depth + 2) * 0x1p-53 * aabs * 1.0009765625;
     // widen by the rounding of acc +- bound itself and an absolute floor
     double b2 = bound + 0x1p-52 * (fabs(acc) + bound) + 0x1p-1070;
     float zm = (float)acc, zl = (float)(acc - b2), zh = (float)(acc + b2);
-    double s64 = sqrtsoftplus64(zm);
+    double s64 = ssp64(zm);
+    double sl64 = s64, sh64 = s64;
+    if (zl != zm || zh != zm) {  // rare: the logit itself is not certified
+      sl64 = ssp64(zl);
+      sh64 = ssp64(zh);
+    }
+    const double rel = 0x1p-40;  // far above the error of ssp64
     float sp = (float)s64;
-    const double rel = 0x1p-44;
-    double sl64 = (zl == zm) ? s64 : sqrtsoftplus64(zl);
-    double sh64 = (zh == zm) ? s64 : sqrtsoftplus64(zh);
     float slo = (float)(sl64 * (1.0 - rel)), shi = (float)(sh64 * (1.0 + rel));
     float b = a.bias[e];
     float key = sp + b, klo = slo + b, khi = shi + b;
     if (key != key) key = klo = khi = -__builtin_huge_valf();  // NaN never wins
     a.kbuf[(size_t)t * a.E + e] = make_float4(key, klo, khi, sp);
   }
+}
 
-  // last-block-done: publish, count, and let the final block select
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last = (atomicAdd(&a.counters[t], 1u) == (unsigned)(a.E - 1));
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  if (tid >= 64) return;
-
-  const int lane = tid;
-  float kp[4], kl[4], kh[4];
-  bool valid[4], sel[4];
+// Selection.  Grid T, one wave per token: reads the E key intervals written
+// by k_route_score (visible at the kernel boundary), picks the top K and
+// writes ids and gates.
+__global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  uint64_t comp[4];
+  float sc[4], kl[4], kh[4];
+  bool wide = false;
   for (int j = 0; j < 4; j++) {
     int ee = lane + 64 * j;
-    valid[j] = ee < a.E;
-    sel[j] = false;
-    float4 v = valid[j] ? a.kbuf[(size_t)t * a.E + ee] : make_float4(0, 0, 0, 0);
-    kp[j] = v.x;
+    float4 v = ee < a.E ? a.kbuf[(size_t)t * a.E + ee] : make_float4(0, 0, 0, 0);
+    comp[j] = ee < a.E ? sel_composite(v.x, ee) : 0ull;
     kl[j] = v.y;
     kh[j] = v.z;
+    sc[j] = v.w;
+    wide |= ee < a.E && (v.y != v.z);
   }
-  const float NEG = -__builtin_huge_valf();
-  int chosen[8];
-  int prev = -1;
-  bool ok = true;
-  // any key with a non-degenerate interval?
-  bool wide = false;
-  for (int j = 0; j < 4; j++) wide |= valid[j] && (kl[j] != kh[j]);
   wide = __any(wide);
+  int sel_e[kMaxRouteK];
+  float sel_s[kMaxRouteK];
+  bool ok = true;
+  float prev_lo = 0.0f;
+  int prev_e = -1;
   for (int k = 0; k < a.K; k++) {
-    float bk = NEG;
-    int be = 1 << 30;
-    for (int j = 0; j < 4; j++) {
-      int ee = lane + 64 * j;
-      if (valid[j] && !sel[j] && key_before(kp[j], ee, bk, be)) {
-        bk = kp[j];
-        be = ee;
-      }
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      float ok2 = __shfl_xor(bk, off);
-      int oe = __shfl_xor(be, off);
-      if (key_before(ok2, oe, bk, be)) {
-        bk = ok2;
-        be = oe;
-      }
-    }
+    uint64_t best = umax64(umax64(comp[0], comp[1]), umax64(comp[2], comp[3]));
+    best = wave_max_u64(best);
+    const int be = 0xFFFF - (int)(uint32_t)(best & 0xFFFFu);
+    const int owner = be & 63, slot = be >> 6;
     for (int j = 0; j < 4; j++)
-      if (lane + 64 * j == be) sel[j] = true;
-    if (lane == 0) a.ids[(size_t)t * a.K + k] = be;
-    if (k < 8) chosen[k] = be;
-    // certification of the order between consecutive selected experts
-    if (wide && prev >= 0) {
-      float4 pa = a.kbuf[(size_t)t * a.E + prev];
-      float4 pb = a.kbuf[(size_t)t * a.E + be];
-      if (!(pa.y > pb.z || (pa.y == pb.z && prev < be))) ok = false;
+      if (lane + 64 * j == be) comp[j] = 0ull;
+    sel_e[k] = be;
+    sel_s[k] = readlane_f32(pick4(sc, slot), owner);
+    if (wide) {
+      float lo = readlane_f32(pick4(kl, slot), owner), hi = readlane_f32(pick4(kh, slot), owner);
+      if (prev_e >= 0 && !(prev_lo > hi || (prev_lo == hi && prev_e < be))) ok = false;
+      prev_lo = lo;
+      prev_e = be;
     }
-    prev = be;
   }
   if (wide) {
     // the last selected expert must precede every unselected one
-    float4 pl = a.kbuf[(size_t)t * a.E + prev];
     for (int j = 0; j < 4; j++) {
       int ee = lane + 64 * j;
-      if (valid[j] && !sel[j] && !(pl.y > kh[j] || (pl.y == kh[j] && prev < ee))) ok = false;
+      if (comp[j] != 0ull && !(prev_lo > kh[j] || (prev_lo == kh[j] && prev_e < ee))) ok = false;
     }
     if (__any(!ok) && lane == 0) raise_fault(a.status, DS4MOE_FAULT_UNCERTIFIED);
   }
-  if (lane == 0) {
-    double ssum = 0.0;
-    for (int k = 0; k < a.K; k++) ssum += (double)a.kbuf[(size_t)t * a.E + a.ids[(size_t)t * a.K + k]].w;
-    for (int k = 0; k < a.K; k++) {
-      double s = (double)a.kbuf[(size_t)t * a.E + a.ids[(size_t)t * a.K + k]].w;
-      a.wts[(size_t)t * a.K + k] = (float)((double)a.scale * s / ssum);
+  double ssum = 0.0;
+  for (int k = 0; k < a.K; k++) ssum += (double)sel_s[k];
+  for (int k = 0; k < a.K; k++)
+    if (lane == k) {
+      a.ids[(size_t)t * a.K + k] = sel_e[k];
+      a.wts[(size_t)t * a.K + k] = (float)((double)a.scale * (double)sel_s[k] / ssum);
     }
-    a.counters[t] = 0u;
-  }
-  (void)chosen;
 }
 
 // Hash routing: one thread per token.  Invalid token ids or table rows

@@ -66,7 +66,7 @@ typedef enum { DS4MOE_Q2_K = 0, DS4MOE_IQ2_XXS = 1, DS4MOE_Q8_0 = 2 } ds4moe_qty
 
 /* Layer shape.  hidden must be a multiple of 256 and inter of 32 (blocks
  * tile the row-major flattening of each matrix, so a block may span rows);
- * top_k <= n_expert <= 256, top_k <= 64. */
+ * top_k <= n_expert <= 256, top_k <= 64 (learned routers: top_k <= 16). */
 typedef struct {
   int32_t hidden;       /* H (4096)                                    */
   int32_t inter;        /* routed expert intermediate size I (2048)    */
@@ -180,6 +180,24 @@ ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_layer_desc* d
 #define DS4MOE_FAULT_BAD_TABLE 0x4u    /* tid2eid row out of range / repeated   */
 #define DS4MOE_FAULT_UNCERTIFIED 0x8u  /* routing not certifiable (see route)   */
 #define DS4MOE_FAULT_F16_RANGE 0x10u   /* an intermediate exceeded binary16     */
+
+/* Kernel classes for ds4moe_profile_events(). */
+#define DS4MOE_K_ROUTE 0     /* router scoring + selection, or hash lookup  */
+#define DS4MOE_K_GATEUP 1    /* gate/up matvec + SwiGLU (any path)          */
+#define DS4MOE_K_DOWN 2      /* down matvec + combine (any path)            */
+#define DS4MOE_K_PERMUTE 3   /* token -> expert permutation                 */
+#define DS4MOE_K_OTHER 4     /* RMSNorm, combine, quantisation helpers      */
+#define DS4MOE_K_CLASSES 5
+
+/*
+ * Profiling hook (measurement only, not part of the method).  After this
+ * call every launch of kernel class `cls` is bracketed by
+ * hipEventRecord(begin) and hipEventRecord(end) on the stream it is launched
+ * on; pass NULL events to stop.  The events are caller-owned HIP events.
+ * Process-wide setting, not thread-safe: set it between calls from one host
+ * thread.  Returns DS4MOE_EINVAL for an unknown class.
+ */
+ds4moe_status ds4moe_profile_events(int32_t cls, hipEvent_t begin, hipEvent_t end);
 
 /*
  * Waits for `stream`, reads and clears the workspace status word.  Returns

@@ -242,3 +242,41 @@ def test_layer_route_and_ffn(widx):
     err = max_rel_err(out.cpu().numpy(), want)
     say("  max|err|/rms =", err)
     assert err <= TOL_FP32
+
+
+def test_layer_graph_replays_match_eager():
+    """Captured layer calls replayed several times, with eager work and
+    synchronisations in between, must reproduce the eager results bit for bit."""
+    from ds4gen.device import make_layer
+    w = g.WORKLOADS[1]
+    say("graph replay")
+    lt = make_layer(w, 0)
+    T = 6
+    x = dev(g.activations(w, n_tok=T))
+    shp = shape_of(w)
+    ws, nb = workspace(shp, 1)
+    d = ds4.layer_desc(ds4.router(w=ptr(lt.router_w), w_dtype=ds4.F16, bias=ptr(lt.bias)),
+                       experts_of(lt, w))
+    ref = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    out = torch.zeros((T, w.H), dtype=torch.float32, device="cuda")
+    row = w.H * 2
+
+    def run(dst, st):
+        for i in range(T):
+            ds4.layer(shp, d, x.data_ptr() + i * row, ds4.BF16, None, dst.data_ptr() + i * w.H * 4,
+                      None, 1, None, None, None, ptr(ws), nb, st)
+
+    run(ref, stream())
+    check_clean(ws)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        run(out, torch.cuda.current_stream().cuda_stream)
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), "replay %d differs" % rep
+        run(ref, stream())  # eager work between replays
+        torch.cuda.synchronize()
+    check_clean(ws)
