@@ -39,7 +39,7 @@ Layout layout_for(const ds4moe_shape& s, int32_t T) {
   L.wts = take(t * K * 4);
   L.xn = take(t * H * 2);
   L.hs = take(K * 64 * kHqDwords * 4);
-  L.perm = take((E + (E + 1) + 2 * t * K + 64) * 4);
+  L.perm = take((E + (E + 1) + 2 * t * K + 3 * (size_t)max_items((int)E, (int)(t * K), (int)t, true) + 64) * 4);
   L.h = take(np * I * 4);
   L.y = take(np * H * 4);
   L.hb = take(np * I * 2);
@@ -189,9 +189,77 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     return launched();
   }
   if (T > 1 && grouped_eligible(s, ex, sh, x, x_dt, T)) {
-    return run_grouped(s, ex, sh, (const uint16_t*)x, T, ids, wts, out, residual, perm_dbg,
-                       at<int32_t>(ws, L.perm), at<uint16_t>(ws, L.hb), at<float>(ws, L.y),
-                       status, st);
+    const int E = s.n_expert, K = s.top_k, TK = T * K;
+    int32_t* counts = at<int32_t>(ws, L.perm);
+    int32_t* offsets = counts + E;
+    int32_t* perm = offsets + E + 1;
+    int32_t* inv = perm + TK;
+    int32_t* items = inv + TK;
+    const int mi = max_items(E, TK, T, sh != nullptr);
+    int32_t* n_items = items + 3 * mi;
+    ds4moe_status rc;
+    {
+      ProfScope prof(DS4MOE_K_PERMUTE, st);
+      rc = launch_permute(ids, TK, E, counts, offsets, perm, inv, status, st);
+      if (rc != DS4MOE_OK) return rc;
+      hipLaunchKernelGGL(k_make_items, dim3(1), dim3(64), 0, st, counts, offsets, E, TK, T,
+                         sh ? 1 : 0, items, n_items);
+    }
+    if ((rc = launched()) != DS4MOE_OK) return rc;
+    GroupArgs g{};
+    g.H = s.hidden;
+    g.I = ex.inter;
+    g.E = E;
+    g.K = K;
+    g.T = T;
+    g.x = (const uint16_t*)x;
+    g.perm = perm;
+    g.items = items;
+    g.n_items = n_items;
+    g.gate = (const uint8_t*)ex.gate;
+    g.up = (const uint8_t*)ex.up;
+    g.down = (const uint8_t*)ex.down;
+    g.qt_g = ex.gate_qtype;
+    g.qt_u = ex.up_qtype;
+    g.qt_d = ex.down_qtype;
+    if (sh) {
+      g.sh_gate = (const uint8_t*)sh->gate;
+      g.sh_up = (const uint8_t*)sh->up;
+      g.sh_down = (const uint8_t*)sh->down;
+      g.sh_qt_g = sh->gate_qtype;
+      g.sh_qt_u = sh->up_qtype;
+      g.sh_qt_d = sh->down_qtype;
+      g.sh_I = sh->inter;
+    }
+    g.grid = ex.grid ? ex.grid : (sh ? sh->grid : nullptr);
+    g.h = at<float>(ws, L.h);
+    g.y = at<float>(ws, L.y);
+    g.status = status;
+    const int imax = g.I > g.sh_I ? g.I : g.sh_I;
+    {
+      ProfScope prof(DS4MOE_K_GATEUP, st);
+      hipLaunchKernelGGL(k_grouped_gateup, dim3((imax + kNT - 1) / kNT, mi), dim3(256), 0, st, g);
+    }
+    if ((rc = launched()) != DS4MOE_OK) return rc;
+    {
+      ProfScope prof(DS4MOE_K_DOWN, st);
+      hipLaunchKernelGGL(k_grouped_down, dim3(s.hidden / kNT, mi), dim3(256), 0, st, g);
+    }
+    if ((rc = launched()) != DS4MOE_OK) return rc;
+    {
+      ProfScope prof(DS4MOE_K_OTHER, st);
+      const size_t n = (size_t)T * s.hidden;
+      hipLaunchKernelGGL(k_grouped_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                         (const float*)g.y, (const int32_t*)inv, wts, T, K, s.hidden, sh ? 1 : 0, out,
+                         residual);
+    }
+    if ((rc = launched()) != DS4MOE_OK) return rc;
+    if (perm_dbg) {
+      if (hipMemcpyAsync(perm_dbg, offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToDevice, st) != hipSuccess ||
+          hipMemcpyAsync(perm_dbg + E + 1, perm, sizeof(int32_t) * 2 * TK, hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return DS4MOE_EDEVICE;
+    }
+    return DS4MOE_OK;
   }
   GenericArgs a{};
   a.x = x;

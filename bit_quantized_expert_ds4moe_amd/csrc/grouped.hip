@@ -1,12 +1,401 @@
-// grouped.hip -- token->expert permutation launch and the batched
-// (several tokens per expert) expert FFN path (gfx950).
+// grouped.hip -- several tokens per expert: token->expert permutation and the
+// grouped MFMA expert FFN (batched decode and prefill), gfx950.
+//
+// Method: FLOW = qiita.com/sukimaengineer/items/cd76fec76d49a098abed, sections
+// "MoE FFN 部の中身" (E(x) = W_down(SiLU(W_gate x) * W_up x), weighted sum,
+// always-on shared expert) and "プリフィルとデコードで何が違うか" (with many
+// tokens the union of selected experts approaches all of them, so the work is
+// a grouped matrix product per expert).  Formats: DS4C2 =
+// qiita.com/yoshiyakato/items/4678be0e7860ddb444ec, sections 3 and 4; FLOW
+// quantisation table (Q8_0).
+//
+// Rows: the (token, slot) pairs sorted by expert occupy rows [0, T*K) (row i
+// is pair perm[i]); the shared expert's rows are [T*K, T*K + T) (token order).
+// Work items (expert, first row, row count <= 64) are listed by the
+// permutation kernel; a grouped kernel block takes one item and 64 output
+// features.
+//
+// Exactness: MFMA operands are exact.  gate/up (bf16 MFMA 16x16x32): A = x
+// (bf16 as given), B = IQ2_XXS grid value * sign (|v| < 128, exact in bf16) or
+// the Q8_0 code; each 32-column group's scale multiplies that group's MFMA
+// result (one FMA per output element per group).  down (f16 MFMA 16x16x16,
+// one 16-value Q2_K sub-block per step): A = the SwiGLU output split as
+// f16 hi + lo (relative error < 2^-21), B = the 2-bit code masked in place in
+// a 16-bit lane, i.e. the binary16 subnormal 4^s q 2^-24; the sub-block factor
+// d*sc*4^-s*2^24 multiplies each step's result; the mins enter through a
+// second MFMA on per-sub-block sums of h against the min nibbles.  Sums are
+// fp32 throughout.
 #include "dev_common.h"
 
 namespace ds4 {
 
+constexpr int kMC = 64;   // rows (pairs) per work item
+constexpr int kNT = 64;   // output features per block (16 per wave)
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(1024) void k_permute(const int32_t* ids, int n, int E, int32_t* counts,
                                                   int32_t* offsets, int32_t* perm, int32_t* inv,
                                                   uint32_t* status);
+
+// Work list: items (e, row0, nrows) for every expert with pairs, then the
+// shared expert's rows (e == E).  One thread, after the permutation.
+__global__ void k_make_items(const int32_t* counts, const int32_t* offsets, int E, int TK, int T,
+                             int with_shared, int32_t* items, int32_t* n_items) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int n = 0;
+  for (int e = 0; e < E; e++)
+    for (int m0 = 0; m0 < counts[e]; m0 += kMC) {
+      items[3 * n] = e;
+      items[3 * n + 1] = offsets[e] + m0;
+      items[3 * n + 2] = min(kMC, counts[e] - m0);
+      n++;
+    }
+  if (with_shared)
+    for (int m0 = 0; m0 < T; m0 += kMC) {
+      items[3 * n] = E;
+      items[3 * n + 1] = TK + m0;
+      items[3 * n + 2] = min(kMC, T - m0);
+      n++;
+    }
+  *n_items = n;
+}
+
+inline int max_items(int E, int TK, int T, bool shared) {
+  return E + (TK + kMC - 1) / kMC + (shared ? (T + kMC - 1) / kMC : 0);
+}
+
+struct GroupArgs {
+  int H, I, E, K, T;
+  const uint16_t* x;        // [T][H] bf16
+  const int32_t* perm;      // [T*K]
+  const int32_t* items;     // [n][3]
+  const int32_t* n_items;
+  const uint8_t *gate, *up, *down;
+  int qt_g, qt_u, qt_d;
+  const uint8_t *sh_gate, *sh_up, *sh_down;
+  int sh_qt_g, sh_qt_u, sh_qt_d, sh_I;
+  const uint8_t* grid;
+  float* h;                 // [T*K + T][I] fp32
+  float* y;                 // [T*K + T][H] fp32
+  uint32_t* status;
+};
+
+__device__ inline int row_token(const GroupArgs& a, int row) {
+  return row < a.T * a.K ? a.perm[row] / a.K : row - a.T * a.K;
+}
+
+// 8 bytes at a 2-byte-aligned address (Q8_0 codes).
+__device__ inline uint2 load8_a2(const uint8_t* p) {
+  const uint16_t* q = (const uint16_t*)p;
+  return make_uint2((uint32_t)q[0] | ((uint32_t)q[1] << 16), (uint32_t)q[2] | ((uint32_t)q[3] << 16));
+}
+
+// four signed bytes -> two bf16 pairs (exact: |c| <= 127)
+__device__ inline void i8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  float f0 = (float)(int8_t)(w & 0xFF), f1 = (float)(int8_t)((w >> 8) & 0xFF);
+  float f2 = (float)(int8_t)((w >> 16) & 0xFF), f3 = (float)(int8_t)(w >> 24);
+  lo = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+  hi = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
+}
+__device__ inline void i8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = f32_to_f16_bits((float)(int8_t)(w & 0xFF)) | (f32_to_f16_bits((float)(int8_t)((w >> 8) & 0xFF)) << 16);
+  hi = f32_to_f16_bits((float)(int8_t)((w >> 16) & 0xFF)) | (f32_to_f16_bits((float)(int8_t)(w >> 24)) << 16);
+}
+
+// IQ2_XXS grid / sign tables replicated 8x (see ffn_b1.hip), built by 256 threads.
+__device__ inline void build_tables8_256(const uint8_t* grid, uint4* gt8, uint4* mt8) {
+  const int t = threadIdx.x;
+  {
+    const uint8_t* g = grid + 8 * t;
+    uint32_t w[4];
+    for (int m = 0; m < 4; m++) {
+      uint32_t lo = __float_as_uint((float)g[2 * m]) >> 16;
+      uint32_t hi = __float_as_uint((float)g[2 * m + 1]) >> 16;
+      w[m] = lo | (hi << 16);
+    }
+    const uint4 v = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int q = 0; q < 8; q++) gt8[8 * t + q] = v;
+  }
+  if (t < 128) {
+    uint32_t s8 = (uint32_t)t | ((uint32_t)(__popc(t) & 1) << 7);
+    uint32_t w[4];
+    for (int m = 0; m < 4; m++)
+      w[m] = (((s8 >> (2 * m)) & 1u) << 15) | (((s8 >> (2 * m + 1)) & 1u) << 31);
+    const uint4 v = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int q = 0; q < 8; q++) mt8[8 * t + q] = v;
+  }
+}
+
+// B fragment (8 values) of a gate/up row for one 32-column group, plus the
+// group scale.  IQ2_XXS: lane sub-vector q of group g of the 256-block at blk.
+__device__ inline void iq2_bfrag(const uint8_t* blk, int g, int q, int rep, const uint4* gt8,
+                                 const uint4* mt8, bf16x8_t& b, float& scale) {
+  const uint8_t* gp = blk + 2 + 8 * g;
+  uint32_t idx = gp[q];
+  const uint16_t* sp = (const uint16_t*)(gp + 4);
+  uint32_t sw = (uint32_t)sp[0] | ((uint32_t)sp[1] << 16);
+  float d = f16_bits_to_f32((uint32_t)((const uint16_t*)blk)[0]);
+  scale = d * (float)(2u * (sw >> 28) + 1u) * 0.125f;
+  uint4 gv = gt8[8 * idx + rep];
+  uint4 mv = mt8[8 * ((sw >> (7 * q)) & 0x7Fu) + rep];
+  uint4 v = make_uint4(gv.x ^ mv.x, gv.y ^ mv.y, gv.z ^ mv.z, gv.w ^ mv.w);
+  b = __builtin_bit_cast(bf16x8_t, v);
+}
+// Q8_0: 32-value block g (of the 256-column chunk at chunk), lane's 8 codes.
+__device__ inline void q80_bfrag(const uint8_t* chunk, int g, int q, bf16x8_t& b, float& scale) {
+  const uint8_t* bp = chunk + g * kQ80Bytes;
+  scale = f16_bits_to_f32((uint32_t)((const uint16_t*)bp)[0]);
+  uint2 c = load8_a2(bp + 2 + 8 * q);
+  uint4 v;
+  i8x4_to_bf16x4(c.x, v.x, v.y);
+  i8x4_to_bf16x4(c.y, v.z, v.w);
+  b = __builtin_bit_cast(bf16x8_t, v);
+}
+
+// gate/up + SwiGLU for one work item and 64 intermediate features.
+// Grid (ceil(Imax/64), max_items), 256 threads; wave w owns features
+// n0 + 16w .. +15 (gate and up).  x tile staged in LDS per 128 columns with
+// 16-byte chunk c of row m at slot c ^ (m & 7) (conflict-free A reads).
+__global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
+  __shared__ uint4 xt[kMC * 16];
+  __shared__ uint4 gt8[256 * 8];
+  __shared__ uint4 mt8[128 * 8];
+  __shared__ int tok[kMC];
+  const int item = blockIdx.y;
+  if (item >= *a.n_items) return;
+  const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
+  const bool sh = e == a.E;
+  const int I = sh ? a.sh_I : a.I;
+  const int n0 = blockIdx.x * kNT;
+  if (n0 >= I) return;
+  const int qg = sh ? a.sh_qt_g : a.qt_g, qu = sh ? a.sh_qt_u : a.qt_u;
+  const uint8_t* G = sh ? a.sh_gate : a.gate;
+  const uint8_t* U = sh ? a.sh_up : a.up;
+  const int ee = sh ? 0 : e;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = lane >> 4, rep = lane & 7;
+  const int n = n0 + 16 * w + (lane & 15);
+  const int nb = a.H / 256;  // 256-column chunks per row
+  if (tid < kMC) tok[tid] = tid < nrows ? row_token(a, row0 + tid) : -1;
+  if (qg == DS4MOE_IQ2_XXS || qu == DS4MOE_IQ2_XXS) build_tables8_256(a.grid, gt8, mt8);
+  const size_t rowg = (size_t)ee * I + n;
+  const int bbg = block_bytes(qg) * (256 / block_values(qg));  // bytes per 256 columns
+  const int bbu = block_bytes(qu) * (256 / block_values(qu));
+  const int mtiles = (nrows + 15) >> 4;
+  f32x4_t accg[4], accu[4];
+  for (int mt = 0; mt < 4; mt++) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  for (int kh = 0; kh < 2 * nb; kh++) {
+    const int kb = kh >> 1, goff = 4 * (kh & 1);
+    for (int c = tid; c < kMC * 16; c += 256) {
+      const int m = c >> 4, ch = c & 15;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (m < nrows) v = ((const uint4*)(a.x + (size_t)tok[m] * a.H + 128 * kh))[ch];
+      xt[m * 16 + (ch ^ (m & 7))] = v;
+    }
+    __syncthreads();
+    const uint8_t* bg = G + (rowg * nb + kb) * bbg;
+    const uint8_t* bu = U + (rowg * nb + kb) * bbu;
+#pragma unroll 1
+    for (int gi = 0; gi < 4; gi++) {
+      const int g = goff + gi;
+      bf16x8_t fg, fu;
+      float sg, su;
+      if (qg == DS4MOE_IQ2_XXS) iq2_bfrag(bg, g, q, rep, gt8, mt8, fg, sg);
+      else q80_bfrag(bg, g, q, fg, sg);
+      if (qu == DS4MOE_IQ2_XXS) iq2_bfrag(bu, g, q, rep, gt8, mt8, fu, su);
+      else q80_bfrag(bu, g, q, fu, su);
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        if (mt >= mtiles) break;
+        const int m = 16 * mt + (lane & 15);
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, xt[m * 16 + ((4 * gi + q) ^ (m & 7))]);
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fg, z, 0, 0, 0);
+        f32x4_t tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fu, z, 0, 0, 0);
+        accg[mt] += sg * tg;
+        accu[mt] += su * tu;
+      }
+    }
+    __syncthreads();
+  }
+  const int hstride = a.I;
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      if (mt >= mtiles) break;
+      const int m = 16 * mt + 4 * q + r;
+      if (m < nrows) a.h[(size_t)(row0 + m) * hstride + n] = silu(accg[mt][r]) * accu[mt][r];
+    }
+}
+
+// down for one work item and 64 output features.  Grid (H/64, max_items).
+// A (the SwiGLU rows) is staged per 256 columns as f16 hi/lo tiles with the
+// same swizzle as above, plus per-16-column sums (hi/lo) for the min term.
+__global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
+  __shared__ uint4 ah[kMC * 32];
+  __shared__ uint4 al[kMC * 32];
+  __shared__ uint2 sh_hi[kMC * 4];  // [m][4 x (4 f16)] sub-block sums, hi part
+  __shared__ uint2 sh_lo[kMC * 4];
+  const int item = blockIdx.y;
+  if (item >= *a.n_items) return;
+  const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
+  const bool shr = e == a.E;
+  const int I = shr ? a.sh_I : a.I;
+  const int qd = shr ? a.sh_qt_d : a.qt_d;
+  const uint8_t* D = shr ? a.sh_down : a.down;
+  const int ee = shr ? 0 : e;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = lane >> 4;
+  const int n = blockIdx.x * kNT + 16 * w + (lane & 15);
+  const int nb = I / 256;
+  const int bbd = block_bytes(qd) * (256 / block_values(qd));
+  const int mtiles = (nrows + 15) >> 4;
+  f32x4_t acc[4];
+  for (int mt = 0; mt < 4; mt++) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const size_t rowd = (size_t)ee * a.H + n;
+  bool range_ok = true;
+  for (int kb = 0; kb < nb; kb++) {
+    // stage: thread -> (row m, 16-column sub-block j): 16 values
+    for (int c = tid; c < kMC * 16; c += 256) {
+      const int m = c >> 4, j = c & 15;
+      float v[16];
+      if (m < nrows) {
+        const float4* hp = (const float4*)(a.h + (size_t)(row0 + m) * a.I + 256 * kb + 16 * j);
+        for (int u = 0; u < 4; u++) {
+          float4 f = hp[u];
+          v[4 * u] = f.x; v[4 * u + 1] = f.y; v[4 * u + 2] = f.z; v[4 * u + 3] = f.w;
+        }
+      } else {
+        for (int u = 0; u < 16; u++) v[u] = 0.f;
+      }
+      uint32_t hi[8], lo[8];
+      float s_sum = 0.f;
+      for (int u = 0; u < 8; u++) {
+        float x0 = v[2 * u], x1 = v[2 * u + 1];
+        range_ok &= fabsf(x0) <= 65504.f && fabsf(x1) <= 65504.f;
+        uint32_t h0 = f32_to_f16_bits(x0), h1 = f32_to_f16_bits(x1);
+        float r0 = x0 - f16_bits_to_f32(h0), r1 = x1 - f16_bits_to_f32(h1);
+        hi[u] = h0 | (h1 << 16);
+        lo[u] = f32_to_f16_bits(r0) | (f32_to_f16_bits(r1) << 16);
+        s_sum += x0 + x1;
+      }
+      // two 16-byte chunks (8 values each) per sub-block
+      const int c0 = 2 * j, c1 = 2 * j + 1;
+      ah[m * 32 + (c0 ^ (m & 7))] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      ah[m * 32 + (c1 ^ (m & 7))] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+      al[m * 32 + (c0 ^ (m & 7))] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      al[m * 32 + (c1 ^ (m & 7))] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+      // sub-block sum split hi/lo, stored at [m][j/4] half-lane (j%4)
+      uint32_t sh16 = f32_to_f16_bits(s_sum);
+      uint32_t sl16 = f32_to_f16_bits(s_sum - f16_bits_to_f32(sh16));
+      ((uint16_t*)sh_hi)[m * 16 + j] = (uint16_t)sh16;
+      ((uint16_t*)sh_lo)[m * 16 + j] = (uint16_t)sl16;
+    }
+    __syncthreads();
+    const uint8_t* blk = D + (rowd * nb + kb) * bbd;
+    if (qd == DS4MOE_Q2_K) {
+      // lane: output row n, k = 4q + j inside each 16-value sub-block
+      uint32_t qs4[4];  // qs dwords at 32hh + 16p + 4q, index 2hh + p
+      for (int hh = 0; hh < 2; hh++)
+        for (int p = 0; p < 2; p++) qs4[2 * hh + p] = *(const uint32_t*)(blk + 16 + 32 * hh + 16 * p + 4 * q);
+      const uint4 scv = *(const uint4*)blk;
+      const uint32_t scw[4] = {scv.x, scv.y, scv.z, scv.w};
+      const uint32_t dd = *(const uint32_t*)(blk + 80);
+      const float d = f16_bits_to_f32(dd & 0xFFFFu), dmin = f16_bits_to_f32(dd >> 16);
+      uint32_t pk[8];  // 16-bit lanes holding whole code bytes: (j0,j1), (j2,j3)
+      for (int i = 0; i < 4; i++) {
+        pk[2 * i] = vperm(0u, qs4[i], 0x0C010C00u);
+        pk[2 * i + 1] = vperm(0u, qs4[i], 0x0C030C02u);
+      }
+#pragma unroll 1
+      for (int sb = 0; sb < 16; sb++) {
+        const int hh = sb >> 3, s = (sb >> 1) & 3, p = sb & 1;
+        const uint32_t mk = 0x00030003u << (2 * s);
+        const int ix = 2 * (2 * hh + p);
+        const uint32_t b0 = pk[ix] & mk, b1 = pk[ix + 1] & mk;
+        const f16x4_t bf = __builtin_bit_cast(f16x4_t, make_uint2(b0, b1));
+        const uint32_t scb = (scw[sb >> 2] >> (8 * (sb & 3))) & 0xFu;
+        const float mult = d * (float)scb * (16777216.0f / (float)(1 << (2 * s)));
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+          if (mt >= mtiles) break;
+          const int m = 16 * mt + (lane & 15);
+          // A fragment: 4 values k = 4q..4q+3 of sub-block sb = half of 16-byte chunk 2sb + q/2
+          const uint4 ch = ah[m * 32 + ((2 * sb + (q >> 1)) ^ (m & 7))];
+          const uint4 cl = al[m * 32 + ((2 * sb + (q >> 1)) ^ (m & 7))];
+          const uint2 fh = (q & 1) ? make_uint2(ch.z, ch.w) : make_uint2(ch.x, ch.y);
+          const uint2 fl = (q & 1) ? make_uint2(cl.z, cl.w) : make_uint2(cl.x, cl.y);
+          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, fh), bf, z, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, fl), bf, t, 0, 0, 0);
+          acc[mt] += mult * t;
+        }
+      }
+      // mins: sum_j m_j * hsum_j over the block's 16 sub-blocks, k = sub-block
+      const uint32_t mn = (scw[q] >> 4) & 0x0F0F0F0Fu;  // min nibbles of sub-blocks 4q..4q+3
+      const uint32_t m0 = vperm(0u, mn, 0x0C010C00u), m1 = vperm(0u, mn, 0x0C030C02u);
+      const f16x4_t bm = __builtin_bit_cast(f16x4_t, make_uint2(m0, m1));
+      const float mmult = dmin * 16777216.0f;
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        if (mt >= mtiles) break;
+        const int m = 16 * mt + (lane & 15);
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, sh_hi[m * 4 + q]), bm, z, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, sh_lo[m * 4 + q]), bm, t, 0, 0, 0);
+        acc[mt] -= mmult * t;
+      }
+    } else {
+      // Q8_0 (shared expert): 32-value blocks, f16 MFMA 16x16x32
+#pragma unroll 1
+      for (int g = 0; g < 8; g++) {
+        const uint8_t* bp = blk + g * kQ80Bytes;
+        const float dq = f16_bits_to_f32((uint32_t)((const uint16_t*)bp)[0]);
+        const uint2 c = load8_a2(bp + 2 + 8 * q);
+        uint4 v;
+        i8x4_to_f16x4(c.x, v.x, v.y);
+        i8x4_to_f16x4(c.y, v.z, v.w);
+        const f16x8_t bf = __builtin_bit_cast(f16x8_t, v);
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+          if (mt >= mtiles) break;
+          const int m = 16 * mt + (lane & 15);
+          const f16x8_t fh = __builtin_bit_cast(f16x8_t, ah[m * 32 + ((4 * g + q) ^ (m & 7))]);
+          const f16x8_t fl = __builtin_bit_cast(f16x8_t, al[m * 32 + ((4 * g + q) ^ (m & 7))]);
+          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(fh, bf, z, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(fl, bf, t, 0, 0, 0);
+          acc[mt] += dq * t;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (!range_ok) raise_fault(a.status, DS4MOE_FAULT_F16_RANGE);
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      if (mt >= mtiles) break;
+      const int m = 16 * mt + 4 * q + r;
+      if (m < nrows) a.y[(size_t)(row0 + m) * a.H + n] = acc[mt][r];
+    }
+}
+
+// out[t] = sum_k w[t][k] y[inv[t*K+k]] (+ y[T*K + t]) (+ residual), fixed order.
+__global__ void k_grouped_combine(const float* y, const int32_t* inv, const float* wts, int T, int K,
+                                  int H, int with_shared, float* out, float* residual) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)T * H) return;
+  const int t = (int)(idx / H), c = (int)(idx % H);
+  float acc = 0.0f;
+  for (int k = 0; k < K; k++) acc = fmaf(wts[t * K + k], y[(size_t)inv[t * K + k] * H + c], acc);
+  if (with_shared) acc += y[((size_t)T * K + t) * H + c];
+  if (residual) residual[idx] += acc;
+  else out[idx] = acc;
+}
 
 inline ds4moe_status launch_permute(const int32_t* ids, int n, int E, int32_t* counts,
                                     int32_t* offsets, int32_t* perm, int32_t* inv,
@@ -22,16 +411,19 @@ inline ds4moe_status launch_permute(const int32_t* ids, int n, int E, int32_t* c
   return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;
 }
 
-inline bool grouped_eligible(const ds4moe_shape&, const ds4moe_experts&, const ds4moe_experts*,
-                             const void*, int32_t, int32_t) {
-  return false;
-}
-
-inline ds4moe_status run_grouped(const ds4moe_shape&, const ds4moe_experts&, const ds4moe_experts*,
-                                 const uint16_t*, int32_t, const int32_t*, const float*, float*,
-                                 float*, int32_t*, int32_t*, uint16_t*, float*, uint32_t*,
-                                 hipStream_t) {
-  return DS4MOE_EUNSUPPORTED;
+// The grouped path needs bf16 x, 256-multiple shapes and formats it knows.
+inline bool grouped_eligible(const ds4moe_shape& s, const ds4moe_experts& ex,
+                             const ds4moe_experts* sh, const void* x, int32_t x_dt, int32_t T) {
+  auto gu_ok = [](int qt) { return qt == DS4MOE_IQ2_XXS || qt == DS4MOE_Q8_0; };
+  auto dn_ok = [](int qt) { return qt == DS4MOE_Q2_K || qt == DS4MOE_Q8_0; };
+  if (x_dt != DS4MOE_BF16 || ((uintptr_t)x % 16) != 0 || s.hidden % 256 || ex.inter % 256) return false;
+  if (!gu_ok(ex.gate_qtype) || !gu_ok(ex.up_qtype) || !dn_ok(ex.down_qtype)) return false;
+  if (((uintptr_t)ex.gate | (uintptr_t)ex.up | (uintptr_t)ex.down) % 16) return false;
+  if (sh) {
+    if (!gu_ok(sh->gate_qtype) || !gu_ok(sh->up_qtype) || !dn_ok(sh->down_qtype)) return false;
+    if (sh->inter % 256 || ((uintptr_t)sh->gate | (uintptr_t)sh->up | (uintptr_t)sh->down) % 16) return false;
+  }
+  return T > 1;
 }
 
 }  // namespace ds4

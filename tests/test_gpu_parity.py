@@ -280,3 +280,59 @@ def test_layer_graph_replays_match_eager():
         run(ref, stream())  # eager work between replays
         torch.cuda.synchronize()
     check_clean(ws)
+
+
+# --------------------------------------------------------------------------
+# grouped (several tokens per expert) path
+# --------------------------------------------------------------------------
+def grouped_case(w, ids, wts, tokens_for_oracle=None, tol=TOL_FP32):
+    from ds4gen.device import make_layer, host_experts, host_shared
+    lt = make_layer(w, 0)
+    T = ids.shape[0]
+    x = g.activations(w, n_tok=T)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, T)
+    out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    pdbg = torch.empty(w.E + 1 + 2 * T * w.K, dtype=torch.int32, device="cuda")
+    xd, idd, wd = dev(x), dev(ids), dev(wts)
+    ds4.expert_ffn(shp, experts_of(lt, w), shared_of(lt, w), ptr(xd), x_dtype(w), T, ptr(idd),
+                   ptr(wd), ptr(out), ptr(pdbg), ptr(ws), nb, stream())
+    check_clean(ws)
+    _, oo, op, oi = oracle.permute(ids, w.E)
+    pd = pdbg.cpu().numpy()
+    np.testing.assert_array_equal(pd[:w.E + 1], oo)
+    np.testing.assert_array_equal(pd[w.E + 1:w.E + 1 + T * w.K], op)
+    np.testing.assert_array_equal(pd[w.E + 1 + T * w.K:], oi)
+    toks = np.arange(T) if tokens_for_oracle is None else np.asarray(tokens_for_oracle)
+    sh = host_shared(w, 0) if w.shared else None
+    want = oracle.moe_ffn(x, "bf16", ids, wts, host_experts(w, 0, np.unique(ids[toks])),
+                          (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed),
+                          tokens=toks, shared=sh, sh_I=w.I)
+    err = max_rel_err(out.cpu().numpy()[toks], want)
+    say("  grouped T=%d max|err|/rms = %g" % (T, err))
+    assert err <= tol
+
+
+def test_grouped_ragged_items_all_outputs():
+    # 12 experts, 150 tokens x top-4: several experts get > 64 pairs (multiple
+    # work items, ragged last tile); shared Q8_0 expert; every output checked
+    w = g.Workload("grouped-small", 11, 150, 512, 256, 12, 4, g.IQ2_XXS, g.IQ2_XXS, g.Q2_K,
+                   "bf16", "f16", shared=True)
+    say("grouped ragged")
+    ids, wts = g.zipf_routing(11, w.T, w.E, w.K)
+    grouped_case(w, ids, wts)
+
+
+def test_grouped_prefill_512_zipf_sampled():
+    # the prefill workload: 512 tokens, 256 experts, Zipf(1.1) routing; outputs of
+    # tokens that hit the most and the least loaded experts are checked
+    w = g.WORKLOADS[3]
+    say("prefill 512")
+    ids, wts = g.zipf_routing(w.seed, w.T, w.E, w.K)
+    counts = np.bincount(ids.ravel(), minlength=w.E)
+    heavy = int(np.argmax(counts))
+    light = [e for e in np.argsort(counts) if counts[e] > 0][0]
+    t_heavy = int(np.where((ids == heavy).any(1))[0][0])
+    t_light = int(np.where((ids == light).any(1))[0][0])
+    grouped_case(w, ids, wts, tokens_for_oracle=[0, t_heavy, t_light, w.T - 1],
+                 tol=TOL_FP32)
