@@ -158,6 +158,174 @@ def bench_decode_b1(args):
     return res
 
 
+def stack_descs(ds4, w, layers):
+    descs = []
+    for l, lt in enumerate(layers):
+        ex = ds4.experts(lt.gate.data_ptr(), lt.up.data_ptr(), lt.down.data_ptr(), w.I,
+                         (w.gate_qt, w.up_qt, w.down_qt), grid=lt.grid.data_ptr())
+        if l < w.n_hash:
+            rt = ds4.router(tid2eid=lt.tid2eid.data_ptr(), vocab=w.vocab)
+        else:
+            rt = ds4.router(w=lt.router_w.data_ptr(), w_dtype=ds4.F16, bias=lt.bias.data_ptr())
+        descs.append(ds4.layer_desc(rt, ex, norm_w=lt.norm_w.data_ptr(), norm_eps=1e-6))
+    return descs
+
+
+def bench_stack(args):
+    """43-layer routed-expert stack at batch-1 decode: one step = one token
+    through every layer (RMSNorm -> routing -> experts -> residual add)."""
+    import numpy as np
+    import torch
+
+    import bit_quantized_expert_ds4moe_amd as ds4
+    import ds4gen as g
+    from ds4gen.device import make_stack, step_inputs, to_dev
+
+    w = g.WORKLOADS[4]
+    log("generating %d layers x %d experts on the device" % (w.n_layers, w.E))
+    t0 = time.perf_counter()
+    layers = make_stack(w, log)
+    torch.cuda.synchronize()
+    log("  done in %.1f s" % (time.perf_counter() - t0))
+    descs = stack_descs(ds4, w, layers)
+    n_steps = args.warmup + args.steps
+    h0, tok = step_inputs(w, n_steps)
+    h0_all, tok_all = to_dev(h0), to_dev(tok)
+    resid = torch.empty((1, w.H), dtype=torch.float32, device="cuda")
+    tokbuf = torch.empty(1, dtype=torch.int32, device="cuda")
+    idx = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out_all = torch.zeros((n_steps, w.H), dtype=torch.float32, device="cuda")
+    shp = ds4.shape(w.H, w.I, w.E, w.K, 1.5)
+    nb = ds4.workspace_size(shp, 1)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+
+    def step(st):
+        torch.index_select(h0_all, 0, idx, out=resid)
+        torch.index_select(tok_all, 0, idx, out=tokbuf)
+        for d in descs:
+            ds4.layer(shp, d, None, ds4.BF16, resid.data_ptr(), None, tokbuf.data_ptr(), 1, None,
+                      None, None, ws.data_ptr(), nb, st)
+        out_all.index_copy_(0, idx, resid)
+        idx.add_(1)
+
+    st = torch.cuda.current_stream().cuda_stream
+    step(st)
+    assert ds4.check(ws.data_ptr(), st) == 0
+    idx.zero_()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step(torch.cuda.current_stream().cuda_stream)
+    for _ in range(args.warmup):
+        gr.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert ds4.check(ws.data_ptr(), st) == 0
+    log("timed %d steps: %.3f ms" % (args.steps, ms))
+
+    # per-kernel events over a few eager steps behind a GPU sleep
+    classes = {"route": ds4.K_ROUTE, "gateup": ds4.K_GATEUP, "down": ds4.K_DOWN, "other": ds4.K_OTHER}
+    n_prof = 2
+    n_ev = n_prof * w.n_layers
+    evs = {c: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_ev)] for c in classes}
+    handles = {c: [(event_handle(a), event_handle(b)) for a, b in evs[c]] for c in classes}
+    used = {c: 0 for c in classes}
+    # the replays above advanced the step index to n_steps: start over so the
+    # eager steps read rows 0 .. n_prof-1 of the step inputs
+    assert n_prof <= n_steps
+    idx.zero_()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(args.sleep_cycles)
+    for j in range(n_prof):
+        torch.index_select(h0_all, 0, idx, out=resid)
+        torch.index_select(tok_all, 0, idx, out=tokbuf)
+        for l, d in enumerate(descs):
+            for c, k in classes.items():
+                if c == "other" and l >= w.n_hash:
+                    ds4.profile_events(k, None, None)
+                    continue
+                ds4.profile_events(k, handles[c][used[c]][0], handles[c][used[c]][1])
+                used[c] += 1
+            ds4.layer(shp, d, None, ds4.BF16, resid.data_ptr(), None, tokbuf.data_ptr(), 1, None,
+                      None, None, ws.data_ptr(), nb, st)
+        idx.add_(1)
+    for k in classes.values():
+        ds4.profile_events(k, None, None)
+    torch.cuda.synchronize()
+    kern_us = {c: float(np.mean([a.elapsed_time(b) for a, b in evs[c][:used[c]]]) * 1e3)
+               for c in classes if used[c]}
+    log("kernel averages (us):", kern_us)
+
+    expert_bytes = w.n_layers * w.K * w.expert_bytes()     # 1,826,095,104 per token
+    gateup_bytes = w.K * 2 * w.blocks_per_expert["gate"] * g.BLOCK_BYTES[w.gate_qt]
+    tok_s = args.steps / (ms * 1e-3)
+    gbs = expert_bytes * tok_s / 1e9
+    ach = gateup_bytes / (kern_us["gateup"] * 1e-6) / 1e9
+    res = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.n_layers, "hash_layers": w.n_hash,
+                   "hidden": w.H, "inter": w.I, "experts": w.E, "top_k": w.K,
+                   "resident_expert_bytes": w.n_layers * w.E * w.expert_bytes(),
+                   "timing": "hip-graph replay of one 43-layer step per token"},
+        "expert_gbs": round(gbs, 1), "expert_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "roofline": {"bound": "hbm", "kernel": "k_gateup_iq2_b1", "achieved": round(ach, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "traffic": None, "bytes_per_launch": gateup_bytes},
+    }
+    if args.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_stack(w, args.cpu_sample)
+    return res
+
+
+def cpu_baseline_stack(w, n_layers):
+    """The oracle on one decode step through the first n_layers layers
+    (normalisation, routing, experts, residual), scaled to 43 layers."""
+    import ds4gen as g
+    import oracle
+    from ds4gen.device import host_experts, step_inputs
+
+    h0, tok = step_inputs(w, 1)
+    resid = h0.copy()
+    t_total = 0.0
+    grid = g.grid(w.seed)
+    for l in range(n_layers):
+        nw = g.norm_weight(w, l)
+        if l < w.n_hash:
+            table = g.hash_table(w, l)
+        else:
+            W, b = g.router_weight(w, l), g.router_bias(w, l)
+        t0 = time.perf_counter()
+        xn = oracle.rmsnorm_bf16(resid, nw, 1e-6)
+        if l < w.n_hash:
+            ids, wts = oracle.route_hash(tok, table, w.E, w.K)
+        else:
+            ids, wts, _, _ = oracle.route(xn, "bf16", W, "f16", b, w.K)
+        t_total += time.perf_counter() - t0
+        mats = host_experts(w, l, ids[0])
+        t0 = time.perf_counter()
+        y = oracle.moe_ffn(xn, "bf16", ids, wts, mats, (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I,
+                           w.E, grid=grid)
+        resid = oracle.residual_add(resid, y)
+        t_total += time.perf_counter() - t0
+    per_token = t_total / n_layers * w.n_layers
+    return {"value": round(1.0 / per_token, 5), "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "one decode step through layers 0..%d (hash and learned routing), "
+                      "scaled to %d layers; weights regenerated outside the timed region"
+                      % (n_layers - 1, w.n_layers)}
+
+
 def cpu_baseline_decode(w, n_tokens):
     """The oracle (routing + expert FFN) on a bounded sample of the workload."""
     import numpy as np
@@ -191,12 +359,14 @@ def cpu_baseline_decode(w, n_tokens):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="decode-b1", choices=["decode-b1"])
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 2000 tokens for decode-b1, 256 for stack-43)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode-b1", choices=["decode-b1", "stack-43"])
     ap.add_argument("--layer-copies", type=int, default=1,
                     help="rotate over this many independently seeded layers")
-    ap.add_argument("--cpu-sample", type=int, default=3, help="tokens in the oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="oracle sample: tokens (decode-b1, default 3) or layers (stack-43, default 6)")
     ap.add_argument("--sleep-cycles", type=int, default=200_000_000,
                     help="GPU spin before the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
@@ -206,11 +376,21 @@ def main():
               "intermediate rows across GPUs but no multi-GPU run is implemented (--gpus 1).",
               file=sys.stderr)
         sys.exit(2)
+    stack = args.workload == "stack-43"
+    if args.steps is None:
+        args.steps = 256 if stack else 2000
+    if args.warmup is None:
+        args.warmup = 8 if stack else 200
+    if args.cpu_sample is None:
+        args.cpu_sample = 6 if stack else 3
     import torch
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    res = bench_decode_b1(args)
+    if args.workload == "stack-43":
+        res = bench_stack(args)
+    else:
+        res = bench_decode_b1(args)
     print(json.dumps(res), flush=True)
 
 

@@ -79,3 +79,28 @@ def host_experts(w, layer, experts):
 
 def host_shared(w, layer):
     return tuple(g.expert_tensor_blocks(w, layer, k, 0, 1) for k in ("sh_gate", "sh_up", "sh_down"))
+
+
+def make_stack(w, log=None):
+    """All layers of a decode stack: layers < w.n_hash use hash routing, the
+    rest a learned router; every layer has an RMSNorm weight.  Expert
+    tensors of every layer are distinct (the layer index is part of the
+    stream) and generated on the device."""
+    grid = to_dev(g.grid(w.seed))
+    layers = []
+    for l in range(w.n_layers):
+        layers.append(make_layer(w, l, hashed=l < w.n_hash, norm=True, grid=grid))
+        if log and (l % 8 == 7 or l == w.n_layers - 1):
+            log("  generated layer %d / %d (%.1f GB of experts)" %
+                (l + 1, w.n_layers, (l + 1) * w.E * w.expert_bytes() / 1e9))
+    return layers
+
+
+def step_inputs(w, n_steps, first_step=0):
+    """Per decode step: a fresh hidden state bf16 N(0,1) widened to fp32 (the
+    residual stream entering layer 0) and a token id uniform over the vocab."""
+    h0 = g.normal(w.seed, g.stream(0, g.X), n_steps * w.H, 0.0, 1.0, "bf16",
+                  first=first_step * w.H).reshape(n_steps, w.H)
+    h0f = (h0.astype(np.uint32) << 16).view(np.float32)
+    tok = g.token_ids(w, n_steps, first=first_step)
+    return h0f, tok
