@@ -27,6 +27,26 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, vendor figure
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
 METRIC = "MoE layer tokens/s + expert-weight HBM GB/s (% of peak), batch-1 decode"
 
+# HBM bytes per dispatch of the gate/up kernel from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes, scaled against a plain device copy of known size (the
+# summary sits in profiles/decode_b1_hbm_traffic.txt).  Reported only while
+# the kernel source still hashes to what was measured.
+GATEUP_TRAFFIC = {
+    "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
+                "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h"),
+    "sha256": "6e4afeb16210e8d01c37d52f2cd8f2450ca9abb21476b26aa67da916737c9df5",
+    "bytes": 26242925,
+}
+
+
+def measured_traffic(rec):
+    import hashlib
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return rec["bytes"] if rec["sha256"] and h.hexdigest() == rec["sha256"] else None
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -151,7 +171,8 @@ def bench_decode_b1(args):
         "kernel_timing": "HIP events recorded by the library around each launch, %d eager steps" % n_prof,
         "roofline": {"bound": "hbm", "kernel": "k_gateup_iq2_b1", "achieved": round(ach, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                     "traffic": None, "bytes_per_launch": gateup_bytes},
+                     "traffic": measured_traffic(GATEUP_TRAFFIC),
+                     "bytes_per_launch": gateup_bytes},
     }
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(w, args.cpu_sample)
@@ -281,7 +302,8 @@ def bench_stack(args):
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
         "roofline": {"bound": "hbm", "kernel": "k_gateup_iq2_b1", "achieved": round(ach, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                     "traffic": None, "bytes_per_launch": gateup_bytes},
+                     "traffic": measured_traffic(GATEUP_TRAFFIC),
+                     "bytes_per_launch": gateup_bytes},
     }
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_stack(w, args.cpu_sample)
@@ -370,6 +392,9 @@ def main():
     ap.add_argument("--sleep-cycles", type=int, default=200_000_000,
                     help="GPU spin before the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB, so that hardware "
+                         "byte counters can be scaled against a transfer of known size")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; the path shards by expert or by "
@@ -387,6 +412,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: %d bytes read, %d written" % (n, n))
+        del src, dst
     if args.workload == "stack-43":
         res = bench_stack(args)
     else:
