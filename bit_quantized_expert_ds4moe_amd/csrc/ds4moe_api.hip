@@ -123,7 +123,8 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
   a.status = status;
   const bool vec = s.hidden % 2048 == 0 && s.hidden <= 4096 && r.w_dtype == DS4MOE_F16 &&
                    (norm_w || x_dt == DS4MOE_BF16) && ((uintptr_t)r.w % 16 == 0) &&
-                   (norm_w ? ((uintptr_t)residual % 16 == 0 && (uintptr_t)norm_w % 16 == 0)
+                   (norm_w ? ((uintptr_t)residual % 16 == 0 && (uintptr_t)norm_w % 16 == 0 &&
+                              (uintptr_t)xn_out % 16 == 0)
                            : (uintptr_t)x % 16 == 0);
   const dim3 grid(s.n_expert, T);
   if (vec && norm_w)
@@ -141,20 +142,44 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
 }
 
 // RMSNorm only (hash layers): one block per token writes xn.
+// RMSNorm of the residual stream to bf16 (used where routing does not fold it
+// in, i.e. hash-routed layers).  One block per token; up to 4096 columns the
+// loads of a thread are all issued before the first use.
 __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, const float* w,
                                                      float eps, int H, uint16_t* xn) {
   __shared__ double sh[8];
+  constexpr int kRegCols = 16;
   const int t = blockIdx.x, tid = threadIdx.x;
+  const float* r = residual + (size_t)t * H;
   double ss = 0.0, dummy = 0.0;
+  if (H <= 256 * kRegCols) {
+    float v[kRegCols], wv[kRegCols];
+#pragma unroll
+    for (int j = 0; j < kRegCols; j++) {
+      const int c = tid + 256 * j;
+      v[j] = c < H ? r[c] : 0.0f;
+      wv[j] = c < H ? w[c] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kRegCols; j++) ss = fma((double)v[j], (double)v[j], ss);
+    block_sum2(ss, dummy, sh);
+    const double ns = 1.0 / sqrt(ss / (double)H + (double)eps);
+#pragma unroll
+    for (int j = 0; j < kRegCols; j++) {
+      const int c = tid + 256 * j;
+      if (c < H)
+        xn[(size_t)t * H + c] = (uint16_t)f64_to_bf16_bits((double)v[j] * ns * (double)wv[j]);
+    }
+    return;
+  }
   for (int c = tid; c < H; c += 256) {
-    double v = (double)residual[(size_t)t * H + c];
+    double v = (double)r[c];
     ss = fma(v, v, ss);
   }
   block_sum2(ss, dummy, sh);
-  double ns = 1.0 / sqrt(ss / (double)H + (double)eps);
+  const double ns = 1.0 / sqrt(ss / (double)H + (double)eps);
   for (int c = tid; c < H; c += 256)
-    xn[(size_t)t * H + c] =
-        (uint16_t)f64_to_bf16_bits((double)residual[(size_t)t * H + c] * ns * (double)w[c]);
+    xn[(size_t)t * H + c] = (uint16_t)f64_to_bf16_bits((double)r[c] * ns * (double)w[c]);
 }
 
 // ---- expert FFN dispatch ----------------------------------------------------

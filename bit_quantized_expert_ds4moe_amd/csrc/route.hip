@@ -129,8 +129,33 @@ __global__ __launch_bounds__(256) void k_route_score(RouteArgs a) {
     for (int j = 0; j < kMaxSlab; j++)
       if (j < a.H / 2048) wv[j] = wp[256 * j + tid];
   }
+  // Normalised input: the residual and norm weight of the thread's own
+  // columns are loaded once, up front; the columns of all threads cover the
+  // row exactly once, so the sum of squares comes from the same registers.
+  float rr[kMaxSlab][8], nw[kMaxSlab][8];
   double nscale = 1.0;
-  if (NORM) {  // RMSNorm scale, recomputed identically by every block
+  if (NORM && VEC) {
+#pragma unroll
+    for (int j = 0; j < kMaxSlab; j++) {
+      if (j >= a.H / 2048) break;
+      const float4* rp = (const float4*)(a.residual + (size_t)t * a.H) + 512 * j + 2 * tid;
+      const float4* np = (const float4*)a.norm_w + 512 * j + 2 * tid;
+      const float4 r0 = rp[0], r1 = rp[1], n0 = np[0], n1 = np[1];
+      rr[j][0] = r0.x; rr[j][1] = r0.y; rr[j][2] = r0.z; rr[j][3] = r0.w;
+      rr[j][4] = r1.x; rr[j][5] = r1.y; rr[j][6] = r1.z; rr[j][7] = r1.w;
+      nw[j][0] = n0.x; nw[j][1] = n0.y; nw[j][2] = n0.z; nw[j][3] = n0.w;
+      nw[j][4] = n1.x; nw[j][5] = n1.y; nw[j][6] = n1.z; nw[j][7] = n1.w;
+    }
+    double ss = 0.0, dummy = 0.0;
+#pragma unroll
+    for (int j = 0; j < kMaxSlab; j++) {
+      if (j >= a.H / 2048) break;
+#pragma unroll
+      for (int u = 0; u < 8; u++) ss = fma((double)rr[j][u], (double)rr[j][u], ss);
+    }
+    block_sum2(ss, dummy, sh);
+    nscale = 1.0 / sqrt(ss / (double)a.H + (double)a.eps);
+  } else if (NORM) {  // generic shapes: strided columns
     double ss = 0.0, dummy = 0.0;
     for (int c = tid; c < a.H; c += 256) {
       double v = (double)a.residual[(size_t)t * a.H + c];
@@ -150,29 +175,26 @@ __global__ __launch_bounds__(256) void k_route_score(RouteArgs a) {
     for (int j = 0; j < kMaxSlab; j++) {
       if (j >= a.H / 2048) break;
       uint32_t xx[4];
-      float rr[8], nw[8];
       if (!NORM) {
         const uint4 xv = ((const uint4*)((const uint16_t*)a.x + (size_t)t * a.H))[256 * j + tid];
         xx[0] = xv.x; xx[1] = xv.y; xx[2] = xv.z; xx[3] = xv.w;
       } else {
-        const float4* rp = (const float4*)(a.residual + (size_t)t * a.H) + 512 * j + 2 * tid;
-        const float4* np = (const float4*)a.norm_w + 512 * j + 2 * tid;
-        float4 r0 = rp[0], r1 = rp[1], n0 = np[0], n1 = np[1];
-        rr[0] = r0.x; rr[1] = r0.y; rr[2] = r0.z; rr[3] = r0.w;
-        rr[4] = r1.x; rr[5] = r1.y; rr[6] = r1.z; rr[7] = r1.w;
-        nw[0] = n0.x; nw[1] = n0.y; nw[2] = n0.z; nw[3] = n0.w;
-        nw[4] = n1.x; nw[5] = n1.y; nw[6] = n1.z; nw[7] = n1.w;
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+          const uint32_t lo = f64_to_bf16_bits((double)rr[j][2 * m] * nscale * (double)nw[j][2 * m]);
+          const uint32_t hi =
+              f64_to_bf16_bits((double)rr[j][2 * m + 1] * nscale * (double)nw[j][2 * m + 1]);
+          xx[m] = lo | (hi << 16);
+        }
+        if (e == 0 && a.xn_out)
+          ((uint4*)(a.xn_out + (size_t)t * a.H))[256 * j + tid] = make_uint4(xx[0], xx[1], xx[2], xx[3]);
       }
       const uint32_t ww[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
 #pragma unroll
       for (int u = 0; u < 8; u++) {
         const uint32_t sh16 = 16 * (u & 1);
-        double xd;
-        if (NORM)
-          xd = bf16_bits_to_f64(f64_to_bf16_bits((double)rr[u] * nscale * (double)nw[u]));
-        else
-          xd = bf16_bits_to_f64((xx[u >> 1] >> sh16) & 0xFFFFu);
-        double p = xd * f16_bits_to_f64((ww[u >> 1] >> sh16) & 0xFFFFu);
+        const double xd = bf16_bits_to_f64((xx[u >> 1] >> sh16) & 0xFFFFu);
+        const double p = xd * f16_bits_to_f64((ww[u >> 1] >> sh16) & 0xFFFFu);
         acc += p;
         aabs += fabs(p);
       }
