@@ -4,10 +4,10 @@
 #include <string.h>
 
 #include "dev_common.h"
+#include "route.hip"
 #include "ffn_b1.hip"
 #include "ffn_generic.hip"
 #include "grouped.hip"
-#include "route.hip"
 
 #define DS4_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -19,7 +19,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Byte offsets of the workspace regions for (shape, n_tok).
 struct Layout {
-  size_t status, kbuf, ids, wts, xn, hs, perm, h, y, hb, total;
+  size_t status, kbuf, ids, wts, xn, perm, h, y, hb, total;
 };
 
 Layout layout_for(const ds4moe_shape& s, int32_t T) {
@@ -38,7 +38,6 @@ Layout layout_for(const ds4moe_shape& s, int32_t T) {
   L.ids = take(t * K * 4);
   L.wts = take(t * K * 4);
   L.xn = take(t * H * 2);
-  L.hs = take(K * 64 * kHqDwords * 4);
   L.perm = take((E + (E + 1) + 2 * t * K + 3 * (size_t)max_items((int)E, (int)(t * K), (int)t, true) + 64) * 4);
   L.h = take(np * I * 4);
   L.y = take(np * H * 4);
@@ -94,7 +93,7 @@ T* at(void* ws, size_t off) {
 ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void* x, int32_t x_dt,
                        const float* residual, const float* norm_w, float eps, uint16_t* xn_out,
                        int32_t T, const int32_t* tok, int32_t* ids, float* wts, void* ws,
-                       const Layout& L, hipStream_t st) {
+                       const Layout& L, hipStream_t st, bool select = true) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   ProfScope prof(DS4MOE_K_ROUTE, st);
   if (r.tid2eid) {
@@ -136,7 +135,7 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
   else
     hipLaunchKernelGGL((k_route_score<false, false>), grid, dim3(256), 0, st, a);
   ds4moe_status rc = launched();
-  if (rc != DS4MOE_OK) return rc;
+  if (rc != DS4MOE_OK || !select) return rc;
   hipLaunchKernelGGL(k_route_select, dim3(T), dim3(64), 0, st, a);
   return launched();
 }
@@ -188,7 +187,44 @@ bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_exper
   return T == 1 && !sh && x_dt == DS4MOE_BF16 && s.hidden == kH && s.inter == kI && ex.inter == kI &&
          s.top_k == 6 && ex.gate_qtype == DS4MOE_IQ2_XXS && ex.up_qtype == DS4MOE_IQ2_XXS &&
          ex.down_qtype == DS4MOE_Q2_K && aligned(x, 16) && aligned(ex.gate, 16) &&
-         aligned(ex.up, 16) && aligned(ex.down, 16);
+         aligned(ex.up, 16) && aligned(ex.down, 16) && aligned(ex.grid, 8);
+}
+
+// Batch-1 fast path: gate/up (+ the top-6 selection when kbuf is given, in
+// which case ids/wts are outputs) then down.
+ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x,
+                        const int32_t* ids_in, const float4* kbuf, int32_t* ids, const float* wts,
+                        float* out, float* residual, void* ws, const Layout& L, hipStream_t st) {
+  uint32_t* status = at<uint32_t>(ws, L.status);
+  float* h = at<float>(ws, L.h);
+  GateUpB1Args g{};
+  g.x = (const uint16_t*)x;
+  g.gate = (const uint8_t*)ex.gate;
+  g.up = (const uint8_t*)ex.up;
+  g.grid = ex.grid;
+  g.ids = ids_in;
+  g.kbuf = kbuf;
+  g.scale = s.routed_scale;
+  g.ids_out = ids;
+  g.wts_out = const_cast<float*>(wts);
+  g.E = s.n_expert;
+  g.h = h;
+  g.status = status;
+  {
+    ProfScope prof(DS4MOE_K_GATEUP, st);
+    if (kbuf)
+      hipLaunchKernelGGL(k_gateup_b1<true>, dim3(kGuBlocks), dim3(kGuWaves * 64), 0, st, g);
+    else
+      hipLaunchKernelGGL(k_gateup_b1<false>, dim3(kGuBlocks), dim3(kGuWaves * 64), 0, st, g);
+  }
+  ds4moe_status rc = launched();
+  if (rc != DS4MOE_OK) return rc;
+  {
+    ProfScope prof(DS4MOE_K_DOWN, st);
+    hipLaunchKernelGGL(k_down_q2k_b1, dim3(kH / 8), dim3(384), 0, st, h, (const uint8_t*)ex.down,
+                       kbuf ? ids : ids_in, wts, s.n_expert, out, residual, status);
+  }
+  return launched();
 }
 
 ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_experts* sh,
@@ -196,23 +232,8 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
                      float* out, float* residual, int32_t* perm_dbg, void* ws, const Layout& L,
                      hipStream_t st) {
   uint32_t* status = at<uint32_t>(ws, L.status);
-  if (fast_b1(s, ex, sh, x, x_dt, T)) {
-    uint32_t* hq = at<uint32_t>(ws, L.hs);
-    {
-      ProfScope prof(DS4MOE_K_GATEUP, st);
-      hipLaunchKernelGGL(k_gateup_iq2_b1, dim3(6 * 64), dim3(512), 0, st, (const uint16_t*)x,
-                         (const uint8_t*)ex.gate, (const uint8_t*)ex.up, ex.grid, ids, s.n_expert,
-                         hq, status);
-    }
-    ds4moe_status rc = launched();
-    if (rc != DS4MOE_OK) return rc;
-    {
-      ProfScope prof(DS4MOE_K_DOWN, st);
-      hipLaunchKernelGGL(k_down_q2k_b1, dim3(kH / 8), dim3(384), 0, st, hq,
-                         (const uint8_t*)ex.down, ids, wts, s.n_expert, out, residual, status);
-    }
-    return launched();
-  }
+  if (fast_b1(s, ex, sh, x, x_dt, T))
+    return launch_b1(s, ex, x, ids, nullptr, nullptr, wts, out, residual, ws, L, st);
   if (T > 1 && grouped_eligible(s, ex, sh, x, x_dt, T)) {
     const int E = s.n_expert, K = s.top_k, TK = T * K;
     int32_t* counts = at<int32_t>(ws, L.perm);
@@ -445,13 +466,22 @@ DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_la
                        desc->norm_eps, shape->hidden, xn);
     if ((rc = launched()) != DS4MOE_OK) return rc;
   }
-  rc = do_route(*shape, r, x, x_dtype, norm ? residual : nullptr, norm ? desc->norm_w : nullptr,
-                desc->norm_eps, norm ? xn : nullptr, n_tok, token_ids, ids, wts, ws, L, stream);
-  if (rc != DS4MOE_OK) return rc;
   const void* fx = norm ? (const void*)xn : x;
   int32_t fdt = norm ? (int32_t)DS4MOE_BF16 : x_dtype;
-  rc = do_ffn(*shape, desc->routed, sh, fx, fdt, n_tok, ids, wts, norm ? nullptr : out,
-              norm ? residual : nullptr, nullptr, ws, L, stream);
+  // batch-1 fast path with a learned router: the top-6 selection runs inside
+  // the gate/up kernel (one kernel boundary fewer)
+  const bool fuse = !r.tid2eid && fast_b1(*shape, desc->routed, sh, norm ? (const void*)xn : x,
+                                          fdt, n_tok);
+  rc = do_route(*shape, r, x, x_dtype, norm ? residual : nullptr, norm ? desc->norm_w : nullptr,
+                desc->norm_eps, norm ? xn : nullptr, n_tok, token_ids, ids, wts, ws, L, stream,
+                !fuse);
+  if (rc != DS4MOE_OK) return rc;
+  if (fuse)
+    rc = launch_b1(*shape, desc->routed, fx, nullptr, at<float4>(ws, L.kbuf), ids, wts,
+                   norm ? nullptr : out, norm ? residual : nullptr, ws, L, stream);
+  else
+    rc = do_ffn(*shape, desc->routed, sh, fx, fdt, n_tok, ids, wts, norm ? nullptr : out,
+                norm ? residual : nullptr, nullptr, ws, L, stream);
   if (rc != DS4MOE_OK) return rc;
   if (ids_dbg &&
       hipMemcpyAsync(ids_dbg, ids, sizeof(int32_t) * n_tok * shape->top_k, hipMemcpyDeviceToDevice,

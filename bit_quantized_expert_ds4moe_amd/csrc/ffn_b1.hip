@@ -37,81 +37,80 @@ constexpr int kRowIq2 = 16 * kIq2Bytes;  // 1056 bytes per gate/up row
 constexpr int kRowQ2k = 8 * kQ2kBytes;   // 672 bytes per down row
 
 // ---------------------------------------------------------------------------
-// SwiGLU output hand-off between the two kernels.  The down matvec gives lane
-// L = 8b + 4hh + c of a wave the 32 columns  i = 256b + 128hh + 32s + 8c + j
-// (s, j < 4, 8) of every row.  The gate/up kernel therefore computes exactly
-// those 32 rows in one workgroup and stores them as 16-bit fixed point with
-// one scale per chunk: h_i ~= S * n_i, n_i = round(32767 h_i / max|h|).
-// Record per (slot k, lane L), 24 dwords:
-//   [0..15]  n as int16 pairs, dword 4s+m = (n[8s+2m], n[8s+2m+1])
-//   [16..19] X_s = sum_j n[8s+j]      (int32, for the min term)
-//   [20]     S                        (fp32)
-// The relative quantisation error (< 2^-16 of the chunk maximum) is eight
-// times below that of binary16 rounding, and every later product is exact.
-constexpr int kHqDwords = 24;
+// gate/up LDS tables, one copy per workgroup:
+//   signs: 7-bit sign field s (with its even-parity eighth bit) as four XOR
+//          masks on bf16 pairs, stored 16 times, copy p at (s << 8) | (p << 4);
+//   grid:  entry e (8 grid values as four bf16 pairs, 16 B) stored 16 times,
+//          copy p at 32 KB + (e << 8) | (p << 4).
+// Lane l reads copy l % 16.  A 16-byte LDS read serves 16 lanes per clock
+// from 16 distinct 16-byte bank groups, so these random lookups never
+// conflict, and both addresses are formed by one or two VALU ops (the grid
+// index byte is moved to bits 8..15 by v_perm); the table bases sit in the
+// 16-bit offset field of the LDS reads.
+constexpr int kSignTab = 128 * 256;                // 32 KB
+constexpr int kGridTab = 256 * 256;                // 64 KB
 
-// LDS tables: grid entry -> 4 bf16 pairs (16 B); 7-bit sign mask -> 4 XOR
-// masks (16 B).  The lookups are random, so each table is stored 8 times:
-// copy p of entry e sits at 16-byte slot 8e + p, i.e. always in bank group p,
-// and lane l reads copy l % 8.  Eight consecutive lanes then touch eight
-// different bank groups whatever their indices: the reads are conflict-free.
-// Built by 512 threads.
-__device__ inline void build_iq2_tables8(const uint8_t* grid, uint4* gt8, uint4* mt8) {
-  const int t = threadIdx.x;
-  {
-    const int e = t >> 1;
-    const uint8_t* g = grid + 8 * e;
-    uint32_t w[4];
-    for (int m = 0; m < 4; m++) {
-      uint32_t lo = __float_as_uint((float)g[2 * m]) >> 16;
-      uint32_t hi = __float_as_uint((float)g[2 * m + 1]) >> 16;
-      w[m] = lo | (hi << 16);
-    }
-    const uint4 v = make_uint4(w[0], w[1], w[2], w[3]);
-    for (int q = 0; q < 4; q++) gt8[8 * e + 4 * (t & 1) + q] = v;
+__device__ inline uint4 grid_pairs(uint2 g) {
+  uint32_t w[4];
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const uint32_t word = m < 2 ? g.x : g.y;
+    const float lo = (float)((word >> (16 * (m & 1))) & 0xFFu);
+    const float hi = (float)((word >> (16 * (m & 1) + 8)) & 0xFFu);
+    w[m] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
   }
-  if (t < 256) {
-    const int e = t >> 1;
-    uint32_t s8 = (uint32_t)e | ((uint32_t)(__popc(e) & 1) << 7);
-    uint32_t w[4];
-    for (int m = 0; m < 4; m++)
-      w[m] = (((s8 >> (2 * m)) & 1u) << 15) | (((s8 >> (2 * m + 1)) & 1u) << 31);
-    const uint4 v = make_uint4(w[0], w[1], w[2], w[3]);
-    for (int q = 0; q < 4; q++) mt8[8 * e + 4 * (t & 1) + q] = v;
-  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ inline uint4 sign_masks(int s7) {
+  const uint32_t s8 = (uint32_t)s7 | ((uint32_t)(__popc(s7) & 1) << 7);
+  uint32_t w[4];
+#pragma unroll
+  for (int m = 0; m < 4; m++)
+    w[m] = (((s8 >> (2 * m)) & 1u) << 15) | (((s8 >> (2 * m + 1)) & 1u) << 31);
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Raw bytes of one lane's IQ2_XXS row segment: block b = lane/4, groups
 // 2j, 2j+1 (j = lane%4), i.e. 64 columns from 256b + 64j.  The 16 group bytes
 // start 2 bytes into a 4-byte word for even b; five aligned dwords cover
 // them, and the fifth is fetched from inside the group when not needed so the
-// last row of a tensor is never overrun.
+// last row of a tensor is never overrun.  dw is the aligned word holding the
+// block scale d.  Offsets are in dwords from the (wave-uniform) row start.
 struct Iq2Seg {
   uint32_t w0, w1, w2, w3, w4, dw;
 };
+struct Iq2Off {
+  uint32_t o0, o4, od;
+};
 
-__device__ inline void iq2_load(const uint8_t* row, int lane, Iq2Seg& sg) {
+__device__ inline Iq2Off iq2_offsets(int lane) {
   const int b = lane >> 2, j = lane & 3;
-  const uint8_t* blk = row + b * kIq2Bytes;
-  const uint8_t* ga = blk + 2 + 16 * j;
-  // pointer arithmetic (not integer casts) keeps these global-memory loads
-  const uint32_t sh = (uint32_t)((uintptr_t)ga & 3);
-  const uint32_t* gp = (const uint32_t*)(ga - sh);
-  sg.w0 = gp[0];
-  sg.w1 = gp[1];
-  sg.w2 = gp[2];
-  sg.w3 = gp[3];
-  sg.w4 = gp[sh ? 4 : 3];
-  sg.dw = *(const uint32_t*)(blk - ((uintptr_t)blk & 3));
+  const uint32_t start = (uint32_t)(kIq2Bytes * b + 2 + 16 * j);
+  Iq2Off o;
+  o.o0 = start >> 2;
+  o.o4 = o.o0 + ((start & 3) ? 4u : 3u);
+  o.od = (uint32_t)(kIq2Bytes * b) >> 2;
+  return o;
 }
 
-__device__ inline float iq2_dot(const Iq2Seg& sg, int lane, const uint32_t* xr, const uint4* gt8,
-                                const uint4* mt8) {
-  const int rep = lane & 7;
-  const int b = lane >> 2;
-  // block start parity decides both misalignments (rows are 16-byte aligned)
-  const uint32_t sh = (b & 1) ? 0u : 2u;
-  float d = f16_bits_to_f32(sh ? (sg.dw & 0xFFFFu) : (sg.dw >> 16));
+// Row r of a wave's rows (rows are kRowIq2 = 264 dwords apart).
+__device__ inline void iq2_load(const uint32_t* __restrict__ base, int r, const Iq2Off& o,
+                                Iq2Seg& sg) {
+  const uint32_t* p = base + r * (kRowIq2 / 4);
+  sg.w0 = p[o.o0];
+  sg.w1 = p[o.o0 + 1];
+  sg.w2 = p[o.o0 + 2];
+  sg.w3 = p[o.o0 + 3];
+  sg.w4 = p[o.o4];
+  sg.dw = p[o.od];
+}
+
+// Partial dot product of one lane's 64 columns with x (bf16 pairs in xr).
+// The group scale d(2s+1)/8 is applied as (16s+8) per group and d/64 once.
+__device__ inline float iq2_dot16(const Iq2Seg& sg, uint32_t sh, const uint32_t* xr,
+                                  const uint8_t* gtab, const uint8_t* stab, uint32_t rep16) {
+  const float d = f16_bits_to_f32(sh ? (sg.dw & 0xFFFFu) : (sg.dw >> 16));
   uint32_t g[4];
   g[0] = align_bytes(sg.w1, sg.w0, sh);
   g[1] = align_bytes(sg.w2, sg.w1, sh);
@@ -120,117 +119,232 @@ __device__ inline float iq2_dot(const Iq2Seg& sg, int lane, const uint32_t* xr, 
   float acc = 0.0f;
 #pragma unroll
   for (int grp = 0; grp < 2; grp++) {
-    uint32_t idxw = g[2 * grp], sw = g[2 * grp + 1];
-    float dg = d * (float)(2u * (sw >> 28) + 1u) * 0.125f;
+    const uint32_t idxw = g[2 * grp], sw = g[2 * grp + 1];
     float gacc = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) {
-      uint4 gv = gt8[8 * ((idxw >> (8 * kk)) & 0xFFu) + rep];
-      uint4 mv = mt8[8 * ((sw >> (7 * kk)) & 0x7Fu) + rep];
+      const uint32_t ga = vperm(idxw, rep16, 0x0C0C0000u | ((4u + kk) << 8));
+      const uint32_t sa = (((sw >> (7 * kk)) & 0x7Fu) << 8) | rep16;
+      const uint4 gv = *(const uint4*)(gtab + ga);
+      const uint4 mv = *(const uint4*)(stab + sa);
       const uint32_t* xp = xr + grp * 16 + kk * 4;
       gacc = dot2_bf16(gv.x ^ mv.x, xp[0], gacc);
       gacc = dot2_bf16(gv.y ^ mv.y, xp[1], gacc);
       gacc = dot2_bf16(gv.z ^ mv.z, xp[2], gacc);
       gacc = dot2_bf16(gv.w ^ mv.w, xp[3], gacc);
     }
-    acc = fmaf(dg, gacc, acc);
+    // 16s + 8 from the top nibble: exact in fp32
+    acc = fmaf((float)(((sw & 0xF0000000u) | 0x08000000u) >> 24), gacc, acc);
   }
-  return acc;
+  return acc * (d * 0.015625f);
 }
 
-// Max over the 64 lanes (result in every lane).
-__device__ inline float wave_max(float v) {
-  v = fmaxf(v, dpp_f32<0xB1>(v));
-  v = fmaxf(v, dpp_f32<0x4E>(v));
-  v = fmaxf(v, dpp_f32<0x141>(v));
-  v = fmaxf(v, dpp_f32<0x140>(v));
-  float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
-}
-
-// gate/up + SwiGLU + fixed-point hand-off for one token.
-// Grid K*64 workgroups of 512 threads: workgroup (k, L) computes the 32 rows
-// of down-lane L for routed slot k; wave w does rows j = 4(w&1)..+3 of
-// bit-pair s = w/2.  All weight loads of a wave are issued before anything
-// else so that their latency overlaps the table build and the x staging.
-__global__ __launch_bounds__(512) void k_gateup_iq2_b1(const uint16_t* __restrict__ x,
-                                                       const uint8_t* __restrict__ gate,
-                                                       const uint8_t* __restrict__ up,
-                                                       const uint8_t* __restrict__ grid,
-                                                       const int32_t* __restrict__ ids, int E,
-                                                       uint32_t* __restrict__ hq,
-                                                       uint32_t* status) {
-  __shared__ uint4 gt8[256 * 8];
-  __shared__ uint4 mt8[128 * 8];
-  __shared__ uint4 xs[kH / 8];
-  __shared__ float hv[32];
-  const int k = blockIdx.x >> 6, L = blockIdx.x & 63;
-  const int b = L >> 3, hh = (L >> 2) & 1, c = L & 3;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, s = w >> 1;
-  int e = ids[k];
-  if (e < 0 || e >= E) {
-    if (tid == 0 && L == 0) raise_fault(status, DS4MOE_FAULT_BAD_ID);
-    e = 0;
-  }
-  const int i0 = 256 * b + 128 * hh + 32 * s + 8 * c + 4 * (w & 1);
-  Iq2Seg sg[4], su[4];
+// Sums over the 64 lanes of eight per-lane values at once.  Lane L ends up
+// holding the total of v[4*((L>>3)&1) + c[L>>4]], c = {0,2,1,3}; every lane
+// of an aligned group of 8 holds the same total.  18 VALU ops instead of 8
+// separate wave reductions.
+__device__ inline float reduce8(const float* v) {
+  float u[4];
 #pragma unroll
-  for (int r = 0; r < 4; r++) {
-    iq2_load(gate + ((size_t)e * kI + i0 + r) * kRowIq2, lane, sg[r]);
-    iq2_load(up + ((size_t)e * kI + i0 + r) * kRowIq2, lane, su[r]);
+  for (int p = 0; p < 4; p++) {
+    // halves: lanes 0-31 <- v[2p] (both halves summed), lanes 32-63 <- v[2p+1]
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2 * p]),
+                                              __float_as_uint(v[2 * p + 1]), false, false);
+    u[p] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-  // x staged in LDS with 16-byte chunk c stored at slot c ^ ((c >> 3) & 7), so
-  // the eight chunks a lane reads land in eight bank groups across lanes
-  xs[tid ^ ((tid >> 3) & 7)] = ((const uint4*)x)[tid];
-  build_iq2_tables8(grid, gt8, mt8);
+  float w2[2];
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    // rows of 16: row 0 <- v[4q], row 1 <- v[4q+2], row 2 <- v[4q+1], row 3 <- v[4q+3]
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(u[2 * q]),
+                                              __float_as_uint(u[2 * q + 1]), false, false);
+    w2[q] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  // within rows of 16: lanes 0-7 <- w2[0], lanes 8-15 <- w2[1]
+  const bool up8 = (threadIdx.x & 8) != 0;
+  const float t = up8 ? w2[0] : w2[1];
+  float z = (up8 ? w2[1] : w2[0]) + dpp_f32<0x128>(t);  // row_ror:8
+  z += dpp_f32<0xB1>(z);
+  z += dpp_f32<0x4E>(z);
+  z += dpp_f32<0x141>(z);
+  return z;
+}
+
+struct GateUpB1Args {
+  const uint16_t* x;       // [4096] bf16
+  const uint8_t* gate;     // [E][2048][1056 B]
+  const uint8_t* up;
+  const uint8_t* grid;     // [256][8]
+  const int32_t* ids;      // [6] (no selection)
+  const float4* kbuf;      // [E] key intervals (selection)
+  float scale;
+  int32_t* ids_out;        // [6] (selection)
+  float* wts_out;          // [6] (selection)
+  int E;
+  float* h;                // [6][2048] SwiGLU output
+  uint32_t* status;
+};
+
+constexpr int kGuWaves = 16;                                  // waves per workgroup
+constexpr int kGuRows = 3;                                    // rows (gate + up) per wave
+constexpr int kGuBlocks = 6 * kI / (kGuWaves * kGuRows);      // 256
+static_assert(kGuBlocks * kGuWaves * kGuRows == 6 * kI, "gate/up rows must tile the 6 slots");
+static_assert(384 + kH / 8 <= kGuWaves * 64 - 64, "x staging needs one helper per 16-byte chunk");
+
+// A wave-uniform int32 read through the scalar cache (the data must not be
+// written while the kernel runs).
+__device__ inline int load_scalar_i32(const int32_t* p, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+// Table build, conflict-free: a thread owns one entry and writes its 16
+// copies in the order p = (j + entry) % 16, so the 16 lanes a store serves in
+// one clock hit 16 different bank groups.
+__device__ inline void store_copies(uint8_t* tab, int entry, uint4 v) {
+#pragma unroll
+  for (int j = 0; j < 16; j++)
+    *(uint4*)(tab + (entry << 8) + (((j + entry) & 15) << 4)) = v;
+}
+
+// gate/up + SwiGLU for one token.  Grid 256 workgroups of 16 waves; wave w of
+// workgroup g handles flattened rows 3u .. 3u+2, u = 16g + w, of the six
+// routed slots (row r of slot k is flattened row 2048k + r), gate and up.
+// With SEL the workgroup first picks the top-6 experts from the router's key
+// intervals (wave 0, while the other waves build the tables and stage x);
+// workgroup 0 publishes ids and gates for the down kernel.  Without SEL the
+// weight loads are issued before the tables are built.
+template <bool SEL>
+__global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
+  // one static array so that the table offsets are compile-time constants
+  __shared__ uint4 lds4[(kSignTab + kGridTab + 2 * kH) / 16 + 2];
+  uint8_t* stab = (uint8_t*)lds4;                        // 32 KB
+  uint8_t* gtab = stab + kSignTab;                       // 64 KB
+  uint4* xs = lds4 + (kSignTab + kGridTab) / 16;         // 8 KB
+  int* sel_e = (int*)(lds4 + (kSignTab + kGridTab + 2 * kH) / 16);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in scalar registers
+  const int row0 = (blockIdx.x * kGuWaves + w) * kGuRows;  // flattened
+  const Iq2Off off = iq2_offsets(lane);
+  Iq2Seg sg[kGuRows], su[kGuRows];
+
+  // helper roles for the table build and x staging; their global loads are
+  // issued before the weight loads so that waiting for them never waits for
+  // weights (the vector memory counter retires in order)
+  const int t = tid - 64;
+  uint2 gb = make_uint2(0, 0);
+  uint4 xv = make_uint4(0, 0, 0, 0);
+  if (t >= 0 && t < 256) gb = *(const uint2*)(a.grid + 8 * t);
+  else if (t >= 384 && t < 384 + kH / 8) xv = ((const uint4*)a.x)[t - 384];
+
+  // Expert of each of the wave's rows (wave-uniform), validated.
+  auto expert_rows = [&](const int* e_of_slot_lds, uint32_t* erow) {
+#pragma unroll
+    for (int r = 0; r < kGuRows; r++) {
+      const int k = (row0 + r) >> 11;
+      int e = SEL ? __builtin_amdgcn_readfirstlane(e_of_slot_lds[k]) : load_scalar_i32(a.ids, k);
+      if (e < 0 || e >= a.E) {
+        if (lane == 0 && ((row0 + r) & (kI - 1)) == 0) raise_fault(a.status, DS4MOE_FAULT_BAD_ID);
+        e = 0;
+      }
+      erow[r] = (uint32_t)e;
+    }
+  };
+  uint32_t erow[kGuRows];
+  auto load_row = [&](int r) {
+    const size_t rowi = (size_t)erow[r] * kI + ((row0 + r) & (kI - 1));
+    iq2_load((const uint32_t*)(a.gate + rowi * kRowIq2), 0, off, sg[r]);
+    iq2_load((const uint32_t*)(a.up + rowi * kRowIq2), 0, off, su[r]);
+  };
+  // Without selection: two rows in flight from the start, the third issued
+  // once the first has been consumed (with every row of every wave requested
+  // at once, each wave's data tends to complete only near the end of the
+  // whole transfer).
+  static_assert(kGuRows == 3, "the load schedule assumes three rows per wave");
+  if (!SEL) {
+    expert_rows(nullptr, erow);
+    load_row(0);
+    load_row(1);
+  }
+
+  if (SEL && w == 0) {
+    int e;
+    float g;
+    const bool first = blockIdx.x == 0;
+    select_wave(a.kbuf, a.E, 6, a.scale, a.status, first, e, g);
+    if (lane < 6) {
+      sel_e[lane] = e;
+      if (first) {
+        a.ids_out[lane] = e;
+        a.wts_out[lane] = g;
+      }
+    }
+  } else if (t >= 0 && t < 256) {
+    store_copies(gtab, t, grid_pairs(gb));
+  } else if (t >= 256 && t < 384) {
+    store_copies(stab, t - 256, sign_masks(t - 256));
+  } else if (t >= 384 && t < 384 + kH / 8) {
+    // x chunk c (16 B) at slot c ^ ((c >> 3) & 7): a lane's eight chunks
+    // then fall in eight bank groups
+    const int c = t - 384;
+    xs[c ^ ((c >> 3) & 7)] = xv;
+  }
   __syncthreads();
+  if (SEL) {  // the loads start only now: request all three rows at once
+    expert_rows(sel_e, erow);
+    load_row(0);
+    load_row(1);
+    load_row(2);
+  }
+
   uint32_t xr[32];
   {
     const int c0 = 32 * (lane >> 2) + 8 * (lane & 3);
-    const int swz = (c0 >> 3) & 7;
+    const int swz = lane & 7;  // (c0 >> 3) & 7
 #pragma unroll
     for (int q = 0; q < 8; q++) {
-      uint4 v = xs[c0 + (q ^ swz)];
+      const uint4 v = xs[c0 + (q ^ swz)];
       xr[4 * q] = v.x;
       xr[4 * q + 1] = v.y;
       xr[4 * q + 2] = v.z;
       xr[4 * q + 3] = v.w;
     }
   }
+  // block start parity decides both misalignments (rows are 16-byte aligned)
+  const uint32_t sh = ((lane >> 2) & 1) ? 0u : 2u;
+  const uint32_t rep16 = (uint32_t)(lane & 15) << 4;
+  float v[8];
+  v[0] = iq2_dot16(sg[0], sh, xr, gtab, stab, rep16);
+  v[4] = iq2_dot16(su[0], sh, xr, gtab, stab, rep16);
+  if (!SEL) load_row(2);
 #pragma unroll
-  for (int r = 0; r < 4; r++) {
-    float g = wave_sum(iq2_dot(sg[r], lane, xr, gt8, mt8));
-    float u = wave_sum(iq2_dot(su[r], lane, xr, gt8, mt8));
-    if (lane == 0) hv[8 * s + 4 * (w & 1) + r] = silu(g) * u;
+  for (int r = 1; r < kGuRows; r++) {
+    v[r] = iq2_dot16(sg[r], sh, xr, gtab, stab, rep16);
+    v[4 + r] = iq2_dot16(su[r], sh, xr, gtab, stab, rep16);
   }
-  __syncthreads();
-  if (w != 0) return;
-  // fixed-point quantisation of the 32 values (lanes 0..31 of wave 0)
-  float h = lane < 32 ? hv[lane] : 0.0f;
-  float m = wave_max(fabsf(h));
-  if (!(m <= 3.0e38f)) raise_fault(status, DS4MOE_FAULT_F16_RANGE);
-  float inv = m > 0.0f ? 1.0f / m : 0.0f;
-  float hn = h * inv;
-  float hp = dpp_f32<0xB1>(hn);  // partner lane t^1
-  int pk = __builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_i16(hn, hp));
-  int n = (int)(short)(pk & 0xFFFF);
-  // X_s: sums of n over aligned groups of 8 lanes
-  int xsum = n;
-  xsum += __builtin_amdgcn_mov_dpp(xsum, 0xB1, 0xF, 0xF, false);
-  xsum += __builtin_amdgcn_mov_dpp(xsum, 0x4E, 0xF, 0xF, false);
-  xsum += __builtin_amdgcn_mov_dpp(xsum, 0x141, 0xF, 0xF, false);
-  uint32_t* rec = hq + ((size_t)k * 64 + L) * kHqDwords;
-  if (lane < 32 && (lane & 1) == 0) rec[lane >> 1] = (uint32_t)pk;
-  if (lane < 32 && (lane & 7) == 0) rec[16 + (lane >> 3)] = (uint32_t)xsum;
-  if (lane == 0) rec[20] = __float_as_uint(m * (1.0f / 32767.0f));
+  v[3] = 0.0f;
+  v[7] = 0.0f;
+  const float tot = reduce8(v);
+  // lane 16*rho holds the gate total of row c[rho]; its up total sits 8 lanes
+  // further on (c = {0,2,1,3}; row 3 is padding)
+  const float upv = dpp_f32<0x128>(tot);
+  if ((lane & 15) == 0 && lane != 48) {
+    const int rho = lane >> 4;
+    const int r = (rho == 1) ? 2 : (rho == 2) ? 1 : rho;
+    a.h[row0 + r] = silu(tot) * upv;
+  }
 }
 
 // down + weighted combine (+ residual) for one token.
 // Grid H/8 workgroups of 6 waves: wave k handles routed slot k for 8 rows.
-__global__ __launch_bounds__(384) void k_down_q2k_b1(const uint32_t* __restrict__ hq,
+// Lane L = 8b + 4hh + c of a wave covers the 32 columns
+// i = 256b + 128hh + 32s + 8c + j (s < 4, j < 8) of every row: the 8 code
+// bytes qs[32hh + 8c .. +7] of block b hold exactly their 2-bit codes.  The
+// lane first turns its 32 SwiGLU values into 16-bit fixed point with one
+// scale, h_i ~= S n_i, n_i = round(32767 h_i / max|h|) (relative error below
+// 2^-16 of the chunk maximum; every later product is exact):
+//   nr[4s + m] = (n[8s + 2m], n[8s + 2m + 1]) as int16 pairs,
+//   xs[s] = sum_j n[8s + j]   (for the min term).
+__global__ __launch_bounds__(384) void k_down_q2k_b1(const float* __restrict__ h,
                                                      const uint8_t* __restrict__ down,
                                                      const int32_t* __restrict__ ids,
                                                      const float* __restrict__ wts, int E,
@@ -239,9 +353,22 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const uint32_t* __restrict_
                                                      uint32_t* status) {
   constexpr int R = 8;
   __shared__ float part[6][R];
-  const int tid = threadIdx.x, lane = tid & 63, k = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int k = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform slot
   const int b = lane >> 3, q8 = lane & 7, hh = q8 >> 2, c = q8 & 3;
-  int e = ids[k];
+  // the SwiGLU values first (the vector memory counter retires in order:
+  // waiting for them then never waits for the weights)
+  float hv[32];
+  {
+    const float4* hp = (const float4*)(h + k * kI + 256 * b + 128 * hh + 8 * c);
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const float4 p0 = hp[8 * s], p1 = hp[8 * s + 1];
+      hv[8 * s + 0] = p0.x; hv[8 * s + 1] = p0.y; hv[8 * s + 2] = p0.z; hv[8 * s + 3] = p0.w;
+      hv[8 * s + 4] = p1.x; hv[8 * s + 5] = p1.y; hv[8 * s + 6] = p1.z; hv[8 * s + 7] = p1.w;
+    }
+  }
+  int e = load_scalar_i32(ids, k);
   if (e < 0 || e >= E) {
     if (lane == 0 && blockIdx.x == 0) raise_fault(status, DS4MOE_FAULT_BAD_ID);
     e = 0;
@@ -258,22 +385,32 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const uint32_t* __restrict_
     sv[r] = *(const uint2*)(blk + soff);
     dd[r] = *(const uint32_t*)(blk + 80);
   }
-  const uint4* rp = (const uint4*)(hq + ((size_t)k * 64 + lane) * kHqDwords);
   uint32_t nr[16];
   int xn[4];
   float S;
   {
-    uint4 v0 = rp[0], v1 = rp[1], v2 = rp[2], v3 = rp[3], v4 = rp[4], v5 = rp[5];
-    nr[0] = v0.x; nr[1] = v0.y; nr[2] = v0.z; nr[3] = v0.w;
-    nr[4] = v1.x; nr[5] = v1.y; nr[6] = v1.z; nr[7] = v1.w;
-    nr[8] = v2.x; nr[9] = v2.y; nr[10] = v2.z; nr[11] = v2.w;
-    nr[12] = v3.x; nr[13] = v3.y; nr[14] = v3.z; nr[15] = v3.w;
-    xn[0] = (int)v4.x; xn[1] = (int)v4.y; xn[2] = (int)v4.z; xn[3] = (int)v4.w;
-    S = __uint_as_float(v5.x);
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) m = fmaxf(m, fabsf(hv[i]));
+    if (!(m <= 3.0e38f)) raise_fault(status, DS4MOE_FAULT_F16_RANGE);
+    const float inv = m > 0.0f ? 1.0f / m : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; q++)
+      nr[q] = (uint32_t)__builtin_bit_cast(
+          int, __builtin_amdgcn_cvt_pknorm_i16(hv[2 * q] * inv, hv[2 * q + 1] * inv));
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      int t = sdot2(nr[4 * s], 0x00010001u, 0);
+      t = sdot2(nr[4 * s + 1], 0x00010001u, t);
+      t = sdot2(nr[4 * s + 2], 0x00010001u, t);
+      xn[s] = sdot2(nr[4 * s + 3], 0x00010001u, t);
+    }
+    S = m * (1.0f / 32767.0f);
   }
-  const float wS = wts[k] * S;
+  const float wS = __int_as_float(load_scalar_i32((const int32_t*)wts, k)) * S;
   const uint32_t cb = (uint32_t)(c >> 1);
   const uint32_t ssel = cb | ((cb + 2) << 8) | ((cb + 4) << 16) | ((cb + 6) << 24);
+  float pr[R];
 #pragma unroll
   for (int r = 0; r < R; r++) {
     uint32_t p0 = vperm(0u, qv[r].x, 0x0C010C00u), p1 = vperm(0u, qv[r].x, 0x0C030C02u);
@@ -292,9 +429,12 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const uint32_t* __restrict_
       B += (int)((S4 >> (8 * s + 4)) & 0xFu) * xn[s];
     }
     float d = f16_bits_to_f32(dd[r] & 0xFFFFu), dmin = f16_bits_to_f32(dd[r] >> 16);
-    float p = wS * fmaf(-dmin, (float)B, d * (float)A);
-    p = wave_sum(p);
-    if (lane == 0) part[k][r] = p;
+    pr[r] = wS * fmaf(-dmin, (float)B, d * (float)A);
+  }
+  const float tot = reduce8(pr);
+  if ((lane & 7) == 0) {
+    const int rho = lane >> 4, eta = (lane >> 3) & 1;
+    part[k][4 * eta + ((rho == 1) ? 2 : (rho == 2) ? 1 : rho)] = tot;
   }
   __syncthreads();
   if (tid < R) {

@@ -230,22 +230,43 @@ __global__ __launch_bounds__(256) void k_route_score(RouteArgs a) {
   }
 }
 
-// Selection.  Grid T, one wave per token: reads the E key intervals written
-// by k_route_score (visible at the kernel boundary), picks the top K and
-// writes ids and gates.
-__global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
-  const int t = blockIdx.x, lane = threadIdx.x;
-  uint64_t comp[4];
+// Order-preserving map of a binary32 key to uint32 (larger key, larger code;
+// keys are never NaN or -0 here), 0 marking an expert out of the running.
+__device__ inline uint32_t key_order(float key) {
+  const uint32_t u = __float_as_uint(key);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+// Top-K selection for one token by one wave, from the E key intervals of
+// k_route_score: K rounds of "largest key, lowest expert index among equal
+// keys" (a wave maximum of the key codes, then the first expert whose code
+// equals it).  On return lane k < K holds slot k: expert id in e_out and gate
+// in w_out.  When report is set, an uncertified order raises the fault bit.
+// Deterministic: every wave that runs it on the same keys gets the same
+// answer.
+__device__ inline void select_wave(const float4* kb, int E, int K, float scale, uint32_t* status,
+                                   bool report, int& e_out, float& w_out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t ko[4];
   float sc[4], kl[4], kh[4];
   bool wide = false;
+#pragma unroll
   for (int j = 0; j < 4; j++) {
-    int ee = lane + 64 * j;
-    float4 v = ee < a.E ? a.kbuf[(size_t)t * a.E + ee] : make_float4(0, 0, 0, 0);
-    comp[j] = ee < a.E ? sel_composite(v.x, ee) : 0ull;
+    const int ee = lane + 64 * j;
+    const float4 v = ee < E ? kb[ee] : make_float4(0, 0, 0, 0);
+    ko[j] = ee < E ? key_order(v.x) : 0u;
     kl[j] = v.y;
     kh[j] = v.z;
     sc[j] = v.w;
-    wide |= ee < a.E && (v.y != v.z);
+    wide |= ee < E && (v.y != v.z);
   }
   wide = __any(wide);
   int sel_e[kMaxRouteK];
@@ -253,17 +274,22 @@ __global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
   bool ok = true;
   float prev_lo = 0.0f;
   int prev_e = -1;
-  for (int k = 0; k < a.K; k++) {
-    uint64_t best = umax64(umax64(comp[0], comp[1]), umax64(comp[2], comp[3]));
-    best = wave_max_u64(best);
-    const int be = 0xFFFF - (int)(uint32_t)(best & 0xFFFFu);
+  for (int k = 0; k < K; k++) {
+    const uint32_t m = wave_max_u32(max(max(ko[0], ko[1]), max(ko[2], ko[3])));
+    int be = 0;
+#pragma unroll
+    for (int j = 3; j >= 0; j--) {
+      const unsigned long long bal = __ballot(ko[j] == m);
+      if (bal) be = 64 * j + __ffsll((long long)bal) - 1;
+    }
     const int owner = be & 63, slot = be >> 6;
+#pragma unroll
     for (int j = 0; j < 4; j++)
-      if (lane + 64 * j == be) comp[j] = 0ull;
+      if (lane + 64 * j == be) ko[j] = 0u;
     sel_e[k] = be;
     sel_s[k] = readlane_f32(pick4(sc, slot), owner);
     if (wide) {
-      float lo = readlane_f32(pick4(kl, slot), owner), hi = readlane_f32(pick4(kh, slot), owner);
+      const float lo = readlane_f32(pick4(kl, slot), owner), hi = readlane_f32(pick4(kh, slot), owner);
       if (prev_e >= 0 && !(prev_lo > hi || (prev_lo == hi && prev_e < be))) ok = false;
       prev_lo = lo;
       prev_e = be;
@@ -271,19 +297,37 @@ __global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
   }
   if (wide) {
     // the last selected expert must precede every unselected one
+#pragma unroll
     for (int j = 0; j < 4; j++) {
-      int ee = lane + 64 * j;
-      if (comp[j] != 0ull && !(prev_lo > kh[j] || (prev_lo == kh[j] && prev_e < ee))) ok = false;
+      const int ee = lane + 64 * j;
+      if (ee < E && ko[j] != 0u && !(prev_lo > kh[j] || (prev_lo == kh[j] && prev_e < ee)))
+        ok = false;
     }
-    if (__any(!ok) && lane == 0) raise_fault(a.status, DS4MOE_FAULT_UNCERTIFIED);
+    if (__any(!ok) && lane == 0 && report) raise_fault(status, DS4MOE_FAULT_UNCERTIFIED);
   }
   double ssum = 0.0;
-  for (int k = 0; k < a.K; k++) ssum += (double)sel_s[k];
-  for (int k = 0; k < a.K; k++)
+  for (int k = 0; k < K; k++) ssum += (double)sel_s[k];
+  e_out = 0;
+  w_out = 0.0f;
+  for (int k = 0; k < K; k++)
     if (lane == k) {
-      a.ids[(size_t)t * a.K + k] = sel_e[k];
-      a.wts[(size_t)t * a.K + k] = (float)((double)a.scale * (double)sel_s[k] / ssum);
+      e_out = sel_e[k];
+      w_out = (float)((double)scale * (double)sel_s[k] / ssum);
     }
+}
+
+// Selection kernel.  Grid T, one wave per token: reads the key intervals
+// written by k_route_score (visible at the kernel boundary), picks the top K
+// and writes ids and gates.
+__global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  int e;
+  float w;
+  select_wave(a.kbuf + (size_t)t * a.E, a.E, a.K, a.scale, a.status, true, e, w);
+  if (lane < a.K) {
+    a.ids[(size_t)t * a.K + lane] = e;
+    a.wts[(size_t)t * a.K + lane] = w;
+  }
 }
 
 // Hash routing: one thread per token.  Invalid token ids or table rows
