@@ -310,6 +310,136 @@ def bench_stack(args):
     return res
 
 
+def bench_batched(args, which):
+    """Batched decode (8 correlated tokens, learned router, Q8_0 shared expert:
+    one ds4moe_layer call per step) or prefill (512 tokens with Zipf-routed
+    experts given: one ds4moe_expert_ffn call per step).  Timed like
+    decode-b1: hip-graph replay of the steps, then eager steps with per-launch
+    events."""
+    import numpy as np
+    import torch
+
+    import bit_quantized_expert_ds4moe_amd as ds4
+    import ds4gen as g
+    from ds4gen.device import make_layer, to_dev
+
+    prefill = which == "prefill-512"
+    w = g.WORKLOADS[3 if prefill else 2]
+    T = w.T
+    log("building layer tensors (%s)" % w.name)
+    lt = make_layer(w, 0)
+    ex = ds4.experts(lt.gate.data_ptr(), lt.up.data_ptr(), lt.down.data_ptr(), w.I,
+                     (w.gate_qt, w.up_qt, w.down_qt), grid=lt.grid.data_ptr())
+    sh = None
+    if w.shared:
+        sh = ds4.experts(lt.shared[0].data_ptr(), lt.shared[1].data_ptr(), lt.shared[2].data_ptr(),
+                         w.I, (g.Q8_0, g.Q8_0, g.Q8_0))
+    shp = ds4.shape(w.H, w.I, w.E, w.K, 1.5)
+    nb = ds4.workspace_size(shp, T)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    n_batches = 1 if prefill else args.warmup + args.steps
+    x = to_dev(g.activations(w, n_tok=T * n_batches))
+    out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    row = w.H * 2
+    if prefill:
+        ids_h, wts_h = g.zipf_routing(w.seed, T, w.E, w.K)
+        ids, wts = to_dev(ids_h), to_dev(wts_h)
+        touched = int(np.unique(ids_h).size)
+
+        def step(i, st):
+            ds4.expert_ffn(shp, ex, None, x.data_ptr(), ds4.BF16, T, ids.data_ptr(), wts.data_ptr(),
+                           out.data_ptr(), None, ws.data_ptr(), nb, st)
+    else:
+        desc = ds4.layer_desc(ds4.router(w=lt.router_w.data_ptr(), w_dtype=ds4.F16,
+                                         bias=lt.bias.data_ptr()), ex, shared=sh)
+        ids_d = torch.empty((n_batches, T, w.K), dtype=torch.int32, device="cuda")
+
+        def step(i, st):
+            ds4.layer(shp, desc, x.data_ptr() + i * T * row, ds4.BF16, None, out.data_ptr(), None, T,
+                      ids_d[i].data_ptr(), None, None, ws.data_ptr(), nb, st)
+
+    st = torch.cuda.current_stream().cuda_stream
+    step(0, st)
+    assert ds4.check(ws.data_ptr(), st) == 0
+
+    def capture(first, count):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            cs = torch.cuda.current_stream().cuda_stream
+            for j in range(count):
+                step(0 if prefill else first + j, cs)
+        return gr
+
+    g_warm = capture(0, args.warmup)
+    g_main = capture(args.warmup, args.steps)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g_main.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert ds4.check(ws.data_ptr(), st) == 0
+    log("timed %d steps: %.3f ms" % (args.steps, ms))
+    if not prefill:
+        touched_per = [int(np.unique(a).size) for a in ids_d[args.warmup:].cpu().numpy()]
+        touched = float(np.mean(touched_per))
+
+    classes = {"permute": ds4.K_PERMUTE, "gateup": ds4.K_GATEUP, "down": ds4.K_DOWN,
+               "combine": ds4.K_OTHER}
+    if not prefill:
+        classes["route"] = ds4.K_ROUTE
+    n_prof = min(args.steps, 50)
+    evs = {c: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_prof)] for c in classes}
+    handles = {c: [(event_handle(a), event_handle(b)) for a, b in evs[c]] for c in classes}
+    torch.cuda.synchronize()
+    torch.cuda._sleep(args.sleep_cycles)
+    for j in range(n_prof):
+        for c, k in classes.items():
+            ds4.profile_events(k, handles[c][j][0], handles[c][j][1])
+        step(0 if prefill else args.warmup + j, st)
+    for k in classes.values():
+        ds4.profile_events(k, None, None)
+    torch.cuda.synchronize()
+    kern_us = {c: float(np.mean([a.elapsed_time(b) for a, b in evs[c]]) * 1e3) for c in classes}
+    log("kernel averages (us):", kern_us)
+
+    per_expert = w.expert_bytes()
+    gateup_expert = 2 * w.blocks_per_expert["gate"] * g.BLOCK_BYTES[w.gate_qt]
+    sh_bytes = 3 * w.I * w.H // 32 * g.BLOCK_BYTES[g.Q8_0] if w.shared else 0
+    step_bytes = touched * per_expert + sh_bytes
+    sec = ms * 1e-3 / args.steps
+    flops = 2.0 * T * (3 * w.H * w.I) * (w.K + (1 if w.shared else 0))
+    gu_bytes = touched * gateup_expert + (2 * sh_bytes // 3)
+    gu_flops = 2.0 * T * (2 * w.H * w.I) * (w.K + (1 if w.shared else 0))
+    gu_s = kern_us["gateup"] * 1e-6
+    res = {
+        "metric": ("prefill tokens/s through one routed-expert layer" if prefill
+                   else "batched-decode tokens/s through one routed-expert layer"),
+        "value": round(T / sec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "tokens_per_step": T, "hidden": w.H, "inter": w.I,
+                   "experts": w.E, "top_k": w.K, "shared_q8_0": bool(w.shared),
+                   "experts_touched_per_step": touched,
+                   "routing": "given Zipf(1.1)" if prefill else "learned router"},
+        "expert_gbs": round(step_bytes / sec / 1e9, 1),
+        "expert_hbm_frac": round(step_bytes / sec / 1e9 / PEAK_HBM_GBS, 4),
+        "mfma_tflops": round(flops / sec / 1e12, 2),
+        "mfma_frac": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "roofline": {"bound": "hbm", "kernel": "k_grouped_gateup",
+                     "achieved": round(gu_bytes / gu_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gu_bytes / gu_s / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": None, "bytes_per_launch": int(gu_bytes),
+                     "mfma_tflops": round(gu_flops / gu_s / 1e12, 2)},
+    }
+    return res
+
+
 def cpu_baseline_stack(w, n_layers):
     """The oracle on one decode step through the first n_layers layers
     (normalisation, routing, experts, residual), scaled to 43 layers."""
@@ -384,7 +514,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 2000 tokens for decode-b1, 256 for stack-43)")
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode-b1", choices=["decode-b1", "stack-43"])
+    ap.add_argument("--workload", default="decode-b1",
+                    choices=["decode-b1", "stack-43", "decode-b8", "prefill-512"])
     ap.add_argument("--layer-copies", type=int, default=1,
                     help="rotate over this many independently seeded layers")
     ap.add_argument("--cpu-sample", type=int, default=None,
@@ -402,10 +533,11 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     stack = args.workload == "stack-43"
+    batched = args.workload in ("decode-b8", "prefill-512")
     if args.steps is None:
-        args.steps = 256 if stack else 2000
+        args.steps = 256 if stack else 200 if batched else 2000
     if args.warmup is None:
-        args.warmup = 8 if stack else 200
+        args.warmup = 8 if stack else 20 if batched else 200
     if args.cpu_sample is None:
         args.cpu_sample = 6 if stack else 3
     import torch
@@ -423,6 +555,8 @@ def main():
         del src, dst
     if args.workload == "stack-43":
         res = bench_stack(args)
+    elif args.workload in ("decode-b8", "prefill-512"):
+        res = bench_batched(args, args.workload)
     else:
         res = bench_decode_b1(args)
     print(json.dumps(res), flush=True)
