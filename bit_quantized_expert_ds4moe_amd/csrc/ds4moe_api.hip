@@ -1,6 +1,7 @@
 // ds4moe_api.hip -- C ABI of libds4moe (declared in include/ds4moe.h):
 // argument checks, workspace layout and kernel dispatch.  Built as one
 // translation unit with the kernel sources.
+#include <hip/hip_ext.h>
 #include <string.h>
 
 #include "dev_common.h"
@@ -70,19 +71,50 @@ ds4moe_status launched() {
   return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;
 }
 
-// Profiling events per kernel class (ds4moe_profile_events).
+// Profiling events per kernel class (ds4moe_profile_events).  While a class
+// scope is open, kernels are launched with hipExtLaunchKernelGGL so that the
+// events take the execution timestamps of the kernels themselves: the start
+// event the first kernel's start, the stop event the last kernel's end.
 hipEvent_t g_prof[DS4MOE_K_CLASSES][2] = {};
 
 struct ProfScope {
+  static ProfScope* active;
   int cls;
-  hipStream_t st;
-  ProfScope(int c, hipStream_t s) : cls(c), st(s) {
-    if (g_prof[cls][0]) (void)hipEventRecord(g_prof[cls][0], st);
-  }
-  ~ProfScope() {
-    if (g_prof[cls][1]) (void)hipEventRecord(g_prof[cls][1], st);
-  }
+  bool started = false;
+  ProfScope* prev;
+  ProfScope(int c, hipStream_t) : cls(c), prev(active) { active = this; }
+  ~ProfScope() { active = prev; }
 };
+ProfScope* ProfScope::active = nullptr;
+
+template <typename... P, typename... A>
+void launch_k(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shm, hipStream_t st,
+              A... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (ProfScope* p = ProfScope::active) {
+    e1 = g_prof[p->cls][1];
+    if (!p->started) e0 = g_prof[p->cls][0];
+    p->started = true;
+  }
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, st, e0, e1, 0u, static_cast<P>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shm, st, static_cast<P>(args)...);
+}
+
+inline ds4moe_status launch_permute(const int32_t* ids, int n, int E, int32_t* counts,
+                                    int32_t* offsets, int32_t* perm, int32_t* inv,
+                                    uint32_t* status, hipStream_t st) {
+  int n2 = 2;
+  while (n2 < n) n2 <<= 1;
+  size_t lds = (size_t)n2 * 4;
+  if (hipFuncSetAttribute((const void*)k_permute, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds) != hipSuccess)
+    return DS4MOE_EDEVICE;
+  launch_k(k_permute, dim3(1), dim3(1024), lds, st, ids, n, E, counts, offsets, perm, inv,
+                     status);
+  return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;
+}
 
 template <typename T>
 T* at(void* ws, size_t off) {
@@ -97,7 +129,7 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
   uint32_t* status = at<uint32_t>(ws, L.status);
   ProfScope prof(DS4MOE_K_ROUTE, st);
   if (r.tid2eid) {
-    hipLaunchKernelGGL(k_route_hash, dim3((T + 255) / 256), dim3(256), 0, st, tok, r.tid2eid,
+    launch_k(k_route_hash, dim3((T + 255) / 256), dim3(256), 0, st, tok, r.tid2eid,
                        r.vocab, s.n_expert, s.top_k, T, s.routed_scale, ids, wts, status);
     return launched();
   }
@@ -127,16 +159,16 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
                            : (uintptr_t)x % 16 == 0);
   const dim3 grid(s.n_expert, T);
   if (vec && norm_w)
-    hipLaunchKernelGGL((k_route_score<true, true>), grid, dim3(256), 0, st, a);
+    launch_k(k_route_score<true, true>, grid, dim3(256), 0, st, a);
   else if (vec)
-    hipLaunchKernelGGL((k_route_score<false, true>), grid, dim3(256), 0, st, a);
+    launch_k(k_route_score<false, true>, grid, dim3(256), 0, st, a);
   else if (norm_w)
-    hipLaunchKernelGGL((k_route_score<true, false>), grid, dim3(256), 0, st, a);
+    launch_k(k_route_score<true, false>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_route_score<false, false>), grid, dim3(256), 0, st, a);
+    launch_k(k_route_score<false, false>, grid, dim3(256), 0, st, a);
   ds4moe_status rc = launched();
   if (rc != DS4MOE_OK || !select) return rc;
-  hipLaunchKernelGGL(k_route_select, dim3(T), dim3(64), 0, st, a);
+  launch_k(k_route_select, dim3(T), dim3(64), 0, st, a);
   return launched();
 }
 
@@ -213,15 +245,15 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   {
     ProfScope prof(DS4MOE_K_GATEUP, st);
     if (kbuf)
-      hipLaunchKernelGGL(k_gateup_b1<true>, dim3(kGuBlocks), dim3(kGuWaves * 64), 0, st, g);
+      launch_k(k_gateup_b1<true>, dim3(kGuBlocks), dim3(kGuWaves * 64), 0, st, g);
     else
-      hipLaunchKernelGGL(k_gateup_b1<false>, dim3(kGuBlocks), dim3(kGuWaves * 64), 0, st, g);
+      launch_k(k_gateup_b1<false>, dim3(kGuBlocks), dim3(kGuWaves * 64), 0, st, g);
   }
   ds4moe_status rc = launched();
   if (rc != DS4MOE_OK) return rc;
   {
     ProfScope prof(DS4MOE_K_DOWN, st);
-    hipLaunchKernelGGL(k_down_q2k_b1, dim3(kH / 8), dim3(384), 0, st, h, (const uint8_t*)ex.down,
+    launch_k(k_down_q2k_b1, dim3(kH / 8), dim3(384), 0, st, h, (const uint8_t*)ex.down,
                        kbuf ? ids : ids_in, wts, s.n_expert, out, residual, status);
   }
   return launched();
@@ -248,7 +280,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       ProfScope prof(DS4MOE_K_PERMUTE, st);
       rc = launch_permute(ids, TK, E, counts, offsets, perm, inv, status, st);
       if (rc != DS4MOE_OK) return rc;
-      hipLaunchKernelGGL(k_make_items, dim3(1), dim3(64), 0, st, counts, offsets, E, TK, T,
+      launch_k(k_make_items, dim3(1), dim3(64), 0, st, counts, offsets, E, TK, T,
                          sh ? 1 : 0, items, n_items);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
@@ -284,18 +316,18 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     const int imax = g.I > g.sh_I ? g.I : g.sh_I;
     {
       ProfScope prof(DS4MOE_K_GATEUP, st);
-      hipLaunchKernelGGL(k_grouped_gateup, dim3((imax + kNT - 1) / kNT, mi), dim3(256), 0, st, g);
+      launch_k(k_grouped_gateup, dim3((imax + kNT - 1) / kNT, mi), dim3(256), 0, st, g);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     {
       ProfScope prof(DS4MOE_K_DOWN, st);
-      hipLaunchKernelGGL(k_grouped_down, dim3(s.hidden / kNT, mi), dim3(256), 0, st, g);
+      launch_k(k_grouped_down, dim3(s.hidden / kNT, mi), dim3(256), 0, st, g);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     {
       ProfScope prof(DS4MOE_K_OTHER, st);
       const size_t n = (size_t)T * s.hidden;
-      hipLaunchKernelGGL(k_grouped_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+      launch_k(k_grouped_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                          (const float*)g.y, (const int32_t*)inv, wts, T, K, s.hidden, sh ? 1 : 0, out,
                          residual);
     }
@@ -344,20 +376,20 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
   const int imax = a.I > a.sh_I ? a.I : a.sh_I;
   {
     ProfScope prof(DS4MOE_K_GATEUP, st);
-    hipLaunchKernelGGL(k_generic_gateup, dim3((imax + 3) / 4, np), dim3(256), 0, st, a);
+    launch_k(k_generic_gateup, dim3((imax + 3) / 4, np), dim3(256), 0, st, a);
   }
   ds4moe_status rc = launched();
   if (rc != DS4MOE_OK) return rc;
   {
     ProfScope prof(DS4MOE_K_DOWN, st);
-    hipLaunchKernelGGL(k_generic_down, dim3((s.hidden + 3) / 4, np), dim3(256), 0, st, a);
+    launch_k(k_generic_down, dim3((s.hidden + 3) / 4, np), dim3(256), 0, st, a);
   }
   rc = launched();
   if (rc != DS4MOE_OK) return rc;
   size_t n = (size_t)T * s.hidden;
   {
     ProfScope prof(DS4MOE_K_OTHER, st);
-    hipLaunchKernelGGL(k_generic_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+    launch_k(k_generic_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   }
   return launched();
 }
@@ -462,7 +494,7 @@ DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_la
   ds4moe_status rc;
   if (norm && r.tid2eid) {
     ProfScope prof(DS4MOE_K_OTHER, stream);
-    hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(n_tok), dim3(256), 0, stream, residual, desc->norm_w,
+    launch_k(k_rmsnorm_bf16, dim3(n_tok), dim3(256), 0, stream, residual, desc->norm_w,
                        desc->norm_eps, shape->hidden, xn);
     if ((rc = launched()) != DS4MOE_OK) return rc;
   }

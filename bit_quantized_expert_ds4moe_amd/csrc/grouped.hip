@@ -397,20 +397,6 @@ __global__ void k_grouped_combine(const float* y, const int32_t* inv, const floa
   else out[idx] = acc;
 }
 
-inline ds4moe_status launch_permute(const int32_t* ids, int n, int E, int32_t* counts,
-                                    int32_t* offsets, int32_t* perm, int32_t* inv,
-                                    uint32_t* status, hipStream_t st) {
-  int n2 = 2;
-  while (n2 < n) n2 <<= 1;
-  size_t lds = (size_t)n2 * 4;
-  if (hipFuncSetAttribute((const void*)k_permute, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) != hipSuccess)
-    return DS4MOE_EDEVICE;
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), lds, st, ids, n, E, counts, offsets, perm, inv,
-                     status);
-  return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;
-}
-
 // The grouped path needs bf16 x, 256-multiple shapes and formats it knows.
 inline bool grouped_eligible(const ds4moe_shape& s, const ds4moe_experts& ex,
                              const ds4moe_experts* sh, const void* x, int32_t x_dt, int32_t T) {
