@@ -310,18 +310,31 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       g.sh_I = sh->inter;
     }
     g.grid = ex.grid ? ex.grid : (sh ? sh->grid : nullptr);
-    g.h = at<float>(ws, L.h);
+    {
+      const size_t np = (size_t)TK + (size_t)T;
+      uint16_t* hbase = at<uint16_t>(ws, L.h);
+      g.hh = hbase;
+      g.hl = hbase + np * (size_t)g.I;
+      uint16_t* sbase = at<uint16_t>(ws, L.hb);
+      g.hsh = sbase;
+      g.hsl = sbase + np * (size_t)(g.I / 16);
+    }
     g.y = at<float>(ws, L.y);
     g.status = status;
     const int imax = g.I > g.sh_I ? g.I : g.sh_I;
     {
       ProfScope prof(DS4MOE_K_GATEUP, st);
-      launch_k(k_grouped_gateup, dim3((imax + kNT - 1) / kNT, mi), dim3(256), 0, st, g);
+      const bool iq2 = g.qt_g == DS4MOE_IQ2_XXS && g.qt_u == DS4MOE_IQ2_XXS && g.I % kGNF == 0;
+      if (iq2) launch_k(k_grouped_gateup_iq2, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
+      if (!iq2 || sh)
+        launch_k(k_grouped_gateup, dim3((imax + kNT - 1) / kNT, mi), dim3(256), 0, st, g);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     {
       ProfScope prof(DS4MOE_K_DOWN, st);
-      launch_k(k_grouped_down, dim3(s.hidden / kNT, mi), dim3(256), 0, st, g);
+      const bool q2k = g.qt_d == DS4MOE_Q2_K && g.H % kDNF == 0;
+      if (q2k) launch_k(k_grouped_down_q2k, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
+      if (!q2k || sh) launch_k(k_grouped_down, dim3(s.hidden / kNT, mi), dim3(256), 0, st, g);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     {

@@ -31,6 +31,11 @@ namespace ds4 {
 
 constexpr int kMC = 64;   // rows (pairs) per work item
 constexpr int kNT = 64;   // output features per block (16 per wave)
+constexpr int kGW = 8;             // pipelined IQ2_XXS gate/up: waves per block
+constexpr int kGNF = 16 * kGW;     // and features per block
+constexpr int kGStage = 128;       // and K columns per stage
+constexpr int kDW = 8;             // pipelined Q2_K down: waves per block
+constexpr int kDNF = 16 * kDW;     // and output features per block
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -77,13 +82,54 @@ struct GroupArgs {
   const uint8_t *sh_gate, *sh_up, *sh_down;
   int sh_qt_g, sh_qt_u, sh_qt_d, sh_I;
   const uint8_t* grid;
-  float* h;                 // [T*K + T][I] fp32
+  uint16_t* hh;             // [T*K + T][I] SwiGLU rows, binary16 high part
+  uint16_t* hl;             // [T*K + T][I] binary16 low part (h - hi, rounded)
+  uint16_t* hsh;            // [T*K + T][I/16] sums of 16 consecutive features, high part
+  uint16_t* hsl;            // [T*K + T][I/16] low part
   float* y;                 // [T*K + T][H] fp32
   uint32_t* status;
 };
 
 __device__ inline int row_token(const GroupArgs& a, int row) {
   return row < a.T * a.K ? a.perm[row] / a.K : row - a.T * a.K;
+}
+
+// SwiGLU epilogue of the grouped gate/up kernels.  Lane (column n = lane%16,
+// quarter q) holds rows 4q + r of each 16-row tile.  The down kernels take h
+// as binary16 high + low parts (relative error < 2^-21) and, for the Q2_K
+// min term, the sum of each 16 consecutive features (a wave's tile) split
+// the same way; the sum runs over the 16 lanes of a DPP row in a fixed order.
+__device__ inline void swiglu_store(const GroupArgs& a, int row0, int nrows, int mtiles, int n,
+                                    int q, const f32x4_t* accg, const f32x4_t* accu) {
+  bool ok = true;
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) {
+    if (mt >= mtiles) break;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int m = 16 * mt + 4 * q + r;
+      const float v = m < nrows ? silu(accg[mt][r]) * accu[mt][r] : 0.0f;
+      ok &= fabsf(v) <= 65504.0f;
+      const uint32_t hi = f32_to_f16_bits(v);
+      const uint32_t lo = f32_to_f16_bits(v - f16_bits_to_f32(hi));
+      float sum = v;
+      sum += dpp_f32<0xB1>(sum);
+      sum += dpp_f32<0x4E>(sum);
+      sum += dpp_f32<0x141>(sum);
+      sum += dpp_f32<0x140>(sum);
+      if (m < nrows) {
+        const size_t row = (size_t)(row0 + m);
+        a.hh[row * a.I + n] = (uint16_t)hi;
+        a.hl[row * a.I + n] = (uint16_t)lo;
+        if ((n & 15) == 0) {
+          const uint32_t shi = f32_to_f16_bits(sum);
+          a.hsh[row * (a.I / 16) + n / 16] = (uint16_t)shi;
+          a.hsl[row * (a.I / 16) + n / 16] = (uint16_t)f32_to_f16_bits(sum - f16_bits_to_f32(shi));
+        }
+      }
+    }
+  }
+  if (!ok) raise_fault(a.status, DS4MOE_FAULT_F16_RANGE);
 }
 
 // 8 bytes at a 2-byte-aligned address (Q8_0 codes).
@@ -167,6 +213,8 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
   if (item >= *a.n_items) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   const bool sh = e == a.E;
+  // routed items with IQ2_XXS gate and up run in k_grouped_gateup_iq2
+  if (!sh && a.qt_g == DS4MOE_IQ2_XXS && a.qt_u == DS4MOE_IQ2_XXS && a.I % kGNF == 0) return;
   const int I = sh ? a.sh_I : a.I;
   const int n0 = blockIdx.x * kNT;
   if (n0 >= I) return;
@@ -220,15 +268,161 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
     }
     __syncthreads();
   }
-  const int hstride = a.I;
+  swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu);
+}
+
+// ---------------------------------------------------------------------------
+// gate/up for routed items with IQ2_XXS gate and up: software-pipelined.
+// Grid (I/128, max_items), 512 threads; wave w owns features n0 + 16w .. +15
+// (gate and up).  The K dimension runs in stages of 128 columns (half an
+// IQ2_XXS block: four 32-column groups).  While stage s is multiplied, the
+// x tile and the weight bytes of stage s+1 are already in flight: x rows go
+// through registers into the other half of a double-buffered LDS tile, the
+// weight bytes (nine aligned dwords covering the four groups, plus the word
+// holding d) sit in a second register set.  One barrier per stage.
+
+struct Iq2Stage {
+  uint32_t D[9];
+  uint32_t dw;
+};
+
+// Stage s of one IQ2_XXS row (row start 16-byte aligned).  The nine dwords
+// cover the 32 group bytes, which start 2 bytes into a word for even blocks;
+// for odd blocks the ninth word is fetched from inside the range instead, so
+// that the last row of a tensor is never overrun.
+__device__ inline void iq2_stage_load(const uint8_t* __restrict__ row, int s, Iq2Stage& st) {
+  const int kb = s >> 1;
+  const int start = kIq2Bytes * kb + 2 + 32 * (s & 1);
+  const int sh = start & 3;
+  const uint32_t* p = (const uint32_t*)(row + (start - sh));
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++)
+  for (int i = 0; i < 8; i++) st.D[i] = p[i];
+  st.D[8] = p[sh ? 8 : 7];
+  st.dw = *(const uint32_t*)(row + ((kIq2Bytes * kb) & ~3));
+}
+
+// B fragment of group j (0..3) of a stage for this lane's quarter q: the grid
+// entry's bf16 pairs with the signs applied; the group scale d(2s+1)/8.
+__device__ inline bf16x8_t iq2_stage_frag(const Iq2Stage& st, int s, int j, int q, uint32_t rep16,
+                                          const uint8_t* gtab, const uint8_t* stab, float& scale) {
+  const uint32_t sh = (s & 2) ? 0u : 2u;  // (2 kb + 2) & 3 with kb = s >> 1
+  const uint32_t idxw = align_bytes(st.D[2 * j + 1], st.D[2 * j], sh);
+  const uint32_t sw = align_bytes(st.D[2 * j + 2], st.D[2 * j + 1], sh);
+  const float d = f16_bits_to_f32((s & 2) ? (st.dw >> 16) : (st.dw & 0xFFFFu));
+  scale = d * (float)((((sw & 0xF0000000u) | 0x08000000u) >> 24)) * 0.015625f;
+  const uint32_t gi = (idxw >> (8 * q)) & 0xFFu;
+  const uint32_t si = (sw >> (7 * q)) & 0x7Fu;
+  const uint4 gv = *(const uint4*)(gtab + ((gi << 7) | rep16));
+  const uint4 mv = *(const uint4*)(stab + ((si << 7) | rep16));
+  return __builtin_bit_cast(bf16x8_t, make_uint4(gv.x ^ mv.x, gv.y ^ mv.y, gv.z ^ mv.z, gv.w ^ mv.w));
+}
+
+__global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
+  __shared__ uint4 xt[2][kMC * 16];      // 2 x 16 KB
+  __shared__ uint4 gt8[256 * 8];         // 32 KB: entry e copy p at (e << 7) | (p << 4)
+  __shared__ uint4 mt8[128 * 8];         // 16 KB
+  __shared__ int tok[kMC];
+  const int item = blockIdx.y;
+  if (item >= *a.n_items) return;
+  const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
+  if (e >= a.E) return;  // shared-expert items run in k_grouped_gateup
+  const int n0 = blockIdx.x * kGNF;
+  if (n0 >= a.I) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = lane >> 4;
+  const int n = n0 + 16 * w + (lane & 15);
+  const uint32_t rep16 = (uint32_t)(lane & 7) << 4;
+  const int rowbytes = (a.H / 256) * kIq2Bytes;
+  const uint8_t* grow = a.gate + ((size_t)e * a.I + n) * rowbytes;
+  const uint8_t* urow = a.up + ((size_t)e * a.I + n) * rowbytes;
+  const int nst = a.H / kGStage;
+  const int mtiles = (nrows + 15) >> 4;
+
+  // stage 0 weights first: their latency overlaps the table build
+  Iq2Stage cg, cu;
+  iq2_stage_load(grow, 0, cg);
+  iq2_stage_load(urow, 0, cu);
+  if (tid < kMC) tok[tid] = tid < nrows ? row_token(a, row0 + tid) : -1;
+  if (tid < 256) {
+    const uint8_t* g = a.grid + 8 * tid;
+    uint32_t wv[4];
+    for (int m = 0; m < 4; m++)
+      wv[m] = (__float_as_uint((float)g[2 * m]) >> 16) |
+              (__float_as_uint((float)g[2 * m + 1]) & 0xFFFF0000u);
+    const uint4 v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    for (int j = 0; j < 8; j++) gt8[8 * tid + ((j + tid) & 7)] = v;
+  } else if (tid < 384) {
+    const int t = tid - 256;
+    const uint32_t s8 = (uint32_t)t | ((uint32_t)(__popc(t) & 1) << 7);
+    uint32_t wv[4];
+    for (int m = 0; m < 4; m++)
+      wv[m] = (((s8 >> (2 * m)) & 1u) << 15) | (((s8 >> (2 * m + 1)) & 1u) << 31);
+    const uint4 v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    for (int j = 0; j < 8; j++) mt8[8 * t + ((j + t) & 7)] = v;
+  }
+  __syncthreads();  // tok visible
+  // x tile of stage 0: chunk c = tid + 512 j -> row c >> 4, 16-byte column chunk c & 15
+  auto x_load = [&](int s, uint4* v) {
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      if (mt >= mtiles) break;
-      const int m = 16 * mt + 4 * q + r;
-      if (m < nrows) a.h[(size_t)(row0 + m) * hstride + n] = silu(accg[mt][r]) * accu[mt][r];
+    for (int j = 0; j < 2; j++) {
+      const int c = tid + 512 * j, m = c >> 4, ch = c & 15;
+      v[j] = m < nrows ? ((const uint4*)(a.x + (size_t)tok[m] * a.H + kGStage * s))[ch]
+                       : make_uint4(0, 0, 0, 0);
     }
+  };
+  auto x_store = [&](int buf, const uint4* v) {
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int c = tid + 512 * j, m = c >> 4, ch = c & 15;
+      xt[buf][m * 16 + (ch ^ (m & 7))] = v[j];
+    }
+  };
+  {
+    uint4 v[2];
+    x_load(0, v);
+    x_store(0, v);
+  }
+  __syncthreads();
+
+  f32x4_t accg[4], accu[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* gtab = (const uint8_t*)gt8;
+  const uint8_t* stab = (const uint8_t*)mt8;
+  for (int s = 0; s < nst; s++) {
+    const bool more = s + 1 < nst;
+    Iq2Stage ng, nu;
+    uint4 xv[2];
+    if (more) {
+      iq2_stage_load(grow, s + 1, ng);
+      iq2_stage_load(urow, s + 1, nu);
+      x_load(s + 1, xv);
+    }
+    const uint4* xb = xt[s & 1];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      float sg, su;
+      const bf16x8_t fg = iq2_stage_frag(cg, s, j, q, rep16, gtab, stab, sg);
+      const bf16x8_t fu = iq2_stage_frag(cu, s, j, q, rep16, gtab, stab, su);
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        if (mt >= mtiles) break;
+        const int m = 16 * mt + (lane & 15);
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, xb[m * 16 + ((4 * j + q) ^ (m & 7))]);
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4_t tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fg, z, 0, 0, 0);
+        const f32x4_t tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fu, z, 0, 0, 0);
+        accg[mt] += sg * tg;
+        accu[mt] += su * tu;
+      }
+    }
+    if (more) {
+      x_store((s + 1) & 1, xv);
+      cg = ng;
+      cu = nu;
+    }
+    __syncthreads();
+  }
+  swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu);
 }
 
 // down for one work item and 64 output features.  Grid (H/64, max_items).
@@ -243,6 +437,8 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
   if (item >= *a.n_items) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   const bool shr = e == a.E;
+  // routed Q2_K items run in k_grouped_down_q2k
+  if (!shr && a.qt_d == DS4MOE_Q2_K && a.H % kDNF == 0) return;
   const int I = shr ? a.sh_I : a.I;
   const int qd = shr ? a.sh_qt_d : a.qt_d;
   const uint8_t* D = shr ? a.sh_down : a.down;
@@ -255,43 +451,31 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
   f32x4_t acc[4];
   for (int mt = 0; mt < 4; mt++) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const size_t rowd = (size_t)ee * a.H + n;
-  bool range_ok = true;
   for (int kb = 0; kb < nb; kb++) {
-    // stage: thread -> (row m, 16-column sub-block j): 16 values
+    // stage: thread -> (row m, 16-column sub-block j): 16 values, high and low parts
     for (int c = tid; c < kMC * 16; c += 256) {
       const int m = c >> 4, j = c & 15;
-      float v[16];
+      uint4 h0 = make_uint4(0, 0, 0, 0), h1 = h0, l0 = h0, l1 = h0;
+      uint16_t sh16 = 0, sl16 = 0;
       if (m < nrows) {
-        const float4* hp = (const float4*)(a.h + (size_t)(row0 + m) * a.I + 256 * kb + 16 * j);
-        for (int u = 0; u < 4; u++) {
-          float4 f = hp[u];
-          v[4 * u] = f.x; v[4 * u + 1] = f.y; v[4 * u + 2] = f.z; v[4 * u + 3] = f.w;
-        }
-      } else {
-        for (int u = 0; u < 16; u++) v[u] = 0.f;
-      }
-      uint32_t hi[8], lo[8];
-      float s_sum = 0.f;
-      for (int u = 0; u < 8; u++) {
-        float x0 = v[2 * u], x1 = v[2 * u + 1];
-        range_ok &= fabsf(x0) <= 65504.f && fabsf(x1) <= 65504.f;
-        uint32_t h0 = f32_to_f16_bits(x0), h1 = f32_to_f16_bits(x1);
-        float r0 = x0 - f16_bits_to_f32(h0), r1 = x1 - f16_bits_to_f32(h1);
-        hi[u] = h0 | (h1 << 16);
-        lo[u] = f32_to_f16_bits(r0) | (f32_to_f16_bits(r1) << 16);
-        s_sum += x0 + x1;
+        const size_t row = (size_t)(row0 + m);
+        const uint4* hp = (const uint4*)(a.hh + row * a.I + 256 * kb + 16 * j);
+        const uint4* lp = (const uint4*)(a.hl + row * a.I + 256 * kb + 16 * j);
+        h0 = hp[0];
+        h1 = hp[1];
+        l0 = lp[0];
+        l1 = lp[1];
+        sh16 = a.hsh[row * (a.I / 16) + 16 * kb + j];
+        sl16 = a.hsl[row * (a.I / 16) + 16 * kb + j];
       }
       // two 16-byte chunks (8 values each) per sub-block
       const int c0 = 2 * j, c1 = 2 * j + 1;
-      ah[m * 32 + (c0 ^ (m & 7))] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      ah[m * 32 + (c1 ^ (m & 7))] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
-      al[m * 32 + (c0 ^ (m & 7))] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      al[m * 32 + (c1 ^ (m & 7))] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
-      // sub-block sum split hi/lo, stored at [m][j/4] half-lane (j%4)
-      uint32_t sh16 = f32_to_f16_bits(s_sum);
-      uint32_t sl16 = f32_to_f16_bits(s_sum - f16_bits_to_f32(sh16));
-      ((uint16_t*)sh_hi)[m * 16 + j] = (uint16_t)sh16;
-      ((uint16_t*)sh_lo)[m * 16 + j] = (uint16_t)sl16;
+      ah[m * 32 + (c0 ^ (m & 7))] = h0;
+      ah[m * 32 + (c1 ^ (m & 7))] = h1;
+      al[m * 32 + (c0 ^ (m & 7))] = l0;
+      al[m * 32 + (c1 ^ (m & 7))] = l1;
+      ((uint16_t*)sh_hi)[m * 16 + j] = sh16;
+      ((uint16_t*)sh_lo)[m * 16 + j] = sl16;
     }
     __syncthreads();
     const uint8_t* blk = D + (rowd * nb + kb) * bbd;
@@ -373,7 +557,160 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
     }
     __syncthreads();
   }
-  if (!range_ok) raise_fault(a.status, DS4MOE_FAULT_F16_RANGE);
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      if (mt >= mtiles) break;
+      const int m = 16 * mt + 4 * q + r;
+      if (m < nrows) a.y[(size_t)(row0 + m) * a.H + n] = acc[mt][r];
+    }
+}
+
+// down for routed items with Q2_K down weights: software-pipelined.
+// Grid (H/128, max_items), 512 threads; wave w owns output features
+// n0 + 16w .. +15.  Stages of 128 columns (half a Q2_K block: eight 16-value
+// sub-blocks).  The SwiGLU tile of stage s+1 (binary16 high and low parts,
+// as written by gate/up) and the weight words of stage s+1 are loaded while
+// stage s is multiplied.  Per sub-block: f16 MFMA 16x16x16 of the h parts
+// against the 2-bit codes read in place (binary16 subnormals 4^s q 2^-24,
+// exact), scaled by d sc 4^-s 2^24; once per block the mins: an MFMA of the
+// 16 sub-block sums against the min nibbles, scaled by dmin 2^24.
+
+struct Q2kStage {
+  uint32_t qa, qb;   // code bytes 32hf + 4q .. +3 and 32hf + 16 + 4q .. +3
+  uint4 sc;          // the block's 16 scale/min bytes
+  uint32_t dd;       // d | dmin << 16
+};
+
+__device__ inline void q2k_stage_load(const uint8_t* __restrict__ row, int s, int q, Q2kStage& st) {
+  const uint8_t* blk = row + kQ2kBytes * (s >> 1);
+  const int hf = s & 1;
+  st.qa = *(const uint32_t*)(blk + 16 + 32 * hf + 4 * q);
+  st.qb = *(const uint32_t*)(blk + 32 + 32 * hf + 4 * q);
+  st.sc = *(const uint4*)blk;
+  st.dd = *(const uint32_t*)(blk + 80);
+}
+
+__global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
+  __shared__ uint4 ah[kMC * 16];   // [m][16 chunks of 8 f16], high parts, 16 KB
+  __shared__ uint4 al[kMC * 16];   // low parts, 16 KB
+  const int item = blockIdx.y;
+  if (item >= *a.n_items) return;
+  const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
+  if (e >= a.E) return;  // shared-expert items run in k_grouped_down
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = lane >> 4;
+  const int n = blockIdx.x * kDNF + 16 * w + (lane & 15);
+  const int rowbytes = (a.I / 256) * kQ2kBytes;
+  const uint8_t* drow = a.down + ((size_t)e * a.H + n) * rowbytes;
+  const int nst = a.I / 128;
+  const int mtiles = (nrows + 15) >> 4;
+
+  Q2kStage cw;
+  q2k_stage_load(drow, 0, q, cw);
+  // SwiGLU tile of a stage: chunk c = tid + 512 j (j < 2) -> row c >> 4,
+  // 8-value chunk c & 15; high and low parts
+  auto h_load = [&](int s, uint4* v) {
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int c = tid + 512 * j, m = c >> 4, ch = c & 15;
+      if (m < nrows) {
+        const size_t off = (size_t)(row0 + m) * a.I + 128 * s + 8 * ch;
+        v[j] = *(const uint4*)(a.hh + off);
+        v[2 + j] = *(const uint4*)(a.hl + off);
+      } else {
+        v[j] = v[2 + j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto h_store = [&](const uint4* v) {
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int c = tid + 512 * j, m = c >> 4, ch = c & 15;
+      ah[m * 16 + (ch ^ (m & 7))] = v[j];
+      al[m * 16 + (ch ^ (m & 7))] = v[2 + j];
+    }
+  };
+  {
+    uint4 v[4];
+    h_load(0, v);
+    h_store(v);
+  }
+  __syncthreads();
+
+  f32x4_t acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nst; s++) {
+    const bool more = s + 1 < nst;
+    Q2kStage nw;
+    uint4 hv[4];
+    if (more) {
+      q2k_stage_load(drow, s + 1, q, nw);
+      h_load(s + 1, hv);
+    }
+    const int hf = s & 1;
+    const float d = f16_bits_to_f32(cw.dd & 0xFFFFu);
+    // 16-bit lanes holding whole code bytes: (byte0, byte1), (byte2, byte3)
+    const uint32_t pa0 = vperm(0u, cw.qa, 0x0C010C00u), pa1 = vperm(0u, cw.qa, 0x0C030C02u);
+    const uint32_t pb0 = vperm(0u, cw.qb, 0x0C010C00u), pb1 = vperm(0u, cw.qb, 0x0C030C02u);
+    const uint32_t scw[4] = {cw.sc.x, cw.sc.y, cw.sc.z, cw.sc.w};
+#pragma unroll
+    for (int sb = 0; sb < 8; sb++) {
+      // sub-block 8hf + sb of the block: shift s2 = sb >> 1, half p = sb & 1
+      const int s2 = sb >> 1, p = sb & 1;
+      const uint32_t mk = 0x00030003u << (2 * s2);
+      const uint32_t b0 = (p ? pb0 : pa0) & mk, b1 = (p ? pb1 : pa1) & mk;
+      const f16x4_t bf = __builtin_bit_cast(f16x4_t, make_uint2(b0, b1));
+      const int j = 8 * hf + sb;
+      const uint32_t scb = (scw[j >> 2] >> (8 * (j & 3))) & 0xFu;
+      const float mult = d * (float)scb * (16777216.0f / (float)(1 << (2 * s2)));
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        if (mt >= mtiles) break;
+        const int m = 16 * mt + (lane & 15);
+        // A: values 16 sb + 4q .. +3 = half (q & 1) of chunk 2 sb + (q >> 1)
+        const int slot = m * 16 + ((2 * sb + (q >> 1)) ^ (m & 7));
+        const uint4 ch = ah[slot], cl = al[slot];
+        const uint2 fh = (q & 1) ? make_uint2(ch.z, ch.w) : make_uint2(ch.x, ch.y);
+        const uint2 fl = (q & 1) ? make_uint2(cl.z, cl.w) : make_uint2(cl.x, cl.y);
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, fh), bf, z, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, fl), bf, t, 0, 0, 0);
+        acc[mt] += mult * t;
+      }
+    }
+    if (hf == 1) {
+      // mins of the block: k = sub-block (16), lane quarter q: sub-blocks 4q .. 4q+3
+      const int kb = s >> 1;
+      const float dmin = f16_bits_to_f32(cw.dd >> 16);
+      const uint32_t mn = (scw[q] >> 4) & 0x0F0F0F0Fu;
+      const uint32_t m0 = vperm(0u, mn, 0x0C010C00u), m1 = vperm(0u, mn, 0x0C030C02u);
+      const f16x4_t bm = __builtin_bit_cast(f16x4_t, make_uint2(m0, m1));
+      const float mmult = dmin * 16777216.0f;
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        if (mt >= mtiles) break;
+        const int m = 16 * mt + (lane & 15);
+        uint2 sh2 = make_uint2(0, 0), sl2 = make_uint2(0, 0);
+        if (m < nrows) {
+          const size_t off = (size_t)(row0 + m) * (a.I / 16) + 16 * kb + 4 * q;
+          sh2 = *(const uint2*)(a.hsh + off);
+          sl2 = *(const uint2*)(a.hsl + off);
+        }
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, sh2), bm, z, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, sl2), bm, t, 0, 0, 0);
+        acc[mt] -= mmult * t;
+      }
+    }
+    __syncthreads();  // every wave is done with the tile of stage s
+    if (more) {
+      h_store(hv);
+      cw = nw;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; mt++)
 #pragma unroll
