@@ -105,14 +105,8 @@ void launch_k(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shm, hipStre
 inline ds4moe_status launch_permute(const int32_t* ids, int n, int E, int32_t* counts,
                                     int32_t* offsets, int32_t* perm, int32_t* inv,
                                     uint32_t* status, hipStream_t st) {
-  int n2 = 2;
-  while (n2 < n) n2 <<= 1;
-  size_t lds = (size_t)n2 * 4;
-  if (hipFuncSetAttribute((const void*)k_permute, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds) != hipSuccess)
-    return DS4MOE_EDEVICE;
-  launch_k(k_permute, dim3(1), dim3(1024), lds, st, ids, n, E, counts, offsets, perm, inv,
-                     status);
+  if (n > kPermMax) return DS4MOE_EUNSUPPORTED;
+  launch_k(k_permute, dim3(1), dim3(1024), 0, st, ids, n, E, counts, offsets, perm, inv, status);
   return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;
 }
 

@@ -44,27 +44,45 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* ids, int n, int
                                                   int32_t* offsets, int32_t* perm, int32_t* inv,
                                                   uint32_t* status);
 
-// Work list: items (e, row0, nrows) for every expert with pairs, then the
-// shared expert's rows (e == E).  One thread, after the permutation.
-__global__ void k_make_items(const int32_t* counts, const int32_t* offsets, int E, int TK, int T,
-                             int with_shared, int32_t* items, int32_t* n_items) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int n = 0;
-  for (int e = 0; e < E; e++)
-    for (int m0 = 0; m0 < counts[e]; m0 += kMC) {
+// Work list: items (e, row0, nrows) for every expert with pairs (experts in
+// ascending order, 64-row pieces), then the shared expert's rows (e == E).
+// One wave of 64 threads, four experts per lane, prefix sum over the lanes.
+__global__ __launch_bounds__(64) void k_make_items(const int32_t* counts, const int32_t* offsets,
+                                                   int E, int TK, int T, int with_shared,
+                                                   int32_t* items, int32_t* n_items) {
+  const int lane = threadIdx.x;
+  int cnt[4], tot = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int e = 4 * lane + j;
+    cnt[j] = e < E ? counts[e] : 0;
+    tot += (cnt[j] + kMC - 1) / kMC;
+  }
+  int incl = tot;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  int n = incl - tot;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int e = 4 * lane + j;
+    for (int m0 = 0; m0 < cnt[j]; m0 += kMC) {
       items[3 * n] = e;
       items[3 * n + 1] = offsets[e] + m0;
-      items[3 * n + 2] = min(kMC, counts[e] - m0);
+      items[3 * n + 2] = min(kMC, cnt[j] - m0);
       n++;
     }
-  if (with_shared)
-    for (int m0 = 0; m0 < T; m0 += kMC) {
-      items[3 * n] = E;
-      items[3 * n + 1] = TK + m0;
-      items[3 * n + 2] = min(kMC, T - m0);
-      n++;
-    }
-  *n_items = n;
+  }
+  const int routed = __shfl(incl, 63);
+  const int ns = with_shared ? (T + kMC - 1) / kMC : 0;
+  for (int i = lane; i < ns; i += 64) {
+    items[3 * (routed + i)] = E;
+    items[3 * (routed + i) + 1] = TK + kMC * i;
+    items[3 * (routed + i) + 2] = min(kMC, T - kMC * i);
+  }
+  if (lane == 0) *n_items = routed + ns;
 }
 
 inline int max_items(int E, int TK, int T, bool shared) {
@@ -203,7 +221,8 @@ __device__ inline void q80_bfrag(const uint8_t* chunk, int g, int q, bf16x8_t& b
 // gate/up + SwiGLU for one work item and 64 intermediate features.
 // Grid (ceil(Imax/64), max_items), 256 threads; wave w owns features
 // n0 + 16w .. +15 (gate and up).  x tile staged in LDS per 128 columns with
-// 16-byte chunk c of row m at slot c ^ (m & 7) (conflict-free A reads).
+// 16-byte chunk c of row m at slot c ^ (m & 15) (conflict-free A reads: the
+// 16 lanes served together read 16 different bank groups).
 __global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
   __shared__ uint4 xt[kMC * 16];
   __shared__ uint4 gt8[256 * 8];
@@ -240,7 +259,7 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
       const int m = c >> 4, ch = c & 15;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (m < nrows) v = ((const uint4*)(a.x + (size_t)tok[m] * a.H + 128 * kh))[ch];
-      xt[m * 16 + (ch ^ (m & 7))] = v;
+      xt[m * 16 + (ch ^ (m & 15))] = v;
     }
     __syncthreads();
     const uint8_t* bg = G + (rowg * nb + kb) * bbg;
@@ -258,7 +277,7 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
       for (int mt = 0; mt < 4; mt++) {
         if (mt >= mtiles) break;
         const int m = 16 * mt + (lane & 15);
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, xt[m * 16 + ((4 * gi + q) ^ (m & 7))]);
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, xt[m * 16 + ((4 * gi + q) ^ (m & 15))]);
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         f32x4_t tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fg, z, 0, 0, 0);
         f32x4_t tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fu, z, 0, 0, 0);
@@ -373,7 +392,7 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       const int c = tid + 512 * j, m = c >> 4, ch = c & 15;
-      xt[buf][m * 16 + (ch ^ (m & 7))] = v[j];
+      xt[buf][m * 16 + (ch ^ (m & 15))] = v[j];
     }
   };
   {
@@ -407,7 +426,7 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
       for (int mt = 0; mt < 4; mt++) {
         if (mt >= mtiles) break;
         const int m = 16 * mt + (lane & 15);
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, xb[m * 16 + ((4 * j + q) ^ (m & 7))]);
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, xb[m * 16 + ((4 * j + q) ^ (m & 15))]);
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         const f32x4_t tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fg, z, 0, 0, 0);
         const f32x4_t tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fu, z, 0, 0, 0);
@@ -470,10 +489,10 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
       }
       // two 16-byte chunks (8 values each) per sub-block
       const int c0 = 2 * j, c1 = 2 * j + 1;
-      ah[m * 32 + (c0 ^ (m & 7))] = h0;
-      ah[m * 32 + (c1 ^ (m & 7))] = h1;
-      al[m * 32 + (c0 ^ (m & 7))] = l0;
-      al[m * 32 + (c1 ^ (m & 7))] = l1;
+      ah[m * 32 + (c0 ^ (m & 15))] = h0;
+      ah[m * 32 + (c1 ^ (m & 15))] = h1;
+      al[m * 32 + (c0 ^ (m & 15))] = l0;
+      al[m * 32 + (c1 ^ (m & 15))] = l1;
       ((uint16_t*)sh_hi)[m * 16 + j] = sh16;
       ((uint16_t*)sh_lo)[m * 16 + j] = sl16;
     }
@@ -507,8 +526,8 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
           if (mt >= mtiles) break;
           const int m = 16 * mt + (lane & 15);
           // A fragment: 4 values k = 4q..4q+3 of sub-block sb = half of 16-byte chunk 2sb + q/2
-          const uint4 ch = ah[m * 32 + ((2 * sb + (q >> 1)) ^ (m & 7))];
-          const uint4 cl = al[m * 32 + ((2 * sb + (q >> 1)) ^ (m & 7))];
+          const uint4 ch = ah[m * 32 + ((2 * sb + (q >> 1)) ^ (m & 15))];
+          const uint4 cl = al[m * 32 + ((2 * sb + (q >> 1)) ^ (m & 15))];
           const uint2 fh = (q & 1) ? make_uint2(ch.z, ch.w) : make_uint2(ch.x, ch.y);
           const uint2 fl = (q & 1) ? make_uint2(cl.z, cl.w) : make_uint2(cl.x, cl.y);
           const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
@@ -518,7 +537,8 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
         }
       }
       // mins: sum_j m_j * hsum_j over the block's 16 sub-blocks, k = sub-block
-      const uint32_t mn = (scw[q] >> 4) & 0x0F0F0F0Fu;  // min nibbles of sub-blocks 4q..4q+3
+      const uint32_t scq = scw[q];
+      const uint32_t mn = (scq >> 4) & 0x0F0F0F0Fu;  // min nibbles of sub-blocks 4q..4q+3
       const uint32_t m0 = vperm(0u, mn, 0x0C010C00u), m1 = vperm(0u, mn, 0x0C030C02u);
       const f16x4_t bm = __builtin_bit_cast(f16x4_t, make_uint2(m0, m1));
       const float mmult = dmin * 16777216.0f;
@@ -546,8 +566,8 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
         for (int mt = 0; mt < 4; mt++) {
           if (mt >= mtiles) break;
           const int m = 16 * mt + (lane & 15);
-          const f16x8_t fh = __builtin_bit_cast(f16x8_t, ah[m * 32 + ((4 * g + q) ^ (m & 7))]);
-          const f16x8_t fl = __builtin_bit_cast(f16x8_t, al[m * 32 + ((4 * g + q) ^ (m & 7))]);
+          const f16x8_t fh = __builtin_bit_cast(f16x8_t, ah[m * 32 + ((4 * g + q) ^ (m & 15))]);
+          const f16x8_t fl = __builtin_bit_cast(f16x8_t, al[m * 32 + ((4 * g + q) ^ (m & 15))]);
           const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
           f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(fh, bf, z, 0, 0, 0);
           t = __builtin_amdgcn_mfma_f32_16x16x32_f16(fl, bf, t, 0, 0, 0);
@@ -627,8 +647,8 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       const int c = tid + 512 * j, m = c >> 4, ch = c & 15;
-      ah[m * 16 + (ch ^ (m & 7))] = v[j];
-      al[m * 16 + (ch ^ (m & 7))] = v[2 + j];
+      ah[m * 16 + (ch ^ (m & 15))] = v[j];
+      al[m * 16 + (ch ^ (m & 15))] = v[2 + j];
     }
   };
   {
@@ -650,11 +670,14 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
       h_load(s + 1, hv);
     }
     const int hf = s & 1;
-    const float d = f16_bits_to_f32(cw.dd & 0xFFFFu);
+    const float d24 = f16_bits_to_f32(cw.dd & 0xFFFFu) * 16777216.0f;
     // 16-bit lanes holding whole code bytes: (byte0, byte1), (byte2, byte3)
     const uint32_t pa0 = vperm(0u, cw.qa, 0x0C010C00u), pa1 = vperm(0u, cw.qa, 0x0C030C02u);
     const uint32_t pb0 = vperm(0u, cw.qb, 0x0C010C00u), pb1 = vperm(0u, cw.qb, 0x0C030C02u);
-    const uint32_t scw[4] = {cw.sc.x, cw.sc.y, cw.sc.z, cw.sc.w};
+    // scale bytes of this half's eight sub-blocks
+    const uint32_t sc0 = hf ? cw.sc.z : cw.sc.x, sc1 = hf ? cw.sc.w : cw.sc.y;
+    const char* ahb = (const char*)ah + 8 * (q & 1);
+    const char* alb = (const char*)al + 8 * (q & 1);
 #pragma unroll
     for (int sb = 0; sb < 8; sb++) {
       // sub-block 8hf + sb of the block: shift s2 = sb >> 1, half p = sb & 1
@@ -662,18 +685,16 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
       const uint32_t mk = 0x00030003u << (2 * s2);
       const uint32_t b0 = (p ? pb0 : pa0) & mk, b1 = (p ? pb1 : pa1) & mk;
       const f16x4_t bf = __builtin_bit_cast(f16x4_t, make_uint2(b0, b1));
-      const int j = 8 * hf + sb;
-      const uint32_t scb = (scw[j >> 2] >> (8 * (j & 3))) & 0xFu;
-      const float mult = d * (float)scb * (16777216.0f / (float)(1 << (2 * s2)));
+      const uint32_t scb = ((sb < 4 ? sc0 : sc1) >> (8 * (sb & 3))) & 0xFu;
+      const float mult = d24 * (1.0f / (float)(1 << (2 * s2))) * (float)scb;
 #pragma unroll
       for (int mt = 0; mt < 4; mt++) {
         if (mt >= mtiles) break;
         const int m = 16 * mt + (lane & 15);
         // A: values 16 sb + 4q .. +3 = half (q & 1) of chunk 2 sb + (q >> 1)
-        const int slot = m * 16 + ((2 * sb + (q >> 1)) ^ (m & 7));
-        const uint4 ch = ah[slot], cl = al[slot];
-        const uint2 fh = (q & 1) ? make_uint2(ch.z, ch.w) : make_uint2(ch.x, ch.y);
-        const uint2 fl = (q & 1) ? make_uint2(cl.z, cl.w) : make_uint2(cl.x, cl.y);
+        const int off = 16 * (m * 16 + ((2 * sb + (q >> 1)) ^ (m & 15)));
+        const uint2 fh = *(const uint2*)(ahb + off);
+        const uint2 fl = *(const uint2*)(alb + off);
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, fh), bf, z, 0, 0, 0);
         t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, fl), bf, t, 0, 0, 0);
@@ -684,7 +705,8 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
       // mins of the block: k = sub-block (16), lane quarter q: sub-blocks 4q .. 4q+3
       const int kb = s >> 1;
       const float dmin = f16_bits_to_f32(cw.dd >> 16);
-      const uint32_t mn = (scw[q] >> 4) & 0x0F0F0F0Fu;
+      const uint32_t scq = q == 0 ? cw.sc.x : q == 1 ? cw.sc.y : q == 2 ? cw.sc.z : cw.sc.w;
+      const uint32_t mn = (scq >> 4) & 0x0F0F0F0Fu;
       const uint32_t m0 = vperm(0u, mn, 0x0C010C00u), m1 = vperm(0u, mn, 0x0C030C02u);
       const f16x4_t bm = __builtin_bit_cast(f16x4_t, make_uint2(m0, m1));
       const float mmult = dmin * 16777216.0f;

@@ -358,64 +358,71 @@ __global__ void k_route_hash(const int32_t* tok, const int32_t* table, int vocab
   }
 }
 
-// Permutation by a bitonic sort of keys (expert << 15 | pair) in LDS; one
-// workgroup of 1024 threads, n = T*K <= 32768.
+// Permutation by a stable counting sort in one workgroup of 1024 threads
+// (n = T*K <= 32768, E <= 256).  The expert ids are staged in LDS as bytes;
+// 64 chunk owners count their contiguous run of pairs per expert; an
+// exclusive scan over chunks (per expert) and over experts gives every
+// (chunk, expert) its first position; each owner then places its pairs in
+// order.  The result is the canonical order: by expert, then by pair index.
+// Invalid ids raise a fault bit and are treated as expert 0.
+constexpr int kPermChunks = 64;
+constexpr int kPermMax = 32768;
+
 __global__ __launch_bounds__(1024) void k_permute(const int32_t* ids, int n, int E, int32_t* counts,
                                                   int32_t* offsets, int32_t* perm, int32_t* inv,
                                                   uint32_t* status) {
-  extern __shared__ uint32_t keys[];
-  __shared__ int cnt[257];
-  int tid = threadIdx.x;
-  int n2 = 2;
-  while (n2 < n) n2 <<= 1;
-  for (int i = tid; i <= E; i += 1024) cnt[i] = 0;
+  __shared__ int tab[kPermChunks * 256];  // [chunk][expert]: counts, then first positions
+  __shared__ uint8_t eid[kPermMax];
+  __shared__ int base[257];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kPermChunks * 256; i += 1024) tab[i] = 0;
   bool bad = false;
-  for (int i = tid; i < n2; i += 1024) {
-    uint32_t key = 0xFFFFFFFFu;
-    if (i < n) {
-      int e = ids[i];
-      if (e < 0 || e >= E) {
-        bad = true;
-        e = 0;
-      }
-      key = ((uint32_t)e << 15) | (uint32_t)i;
+  for (int i = tid; i < n; i += 1024) {
+    int e = ids[i];
+    if (e < 0 || e >= E) {
+      bad = true;
+      e = 0;
     }
-    keys[i] = key;
+    eid[i] = (uint8_t)e;
   }
   if (bad) raise_fault(status, DS4MOE_FAULT_BAD_ID);
   __syncthreads();
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < n2; i += 1024) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          uint32_t a = keys[i], b = keys[ixj];
-          bool up = (i & k) == 0;
-          if ((a > b) == up) {
-            keys[i] = b;
-            keys[ixj] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int i = tid; i < n; i += 1024) {
-    uint32_t key = keys[i];
-    int p = (int)(key & 0x7FFFu);
-    perm[i] = p;
-    inv[p] = i;
-    atomicAdd(&cnt[key >> 15], 1);
+  const int per = (n + kPermChunks - 1) / kPermChunks;
+  if (tid < kPermChunks) {
+    const int i0 = tid * per, i1 = min(n, i0 + per);
+    for (int i = i0; i < i1; i++) tab[tid * 256 + eid[i]]++;
   }
   __syncthreads();
-  if (tid == 0) {
+  if (tid < E) {  // per expert: exclusive prefix over chunks, total
+    int run = 0;
+    for (int c = 0; c < kPermChunks; c++) {
+      const int v = tab[c * 256 + tid];
+      tab[c * 256 + tid] = run;
+      run += v;
+    }
+    base[tid] = run;
+  }
+  __syncthreads();
+  if (tid == 0) {  // exclusive scan over experts
     int run = 0;
     for (int e = 0; e < E; e++) {
-      counts[e] = cnt[e];
+      const int c = base[e];
+      counts[e] = c;
       offsets[e] = run;
-      run += cnt[e];
+      base[e] = run;
+      run += c;
     }
     offsets[E] = run;
+  }
+  __syncthreads();
+  if (tid < kPermChunks) {
+    const int i0 = tid * per, i1 = min(n, i0 + per);
+    for (int i = i0; i < i1; i++) {
+      const int e = eid[i];
+      const int pos = base[e] + tab[tid * 256 + e]++;
+      perm[pos] = i;
+      inv[i] = pos;
+    }
   }
 }
 
