@@ -185,6 +185,7 @@ struct GateUpB1Args {
   uint32_t* status;
 };
 
+constexpr int kDnRows = 4;                                   // down rows per wave
 constexpr int kGuWaves = 16;                                  // waves per workgroup
 constexpr int kGuRows = 3;                                    // rows (gate + up) per wave
 constexpr int kGuBlocks = 6 * kI / (kGuWaves * kGuRows);      // 256
@@ -335,7 +336,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
 }
 
 // down + weighted combine (+ residual) for one token.
-// Grid H/8 workgroups of 6 waves: wave k handles routed slot k for 8 rows.
+// Grid H/kDnRows workgroups of 6 waves: wave k handles routed slot k for
+// kDnRows rows.
 // Lane L = 8b + 4hh + c of a wave covers the 32 columns
 // i = 256b + 128hh + 32s + 8c + j (s < 4, j < 8) of every row: the 8 code
 // bytes qs[32hh + 8c .. +7] of block b hold exactly their 2-bit codes.  The
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const float* __restrict__ h
                                                      float* __restrict__ out,
                                                      float* __restrict__ residual,
                                                      uint32_t* status) {
-  constexpr int R = 8;
+  constexpr int R = kDnRows;
   __shared__ float part[6][R];
   const int tid = threadIdx.x, lane = tid & 63;
   const int k = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform slot
@@ -410,7 +412,7 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const float* __restrict__ h
   const float wS = __int_as_float(load_scalar_i32((const int32_t*)wts, k)) * S;
   const uint32_t cb = (uint32_t)(c >> 1);
   const uint32_t ssel = cb | ((cb + 2) << 8) | ((cb + 4) << 16) | ((cb + 6) << 24);
-  float pr[R];
+  float pr[8];
 #pragma unroll
   for (int r = 0; r < R; r++) {
     uint32_t p0 = vperm(0u, qv[r].x, 0x0C010C00u), p1 = vperm(0u, qv[r].x, 0x0C030C02u);
@@ -431,10 +433,13 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const float* __restrict__ h
     float d = f16_bits_to_f32(dd[r] & 0xFFFFu), dmin = f16_bits_to_f32(dd[r] >> 16);
     pr[r] = wS * fmaf(-dmin, (float)B, d * (float)A);
   }
+#pragma unroll
+  for (int r = R; r < 8; r++) pr[r] = 0.0f;
   const float tot = reduce8(pr);
   if ((lane & 7) == 0) {
     const int rho = lane >> 4, eta = (lane >> 3) & 1;
-    part[k][4 * eta + ((rho == 1) ? 2 : (rho == 2) ? 1 : rho)] = tot;
+    const int r = 4 * eta + ((rho == 1) ? 2 : (rho == 2) ? 1 : rho);
+    if (r < R) part[k][r] = tot;
   }
   __syncthreads();
   if (tid < R) {
