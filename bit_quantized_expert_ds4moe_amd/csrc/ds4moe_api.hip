@@ -208,9 +208,13 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, con
 }
 
 // ---- expert FFN dispatch ----------------------------------------------------
-bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_experts* sh,
-             const void* x, int32_t x_dt, int32_t T) {
-  return T == 1 && !sh && x_dt == DS4MOE_BF16 && s.hidden == kH && s.inter == kI && ex.inter == kI &&
+// Few tokens (up to kB1MaxTokens) with the V4-Flash expert shape and formats:
+// the streaming matvec kernels, one grid row per token (the routed experts;
+// a shared expert then runs through the grouped path).
+constexpr int kB1MaxTokens = 16;
+bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x, int32_t x_dt,
+             int32_t T) {
+  return T >= 1 && T <= kB1MaxTokens && x_dt == DS4MOE_BF16 && s.hidden == kH && s.inter == kI && ex.inter == kI &&
          s.top_k == 6 && ex.gate_qtype == DS4MOE_IQ2_XXS && ex.up_qtype == DS4MOE_IQ2_XXS &&
          ex.down_qtype == DS4MOE_Q2_K && aligned(x, 16) && aligned(ex.gate, 16) &&
          aligned(ex.up, 16) && aligned(ex.down, 16) && aligned(ex.grid, 8);
@@ -219,8 +223,9 @@ bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_exper
 // Batch-1 fast path: gate/up (+ the top-6 selection when kbuf is given, in
 // which case ids/wts are outputs) then down.
 ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x,
-                        const int32_t* ids_in, const float4* kbuf, int32_t* ids, const float* wts,
-                        float* out, float* residual, void* ws, const Layout& L, hipStream_t st) {
+                        int32_t T, const int32_t* ids_in, const float4* kbuf, int32_t* ids,
+                        const float* wts, float* out, float* residual, void* ws, const Layout& L,
+                        hipStream_t st) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   float* h = at<float>(ws, L.h);
   GateUpB1Args g{};
@@ -239,18 +244,37 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   {
     ProfScope prof(DS4MOE_K_GATEUP, st);
     if (kbuf)
-      launch_k(k_gateup_b1<true>, dim3(kGuBlocks), dim3(kGuWaves * 64), 0, st, g);
+      launch_k(k_gateup_b1<true>, dim3(kGuBlocks, 1), dim3(kGuWaves * 64), 0, st, g);
     else
-      launch_k(k_gateup_b1<false>, dim3(kGuBlocks), dim3(kGuWaves * 64), 0, st, g);
+      launch_k(k_gateup_b1<false>, dim3(kGuBlocks, T), dim3(kGuWaves * 64), 0, st, g);
   }
   ds4moe_status rc = launched();
   if (rc != DS4MOE_OK) return rc;
   {
     ProfScope prof(DS4MOE_K_DOWN, st);
-    launch_k(k_down_q2k_b1, dim3(kH / kDnRows), dim3(384), 0, st, h, (const uint8_t*)ex.down,
+    launch_k(k_down_q2k_b1, dim3(kH / kDnRows, kbuf ? 1 : T), dim3(384), 0, st, h,
+             (const uint8_t*)ex.down,
                        kbuf ? ids : ids_in, wts, s.n_expert, out, residual, status);
   }
   return launched();
+}
+
+// Permutation for the caller's debug buffer (offsets[E+1], perm, inv).
+ds4moe_status permute_dbg(const ds4moe_shape& s, int32_t T, const int32_t* ids, int32_t* perm_dbg,
+                          void* ws, const Layout& L, hipStream_t st) {
+  const int E = s.n_expert, TK = T * s.top_k;
+  int32_t* counts = at<int32_t>(ws, L.perm);
+  int32_t* offsets = counts + E;
+  int32_t* perm = offsets + E + 1;
+  int32_t* inv = perm + TK;
+  ProfScope prof(DS4MOE_K_PERMUTE, st);
+  ds4moe_status rc = launch_permute(ids, TK, E, counts, offsets, perm, inv,
+                                    at<uint32_t>(ws, L.status), st);
+  if (rc != DS4MOE_OK) return rc;
+  if (hipMemcpyAsync(perm_dbg, offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToDevice, st) != hipSuccess ||
+      hipMemcpyAsync(perm_dbg + E + 1, perm, sizeof(int32_t) * 2 * TK, hipMemcpyDeviceToDevice, st) != hipSuccess)
+    return DS4MOE_EDEVICE;
+  return DS4MOE_OK;
 }
 
 ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_experts* sh,
@@ -258,9 +282,14 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
                      float* out, float* residual, int32_t* perm_dbg, void* ws, const Layout& L,
                      hipStream_t st) {
   uint32_t* status = at<uint32_t>(ws, L.status);
-  if (fast_b1(s, ex, sh, x, x_dt, T))
-    return launch_b1(s, ex, x, ids, nullptr, nullptr, wts, out, residual, ws, L, st);
-  if (T > 1 && grouped_eligible(s, ex, sh, x, x_dt, T)) {
+  const bool b1 = fast_b1(s, ex, x, x_dt, T) && (!sh || grouped_eligible(s, ex, sh, x, x_dt, T));
+  if (b1) {
+    ds4moe_status rc = launch_b1(s, ex, x, T, ids, nullptr, nullptr, wts, out, residual, ws, L, st);
+    if (rc == DS4MOE_OK && perm_dbg)  // the few-token path needs no permutation: make it for the caller
+      rc = permute_dbg(s, T, ids, perm_dbg, ws, L, st);
+    if (rc != DS4MOE_OK || !sh) return rc;
+  }
+  if (b1 || (T > 1 && grouped_eligible(s, ex, sh, x, x_dt, T))) {
     const int E = s.n_expert, K = s.top_k, TK = T * K;
     int32_t* counts = at<int32_t>(ws, L.perm);
     int32_t* offsets = counts + E;
@@ -272,10 +301,14 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     ds4moe_status rc;
     {
       ProfScope prof(DS4MOE_K_PERMUTE, st);
-      rc = launch_permute(ids, TK, E, counts, offsets, perm, inv, status, st);
-      if (rc != DS4MOE_OK) return rc;
-      launch_k(k_make_items, dim3(1), dim3(64), 0, st, counts, offsets, E, TK, T,
-                         sh ? 1 : 0, items, n_items);
+      if (b1) {  // the routed experts are done: the shared expert's rows only
+        launch_k(k_make_shared_items, dim3(1), dim3(64), 0, st, E, TK, T, items, n_items);
+      } else {
+        rc = launch_permute(ids, TK, E, counts, offsets, perm, inv, status, st);
+        if (rc != DS4MOE_OK) return rc;
+        launch_k(k_make_items, dim3(1), dim3(64), 0, st, counts, offsets, E, TK, T,
+                 sh ? 1 : 0, items, n_items);
+      }
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     GroupArgs g{};
@@ -319,7 +352,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     {
       ProfScope prof(DS4MOE_K_GATEUP, st);
       const bool iq2 = g.qt_g == DS4MOE_IQ2_XXS && g.qt_u == DS4MOE_IQ2_XXS && g.I % kGNF == 0;
-      if (iq2) launch_k(k_grouped_gateup_iq2, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
+      if (iq2 && !b1) launch_k(k_grouped_gateup_iq2, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
       if (!iq2 || sh)
         launch_k(k_grouped_gateup, dim3((imax + kNT - 1) / kNT, mi), dim3(256), 0, st, g);
     }
@@ -327,19 +360,23 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     {
       ProfScope prof(DS4MOE_K_DOWN, st);
       const bool q2k = g.qt_d == DS4MOE_Q2_K && g.H % kDNF == 0;
-      if (q2k) launch_k(k_grouped_down_q2k, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
+      if (q2k && !b1) launch_k(k_grouped_down_q2k, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
       if (!q2k || sh) launch_k(k_grouped_down, dim3(s.hidden / kNT, mi), dim3(256), 0, st, g);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     {
       ProfScope prof(DS4MOE_K_OTHER, st);
       const size_t n = (size_t)T * s.hidden;
-      launch_k(k_grouped_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                         (const float*)g.y, (const int32_t*)inv, wts, T, K, s.hidden, sh ? 1 : 0, out,
-                         residual);
+      if (b1)
+        launch_k(k_add_shared, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                 (const float*)g.y, TK, T, s.hidden, residual ? residual : out);
+      else
+        launch_k(k_grouped_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                 (const float*)g.y, (const int32_t*)inv, wts, T, K, s.hidden, sh ? 1 : 0, out,
+                 residual);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
-    if (perm_dbg) {
+    if (perm_dbg && !b1) {
       if (hipMemcpyAsync(perm_dbg, offsets, sizeof(int32_t) * (E + 1), hipMemcpyDeviceToDevice, st) != hipSuccess ||
           hipMemcpyAsync(perm_dbg + E + 1, perm, sizeof(int32_t) * 2 * TK, hipMemcpyDeviceToDevice, st) != hipSuccess)
         return DS4MOE_EDEVICE;
@@ -509,14 +546,14 @@ DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_la
   int32_t fdt = norm ? (int32_t)DS4MOE_BF16 : x_dtype;
   // batch-1 fast path with a learned router: the top-6 selection runs inside
   // the gate/up kernel (one kernel boundary fewer)
-  const bool fuse = !r.tid2eid && fast_b1(*shape, desc->routed, sh, norm ? (const void*)xn : x,
-                                          fdt, n_tok);
+  const bool fuse = !r.tid2eid && !sh && n_tok == 1 &&
+                    fast_b1(*shape, desc->routed, norm ? (const void*)xn : x, fdt, n_tok);
   rc = do_route(*shape, r, x, x_dtype, norm ? residual : nullptr, norm ? desc->norm_w : nullptr,
                 desc->norm_eps, norm ? xn : nullptr, n_tok, token_ids, ids, wts, ws, L, stream,
                 !fuse);
   if (rc != DS4MOE_OK) return rc;
   if (fuse)
-    rc = launch_b1(*shape, desc->routed, fx, nullptr, at<float4>(ws, L.kbuf), ids, wts,
+    rc = launch_b1(*shape, desc->routed, fx, 1, nullptr, at<float4>(ws, L.kbuf), ids, wts,
                    norm ? nullptr : out, norm ? residual : nullptr, ws, L, stream);
   else
     rc = do_ffn(*shape, desc->routed, sh, fx, fdt, n_tok, ids, wts, norm ? nullptr : out,

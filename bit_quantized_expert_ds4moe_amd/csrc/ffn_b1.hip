@@ -225,6 +225,11 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in scalar registers
   const int row0 = (blockIdx.x * kGuWaves + w) * kGuRows;  // flattened
+  // token t = blockIdx.y (several tokens: one grid row each; selection only at T = 1)
+  const int tok = blockIdx.y;
+  const uint16_t* xtok = a.x + (size_t)tok * kH;
+  const int32_t* idtok = a.ids + 6 * tok;
+  float* htok = a.h + (size_t)tok * 6 * kI;
   const Iq2Off off = iq2_offsets(lane);
   Iq2Seg sg[kGuRows], su[kGuRows];
 
@@ -235,14 +240,14 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
   uint2 gb = make_uint2(0, 0);
   uint4 xv = make_uint4(0, 0, 0, 0);
   if (t >= 0 && t < 256) gb = *(const uint2*)(a.grid + 8 * t);
-  else if (t >= 384 && t < 384 + kH / 8) xv = ((const uint4*)a.x)[t - 384];
+  else if (t >= 384 && t < 384 + kH / 8) xv = ((const uint4*)xtok)[t - 384];
 
   // Expert of each of the wave's rows (wave-uniform), validated.
   auto expert_rows = [&](const int* e_of_slot_lds, uint32_t* erow) {
 #pragma unroll
     for (int r = 0; r < kGuRows; r++) {
       const int k = (row0 + r) >> 11;
-      int e = SEL ? __builtin_amdgcn_readfirstlane(e_of_slot_lds[k]) : load_scalar_i32(a.ids, k);
+      int e = SEL ? __builtin_amdgcn_readfirstlane(e_of_slot_lds[k]) : load_scalar_i32(idtok, k);
       if (e < 0 || e >= a.E) {
         if (lane == 0 && ((row0 + r) & (kI - 1)) == 0) raise_fault(a.status, DS4MOE_FAULT_BAD_ID);
         e = 0;
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
   if (SEL && w == 0) {
     int e;
     float g;
-    const bool first = blockIdx.x == 0;
+    const bool first = blockIdx.x == 0 && blockIdx.y == 0;
     select_wave(a.kbuf, a.E, 6, a.scale, a.status, first, e, g);
     if (lane < 6) {
       sel_e[lane] = e;
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
   if ((lane & 15) == 0 && lane != 48) {
     const int rho = lane >> 4;
     const int r = (rho == 1) ? 2 : (rho == 2) ? 1 : rho;
-    a.h[row0 + r] = silu(tot) * upv;
+    htok[row0 + r] = silu(tot) * upv;
   }
 }
 
@@ -358,6 +363,13 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const float* __restrict__ h
   const int tid = threadIdx.x, lane = tid & 63;
   const int k = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform slot
   const int b = lane >> 3, q8 = lane & 7, hh = q8 >> 2, c = q8 & 3;
+  // token t = blockIdx.y
+  const int tok = blockIdx.y;
+  h += (size_t)tok * 6 * kI;
+  ids += 6 * tok;
+  wts += 6 * tok;
+  if (out) out += (size_t)tok * kH;
+  if (residual) residual += (size_t)tok * kH;
   // the SwiGLU values first (the vector memory counter retires in order:
   // waiting for them then never waits for the weights)
   float hv[32];
@@ -375,7 +387,7 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const float* __restrict__ h
     if (lane == 0 && blockIdx.x == 0) raise_fault(status, DS4MOE_FAULT_BAD_ID);
     e = 0;
   }
-  const int row0 = blockIdx.x * R;
+  const int row0 = blockIdx.x * R;  // output rows of token tok
   const uint8_t* base = down + ((size_t)e * kH + row0) * kRowQ2k + b * kQ2kBytes;
   const int qoff = 16 + 32 * hh + 8 * c, soff = 8 * hh;
   uint2 qv[R], sv[R];

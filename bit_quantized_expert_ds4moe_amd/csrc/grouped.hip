@@ -85,6 +85,25 @@ __global__ __launch_bounds__(64) void k_make_items(const int32_t* counts, const 
   if (lane == 0) *n_items = routed + ns;
 }
 
+// Work list of the shared expert alone (its rows T*K .. T*K+T-1), for calls
+// whose routed experts take the few-token path.
+__global__ void k_make_shared_items(int E, int TK, int T, int32_t* items, int32_t* n_items) {
+  const int i = threadIdx.x, ns = (T + kMC - 1) / kMC;
+  for (int j = i; j < ns; j += blockDim.x) {
+    items[3 * j] = E;
+    items[3 * j + 1] = TK + kMC * j;
+    items[3 * j + 2] = min(kMC, T - kMC * j);
+  }
+  if (i == 0) *n_items = ns;
+}
+
+// dst[t][c] += y[T*K + t][c]: adds the shared expert's rows.
+__global__ void k_add_shared(const float* y, int TK, int T, int H, float* dst) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)T * H) return;
+  dst[idx] += y[(size_t)TK * H + idx];
+}
+
 inline int max_items(int E, int TK, int T, bool shared) {
   return E + (TK + kMC - 1) / kMC + (shared ? (T + kMC - 1) / kMC : 0);
 }
