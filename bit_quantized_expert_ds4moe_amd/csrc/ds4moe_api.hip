@@ -18,9 +18,13 @@ using namespace ds4;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+constexpr int kB1MaxTokens = 16;   // few-token calls use the streaming matvec kernels
+constexpr int kSharedSplitG = 16;  // K shares of a shared expert's gate/up in such calls (<= kMaxSplit)
+constexpr int kSharedSplitD = 4;   // and of its down
+
 // Byte offsets of the workspace regions for (shape, n_tok).
 struct Layout {
-  size_t status, kbuf, ids, wts, xn, perm, h, y, hb, total;
+  size_t status, kbuf, ids, wts, xn, perm, h, y, hb, part, total;
 };
 
 Layout layout_for(const ds4moe_shape& s, int32_t T) {
@@ -43,6 +47,8 @@ Layout layout_for(const ds4moe_shape& s, int32_t T) {
   L.h = take(np * I * 4);
   L.y = take(np * H * 4);
   L.hb = take(np * I * 2);
+  // K shares of a shared expert in few-token calls
+  L.part = take(t <= (size_t)kB1MaxTokens ? (size_t)kSharedSplitG * t * (2 * I > H ? 2 * I : H) * 4 : 0);
   L.total = o;
   return L;
 }
@@ -210,8 +216,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, con
 // ---- expert FFN dispatch ----------------------------------------------------
 // Few tokens (up to kB1MaxTokens) with the V4-Flash expert shape and formats:
 // the streaming matvec kernels, one grid row per token (the routed experts;
-// a shared expert then runs through the grouped path).
-constexpr int kB1MaxTokens = 16;
+// a shared expert then runs through the grouped path, split along K).
 bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x, int32_t x_dt,
              int32_t T) {
   return T >= 1 && T <= kB1MaxTokens && x_dt == DS4MOE_BF16 && s.hidden == kH && s.inter == kI && ex.inter == kI &&
@@ -347,13 +352,27 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       g.hsl = sbase + np * (size_t)(g.I / 16);
     }
     g.y = at<float>(ws, L.y);
+    g.ksplit_g = g.ksplit_d = 1;
+    g.part = at<float>(ws, L.part);
+    if (b1 && sh) {
+      if ((g.H / 64) % kSharedSplitG == 0) g.ksplit_g = kSharedSplitG;
+      if ((g.sh_I / 256) % kSharedSplitD == 0) g.ksplit_d = kSharedSplitD;
+    }
     g.status = status;
     const int imax = g.I > g.sh_I ? g.I : g.sh_I;
     {
       ProfScope prof(DS4MOE_K_GATEUP, st);
       const bool iq2 = g.qt_g == DS4MOE_IQ2_XXS && g.qt_u == DS4MOE_IQ2_XXS && g.I % kGNF == 0;
+      const bool q80 = sh && q80_shared_fast(g);
       if (iq2 && !b1) launch_k(k_grouped_gateup_iq2, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
-      if (!iq2 || sh)
+      if (q80) {
+        launch_k(k_grouped_gateup_q80, dim3(g.sh_I / kGNF, mi, g.ksplit_g), dim3(kGW * 64), 0, st, g);
+        if (g.ksplit_g > 1)
+          launch_k(k_swiglu_finish, dim3((T * g.sh_I + 255) / 256), dim3(256), 0, st, g);
+      } else {
+        g.ksplit_g = 1;
+      }
+      if ((!iq2 && !b1) || (sh && !q80))
         launch_k(k_grouped_gateup, dim3((imax + kNT - 1) / kNT, mi), dim3(256), 0, st, g);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
@@ -361,7 +380,8 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       ProfScope prof(DS4MOE_K_DOWN, st);
       const bool q2k = g.qt_d == DS4MOE_Q2_K && g.H % kDNF == 0;
       if (q2k && !b1) launch_k(k_grouped_down_q2k, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
-      if (!q2k || sh) launch_k(k_grouped_down, dim3(s.hidden / kNT, mi), dim3(256), 0, st, g);
+      if (!q2k || sh)
+        launch_k(k_grouped_down, dim3(s.hidden / kNT, mi, g.ksplit_d), dim3(256), 0, st, g);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     {
@@ -369,7 +389,8 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       const size_t n = (size_t)T * s.hidden;
       if (b1)
         launch_k(k_add_shared, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                 (const float*)g.y, TK, T, s.hidden, residual ? residual : out);
+                 (const float*)g.y, (const float*)g.part, g.ksplit_d, TK, T, s.hidden,
+                 residual ? residual : out);
       else
         launch_k(k_grouped_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                  (const float*)g.y, (const int32_t*)inv, wts, T, K, s.hidden, sh ? 1 : 0, out,

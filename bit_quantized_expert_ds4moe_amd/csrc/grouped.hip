@@ -97,11 +97,20 @@ __global__ void k_make_shared_items(int E, int TK, int T, int32_t* items, int32_
   if (i == 0) *n_items = ns;
 }
 
-// dst[t][c] += y[T*K + t][c]: adds the shared expert's rows.
-__global__ void k_add_shared(const float* y, int TK, int T, int H, float* dst) {
+// dst[t][c] += shared expert output of token t: y[T*K + t][c], or the sum of
+// its K shares part[z][t][c] taken in z order.
+__global__ void k_add_shared(const float* y, const float* part, int ks, int TK, int T, int H,
+                             float* dst) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (size_t)T * H) return;
-  dst[idx] += y[(size_t)TK * H + idx];
+  float v;
+  if (ks == 1) {
+    v = y[(size_t)TK * H + idx];
+  } else {
+    v = 0.0f;
+    for (int z = 0; z < ks; z++) v += part[(size_t)z * T * H + idx];
+  }
+  dst[idx] += v;
 }
 
 inline int max_items(int E, int TK, int T, bool shared) {
@@ -125,6 +134,10 @@ struct GroupArgs {
   uint16_t* hsl;            // [T*K + T][I/16] low part
   float* y;                 // [T*K + T][H] fp32
   uint32_t* status;
+  // K split of the shared expert's kernels (few-token calls): partial sums
+  // [split][T][2*I] (gate, up) then [split][T][H] (down), reduced in a fixed order
+  int ksplit_g, ksplit_d;
+  float* part;
 };
 
 __device__ inline int row_token(const GroupArgs& a, int row) {
@@ -237,6 +250,10 @@ __device__ inline void q80_bfrag(const uint8_t* chunk, int g, int q, bf16x8_t& b
   b = __builtin_bit_cast(bf16x8_t, v);
 }
 
+__host__ __device__ inline bool q80_shared_fast(const GroupArgs& a) {
+  return a.sh_qt_g == DS4MOE_Q8_0 && a.sh_qt_u == DS4MOE_Q8_0 && a.sh_I % kGNF == 0 && a.H % 64 == 0;
+}
+
 // gate/up + SwiGLU for one work item and 64 intermediate features.
 // Grid (ceil(Imax/64), max_items), 256 threads; wave w owns features
 // n0 + 16w .. +15 (gate and up).  x tile staged in LDS per 128 columns with
@@ -251,8 +268,10 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
   if (item >= *a.n_items) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   const bool sh = e == a.E;
-  // routed items with IQ2_XXS gate and up run in k_grouped_gateup_iq2
+  // routed items with IQ2_XXS gate and up run in k_grouped_gateup_iq2, a
+  // Q8_0 shared expert in k_grouped_gateup_q80
   if (!sh && a.qt_g == DS4MOE_IQ2_XXS && a.qt_u == DS4MOE_IQ2_XXS && a.I % kGNF == 0) return;
+  if (sh && q80_shared_fast(a)) return;
   const int I = sh ? a.sh_I : a.I;
   const int n0 = blockIdx.x * kNT;
   if (n0 >= I) return;
@@ -463,6 +482,175 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
   swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu);
 }
 
+// ---------------------------------------------------------------------------
+// gate/up of the shared expert (Q8_0 gate and up), software-pipelined like
+// k_grouped_gateup_iq2.  Stages of 64 columns (two Q8_0 blocks); per block a
+// lane holds the three aligned words covering its 8 codes and the word with
+// d.  B = the codes in bf16 (exact), the block scale multiplies each result.
+struct Q80Stage {
+  uint32_t c[2][3];
+  uint32_t dw[2];
+};
+
+__device__ inline void q80_stage_load(const uint8_t* __restrict__ row, int s, int q, Q80Stage& st) {
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int b = 2 * s + i;
+    const int start = kQ80Bytes * b + 2 + 8 * q;
+    const int sh = start & 3;
+    const uint32_t* p = (const uint32_t*)(row + (start - sh));
+    st.c[i][0] = p[0];
+    st.c[i][1] = p[1];
+    st.c[i][2] = p[sh ? 2 : 1];  // never past the row when not needed
+    st.dw[i] = *(const uint32_t*)(row + ((kQ80Bytes * b) & ~3));
+  }
+}
+
+// block i (0, 1) of a stage: (2i + 2) & 3 is the codes' misalignment, (2i) & 3
+// the position of d
+__device__ inline bf16x8_t q80_stage_frag(const Q80Stage& st, int i, float& scale) {
+  const uint32_t sh = i ? 0u : 2u;
+  const uint32_t c0 = align_bytes(st.c[i][1], st.c[i][0], sh);
+  const uint32_t c1 = align_bytes(st.c[i][2], st.c[i][1], sh);
+  scale = f16_bits_to_f32(i ? (st.dw[i] >> 16) : (st.dw[i] & 0xFFFFu));
+  uint4 v;
+  i8x4_to_bf16x4(c0, v.x, v.y);
+  i8x4_to_bf16x4(c1, v.z, v.w);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_q80(GroupArgs a) {
+  __shared__ uint4 xt[2][kMC * 8];  // 2 x 8 KB: row m, 16-byte chunk c at m*8 + (c ^ ((m >> 1) & 7))
+  __shared__ int tok[kMC];
+  const int item = blockIdx.y;
+  if (item >= *a.n_items) return;
+  const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
+  if (e != a.E) return;  // the shared expert only
+  const int n0 = blockIdx.x * kGNF;
+  if (n0 >= a.sh_I) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = lane >> 4;
+  const int n = n0 + 16 * w + (lane & 15);
+  const int rowbytes = (a.H / 32) * kQ80Bytes;
+  const uint8_t* grow = a.sh_gate + (size_t)n * rowbytes;
+  const uint8_t* urow = a.sh_up + (size_t)n * rowbytes;
+  // this block's share of the K stages (a.ksplit_g blocks along z)
+  const int nall = a.H / 64, nsp = nall / a.ksplit_g, s0 = blockIdx.z * nsp;
+  const int mtiles = (nrows + 15) >> 4;
+  Q80Stage cg, cu;
+  q80_stage_load(grow, s0, q, cg);
+  q80_stage_load(urow, s0, q, cu);
+  if (tid < kMC) tok[tid] = tid < nrows ? row_token(a, row0 + tid) : -1;
+  __syncthreads();
+  // x tile of a stage: thread -> row tid >> 3, chunk tid & 7
+  const int xm = tid >> 3, xc = tid & 7;
+  auto x_load = [&](int s) -> uint4 {
+    return xm < nrows ? ((const uint4*)(a.x + (size_t)tok[xm] * a.H + 64 * s))[xc]
+                      : make_uint4(0, 0, 0, 0);
+  };
+  auto x_store = [&](int buf, uint4 v) { xt[buf][xm * 8 + (xc ^ ((xm >> 1) & 7))] = v; };
+  x_store(s0 & 1, x_load(s0));
+  __syncthreads();
+  f32x4_t accg[4], accu[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = s0; s < s0 + nsp; s++) {
+    const bool more = s + 1 < s0 + nsp;
+    Q80Stage ng, nu;
+    uint4 xv = make_uint4(0, 0, 0, 0);
+    if (more) {
+      q80_stage_load(grow, s + 1, q, ng);
+      q80_stage_load(urow, s + 1, q, nu);
+      xv = x_load(s + 1);
+    }
+    const uint4* xb = xt[s & 1];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      float sg, su;
+      const bf16x8_t fg = q80_stage_frag(cg, i, sg);
+      const bf16x8_t fu = q80_stage_frag(cu, i, su);
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        if (mt >= mtiles) break;
+        const int m = 16 * mt + (lane & 15);
+        const bf16x8_t af =
+            __builtin_bit_cast(bf16x8_t, xb[m * 8 + ((4 * i + q) ^ ((m >> 1) & 7))]);
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4_t tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fg, z, 0, 0, 0);
+        const f32x4_t tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fu, z, 0, 0, 0);
+        accg[mt] += sg * tg;
+        accu[mt] += su * tu;
+      }
+    }
+    if (more) {
+      x_store((s + 1) & 1, xv);
+      cg = ng;
+      cu = nu;
+    }
+    __syncthreads();
+  }
+  if (a.ksplit_g == 1) {
+    swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu);
+    return;
+  }
+  // partial sums of this K share: part[z][row - T*K][f] (gate), [.. + I] (up)
+  const int TK = a.T * a.K;
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      if (mt >= mtiles) break;
+      const int m = 16 * mt + 4 * q + r;
+      if (m < nrows) {
+        float* pp = a.part + ((size_t)blockIdx.z * a.T + (row0 + m - TK)) * 2 * a.sh_I;
+        pp[n] = accg[mt][r];
+        pp[a.sh_I + n] = accu[mt][r];
+      }
+    }
+}
+
+// Reduces the K shares of the shared expert's gate/up in a fixed order and
+// writes the SwiGLU rows like swiglu_store: binary16 high/low parts and the
+// sums of 16 consecutive features (DPP inside each row of 16 lanes).  One
+// thread per (token, feature); all loads of a thread are issued together.
+constexpr int kMaxSplit = 16;
+__global__ __launch_bounds__(256) void k_swiglu_finish(GroupArgs a) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int I = a.sh_I;
+  const bool live = idx < a.T * I;
+  const int t = live ? idx / I : 0, f = live ? idx % I : 0;
+  float gp[kMaxSplit], up[kMaxSplit];
+#pragma unroll
+  for (int z = 0; z < kMaxSplit; z++) {
+    const float* pp = a.part + ((size_t)z * a.T + t) * 2 * I;
+    const bool use = live && z < a.ksplit_g;
+    gp[z] = use ? pp[f] : 0.0f;
+    up[z] = use ? pp[I + f] : 0.0f;
+  }
+  float g = 0.0f, u = 0.0f;
+#pragma unroll
+  for (int z = 0; z < kMaxSplit; z++) {
+    g += gp[z];
+    u += up[z];
+  }
+  const float v = live ? silu(g) * u : 0.0f;
+  float sum = v;
+  sum += dpp_f32<0xB1>(sum);
+  sum += dpp_f32<0x4E>(sum);
+  sum += dpp_f32<0x141>(sum);
+  sum += dpp_f32<0x140>(sum);
+  if (!live) return;
+  const size_t row = (size_t)a.T * a.K + t;
+  const uint32_t hi = f32_to_f16_bits(v);
+  a.hh[row * a.I + f] = (uint16_t)hi;
+  a.hl[row * a.I + f] = (uint16_t)f32_to_f16_bits(v - f16_bits_to_f32(hi));
+  if ((f & 15) == 0) {
+    const uint32_t shi = f32_to_f16_bits(sum);
+    a.hsh[row * (a.I / 16) + f / 16] = (uint16_t)shi;
+    a.hsl[row * (a.I / 16) + f / 16] = (uint16_t)f32_to_f16_bits(sum - f16_bits_to_f32(shi));
+  }
+  if (!(fabsf(v) <= 65504.0f)) raise_fault(a.status, DS4MOE_FAULT_F16_RANGE);
+}
+
 // down for one work item and 64 output features.  Grid (H/64, max_items).
 // A (the SwiGLU rows) is staged per 256 columns as f16 hi/lo tiles with the
 // same swizzle as above, plus per-16-column sums (hi/lo) for the min term.
@@ -489,7 +677,9 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
   f32x4_t acc[4];
   for (int mt = 0; mt < 4; mt++) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const size_t rowd = (size_t)ee * a.H + n;
-  for (int kb = 0; kb < nb; kb++) {
+  // K share (shared-expert split, a.ksplit_d blocks along z)
+  const int ks = shr ? a.ksplit_d : 1, nbs = nb / ks, kb0 = blockIdx.z * nbs;
+  for (int kb = kb0; kb < kb0 + nbs; kb++) {
     // stage: thread -> (row m, 16-column sub-block j): 16 values, high and low parts
     for (int c = tid; c < kMC * 16; c += 256) {
       const int m = c >> 4, j = c & 15;
@@ -602,7 +792,10 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
     for (int r = 0; r < 4; r++) {
       if (mt >= mtiles) break;
       const int m = 16 * mt + 4 * q + r;
-      if (m < nrows) a.y[(size_t)(row0 + m) * a.H + n] = acc[mt][r];
+      if (m < nrows) {
+        if (ks == 1) a.y[(size_t)(row0 + m) * a.H + n] = acc[mt][r];
+        else a.part[((size_t)blockIdx.z * a.T + (row0 + m - a.T * a.K)) * a.H + n] = acc[mt][r];
+      }
     }
 }
 
