@@ -64,16 +64,21 @@ __device__ __noinline__ uint32_t f64_to_bf16_bits_general(double v) {
   return sign | (uint32_t)q;
 }
 
-// Same rounding; inline fast path for results in the normal bfloat16 range
-// (a carry out of the mantissa moves into the exponent by itself), the
-// general routine otherwise.
-__device__ inline uint32_t f64_to_bf16_bits(double v) {
+// Same rounding for results in the normal bfloat16 range (a carry out of
+// the mantissa moves into the exponent by itself); ok is false otherwise and
+// the result must then come from f64_to_bf16_bits_general.
+__device__ inline uint32_t f64_to_bf16_bits_fast(double v, bool& ok) {
   uint64_t b = __double_as_longlong(v);
   uint64_t r = b + 0x00000FFFFFFFFFFFULL + ((b >> 45) & 1);
   int e8 = (int)((r >> 52) & 0x7FF) - 1023 + 127;
-  if (e8 >= 1 && e8 <= 254 && (b & 0x7FFFFFFFFFFFFFFFULL) != 0)
-    return (uint32_t)((b >> 48) & 0x8000u) | ((uint32_t)e8 << 7) | (uint32_t)((r >> 45) & 0x7Fu);
-  return f64_to_bf16_bits_general(v);
+  ok = e8 >= 1 && e8 <= 254 && (b & 0x7FFFFFFFFFFFFFFFULL) != 0;
+  return (uint32_t)((b >> 48) & 0x8000u) | ((uint32_t)(e8 & 0xFF) << 7) | (uint32_t)((r >> 45) & 0x7Fu);
+}
+
+__device__ inline uint32_t f64_to_bf16_bits(double v) {
+  bool ok;
+  const uint32_t r = f64_to_bf16_bits_fast(v, ok);
+  return ok ? r : f64_to_bf16_bits_general(v);
 }
 
 // ---- packed dot products ----------------------------------------------------

@@ -195,11 +195,26 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, con
     for (int j = 0; j < kRegCols; j++) ss = fma((double)v[j], (double)v[j], ss);
     block_sum2(ss, dummy, sh);
     const double ns = 1.0 / sqrt(ss / (double)H + (double)eps);
+    // results outside the normal bfloat16 range (rare) take the general
+    // rounding in a separate pass, so the common loop has no call in it
+    uint32_t r[kRegCols];
+    bool all_ok = true;
+#pragma unroll
+    for (int j = 0; j < kRegCols; j++) {
+      bool ok;
+      r[j] = f64_to_bf16_bits_fast((double)v[j] * ns * (double)wv[j], ok);
+      all_ok &= ok;
+    }
+    if (!all_ok)
+      for (int j = 0; j < kRegCols; j++) {
+        bool ok;
+        (void)f64_to_bf16_bits_fast((double)v[j] * ns * (double)wv[j], ok);
+        if (!ok) r[j] = f64_to_bf16_bits_general((double)v[j] * ns * (double)wv[j]);
+      }
 #pragma unroll
     for (int j = 0; j < kRegCols; j++) {
       const int c = tid + 256 * j;
-      if (c < H)
-        xn[(size_t)t * H + c] = (uint16_t)f64_to_bf16_bits((double)v[j] * ns * (double)wv[j]);
+      if (c < H) xn[(size_t)t * H + c] = (uint16_t)r[j];
     }
     return;
   }

@@ -179,13 +179,24 @@ __global__ __launch_bounds__(256) void k_route_score(RouteArgs a) {
         const uint4 xv = ((const uint4*)((const uint16_t*)a.x + (size_t)t * a.H))[256 * j + tid];
         xx[0] = xv.x; xx[1] = xv.y; xx[2] = xv.z; xx[3] = xv.w;
       } else {
+        // rare results outside the normal bfloat16 range take the general
+        // rounding in a separate pass (no call in the common path)
+        uint32_t bb[8];
+        bool all_ok = true;
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-          const uint32_t lo = f64_to_bf16_bits((double)rr[j][2 * m] * nscale * (double)nw[j][2 * m]);
-          const uint32_t hi =
-              f64_to_bf16_bits((double)rr[j][2 * m + 1] * nscale * (double)nw[j][2 * m + 1]);
-          xx[m] = lo | (hi << 16);
+        for (int u = 0; u < 8; u++) {
+          bool ok;
+          bb[u] = f64_to_bf16_bits_fast((double)rr[j][u] * nscale * (double)nw[j][u], ok);
+          all_ok &= ok;
         }
+        if (!all_ok)
+          for (int u = 0; u < 8; u++) {
+            bool ok;
+            (void)f64_to_bf16_bits_fast((double)rr[j][u] * nscale * (double)nw[j][u], ok);
+            if (!ok) bb[u] = f64_to_bf16_bits_general((double)rr[j][u] * nscale * (double)nw[j][u]);
+          }
+#pragma unroll
+        for (int m = 0; m < 4; m++) xx[m] = bb[2 * m] | (bb[2 * m + 1] << 16);
         if (e == 0 && a.xn_out)
           ((uint4*)(a.xn_out + (size_t)t * a.H))[256 * j + tid] = make_uint4(xx[0], xx[1], xx[2], xx[3]);
       }
