@@ -316,7 +316,8 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     int32_t* perm = offsets + E + 1;
     int32_t* inv = perm + TK;
     int32_t* items = inv + TK;
-    const int mi = max_items(E, TK, T, sh != nullptr);
+    // grid rows: every possible work item, or just the shared expert's rows
+    const int mi = b1 ? (T + kMC - 1) / kMC : max_items(E, TK, T, sh != nullptr);
     int32_t* n_items = items + 3 * mi;
     ds4moe_status rc;
     {
