@@ -33,9 +33,10 @@ METRIC = "MoE layer tokens/s + expert-weight HBM GB/s (% of peak), batch-1 decod
 # the kernel source still hashes to what was measured.
 GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
-                "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h"),
-    "sha256": "6e4afeb16210e8d01c37d52f2cd8f2450ca9abb21476b26aa67da916737c9df5",
-    "bytes": 26242925,
+                "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
+                "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
+    "sha256": "2a9c6c050a80e46e40fed7cffed07d7440837ba6f38870ae9753fb266399fcca",
+    "bytes": 26323009,
 }
 
 
@@ -389,10 +390,12 @@ def bench_batched(args, which):
         touched_per = [int(np.unique(a).size) for a in ids_d[args.warmup:].cpu().numpy()]
         touched = float(np.mean(touched_per))
 
-    classes = {"permute": ds4.K_PERMUTE, "gateup": ds4.K_GATEUP, "down": ds4.K_DOWN,
-               "combine": ds4.K_OTHER}
-    if not prefill:
-        classes["route"] = ds4.K_ROUTE
+    if prefill:
+        classes = {"permute": ds4.K_PERMUTE, "gateup": ds4.K_GATEUP, "down": ds4.K_DOWN,
+                   "combine": ds4.K_OTHER}
+    else:  # few-token path: routed experts per token, then the shared expert as one class
+        classes = {"route": ds4.K_ROUTE, "gateup": ds4.K_GATEUP, "down": ds4.K_DOWN,
+                   "shared_expert": ds4.K_OTHER}
     n_prof = min(args.steps, 50)
     evs = {c: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n_prof)] for c in classes}
@@ -415,8 +418,10 @@ def bench_batched(args, which):
     step_bytes = touched * per_expert + sh_bytes
     sec = ms * 1e-3 / args.steps
     flops = 2.0 * T * (3 * w.H * w.I) * (w.K + (1 if w.shared else 0))
-    gu_bytes = touched * gateup_expert + (2 * sh_bytes // 3)
-    gu_flops = 2.0 * T * (2 * w.H * w.I) * (w.K + (1 if w.shared else 0))
+    # dominant kernel: gate/up of the routed experts; algorithmic bytes = the
+    # distinct experts' gate and up tensors (repeats within a step are cache hits)
+    gu_bytes = touched * gateup_expert
+    gu_flops = 2.0 * T * (2 * w.H * w.I) * w.K
     gu_s = kern_us["gateup"] * 1e-6
     res = {
         "metric": ("prefill tokens/s through one routed-expert layer" if prefill
@@ -433,7 +438,7 @@ def bench_batched(args, which):
         "mfma_tflops": round(flops / sec / 1e12, 2),
         "mfma_frac": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
-        "roofline": {"bound": "hbm", "kernel": "k_grouped_gateup",
+        "roofline": {"bound": "hbm", "kernel": "k_grouped_gateup_iq2" if prefill else "k_gateup_b1",
                      "achieved": round(gu_bytes / gu_s / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gu_bytes / gu_s / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": None, "bytes_per_launch": int(gu_bytes),

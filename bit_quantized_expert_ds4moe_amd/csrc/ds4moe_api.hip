@@ -88,8 +88,13 @@ struct ProfScope {
   int cls;
   bool started = false;
   ProfScope* prev;
-  ProfScope(int c, hipStream_t) : cls(c), prev(active) { active = this; }
-  ~ProfScope() { active = prev; }
+  bool on;  // a disabled scope leaves its kernels to the enclosing one
+  ProfScope(int c, hipStream_t, bool enabled = true) : cls(c), prev(active), on(enabled) {
+    if (on) active = this;
+  }
+  ~ProfScope() {
+    if (on) active = prev;
+  }
 };
 ProfScope* ProfScope::active = nullptr;
 
@@ -310,6 +315,8 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     if (rc != DS4MOE_OK || !sh) return rc;
   }
   if (b1 || (T > 1 && grouped_eligible(s, ex, sh, x, x_dt, T))) {
+    // after the few-token path, the shared expert's kernels time as one class
+    ProfScope shared_only(DS4MOE_K_OTHER, st, b1);
     const int E = s.n_expert, K = s.top_k, TK = T * K;
     int32_t* counts = at<int32_t>(ws, L.perm);
     int32_t* offsets = counts + E;
@@ -321,7 +328,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     int32_t* n_items = items + 3 * mi;
     ds4moe_status rc;
     {
-      ProfScope prof(DS4MOE_K_PERMUTE, st);
+      ProfScope prof(DS4MOE_K_PERMUTE, st, !b1);
       if (b1) {  // the routed experts are done: the shared expert's rows only
         launch_k(k_make_shared_items, dim3(1), dim3(64), 0, st, E, TK, T, items, n_items);
       } else {
@@ -377,7 +384,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     g.status = status;
     const int imax = g.I > g.sh_I ? g.I : g.sh_I;
     {
-      ProfScope prof(DS4MOE_K_GATEUP, st);
+      ProfScope prof(DS4MOE_K_GATEUP, st, !b1);
       const bool iq2 = g.qt_g == DS4MOE_IQ2_XXS && g.qt_u == DS4MOE_IQ2_XXS && g.I % kGNF == 0;
       const bool q80 = sh && q80_shared_fast(g);
       if (iq2 && !b1) launch_k(k_grouped_gateup_iq2, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
@@ -393,7 +400,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     {
-      ProfScope prof(DS4MOE_K_DOWN, st);
+      ProfScope prof(DS4MOE_K_DOWN, st, !b1);
       const bool q2k = g.qt_d == DS4MOE_Q2_K && g.H % kDNF == 0;
       if (q2k && !b1) launch_k(k_grouped_down_q2k, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
       if (!q2k || sh)
@@ -401,7 +408,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     {
-      ProfScope prof(DS4MOE_K_OTHER, st);
+      ProfScope prof(DS4MOE_K_OTHER, st, !b1);
       const size_t n = (size_t)T * s.hidden;
       if (b1)
         launch_k(k_add_shared, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
