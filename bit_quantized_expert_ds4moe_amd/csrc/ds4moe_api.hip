@@ -277,7 +277,7 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   if (rc != DS4MOE_OK) return rc;
   {
     ProfScope prof(DS4MOE_K_DOWN, st);
-    launch_k(k_down_q2k_b1, dim3(kH / kDnRows, kbuf ? 1 : T), dim3(384), 0, st, h,
+    launch_k(k_down_q2k_b1, dim3(kH / kDnBlockRows, kbuf ? 1 : T), dim3(kDnThreads), 0, st, h,
              (const uint8_t*)ex.down,
                        kbuf ? ids : ids_in, wts, s.n_expert, out, residual, status);
   }

@@ -120,21 +120,28 @@ __device__ inline float iq2_dot16(const Iq2Seg& sg, uint32_t sh, const uint32_t*
 #pragma unroll
   for (int grp = 0; grp < 2; grp++) {
     const uint32_t idxw = g[2 * grp], sw = g[2 * grp + 1];
-    float gacc = 0.0f;
+    // all eight table reads of the group first, so that one LDS round trip
+    // covers four entries
+    uint4 gv[4], mv[4];
 #pragma unroll
     for (int kk = 0; kk < 4; kk++) {
       const uint32_t ga = vperm(idxw, rep16, 0x0C0C0000u | ((4u + kk) << 8));
       const uint32_t sa = (((sw >> (7 * kk)) & 0x7Fu) << 8) | rep16;
-      const uint4 gv = *(const uint4*)(gtab + ga);
-      const uint4 mv = *(const uint4*)(stab + sa);
+      gv[kk] = *(const uint4*)(gtab + ga);
+      mv[kk] = *(const uint4*)(stab + sa);
+    }
+    float ga0 = 0.0f, ga1 = 0.0f;  // two chains of dependent dot products
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
       const uint32_t* xp = xr + grp * 16 + kk * 4;
-      gacc = dot2_bf16(gv.x ^ mv.x, xp[0], gacc);
-      gacc = dot2_bf16(gv.y ^ mv.y, xp[1], gacc);
-      gacc = dot2_bf16(gv.z ^ mv.z, xp[2], gacc);
-      gacc = dot2_bf16(gv.w ^ mv.w, xp[3], gacc);
+      float& ac = (kk & 1) ? ga1 : ga0;
+      ac = dot2_bf16(gv[kk].x ^ mv[kk].x, xp[0], ac);
+      ac = dot2_bf16(gv[kk].y ^ mv[kk].y, xp[1], ac);
+      ac = dot2_bf16(gv[kk].z ^ mv[kk].z, xp[2], ac);
+      ac = dot2_bf16(gv[kk].w ^ mv[kk].w, xp[3], ac);
     }
     // 16s + 8 from the top nibble: exact in fp32
-    acc = fmaf((float)(((sw & 0xF0000000u) | 0x08000000u) >> 24), gacc, acc);
+    acc = fmaf((float)(((sw & 0xF0000000u) | 0x08000000u) >> 24), ga0 + ga1, acc);
   }
   return acc * (d * 0.015625f);
 }
@@ -185,7 +192,7 @@ struct GateUpB1Args {
   uint32_t* status;
 };
 
-constexpr int kDnRows = 4;                                   // down rows per wave
+constexpr int kDnRows = 8;                                   // down rows per wave
 constexpr int kGuWaves = 16;                                  // waves per workgroup
 constexpr int kGuRows = 3;                                    // rows (gate + up) per wave
 constexpr int kGuBlocks = 6 * kI / (kGuWaves * kGuRows);      // 256
@@ -262,9 +269,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
     iq2_load((const uint32_t*)(a.up + rowi * kRowIq2), 0, off, su[r]);
   };
   // Without selection: two rows in flight from the start, the third issued
-  // once the first has been consumed (with every row of every wave requested
-  // at once, each wave's data tends to complete only near the end of the
-  // whole transfer).
+  // after the table build.
   static_assert(kGuRows == 3, "the load schedule assumes three rows per wave");
   if (!SEL) {
     expert_rows(nullptr, erow);
@@ -300,6 +305,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
     load_row(0);
     load_row(1);
     load_row(2);
+  } else {
+    load_row(2);
   }
 
   uint32_t xr[32];
@@ -321,7 +328,6 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
   float v[8];
   v[0] = iq2_dot16(sg[0], sh, xr, gtab, stab, rep16);
   v[4] = iq2_dot16(su[0], sh, xr, gtab, stab, rep16);
-  if (!SEL) load_row(2);
 #pragma unroll
   for (int r = 1; r < kGuRows; r++) {
     v[r] = iq2_dot16(sg[r], sh, xr, gtab, stab, rep16);
@@ -341,8 +347,11 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
 }
 
 // down + weighted combine (+ residual) for one token.
-// Grid H/kDnRows workgroups of 6 waves: wave k handles routed slot k for
-// kDnRows rows.
+// Grid (H / kDnBlockRows, T), 12 waves: wave w handles routed slot k = w / 2
+// for kDnRows rows (w odd: the second half of the workgroup's 16 rows).
+// The token's six SwiGLU vectors (48 KB) are read once per workgroup into
+// LDS before any weight is requested (the vector memory path of a compute
+// unit returns data in request order, so h must not queue behind weights).
 // Lane L = 8b + 4hh + c of a wave covers the 32 columns
 // i = 256b + 128hh + 32s + 8c + j (s < 4, j < 8) of every row: the 8 code
 // bytes qs[32hh + 8c .. +7] of block b hold exactly their 2-bit codes.  The
@@ -351,17 +360,32 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
 // 2^-16 of the chunk maximum; every later product is exact):
 //   nr[4s + m] = (n[8s + 2m], n[8s + 2m + 1]) as int16 pairs,
 //   xs[s] = sum_j n[8s + j]   (for the min term).
-__global__ __launch_bounds__(384) void k_down_q2k_b1(const float* __restrict__ h,
-                                                     const uint8_t* __restrict__ down,
-                                                     const int32_t* __restrict__ ids,
-                                                     const float* __restrict__ wts, int E,
-                                                     float* __restrict__ out,
-                                                     float* __restrict__ residual,
-                                                     uint32_t* status) {
+// The h vectors sit in LDS as 16-byte chunks; chunk G of a slot (G = f / 4
+// for value f) is stored at G ^ q0 ^ (q1 << 3), q = (G >> 5) & 3, so that the
+// 16 lanes one 16-byte LDS read serves hit 16 distinct bank groups.
+constexpr int kDnBlockRows = 2 * kDnRows;  // 16 output rows per workgroup
+constexpr int kDnThreads = 12 * 64;
+
+__device__ inline int dn_chunk(int G) {
+  const int q = (G >> 5) & 3;
+  return G ^ (q & 1) ^ ((q >> 1) << 3);
+}
+
+__global__ __launch_bounds__(kDnThreads) void k_down_q2k_b1(const float* __restrict__ h,
+                                                            const uint8_t* __restrict__ down,
+                                                            const int32_t* __restrict__ ids,
+                                                            const float* __restrict__ wts, int E,
+                                                            float* __restrict__ out,
+                                                            float* __restrict__ residual,
+                                                            uint32_t* status) {
   constexpr int R = kDnRows;
-  __shared__ float part[6][R];
+  constexpr int kChunks = 6 * kI / 4;  // 16-byte chunks of h
+  static_assert(kChunks % kDnThreads == 0, "h chunks must tile the workgroup");
+  __shared__ float4 hs[kChunks];  // 48 KB
+  __shared__ float part[6][kDnBlockRows];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int k = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform slot
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int k = w >> 1, rh = w & 1;
   const int b = lane >> 3, q8 = lane & 7, hh = q8 >> 2, c = q8 & 3;
   // token t = blockIdx.y
   const int tok = blockIdx.y;
@@ -370,24 +394,25 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const float* __restrict__ h
   wts += 6 * tok;
   if (out) out += (size_t)tok * kH;
   if (residual) residual += (size_t)tok * kH;
-  // the SwiGLU values first (the vector memory counter retires in order:
-  // waiting for them then never waits for the weights)
-  float hv[32];
-  {
-    const float4* hp = (const float4*)(h + k * kI + 256 * b + 128 * hh + 8 * c);
-#pragma unroll
-    for (int s = 0; s < 4; s++) {
-      const float4 p0 = hp[8 * s], p1 = hp[8 * s + 1];
-      hv[8 * s + 0] = p0.x; hv[8 * s + 1] = p0.y; hv[8 * s + 2] = p0.z; hv[8 * s + 3] = p0.w;
-      hv[8 * s + 4] = p1.x; hv[8 * s + 5] = p1.y; hv[8 * s + 6] = p1.z; hv[8 * s + 7] = p1.w;
-    }
-  }
+  // 1. h into LDS
+  static_assert(kChunks == 4 * kDnThreads, "four h chunks per thread");
+  const float4* hg = (const float4*)h + tid;
+  const float4 hc0 = hg[0], hc1 = hg[kDnThreads], hc2 = hg[2 * kDnThreads], hc3 = hg[3 * kDnThreads];
+  auto put = [&](int q, float4 v) {
+    const int G = tid + kDnThreads * q;
+    hs[(G & ~511) | dn_chunk(G & 511)] = v;
+  };
+  put(0, hc0);
+  put(1, hc1);
+  put(2, hc2);
+  put(3, hc3);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // 2. this wave's weights, requested only once the whole workgroup has its
+  // h: in the other order the h lines queue behind weight traffic
   int e = load_scalar_i32(ids, k);
-  if (e < 0 || e >= E) {
-    if (lane == 0 && blockIdx.x == 0) raise_fault(status, DS4MOE_FAULT_BAD_ID);
-    e = 0;
-  }
-  const int row0 = blockIdx.x * R;  // output rows of token tok
+  const bool bad_id = e < 0 || e >= E;
+  e = bad_id ? 0 : e;
+  const int row0 = blockIdx.x * kDnBlockRows + rh * R;  // output rows of token tok
   const uint8_t* base = down + ((size_t)e * kH + row0) * kRowQ2k + b * kQ2kBytes;
   const int qoff = 16 + 32 * hh + 8 * c, soff = 8 * hh;
   uint2 qv[R], sv[R];
@@ -399,14 +424,27 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const float* __restrict__ h
     sv[r] = *(const uint2*)(blk + soff);
     dd[r] = *(const uint32_t*)(blk + 80);
   }
+  // 3. this lane's 32 values of slot k, as 16-bit fixed point
+  float hv[32];
+  {
+    const int G0 = 64 * b + 32 * hh + 2 * c;  // chunk of s = 0, first half
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const float4 p0 = hs[512 * k + dn_chunk(G0 + 8 * s)];
+      const float4 p1 = hs[512 * k + dn_chunk(G0 + 8 * s + 1)];
+      hv[8 * s + 0] = p0.x; hv[8 * s + 1] = p0.y; hv[8 * s + 2] = p0.z; hv[8 * s + 3] = p0.w;
+      hv[8 * s + 4] = p1.x; hv[8 * s + 5] = p1.y; hv[8 * s + 6] = p1.z; hv[8 * s + 7] = p1.w;
+    }
+  }
   uint32_t nr[16];
   int xn[4];
   float S;
+  bool h_range;
   {
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; i++) m = fmaxf(m, fabsf(hv[i]));
-    if (!(m <= 3.0e38f)) raise_fault(status, DS4MOE_FAULT_F16_RANGE);
+    h_range = !(m <= 3.0e38f);
     const float inv = m > 0.0f ? 1.0f / m : 0.0f;
 #pragma unroll
     for (int q = 0; q < 16; q++)
@@ -421,6 +459,7 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const float* __restrict__ h
     }
     S = m * (1.0f / 32767.0f);
   }
+  // 4. the rows
   const float wS = __int_as_float(load_scalar_i32((const int32_t*)wts, k)) * S;
   const uint32_t cb = (uint32_t)(c >> 1);
   const uint32_t ssel = cb | ((cb + 2) << 8) | ((cb + 4) << 16) | ((cb + 6) << 24);
@@ -439,27 +478,31 @@ __global__ __launch_bounds__(384) void k_down_q2k_b1(const float* __restrict__ h
       t = sdot2(p2 & mk, nr[4 * s + 2], t);
       t = sdot2(p3 & mk, nr[4 * s + 3], t);
       t >>= 2 * s;  // codes were read in place, i.e. times 4^s; exact
-      A += (int)((S4 >> (8 * s)) & 0xFu) * t;
-      B += (int)((S4 >> (8 * s + 4)) & 0xFu) * xn[s];
+      // |t| <= 3 * 8 * 32767 and |xn| <= 8 * 32767 fit 24 bits: full-rate
+      // 24-bit multiply-adds, exact
+      A = __mul24((int)((S4 >> (8 * s)) & 0xFu), t) + A;
+      B = __mul24((int)((S4 >> (8 * s + 4)) & 0xFu), xn[s]) + B;
     }
     float d = f16_bits_to_f32(dd[r] & 0xFFFFu), dmin = f16_bits_to_f32(dd[r] >> 16);
     pr[r] = wS * fmaf(-dmin, (float)B, d * (float)A);
   }
-#pragma unroll
-  for (int r = R; r < 8; r++) pr[r] = 0.0f;
+  static_assert(R == 8, "one reduction covers the eight rows of a wave");
   const float tot = reduce8(pr);
   if ((lane & 7) == 0) {
     const int rho = lane >> 4, eta = (lane >> 3) & 1;
     const int r = 4 * eta + ((rho == 1) ? 2 : (rho == 2) ? 1 : rho);
-    if (r < R) part[k][r] = tot;
+    part[k][rh * R + r] = tot;
   }
   __syncthreads();
-  if (tid < R) {
+  if (tid < kDnBlockRows) {
     float acc = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) +
                 (part[4][tid] + part[5][tid]);
-    if (residual) residual[row0 + tid] += acc;
-    else out[row0 + tid] = acc;
+    const int row = blockIdx.x * kDnBlockRows + tid;
+    if (residual) residual[row] += acc;
+    else out[row] = acc;
   }
+  if (bad_id && lane == 0 && blockIdx.x == 0 && rh == 0) raise_fault(status, DS4MOE_FAULT_BAD_ID);
+  if (h_range) raise_fault(status, DS4MOE_FAULT_F16_RANGE);
 }
 
 }  // namespace ds4

@@ -99,9 +99,6 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
   return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)),
                 umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
-__device__ inline float pick4(const float* a, int j) {
-  return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
-}
 __device__ inline float readlane_f32(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
@@ -247,44 +244,43 @@ __device__ inline uint32_t key_order(float key) {
   const uint32_t u = __float_as_uint(key);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// Maximum over the 64 lanes, left in every lane: DPP maxima inside rows of
+// 16, then the two lane-swap steps across rows (no scalar round trip).
 __device__ inline uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
-  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
-             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max((uint32_t)h[0], (uint32_t)h[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max((uint32_t)q[0], (uint32_t)q[1]);
 }
 
-// Top-K selection for one token by one wave, from the E key intervals of
-// k_route_score: K rounds of "largest key, lowest expert index among equal
-// keys" (a wave maximum of the key codes, then the first expert whose code
-// equals it).  On return lane k < K holds slot k: expert id in e_out and gate
-// in w_out.  When report is set, an uncertified order raises the fault bit.
-// Deterministic: every wave that runs it on the same keys gets the same
-// answer.
+// Top-K selection for one token by one wave, from the E <= 256 key intervals
+// of k_route_score: K rounds of "largest key, lowest expert index among
+// equal keys" (a wave maximum of the key codes, then the first expert whose
+// code equals it).  Lane k < K records the k-th expert; the winners' scores
+// and intervals are read back afterwards (one load per lane, from lines the
+// wave has just read), so a round carries no per-winner lookups.  On return
+// lane k < K holds slot k: expert id in e_out and gate in w_out.  When report
+// is set, an uncertified order raises the fault bit.  Deterministic: every
+// wave that runs it on the same keys gets the same answer.
 __device__ inline void select_wave(const float4* kb, int E, int K, float scale, uint32_t* status,
                                    bool report, int& e_out, float& w_out) {
   const int lane = threadIdx.x & 63;
   uint32_t ko[4];
-  float sc[4], kl[4], kh[4];
+  float kh[4];
   bool wide = false;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int ee = lane + 64 * j;
     const float4 v = ee < E ? kb[ee] : make_float4(0, 0, 0, 0);
     ko[j] = ee < E ? key_order(v.x) : 0u;
-    kl[j] = v.y;
     kh[j] = v.z;
-    sc[j] = v.w;
     wide |= ee < E && (v.y != v.z);
   }
-  wide = __any(wide);
-  int sel_e[kMaxRouteK];
-  float sel_s[kMaxRouteK];
-  bool ok = true;
-  float prev_lo = 0.0f;
-  int prev_e = -1;
+  int e_sel = 0;  // lane k: the k-th winner
   for (int k = 0; k < K; k++) {
     const uint32_t m = wave_max_u32(max(max(ko[0], ko[1]), max(ko[2], ko[3])));
     int be = 0;
@@ -293,38 +289,33 @@ __device__ inline void select_wave(const float4* kb, int E, int K, float scale, 
       const unsigned long long bal = __ballot(ko[j] == m);
       if (bal) be = 64 * j + __ffsll((long long)bal) - 1;
     }
-    const int owner = be & 63, slot = be >> 6;
 #pragma unroll
     for (int j = 0; j < 4; j++)
       if (lane + 64 * j == be) ko[j] = 0u;
-    sel_e[k] = be;
-    sel_s[k] = readlane_f32(pick4(sc, slot), owner);
-    if (wide) {
-      const float lo = readlane_f32(pick4(kl, slot), owner), hi = readlane_f32(pick4(kh, slot), owner);
-      if (prev_e >= 0 && !(prev_lo > hi || (prev_lo == hi && prev_e < be))) ok = false;
-      prev_lo = lo;
-      prev_e = be;
-    }
+    if (lane == k) e_sel = be;
   }
-  if (wide) {
-    // the last selected expert must precede every unselected one
+  const float4 win = lane < K ? kb[e_sel] : make_float4(0, 0, 0, 0);  // key, lo, hi, score
+  if (__any(wide)) {
+    bool ok = true;
+    // consecutive winners: the interval of winner k-1 lies above that of k
+    const float plo = __shfl_up(win.y, 1);
+    const int pe = __shfl_up(e_sel, 1);
+    if (lane >= 1 && lane < K && !(plo > win.z || (plo == win.z && pe < e_sel))) ok = false;
+    // the last winner precedes every unselected expert
+    const float last_lo = readlane_f32(win.y, K - 1);
+    const int last_e = __builtin_amdgcn_readlane(e_sel, K - 1);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int ee = lane + 64 * j;
-      if (ee < E && ko[j] != 0u && !(prev_lo > kh[j] || (prev_lo == kh[j] && prev_e < ee)))
+      if (ee < E && ko[j] != 0u && !(last_lo > kh[j] || (last_lo == kh[j] && last_e < ee)))
         ok = false;
     }
     if (__any(!ok) && lane == 0 && report) raise_fault(status, DS4MOE_FAULT_UNCERTIFIED);
   }
   double ssum = 0.0;
-  for (int k = 0; k < K; k++) ssum += (double)sel_s[k];
-  e_out = 0;
-  w_out = 0.0f;
-  for (int k = 0; k < K; k++)
-    if (lane == k) {
-      e_out = sel_e[k];
-      w_out = (float)((double)scale * (double)sel_s[k] / ssum);
-    }
+  for (int k = 0; k < K; k++) ssum += (double)readlane_f32(win.w, k);
+  e_out = lane < K ? e_sel : 0;
+  w_out = lane < K ? (float)((double)scale * (double)win.w / ssum) : 0.0f;
 }
 
 // Selection kernel.  Grid T, one wave per token: reads the key intervals

@@ -88,6 +88,61 @@ def test_route_ties_and_bias():
     np.testing.assert_allclose(wts, owts, rtol=2e-6)
 
 
+def tied_router(w):
+    """Router with experts 10, 74 (same lane slot set), 138 and 200 given
+    identical keys that beat all others but expert 77: the order must be
+    77, 10, 74, 138, 200 (equal keys go to the lower index)."""
+    W = g.router_weight(w, 0).copy()
+    b = g.router_bias(w, 0).copy()
+    for e in (74, 138, 200):
+        W[e] = W[10]
+    b[[10, 74, 138, 200]] = 30.0
+    b[77] = 50.0
+    return W, b
+
+
+def test_route_many_ties():
+    w = g.WORKLOADS[1]
+    T = 4
+    x = g.activations(w, n_tok=T)
+    W, b = tied_router(w)
+    ids, wts = run_route(w, dev(x), dev(W), dev(b), T)
+    oids, owts, _, _ = oracle.route(x, "bf16", W, "f16", b, w.K)
+    np.testing.assert_array_equal(ids, oids)
+    assert np.all(ids[:, :5] == [77, 10, 74, 138, 200])
+    np.testing.assert_allclose(wts, owts, rtol=2e-6)
+
+
+def test_layer_fused_selection_ties():
+    """Batch-1 layer call (selection fused into the gate/up kernel) on tied keys."""
+    from ds4gen.device import make_layer, host_experts
+    w = g.WORKLOADS[1]
+    say("layer fused selection ties")
+    lt = make_layer(w, 0)
+    W, b = tied_router(w)
+    x = g.activations(w, n_tok=1)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, 1)
+    Wd, bd = dev(W), dev(b)
+    d = ds4.layer_desc(ds4.router(w=ptr(Wd), w_dtype=ds4.F16, bias=ptr(bd)), experts_of(lt, w))
+    out = torch.empty((1, w.H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((1, w.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((1, w.K), dtype=torch.float32, device="cuda")
+    xd = dev(x)
+    ds4.layer(shp, d, ptr(xd), x_dtype(w), None, ptr(out), None, 1, ptr(ids), ptr(wts), None,
+              ptr(ws), nb, stream())
+    check_clean(ws)
+    oids, owts, _, _ = oracle.route(x, "bf16", W, "f16", b, w.K)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    assert list(oids[0, :5]) == [77, 10, 74, 138, 200]
+    np.testing.assert_allclose(wts.cpu().numpy(), owts, rtol=2e-6)
+    want = oracle.moe_ffn(x, "bf16", oids, owts, host_experts(w, 0, np.unique(oids)),
+                          (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed))
+    err = max_rel_err(out.cpu().numpy(), want)
+    say("  max|err|/rms =", err)
+    assert err <= TOL_FP32
+
+
 def test_hash_route_is_table_lookup():
     w = g.WORKLOADS[4]
     say("hash route")
