@@ -348,27 +348,54 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
 
 // down + weighted combine (+ residual) for one token.
 // Grid (H / kDnBlockRows, T), 12 waves: wave w handles routed slot k = w / 2
-// for kDnRows rows (w odd: the second half of the workgroup's 16 rows).
+// for kDnRows rows (w odd: the second half of the workgroup's 16 rows), two
+// rows per step: lanes 0-31 take the even row, lanes 32-63 the odd one.
 // The token's six SwiGLU vectors (48 KB) are read once per workgroup into
 // LDS before any weight is requested (the vector memory path of a compute
 // unit returns data in request order, so h must not queue behind weights).
-// Lane L = 8b + 4hh + c of a wave covers the 32 columns
-// i = 256b + 128hh + 32s + 8c + j (s < 4, j < 8) of every row: the 8 code
-// bytes qs[32hh + 8c .. +7] of block b hold exactly their 2-bit codes.  The
-// lane first turns its 32 SwiGLU values into 16-bit fixed point with one
-// scale, h_i ~= S n_i, n_i = round(32767 h_i / max|h|) (relative error below
-// 2^-16 of the chunk maximum; every later product is exact):
-//   nr[4s + m] = (n[8s + 2m], n[8s + 2m + 1]) as int16 pairs,
-//   xs[s] = sum_j n[8s + j]   (for the min term).
+// Lane 32u + L (L < 32), b = L >> 2, hq = (L >> 1) & 1, p = L & 1, covers
+// the 64 columns i = 256b + 128hq + 32s + 16p + l (s < 4, l < 16) of its
+// row: their 2-bit codes are exactly the 16 bytes qs[32hq + 16p .. +15] of
+// block b (one 16-byte load), their sub-blocks are j = 8hq + 2s + p (scale
+// bytes 8hq + p + 2s, inside the 8 bytes at 8hq), and d, dmin sit at byte 80:
+// three loads per lane serve two rows.  The lane first turns its 64 SwiGLU
+// values into 16-bit fixed point with one scale, h_i ~= S n_i,
+// n_i = round(32767 h_i / max|h|) (relative error below 2^-16 of the chunk
+// maximum; every later product is exact):
+//   nr[8s + q] = (n[16s + 2q], n[16s + 2q + 1]) as int16 pairs,
+//   xn[s] = sum_l n[16s + l]   (for the min term).
 // The h vectors sit in LDS as 16-byte chunks; chunk G of a slot (G = f / 4
-// for value f) is stored at G ^ q0 ^ (q1 << 3), q = (G >> 5) & 3, so that the
-// 16 lanes one 16-byte LDS read serves hit 16 distinct bank groups.
+// for value f) is stored at G ^ ((G >> 6) & 3) ^ (((G >> 5) & 1) << 3), so
+// that the 16 lanes one 16-byte LDS read serves hit 16 distinct bank groups.
 constexpr int kDnBlockRows = 2 * kDnRows;  // 16 output rows per workgroup
 constexpr int kDnThreads = 12 * 64;
 
 __device__ inline int dn_chunk(int G) {
-  const int q = (G >> 5) & 3;
-  return G ^ (q & 1) ^ ((q >> 1) << 3);
+  return G ^ ((G >> 6) & 3) ^ (((G >> 5) & 1) << 3);
+}
+
+// Sums over the 32 lanes of each wave half of four per-lane values at once
+// (value m of half u is row 2m + u of the wave).  Lane L ends up holding the
+// total of m = (rho & 1) + 2 * ((L >> 3) & 1), u = rho >> 1, rho = L >> 4;
+// every lane of an aligned group of 8 holds the same total.
+__device__ inline float reduce4x2(const float* v) {
+  float w[2];
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    // rows of 16: row 0 <- v[2q] (half 0), row 1 <- v[2q+1] (half 0),
+    // row 2 <- v[2q] (half 1), row 3 <- v[2q+1] (half 1)
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[2 * q]),
+                                              __float_as_uint(v[2 * q + 1]), false, false);
+    w[q] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  // within rows of 16: lanes 0-7 <- w[0], lanes 8-15 <- w[1]
+  const bool up8 = (threadIdx.x & 8) != 0;
+  const float t = up8 ? w[0] : w[1];
+  float z = (up8 ? w[1] : w[0]) + dpp_f32<0x128>(t);  // row_ror:8
+  z += dpp_f32<0xB1>(z);
+  z += dpp_f32<0x4E>(z);
+  z += dpp_f32<0x141>(z);
+  return z;
 }
 
 __global__ __launch_bounds__(kDnThreads) void k_down_q2k_b1(const float* __restrict__ h,
@@ -380,13 +407,13 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q2k_b1(const float* __restr
                                                             uint32_t* status) {
   constexpr int R = kDnRows;
   constexpr int kChunks = 6 * kI / 4;  // 16-byte chunks of h
-  static_assert(kChunks % kDnThreads == 0, "h chunks must tile the workgroup");
+  static_assert(R == 8, "four steps of two rows per wave");
   __shared__ float4 hs[kChunks];  // 48 KB
   __shared__ float part[6][kDnBlockRows];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int k = w >> 1, rh = w & 1;
-  const int b = lane >> 3, q8 = lane & 7, hh = q8 >> 2, c = q8 & 3;
+  const int u = lane >> 5, L = lane & 31, b = L >> 2, hq = (L >> 1) & 1, p = L & 1;
   // token t = blockIdx.y
   const int tok = blockIdx.y;
   h += (size_t)tok * 6 * kI;
@@ -394,6 +421,9 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q2k_b1(const float* __restr
   wts += 6 * tok;
   if (out) out += (size_t)tok * kH;
   if (residual) residual += (size_t)tok * kH;
+  // the expert id and gate first: the weight addresses wait for the id
+  int e = load_scalar_i32(ids, k);
+  const float wk = __int_as_float(load_scalar_i32((const int32_t*)wts, k));
   // 1. h into LDS
   static_assert(kChunks == 4 * kDnThreads, "four h chunks per thread");
   const float4* hg = (const float4*)h + tid;
@@ -409,89 +439,92 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q2k_b1(const float* __restr
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   // 2. this wave's weights, requested only once the whole workgroup has its
   // h: in the other order the h lines queue behind weight traffic
-  int e = load_scalar_i32(ids, k);
   const bool bad_id = e < 0 || e >= E;
   e = bad_id ? 0 : e;
   const int row0 = blockIdx.x * kDnBlockRows + rh * R;  // output rows of token tok
-  const uint8_t* base = down + ((size_t)e * kH + row0) * kRowQ2k + b * kQ2kBytes;
-  const int qoff = 16 + 32 * hh + 8 * c, soff = 8 * hh;
-  uint2 qv[R], sv[R];
-  uint32_t dd[R];
+  const uint8_t* base = down + ((size_t)e * kH + row0 + u) * kRowQ2k + b * kQ2kBytes;
+  uint4 cv[R / 2];
+  uint2 sc[R / 2];
+  uint32_t dd[R / 2];
 #pragma unroll
-  for (int r = 0; r < R; r++) {
-    const uint8_t* blk = base + r * kRowQ2k;
-    qv[r] = *(const uint2*)(blk + qoff);
-    sv[r] = *(const uint2*)(blk + soff);
-    dd[r] = *(const uint32_t*)(blk + 80);
+  for (int m = 0; m < R / 2; m++) {
+    const uint8_t* blk = base + 2 * m * kRowQ2k;
+    cv[m] = *(const uint4*)(blk + 16 + 32 * hq + 16 * p);
+    sc[m] = *(const uint2*)(blk + 8 * hq);
+    dd[m] = *(const uint32_t*)(blk + 80);
   }
-  // 3. this lane's 32 values of slot k, as 16-bit fixed point
-  float hv[32];
+  // 3. this lane's 64 values of slot k, as 16-bit fixed point
+  float hv[64];
   {
-    const int G0 = 64 * b + 32 * hh + 2 * c;  // chunk of s = 0, first half
+    const int G0 = 64 * b + 32 * hq + 4 * p;  // chunk of s = 0
 #pragma unroll
-    for (int s = 0; s < 4; s++) {
-      const float4 p0 = hs[512 * k + dn_chunk(G0 + 8 * s)];
-      const float4 p1 = hs[512 * k + dn_chunk(G0 + 8 * s + 1)];
-      hv[8 * s + 0] = p0.x; hv[8 * s + 1] = p0.y; hv[8 * s + 2] = p0.z; hv[8 * s + 3] = p0.w;
-      hv[8 * s + 4] = p1.x; hv[8 * s + 5] = p1.y; hv[8 * s + 6] = p1.z; hv[8 * s + 7] = p1.w;
-    }
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+      for (int m4 = 0; m4 < 4; m4++) {
+        const float4 q = hs[512 * k + dn_chunk(G0 + 8 * s + m4)];
+        hv[16 * s + 4 * m4 + 0] = q.x;
+        hv[16 * s + 4 * m4 + 1] = q.y;
+        hv[16 * s + 4 * m4 + 2] = q.z;
+        hv[16 * s + 4 * m4 + 3] = q.w;
+      }
   }
-  uint32_t nr[16];
+  uint32_t nr[32];
   int xn[4];
   float S;
   bool h_range;
   {
-    float m = 0.0f;
+    float mx = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; i++) m = fmaxf(m, fabsf(hv[i]));
-    h_range = !(m <= 3.0e38f);
-    const float inv = m > 0.0f ? 1.0f / m : 0.0f;
+    for (int i = 0; i < 64; i++) mx = fmaxf(mx, fabsf(hv[i]));
+    h_range = !(mx <= 3.0e38f);
+    const float inv = mx > 0.0f ? 1.0f / mx : 0.0f;
 #pragma unroll
-    for (int q = 0; q < 16; q++)
+    for (int q = 0; q < 32; q++)
       nr[q] = (uint32_t)__builtin_bit_cast(
           int, __builtin_amdgcn_cvt_pknorm_i16(hv[2 * q] * inv, hv[2 * q + 1] * inv));
 #pragma unroll
     for (int s = 0; s < 4; s++) {
-      int t = sdot2(nr[4 * s], 0x00010001u, 0);
-      t = sdot2(nr[4 * s + 1], 0x00010001u, t);
-      t = sdot2(nr[4 * s + 2], 0x00010001u, t);
-      xn[s] = sdot2(nr[4 * s + 3], 0x00010001u, t);
+      int t = 0;
+#pragma unroll
+      for (int q = 0; q < 8; q++) t = sdot2(nr[8 * s + q], 0x00010001u, t);
+      xn[s] = t;
     }
-    S = m * (1.0f / 32767.0f);
+    S = mx * (1.0f / 32767.0f);
   }
   // 4. the rows
-  const float wS = __int_as_float(load_scalar_i32((const int32_t*)wts, k)) * S;
-  const uint32_t cb = (uint32_t)(c >> 1);
-  const uint32_t ssel = cb | ((cb + 2) << 8) | ((cb + 4) << 16) | ((cb + 6) << 24);
-  float pr[8];
+  const float wS = wk * S;
+  const uint32_t ssel = (uint32_t)p | ((uint32_t)(p + 2) << 8) | ((uint32_t)(p + 4) << 16) |
+                        ((uint32_t)(p + 6) << 24);
+  float pr[R / 2];
 #pragma unroll
-  for (int r = 0; r < R; r++) {
-    uint32_t p0 = vperm(0u, qv[r].x, 0x0C010C00u), p1 = vperm(0u, qv[r].x, 0x0C030C02u);
-    uint32_t p2 = vperm(0u, qv[r].y, 0x0C010C00u), p3 = vperm(0u, qv[r].y, 0x0C030C02u);
-    uint32_t S4 = vperm(sv[r].y, sv[r].x, ssel);
+  for (int m = 0; m < R / 2; m++) {
+    // the code bytes l = 2q, 2q + 1 in the two 16-bit halves
+    uint32_t P[8];
+    const uint32_t cw[4] = {cv[m].x, cv[m].y, cv[m].z, cv[m].w};
+#pragma unroll
+    for (int q = 0; q < 8; q++) P[q] = vperm(0u, cw[q >> 1], (q & 1) ? 0x0C030C02u : 0x0C010C00u);
+    const uint32_t S4 = vperm(sc[m].y, sc[m].x, ssel);  // scale | min << 4 of sub-block s
     int A = 0, B = 0;
 #pragma unroll
     for (int s = 0; s < 4; s++) {
       const uint32_t mk = 0x00030003u << (2 * s);
-      int t = sdot2(p0 & mk, nr[4 * s], 0);
-      t = sdot2(p1 & mk, nr[4 * s + 1], t);
-      t = sdot2(p2 & mk, nr[4 * s + 2], t);
-      t = sdot2(p3 & mk, nr[4 * s + 3], t);
+      int t = 0;
+#pragma unroll
+      for (int q = 0; q < 8; q++) t = sdot2(P[q] & mk, nr[8 * s + q], t);
       t >>= 2 * s;  // codes were read in place, i.e. times 4^s; exact
-      // |t| <= 3 * 8 * 32767 and |xn| <= 8 * 32767 fit 24 bits: full-rate
+      // |t| <= 3 * 16 * 32767 and |xn| <= 16 * 32767 fit 24 bits: full-rate
       // 24-bit multiply-adds, exact
       A = __mul24((int)((S4 >> (8 * s)) & 0xFu), t) + A;
       B = __mul24((int)((S4 >> (8 * s + 4)) & 0xFu), xn[s]) + B;
     }
-    float d = f16_bits_to_f32(dd[r] & 0xFFFFu), dmin = f16_bits_to_f32(dd[r] >> 16);
-    pr[r] = wS * fmaf(-dmin, (float)B, d * (float)A);
+    const float d = f16_bits_to_f32(dd[m] & 0xFFFFu), dmin = f16_bits_to_f32(dd[m] >> 16);
+    pr[m] = wS * fmaf(-dmin, (float)B, d * (float)A);
   }
-  static_assert(R == 8, "one reduction covers the eight rows of a wave");
-  const float tot = reduce8(pr);
+  const float tot = reduce4x2(pr);
   if ((lane & 7) == 0) {
-    const int rho = lane >> 4, eta = (lane >> 3) & 1;
-    const int r = 4 * eta + ((rho == 1) ? 2 : (rho == 2) ? 1 : rho);
-    part[k][rh * R + r] = tot;
+    const int rho = lane >> 4, up8 = (lane >> 3) & 1;
+    const int m = (rho & 1) + 2 * up8, uu = rho >> 1;
+    part[k][rh * R + 2 * m + uu] = tot;
   }
   __syncthreads();
   if (tid < kDnBlockRows) {
