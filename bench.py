@@ -35,8 +35,8 @@ GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "2a9c6c050a80e46e40fed7cffed07d7440837ba6f38870ae9753fb266399fcca",
-    "bytes": 26323009,
+    "sha256": "d434befe504f0e6fa5c1c4bf98eea9e3fb35b980afd14375b954ef14696fe2d4",
+    "bytes": 26272728,
 }
 
 
