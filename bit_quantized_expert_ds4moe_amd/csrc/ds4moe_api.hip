@@ -387,7 +387,10 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       ProfScope prof(DS4MOE_K_GATEUP, st, !b1);
       const bool iq2 = g.qt_g == DS4MOE_IQ2_XXS && g.qt_u == DS4MOE_IQ2_XXS && g.I % kGNF == 0;
       const bool q80 = sh && q80_shared_fast(g);
-      if (iq2 && !b1) launch_k(k_grouped_gateup_iq2, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
+      if (iq2 && !b1) {  // small items (at most one per expert) and the rest
+        launch_k(k_grouped_gateup_iq2<1>, dim3(g.I / kGNF, E < TK ? E : TK), dim3(kGW * 64), 0, st, g);
+        launch_k(k_grouped_gateup_iq2<4>, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
+      }
       if (q80) {
         launch_k(k_grouped_gateup_q80, dim3(g.sh_I / kGNF, mi, g.ksplit_g), dim3(kGW * 64), 0, st, g);
         if (g.ksplit_g > 1)

@@ -44,45 +44,60 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* ids, int n, int
                                                   int32_t* offsets, int32_t* perm, int32_t* inv,
                                                   uint32_t* status);
 
-// Work list: items (e, row0, nrows) for every expert with pairs (experts in
-// ascending order, 64-row pieces), then the shared expert's rows (e == E).
-// One wave of 64 threads, four experts per lane, prefix sum over the lanes.
+// Work list: items (e, row0, nrows) for every expert with pairs (64-row
+// pieces), then the shared expert's rows (e == E).  Items of at most 16 rows
+// (an expert's last piece) come first, in ascending expert order, so that a
+// kernel specialised for one 16-row tile can take them; n_items[0] is the
+// number of items, n_items[1] the number of those small ones.  One wave of 64
+// threads, four experts per lane, prefix sums over the lanes.
+__device__ inline int wave_prefix_excl(int v, int& total) {
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d);
+    if ((int)(threadIdx.x & 63) >= d) incl += u;
+  }
+  total = __shfl(incl, 63);
+  return incl - v;
+}
+
 __global__ __launch_bounds__(64) void k_make_items(const int32_t* counts, const int32_t* offsets,
                                                    int E, int TK, int T, int with_shared,
                                                    int32_t* items, int32_t* n_items) {
   const int lane = threadIdx.x;
-  int cnt[4], tot = 0;
+  int cnt[4], nsm = 0, nlg = 0;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int e = 4 * lane + j;
     cnt[j] = e < E ? counts[e] : 0;
-    tot += (cnt[j] + kMC - 1) / kMC;
+    const int rem = cnt[j] % kMC;
+    nsm += (rem > 0 && rem <= 16) ? 1 : 0;
+    nlg += cnt[j] / kMC + (rem > 16 ? 1 : 0);
   }
-  int incl = tot;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d);
-    if (lane >= d) incl += v;
-  }
-  int n = incl - tot;
+  int small_total, large_total;
+  int ps = wave_prefix_excl(nsm, small_total);
+  int pl = small_total + wave_prefix_excl(nlg, large_total);
+  auto put = [&](int i, int e, int r0, int nr) {
+    items[3 * i] = e;
+    items[3 * i + 1] = r0;
+    items[3 * i + 2] = nr;
+  };
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int e = 4 * lane + j;
     for (int m0 = 0; m0 < cnt[j]; m0 += kMC) {
-      items[3 * n] = e;
-      items[3 * n + 1] = offsets[e] + m0;
-      items[3 * n + 2] = min(kMC, cnt[j] - m0);
-      n++;
+      const int nr = min(kMC, cnt[j] - m0);
+      if (nr <= 16) put(ps++, e, offsets[e] + m0, nr);
+      else put(pl++, e, offsets[e] + m0, nr);
     }
   }
-  const int routed = __shfl(incl, 63);
+  const int routed = small_total + large_total;
   const int ns = with_shared ? (T + kMC - 1) / kMC : 0;
-  for (int i = lane; i < ns; i += 64) {
-    items[3 * (routed + i)] = E;
-    items[3 * (routed + i) + 1] = TK + kMC * i;
-    items[3 * (routed + i) + 2] = min(kMC, T - kMC * i);
+  for (int i = lane; i < ns; i += 64) put(routed + i, E, TK + kMC * i, min(kMC, T - kMC * i));
+  if (lane == 0) {
+    n_items[0] = routed + ns;
+    n_items[1] = small_total;
   }
-  if (lane == 0) *n_items = routed + ns;
 }
 
 // Work list of the shared expert alone (its rows T*K .. T*K+T-1), for calls
@@ -94,7 +109,10 @@ __global__ void k_make_shared_items(int E, int TK, int T, int32_t* items, int32_
     items[3 * j + 1] = TK + kMC * j;
     items[3 * j + 2] = min(kMC, T - kMC * j);
   }
-  if (i == 0) *n_items = ns;
+  if (i == 0) {
+    n_items[0] = ns;
+    n_items[1] = 0;
+  }
 }
 
 // dst[t][c] += shared expert output of token t: y[T*K + t][c], or the sum of
@@ -149,11 +167,12 @@ __device__ inline int row_token(const GroupArgs& a, int row) {
 // as binary16 high + low parts (relative error < 2^-21) and, for the Q2_K
 // min term, the sum of each 16 consecutive features (a wave's tile) split
 // the same way; the sum runs over the 16 lanes of a DPP row in a fixed order.
+template <int MT = 4>
 __device__ inline void swiglu_store(const GroupArgs& a, int row0, int nrows, int mtiles, int n,
                                     int q, const f32x4_t* accg, const f32x4_t* accu) {
   bool ok = true;
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++) {
+  for (int mt = 0; mt < MT; mt++) {
     if (mt >= mtiles) break;
 #pragma unroll
     for (int r = 0; r < 4; r++) {
@@ -374,13 +393,18 @@ __device__ inline bf16x8_t iq2_stage_frag(const Iq2Stage& st, int s, int j, int 
   return __builtin_bit_cast(bf16x8_t, make_uint4(gv.x ^ mv.x, gv.y ^ mv.y, gv.z ^ mv.z, gv.w ^ mv.w));
 }
 
+// MT = 1: the small items (at most 16 rows, listed first); MT = 4: the rest.
+template <int MT>
 __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
-  __shared__ uint4 xt[2][kMC * 16];      // 2 x 16 KB
+  constexpr int kRows = 16 * MT;         // x tile rows
+  constexpr int kXC = kRows * 16;        // 16-byte chunks of an x tile stage
+  __shared__ uint4 xt[2][kXC];           // 2 x (MT x 4 KB)
   __shared__ uint4 gt8[256 * 8];         // 32 KB: entry e copy p at (e << 7) | (p << 4)
   __shared__ uint4 mt8[128 * 8];         // 16 KB
   __shared__ int tok[kMC];
-  const int item = blockIdx.y;
-  if (item >= *a.n_items) return;
+  const int n_small = a.n_items[1];
+  const int item = (MT == 1 ? 0 : n_small) + (int)blockIdx.y;
+  if (item >= (MT == 1 ? n_small : a.n_items[0])) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   if (e >= a.E) return;  // shared-expert items run in k_grouped_gateup
   const int n0 = blockIdx.x * kGNF;
@@ -418,37 +442,38 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
   }
   __syncthreads();  // tok visible
   // x tile of stage 0: chunk c = tid + 512 j -> row c >> 4, 16-byte column chunk c & 15
+  constexpr int kXJ = (kXC + kGW * 64 - 1) / (kGW * 64);  // chunks per thread
   auto x_load = [&](int s, uint4* v) {
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int c = tid + 512 * j, m = c >> 4, ch = c & 15;
-      v[j] = m < nrows ? ((const uint4*)(a.x + (size_t)tok[m] * a.H + kGStage * s))[ch]
-                       : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < kXJ; j++) {
+      const int c = tid + kGW * 64 * j, m = c >> 4, ch = c & 15;
+      v[j] = (c < kXC && m < nrows) ? ((const uint4*)(a.x + (size_t)tok[m] * a.H + kGStage * s))[ch]
+                                    : make_uint4(0, 0, 0, 0);
     }
   };
   auto x_store = [&](int buf, const uint4* v) {
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int c = tid + 512 * j, m = c >> 4, ch = c & 15;
-      xt[buf][m * 16 + (ch ^ (m & 15))] = v[j];
+    for (int j = 0; j < kXJ; j++) {
+      const int c = tid + kGW * 64 * j, m = c >> 4, ch = c & 15;
+      if (c < kXC) xt[buf][m * 16 + (ch ^ (m & 15))] = v[j];
     }
   };
   {
-    uint4 v[2];
+    uint4 v[kXJ];
     x_load(0, v);
     x_store(0, v);
   }
   __syncthreads();
 
-  f32x4_t accg[4], accu[4];
+  f32x4_t accg[MT], accu[MT];
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; mt++) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint8_t* gtab = (const uint8_t*)gt8;
   const uint8_t* stab = (const uint8_t*)mt8;
   for (int s = 0; s < nst; s++) {
     const bool more = s + 1 < nst;
     Iq2Stage ng, nu;
-    uint4 xv[2];
+    uint4 xv[kXJ];
     if (more) {
       iq2_stage_load(grow, s + 1, ng);
       iq2_stage_load(urow, s + 1, nu);
@@ -461,8 +486,8 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
       const bf16x8_t fg = iq2_stage_frag(cg, s, j, q, rep16, gtab, stab, sg);
       const bf16x8_t fu = iq2_stage_frag(cu, s, j, q, rep16, gtab, stab, su);
 #pragma unroll
-      for (int mt = 0; mt < 4; mt++) {
-        if (mt >= mtiles) break;
+      for (int mt = 0; mt < MT; mt++) {
+        if (MT > 1 && mt >= mtiles) break;
         const int m = 16 * mt + (lane & 15);
         const bf16x8_t af = __builtin_bit_cast(bf16x8_t, xb[m * 16 + ((4 * j + q) ^ (m & 15))]);
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
@@ -479,7 +504,7 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
     }
     __syncthreads();
   }
-  swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu);
+  swiglu_store<MT>(a, row0, nrows, mtiles, n, q, accg, accu);
 }
 
 // ---------------------------------------------------------------------------
