@@ -24,7 +24,7 @@ constexpr int kSharedSplitD = 4;   // and of its down
 
 // Byte offsets of the workspace regions for (shape, n_tok).
 struct Layout {
-  size_t status, kbuf, ids, wts, xn, perm, h, y, hb, part, total;
+  size_t status, kbuf, ids, wts, xn, x16, perm, h, y, hb, part, total;
 };
 
 Layout layout_for(const ds4moe_shape& s, int32_t T) {
@@ -43,6 +43,7 @@ Layout layout_for(const ds4moe_shape& s, int32_t T) {
   L.ids = take(t * K * 4);
   L.wts = take(t * K * 4);
   L.xn = take(t * H * 2);
+  L.x16 = take(t * H * 2);
   L.perm = take((E + (E + 1) + 2 * t * K + 3 * (size_t)max_items((int)E, (int)(t * K), (int)t, true) + 64) * 4);
   L.h = take(np * I * 4);
   L.y = take(np * H * 4);
@@ -346,6 +347,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     g.K = K;
     g.T = T;
     g.x = (const uint16_t*)x;
+    g.x16 = at<uint16_t>(ws, L.x16);
     g.perm = perm;
     g.items = items;
     g.n_items = n_items;
@@ -385,9 +387,12 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     const int imax = g.I > g.sh_I ? g.I : g.sh_I;
     {
       ProfScope prof(DS4MOE_K_GATEUP, st, !b1);
-      const bool iq2 = g.qt_g == DS4MOE_IQ2_XXS && g.qt_u == DS4MOE_IQ2_XXS && g.I % kGNF == 0;
+      const bool iq2 = iq2_grouped_fast(g);
       const bool q80 = sh && q80_shared_fast(g);
-      if (iq2 && !b1) {  // small items (at most one per expert) and the rest
+      if (iq2 && !b1) {  // x in binary16; small items (at most one per expert) and the rest
+        const size_t n8 = (size_t)T * g.H / 8;
+        launch_k(k_x_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, g.x, n8,
+                 at<uint16_t>(ws, L.x16), status);
         launch_k(k_grouped_gateup_iq2<1>, dim3(g.I / kGNF, E < TK ? E : TK), dim3(kGW * 64), 0, st, g);
         launch_k(k_grouped_gateup_iq2<4>, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
       }

@@ -15,16 +15,20 @@
 // permutation kernel; a grouped kernel block takes one item and 64 output
 // features.
 //
-// Exactness: MFMA operands are exact.  gate/up (bf16 MFMA 16x16x32): A = x
-// (bf16 as given), B = IQ2_XXS grid value * sign (|v| < 128, exact in bf16) or
-// the Q8_0 code; each 32-column group's scale multiplies that group's MFMA
-// result (one FMA per output element per group).  down (f16 MFMA 16x16x16,
+// Exactness: MFMA operands are exact.  IQ2_XXS gate/up (f16 MFMA
+// 16x16x32): A = x in binary16 (exact for the bf16 inputs within the
+// binary16 range), B = grid value * sign * (2s + 1) (an integer, exact); the
+// block scale d rescales the fp32 accumulators.  Other gate/up formats (bf16
+// MFMA 16x16x32): A = x as given, B = the grid value * sign or the Q8_0 code;
+// each 32-column group's scale multiplies that group's MFMA result.  down (f16 MFMA 16x16x16,
 // one 16-value Q2_K sub-block per step): A = the SwiGLU output split as
 // f16 hi + lo (relative error < 2^-21), B = the 2-bit code masked in place in
 // a 16-bit lane, i.e. the binary16 subnormal 4^s q 2^-24; the sub-block factor
 // d*sc*4^-s*2^24 multiplies each step's result; the mins enter through a
 // second MFMA on per-sub-block sums of h against the min nibbles.  Sums are
 // fp32 throughout.
+#include <type_traits>
+
 #include "dev_common.h"
 
 namespace ds4 {
@@ -138,6 +142,7 @@ inline int max_items(int E, int TK, int T, bool shared) {
 struct GroupArgs {
   int H, I, E, K, T;
   const uint16_t* x;        // [T][H] bf16
+  const uint16_t* x16;      // [T][H] the same in binary16 (IQ2_XXS gate/up)
   const int32_t* perm;      // [T*K]
   const int32_t* items;     // [n][3]
   const int32_t* n_items;
@@ -269,6 +274,11 @@ __device__ inline void q80_bfrag(const uint8_t* chunk, int g, int q, bf16x8_t& b
   b = __builtin_bit_cast(bf16x8_t, v);
 }
 
+__host__ __device__ inline bool iq2_grouped_fast(const GroupArgs& a) {
+  return a.qt_g == DS4MOE_IQ2_XXS && a.qt_u == DS4MOE_IQ2_XXS && a.I % kGNF == 0 && a.H % 512 == 0 &&
+         (uintptr_t)a.grid % 8 == 0;
+}
+
 __host__ __device__ inline bool q80_shared_fast(const GroupArgs& a) {
   return a.sh_qt_g == DS4MOE_Q8_0 && a.sh_qt_u == DS4MOE_Q8_0 && a.sh_I % kGNF == 0 && a.H % 64 == 0;
 }
@@ -289,7 +299,7 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
   const bool sh = e == a.E;
   // routed items with IQ2_XXS gate and up run in k_grouped_gateup_iq2, a
   // Q8_0 shared expert in k_grouped_gateup_q80
-  if (!sh && a.qt_g == DS4MOE_IQ2_XXS && a.qt_u == DS4MOE_IQ2_XXS && a.I % kGNF == 0) return;
+  if (!sh && iq2_grouped_fast(a)) return;
   if (sh && q80_shared_fast(a)) return;
   const int I = sh ? a.sh_I : a.I;
   const int n0 = blockIdx.x * kNT;
@@ -349,59 +359,109 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
 
 // ---------------------------------------------------------------------------
 // gate/up for routed items with IQ2_XXS gate and up: software-pipelined.
-// Grid (I/128, max_items), 512 threads; wave w owns features n0 + 16w .. +15
-// (gate and up).  The K dimension runs in stages of 128 columns (half an
-// IQ2_XXS block: four 32-column groups).  While stage s is multiplied, the
-// x tile and the weight bytes of stage s+1 are already in flight: x rows go
-// through registers into the other half of a double-buffered LDS tile, the
-// weight bytes (nine aligned dwords covering the four groups, plus the word
-// holding d) sit in a second register set.  One barrier per stage.
-
-struct Iq2Stage {
-  uint32_t D[9];
-  uint32_t dw;
+// Grid (I/128, items), 512 threads; wave w owns features n0 + 16w .. +15
+// (gate and up).  K runs in stages of 128 columns (half an IQ2_XXS block:
+// four 32-column sub-blocks).  In a stage, lane quarter q takes sub-block q
+// whole: its four 8-value groups are the B fragments of the stage's four
+// MFMA steps (step j covers columns 32q + 8j .. +7 of the stage in quarter
+// q; the A fragments are read in the same column order, and a sum over K
+// does not depend on that order).  The sub-block factor 2s + 1 is then one
+// number per lane and goes into B, in binary16:
+//   B = grid * sign * (2s + 1)   (an integer of at most 2046 for grid values
+//                                 up to 66, so exact; the format's are 8..43)
+//   A = x in binary16 (converted once per call).
+// The block scale d is shared by the four quarters of a row (one block per
+// stage pair) and by the accumulator columns a lane holds (its own feature),
+// so it is applied to the fp32 accumulators: they hold the sum divided by the
+// current block's d and are rescaled by d_prev / d at each block start (one
+// rounding per block), times d / 8 at the end.  A lane needs only its
+// sub-block's 8 bytes (three aligned words when the block starts two bytes
+// into a word) and the word holding d, so four stages of weights fit in a
+// register ring: stage s + 3 is requested while stage s is multiplied, and
+// x rows two stages ahead go through registers into a double-buffered LDS
+// tile.  One barrier per stage.
+struct Iq2Sub {
+  uint32_t w0, w1, w2, dw;
 };
 
-// Stage s of one IQ2_XXS row (row start 16-byte aligned).  The nine dwords
-// cover the 32 group bytes, which start 2 bytes into a word for even blocks;
-// for odd blocks the ninth word is fetched from inside the range instead, so
-// that the last row of a tensor is never overrun.
-__device__ inline void iq2_stage_load(const uint8_t* __restrict__ row, int s, Iq2Stage& st) {
+// Sub-block q of stage s.  EVEN: block s >> 1 is even, so (block size 66)
+// its bytes start two bytes into a word; the third word then ends inside
+// the next block, which exists (an even number of blocks per row).
+template <bool EVEN>
+__device__ inline void iq2_sub_load(const uint8_t* __restrict__ row, int s, int q, Iq2Sub& o) {
   const int kb = s >> 1;
-  const int start = kIq2Bytes * kb + 2 + 32 * (s & 1);
-  const int sh = start & 3;
-  const uint32_t* p = (const uint32_t*)(row + (start - sh));
-#pragma unroll
-  for (int i = 0; i < 8; i++) st.D[i] = p[i];
-  st.D[8] = p[sh ? 8 : 7];
-  st.dw = *(const uint32_t*)(row + ((kIq2Bytes * kb) & ~3));
+  const int start = kIq2Bytes * kb + 2 + 32 * (s & 1) + 8 * q;
+  const uint32_t* p = (const uint32_t*)(row + (start & ~3));
+  o.w0 = p[0];
+  o.w1 = p[1];
+  if (EVEN) o.w2 = p[2];
+  o.dw = *(const uint32_t*)(row + ((kIq2Bytes * kb) & ~3));
 }
 
-// B fragment of group j (0..3) of a stage for this lane's quarter q: the grid
-// entry's bf16 pairs with the signs applied; the group scale d(2s+1)/8.
-__device__ inline bf16x8_t iq2_stage_frag(const Iq2Stage& st, int s, int j, int q, uint32_t rep16,
-                                          const uint8_t* gtab, const uint8_t* stab, float& scale) {
-  const uint32_t sh = (s & 2) ? 0u : 2u;  // (2 kb + 2) & 3 with kb = s >> 1
-  const uint32_t idxw = align_bytes(st.D[2 * j + 1], st.D[2 * j], sh);
-  const uint32_t sw = align_bytes(st.D[2 * j + 2], st.D[2 * j + 1], sh);
-  const float d = f16_bits_to_f32((s & 2) ? (st.dw >> 16) : (st.dw & 0xFFFFu));
-  scale = d * (float)((((sw & 0xF0000000u) | 0x08000000u) >> 24)) * 0.015625f;
-  const uint32_t gi = (idxw >> (8 * q)) & 0xFFu;
-  const uint32_t si = (sw >> (7 * q)) & 0x7Fu;
+// index word, sign/scale word, the block's d (1 when d is 0) and the B factor
+// (2s + 1) twice in binary16 (0 when d is 0)
+template <bool EVEN>
+__device__ inline uint32_t iq2_sub_words(const Iq2Sub& o, uint32_t& idx, uint32_t& sgn, float& d) {
+  idx = EVEN ? align_bytes(o.w1, o.w0, 2) : o.w0;
+  sgn = EVEN ? align_bytes(o.w2, o.w1, 2) : o.w1;
+  const float dv = f16_bits_to_f32(EVEN ? (o.dw & 0xFFFFu) : (o.dw >> 16));
+  d = dv != 0.0f ? dv : 1.0f;
+  const uint32_t h = f32_to_f16_bits((float)(2u * (sgn >> 28) + 1u));
+  return dv != 0.0f ? h | (h << 16) : 0u;
+}
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// group j of the lane's sub-block as the binary16 B fragment
+__device__ inline f16x8_t iq2_sub_frag(uint32_t idx, uint32_t sgn, int j, uint32_t sc2,
+                                       uint32_t rep16, const uint8_t* gtab, const uint8_t* stab) {
+  const uint32_t gi = (idx >> (8 * j)) & 0xFFu;
+  const uint32_t si = (sgn >> (7 * j)) & 0x7Fu;
   const uint4 gv = *(const uint4*)(gtab + ((gi << 7) | rep16));
   const uint4 mv = *(const uint4*)(stab + ((si << 7) | rep16));
-  return __builtin_bit_cast(bf16x8_t, make_uint4(gv.x ^ mv.x, gv.y ^ mv.y, gv.z ^ mv.z, gv.w ^ mv.w));
+  const f16x2_t c = __builtin_bit_cast(f16x2_t, sc2);
+  const f16x2_t b0 = __builtin_bit_cast(f16x2_t, gv.x ^ mv.x) * c;
+  const f16x2_t b1 = __builtin_bit_cast(f16x2_t, gv.y ^ mv.y) * c;
+  const f16x2_t b2 = __builtin_bit_cast(f16x2_t, gv.z ^ mv.z) * c;
+  const f16x2_t b3 = __builtin_bit_cast(f16x2_t, gv.w ^ mv.w) * c;
+  return __builtin_bit_cast(
+      f16x8_t, make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1),
+                          __builtin_bit_cast(uint32_t, b2), __builtin_bit_cast(uint32_t, b3)));
+}
+
+// the IQ2_XXS grid in binary16 (entry e, copy p at (e << 7) | (p << 4); gb =
+// the 8 grid bytes of entry threadIdx.x) and the 128 sign patterns as masks
+// of the binary16 sign bits
+__device__ inline void build_tables8_f16(uint2 gb, uint4* gt8, uint4* mt8) {
+  const int tid = threadIdx.x;
+  if (tid < 256) {
+    uint32_t wv[4];
+    for (int m = 0; m < 4; m++) {
+      const uint32_t b2 = (m < 2 ? gb.x : gb.y) >> (16 * (m & 1));
+      wv[m] = f32_to_f16_bits((float)(b2 & 0xFFu)) | (f32_to_f16_bits((float)((b2 >> 8) & 0xFFu)) << 16);
+    }
+    const uint4 v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    for (int j = 0; j < 8; j++) gt8[8 * tid + ((j + tid) & 7)] = v;
+  } else if (tid < 384) {
+    const int t = tid - 256;
+    const uint32_t s8 = (uint32_t)t | ((uint32_t)(__popc(t) & 1) << 7);
+    uint32_t wv[4];
+    for (int m = 0; m < 4; m++)
+      wv[m] = (((s8 >> (2 * m)) & 1u) << 15) | (((s8 >> (2 * m + 1)) & 1u) << 31);
+    const uint4 v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    for (int j = 0; j < 8; j++) mt8[8 * t + ((j + t) & 7)] = v;
+  }
 }
 
 // MT = 1: the small items (at most 16 rows, listed first); MT = 4: the rest.
 template <int MT>
 __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
-  constexpr int kRows = 16 * MT;         // x tile rows
-  constexpr int kXC = kRows * 16;        // 16-byte chunks of an x tile stage
-  __shared__ uint4 xt[2][kXC];           // 2 x (MT x 4 KB)
-  __shared__ uint4 gt8[256 * 8];         // 32 KB: entry e copy p at (e << 7) | (p << 4)
-  __shared__ uint4 mt8[128 * 8];         // 16 KB
-  __shared__ int tok[kMC];
+  constexpr int kRows = 16 * MT;                           // x tile rows
+  constexpr int kXC = kRows * 16;                          // 16-byte chunks of an x stage
+  constexpr int kXJ = (kXC + kGW * 64 - 1) / (kGW * 64);  // chunks per thread
+  __shared__ uint4 xt[2][kXC];    // 2 x (MT x 4 KB)
+  __shared__ uint4 gt8[256 * 8];  // 32 KB
+  __shared__ uint4 mt8[128 * 8];  // 16 KB (MT = 4: 80 KB in all, two blocks per CU)
   const int n_small = a.n_items[1];
   const int item = (MT == 1 ? 0 : n_small) + (int)blockIdx.y;
   if (item >= (MT == 1 ? n_small : a.n_items[0])) return;
@@ -415,96 +475,151 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
   const int rowbytes = (a.H / 256) * kIq2Bytes;
   const uint8_t* grow = a.gate + ((size_t)e * a.I + n) * rowbytes;
   const uint8_t* urow = a.up + ((size_t)e * a.I + n) * rowbytes;
-  const int nst = a.H / kGStage;
+  const int nst = a.H / kGStage;  // a multiple of 4
   const int mtiles = (nrows + 15) >> 4;
 
-  // stage 0 weights first: their latency overlaps the table build
-  Iq2Stage cg, cu;
-  iq2_stage_load(grow, 0, cg);
-  iq2_stage_load(urow, 0, cu);
-  if (tid < kMC) tok[tid] = tid < nrows ? row_token(a, row0 + tid) : -1;
-  if (tid < 256) {
-    const uint8_t* g = a.grid + 8 * tid;
-    uint32_t wv[4];
-    for (int m = 0; m < 4; m++)
-      wv[m] = (__float_as_uint((float)g[2 * m]) >> 16) |
-              (__float_as_uint((float)g[2 * m + 1]) & 0xFFFF0000u);
-    const uint4 v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-    for (int j = 0; j < 8; j++) gt8[8 * tid + ((j + tid) & 7)] = v;
-  } else if (tid < 384) {
-    const int t = tid - 256;
-    const uint32_t s8 = (uint32_t)t | ((uint32_t)(__popc(t) & 1) << 7);
-    uint32_t wv[4];
-    for (int m = 0; m < 4; m++)
-      wv[m] = (((s8 >> (2 * m)) & 1u) << 15) | (((s8 >> (2 * m + 1)) & 1u) << 31);
-    const uint4 v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-    for (int j = 0; j < 8; j++) mt8[8 * t + ((j + t) & 7)] = v;
+  // x chunk c = tid + 512 j (mod the tile) -> row c >> 4, 16-byte column
+  // chunk c & 15.  Every lane loads (rows past the item repeat row 0: their
+  // results are never stored) and stores (threads past the tile store the
+  // same chunk again), so no branch lets the compiler move a load down to
+  // its store or hide it from the wait counts.  Plain vector values, so
+  // that nothing goes through a private array.
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  struct XV {
+    u32x4_t v[kXJ];
+  };
+  // Vector memory returns in order, so the loads go out in the order they
+  // are needed: the grid bytes and the tokens of this thread's x rows, the
+  // weights of stages 0 and 1, x of stages 0 and 1, then the weights of
+  // stage 2 (in the loop, as in the first stage, x then weights).
+  const uint2 gb = *(const uint2*)(a.grid + 8 * (tid & 255));
+  int xtok[kXJ];
+#pragma unroll
+  for (int j = 0; j < kXJ; j++) {
+    const int m = ((tid + kGW * 64 * j) & (kXC - 1)) >> 4;
+    xtok[j] = a.perm[row0 + (m < nrows ? m : 0)] / a.K;  // routed rows only
   }
-  __syncthreads();  // tok visible
-  // x tile of stage 0: chunk c = tid + 512 j -> row c >> 4, 16-byte column chunk c & 15
-  constexpr int kXJ = (kXC + kGW * 64 - 1) / (kGW * 64);  // chunks per thread
-  auto x_load = [&](int s, uint4* v) {
+  __builtin_amdgcn_sched_barrier(0);
+  // ring slot s & 3 holds stage s ([0] gate, [1] up)
+  Iq2Sub W[4][2];
+  iq2_sub_load<true>(grow, 0, q, W[0][0]);
+  iq2_sub_load<true>(urow, 0, q, W[0][1]);
+  iq2_sub_load<true>(grow, 1, q, W[1][0]);
+  iq2_sub_load<true>(urow, 1, q, W[1][1]);
+  __builtin_amdgcn_sched_barrier(0);
+  build_tables8_f16(gb, gt8, mt8);
+  const uint16_t* xrow[kXJ];
+#pragma unroll
+  for (int j = 0; j < kXJ; j++)
+    xrow[j] = a.x16 + (size_t)xtok[j] * a.H + 8 * ((tid + kGW * 64 * j) & 15);
+  auto x_load = [&](int s) {
+    XV r;
+#pragma unroll
+    for (int j = 0; j < kXJ; j++) r.v[j] = *(const u32x4_t*)(xrow[j] + kGStage * s);
+    return r;
+  };
+  u32x4_t* xtv = (u32x4_t*)&xt[0][0];
+  auto x_store = [&](int buf, const XV& x) {
 #pragma unroll
     for (int j = 0; j < kXJ; j++) {
-      const int c = tid + kGW * 64 * j, m = c >> 4, ch = c & 15;
-      v[j] = (c < kXC && m < nrows) ? ((const uint4*)(a.x + (size_t)tok[m] * a.H + kGStage * s))[ch]
-                                    : make_uint4(0, 0, 0, 0);
+      const int c = (tid + kGW * 64 * j) & (kXC - 1), m = c >> 4, ch = c & 15;
+      xtv[buf * kXC + m * 16 + (ch ^ (m & 15))] = x.v[j];
     }
   };
-  auto x_store = [&](int buf, const uint4* v) {
-#pragma unroll
-    for (int j = 0; j < kXJ; j++) {
-      const int c = tid + kGW * 64 * j, m = c >> 4, ch = c & 15;
-      if (c < kXC) xt[buf][m * 16 + (ch ^ (m & 15))] = v[j];
-    }
-  };
-  {
-    uint4 v[kXJ];
-    x_load(0, v);
-    x_store(0, v);
-  }
-  __syncthreads();
+  XV X0 = x_load(0), X1 = x_load(1);  // x ring: stage s in X0 (s even) or X1
+  __builtin_amdgcn_sched_barrier(0);
+  iq2_sub_load<false>(grow, 2, q, W[2][0]);
+  iq2_sub_load<false>(urow, 2, q, W[2][1]);
+  __builtin_amdgcn_sched_barrier(0);
+  x_store(0, X0);
+  __syncthreads();  // tables and x of stage 0
 
   f32x4_t accg[MT], accu[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint8_t* gtab = (const uint8_t*)gt8;
   const uint8_t* stab = (const uint8_t*)mt8;
-  for (int s = 0; s < nst; s++) {
-    const bool more = s + 1 < nst;
-    Iq2Stage ng, nu;
-    uint4 xv[kXJ];
-    if (more) {
-      iq2_stage_load(grow, s + 1, ng);
-      iq2_stage_load(urow, s + 1, nu);
-      x_load(s + 1, xv);
+  float dgp = 1.0f, dup = 1.0f;  // d of the current block (gate, up)
+  // stage s = s0 + R (s0 % 4 == 0): block s >> 1 is even for R = 0, 1
+  auto stage = [&](int s, auto Rc) {
+    constexpr int R = decltype(Rc)::value;
+    constexpr bool EVEN = R < 2;
+    // requests: x of stage s + 2, weights of stage s + 3 (past the end: a
+    // repeat of stage s - 1, which has the same block parity; never used)
+    // (x first: a wait for it then never waits for these weights)
+    if constexpr ((R & 1) == 0) X0 = x_load(min(s + 2, nst - 1));
+    else X1 = x_load(min(s + 2, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    const int sw = s + 3 < nst ? s + 3 : s - 1;
+    constexpr bool EVEN3 = ((R + 3) >> 1 & 1) == 0;
+    iq2_sub_load<EVEN3>(grow, sw, q, W[(R + 3) & 3][0]);
+    iq2_sub_load<EVEN3>(urow, sw, q, W[(R + 3) & 3][1]);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t ig, sg, iu, su;
+    float dg, du;
+    const uint32_t cg = iq2_sub_words<EVEN>(W[R][0], ig, sg, dg);
+    const uint32_t cu = iq2_sub_words<EVEN>(W[R][1], iu, su, du);
+    if constexpr ((R & 1) == 0) {  // a block starts: sums in units of its d
+      const float rg = dgp / dg, ru = dup / du;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        accg[mt] *= rg;
+        accu[mt] *= ru;
+      }
+      dgp = dg;
+      dup = du;
     }
-    const uint4* xb = xt[s & 1];
+    const uint4* xb = xt[R & 1];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      float sg, su;
-      const bf16x8_t fg = iq2_stage_frag(cg, s, j, q, rep16, gtab, stab, sg);
-      const bf16x8_t fu = iq2_stage_frag(cu, s, j, q, rep16, gtab, stab, su);
+      const f16x8_t fg = iq2_sub_frag(ig, sg, j, cg, rep16, gtab, stab);
+      const f16x8_t fu = iq2_sub_frag(iu, su, j, cu, rep16, gtab, stab);
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) {
         if (MT > 1 && mt >= mtiles) break;
         const int m = 16 * mt + (lane & 15);
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, xb[m * 16 + ((4 * j + q) ^ (m & 15))]);
-        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4_t tg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fg, z, 0, 0, 0);
-        const f32x4_t tu = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, fu, z, 0, 0, 0);
-        accg[mt] += sg * tg;
-        accu[mt] += su * tu;
+        const f16x8_t af = __builtin_bit_cast(f16x8_t, xb[m * 16 + ((4 * q + j) ^ (m & 15))]);
+        accg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fg, accg[mt], 0, 0, 0);
+        accu[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fu, accu[mt], 0, 0, 0);
       }
     }
-    if (more) {
-      x_store((s + 1) & 1, xv);
-      cg = ng;
-      cu = nu;
-    }
+    // x of stage s + 1 into the other buffer (after the last stage: unused)
+    if constexpr ((R & 1) == 0) x_store(1, X1);
+    else x_store(0, X0);
     __syncthreads();
+  };
+  for (int s0 = 0; s0 < nst; s0 += 4) {
+    stage(s0, std::integral_constant<int, 0>{});
+    stage(s0 + 1, std::integral_constant<int, 1>{});
+    stage(s0 + 2, std::integral_constant<int, 2>{});
+    stage(s0 + 3, std::integral_constant<int, 3>{});
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) {
+    accg[mt] *= dgp * 0.125f;
+    accu[mt] *= dup * 0.125f;
   }
   swiglu_store<MT>(a, row0, nrows, mtiles, n, q, accg, accu);
+}
+
+// x (bf16) -> binary16 for k_grouped_gateup_iq2; magnitudes beyond the
+// binary16 range raise DS4MOE_FAULT_F16_RANGE.
+__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, size_t n8,
+                                                 uint16_t* __restrict__ x16, uint32_t* status) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 v = ((const uint4*)x)[i];
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+  bool ok = true;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const float lo = __uint_as_float(in[k] << 16), hi = __uint_as_float(in[k] & 0xFFFF0000u);
+    ok &= fabsf(lo) <= 65504.0f && fabsf(hi) <= 65504.0f;
+    o[k] = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+  }
+  ((uint4*)x16)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  if (!ok) raise_fault(status, DS4MOE_FAULT_F16_RANGE);
 }
 
 // ---------------------------------------------------------------------------
