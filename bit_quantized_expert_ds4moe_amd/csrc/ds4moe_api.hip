@@ -409,8 +409,11 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     if ((rc = launched()) != DS4MOE_OK) return rc;
     {
       ProfScope prof(DS4MOE_K_DOWN, st, !b1);
-      const bool q2k = g.qt_d == DS4MOE_Q2_K && g.H % kDNF == 0;
-      if (q2k && !b1) launch_k(k_grouped_down_q2k, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
+      const bool q2k = q2k_grouped_fast(g);
+      if (q2k && !b1) {  // small items and the rest
+        launch_k(k_grouped_down_q2k<1>, dim3(g.H / kDNF, E < TK ? E : TK), dim3(kDW * 64), 0, st, g);
+        launch_k(k_grouped_down_q2k<4>, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
+      }
       if (!q2k || sh)
         launch_k(k_grouped_down, dim3(s.hidden / kNT, mi, g.ksplit_d), dim3(256), 0, st, g);
     }

@@ -279,6 +279,10 @@ __host__ __device__ inline bool iq2_grouped_fast(const GroupArgs& a) {
          (uintptr_t)a.grid % 8 == 0;
 }
 
+__host__ __device__ inline bool q2k_grouped_fast(const GroupArgs& a) {
+  return a.qt_d == DS4MOE_Q2_K && a.H % kDNF == 0 && a.I % 512 == 0;
+}
+
 __host__ __device__ inline bool q80_shared_fast(const GroupArgs& a) {
   return a.sh_qt_g == DS4MOE_Q8_0 && a.sh_qt_u == DS4MOE_Q8_0 && a.sh_I % kGNF == 0 && a.H % 64 == 0;
 }
@@ -804,7 +808,7 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   const bool shr = e == a.E;
   // routed Q2_K items run in k_grouped_down_q2k
-  if (!shr && a.qt_d == DS4MOE_Q2_K && a.H % kDNF == 0) return;
+  if (!shr && q2k_grouped_fast(a)) return;
   const int I = shr ? a.sh_I : a.I;
   const int qd = shr ? a.sh_qt_d : a.qt_d;
   const uint8_t* D = shr ? a.sh_down : a.down;
@@ -940,158 +944,189 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
 }
 
 // down for routed items with Q2_K down weights: software-pipelined.
-// Grid (H/128, max_items), 512 threads; wave w owns output features
-// n0 + 16w .. +15.  Stages of 128 columns (half a Q2_K block: eight 16-value
-// sub-blocks).  The SwiGLU tile of stage s+1 (binary16 high and low parts,
-// as written by gate/up) and the weight words of stage s+1 are loaded while
-// stage s is multiplied.  Per sub-block: f16 MFMA 16x16x16 of the h parts
-// against the 2-bit codes read in place (binary16 subnormals 4^s q 2^-24,
-// exact), scaled by d sc 4^-s 2^24; once per block the mins: an MFMA of the
-// 16 sub-block sums against the min nibbles, scaled by dmin 2^24.
-
-struct Q2kStage {
-  uint32_t qa, qb;   // code bytes 32hf + 4q .. +3 and 32hf + 16 + 4q .. +3
-  uint4 sc;          // the block's 16 scale/min bytes
-  uint32_t dd;       // d | dmin << 16
+// Grid (H/128, items), 512 threads; wave w owns output features
+// n0 + 16w .. +15.  K runs in stages of 128 columns (half a Q2_K block: its
+// 32 code bytes hold four 2-bit planes of 32 columns each).  In a stage,
+// lane quarter q takes code bytes 8q .. 8q+7 of the half: plane j of them is
+// the B fragment of MFMA step j (f16 16x16x32), columns 32j + 8q .. +7 of
+// the stage, all in one 16-value sub-block, so its scale nibble goes into B:
+//   B = q * sc as a binary16 subnormal (q * sc * 2^-24, exact),
+//   A = the SwiGLU rows as binary16 high and low parts (two MFMAs),
+// and, as in the IQ2_XXS gate/up kernel, the accumulators hold the sum in
+// units of the current block's d (rescaled at each block start).  The mins:
+// per stage one f16 16x16x16 MFMA of the eight sub-block sums of h (hi, lo;
+// written by gate/up) against the min nibbles (quarters 0 and 1; B = 0 in
+// quarters 2 and 3), scaled by dmin / d.  Weights of stage s + 3 and the h
+// tile (with the sums) of stage s + 2 are in flight while stage s is
+// multiplied; one barrier per stage.
+struct Q2kSub {
+  uint32_t c0, c1, s0, s1, dd;  // the lane's code bytes, the half's scale bytes, d | dmin << 16
 };
 
-__device__ inline void q2k_stage_load(const uint8_t* __restrict__ row, int s, int q, Q2kStage& st) {
+__device__ inline void q2k_sub_load(const uint8_t* __restrict__ row, int s, int q, Q2kSub& o) {
   const uint8_t* blk = row + kQ2kBytes * (s >> 1);
   const int hf = s & 1;
-  st.qa = *(const uint32_t*)(blk + 16 + 32 * hf + 4 * q);
-  st.qb = *(const uint32_t*)(blk + 32 + 32 * hf + 4 * q);
-  st.sc = *(const uint4*)blk;
-  st.dd = *(const uint32_t*)(blk + 80);
+  const uint32_t* c = (const uint32_t*)(blk + 16 + 32 * hf + 8 * q);
+  o.c0 = c[0];
+  o.c1 = c[1];
+  const uint32_t* sc = (const uint32_t*)(blk + 8 * hf);
+  o.s0 = sc[0];
+  o.s1 = sc[1];
+  o.dd = *(const uint32_t*)(blk + 80);
 }
 
+// MT = 1: the small items (at most 16 rows, listed first); MT = 4: the rest.
+template <int MT>
 __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
-  __shared__ uint4 ah[kMC * 16];   // [m][16 chunks of 8 f16], high parts, 16 KB
-  __shared__ uint4 al[kMC * 16];   // low parts, 16 KB
-  const int item = blockIdx.y;
-  if (item >= *a.n_items) return;
+  constexpr int kRows = 16 * MT;
+  constexpr int kHC = kRows * 32;                          // h chunks of a stage (hi, lo)
+  constexpr int kHJ = (kHC + kDW * 64 - 1) / (kDW * 64);  // per thread
+  constexpr int kSC = kRows * 2;                           // sum chunks (hi, lo)
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ u32x4_t ht[2][kHC];  // row m: [hi 16 chunks][lo 16 chunks], chunk c at c ^ (m & 15)
+  __shared__ u32x4_t st[2][kSC];  // row m: [8 sums hi][8 sums lo]
+  const int n_small = a.n_items[1];
+  const int item = (MT == 1 ? 0 : n_small) + (int)blockIdx.y;
+  if (item >= (MT == 1 ? n_small : a.n_items[0])) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   if (e >= a.E) return;  // shared-expert items run in k_grouped_down
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = lane >> 4;
   const int n = blockIdx.x * kDNF + 16 * w + (lane & 15);
   const int rowbytes = (a.I / 256) * kQ2kBytes;
   const uint8_t* drow = a.down + ((size_t)e * a.H + n) * rowbytes;
-  const int nst = a.I / 128;
+  const int nst = a.I / 128;  // a multiple of 4
   const int mtiles = (nrows + 15) >> 4;
-
-  Q2kStage cw;
-  q2k_stage_load(drow, 0, q, cw);
-  // SwiGLU tile of a stage: chunk c = tid + 512 j (j < 2) -> row c >> 4,
-  // 8-value chunk c & 15; high and low parts
-  auto h_load = [&](int s, uint4* v) {
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int c = tid + 512 * j, m = c >> 4, ch = c & 15;
-      if (m < nrows) {
-        const size_t off = (size_t)(row0 + m) * a.I + 128 * s + 8 * ch;
-        v[j] = *(const uint4*)(a.hh + off);
-        v[2 + j] = *(const uint4*)(a.hl + off);
-      } else {
-        v[j] = v[2 + j] = make_uint4(0, 0, 0, 0);
-      }
-    }
+  // h tile loads: chunk c = tid + 512 j -> row c >> 5, part (c >> 4) & 1,
+  // chunk c & 15; sum chunk cs = tid mod 2 kRows -> row cs >> 1, part cs & 1.
+  // Rows past the item repeat row 0 (never stored); threads past a tile load
+  // and store a chunk again: no branches around loads or stores.
+  struct HV {
+    u32x4_t v[kHJ];
+    u32x4_t sm;
   };
-  auto h_store = [&](const uint4* v) {
+  const uint16_t* hsrc[kHJ];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int c = tid + 512 * j, m = c >> 4, ch = c & 15;
-      ah[m * 16 + (ch ^ (m & 15))] = v[j];
-      al[m * 16 + (ch ^ (m & 15))] = v[2 + j];
-    }
-  };
-  {
-    uint4 v[4];
-    h_load(0, v);
-    h_store(v);
+  for (int j = 0; j < kHJ; j++) {
+    const int c = (tid + kDW * 64 * j) & (kHC - 1), m = c >> 5;
+    const size_t r = (size_t)(row0 + (m < nrows ? m : 0));
+    hsrc[j] = ((c >> 4) & 1 ? a.hl : a.hh) + r * a.I + 8 * (c & 15);
   }
+  const int cs = tid & (kSC - 1), ms = cs >> 1;
+  const uint16_t* ssrc = ((cs & 1) ? a.hsl : a.hsh) + (size_t)(row0 + (ms < nrows ? ms : 0)) * (a.I / 16);
+  auto h_load = [&](int s) {
+    HV r;
+#pragma unroll
+    for (int j = 0; j < kHJ; j++) r.v[j] = *(const u32x4_t*)(hsrc[j] + 128 * s);
+    r.sm = *(const u32x4_t*)(ssrc + 8 * s);
+    return r;
+  };
+  auto h_store = [&](int buf, const HV& h) {
+#pragma unroll
+    for (int j = 0; j < kHJ; j++) {
+      const int c = (tid + kDW * 64 * j) & (kHC - 1), m = c >> 5;
+      ht[buf][m * 32 + (c & 16) + ((c & 15) ^ (m & 15))] = h.v[j];
+    }
+    st[buf][cs] = h.sm;
+  };
+  // in-order returns: weights of stages 0 and 1, h of stages 0 and 1, then
+  // the weights of stage 2 (in the loop, as in the first stage, h then weights)
+  Q2kSub W[4];
+  q2k_sub_load(drow, 0, q, W[0]);
+  q2k_sub_load(drow, 1, q, W[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  HV H0 = h_load(0), H1 = h_load(1);
+  __builtin_amdgcn_sched_barrier(0);
+  q2k_sub_load(drow, 2, q, W[2]);
+  __builtin_amdgcn_sched_barrier(0);
+  h_store(0, H0);
   __syncthreads();
 
-  f32x4_t acc[4];
+  f32x4_t acc[MT];
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nst; s++) {
-    const bool more = s + 1 < nst;
-    Q2kStage nw;
-    uint4 hv[4];
-    if (more) {
-      q2k_stage_load(drow, s + 1, q, nw);
-      h_load(s + 1, hv);
+  for (int mt = 0; mt < MT; mt++) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float dp = 1.0f;  // d of the current block
+  auto stage = [&](int s, auto Rc) {
+    constexpr int R = decltype(Rc)::value;
+    if constexpr ((R & 1) == 0) H0 = h_load(min(s + 2, nst - 1));
+    else H1 = h_load(min(s + 2, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    q2k_sub_load(drow, s + 3 < nst ? s + 3 : s - 1, q, W[(R + 3) & 3]);
+    __builtin_amdgcn_sched_barrier(0);
+    const Q2kSub& cw = W[R];
+    const float dv = f16_bits_to_f32(cw.dd & 0xFFFFu);
+    const float d = dv != 0.0f ? dv : 1.0f;
+    if constexpr ((R & 1) == 0) {  // a block starts: sums in units of its d
+      const float r = dp / d;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) acc[mt] *= r;
+      dp = d;
     }
-    const int hf = s & 1;
-    const float d24 = f16_bits_to_f32(cw.dd & 0xFFFFu) * 16777216.0f;
-    // 16-bit lanes holding whole code bytes: (byte0, byte1), (byte2, byte3)
-    const uint32_t pa0 = vperm(0u, cw.qa, 0x0C010C00u), pa1 = vperm(0u, cw.qa, 0x0C030C02u);
-    const uint32_t pb0 = vperm(0u, cw.qb, 0x0C010C00u), pb1 = vperm(0u, cw.qb, 0x0C030C02u);
-    // scale bytes of this half's eight sub-blocks
-    const uint32_t sc0 = hf ? cw.sc.z : cw.sc.x, sc1 = hf ? cw.sc.w : cw.sc.y;
-    const char* ahb = (const char*)ah + 8 * (q & 1);
-    const char* alb = (const char*)al + 8 * (q & 1);
+    // scale bytes 2j + (q >> 1) of the half (sub-block 8hf + 2j + (q >> 1))
+    const uint32_t s4 = vperm(cw.s1, cw.s0, (q >> 1) ? 0x07050301u : 0x06040200u);
+    const uint32_t scm = dv != 0.0f ? s4 & 0x0F0F0F0Fu : 0u;
+    // code bytes in 16-bit lanes: (b0, b1), (b2, b3), (b4, b5), (b6, b7)
+    const uint32_t P0 = vperm(0u, cw.c0, 0x0C010C00u), P1 = vperm(0u, cw.c0, 0x0C030C02u);
+    const uint32_t P2 = vperm(0u, cw.c1, 0x0C010C00u), P3 = vperm(0u, cw.c1, 0x0C030C02u);
+    const u32x4_t* hb = ht[R & 1];
 #pragma unroll
-    for (int sb = 0; sb < 8; sb++) {
-      // sub-block 8hf + sb of the block: shift s2 = sb >> 1, half p = sb & 1
-      const int s2 = sb >> 1, p = sb & 1;
-      const uint32_t mk = 0x00030003u << (2 * s2);
-      const uint32_t b0 = (p ? pb0 : pa0) & mk, b1 = (p ? pb1 : pa1) & mk;
-      const f16x4_t bf = __builtin_bit_cast(f16x4_t, make_uint2(b0, b1));
-      const uint32_t scb = ((sb < 4 ? sc0 : sc1) >> (8 * (sb & 3))) & 0xFu;
-      const float mult = d24 * (1.0f / (float)(1 << (2 * s2))) * (float)scb;
+    for (int j = 0; j < 4; j++) {
+      const uint32_t sc = (scm >> (8 * j)) & 0xFFu;
+      // q * sc < 46 in each 16-bit lane: the binary16 subnormal q sc 2^-24
+      const uint4 bv = make_uint4(__mul24((P0 >> (2 * j)) & 0x00030003u, sc),
+                                  __mul24((P1 >> (2 * j)) & 0x00030003u, sc),
+                                  __mul24((P2 >> (2 * j)) & 0x00030003u, sc),
+                                  __mul24((P3 >> (2 * j)) & 0x00030003u, sc));
+      const f16x8_t bf = __builtin_bit_cast(f16x8_t, bv);
 #pragma unroll
-      for (int mt = 0; mt < 4; mt++) {
-        if (mt >= mtiles) break;
+      for (int mt = 0; mt < MT; mt++) {
+        if (MT > 1 && mt >= mtiles) break;
         const int m = 16 * mt + (lane & 15);
-        // A: values 16 sb + 4q .. +3 = half (q & 1) of chunk 2 sb + (q >> 1)
-        const int off = 16 * (m * 16 + ((2 * sb + (q >> 1)) ^ (m & 15)));
-        const uint2 fh = *(const uint2*)(ahb + off);
-        const uint2 fl = *(const uint2*)(alb + off);
-        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, fh), bf, z, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, fl), bf, t, 0, 0, 0);
-        acc[mt] += mult * t;
+        const int c = (4 * j + q) ^ (m & 15);
+        const f16x8_t ahi = __builtin_bit_cast(f16x8_t, hb[m * 32 + c]);
+        const f16x8_t alo = __builtin_bit_cast(f16x8_t, hb[m * 32 + 16 + c]);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bf, acc[mt], 0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bf, acc[mt], 0, 0, 0);
       }
     }
-    if (hf == 1) {
-      // mins of the block: k = sub-block (16), lane quarter q: sub-blocks 4q .. 4q+3
-      const int kb = s >> 1;
-      const float dmin = f16_bits_to_f32(cw.dd >> 16);
-      const uint32_t scq = q == 0 ? cw.sc.x : q == 1 ? cw.sc.y : q == 2 ? cw.sc.z : cw.sc.w;
-      const uint32_t mn = (scq >> 4) & 0x0F0F0F0Fu;
-      const uint32_t m0 = vperm(0u, mn, 0x0C010C00u), m1 = vperm(0u, mn, 0x0C030C02u);
+    // mins of the half's eight sub-blocks: quarter q < 2 holds 4q .. 4q+3
+    {
+      const uint32_t mn = ((q & 1) ? cw.s1 : cw.s0) >> 4 & 0x0F0F0F0Fu;
+      const uint32_t m0 = q < 2 ? vperm(0u, mn, 0x0C010C00u) : 0u;
+      const uint32_t m1 = q < 2 ? vperm(0u, mn, 0x0C030C02u) : 0u;
       const f16x4_t bm = __builtin_bit_cast(f16x4_t, make_uint2(m0, m1));
-      const float mmult = dmin * 16777216.0f;
+      const float fmin = f16_bits_to_f32(cw.dd >> 16) / d;
+      const u32x4_t* sb = st[R & 1];
 #pragma unroll
-      for (int mt = 0; mt < 4; mt++) {
-        if (mt >= mtiles) break;
+      for (int mt = 0; mt < MT; mt++) {
+        if (MT > 1 && mt >= mtiles) break;
         const int m = 16 * mt + (lane & 15);
-        uint2 sh2 = make_uint2(0, 0), sl2 = make_uint2(0, 0);
-        if (m < nrows) {
-          const size_t off = (size_t)(row0 + m) * (a.I / 16) + 16 * kb + 4 * q;
-          sh2 = *(const uint2*)(a.hsh + off);
-          sl2 = *(const uint2*)(a.hsl + off);
-        }
+        const uint2* sp = (const uint2*)&sb[2 * m];
+        const uint2 shi = sp[q & 1], slo = sp[2 + (q & 1)];
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, sh2), bm, z, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, sl2), bm, t, 0, 0, 0);
-        acc[mt] -= mmult * t;
+        f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, shi), bm, z, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, slo), bm, t, 0, 0, 0);
+        acc[mt] -= fmin * t;
       }
     }
-    __syncthreads();  // every wave is done with the tile of stage s
-    if (more) {
-      h_store(hv);
-      cw = nw;
-    }
+    // h of stage s + 1 into the other buffers (after the last stage: unused)
+    if constexpr ((R & 1) == 0) h_store(1, H1);
+    else h_store(0, H0);
     __syncthreads();
+  };
+  for (int s0 = 0; s0 < nst; s0 += 4) {
+    stage(s0, std::integral_constant<int, 0>{});
+    stage(s0 + 1, std::integral_constant<int, 1>{});
+    stage(s0 + 2, std::integral_constant<int, 2>{});
+    stage(s0 + 3, std::integral_constant<int, 3>{});
   }
+  const float fin = dp * 16777216.0f;
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++)
+  for (int mt = 0; mt < MT; mt++)
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       if (mt >= mtiles) break;
       const int m = 16 * mt + 4 * q + r;
-      if (m < nrows) a.y[(size_t)(row0 + m) * a.H + n] = acc[mt][r];
+      if (m < nrows) a.y[(size_t)(row0 + m) * a.H + n] = acc[mt][r] * fin;
     }
 }
 
