@@ -393,7 +393,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
         const size_t n8 = (size_t)T * g.H / 8;
         launch_k(k_x_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, g.x, n8,
                  at<uint16_t>(ws, L.x16), status);
-        launch_k(k_grouped_gateup_iq2<1>, dim3(g.I / kGNF, E < TK ? E : TK), dim3(kGW * 64), 0, st, g);
+        launch_k(k_grouped_gateup_iq2_small, dim3(g.I / kGNF, E < TK ? E : TK), dim3(kGW * 64), 0, st, g);
         launch_k(k_grouped_gateup_iq2<4>, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
       }
       if (q80) {

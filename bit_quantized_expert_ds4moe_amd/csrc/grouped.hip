@@ -564,7 +564,8 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
     const uint32_t cg = iq2_sub_words<EVEN>(W[R][0], ig, sg, dg);
     const uint32_t cu = iq2_sub_words<EVEN>(W[R][1], iu, su, du);
     if constexpr ((R & 1) == 0) {  // a block starts: sums in units of its d
-      const float rg = dgp / dg, ru = dup / du;
+      // (hardware reciprocal: within 1 ulp, one rounding per block either way)
+      const float rg = dgp * __builtin_amdgcn_rcpf(dg), ru = dup * __builtin_amdgcn_rcpf(du);
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) {
         accg[mt] *= rg;
@@ -604,6 +605,113 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
     accu[mt] *= dup * 0.125f;
   }
   swiglu_store<MT>(a, row0, nrows, mtiles, n, q, accg, accu);
+}
+
+// Small items (at most 16 rows, listed first): as k_grouped_gateup_iq2 with
+// MT = 1, but the x tiles sit in an LDS ring of eight stages and the block
+// synchronises once per four stages instead of once per stage, so that its
+// waves drift apart within a round and their memory, VALU and MFMA phases
+// overlap.  During round r (stages 4r .. 4r+3) the ring holds round r's tiles
+// (read) and receives round r + 1's: stage s requests x of stage s + 5 and
+// stores x of stage s + 4 (requested one stage earlier) into the slot of
+// stage s - 4, which every wave finished before the last barrier.
+__global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2_small(GroupArgs a) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ uint4 gt8[256 * 8];       // 32 KB
+  __shared__ uint4 mt8[128 * 8];       // 16 KB
+  __shared__ u32x4_t xr[8][16 * 16];   // 32 KB: 80 KB in all, two blocks per CU
+  const int item = (int)blockIdx.y;
+  if (item >= a.n_items[1]) return;
+  const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
+  if (e >= a.E) return;
+  const int n0 = blockIdx.x * kGNF;
+  if (n0 >= a.I) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = lane >> 4;
+  const int n = n0 + 16 * w + (lane & 15);
+  const uint32_t rep16 = (uint32_t)(lane & 7) << 4;
+  const int rowbytes = (a.H / 256) * kIq2Bytes;
+  const uint8_t* grow = a.gate + ((size_t)e * a.I + n) * rowbytes;
+  const uint8_t* urow = a.up + ((size_t)e * a.I + n) * rowbytes;
+  const int nst = a.H / kGStage;  // a multiple of 4
+  // x chunk c = tid & 255 (the upper half of the block repeats the lower):
+  // row c >> 4 (past the item: row 0, computed and dropped), column chunk c & 15
+  const int c = tid & 255, xm = c >> 4, xch = c & 15;
+  const int xslot = xm * 16 + (xch ^ xm);
+  // in-order returns: grid bytes and the token, weights of stages 0 and 1,
+  // x of stages 0-4, weights of stage 2
+  const uint2 gb = *(const uint2*)(a.grid + 8 * (tid & 255));
+  const int xtok = a.perm[row0 + (xm < nrows ? xm : 0)] / a.K;
+  __builtin_amdgcn_sched_barrier(0);
+  Iq2Sub W[4][2];
+  iq2_sub_load<true>(grow, 0, q, W[0][0]);
+  iq2_sub_load<true>(urow, 0, q, W[0][1]);
+  iq2_sub_load<true>(grow, 1, q, W[1][0]);
+  iq2_sub_load<true>(urow, 1, q, W[1][1]);
+  __builtin_amdgcn_sched_barrier(0);
+  build_tables8_f16(gb, gt8, mt8);
+  const u32x4_t* xp = (const u32x4_t*)(a.x16 + (size_t)xtok * a.H) + xch;
+  auto x_load = [&](int s) { return xp[16 * s]; };
+  u32x4_t x0 = x_load(0), x1 = x_load(1), x2 = x_load(2), x3 = x_load(3);
+  u32x4_t XA = x_load(min(4, nst - 1)), XB;  // x of stage s + 4 (to store), of s + 5 (in flight)
+  __builtin_amdgcn_sched_barrier(0);
+  iq2_sub_load<false>(grow, 2, q, W[2][0]);
+  iq2_sub_load<false>(urow, 2, q, W[2][1]);
+  __builtin_amdgcn_sched_barrier(0);
+  xr[0][xslot] = x0;
+  xr[1][xslot] = x1;
+  xr[2][xslot] = x2;
+  xr[3][xslot] = x3;
+  __syncthreads();  // tables, x of round 0
+
+  f32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  const uint8_t* gtab = (const uint8_t*)gt8;
+  const uint8_t* stab = (const uint8_t*)mt8;
+  float dgp = 1.0f, dup = 1.0f;
+  const int m = lane & 15;
+  auto stage = [&](int s, auto Rc) {
+    constexpr int R = decltype(Rc)::value;
+    constexpr bool EVEN = R < 2;
+    u32x4_t& xin = (R & 1) ? XA : XB;   // receives x of stage s + 5
+    u32x4_t& xout = (R & 1) ? XB : XA;  // holds x of stage s + 4
+    xin = x_load(min(s + 5, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    const int sw = s + 3 < nst ? s + 3 : s - 1;
+    constexpr bool EVEN3 = ((R + 3) >> 1 & 1) == 0;
+    iq2_sub_load<EVEN3>(grow, sw, q, W[(R + 3) & 3][0]);
+    iq2_sub_load<EVEN3>(urow, sw, q, W[(R + 3) & 3][1]);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t ig, sg, iu, su;
+    float dg, du;
+    const uint32_t cg = iq2_sub_words<EVEN>(W[R][0], ig, sg, dg);
+    const uint32_t cu = iq2_sub_words<EVEN>(W[R][1], iu, su, du);
+    if constexpr ((R & 1) == 0) {  // a block starts: sums in units of its d
+      // (hardware reciprocal: within 1 ulp, one rounding per block either way)
+      const float rg = dgp * __builtin_amdgcn_rcpf(dg), ru = dup * __builtin_amdgcn_rcpf(du);
+      accg *= rg;
+      accu *= ru;
+      dgp = dg;
+      dup = du;
+    }
+    const u32x4_t* xb = xr[s & 7];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f16x8_t fg = iq2_sub_frag(ig, sg, j, cg, rep16, gtab, stab);
+      const f16x8_t fu = iq2_sub_frag(iu, su, j, cu, rep16, gtab, stab);
+      const f16x8_t af = __builtin_bit_cast(f16x8_t, xb[m * 16 + ((4 * q + j) ^ m)]);
+      accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fg, accg, 0, 0, 0);
+      accu = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fu, accu, 0, 0, 0);
+    }
+    xr[(s + 4) & 7][xslot] = xout;  // past the last stage: unused
+    if constexpr (R == 3) __syncthreads();
+  };
+  for (int s0 = 0; s0 < nst; s0 += 4) {
+    stage(s0, std::integral_constant<int, 0>{});
+    stage(s0 + 1, std::integral_constant<int, 1>{});
+    stage(s0 + 2, std::integral_constant<int, 2>{});
+    stage(s0 + 3, std::integral_constant<int, 3>{});
+  }
+  f32x4_t ag[1] = {accg * (dgp * 0.125f)}, au[1] = {accu * (dup * 0.125f)};
+  swiglu_store<1>(a, row0, nrows, 1, n, q, ag, au);
 }
 
 // x (bf16) -> binary16 for k_grouped_gateup_iq2; magnitudes beyond the
@@ -1055,8 +1163,9 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
     const Q2kSub& cw = W[R];
     const float dv = f16_bits_to_f32(cw.dd & 0xFFFFu);
     const float d = dv != 0.0f ? dv : 1.0f;
+    const float rd = __builtin_amdgcn_rcpf(d);  // within 1 ulp
     if constexpr ((R & 1) == 0) {  // a block starts: sums in units of its d
-      const float r = dp / d;
+      const float r = dp * rd;
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) acc[mt] *= r;
       dp = d;
@@ -1094,7 +1203,7 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
       const uint32_t m0 = q < 2 ? vperm(0u, mn, 0x0C010C00u) : 0u;
       const uint32_t m1 = q < 2 ? vperm(0u, mn, 0x0C030C02u) : 0u;
       const f16x4_t bm = __builtin_bit_cast(f16x4_t, make_uint2(m0, m1));
-      const float fmin = f16_bits_to_f32(cw.dd >> 16) / d;
+      const float fmin = f16_bits_to_f32(cw.dd >> 16) * rd;
       const u32x4_t* sb = st[R & 1];
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) {

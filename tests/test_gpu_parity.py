@@ -391,3 +391,69 @@ def test_grouped_prefill_512_zipf_sampled():
     t_light = int(np.where((ids == light).any(1))[0][0])
     grouped_case(w, ids, wts, tokens_for_oracle=[0, t_heavy, t_light, w.T - 1],
                  tol=TOL_FP32)
+
+
+def _grouped_fast_case(zero_d):
+    # hidden 512, inter 512: both pipelined kernels (IQ2_XXS gate/up with four
+    # 128-column stages, Q2_K down with four), 160 tokens x top-4 over 16
+    # experts with Zipf(1.1) routing: items of 64 rows, ragged last pieces and
+    # small items (at most 16 rows); every output checked.  zero_d: every
+    # third gate/up block and every third down block has d = 0 (a block of
+    # zeros in the main term; the down mins still count), every fifth down
+    # block dmin = 0.
+    from ds4gen.device import make_layer, host_experts
+    w = g.Workload("grouped-fast", 13, 160, 512, 512, 16, 4, g.IQ2_XXS, g.IQ2_XXS, g.Q2_K,
+                   "bf16", "f16")
+    lt = make_layer(w, 0)
+    ids, wts = g.zipf_routing(13, w.T, w.E, w.K)
+    counts = np.bincount(ids.ravel(), minlength=w.E)
+    assert (counts > 64).any() and ((counts > 0) & (counts <= 16)).any()
+    assert ((counts > 64) & (counts % 64 > 0) & (counts % 64 <= 16)).any()
+    bpe = w.blocks_per_expert
+
+    def patch(a, nbytes, views):
+        v = a.reshape(-1, nbytes)
+        for rows, lo, hi in views:
+            v[rows, lo:hi] = 0
+
+    iq2_z = [(slice(1, None, 3), 0, 2)]
+    q2k_z = [(slice(1, None, 3), 80, 82), (slice(2, None, 5), 82, 84)]
+    if zero_d:
+        for t, nbytes, views in ((lt.gate, 66, iq2_z), (lt.up, 66, iq2_z), (lt.down, 84, q2k_z)):
+            tv = t.view(w.E, -1)
+            for e in range(w.E):
+                row = tv[e].view(-1, nbytes)
+                for rows, lo, hi in views:
+                    row[rows, lo:hi] = 0
+    hx = host_experts(w, 0, np.unique(ids))
+    if zero_d:
+        for e in hx:
+            gb, ub, db = (np.array(a, copy=True) for a in hx[e])
+            patch(gb, 66, iq2_z)
+            patch(ub, 66, iq2_z)
+            patch(db, 84, q2k_z)
+            assert gb.size == bpe["gate"] * 66 and db.size == bpe["down"] * 84
+            hx[e] = (gb, ub, db)
+    x = g.activations(w, n_tok=w.T)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, w.T)
+    out = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+    xd, idd, wd = dev(x), dev(ids), dev(wts)
+    ds4.expert_ffn(shp, experts_of(lt, w), None, ptr(xd), x_dtype(w), w.T, ptr(idd), ptr(wd),
+                   ptr(out), None, ptr(ws), nb, stream())
+    check_clean(ws)
+    want = oracle.moe_ffn(x, "bf16", ids, wts, hx, (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I,
+                          w.E, grid=g.grid(w.seed), tokens=np.arange(w.T))
+    err = max_rel_err(out.cpu().numpy(), want)
+    say("  grouped-fast zero_d=%d max|err|/rms = %g" % (zero_d, err))
+    assert err <= TOL_FP32
+
+
+def test_grouped_pipelined_kernels_all_outputs():
+    say("grouped pipelined kernels")
+    _grouped_fast_case(False)
+
+
+def test_grouped_pipelined_kernels_zero_scales():
+    say("grouped pipelined kernels, d = 0 blocks")
+    _grouped_fast_case(True)
