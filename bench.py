@@ -438,7 +438,7 @@ def bench_batched(args, which):
         "mfma_tflops": round(flops / sec / 1e12, 2),
         "mfma_frac": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
-        "roofline": {"bound": "hbm", "kernel": "k_grouped_gateup_iq2" if prefill else "k_gateup_b1",
+        "roofline": {"bound": "hbm", "kernel": ("grouped IQ2_XXS gate/up: k_x_to_f16 + k_grouped_gateup_iq2_small + k_grouped_gateup_iq2<4>" if prefill else "k_gateup_b1"),
                      "achieved": round(gu_bytes / gu_s / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gu_bytes / gu_s / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": None, "bytes_per_launch": int(gu_bytes),
