@@ -11,7 +11,8 @@ region.  Prints one JSON line.
 
 Other workloads (--workload): decode-b8 (8 correlated tokens + Q8_0 shared
 expert), prefill-512 (Zipf-routed 512-token chunk), stack-43 (43-layer
-decode stack, hash routing in layers 0-2).
+decode stack, hash routing in layers 0-2), decode-sweep (the decode-b8 layer
+at 1 to 64 tokens per call).
 """
 import argparse
 import json
@@ -447,6 +448,107 @@ def bench_batched(args, which):
     return res
 
 
+def bench_sweep(args):
+    """Decode batch sweep: the config-2 layer (learned router, Q8_0 shared
+    expert, correlated tokens) at T = 1 .. 64 tokens per call, one
+    ds4moe_layer call per step.  Up to 13 tokens the routed experts run
+    through the streaming matvec kernels (one grid row per token), above that
+    through the grouped MFMA kernels; the sweep shows where the union of
+    experts makes the grouped form pay.  Each T: hip-graph replay of `steps` calls on distinct
+    tokens after `warmup` calls."""
+    import numpy as np
+    import torch
+
+    import bit_quantized_expert_ds4moe_amd as ds4
+    import ds4gen as g
+    from ds4gen.device import make_layer, to_dev
+
+    w = g.WORKLOADS[2]
+    sizes = [1, 2, 4, 8, 12, 13, 14, 16, 24, 32, 48, 64]
+    tmax = max(sizes)
+    log("building layer tensors (%s)" % w.name)
+    lt = make_layer(w, 0)
+    ex = ds4.experts(lt.gate.data_ptr(), lt.up.data_ptr(), lt.down.data_ptr(), w.I,
+                     (w.gate_qt, w.up_qt, w.down_qt), grid=lt.grid.data_ptr())
+    sh = ds4.experts(lt.shared[0].data_ptr(), lt.shared[1].data_ptr(), lt.shared[2].data_ptr(),
+                     w.I, (g.Q8_0, g.Q8_0, g.Q8_0))
+    shp = ds4.shape(w.H, w.I, w.E, w.K, 1.5)
+    nb = ds4.workspace_size(shp, tmax)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    n_calls = args.warmup + args.steps
+    x = to_dev(g.activations(w, n_tok=tmax * n_calls))
+    out = torch.empty((tmax, w.H), dtype=torch.float32, device="cuda")
+    ids_d = torch.empty((n_calls, tmax, w.K), dtype=torch.int32, device="cuda")
+    row = w.H * 2
+    desc = ds4.layer_desc(ds4.router(w=lt.router_w.data_ptr(), w_dtype=ds4.F16,
+                                     bias=lt.bias.data_ptr()), ex, shared=sh)
+    st = torch.cuda.current_stream().cuda_stream
+    per_expert = w.expert_bytes()
+    sh_bytes = 3 * w.I * w.H // 32 * g.BLOCK_BYTES[g.Q8_0]
+    # untimed: bring the clocks up before the first (smallest) size
+    for i in range(200):
+        ds4.layer(shp, desc, x.data_ptr() + (i % n_calls) * 8 * row, ds4.BF16, None, out.data_ptr(),
+                  None, 8, None, None, None, ws.data_ptr(), nb, st)
+    torch.cuda.synchronize()
+    rows = []
+    for T in sizes:
+        def step(i, s, ids_out=None):
+            ds4.layer(shp, desc, x.data_ptr() + i * T * row, ds4.BF16, None, out.data_ptr(), None, T,
+                      ids_out, None, None, ws.data_ptr(), nb, s)
+
+        step(0, st)
+        assert ds4.check(ws.data_ptr(), st) == 0
+
+        def capture(first, count):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                cs = torch.cuda.current_stream().cuda_stream
+                for j in range(count):
+                    step(first + j, cs)
+            return gr
+
+        g_warm = capture(0, args.warmup)
+        g_main = capture(args.warmup, args.steps)
+        g_warm.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g_main.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        assert ds4.check(ws.data_ptr(), st) == 0
+        for i in range(args.warmup, n_calls):
+            step(i, st, ids_d[i].data_ptr())
+        torch.cuda.synchronize()
+        idh = ids_d[args.warmup:, :T].cpu().numpy()
+        touched = float(np.mean([np.unique(a).size for a in idh]))
+        sec = ms * 1e-3 / args.steps
+        rows.append({"T": T, "tokens_per_s": round(T / sec, 1), "us_per_step": round(sec * 1e6, 2),
+                     "experts_touched": round(touched, 2),
+                     "expert_gbs": round((touched * per_expert + sh_bytes) / sec / 1e9, 1)})
+        log("T=%d: %s" % (T, rows[-1]))
+        del g_warm, g_main
+    last = rows[-1]
+    return {
+        "metric": "batched-decode tokens/s through one routed-expert layer (sweep; value at T=%d)" % tmax,
+        "value": last["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": last["us_per_step"] * 1e-3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "v4flash-layer-decode-sweep-1-64", "hidden": w.H, "inter": w.I,
+                   "experts": w.E, "top_k": w.K, "shared_q8_0": True, "routing": "learned router",
+                   "tokens_per_call": sizes},
+        "sweep": rows,
+        "expert_gbs": last["expert_gbs"],
+        "expert_hbm_frac": round(last["expert_gbs"] / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "whole layer call at T=%d" % tmax,
+                     "achieved": last["expert_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(last["expert_gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": None},
+    }
+
+
 def cpu_baseline_stack(w, n_layers):
     """The oracle on one decode step through the first n_layers layers
     (normalisation, routing, experts, residual), scaled to 43 layers."""
@@ -522,7 +624,7 @@ def main():
                     help="timed steps (default 2000 tokens for decode-b1, 256 for stack-43)")
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode-b1",
-                    choices=["decode-b1", "stack-43", "decode-b8", "prefill-512"])
+                    choices=["decode-b1", "stack-43", "decode-b8", "prefill-512", "decode-sweep"])
     ap.add_argument("--layer-copies", type=int, default=1,
                     help="rotate over this many independently seeded layers")
     ap.add_argument("--cpu-sample", type=int, default=None,
@@ -542,9 +644,9 @@ def main():
     stack = args.workload == "stack-43"
     batched = args.workload in ("decode-b8", "prefill-512")
     if args.steps is None:
-        args.steps = 256 if stack else 200 if batched else 2000
+        args.steps = 256 if stack else 200 if batched else 50 if args.workload == "decode-sweep" else 2000
     if args.warmup is None:
-        args.warmup = 8 if stack else 20 if batched else 200
+        args.warmup = 8 if stack else 20 if batched else 5 if args.workload == "decode-sweep" else 200
     if args.cpu_sample is None:
         args.cpu_sample = 6 if stack else 3
     import torch
@@ -564,6 +666,8 @@ def main():
         res = bench_stack(args)
     elif args.workload in ("decode-b8", "prefill-512"):
         res = bench_batched(args, args.workload)
+    elif args.workload == "decode-sweep":
+        res = bench_sweep(args)
     else:
         res = bench_decode_b1(args)
     print(json.dumps(res), flush=True)

@@ -18,9 +18,13 @@ using namespace ds4;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-constexpr int kB1MaxTokens = 16;   // few-token calls use the streaming matvec kernels
-constexpr int kSharedSplitG = 16;  // K shares of a shared expert's gate/up in such calls (<= kMaxSplit)
+// Few-token calls use the streaming matvec kernels: each token reads its six
+// experts, which beats the grouped kernels' one read per distinct expert up to
+// about 13 tokens of correlated decode (measured crossover 12..16 tokens).
+constexpr int kB1MaxTokens = 13;
+constexpr int kSharedSplitG = 16;  // K shares of a shared expert's gate/up in calls of few tokens (<= kMaxSplit)
 constexpr int kSharedSplitD = 4;   // and of its down
+constexpr int kSharedSplitMaxT = 64;  // "few": one work item of shared rows
 
 // Byte offsets of the workspace regions for (shape, n_tok).
 struct Layout {
@@ -49,7 +53,7 @@ Layout layout_for(const ds4moe_shape& s, int32_t T) {
   L.y = take(np * H * 4);
   L.hb = take(np * I * 2);
   // K shares of a shared expert in few-token calls
-  L.part = take(t <= (size_t)kB1MaxTokens ? (size_t)kSharedSplitG * t * (2 * I > H ? 2 * I : H) * 4 : 0);
+  L.part = take(t <= (size_t)kSharedSplitMaxT ? (size_t)kSharedSplitG * t * (2 * I > H ? 2 * I : H) * 4 : 0);
   L.total = o;
   return L;
 }
@@ -379,7 +383,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     g.y = at<float>(ws, L.y);
     g.ksplit_g = g.ksplit_d = 1;
     g.part = at<float>(ws, L.part);
-    if (b1 && sh) {
+    if (sh && T <= kSharedSplitMaxT) {  // a single item of shared rows: spread it along K
       if ((g.H / 64) % kSharedSplitG == 0) g.ksplit_g = kSharedSplitG;
       if ((g.sh_I / 256) % kSharedSplitD == 0) g.ksplit_d = kSharedSplitD;
     }
@@ -421,14 +425,17 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     {
       ProfScope prof(DS4MOE_K_OTHER, st, !b1);
       const size_t n = (size_t)T * s.hidden;
-      if (b1)
+      // the shared expert's output: y rows T*K.. (one share) or the K shares
+      // in part, added by k_add_shared after the routed combine
+      const bool add_sh = sh && (b1 || g.ksplit_d > 1);
+      if (!b1)
+        launch_k(k_grouped_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                 (const float*)g.y, (const int32_t*)inv, wts, T, K, s.hidden,
+                 (sh && !add_sh) ? 1 : 0, out, residual);
+      if (add_sh)
         launch_k(k_add_shared, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                  (const float*)g.y, (const float*)g.part, g.ksplit_d, TK, T, s.hidden,
                  residual ? residual : out);
-      else
-        launch_k(k_grouped_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                 (const float*)g.y, (const int32_t*)inv, wts, T, K, s.hidden, sh ? 1 : 0, out,
-                 residual);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     if (perm_dbg && !b1) {

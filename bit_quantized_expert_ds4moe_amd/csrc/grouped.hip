@@ -915,8 +915,9 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
   if (item >= *a.n_items) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   const bool shr = e == a.E;
-  // routed Q2_K items run in k_grouped_down_q2k
-  if (!shr && q2k_grouped_fast(a)) return;
+  // routed Q2_K items run in k_grouped_down_q2k; only the shared expert is
+  // split along K (grid z)
+  if (!shr && (q2k_grouped_fast(a) || blockIdx.z > 0)) return;
   const int I = shr ? a.sh_I : a.I;
   const int qd = shr ? a.sh_qt_d : a.qt_d;
   const uint8_t* D = shr ? a.sh_down : a.down;
@@ -1252,7 +1253,9 @@ __global__ void k_grouped_combine(const float* y, const int32_t* inv, const floa
   else out[idx] = acc;
 }
 
-// The grouped path needs bf16 x, 256-multiple shapes and formats it knows.
+// The grouped kernels need bf16 x, 256-multiple shapes and formats they know
+// (any token count: at one token they run the shared expert after the
+// streaming matvec kernels).
 inline bool grouped_eligible(const ds4moe_shape& s, const ds4moe_experts& ex,
                              const ds4moe_experts* sh, const void* x, int32_t x_dt, int32_t T) {
   auto gu_ok = [](int qt) { return qt == DS4MOE_IQ2_XXS || qt == DS4MOE_Q8_0; };
@@ -1264,7 +1267,7 @@ inline bool grouped_eligible(const ds4moe_shape& s, const ds4moe_experts& ex,
     if (!gu_ok(sh->gate_qtype) || !gu_ok(sh->up_qtype) || !dn_ok(sh->down_qtype)) return false;
     if (sh->inter % 256 || ((uintptr_t)sh->gate | (uintptr_t)sh->up | (uintptr_t)sh->down) % 16) return false;
   }
-  return T > 1;
+  return T >= 1;
 }
 
 }  // namespace ds4

@@ -266,6 +266,15 @@ def test_ffn_v4_decode_b8_shared_q8():
     assert ffn_case(2, 8) <= TOL_FP32
 
 
+@pytest.mark.parametrize("T", [1, 17, 64])
+def test_ffn_v4_decode_batch_shared_split(T):
+    # one token (matvec kernels, then the shared expert alone through the
+    # grouped kernels) and just past the few-token path (routed experts
+    # through the grouped kernels too); the Q8_0 shared expert's single item
+    # is split along K (16 and 4 shares) and added after the routed part
+    assert ffn_case(2, T, tokens_for_oracle=sorted({0, T // 2, T - 1})) <= TOL_FP32
+
+
 # --------------------------------------------------------------------------
 # whole layer
 # --------------------------------------------------------------------------
