@@ -45,6 +45,9 @@ def lib():
         L.or_moe_ffn.argtypes = [i32, i32, i32, i32, vp, i32, vp, vp, vp, i32,
                                  i32, vp, i32, vp, i32, vp, vp, i32, i32, vp, vp, vp, vp]
         L.or_moe_ffn.restype = i32
+        L.or_imatrix.argtypes = [i32, i32, i32, i32, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp,
+                                 vp, vp]
+        L.or_imatrix.restype = i32
         L.or_rmsnorm_bf16.argtypes = [i32, i32, vp, vp, dbl, vp]
         L.or_rmsnorm_bf16.restype = i32
         L.or_residual_add.argtypes = [i64, vp, vp]
@@ -172,6 +175,32 @@ def moe_ffn(x, xfmt, ids, wts, experts, qts, H, I, E, grid=None, tokens=None, sh
     if rc != 0:
         raise ValueError("or_moe_ffn rc=%d" % rc)
     return out
+
+
+def imatrix(x, xfmt, ids, wts, experts, qts, H, I, E, grid=None):
+    """Importance statistics of one call (DS4C2 sec. 5): per expert and
+    column, the sum over its (token, slot) pairs of x^2 (gate/up input, [E][H])
+    and of (w * h)^2 (down input, [E][I]), fp64.  experts: dict e -> (gate,
+    up[, down]) bytes for every expert used; qts: (gate_qt, up_qt, ...)."""
+    x = _c(x, np.float32 if xfmt == "f32" else np.uint16)
+    ids = _c(ids, np.int32)
+    wts = _c(wts, np.float32)
+    T, K = ids.shape
+    keep = []
+    arrs = [(ctypes.c_void_p * E)() for _ in range(2)]
+    for e, mats in experts.items():
+        for j in range(2):
+            a = _c(mats[j], np.uint8)
+            keep.append(a)
+            arrs[j][e] = a.ctypes.data
+    g = None if grid is None else _c(grid, np.uint8)
+    gu = np.zeros((E, H), np.float64)
+    dn = np.zeros((E, I), np.float64)
+    rc = lib().or_imatrix(H, I, E, K, T, _p(x), dtype_code(x, xfmt), _p(ids), _p(wts), qts[0],
+                          arrs[0], qts[1], arrs[1], _p(g), _p(gu), _p(dn))
+    if rc != 0:
+        raise ValueError("or_imatrix rc=%d" % rc)
+    return gu, dn
 
 
 def rmsnorm_bf16(h, w, eps=1e-6):

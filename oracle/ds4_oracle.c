@@ -499,6 +499,68 @@ EXPORT int or_moe_ffn(int H, int I, int E, int K, const void* x, int xdt, const 
 }
 
 /* ------------------------------------------------------------------ */
+/* Importance statistics of the routed experts' inputs (DS4C2 sec. 5,  */
+/* "imatrix": activation statistics, not weight statistics; sec. 7:    */
+/* one entry of n_expert * n_columns values per tensor)                */
+/* ------------------------------------------------------------------ */
+
+/*
+ * For every token t < T and slot k < K with e = ids[t][k]:
+ *   gu[e][c] += x[t][c]^2                 (c < H: the gate/up input, i.e. the
+ *                                          FFN-normalised activation as given)
+ *   dn[e][i] += (w_tk * h_tk[i])^2        (i < I: the down input, the SwiGLU
+ *                                          row of the pair after its routing
+ *                                          weight is applied)
+ * with h_tk = SiLU(W_gate[e] x_t) * (W_up[e] x_t) in fp64.  Reading: the
+ * routing weight is the one the layer multiplies the expert's output by (it
+ * includes the routed scaling, so the weights of a token sum to 1.5).  gu and
+ * dn (E*H and E*I doubles) are accumulated into, in token-then-slot order.
+ */
+EXPORT int or_imatrix(int H, int I, int E, int K, int T, const void* x, int xdt,
+                      const int32_t* ids, const float* wts, int gate_qt,
+                      const uint8_t* const* expert_gate, int up_qt,
+                      const uint8_t* const* expert_up, const uint8_t* grid, double* gu,
+                      double* dn) {
+  if (H <= 0 || I <= 0 || E <= 0 || K <= 0 || T < 0) return OR_EINVAL;
+  int xsz = xdt == OR_F32 ? 4 : 2;
+  for (int64_t j = 0; j < (int64_t)T * K; j++)
+    if (ids[j] < 0 || ids[j] >= E) return OR_EINVAL;
+  double* xv = (double*)malloc(sizeof(double) * H);
+  double* g = (double*)malloc(sizeof(double) * I);
+  double* u = (double*)malloc(sizeof(double) * I);
+  int rc = OR_OK;
+  for (int e = 0; e < E && rc == OR_OK; e++) {
+    int used = 0;
+    for (int64_t j = 0; j < (int64_t)T * K; j++) used |= ids[j] == e;
+    if (!used) continue;
+    if (!expert_gate[e] || !expert_up[e]) { rc = OR_EINVAL; break; }
+    double* Wg = decode_matrix(gate_qt, expert_gate[e], I, H, grid);
+    double* Wu = decode_matrix(up_qt, expert_up[e], I, H, grid);
+    for (int t = 0; t < T; t++)
+      for (int k = 0; k < K; k++) {
+        if (ids[(int64_t)t * K + k] != e) continue;
+        for (int c = 0; c < H; c++) {
+          xv[c] = load_elem((const char*)x + (int64_t)t * H * xsz, xdt, c);
+          gu[(int64_t)e * H + c] += xv[c] * xv[c];
+        }
+        matvec(Wg, xv, I, H, g);
+        matvec(Wu, xv, I, H, u);
+        double w = (double)wts[(int64_t)t * K + k];
+        for (int i = 0; i < I; i++) {
+          double v = w * (silu(g[i]) * u[i]);
+          dn[(int64_t)e * I + i] += v * v;
+        }
+      }
+    free(Wg);
+    free(Wu);
+  }
+  free(xv);
+  free(g);
+  free(u);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ */
 /* RMSNorm before the MoE block, residual add after (FLOW token flow)  */
 /* ------------------------------------------------------------------ */
 

@@ -463,3 +463,75 @@ def test_sizes_match_pages():
     assert abs(per_tok_layer / 1e6 - 42) < 1
     assert 43 * per_tok_layer == 1_826_095_104      # "about 1.8 GB per token"
     assert 256 * w.expert_bytes() == 1_811_939_328  # "about 1.8 GB per layer"
+
+
+# --------------------------------------------------------------------------
+# importance statistics (imatrix): DS4C2 sec. 5 and 7
+# --------------------------------------------------------------------------
+def q80_identity(n):
+    """Q8_0 matrix [n][n] = identity (one 32-value block per row, d = 1.0)."""
+    assert n == 32
+    rows = np.zeros((n, 34), np.uint8)
+    for i in range(n):
+        rows[i, 0:2] = np.array([0x3C00], np.uint16).view(np.uint8)
+        rows[i, 2 + i] = 1
+    return rows.ravel()
+
+
+def test_imatrix_gate_up_hand_values():
+    # x[t][c] = t + 1; pairs (t, e): (0,0) (0,1) (1,1) (1,2) (2,0) (2,2)
+    H = I = 32
+    x = np.array([[t + 1.0] * H for t in range(3)], np.float32)
+    ids = np.array([[0, 1], [1, 2], [0, 2]], np.int32)
+    wts = np.full((3, 2), 0.75, np.float32)
+    blk = ds4gen.blocks(ds4gen.Q8_0, 5, 1, 0, I * H // 32)
+    mats = {e: (blk, blk) for e in range(3)}
+    gu, _ = oracle.imatrix(x, "f32", ids, wts, mats, (ds4gen.Q8_0, ds4gen.Q8_0), H, I, 4)
+    np.testing.assert_array_equal(gu[0], 10.0)   # 1 + 9
+    np.testing.assert_array_equal(gu[1], 5.0)    # 1 + 4
+    np.testing.assert_array_equal(gu[2], 13.0)   # 4 + 9
+    np.testing.assert_array_equal(gu[3], 0.0)    # never selected
+
+
+def test_imatrix_down_is_square_of_weighted_swiglu_row():
+    # with W_down = identity, E(x) = h, so a single pair's FFN output is w*h:
+    # the down statistic of an expert is the sum of its pairs' squared outputs
+    H = I = 32
+    ident = q80_identity(32)
+    mats = {e: (ds4gen.blocks(ds4gen.Q8_0, 7, 2 * e, 0, 32),
+                ds4gen.blocks(ds4gen.Q8_0, 7, 2 * e + 1, 0, 32), ident) for e in range(2)}
+    qts = (ds4gen.Q8_0, ds4gen.Q8_0, ds4gen.Q8_0)
+    x = np.random.default_rng(3).normal(size=(3, H)).astype(np.float32)
+    ids = np.array([[0, 1], [1, 0], [1, 0]], np.int32)
+    wts = np.array([[1.25, 0.25], [0.5, 1.0], [0.75, 0.75]], np.float32)
+    _, dn = oracle.imatrix(x, "f32", ids, wts, mats, qts, H, I, 2)
+    want = np.zeros((2, I))
+    for t in range(3):
+        for k in range(2):
+            e = int(ids[t, k])
+            y = oracle.moe_ffn(x[t:t + 1], "f32", ids[t:t + 1, k:k + 1], wts[t:t + 1, k:k + 1],
+                               {e: mats[e]}, qts, H, I, 2)
+            want[e] += y[0].astype(np.float64) ** 2
+    np.testing.assert_allclose(dn, want, rtol=2e-7)
+
+
+def test_imatrix_invariants():
+    # every token feeds K experts: sum over experts of the gate/up statistic is
+    # K * sum_t x^2; doubling the routing weights multiplies the down statistic
+    # by exactly 4; the expert bytes do not enter the gate/up statistic
+    w = ds4gen.WORKLOADS[0]
+    mats = tiny_experts(w, w.E)
+    x = ds4gen.activations(w)
+    ids = np.array([[0, 5], [15, 3], [7, 8], [5, 0]], np.int32)
+    wts = np.array([[1.0, 0.5], [0.75, 0.75], [1.25, 0.25], [0.5, 1.0]], np.float32)
+    qts = (w.gate_qt, w.up_qt, w.down_qt)
+    gu, dn = oracle.imatrix(x, "f32", ids, wts, mats, qts, w.H, w.I, w.E)
+    x64 = x.astype(np.float64)
+    np.testing.assert_allclose(gu.sum(0), ids.shape[1] * (x64 ** 2).sum(0), rtol=1e-15)
+    gu2, dn2 = oracle.imatrix(x, "f32", ids, 2 * wts, mats, qts, w.H, w.I, w.E)
+    np.testing.assert_array_equal(gu2, gu)
+    np.testing.assert_array_equal(dn2, 4 * dn)
+    other = {e: tiny_experts(w, w.E)[(e + 1) % w.E] for e in range(w.E)}
+    gu3, dn3 = oracle.imatrix(x, "f32", ids, wts, other, qts, w.H, w.I, w.E)
+    np.testing.assert_array_equal(gu3, gu)
+    assert not np.array_equal(dn3, dn)
