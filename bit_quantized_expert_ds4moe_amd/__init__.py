@@ -18,7 +18,8 @@ Q2_K, IQ2_XXS, Q8_0 = 0, 1, 2
 FAULT_BAD_ID, FAULT_BAD_TOKEN, FAULT_BAD_TABLE, FAULT_UNCERTIFIED, FAULT_F16_RANGE = 1, 2, 4, 8, 16
 
 EXPORTED = ("ds4moe_workspace_size", "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn",
-            "ds4moe_layer", "ds4moe_profile_events", "ds4moe_check", "ds4moe_status_string")
+            "ds4moe_expert_ffn_imatrix", "ds4moe_layer", "ds4moe_profile_events", "ds4moe_check",
+            "ds4moe_status_string")
 K_ROUTE, K_GATEUP, K_DOWN, K_PERMUTE, K_OTHER = range(5)
 
 
@@ -72,6 +73,10 @@ def lib():
                                         ctypes.POINTER(Experts), vp, i32, i32, vp, vp, vp, vp, vp,
                                         sz, vp]
         L.ds4moe_expert_ffn.restype = i32
+        L.ds4moe_expert_ffn_imatrix.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Experts),
+                                                ctypes.POINTER(Experts), vp, i32, i32, vp, vp, vp,
+                                                vp, vp, vp, sz, vp]
+        L.ds4moe_expert_ffn_imatrix.restype = i32
         L.ds4moe_layer.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(LayerDesc), vp, i32, vp,
                                    vp, vp, i32, vp, vp, vp, vp, sz, vp]
         L.ds4moe_layer.restype = i32
@@ -134,6 +139,17 @@ def expert_ffn(shp, routed, shared, x, x_dtype, n_tok, ids, weights, out, perm_d
     _ok(lib().ds4moe_expert_ffn(ctypes.byref(shp), ctypes.byref(routed), sh, x, x_dtype, n_tok,
                                 ids, weights, out, perm_dbg, ws, ws_bytes, stream),
         "ds4moe_expert_ffn")
+
+
+def expert_ffn_imatrix(shp, routed, shared, x, x_dtype, n_tok, ids, weights, out, imx_gateup,
+                       imx_down, ws, ws_bytes, stream=0):
+    """expert_ffn plus the importance statistics, accumulated into imx_gateup
+    (fp32 [E][hidden]) and imx_down (fp32 [E][inter]), device pointers."""
+    sh = ctypes.byref(shared) if shared is not None else None
+    _ok(lib().ds4moe_expert_ffn_imatrix(ctypes.byref(shp), ctypes.byref(routed), sh, x, x_dtype,
+                                        n_tok, ids, weights, out, imx_gateup, imx_down, ws,
+                                        ws_bytes, stream),
+        "ds4moe_expert_ffn_imatrix")
 
 
 def layer(shp, desc, x, x_dtype, residual, out, token_ids, n_tok, ids_dbg, w_dbg, xn_dbg, ws,

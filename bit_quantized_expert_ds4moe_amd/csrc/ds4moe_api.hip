@@ -307,16 +307,62 @@ ds4moe_status permute_dbg(const ds4moe_shape& s, int32_t T, const int32_t* ids, 
   return DS4MOE_OK;
 }
 
+// Importance statistics (ds4moe_expert_ffn_imatrix): launched by do_ffn once
+// the routed SwiGLU rows exist and before anything reuses their memory.
+struct ImxOut {
+  float* gu;
+  float* dn;
+};
+
+ds4moe_status launch_imatrix(const ds4moe_shape& s, const ImxOut& o, const void* x, int32_t x_dt,
+                             int32_t T, const int32_t* ids, const float* wts, const float* h32,
+                             int h_stride, const uint16_t* hh, const uint16_t* hl, bool have_perm,
+                             void* ws, const Layout& L, hipStream_t st) {
+  const int E = s.n_expert, TK = T * s.top_k;
+  int32_t* counts = at<int32_t>(ws, L.perm);
+  int32_t* offsets = counts + E;
+  int32_t* perm = offsets + E + 1;
+  int32_t* inv = perm + TK;
+  ProfScope prof(DS4MOE_K_OTHER, st);
+  if (!have_perm) {
+    ds4moe_status rc = launch_permute(ids, TK, E, counts, offsets, perm, inv,
+                                      at<uint32_t>(ws, L.status), st);
+    if (rc != DS4MOE_OK) return rc;
+  }
+  ImxArgs a{};
+  a.x = x;
+  a.x_dt = x_dt;
+  a.H = s.hidden;
+  a.I = s.inter;
+  a.K = s.top_k;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.wts = wts;
+  a.h32 = h32;
+  a.h_stride = h_stride;
+  a.hh = hh;
+  a.hl = hl;
+  a.gu = o.gu;
+  a.dn = o.dn;
+  const int cmax = s.hidden > s.inter ? s.hidden : s.inter;
+  launch_k(k_imatrix, dim3(E, (cmax + 255) / 256), dim3(256), 0, st, a);
+  return launched();
+}
+
 ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_experts* sh,
                      const void* x, int32_t x_dt, int32_t T, const int32_t* ids, const float* wts,
                      float* out, float* residual, int32_t* perm_dbg, void* ws, const Layout& L,
-                     hipStream_t st) {
+                     hipStream_t st, const ImxOut* imx = nullptr) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   const bool b1 = fast_b1(s, ex, x, x_dt, T) && (!sh || grouped_eligible(s, ex, sh, x, x_dt, T));
   if (b1) {
     ds4moe_status rc = launch_b1(s, ex, x, T, ids, nullptr, nullptr, wts, out, residual, ws, L, st);
     if (rc == DS4MOE_OK && perm_dbg)  // the few-token path needs no permutation: make it for the caller
       rc = permute_dbg(s, T, ids, perm_dbg, ws, L, st);
+    // h: fp32 [T][6][I] by pair; the shared expert's rows below reuse its memory
+    if (rc == DS4MOE_OK && imx)
+      rc = launch_imatrix(s, *imx, x, x_dt, T, ids, wts, at<float>(ws, L.h), s.inter, nullptr,
+                          nullptr, false, ws, L, st);
     if (rc != DS4MOE_OK || !sh) return rc;
   }
   if (b1 || (T > 1 && grouped_eligible(s, ex, sh, x, x_dt, T))) {
@@ -422,6 +468,10 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
         launch_k(k_grouped_down, dim3(s.hidden / kNT, mi, g.ksplit_d), dim3(256), 0, st, g);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
+    if (imx && !b1 &&
+        (rc = launch_imatrix(s, *imx, x, x_dt, T, ids, wts, nullptr, 0, g.hh, g.hl, true, ws, L,
+                             st)) != DS4MOE_OK)
+      return rc;
     {
       ProfScope prof(DS4MOE_K_OTHER, st, !b1);
       const size_t n = (size_t)T * s.hidden;
@@ -491,6 +541,9 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     launch_k(k_generic_down, dim3((s.hidden + 3) / 4, np), dim3(256), 0, st, a);
   }
   rc = launched();
+  if (rc == DS4MOE_OK && imx)  // h: fp32 [pairs][max(I, sh_I)] by pair
+    rc = launch_imatrix(s, *imx, x, x_dt, T, ids, wts, a.h, imax, nullptr, nullptr, false, ws, L,
+                        st);
   if (rc != DS4MOE_OK) return rc;
   size_t n = (size_t)T * s.hidden;
   {
@@ -564,6 +617,28 @@ DS4_EXPORT ds4moe_status ds4moe_expert_ffn(const ds4moe_shape* shape,
   if ((int64_t)n_tok * shape->top_k > 32768) return DS4MOE_EUNSUPPORTED;
   return do_ffn(*shape, *routed, shared, x, x_dtype, n_tok, expert_ids, weights, out, nullptr,
                 perm_dbg, ws, L, stream);
+}
+
+DS4_EXPORT ds4moe_status ds4moe_expert_ffn_imatrix(const ds4moe_shape* shape,
+                                                   const ds4moe_experts* routed,
+                                                   const ds4moe_experts* shared, const void* x,
+                                                   int32_t x_dtype, int32_t n_tok,
+                                                   const int32_t* expert_ids, const float* weights,
+                                                   float* out, float* imx_gateup, float* imx_down,
+                                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!shape_ok(shape) || !experts_ok(routed, shape->hidden) || !x || !x_dtype_ok(x_dtype) ||
+      !expert_ids || !weights || !out || !imx_gateup || !imx_down || !ws || n_tok < 0)
+    return DS4MOE_EINVAL;
+  if (routed->inter != shape->inter) return DS4MOE_EINVAL;
+  if (shared && (!experts_ok(shared, shape->hidden) || shared->inter > shape->inter))
+    return DS4MOE_EINVAL;
+  if (n_tok == 0) return DS4MOE_OK;
+  Layout L = layout_for(*shape, n_tok);
+  if (ws_bytes < L.total) return DS4MOE_EWORKSPACE;
+  if ((int64_t)n_tok * shape->top_k > 32768) return DS4MOE_EUNSUPPORTED;
+  const ImxOut imx{imx_gateup, imx_down};
+  return do_ffn(*shape, *routed, shared, x, x_dtype, n_tok, expert_ids, weights, out, nullptr,
+                nullptr, ws, L, stream, &imx);
 }
 
 DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_layer_desc* desc,

@@ -1253,6 +1253,60 @@ __global__ void k_grouped_combine(const float* y, const int32_t* inv, const floa
   else out[idx] = acc;
 }
 
+// Importance statistics of the routed experts' inputs (DS4C2 =
+// qiita.com/yoshiyakato/items/4678be0e7860ddb444ec, sections 5 and 7): per
+// expert and input column, the sum over the expert's pairs of x^2 (gate/up
+// input) and of (w h)^2 (down input: the SwiGLU row after the routing
+// weight), accumulated into fp32 [E][H] and [E][I].  Grid (E, ceil(max(H,
+// I)/256)), 256 threads: thread c of column block b owns column 256b + c of
+// both sums, walks the expert's pairs in sorted order (token, then slot) in
+// fp64 and adds once, so results do not depend on the launch.  h: fp32 rows
+// indexed by pair (h_stride apart), or binary16 high + low parts indexed by
+// sorted row (the grouped path).
+struct ImxArgs {
+  const void* x;
+  int x_dt, H, I, K;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const float* wts;
+  const float* h32;
+  int h_stride;
+  const uint16_t* hh;
+  const uint16_t* hl;
+  float* gu;
+  float* dn;
+};
+
+__global__ __launch_bounds__(256) void k_imatrix(ImxArgs a) {
+  const int e = blockIdx.x, c = blockIdx.y * 256 + threadIdx.x;
+  const int r0 = a.offsets[e], r1 = a.offsets[e + 1];
+  if (r0 == r1) return;
+  const bool cg = c < a.H, cd = c < a.I;
+  double sg = 0.0, sd = 0.0;
+  for (int r = r0; r < r1; r++) {
+    const int p = a.perm[r], t = p / a.K;
+    if (cg) {
+      const size_t xi = (size_t)t * a.H + c;
+      const double v = a.x_dt == DS4MOE_F32 ? (double)((const float*)a.x)[xi]
+                                            : (double)bf16_bits_to_f32(((const uint16_t*)a.x)[xi]);
+      sg += v * v;
+    }
+    if (cd) {
+      double hv;
+      if (a.hh) {
+        const size_t hi = (size_t)r * a.I + c;
+        hv = (double)f16_bits_to_f32(a.hh[hi]) + (double)f16_bits_to_f32(a.hl[hi]);
+      } else {
+        hv = (double)a.h32[(size_t)p * a.h_stride + c];
+      }
+      const double v = (double)a.wts[p] * hv;
+      sd += v * v;
+    }
+  }
+  if (cg) a.gu[(size_t)e * a.H + c] += (float)sg;
+  if (cd) a.dn[(size_t)e * a.I + c] += (float)sd;
+}
+
 // The grouped kernels need bf16 x, 256-multiple shapes and formats they know
 // (any token count: at one token they run the shared expert after the
 // streaming matvec kernels).

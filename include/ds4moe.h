@@ -149,9 +149,10 @@ ds4moe_status ds4moe_permute(const ds4moe_shape* shape, const int32_t* expert_id
  * Expert FFN and weighted combine (FLOW "MoE FFN" section):
  *   out[t] = sum_k weights[t][k] * E_{expert_ids[t][k]}(x[t])  + shared(x[t])
  * x: [n_tok][hidden] BF16 or F32; out: fp32 [n_tok][hidden].  `shared` may
- * be NULL.  Accumulation is fp32 (decode paths) or bf16 x bf16 MFMA with
- * fp32 accumulation (prefill path, n_tok > 64).  The permutation used for
- * n_tok > 1 may be captured: perm_dbg (nullable) receives
+ * be NULL.  Accumulation is fp32: dot products of exact products (decode
+ * paths, up to 13 tokens with the V4-Flash shape and formats) or MFMAs on
+ * exact binary16/bf16 operands (grouped path, more tokens).  The permutation
+ * used for n_tok > 1 may be captured: perm_dbg (nullable) receives
  * offsets[n_expert+1], perm[n_tok*top_k], inv[n_tok*top_k] (int32).
  */
 ds4moe_status ds4moe_expert_ffn(const ds4moe_shape* shape, const ds4moe_experts* routed,
@@ -159,6 +160,32 @@ ds4moe_status ds4moe_expert_ffn(const ds4moe_shape* shape, const ds4moe_experts*
                                 int32_t n_tok, const int32_t* expert_ids, const float* weights,
                                 float* out, int32_t* perm_dbg, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/*
+ * ds4moe_expert_ffn, plus the importance statistics of the routed experts'
+ * inputs ("imatrix", DS4C2 = qiita.com/yoshiyakato/items/4678be0e7860ddb444ec,
+ * sections 5 and 7: activation statistics per input column, one entry of
+ * n_expert * n_columns values per expert tensor).  For every pair (t, k)
+ * with e = expert_ids[t][k], in sorted pair order:
+ *   imx_gateup[e][c] += x[t][c]^2                   c < hidden
+ *       (the gate and up input; x is the FFN-normalised activation)
+ *   imx_down[e][i]   += (weights[t][k] * h[t][k][i])^2   i < inter
+ *       (the down input: the pair's SwiGLU row after its routing weight)
+ * imx_gateup: fp32 [n_expert][hidden], imx_down: fp32 [n_expert][inter],
+ * device, caller-owned, accumulated into (zero them before a calibration
+ * run); each call adds its own sums (fp64 inside the call, one fp32 rounding
+ * per element per call), so results do not depend on the launch shape.  h is
+ * the SwiGLU row the FFN computed (fp32, or binary16 high + low parts on the
+ * grouped path, relative error < 2^-21).  The shared expert has no entry.
+ * Same arguments, errors and workspace as ds4moe_expert_ffn (no perm_dbg);
+ * both statistics pointers are required.
+ */
+ds4moe_status ds4moe_expert_ffn_imatrix(const ds4moe_shape* shape, const ds4moe_experts* routed,
+                                        const ds4moe_experts* shared, const void* x,
+                                        int32_t x_dtype, int32_t n_tok, const int32_t* expert_ids,
+                                        const float* weights, float* out, float* imx_gateup,
+                                        float* imx_down, void* ws, size_t ws_bytes,
+                                        hipStream_t stream);
 
 /*
  * A whole MoE layer.  If desc->norm_w is set: xn = RMSNorm(residual)

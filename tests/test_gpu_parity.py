@@ -466,3 +466,57 @@ def test_grouped_pipelined_kernels_all_outputs():
 def test_grouped_pipelined_kernels_zero_scales():
     say("grouped pipelined kernels, d = 0 blocks")
     _grouped_fast_case(True)
+
+
+# --------------------------------------------------------------------------
+# importance statistics (ds4moe_expert_ffn_imatrix)
+# --------------------------------------------------------------------------
+def _imatrix_case(w, T, ids=None, wts=None, lt=None):
+    from ds4gen.device import make_layer, host_experts
+    lt = make_layer(w, 0) if lt is None else lt
+    x = g.activations(w, n_tok=T)
+    if ids is None:
+        ids, wts, _, _ = oracle.route(x, x_fmt(w), g.router_weight(w, 0), w.router_fmt,
+                                      g.router_bias(w, 0), w.K)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, T)
+    out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    gu = torch.zeros((w.E, w.H), dtype=torch.float32, device="cuda")
+    dn = torch.zeros((w.E, w.I), dtype=torch.float32, device="cuda")
+    xd, idd, wd = dev(x), dev(ids), dev(wts)
+    for rep in range(2):  # the second call adds the same sums again
+        ds4.expert_ffn_imatrix(shp, experts_of(lt, w), shared_of(lt, w), ptr(xd), x_dtype(w), T,
+                               ptr(idd), ptr(wd), ptr(out), ptr(gu), ptr(dn), ptr(ws), nb, stream())
+        check_clean(ws)
+        if rep == 0:
+            gu1, dn1 = gu.cpu().numpy().copy(), dn.cpu().numpy().copy()
+    gu2, dn2 = gu.cpu().numpy(), dn.cpu().numpy()
+    np.testing.assert_array_equal(gu2, 2 * gu1)
+    np.testing.assert_array_equal(dn2, 2 * dn1)
+    hx = host_experts(w, 0, np.unique(ids))
+    want_gu, want_dn = oracle.imatrix(x, x_fmt(w), ids, wts, hx, (w.gate_qt, w.up_qt), w.H, w.I,
+                                      w.E, grid=g.grid(w.seed))
+    np.testing.assert_allclose(gu1, want_gu, rtol=2e-7, atol=0)
+    err = np.abs(dn1 - want_dn).max() / np.sqrt((want_dn ** 2).mean())
+    say("  imatrix %s T=%d: down max|err|/rms = %g" % (w.name, T, err))
+    assert err <= TOL_FP32
+    assert (want_dn[np.unique(ids)] > 0).all() and not want_dn[np.setdiff1d(np.arange(w.E), ids)].any()
+    return lt
+
+
+def test_imatrix_decode_paths():
+    # matvec kernels (4 tokens of config 1), the same with a Q8_0 shared expert
+    # (config 2, 8 tokens: the shared expert's rows reuse the routed rows'
+    # memory after the statistics), the generic kernels (config 0, f32 x)
+    say("imatrix decode")
+    _imatrix_case(g.WORKLOADS[1], 4)
+    _imatrix_case(g.WORKLOADS[2], 8)
+    _imatrix_case(g.WORKLOADS[0], 4)
+
+
+def test_imatrix_grouped_path():
+    say("imatrix grouped")
+    w = g.Workload("grouped-fast", 13, 160, 512, 512, 16, 4, g.IQ2_XXS, g.IQ2_XXS, g.Q2_K,
+                   "bf16", "f16")
+    ids, wts = g.zipf_routing(13, w.T, w.E, w.K)
+    _imatrix_case(w, w.T, ids, wts)
