@@ -348,9 +348,18 @@ def bench_batched(args, which):
         ids, wts = to_dev(ids_h), to_dev(wts_h)
         touched = int(np.unique(ids_h).size)
 
-        def step(i, st):
-            ds4.expert_ffn(shp, ex, None, x.data_ptr(), ds4.BF16, T, ids.data_ptr(), wts.data_ptr(),
-                           out.data_ptr(), None, ws.data_ptr(), nb, st)
+        if args.imatrix:  # importance statistics collected in the same call
+            imx_gu = torch.zeros((w.E, w.H), dtype=torch.float32, device="cuda")
+            imx_dn = torch.zeros((w.E, w.I), dtype=torch.float32, device="cuda")
+
+            def step(i, st):
+                ds4.expert_ffn_imatrix(shp, ex, None, x.data_ptr(), ds4.BF16, T, ids.data_ptr(),
+                                       wts.data_ptr(), out.data_ptr(), imx_gu.data_ptr(),
+                                       imx_dn.data_ptr(), ws.data_ptr(), nb, st)
+        else:
+            def step(i, st):
+                ds4.expert_ffn(shp, ex, None, x.data_ptr(), ds4.BF16, T, ids.data_ptr(),
+                               wts.data_ptr(), out.data_ptr(), None, ws.data_ptr(), nb, st)
     else:
         desc = ds4.layer_desc(ds4.router(w=lt.router_w.data_ptr(), w_dtype=ds4.F16,
                                          bias=lt.bias.data_ptr()), ex, shared=sh)
@@ -433,7 +442,8 @@ def bench_batched(args, which):
         "config": {"workload": w.name, "tokens_per_step": T, "hidden": w.H, "inter": w.I,
                    "experts": w.E, "top_k": w.K, "shared_q8_0": bool(w.shared),
                    "experts_touched_per_step": touched,
-                   "routing": "given Zipf(1.1)" if prefill else "learned router"},
+                   "routing": "given Zipf(1.1)" if prefill else "learned router",
+                   "imatrix": bool(prefill and args.imatrix)},
         "expert_gbs": round(step_bytes / sec / 1e9, 1),
         "expert_hbm_frac": round(step_bytes / sec / 1e9 / PEAK_HBM_GBS, 4),
         "mfma_tflops": round(flops / sec / 1e12, 2),
@@ -632,6 +642,8 @@ def main():
     ap.add_argument("--sleep-cycles", type=int, default=200_000_000,
                     help="GPU spin before the per-kernel event pass")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--imatrix", action="store_true",
+                    help="prefill-512: collect the importance statistics in the same call")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB, so that hardware "
                          "byte counters can be scaled against a transfer of known size")

@@ -345,7 +345,12 @@ ds4moe_status launch_imatrix(const ds4moe_shape& s, const ImxOut& o, const void*
   a.gu = o.gu;
   a.dn = o.dn;
   const int cmax = s.hidden > s.inter ? s.hidden : s.inter;
-  launch_k(k_imatrix, dim3(E, (cmax + 255) / 256), dim3(256), 0, st, a);
+  const dim3 grid(E, (cmax + 63) / 64), block(256);
+  const bool xf32 = x_dt == DS4MOE_F32;
+  if (xf32 && hh) launch_k(k_imatrix<true, true>, grid, block, 0, st, a);
+  else if (xf32) launch_k(k_imatrix<true, false>, grid, block, 0, st, a);
+  else if (hh) launch_k(k_imatrix<false, true>, grid, block, 0, st, a);
+  else launch_k(k_imatrix<false, false>, grid, block, 0, st, a);
   return launched();
 }
 

@@ -1258,11 +1258,13 @@ __global__ void k_grouped_combine(const float* y, const int32_t* inv, const floa
 // expert and input column, the sum over the expert's pairs of x^2 (gate/up
 // input) and of (w h)^2 (down input: the SwiGLU row after the routing
 // weight), accumulated into fp32 [E][H] and [E][I].  Grid (E, ceil(max(H,
-// I)/256)), 256 threads: thread c of column block b owns column 256b + c of
-// both sums, walks the expert's pairs in sorted order (token, then slot) in
-// fp64 and adds once, so results do not depend on the launch.  h: fp32 rows
-// indexed by pair (h_stride apart), or binary16 high + low parts indexed by
-// sorted row (the grouped path).
+// I)/64)), 256 threads: lane L of wave j owns column 64b + L and sums the
+// expert's pairs j, j+4, j+8, .. of its sorted list in fp64 (sixteen pair
+// ids per vector load, the sixteen pairs' loads issued before their sums);
+// the four wave sums are added in wave order and once into the output, so
+// the result depends only on the call's inputs.  h: fp32 rows indexed by
+// pair (h_stride apart), or binary16 high + low parts indexed by sorted row
+// (the grouped path).
 struct ImxArgs {
   const void* x;
   int x_dt, H, I, K;
@@ -1277,34 +1279,62 @@ struct ImxArgs {
   float* dn;
 };
 
+// XF32: x is fp32 (else bf16); HF16: h as binary16 parts by sorted row
+// (else fp32 by pair).  Branch-free inner loop, so a batch's loads issue
+// together.
+template <bool XF32, bool HF16>
 __global__ __launch_bounds__(256) void k_imatrix(ImxArgs a) {
-  const int e = blockIdx.x, c = blockIdx.y * 256 + threadIdx.x;
-  const int r0 = a.offsets[e], r1 = a.offsets[e + 1];
-  if (r0 == r1) return;
+  __shared__ double part[2][4][64];
+  const int e = blockIdx.x, lane = threadIdx.x & 63;
+  const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = blockIdx.y * 64 + lane;
+  const int r0 = __builtin_amdgcn_readfirstlane(a.offsets[e]);
+  const int n = __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - r0;
+  if (n <= 0) return;
   const bool cg = c < a.H, cd = c < a.I;
+  const int cgc = cg ? c : 0, cdc = cd ? c : 0;  // loads stay in bounds
+  constexpr int U = 16;
   double sg = 0.0, sd = 0.0;
-  for (int r = r0; r < r1; r++) {
-    const int p = a.perm[r], t = p / a.K;
-    if (cg) {
-      const size_t xi = (size_t)t * a.H + c;
-      const double v = a.x_dt == DS4MOE_F32 ? (double)((const float*)a.x)[xi]
-                                            : (double)bf16_bits_to_f32(((const uint16_t*)a.x)[xi]);
-      sg += v * v;
-    }
-    if (cd) {
-      double hv;
-      if (a.hh) {
-        const size_t hi = (size_t)r * a.I + c;
-        hv = (double)f16_bits_to_f32(a.hh[hi]) + (double)f16_bits_to_f32(a.hl[hi]);
+  for (int i0 = j; i0 < n; i0 += 4 * U) {
+    // the batch's pair ids: one vector load (lane u < U), then broadcast
+    const int il = i0 + 4 * (lane & (U - 1));
+    const int pl = a.perm[r0 + (il < n ? il : n - 1)];
+    float xv[U], hv[U], lv[U], wv[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int i = i0 + 4 * u;
+      const int r = r0 + (i < n ? i : n - 1);  // past the end: a repeat, weighted 0
+      const int p = __builtin_amdgcn_readlane(pl, u), t = p / a.K;
+      const size_t xi = (size_t)t * a.H + cgc;
+      if constexpr (XF32) xv[u] = ((const float*)a.x)[xi];
+      else xv[u] = bf16_bits_to_f32(((const uint16_t*)a.x)[xi]);
+      if constexpr (HF16) {
+        const size_t hi = (size_t)r * a.I + cdc;
+        hv[u] = f16_bits_to_f32(a.hh[hi]);
+        lv[u] = f16_bits_to_f32(a.hl[hi]);
       } else {
-        hv = (double)a.h32[(size_t)p * a.h_stride + c];
+        hv[u] = a.h32[(size_t)p * a.h_stride + cdc];
+        lv[u] = 0.0f;
       }
-      const double v = (double)a.wts[p] * hv;
+      wv[u] = i < n ? a.wts[p] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const double x = (double)xv[u];
+      sg += i0 + 4 * u < n ? x * x : 0.0;
+      const double v = (double)wv[u] * ((double)hv[u] + (double)lv[u]);
       sd += v * v;
     }
   }
-  if (cg) a.gu[(size_t)e * a.H + c] += (float)sg;
-  if (cd) a.dn[(size_t)e * a.I + c] += (float)sd;
+  part[0][j][lane] = sg;
+  part[1][j][lane] = sd;
+  __syncthreads();
+  if (j == 0) {
+    const double tg = ((part[0][0][lane] + part[0][1][lane]) + part[0][2][lane]) + part[0][3][lane];
+    const double td = ((part[1][0][lane] + part[1][1][lane]) + part[1][2][lane]) + part[1][3][lane];
+    if (cg) a.gu[(size_t)e * a.H + c] += (float)tg;
+    if (cd) a.dn[(size_t)e * a.I + c] += (float)td;
+  }
 }
 
 // The grouped kernels need bf16 x, 256-multiple shapes and formats they know

@@ -166,15 +166,16 @@ ds4moe_status ds4moe_expert_ffn(const ds4moe_shape* shape, const ds4moe_experts*
  * inputs ("imatrix", DS4C2 = qiita.com/yoshiyakato/items/4678be0e7860ddb444ec,
  * sections 5 and 7: activation statistics per input column, one entry of
  * n_expert * n_columns values per expert tensor).  For every pair (t, k)
- * with e = expert_ids[t][k], in sorted pair order:
+ * with e = expert_ids[t][k]:
  *   imx_gateup[e][c] += x[t][c]^2                   c < hidden
  *       (the gate and up input; x is the FFN-normalised activation)
  *   imx_down[e][i]   += (weights[t][k] * h[t][k][i])^2   i < inter
  *       (the down input: the pair's SwiGLU row after its routing weight)
  * imx_gateup: fp32 [n_expert][hidden], imx_down: fp32 [n_expert][inter],
  * device, caller-owned, accumulated into (zero them before a calibration
- * run); each call adds its own sums (fp64 inside the call, one fp32 rounding
- * per element per call), so results do not depend on the launch shape.  h is
+ * run); each call adds its own sums (fp64 in a fixed order inside the call,
+ * one fp32 rounding per element per call): repeated calls on the same inputs
+ * add bit-identical amounts.  h is
  * the SwiGLU row the FFN computed (fp32, or binary16 high + low parts on the
  * grouped path, relative error < 2^-21).  The shared expert has no entry.
  * Same arguments, errors and workspace as ds4moe_expert_ffn (no perm_dbg);
