@@ -18,9 +18,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROUTER_W, ROUTER_B, GATE, UP, DOWN, SH_GATE, SH_UP, SH_DOWN, GRID, X, TID2EID, NORM, \
     ROUTE, GATES, COMMON, TOKID, RANKPERM = range(1, 18)
 
-Q2_K, IQ2_XXS, Q8_0 = 0, 1, 2
-BLOCK_BYTES = {Q2_K: 84, IQ2_XXS: 66, Q8_0: 34}
-BLOCK_VALUES = {Q2_K: 256, IQ2_XXS: 256, Q8_0: 32}
+Q2_K, IQ2_XXS, Q8_0, Q4_K = 0, 1, 2, 3
+BLOCK_BYTES = {Q2_K: 84, IQ2_XXS: 66, Q8_0: 34, Q4_K: 144}
+BLOCK_VALUES = {Q2_K: 256, IQ2_XXS: 256, Q8_0: 32, Q4_K: 256}
 
 _host = None
 _dev = None

@@ -60,10 +60,11 @@ enum {
 };
 
 /* Block formats the generator can emit (byte sizes per block). */
-enum { DS4GEN_Q2_K = 0, DS4GEN_IQ2_XXS = 1, DS4GEN_Q8_0 = 2 };
+enum { DS4GEN_Q2_K = 0, DS4GEN_IQ2_XXS = 1, DS4GEN_Q8_0 = 2, DS4GEN_Q4_K = 3 };
 #define DS4GEN_Q2K_BYTES 84
 #define DS4GEN_IQ2_BYTES 66
 #define DS4GEN_Q80_BYTES 34
+#define DS4GEN_Q4K_BYTES 144
 
 GEN_HD uint64_t gen_mix64(uint64_t z) {
   z ^= z >> 30;
@@ -188,9 +189,27 @@ GEN_HD void gen_q80_block(uint64_t key, uint64_t blk, uint8_t* out) {
   }
 }
 
+/*
+ * Q4_K-format block `blk` (144 bytes, 256 values): fp16 d ~ U[1e-4,4e-4] at
+ * bytes 0..1, fp16 dmin ~ U[0,2e-4] at 2..3, then 140 uniform random bytes
+ * (the 12 bytes of 6-bit scales and mins, whose 96 bits are all fields, and
+ * the 128 bytes of 4-bit codes).  d is smaller than for Q2_K so that the
+ * weights' magnitude is alike (6-bit scales, 4-bit codes).  Draw indices
+ * 20*blk + 0..19.
+ */
+GEN_HD void gen_q4k_block(uint64_t key, uint64_t blk, uint8_t* out) {
+  uint64_t base = blk * 20ULL;
+  gen_put_u16(out, gen_f16(gen_uniform(gen_draw(key, base), 1e-4, 4e-4)));
+  gen_put_u16(out + 2, gen_f16(gen_uniform(gen_draw(key, base + 1), 0.0, 2e-4)));
+  uint8_t tail[144];
+  for (int j = 0; j < 18; j++) gen_put_u64(tail + 8 * j, gen_draw(key, base + 2 + j));
+  for (int i = 0; i < 140; i++) out[4 + i] = tail[i];
+}
+
 GEN_HD int gen_block_bytes(int qtype) {
   return qtype == DS4GEN_Q2_K ? DS4GEN_Q2K_BYTES
        : qtype == DS4GEN_IQ2_XXS ? DS4GEN_IQ2_BYTES
+       : qtype == DS4GEN_Q4_K ? DS4GEN_Q4K_BYTES
        : DS4GEN_Q80_BYTES;
 }
 
@@ -199,6 +218,7 @@ GEN_HD int gen_block_values(int qtype) { return qtype == DS4GEN_Q8_0 ? 32 : 256;
 GEN_HD void gen_block(int qtype, uint64_t key, uint64_t blk, uint8_t* out) {
   if (qtype == DS4GEN_Q2_K) gen_q2k_block(key, blk, out);
   else if (qtype == DS4GEN_IQ2_XXS) gen_iq2_block(key, blk, out);
+  else if (qtype == DS4GEN_Q4_K) gen_q4k_block(key, blk, out);
   else gen_q80_block(key, blk, out);
 }
 

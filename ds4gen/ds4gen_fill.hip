@@ -12,7 +12,7 @@
 #include "ds4gen.h"
 
 #define FILL_THREADS 256
-#define FILL_MAX_BYTES 84
+#define FILL_MAX_BYTES 144
 
 template <int QT, int BB>
 __global__ __launch_bounds__(FILL_THREADS) void gen_fill_kernel(uint64_t key, uint64_t first,
@@ -53,6 +53,9 @@ extern "C" __attribute__((visibility("default"))) int ds4gen_dev_blocks(
                        dim3(FILL_THREADS), 0, st, key, first, n, o);
   else if (qtype == DS4GEN_Q8_0)
     hipLaunchKernelGGL((gen_fill_kernel<DS4GEN_Q8_0, DS4GEN_Q80_BYTES>), dim3((unsigned)grid),
+                       dim3(FILL_THREADS), 0, st, key, first, n, o);
+  else if (qtype == DS4GEN_Q4_K)
+    hipLaunchKernelGGL((gen_fill_kernel<DS4GEN_Q4_K, DS4GEN_Q4K_BYTES>), dim3((unsigned)grid),
                        dim3(FILL_THREADS), 0, st, key, first, n, o);
   else
     return -1;

@@ -11,7 +11,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 F32, F16, BF16 = 0, 1, 2
-Q2_K, IQ2_XXS, Q8_0 = 0, 1, 2
+Q2_K, IQ2_XXS, Q8_0, Q4_K = 0, 1, 2, 3
 
 _L = None
 
@@ -83,8 +83,8 @@ def round_bf16(v):
 
 def dequant(qt, blocks, grid=None):
     blocks = _c(blocks, np.uint8)
-    bb = {Q2_K: 84, IQ2_XXS: 66, Q8_0: 34}[qt]
-    bv = {Q2_K: 256, IQ2_XXS: 256, Q8_0: 32}[qt]
+    bb = {Q2_K: 84, IQ2_XXS: 66, Q8_0: 34, Q4_K: 144}[qt]
+    bv = {Q2_K: 256, IQ2_XXS: 256, Q8_0: 32, Q4_K: 256}[qt]
     n = blocks.size // bb
     out = np.empty(n * bv, dtype=np.float64)
     g = None if grid is None else _c(grid, np.uint8)

@@ -34,7 +34,7 @@
 #define EXPORT __attribute__((visibility("default")))
 
 enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
-enum { OR_Q2_K = 0, OR_IQ2_XXS = 1, OR_Q8_0 = 2 };
+enum { OR_Q2_K = 0, OR_IQ2_XXS = 1, OR_Q8_0 = 2, OR_Q4_K = 3 };
 enum { OR_OK = 0, OR_EINVAL = -1, OR_EUNCERTAIN = -6 };
 
 /* ------------------------------------------------------------------ */
@@ -154,19 +154,56 @@ static void decode_q80(const uint8_t* b, double* y) {
   for (int i = 0; i < 32; i++) y[i] = d * (double)(int8_t)b[2 + i];
 }
 
-static int block_bytes(int qt) { return qt == OR_Q2_K ? 84 : qt == OR_IQ2_XXS ? 66 : 34; }
+/*
+ * Q4_K, 144 bytes per 256 values.  The pages give the size (DS4C2 sec. 3,
+ * type table: q4_K, 256 values, 144 bytes), say that Q2_K and Q4_K are
+ * affine formats with a scale and a minimum per sub-block of a super-block
+ * (FLOW, quantisation section), and leave the layout to the ggml k-quant
+ * family.  Reading (that family's layout; 2 + 2 + 12 + 128 = 144 bytes):
+ *   bytes 0..1 fp16 d, 2..3 fp16 dmin (LE)
+ *   bytes 4..15 six-bit scale sc_j and min m_j of the 32-value sub-blocks
+ *     j = 0..7:  j < 4:  sc_j = S[j] & 63,  m_j = S[j+4] & 63
+ *                j >= 4: sc_j = (S[j+4] & 15) | (S[j-4] >> 6) << 4
+ *                        m_j  = (S[j+4] >> 4) | (S[j] >> 6) << 4   (S = bytes 4..15)
+ *   bytes 16..143 four-bit codes: byte 16+32c+l holds value 64c+l in its
+ *     low nibble and value 64c+32+l in its high nibble (c < 4, l < 32)
+ *   value i:  y = d * sc_j * q_i - dmin * m_j,   j = i / 32
+ */
+static void decode_q4k(const uint8_t* b, double* y) {
+  double d = or_f16_value(rd_u16(b)), dmin = or_f16_value(rd_u16(b + 2));
+  const uint8_t* S = b + 4;
+  for (int i = 0; i < 256; i++) {
+    int c = i / 64, l = i % 32, hi = (i % 64) / 32, j = i / 32;
+    int byte = b[16 + 32 * c + l];
+    int q = hi ? byte >> 4 : byte & 15;
+    int sc, m;
+    if (j < 4) {
+      sc = S[j] & 63;
+      m = S[j + 4] & 63;
+    } else {
+      sc = (S[j + 4] & 15) | ((S[j - 4] >> 6) << 4);
+      m = (S[j + 4] >> 4) | ((S[j] >> 6) << 4);
+    }
+    y[i] = d * (double)sc * (double)q - dmin * (double)m;
+  }
+}
+
+static int block_bytes(int qt) {
+  return qt == OR_Q2_K ? 84 : qt == OR_IQ2_XXS ? 66 : qt == OR_Q4_K ? 144 : 34;
+}
 static int block_vals(int qt) { return qt == OR_Q8_0 ? 32 : 256; }
 
 /* Decode n consecutive blocks (the row-major flattening of a matrix). */
 EXPORT int or_dequant(int qt, const uint8_t* blocks, int64_t n_blocks, const uint8_t* grid,
                       double* out) {
-  if (qt < 0 || qt > 2 || (qt == OR_IQ2_XXS && !grid)) return OR_EINVAL;
+  if (qt < 0 || qt > 3 || (qt == OR_IQ2_XXS && !grid)) return OR_EINVAL;
   int bb = block_bytes(qt), bv = block_vals(qt);
   for (int64_t i = 0; i < n_blocks; i++) {
     const uint8_t* b = blocks + i * bb;
     double* y = out + i * bv;
     if (qt == OR_Q2_K) decode_q2k(b, y);
     else if (qt == OR_IQ2_XXS) decode_iq2xxs(b, grid, y);
+    else if (qt == OR_Q4_K) decode_q4k(b, y);
     else decode_q80(b, y);
   }
   return OR_OK;

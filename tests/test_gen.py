@@ -6,7 +6,7 @@ import oracle
 
 
 def test_blocks_are_random_access_and_deterministic():
-    for qt in (ds4gen.Q2_K, ds4gen.IQ2_XXS, ds4gen.Q8_0):
+    for qt in (ds4gen.Q2_K, ds4gen.IQ2_XXS, ds4gen.Q8_0, ds4gen.Q4_K):
         a = ds4gen.blocks(qt, 7, 3, 100, 20)
         b = ds4gen.blocks(qt, 7, 3, 110, 5)
         bb = ds4gen.BLOCK_BYTES[qt]
@@ -26,6 +26,13 @@ def test_block_field_ranges():
     q8 = ds4gen.blocks(ds4gen.Q8_0, 1, 6, 0, 2000).reshape(2000, 34)
     codes = q8[:, 2:].view(np.int8)
     assert codes.min() == -127 and codes.max() == 127
+    q4 = ds4gen.blocks(ds4gen.Q4_K, 1, 4, 0, 2000).reshape(2000, 144)
+    d = q4[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
+    dmin = q4[:, 2:4].copy().view(np.float16).astype(np.float64).ravel()
+    assert d.min() >= 1e-4 * (1 - 2 ** -10) and d.max() <= 4e-4 * (1 + 2 ** -10)
+    assert dmin.min() >= 0 and dmin.max() <= 2e-4 * (1 + 2 ** -10)
+    nib = np.concatenate([q4[:, 16:] & 15, q4[:, 16:] >> 4])
+    assert nib.min() == 0 and nib.max() == 15
     g = ds4gen.grid(1)
     assert set(np.unique(g).tolist()) == {8, 25, 43}
 

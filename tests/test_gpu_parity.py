@@ -31,7 +31,7 @@ def dev(a):
 # --------------------------------------------------------------------------
 # generator: device fill == host bytes
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("qt", [g.Q2_K, g.IQ2_XXS, g.Q8_0])
+@pytest.mark.parametrize("qt", [g.Q2_K, g.IQ2_XXS, g.Q8_0, g.Q4_K])
 def test_device_fill_matches_host(qt):
     say("device fill qt", qt)
     n, first = 1000 + 37, 12345

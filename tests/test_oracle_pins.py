@@ -535,3 +535,80 @@ def test_imatrix_invariants():
     gu3, dn3 = oracle.imatrix(x, "f32", ids, wts, other, qts, w.H, w.I, w.E)
     np.testing.assert_array_equal(gu3, gu)
     assert not np.array_equal(dn3, dn)
+
+
+# --------------------------------------------------------------------------
+# Q4_K decode (DS4C2 sec. 3 type table: 256 values in 144 bytes; layout by
+# reading, see oracle/ds4_oracle.c)
+# --------------------------------------------------------------------------
+def q4k_block(d_bits, dmin_bits, sc, mn, codes):
+    """Pack a Q4_K block from its fields (the inverse of the reading)."""
+    b = np.zeros(144, np.uint8)
+    b[0:2] = np.array([d_bits], np.uint16).view(np.uint8)
+    b[2:4] = np.array([dmin_bits], np.uint16).view(np.uint8)
+    S = np.zeros(12, np.int64)
+    for j in range(4):
+        S[j] = sc[j] & 63
+        S[j + 4] = mn[j] & 63
+    for j in range(4, 8):
+        S[j + 4] = (sc[j] & 15) | ((mn[j] & 15) << 4)
+        S[j - 4] |= (sc[j] >> 4) << 6
+        S[j] |= (mn[j] >> 4) << 6
+    b[4:16] = S.astype(np.uint8)
+    for c in range(4):
+        for l in range(32):
+            b[16 + 32 * c + l] = (codes[64 * c + l] & 15) | ((codes[64 * c + 32 + l] & 15) << 4)
+    return b
+
+
+def test_q4k_block_size_matches_page():
+    assert ds4gen.BLOCK_BYTES[ds4gen.Q4_K] == 144 == 2 + 2 + 12 + 128
+    assert ds4gen.BLOCK_VALUES[ds4gen.Q4_K] == 256
+
+
+def test_q4k_literal_block():
+    # every code 15, every scale and min 63, d = 2^-10, dmin = 2^-11:
+    # y = 945 * 2^-10 - 63 * 2^-11 = 0.89208984375 everywhere
+    b = q4k_block(0x1400, 0x1000, [63] * 8, [63] * 8, [15] * 256)
+    assert (b[4:16] == 255).all()
+    np.testing.assert_array_equal(oracle.dequant(oracle.Q4_K, b), 0.89208984375)
+
+
+def test_q4k_six_bit_scales_and_mins():
+    # distinct 6-bit scale/min per sub-block, all codes 1: sub-block j is
+    # d*sc_j - dmin*m_j (the upper four use the split high bits)
+    sc = [1, 2, 45, 63, 20, 33, 48, 17]
+    mn = [0, 5, 62, 31, 37, 16, 63, 50]
+    b = q4k_block(0x3C00, 0x3800, sc, mn, [1] * 256)  # d = 1, dmin = 0.5
+    y = oracle.dequant(oracle.Q4_K, b)
+    for j in range(8):
+        np.testing.assert_array_equal(y[32 * j: 32 * j + 32], sc[j] - 0.5 * mn[j])
+
+
+def test_q4k_code_positions():
+    # a single nonzero code at each position lands on its value index
+    sc, mn = [3] * 8, [0] * 8
+    for i in (0, 31, 32, 63, 64, 100, 191, 200, 255):
+        codes = [0] * 256
+        codes[i] = 9
+        b = q4k_block(0x3C00, 0x0000, sc, mn, codes)
+        want = np.zeros(256)
+        want[i] = 27.0
+        np.testing.assert_array_equal(oracle.dequant(oracle.Q4_K, b), want)
+        # the byte holding value i: low nibble for the first 32 of each 64
+        c, r = divmod(i, 64)
+        assert b[16 + 32 * c + (r % 32)] == (9 if r < 32 else 9 << 4)
+
+
+def test_ffn_q4k_experts_bruteforce():
+    # all three expert matrices in Q4_K (down blocks span a row exactly)
+    w = ds4gen.Workload("t4", 21, 3, 256, 256, 4, 2, ds4gen.Q4_K, ds4gen.Q4_K, ds4gen.Q4_K,
+                        "f32", "f32")
+    mats = tiny_experts(w, w.E)
+    x = ds4gen.activations(w)
+    ids = np.array([[0, 3], [2, 1], [3, 2]], np.int32)
+    wts = np.array([[1.0, 0.5], [0.75, 0.75], [1.25, 0.25]], np.float32)
+    qts = (w.gate_qt, w.up_qt, w.down_qt)
+    got = oracle.moe_ffn(x, "f32", ids, wts, mats, qts, w.H, w.I, w.E)
+    want = brute_ffn(x.astype(np.float64), mats, ids, wts, qts, w.H, w.I)
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-6 * np.abs(want).max())
