@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libds4moe.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EDEVICE, EDATA = 0, -1, -2, -3, -4, -5
 F32, F16, BF16 = 0, 1, 2
-Q2_K, IQ2_XXS, Q8_0 = 0, 1, 2
+Q2_K, IQ2_XXS, Q8_0, Q4_K = 0, 1, 2, 3
 FAULT_BAD_ID, FAULT_BAD_TOKEN, FAULT_BAD_TABLE, FAULT_UNCERTIFIED, FAULT_F16_RANGE = 1, 2, 4, 8, 16
 
 EXPORTED = ("ds4moe_workspace_size", "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn",

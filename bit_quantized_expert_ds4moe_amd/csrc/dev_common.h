@@ -17,9 +17,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kQ2kBytes = 84;
 constexpr int kIq2Bytes = 66;
 constexpr int kQ80Bytes = 34;
+constexpr int kQ4kBytes = 144;
 
 __host__ __device__ inline int block_bytes(int qt) {
-  return qt == DS4MOE_Q2_K ? kQ2kBytes : qt == DS4MOE_IQ2_XXS ? kIq2Bytes : kQ80Bytes;
+  return qt == DS4MOE_Q2_K ? kQ2kBytes : qt == DS4MOE_IQ2_XXS ? kIq2Bytes : qt == DS4MOE_Q4_K ? kQ4kBytes : kQ80Bytes;
 }
 __host__ __device__ inline int block_values(int qt) { return qt == DS4MOE_Q8_0 ? 32 : 256; }
 

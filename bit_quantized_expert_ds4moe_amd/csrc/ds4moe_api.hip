@@ -64,7 +64,9 @@ bool shape_ok(const ds4moe_shape* s) {
          s->top_k <= 64;
 }
 
-bool qtype_ok(int32_t q) { return q == DS4MOE_Q2_K || q == DS4MOE_IQ2_XXS || q == DS4MOE_Q8_0; }
+bool qtype_ok(int32_t q) {
+  return q == DS4MOE_Q2_K || q == DS4MOE_IQ2_XXS || q == DS4MOE_Q8_0 || q == DS4MOE_Q4_K;
+}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 

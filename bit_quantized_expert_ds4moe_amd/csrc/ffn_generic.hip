@@ -5,7 +5,8 @@
 //
 // Method: FLOW = qiita.com/sukimaengineer/items/cd76fec76d49a098abed, section
 // "MoE FFN 部の中身".  Formats: DS4C2 = qiita.com/yoshiyakato/items/
-// 4678be0e7860ddb444ec, sections 3 and 4; FLOW quantisation table (Q8_0).
+// 4678be0e7860ddb444ec, sections 3 and 4; FLOW quantisation table (Q8_0);
+// Q4_K: size from the DS4C2 type table, layout of the k-quant family.
 #include "dev_common.h"
 
 namespace ds4 {
@@ -18,6 +19,18 @@ __device__ inline float decode_at(int qt, const uint8_t* base, size_t n, const u
     return d * (float)(int8_t)b[2 + (n & 31)];
   }
   const int i = (int)(n & 255);
+  if (qt == DS4MOE_Q4_K) {
+    const uint8_t* b = base + (n >> 8) * kQ4kBytes;
+    const int c = i >> 6, l = i & 31, hi = (i >> 5) & 1, j = i >> 5;
+    const int byte = b[16 + 32 * c + l];
+    const int q = hi ? byte >> 4 : byte & 15;
+    const uint8_t* S = b + 4;
+    const int sc = j < 4 ? (S[j] & 63) : ((S[j + 4] & 15) | ((S[j - 4] >> 6) << 4));
+    const int m = j < 4 ? (S[j + 4] & 63) : ((S[j + 4] >> 4) | ((S[j] >> 6) << 4));
+    const float d = f16_bits_to_f32((uint32_t)b[0] | ((uint32_t)b[1] << 8));
+    const float dmin = f16_bits_to_f32((uint32_t)b[2] | ((uint32_t)b[3] << 8));
+    return d * (float)sc * (float)q - dmin * (float)m;
+  }
   if (qt == DS4MOE_Q2_K) {
     const uint8_t* b = base + (n >> 8) * kQ2kBytes;
     int hh = i >> 7, s = (i >> 5) & 3, l = i & 31, j = i >> 4;

@@ -61,8 +61,12 @@ typedef enum { DS4MOE_F32 = 0, DS4MOE_F16 = 1, DS4MOE_BF16 = 2 } ds4moe_dtype;
  *            fp16 d, fp16 dmin;  y = d*sc*q - dmin*m
  *  IQ2_XXS   66 B / 256 values: fp16 d, 8 groups of (4 grid-index bytes,
  *            u32 of 4x7 sign bits + 4-bit scale s); y = d*(2s+1)/8*grid*sign
- *  Q8_0      34 B / 32 values: fp16 d, 32 int8; y = d*c                    */
-typedef enum { DS4MOE_Q2_K = 0, DS4MOE_IQ2_XXS = 1, DS4MOE_Q8_0 = 2 } ds4moe_qtype;
+ *  Q8_0      34 B / 32 values: fp16 d, 32 int8; y = d*c
+ *  Q4_K      144 B / 256 values (size from the DS4C2 type table; layout of
+ *            the k-quant family): fp16 d, fp16 dmin, 12 B of 6-bit scale and
+ *            min per 32-value sub-block, 128 B of 4-bit codes (byte 32c+l:
+ *            values 64c+l low nibble, 64c+32+l high); y = d*sc*q - dmin*m    */
+typedef enum { DS4MOE_Q2_K = 0, DS4MOE_IQ2_XXS = 1, DS4MOE_Q8_0 = 2, DS4MOE_Q4_K = 3 } ds4moe_qtype;
 
 /* Layer shape.  hidden must be a multiple of 256 and inter of 32 (blocks
  * tile the row-major flattening of each matrix, so a block may span rows);
