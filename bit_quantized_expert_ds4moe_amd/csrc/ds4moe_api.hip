@@ -7,6 +7,7 @@
 #include "dev_common.h"
 #include "route.hip"
 #include "ffn_b1.hip"
+#include "ffn_q4k.hip"
 #include "ffn_generic.hip"
 #include "grouped.hip"
 
@@ -246,9 +247,12 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, con
 // a shared expert then runs through the grouped path, split along K).
 bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x, int32_t x_dt,
              int32_t T) {
+  // gate/up: both IQ2_XXS or both Q4_K; down: Q2_K or Q4_K
+  const bool gu = (ex.gate_qtype == DS4MOE_IQ2_XXS && ex.up_qtype == DS4MOE_IQ2_XXS) ||
+                  (ex.gate_qtype == DS4MOE_Q4_K && ex.up_qtype == DS4MOE_Q4_K);
+  const bool dn = ex.down_qtype == DS4MOE_Q2_K || ex.down_qtype == DS4MOE_Q4_K;
   return T >= 1 && T <= kB1MaxTokens && x_dt == DS4MOE_BF16 && s.hidden == kH && s.inter == kI && ex.inter == kI &&
-         s.top_k == 6 && ex.gate_qtype == DS4MOE_IQ2_XXS && ex.up_qtype == DS4MOE_IQ2_XXS &&
-         ex.down_qtype == DS4MOE_Q2_K && aligned(x, 16) && aligned(ex.gate, 16) &&
+         s.top_k == 6 && gu && dn && aligned(x, 16) && aligned(ex.gate, 16) &&
          aligned(ex.up, 16) && aligned(ex.down, 16) && aligned(ex.grid, 8);
 }
 
@@ -275,8 +279,13 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   g.status = status;
   {
     ProfScope prof(DS4MOE_K_GATEUP, st);
-    if (kbuf)
+    const bool q4 = ex.gate_qtype == DS4MOE_Q4_K;
+    if (kbuf && q4)
+      launch_k(k_gateup_q4k_b1<true>, dim3(kGuBlocks, 1), dim3(kGuWaves * 64), 0, st, g);
+    else if (kbuf)
       launch_k(k_gateup_b1<true>, dim3(kGuBlocks, 1), dim3(kGuWaves * 64), 0, st, g);
+    else if (q4)
+      launch_k(k_gateup_q4k_b1<false>, dim3(kGuBlocks, T), dim3(kGuWaves * 64), 0, st, g);
     else
       launch_k(k_gateup_b1<false>, dim3(kGuBlocks, T), dim3(kGuWaves * 64), 0, st, g);
   }
@@ -284,9 +293,9 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   if (rc != DS4MOE_OK) return rc;
   {
     ProfScope prof(DS4MOE_K_DOWN, st);
-    launch_k(k_down_q2k_b1, dim3(kH / kDnBlockRows, kbuf ? 1 : T), dim3(kDnThreads), 0, st, h,
-             (const uint8_t*)ex.down,
-                       kbuf ? ids : ids_in, wts, s.n_expert, out, residual, status);
+    launch_k(ex.down_qtype == DS4MOE_Q4_K ? k_down_q4k_b1 : k_down_q2k_b1,
+             dim3(kH / kDnBlockRows, kbuf ? 1 : T), dim3(kDnThreads), 0, st, h,
+             (const uint8_t*)ex.down, kbuf ? ids : ids_in, wts, s.n_expert, out, residual, status);
   }
   return launched();
 }

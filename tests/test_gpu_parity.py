@@ -278,10 +278,19 @@ def test_ffn_v4_decode_batch_shared_split(T):
 # --------------------------------------------------------------------------
 # whole layer
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("widx", [0, 1])
+Q4_LAYER = g.Workload("v4flash-layer-q4k", 33, 1, 4096, 2048, 256, 6, g.Q4_K, g.Q4_K, g.Q4_K,
+                      "bf16", "f16")
+MIXED_LAYER = g.Workload("v4flash-layer-iq2-q4k-down", 34, 1, 4096, 2048, 256, 6, g.IQ2_XXS,
+                         g.IQ2_XXS, g.Q4_K, "bf16", "f16")
+
+
+@pytest.mark.parametrize("widx", [0, 1, "q4k", "mixed"])
 def test_layer_route_and_ffn(widx):
+    # configs 0 and 1; the config-1 layer with Q4_K experts (the fast path's
+    # Q4_K kernels, selection fused into gate/up) and with IQ2_XXS gate/up and
+    # Q4_K down
     from ds4gen.device import make_layer, host_experts
-    w = g.WORKLOADS[widx]
+    w = {"q4k": Q4_LAYER, "mixed": MIXED_LAYER}.get(widx) or g.WORKLOADS[widx]
     say("layer", w.name)
     T = w.T
     lt = make_layer(w, 0)
