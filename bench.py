@@ -11,8 +11,9 @@ region.  Prints one JSON line.
 
 Other workloads (--workload): decode-b8 (8 correlated tokens + Q8_0 shared
 expert), prefill-512 (Zipf-routed 512-token chunk), stack-43 (43-layer
-decode stack, hash routing in layers 0-2), decode-sweep (the decode-b8 layer
-at 1 to 64 tokens per call).
+decode stack, hash routing in layers 0-2), stack-43-q4k (the same stack with
+Q4_K routed experts in layers 37-42), decode-sweep (the decode-b8 layer at 1
+to 64 tokens per call).
 """
 import argparse
 import json
@@ -184,8 +185,9 @@ def bench_decode_b1(args):
 def stack_descs(ds4, w, layers):
     descs = []
     for l, lt in enumerate(layers):
+        wl = w.at_layer(l)
         ex = ds4.experts(lt.gate.data_ptr(), lt.up.data_ptr(), lt.down.data_ptr(), w.I,
-                         (w.gate_qt, w.up_qt, w.down_qt), grid=lt.grid.data_ptr())
+                         (wl.gate_qt, wl.up_qt, wl.down_qt), grid=lt.grid.data_ptr())
         if l < w.n_hash:
             rt = ds4.router(tid2eid=lt.tid2eid.data_ptr(), vocab=w.vocab)
         else:
@@ -194,9 +196,10 @@ def stack_descs(ds4, w, layers):
     return descs
 
 
-def bench_stack(args):
+def bench_stack(args, mixed=False):
     """43-layer routed-expert stack at batch-1 decode: one step = one token
-    through every layer (RMSNorm -> routing -> experts -> residual add)."""
+    through every layer (RMSNorm -> routing -> experts -> residual add).
+    mixed: the routed experts of layers 37-42 are Q4_K (gate, up and down)."""
     import numpy as np
     import torch
 
@@ -204,7 +207,7 @@ def bench_stack(args):
     import ds4gen as g
     from ds4gen.device import make_stack, step_inputs, to_dev
 
-    w = g.WORKLOADS[4]
+    w = g.WORKLOADS[5 if mixed else 4]
     log("generating %d layers x %d experts on the device" % (w.n_layers, w.E))
     t0 = time.perf_counter()
     layers = make_stack(w, log)
@@ -260,6 +263,7 @@ def bench_stack(args):
                for _ in range(n_ev)] for c in classes}
     handles = {c: [(event_handle(a), event_handle(b)) for a, b in evs[c]] for c in classes}
     used = {c: 0 for c in classes}
+    ev_q4 = {c: [] for c in classes}     # whether each recorded launch is in a Q4_K layer
     # the replays above advanced the step index to n_steps: start over so the
     # eager steps read rows 0 .. n_prof-1 of the step inputs
     assert n_prof <= n_steps
@@ -275,6 +279,7 @@ def bench_stack(args):
                     ds4.profile_events(k, None, None)
                     continue
                 ds4.profile_events(k, handles[c][used[c]][0], handles[c][used[c]][1])
+                ev_q4[c].append(l in w.q4_layers)
                 used[c] += 1
             ds4.layer(shp, d, None, ds4.BF16, resid.data_ptr(), None, tokbuf.data_ptr(), 1, None,
                       None, None, ws.data_ptr(), nb, st)
@@ -282,11 +287,18 @@ def bench_stack(args):
     for k in classes.values():
         ds4.profile_events(k, None, None)
     torch.cuda.synchronize()
-    kern_us = {c: float(np.mean([a.elapsed_time(b) for a, b in evs[c][:used[c]]]) * 1e3)
-               for c in classes if used[c]}
-    log("kernel averages (us):", kern_us)
+    def mean_us(c, q4):
+        t = [a.elapsed_time(b) for (a, b), f in zip(evs[c][:used[c]], ev_q4[c]) if f == q4]
+        return float(np.mean(t)) * 1e3 if t else None
 
-    expert_bytes = w.n_layers * w.K * w.expert_bytes()     # 1,826,095,104 per token
+    kern_us = {c: mean_us(c, False) for c in classes if used[c]}
+    log("kernel averages (us):", kern_us)
+    kern_us_q4 = {c: mean_us(c, True) for c in ("gateup", "down")} if w.q4_layers else None
+    if kern_us_q4:
+        log("kernel averages in the Q4_K layers (us):", kern_us_q4)
+
+    # 1,826,095,104 per token (all q2); 2,080,899,072 with layers 37-42 in Q4_K
+    expert_bytes = w.token_expert_bytes()
     gateup_bytes = w.K * 2 * w.blocks_per_expert["gate"] * g.BLOCK_BYTES[w.gate_qt]
     tok_s = args.steps / (ms * 1e-3)
     gbs = expert_bytes * tok_s / 1e9
@@ -298,7 +310,8 @@ def bench_stack(args):
         "data": "synthetic",
         "config": {"workload": w.name, "layers": w.n_layers, "hash_layers": w.n_hash,
                    "hidden": w.H, "inter": w.I, "experts": w.E, "top_k": w.K,
-                   "resident_expert_bytes": w.n_layers * w.E * w.expert_bytes(),
+                   "q4k_layers": list(w.q4_layers),
+                   "resident_expert_bytes": w.stack_expert_bytes(),
                    "timing": "hip-graph replay of one 43-layer step per token"},
         "expert_gbs": round(gbs, 1), "expert_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
@@ -307,6 +320,19 @@ def bench_stack(args):
                      "traffic": measured_traffic(GATEUP_TRAFFIC),
                      "bytes_per_launch": gateup_bytes},
     }
+    if kern_us_q4:
+        # the Q4_K layers' gate/up kernel, beside the dominant one: 40 IQ2_XXS
+        # layers against 6 Q4_K layers
+        w4 = w.at_layer(w.q4_layers[0])
+        b4 = w4.K * 2 * w4.blocks_per_expert["gate"] * g.BLOCK_BYTES[w4.gate_qt]
+        a4 = b4 / (kern_us_q4["gateup"] * 1e-6) / 1e9
+        n4 = len(w.q4_layers)
+        assert kern_us["gateup"] * (w.n_layers - n4) > kern_us_q4["gateup"] * n4
+        res["kernels_us_q4k_layers"] = {k: round(v, 3) for k, v in kern_us_q4.items()}
+        res["roofline_q4k"] = {"bound": "hbm", "kernel": "k_gateup_q4k_b1", "achieved": round(a4, 1),
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(a4 / PEAK_HBM_GBS, 4), "traffic": None,
+                               "bytes_per_launch": b4}
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_stack(w, args.cpu_sample)
     return res
@@ -560,17 +586,26 @@ def bench_sweep(args):
 
 
 def cpu_baseline_stack(w, n_layers):
-    """The oracle on one decode step through the first n_layers layers
-    (normalisation, routing, experts, residual), scaled to 43 layers."""
+    """The oracle on one decode step through a sample of n_layers layers
+    (normalisation, routing, experts, residual), scaled to 43 layers: the
+    first n_layers layers, or, with Q4_K layers, the first n_layers/2 layers
+    and then the first Q4_K layers, each kind scaled by its own layer count."""
     import ds4gen as g
     import oracle
     from ds4gen.device import host_experts, step_inputs
 
     h0, tok = step_inputs(w, 1)
     resid = h0.copy()
-    t_total = 0.0
     grid = g.grid(w.seed)
-    for l in range(n_layers):
+    if w.q4_layers:
+        n2 = max(1, n_layers // 2)
+        sample = list(range(n2)) + list(w.q4_layers[:max(1, n_layers - n2)])
+    else:
+        sample = list(range(n_layers))
+    t_kind = {}
+    for l in sample:
+        t_total = 0.0
+        wl = w.at_layer(l)
         nw = g.norm_weight(w, l)
         if l < w.n_hash:
             table = g.hash_table(w, l)
@@ -585,16 +620,19 @@ def cpu_baseline_stack(w, n_layers):
         t_total += time.perf_counter() - t0
         mats = host_experts(w, l, ids[0])
         t0 = time.perf_counter()
-        y = oracle.moe_ffn(xn, "bf16", ids, wts, mats, (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I,
-                           w.E, grid=grid)
+        y = oracle.moe_ffn(xn, "bf16", ids, wts, mats, (wl.gate_qt, wl.up_qt, wl.down_qt), w.H,
+                           w.I, w.E, grid=grid)
         resid = oracle.residual_add(resid, y)
         t_total += time.perf_counter() - t0
-    per_token = t_total / n_layers * w.n_layers
+        t_kind.setdefault(l in w.q4_layers, []).append(t_total)
+    n4 = len(w.q4_layers)
+    per_token = sum(sum(t) / len(t) * (n4 if q4 else w.n_layers - n4) for q4, t in t_kind.items())
     return {"value": round(1.0 / per_token, 5), "unit": "tokens/s", "cores": oracle.max_threads(),
             "kind": "oracle",
-            "sample": "one decode step through layers 0..%d (hash and learned routing), "
+            "sample": "one decode step through layers %s (hash and learned routing%s), "
                       "scaled to %d layers; weights regenerated outside the timed region"
-                      % (n_layers - 1, w.n_layers)}
+                      % (",".join(map(str, sample)), ", Q4_K layers timed separately" if n4 else "",
+                         w.n_layers)}
 
 
 def cpu_baseline_decode(w, n_tokens):
@@ -634,7 +672,8 @@ def main():
                     help="timed steps (default 2000 tokens for decode-b1, 256 for stack-43)")
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode-b1",
-                    choices=["decode-b1", "stack-43", "decode-b8", "prefill-512", "decode-sweep"])
+                    choices=["decode-b1", "stack-43", "stack-43-q4k", "decode-b8", "prefill-512",
+                             "decode-sweep"])
     ap.add_argument("--layer-copies", type=int, default=1,
                     help="rotate over this many independently seeded layers")
     ap.add_argument("--cpu-sample", type=int, default=None,
@@ -653,7 +692,7 @@ def main():
               "intermediate rows across GPUs but no multi-GPU run is implemented (--gpus 1).",
               file=sys.stderr)
         sys.exit(2)
-    stack = args.workload == "stack-43"
+    stack = args.workload in ("stack-43", "stack-43-q4k")
     batched = args.workload in ("decode-b8", "prefill-512")
     if args.steps is None:
         args.steps = 256 if stack else 200 if batched else 50 if args.workload == "decode-sweep" else 2000
@@ -674,8 +713,8 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: %d bytes read, %d written" % (n, n))
         del src, dst
-    if args.workload == "stack-43":
-        res = bench_stack(args)
+    if stack:
+        res = bench_stack(args, mixed=args.workload == "stack-43-q4k")
     elif args.workload in ("decode-b8", "prefill-512"):
         res = bench_batched(args, args.workload)
     elif args.workload == "decode-sweep":

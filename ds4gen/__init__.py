@@ -8,7 +8,7 @@ not decode, route or multiply anything.
 import ctypes
 import math
 import os
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 
 import numpy as np
 
@@ -155,6 +155,22 @@ class Workload:
     steps: int = 1
     routing: str = "router"   # "router" | "given-zipf"
     corr: float = 0.0         # token correlation (alpha) for batched decode
+    q4_layers: tuple = ()     # layers whose routed experts are all Q4_K
+
+    def at_layer(self, layer):
+        """The description of one layer of a stack: the same workload, with
+        Q4_K gate/up/down where the layer is one of q4_layers."""
+        if layer in self.q4_layers:
+            return replace(self, gate_qt=Q4_K, up_qt=Q4_K, down_qt=Q4_K, q4_layers=())
+        return self
+
+    def stack_expert_bytes(self):
+        """Bytes of every routed expert of every layer."""
+        return self.E * sum(self.at_layer(l).expert_bytes() for l in range(self.n_layers))
+
+    def token_expert_bytes(self):
+        """Routed-expert bytes one decode token reads through all layers."""
+        return self.K * sum(self.at_layer(l).expert_bytes() for l in range(self.n_layers))
 
     @property
     def blocks_per_expert(self):
@@ -182,6 +198,10 @@ WORKLOADS = [
              Q2_K, "bf16", "f16", routing="given-zipf"),
     Workload("v4flash-43-layer-stack-decode-b1", 4, 1, 4096, 2048, 256, 6, IQ2_XXS, IQ2_XXS,
              Q2_K, "bf16", "f16", n_layers=43, n_hash=3, steps=256),
+    # the same stack with the routed experts of the last six layers in Q4_K
+    Workload("v4flash-43-layer-stack-decode-b1-q4k-37-42", 5, 1, 4096, 2048, 256, 6, IQ2_XXS,
+             IQ2_XXS, Q2_K, "bf16", "f16", n_layers=43, n_hash=3, steps=256,
+             q4_layers=(37, 38, 39, 40, 41, 42)),
 ]
 
 KIND = {"gate": GATE, "up": UP, "down": DOWN, "sh_gate": SH_GATE, "sh_up": SH_UP,
@@ -190,6 +210,7 @@ KIND = {"gate": GATE, "up": UP, "down": DOWN, "sh_gate": SH_GATE, "sh_up": SH_UP
 
 def expert_tensor_blocks(w, layer, which, first_expert, n_experts):
     """Host bytes of experts [first, first+n) of one stacked tensor."""
+    w = w.at_layer(layer)
     qt = w.qtype(which)
     bpe = w.blocks_per_expert[which] if not which.startswith("sh_") else w.I * w.H // 32
     return blocks(qt, w.seed, stream(layer, KIND[which]), first_expert * bpe, n_experts * bpe)

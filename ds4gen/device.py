@@ -19,6 +19,7 @@ def _stream():
 
 def expert_tensor(w, layer, which, n_experts=None):
     """All experts of one stacked tensor, filled on the device."""
+    w = w.at_layer(layer)
     qt = w.qtype(which)
     if which.startswith("sh_"):
         n_experts = 1
@@ -83,16 +84,18 @@ def host_shared(w, layer):
 
 def make_stack(w, log=None):
     """All layers of a decode stack: layers < w.n_hash use hash routing, the
-    rest a learned router; every layer has an RMSNorm weight.  Expert
+    rest a learned router; every layer has an RMSNorm weight; the formats of
+    each layer's experts are w.at_layer(layer)'s.  Expert
     tensors of every layer are distinct (the layer index is part of the
     stream) and generated on the device."""
     grid = to_dev(g.grid(w.seed))
     layers = []
+    done = 0
     for l in range(w.n_layers):
         layers.append(make_layer(w, l, hashed=l < w.n_hash, norm=True, grid=grid))
+        done += w.E * w.at_layer(l).expert_bytes()
         if log and (l % 8 == 7 or l == w.n_layers - 1):
-            log("  generated layer %d / %d (%.1f GB of experts)" %
-                (l + 1, w.n_layers, (l + 1) * w.E * w.expert_bytes() / 1e9))
+            log("  generated layer %d / %d (%.1f GB of experts)" % (l + 1, w.n_layers, done / 1e9))
     return layers
 
 

@@ -154,14 +154,17 @@ GEN_HD void gen_put_u16(uint8_t* p, uint16_t v) {
 /*
  * Q2_K-format block number `blk` of a tensor stream (84 bytes):
  * bytes 0..15 scale|min nibbles, 16..79 two-bit codes (all uniform random),
- * 80..81 fp16 d ~ U[1e-3,1e-2], 82..83 fp16 dmin ~ U[0,5e-3].
+ * 80..81 fp16 d ~ U[1e-3,1e-2], 82..83 fp16 dmin ~ U[3e-3,1.35e-2].
+ * E[dmin] = 1.5 E[d] = E[d] E[code] makes E[dmin*min] = E[d*scale*code]
+ * (scale and min nibbles share a distribution): the decoded weights are
+ * zero-mean, as a quantised weight matrix is, with RMS about 0.09.
  * Draw indices 12*blk + 0..11.
  */
 GEN_HD void gen_q2k_block(uint64_t key, uint64_t blk, uint8_t* out) {
   uint64_t base = blk * 12ULL;
   for (int j = 0; j < 10; j++) gen_put_u64(out + 8 * j, gen_draw(key, base + j));
   gen_put_u16(out + 80, gen_f16(gen_uniform(gen_draw(key, base + 10), 1e-3, 1e-2)));
-  gen_put_u16(out + 82, gen_f16(gen_uniform(gen_draw(key, base + 11), 0.0, 5e-3)));
+  gen_put_u16(out + 82, gen_f16(gen_uniform(gen_draw(key, base + 11), 3e-3, 1.35e-2)));
 }
 
 /*
@@ -191,16 +194,17 @@ GEN_HD void gen_q80_block(uint64_t key, uint64_t blk, uint8_t* out) {
 
 /*
  * Q4_K-format block `blk` (144 bytes, 256 values): fp16 d ~ U[1e-4,4e-4] at
- * bytes 0..1, fp16 dmin ~ U[0,2e-4] at 2..3, then 140 uniform random bytes
- * (the 12 bytes of 6-bit scales and mins, whose 96 bits are all fields, and
- * the 128 bytes of 4-bit codes).  d is smaller than for Q2_K so that the
- * weights' magnitude is alike (6-bit scales, 4-bit codes).  Draw indices
- * 20*blk + 0..19.
+ * bytes 0..1, fp16 dmin ~ U[7.5e-4,3e-3] at 2..3, then 140 uniform random
+ * bytes (the 12 bytes of 6-bit scales and mins, whose 96 bits are all fields,
+ * and the 128 bytes of 4-bit codes).  d is smaller than for Q2_K so that the
+ * weights' magnitude is alike (6-bit scales, 4-bit codes: RMS about 0.074);
+ * E[dmin] = 7.5 E[d] = E[d] E[code] makes the decoded weights zero-mean.
+ * Draw indices 20*blk + 0..19.
  */
 GEN_HD void gen_q4k_block(uint64_t key, uint64_t blk, uint8_t* out) {
   uint64_t base = blk * 20ULL;
   gen_put_u16(out, gen_f16(gen_uniform(gen_draw(key, base), 1e-4, 4e-4)));
-  gen_put_u16(out + 2, gen_f16(gen_uniform(gen_draw(key, base + 1), 0.0, 2e-4)));
+  gen_put_u16(out + 2, gen_f16(gen_uniform(gen_draw(key, base + 1), 7.5e-4, 3e-3)));
   uint8_t tail[144];
   for (int j = 0; j < 18; j++) gen_put_u64(tail + 8 * j, gen_draw(key, base + 2 + j));
   for (int i = 0; i < 140; i++) out[4 + i] = tail[i];

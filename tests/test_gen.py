@@ -19,7 +19,7 @@ def test_block_field_ranges():
     d = q[:, 80:82].copy().view(np.float16).astype(np.float64).ravel()
     dmin = q[:, 82:84].copy().view(np.float16).astype(np.float64).ravel()
     assert d.min() >= 1e-3 * (1 - 2 ** -10) and d.max() <= 1e-2 * (1 + 2 ** -10)
-    assert dmin.min() >= 0 and dmin.max() <= 5e-3 * (1 + 2 ** -10)
+    assert dmin.min() >= 3e-3 * (1 - 2 ** -10) and dmin.max() <= 1.35e-2 * (1 + 2 ** -10)
     iq = ds4gen.blocks(ds4gen.IQ2_XXS, 1, 3, 0, 2000).reshape(2000, 66)
     d = iq[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
     assert d.min() >= 1e-4 * (1 - 2 ** -10) and d.max() <= 2e-3 * (1 + 2 ** -10)
@@ -30,11 +30,23 @@ def test_block_field_ranges():
     d = q4[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
     dmin = q4[:, 2:4].copy().view(np.float16).astype(np.float64).ravel()
     assert d.min() >= 1e-4 * (1 - 2 ** -10) and d.max() <= 4e-4 * (1 + 2 ** -10)
-    assert dmin.min() >= 0 and dmin.max() <= 2e-4 * (1 + 2 ** -10)
+    assert dmin.min() >= 7.5e-4 * (1 - 2 ** -10) and dmin.max() <= 3e-3 * (1 + 2 ** -10)
     nib = np.concatenate([q4[:, 16:] & 15, q4[:, 16:] >> 4])
     assert nib.min() == 0 and nib.max() == 15
     g = ds4gen.grid(1)
     assert set(np.unique(g).tolist()) == {8, 25, 43}
+
+
+def test_decoded_weights_are_zero_mean():
+    # every weight format decodes to a zero-mean matrix of RMS 0.07-0.1, so
+    # that a deep stack keeps its residual stream free of a common direction
+    grid = ds4gen.grid(1)
+    for qt, lo, hi in ((ds4gen.Q2_K, 0.085, 0.1), (ds4gen.IQ2_XXS, 0.07, 0.09),
+                       (ds4gen.Q4_K, 0.065, 0.085)):
+        v = oracle.dequant(qt, ds4gen.blocks(qt, 1, 9, 0, 4000), grid=grid)
+        rms = np.sqrt(np.mean(v * v))
+        assert lo < rms < hi, (qt, rms)
+        assert abs(v.mean()) < 0.02 * rms, (qt, v.mean(), rms)
 
 
 def test_rounding_matches_independent_conversions():

@@ -1,5 +1,6 @@
 """The 43-layer decode stack at full size (about 78 GB of distinct 2-bit
-experts resident in HBM), teacher-forced against the oracle.
+experts resident in HBM; about 89 GB in the mixed form whose layers 37-42 hold
+Q4_K experts), teacher-forced against the oracle.
 
 Routing over a free-running stack cannot be bit-exact between two fp32
 implementations (rounding-order differences grow through the residual and
@@ -19,19 +20,19 @@ from gpu_util import TOL_FP32, check_clean, max_rel_err, ptr, say, stream, works
 
 pytestmark = pytest.mark.gpu
 
-FFN_LAYERS = (0, 2, 3, 21, 42)
+FFN_LAYERS = (0, 2, 3, 21, 36, 37, 42)
 
 
-@pytest.fixture(scope="module")
-def stack():
+@pytest.fixture(scope="module", params=[4, 5], ids=["q2", "q2-q4k-37-42"])
+def stack(request):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import gc
     gc.collect()
     torch.cuda.empty_cache()
     from ds4gen.device import make_stack
-    w = g.WORKLOADS[4]
-    say("generating the 43-layer stack")
+    w = g.WORKLOADS[request.param]
+    say("generating the 43-layer stack", w.name)
     layers = make_stack(w, say)
     torch.cuda.synchronize()
     yield w, layers
@@ -43,8 +44,9 @@ def stack():
 def descs_for(w, layers):
     out = []
     for l, lt in enumerate(layers):
-        ex = ds4.experts(ptr(lt.gate), ptr(lt.up), ptr(lt.down), w.I, (w.gate_qt, w.up_qt, w.down_qt),
-                         grid=ptr(lt.grid))
+        wl = w.at_layer(l)
+        ex = ds4.experts(ptr(lt.gate), ptr(lt.up), ptr(lt.down), w.I,
+                         (wl.gate_qt, wl.up_qt, wl.down_qt), grid=ptr(lt.grid))
         if l < w.n_hash:
             rt = ds4.router(tid2eid=ptr(lt.tid2eid), vocab=w.vocab)
         else:
@@ -57,7 +59,7 @@ def descs_for(w, layers):
 def test_stack_teacher_forced(stack, step):
     from ds4gen.device import host_experts, step_inputs, to_dev
     w, layers = stack
-    say("stack step", step)
+    say("stack", w.name, "step", step)
     h0, tok = step_inputs(w, 1, first_step=step)
     shp = ds4.shape(w.H, w.I, w.E, w.K, 1.5)
     ws, nb = workspace(shp, 1)
@@ -92,8 +94,9 @@ def test_stack_teacher_forced(stack, step):
         np.testing.assert_array_equal(ids, oids, err_msg="layer %d expert ids" % l)
         np.testing.assert_allclose(wts, owts, rtol=2e-6)
         if l in FFN_LAYERS:
+            wl = w.at_layer(l)
             y = oracle.moe_ffn(xn, "bf16", oids, owts, host_experts(w, l, oids[0]),
-                               (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=grid)
+                               (wl.gate_qt, wl.up_qt, wl.down_qt), w.H, w.I, w.E, grid=grid)
             want = oracle.residual_add(r_in, y)
             err = max_rel_err(r_out - r_in, want - r_in)
             say("  layer %2d ids %s  ffn max|err|/rms = %.3g" % (l, ids[0].tolist(), err))

@@ -465,6 +465,31 @@ def test_sizes_match_pages():
     assert 256 * w.expert_bytes() == 1_811_939_328  # "about 1.8 GB per layer"
 
 
+def test_mixed_stack_sizes_match_pages():
+    # FLOW § "パラメータはどこにあるか: 層別の内訳": one layer of routed experts
+    # is about 3.6 GB in Q4_K (about 4.5 bpw) and raising one layer from the
+    # q2 mix to Q4_K costs about 1.8 GB.  DS4C2 §10: the best mixed file takes
+    # the routed experts of layers 37-42 from the Q4 file, about 91 GB against
+    # about 153 GB for all-Q4; BENCH16: the q2 file is 80.76 GiB.  With gate,
+    # up and down all in Q4_K those three sizes agree to within rounding.
+    w = ds4gen.WORKLOADS[5]
+    q2, q4 = w.at_layer(0), w.at_layer(37)
+    assert (q2.gate_qt, q2.up_qt, q2.down_qt) == (ds4gen.IQ2_XXS, ds4gen.IQ2_XXS, ds4gen.Q2_K)
+    assert (q4.gate_qt, q4.up_qt, q4.down_qt) == (ds4gen.Q4_K,) * 3
+    assert [l for l in range(43) if w.at_layer(l).gate_qt == ds4gen.Q4_K] == list(range(37, 43))
+    assert q4.expert_bytes() == 3 * 2048 * 4096 // 256 * 144 == 14_155_776
+    assert abs(q4.expert_bytes() * 8 / (3 * 2048 * 4096) - 4.5) < 1e-12
+    assert 256 * q4.expert_bytes() == 3_623_878_656                 # "about 3.6 GB"
+    step = 256 * (q4.expert_bytes() - q2.expert_bytes())
+    assert step == 1_811_939_328                                     # "about 1.8 GB"
+    q2_file = 80.76 * 2 ** 30
+    assert abs((q2_file + 6 * step) / 2 ** 30 - 91) < 0.5
+    assert abs((q2_file + 43 * step) / 2 ** 30 - 153) < 0.5
+    assert w.stack_expert_bytes() == 37 * 256 * 7_077_888 + 6 * 256 * 14_155_776
+    assert ds4gen.WORKLOADS[4].stack_expert_bytes() == 43 * 256 * 7_077_888
+    assert w.token_expert_bytes() == 37 * 6 * 7_077_888 + 6 * 6 * 14_155_776 == 2_080_899_072
+
+
 # --------------------------------------------------------------------------
 # importance statistics (imatrix): DS4C2 sec. 5 and 7
 # --------------------------------------------------------------------------
