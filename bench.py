@@ -37,8 +37,22 @@ GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "d434befe504f0e6fa5c1c4bf98eea9e3fb35b980afd14375b954ef14696fe2d4",
-    "bytes": 26272728,
+    "sha256": "eccfd29fc254cbdd4edd47399d496d5fe3cbfd392ee8d2bb341caa851d1c7f91",
+    "bytes": 26272900,
+}
+
+
+# The same for the Q4_K gate/up kernel of the mixed stack (summary in
+# profiles/stack43_q4k_hbm_traffic.txt): FETCH_SIZE 27,769.61 KiB x 1.99975
+# (the 256 MiB copy reads 131,088.44 KiB by that counter) + WRITE_SIZE
+# 53.26 KiB, per dispatch.
+Q4K_GATEUP_TRAFFIC = {
+    "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_q4k.hip",
+                "bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
+                "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
+                "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
+    "sha256": "511c7290af6e9f08246069c74ecd3eb6f3e2507811157cd97bbb304f9994b085",
+    "bytes": 56919567,
 }
 
 
@@ -331,7 +345,8 @@ def bench_stack(args, mixed=False):
         res["kernels_us_q4k_layers"] = {k: round(v, 3) for k, v in kern_us_q4.items()}
         res["roofline_q4k"] = {"bound": "hbm", "kernel": "k_gateup_q4k_b1", "achieved": round(a4, 1),
                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                               "frac": round(a4 / PEAK_HBM_GBS, 4), "traffic": None,
+                               "frac": round(a4 / PEAK_HBM_GBS, 4),
+                               "traffic": measured_traffic(Q4K_GATEUP_TRAFFIC),
                                "bytes_per_launch": b4}
     if args.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_stack(w, args.cpu_sample)

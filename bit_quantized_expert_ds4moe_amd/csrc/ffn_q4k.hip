@@ -14,8 +14,9 @@
 //
 // A lane always covers the same 64 consecutive values of a row: chunk c of
 // block b (lane L: b = L >> 2 of the 16 blocks of a 4096-value row, c = L & 3),
-// i.e. the block's 16-byte header and the 32 code bytes at 16 + 32c: three
-// 16-byte loads per row.  The lane's activations are held as 16-bit fixed
+// i.e. the 32 code bytes at 16 + 32c and dword c of the block's 16-byte
+// header; the four lanes of a block exchange their header dwords with DPP
+// quad permutes when the row is used, so a row costs a lane 9 registers.  The lane's activations are held as 16-bit fixed
 // point with one scale (x ~= S n, n = round(32767 x / max|x|), error below
 // 2^-16 of the lane's maximum), paired as the code bytes pair up inside
 // 16-bit lanes: a code dword w holds bytes (4k .. 4k+3), so w & 0x000F000F
@@ -31,15 +32,22 @@ constexpr int kRowQ4kGu = 16 * kQ4kBytes;  // 2304 bytes per gate/up row
 constexpr int kRowQ4kDn = 8 * kQ4kBytes;   // 1152 bytes per down row
 
 struct Q4Seg {
-  uint4 hd;      // d | dmin << 16, then the 12 scale/min bytes
+  uint32_t hw;   // dword c of the header (d | dmin << 16, then the 12 scale/min bytes)
   uint4 c0, c1;  // the 32 code bytes of the lane's chunk
 };
 
 __device__ inline void q4k_load(const uint8_t* __restrict__ row, int b, int c, Q4Seg& s) {
   const uint8_t* blk = row + kQ4kBytes * b;  // 144 = 9 * 16: 16-byte aligned
-  s.hd = *(const uint4*)blk;
+  s.hw = *(const uint32_t*)(blk + 4 * c);
   s.c0 = *(const uint4*)(blk + 16 + 32 * c);
   s.c1 = *(const uint4*)(blk + 32 + 32 * c);
+}
+
+// dword J of the header, from lane J of the lane's quad (all four lanes of a
+// quad are active wherever a row is used)
+template <int J>
+__device__ inline uint32_t q4k_hdr(uint32_t hw) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)hw, J * 0x55, 0xF, 0xF, false);  // quad_perm [J,J,J,J]
 }
 
 // A lane's 64 activations as fixed point: xl[2k], xl[2k+1] pair values
@@ -89,21 +97,21 @@ __device__ inline float q4k_dot64(const Q4Seg& s, int c, const uint32_t* xl, con
     ah = sdot2(w8 & 0x00F000F0u, xh[2 * k + 1], ah);
   }
   // scale and min of sub-blocks j0 = 2c, j1 = 2c + 1 (6-bit fields)
+  const uint32_t hx = q4k_hdr<0>(s.hw), hy = q4k_hdr<1>(s.hw), hz = q4k_hdr<2>(s.hw),
+                 hv = q4k_hdr<3>(s.hw);
   const uint32_t t = 16u * (uint32_t)(c & 1);  // byte 2(c & 1) of the dwords, as a bit offset
-  const uint32_t y2 = s.hd.y >> t, z2 = s.hd.z >> t, w2 = s.hd.w >> t;
-  int sc0, sc1, m0, m1;
-  if (c < 2) {
-    sc0 = y2 & 63;
-    sc1 = (y2 >> 8) & 63;
-    m0 = z2 & 63;
-    m1 = (z2 >> 8) & 63;
-  } else {
-    sc0 = (w2 & 15) | (((y2 >> 6) & 3) << 4);
-    sc1 = ((w2 >> 8) & 15) | (((y2 >> 14) & 3) << 4);
-    m0 = ((w2 >> 4) & 15) | (((z2 >> 6) & 3) << 4);
-    m1 = ((w2 >> 12) & 15) | (((z2 >> 14) & 3) << 4);
-  }
-  const float d = f16_bits_to_f32(s.hd.x & 0xFFFFu), dmin = f16_bits_to_f32(s.hd.x >> 16);
+  const uint32_t y2 = hy >> t, z2 = hz >> t, w2 = hv >> t;
+  // chunks 0, 1: six bits of bytes 4..11; chunks 2, 3: a nibble of bytes
+  // 12..15 and the top two bits of bytes 4..11 (as bits 4, 5).  Written
+  // without a branch on the lane's chunk, so that nothing per row is hoisted.
+  const bool hi = c >= 2;
+  const uint32_t mlo = hi ? 15u : 63u, mhi = hi ? 0x30u : 0u;
+  const uint32_t srs = hi ? w2 : y2, srm = hi ? (w2 >> 4) : z2;
+  const int sc0 = (int)((srs & mlo) | ((y2 >> 2) & mhi));
+  const int sc1 = (int)(((srs >> 8) & mlo) | ((y2 >> 10) & mhi));
+  const int m0 = (int)((srm & mlo) | ((z2 >> 2) & mhi));
+  const int m1 = (int)(((srm >> 8) & mlo) | ((z2 >> 10) & mhi));
+  const float d = f16_bits_to_f32(hx & 0xFFFFu), dmin = f16_bits_to_f32(hx >> 16);
   const float main = (float)sc0 * (float)al + (float)sc1 * (float)(ah >> 4);  // ah is a multiple of 16
   const int mins = __mul24(m0, sl) + __mul24(m1, sh);  // |sl|, |sh| < 2^21
   return fmaf(d, main, -dmin * (float)mins);
