@@ -53,6 +53,14 @@ def lib():
         L.or_residual_add.argtypes = [i64, vp, vp]
         L.or_max_threads.restype = i32
         L.or_set_threads.argtypes = [i32]
+        L.en_f16_bits.argtypes = [ctypes.c_float]
+        L.en_f16_bits.restype = ctypes.c_uint16
+        L.en_iq2_map_bytes.restype = i64
+        L.en_iq2_map_build.argtypes = [vp, i32, vp]
+        L.en_iq2_map_build.restype = i32
+        L.en_quantize.argtypes = [i32, vp, i64, i64, i64, vp, i64, vp, vp, vp]
+        L.en_quantize.restype = i32
+        L.en_column_energy.argtypes = [vp, i64, i64, i64, vp]
         _L = L
     return _L
 
@@ -225,3 +233,63 @@ def set_threads(n):
 
 def max_threads():
     return lib().or_max_threads()
+
+
+# ---------------------------------------------------------------------------
+# block encoders (ds4_encode.c)
+# ---------------------------------------------------------------------------
+IQ2_KEYS = 6561
+
+
+def f16_bits(v):
+    """binary32 value -> binary16 bits, round to nearest even."""
+    return int(lib().en_f16_bits(float(np.float32(v))))
+
+
+def iq2_map(grid, n_grid=None):
+    """Neighbour map of an IQ2_XXS grid ([n][8] bytes of 8, 25, 43):
+    (count [6561] uint16, idx [6561][256] uint8, raw bytes)."""
+    g = _c(grid, np.uint8)
+    n = g.size // 8 if n_grid is None else n_grid
+    raw = np.zeros(lib().en_iq2_map_bytes(), np.uint8)
+    rc = lib().en_iq2_map_build(_p(g), n, _p(raw))
+    if rc != 0:
+        raise ValueError("en_iq2_map_build rc=%d" % rc)
+    count = raw[:2 * IQ2_KEYS].view(np.uint16)
+    idx = raw[2 * IQ2_KEYS:].reshape(IQ2_KEYS, 256)
+    return count, idx, raw
+
+
+def quantize(qt, src, importance=None, grid=None, imp_stride=None, map_raw=None):
+    """Encode src [n_mats][rows][cols] (or [rows][cols]) float32 into blocks
+    (uint8, n_mats*rows*cols/256 blocks).  importance: None, [cols] (shared)
+    or [n_mats][cols]."""
+    x = _c(src, np.float32)
+    if x.ndim == 2:
+        x = x[None]
+    n_mats, rows, cols = x.shape
+    imp = None if importance is None else _c(importance, np.float32)
+    if imp_stride is None:
+        imp_stride = 0 if imp is None or imp.ndim == 1 else cols
+    g = None if grid is None else _c(grid, np.uint8)
+    if qt == IQ2_XXS and map_raw is None and g is not None:
+        map_raw = iq2_map(g)[2]
+    bb = {Q2_K: 84, IQ2_XXS: 66}[qt]
+    out = np.zeros(n_mats * rows * cols // 256 * bb, np.uint8)
+    rc = lib().en_quantize(qt, _p(x), n_mats, rows, cols, None if imp is None else _p(imp),
+                           imp_stride, None if g is None else _p(g),
+                           None if map_raw is None else _p(map_raw), _p(out))
+    if rc != 0:
+        raise ValueError("en_quantize rc=%d" % rc)
+    return out
+
+
+def column_energy(src):
+    """sum_r W[r][c]^2 per matrix of src [n_mats][rows][cols], fp64."""
+    x = _c(src, np.float32)
+    if x.ndim == 2:
+        x = x[None]
+    n_mats, rows, cols = x.shape
+    out = np.empty((n_mats, cols), np.float64)
+    lib().en_column_energy(_p(x), n_mats, rows, cols, _p(out))
+    return out
