@@ -16,10 +16,12 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EDEVICE, EDATA = 0, -1, -2, -3, -4, -5
 F32, F16, BF16 = 0, 1, 2
 Q2_K, IQ2_XXS, Q8_0, Q4_K = 0, 1, 2, 3
 FAULT_BAD_ID, FAULT_BAD_TOKEN, FAULT_BAD_TABLE, FAULT_UNCERTIFIED, FAULT_F16_RANGE = 1, 2, 4, 8, 16
+FAULT_BAD_INPUT = 32
 
 EXPORTED = ("ds4moe_workspace_size", "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn",
             "ds4moe_expert_ffn_imatrix", "ds4moe_layer", "ds4moe_profile_events", "ds4moe_check",
-            "ds4moe_status_string")
+            "ds4moe_status_string", "ds4moe_iq2_map_bytes", "ds4moe_iq2_map_build",
+            "ds4moe_quantize", "ds4moe_column_energy")
 K_ROUTE, K_GATEUP, K_DOWN, K_PERMUTE, K_OTHER = range(5)
 
 
@@ -86,6 +88,15 @@ def lib():
         L.ds4moe_check.restype = i32
         L.ds4moe_status_string.argtypes = [i32]
         L.ds4moe_status_string.restype = ctypes.c_char_p
+        i64 = ctypes.c_int64
+        L.ds4moe_iq2_map_bytes.argtypes = []
+        L.ds4moe_iq2_map_bytes.restype = sz
+        L.ds4moe_iq2_map_build.argtypes = [vp, vp, vp, sz, vp]
+        L.ds4moe_iq2_map_build.restype = i32
+        L.ds4moe_quantize.argtypes = [i32, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, sz, vp]
+        L.ds4moe_quantize.restype = i32
+        L.ds4moe_column_energy.argtypes = [vp, i64, i64, i64, vp, vp]
+        L.ds4moe_column_energy.restype = i32
         _lib = L
     return _lib
 
@@ -162,6 +173,26 @@ def layer(shp, desc, x, x_dtype, residual, out, token_ids, n_tok, ids_dbg, w_dbg
 def profile_events(cls, begin, end):
     """begin/end: HIP event handles (int) or None to stop."""
     _ok(lib().ds4moe_profile_events(cls, begin, end), "ds4moe_profile_events")
+
+
+def iq2_map_bytes():
+    return int(lib().ds4moe_iq2_map_bytes())
+
+
+def iq2_map_build(grid, map_out, ws, ws_bytes, stream=0):
+    """Neighbour map of an IQ2_XXS grid (device pointers)."""
+    _ok(lib().ds4moe_iq2_map_build(grid, map_out, ws, ws_bytes, stream), "ds4moe_iq2_map_build")
+
+
+def quantize(qtype, src, n_mats, rows, cols, importance, imp_stride, grid, iq2_map, dst, ws,
+             ws_bytes, stream=0):
+    """fp32 matrices [n_mats][rows][cols] -> Q2_K / IQ2_XXS blocks (device pointers)."""
+    _ok(lib().ds4moe_quantize(qtype, src, n_mats, rows, cols, importance, imp_stride, grid,
+                              iq2_map, dst, ws, ws_bytes, stream), "ds4moe_quantize")
+
+
+def column_energy(src, n_mats, rows, cols, out, stream=0):
+    _ok(lib().ds4moe_column_energy(src, n_mats, rows, cols, out, stream), "ds4moe_column_energy")
 
 
 def check(ws, stream=0):

@@ -10,6 +10,7 @@
 #include "ffn_q4k.hip"
 #include "ffn_generic.hip"
 #include "grouped.hip"
+#include "encode.hip"
 
 #define DS4_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -731,6 +732,72 @@ DS4_EXPORT ds4moe_status ds4moe_profile_events(int32_t cls, hipEvent_t begin, hi
   g_prof[cls][0] = begin;
   g_prof[cls][1] = end;
   return DS4MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Block encoders (encode.hip)
+// ---------------------------------------------------------------------------
+DS4_EXPORT size_t ds4moe_iq2_map_bytes(void) { return kIq2MapBytes; }
+
+DS4_EXPORT ds4moe_status ds4moe_iq2_map_build(const uint8_t* grid, void* map, void* ws,
+                                              size_t ws_bytes, hipStream_t stream) {
+  if (!grid || !map || !ws || ws_bytes < 256 || ((uintptr_t)grid & 7) || ((uintptr_t)map & 1))
+    return DS4MOE_EINVAL;
+  ProfScope prof(DS4MOE_K_OTHER, stream);
+  launch_k(k_iq2_map, dim3((kIq2Keys + 3) / 4), dim3(kEncThreads), 0, stream, grid,
+           static_cast<uint8_t*>(map), at<uint32_t>(ws, 0));
+  return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;
+}
+
+DS4_EXPORT ds4moe_status ds4moe_quantize(int32_t qtype, const float* src, int64_t n_mats,
+                                         int64_t rows, int64_t cols, const float* importance,
+                                         int64_t imp_stride, const uint8_t* grid,
+                                         const void* iq2_map, void* dst, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+  if ((qtype != DS4MOE_Q2_K && qtype != DS4MOE_IQ2_XXS) || !src || !dst || !ws ||
+      ws_bytes < 256 || n_mats < 0 || rows < 0 || cols < 0 || cols % 256 || imp_stride < 0 ||
+      imp_stride % 4 || ((uintptr_t)src & 15) || ((uintptr_t)importance & 15))
+    return DS4MOE_EINVAL;
+  if (qtype == DS4MOE_IQ2_XXS &&
+      (!importance || !grid || !iq2_map || ((uintptr_t)grid & 7) || ((uintptr_t)iq2_map & 1) ||
+       ((uintptr_t)dst & 1)))
+    return DS4MOE_EINVAL;
+  if (qtype == DS4MOE_Q2_K && ((uintptr_t)dst & 3)) return DS4MOE_EINVAL;
+  const int64_t n_blocks = n_mats * rows * (cols / 256);
+  if (n_blocks == 0) return DS4MOE_OK;
+  EncArgs a;
+  a.src = src;
+  a.imp = importance;
+  a.grid = grid;
+  a.map = static_cast<const uint8_t*>(iq2_map);
+  a.dst = static_cast<uint8_t*>(dst);
+  a.status = at<uint32_t>(ws, 0);
+  a.n_blocks = n_blocks;
+  a.bpr = cols / 256;
+  a.rows = rows;
+  a.imp_stride = imp_stride;
+  ProfScope prof(DS4MOE_K_OTHER, stream);
+  const int per = qtype == DS4MOE_Q2_K ? kEncThreads / 16 : kEncThreads / 8;
+  const int64_t wgs = (n_blocks + per - 1) / per;
+  if (wgs > 0x7FFFFFFF) return DS4MOE_EUNSUPPORTED;
+  if (qtype == DS4MOE_Q2_K)
+    launch_k(k_encode_q2k, dim3((uint32_t)wgs), dim3(kEncThreads), 0, stream, a);
+  else
+    launch_k(k_encode_iq2, dim3((uint32_t)wgs), dim3(kEncThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;
+}
+
+DS4_EXPORT ds4moe_status ds4moe_column_energy(const float* src, int64_t n_mats, int64_t rows,
+                                              int64_t cols, float* out, hipStream_t stream) {
+  if (!src || !out || n_mats < 0 || rows < 0 || cols < 0) return DS4MOE_EINVAL;
+  const int64_t n = n_mats * cols;
+  if (n == 0) return DS4MOE_OK;
+  const int64_t wgs = (n + kEncThreads - 1) / kEncThreads;
+  if (wgs > 0x7FFFFFFF) return DS4MOE_EUNSUPPORTED;
+  ProfScope prof(DS4MOE_K_OTHER, stream);
+  launch_k(k_column_energy, dim3((uint32_t)wgs), dim3(kEncThreads), 0, stream, src, n_mats, rows,
+           cols, out);
+  return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;
 }
 
 DS4_EXPORT ds4moe_status ds4moe_check(void* ws, hipStream_t stream, uint32_t* faults) {

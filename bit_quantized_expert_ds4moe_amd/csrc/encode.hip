@@ -1,0 +1,483 @@
+// encode.hip -- block encoders on gfx950: fp32 matrices to Q2_K and IQ2_XXS
+// blocks, plain or weighted by per-column importance, the IQ2_XXS neighbour
+// map of a grid, and the column-energy fallback importance.
+//
+// Pages: DS4C2 = qiita.com/yoshiyakato/items/4678be0e7860ddb444ec, sec. 3
+// (Q2_K: scale and min per 16 values, 2-bit codes, four per byte; with an
+// importance vector the weighted variant), sec. 4 (IQ2_XXS: 8 groups of 32,
+// four grid indices and four 7-bit sign masks per group, fp16 block scale
+// and 4-bit group nibble, 256-entry grid, off-grid tuples searched in a
+// two-shell neighbour list; importance required), sec. 5, 7, 8 (importance =
+// sum of squared activations per column, one vector per expert; fallback =
+// column energy of the weights).
+//
+// The pages print no search procedure; these kernels carry out the plain one
+// written out with the block layouts of the decoders:
+//   Q2_K, per 16-value sub-block: start from the range (m = -min(0, min x),
+//     s = (max x + m) / 3), four rounds of codes -> weighted least-squares
+//     (s, m) (m, then s, clamped at 0), keeping the lowest weighted error
+//     (strictly lower replaces); d = max s / 15 and dmin = max m / 15 in fp16,
+//     nibbles rint(s / d), rint(m / dmin), codes nearest for the stored pair.
+//   IQ2_XXS, per 32-value group: signs of x with, in a tuple of 8 with an odd
+//     number of negatives, the smallest w x^2 flipped; targets t = sign * x;
+//     16 candidate scales tmax / (24 + 2c): tuples take the grid entry of the
+//     nearest levels (8 | 25 | 43, cut at 16.5 and 34) or the best entry of
+//     that key's list, the scale is refitted (sum w t g / sum w g^2) and
+//     scored by sum w (t - S g)^2; d = 8 max S / 31 in fp16, nibble
+//     rint((8 S / d - 1) / 2), tuples assigned again at d (2s + 1) / 8.
+// Every integer decision is taken in binary32 in that order: sums run over
+// the values in index order with one rounding per operation (contraction is
+// switched off in each function), divisions are IEEE divisions, rint rounds
+// half to even, fp16 conversion rounds to nearest even.  One lane owns a
+// Q2_K sub-block or an IQ2_XXS group, so its sums are sequential as written;
+// block maxima are exact in any order.
+#include "dev_common.h"
+
+namespace ds4 {
+
+constexpr int kIq2Keys = 6561;                                 // 3^8 level tuples
+constexpr size_t kIq2MapBytes = 2 * kIq2Keys + 256 * kIq2Keys;  // counts, then lists
+constexpr int kEncThreads = 256;
+
+__device__ inline float enc_clamp(float v, float lo, float hi) { return fminf(fmaxf(v, lo), hi); }
+
+__device__ inline uint16_t enc_f16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (_Float16)v);  // v_cvt_f16_f32: nearest even
+}
+__device__ inline float enc_f16_float(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// maximum over the aligned group of N lanes (N = 8 or 16)
+template <int N>
+__device__ inline float enc_group_max(float v) {
+#pragma unroll
+  for (int o = 1; o < N; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ inline bool enc_bad_value(float x) { return !(fabsf(x) <= 3.402823466e38f); }
+__device__ inline bool enc_bad_weight(float w) { return !(w >= 0.0f && w <= 3.402823466e38f); }
+
+// ---------------------------------------------------------------------------
+// Q2_K
+// ---------------------------------------------------------------------------
+__device__ inline int q2e_code(float x, float s, float m) {
+#pragma clang fp contract(off)
+  if (!(s > 0.0f)) return 0;
+  return (int)enc_clamp(__builtin_rintf((x + m) / s), 0.0f, 3.0f);
+}
+
+__device__ inline float q2e_err(const float* x, const float* w, float s, float m) {
+#pragma clang fp contract(off)
+  float e = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    float t = s * (float)q2e_code(x[i], s, m);
+    t = t - m;
+    const float r = t - x[i];
+    e = e + w[i] * (r * r);
+  }
+  return e;
+}
+
+__device__ inline void q2e_fit(const float* x, const float* w, float& s_out, float& m_out) {
+#pragma clang fp contract(off)
+  float lo = 0.0f, hi = x[0];
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    lo = fminf(lo, x[i]);
+    hi = fmaxf(hi, x[i]);
+  }
+  float s = (hi - lo) / 3.0f, m = -lo;
+  if (!(s > 0.0f)) s = 0.0f;
+  float bs = s, bm = m, be = q2e_err(x, w, s, m);
+  for (int it = 0; it < 4; it++) {
+    float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f, T0 = 0.0f, T1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const float q = (float)q2e_code(x[i], s, m);
+      const float wq = w[i] * q;
+      S0 = S0 + w[i];
+      S1 = S1 + wq;
+      S2 = S2 + wq * q;
+      T0 = T0 + w[i] * x[i];
+      T1 = T1 + wq * x[i];
+    }
+    const float det = S0 * S2 - S1 * S1;
+    if (!(det > 0.0f)) break;
+    float ns = (S0 * T1 - S1 * T0) / det;
+    float nm = (S1 * T1 - S2 * T0) / det;
+    if (nm < 0.0f) {
+      nm = 0.0f;
+      ns = S2 > 0.0f ? T1 / S2 : 0.0f;
+    }
+    if (ns < 0.0f) {
+      ns = 0.0f;
+      nm = S0 > 0.0f ? -T0 / S0 : 0.0f;
+      if (nm < 0.0f) nm = 0.0f;
+    }
+    const float e = q2e_err(x, w, ns, nm);
+    if (e < be) {
+      be = e;
+      bs = ns;
+      bm = nm;
+    }
+    s = ns;
+    m = nm;
+  }
+  s_out = bs;
+  m_out = bm;
+}
+
+struct EncArgs {
+  const float* src;       // [n_rows][cols] (matrices stacked)
+  const float* imp;       // nullable: [n_mats][cols] at imp_stride, or [cols]
+  const uint8_t* grid;    // IQ2_XXS
+  const uint8_t* map;     // IQ2_XXS
+  uint8_t* dst;
+  uint32_t* status;
+  int64_t n_blocks;       // n_rows * bpr
+  int64_t bpr;            // blocks per row = cols / 256
+  int64_t rows;           // rows per matrix
+  int64_t imp_stride;
+};
+
+// the importance of column 256 b + c of block `blk`'s row (matrix of the row)
+__device__ inline const float* enc_imp_row(const EncArgs& a, int64_t blk) {
+  const int64_t r = blk / a.bpr;
+  const int64_t m = r / a.rows;
+  return a.imp + m * a.imp_stride + (blk - r * a.bpr) * 256;
+}
+
+// 16 lanes per block (lane j: sub-block j), 16 blocks per workgroup.  The
+// block's bytes are assembled in LDS and leave as 21 dwords.
+__global__ __launch_bounds__(kEncThreads) void k_encode_q2k(EncArgs a) {
+#pragma clang fp contract(off)
+  __shared__ uint32_t codes[kEncThreads / 16][64];  // one byte per value
+  __shared__ uint32_t sbytes[kEncThreads / 16][4];
+  const int tid = threadIdx.x, j = tid & 15, lb = tid >> 4;
+  const int64_t blk0 = (int64_t)blockIdx.x * (kEncThreads / 16) + lb;
+  const bool live = blk0 < a.n_blocks;
+  const int64_t blk = live ? blk0 : 0;
+  float x[16], w[16];
+  const float4* xp = (const float4*)(a.src + blk * 256 + 16 * j);
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const float4 v = xp[q];
+    x[4 * q] = v.x;
+    x[4 * q + 1] = v.y;
+    x[4 * q + 2] = v.z;
+    x[4 * q + 3] = v.w;
+  }
+  if (a.imp) {
+    const float4* wp = (const float4*)(enc_imp_row(a, blk) + 16 * j);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float4 v = wp[q];
+      w[4 * q] = v.x;
+      w[4 * q + 1] = v.y;
+      w[4 * q + 2] = v.z;
+      w[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; i++) w[i] = 1.0f;
+  }
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 16; i++) bad |= enc_bad_value(x[i]) || enc_bad_weight(w[i]);
+  if (bad && live) raise_fault(a.status, DS4MOE_FAULT_BAD_INPUT);
+
+  float s, m;
+  q2e_fit(x, w, s, m);
+  float smax = enc_group_max<16>(s), mmax = enc_group_max<16>(m);
+  if (!(smax > 0.0f)) smax = 0.0f;
+  if (!(mmax > 0.0f)) mmax = 0.0f;
+  const uint16_t dh = enc_f16_bits(smax / 15.0f), mh = enc_f16_bits(mmax / 15.0f);
+  const float d = enc_f16_float(dh), dmin = enc_f16_float(mh);
+  const int sc = d > 0.0f ? (int)enc_clamp(__builtin_rintf(s / d), 0.0f, 15.0f) : 0;
+  const int mn = dmin > 0.0f ? (int)enc_clamp(__builtin_rintf(m / dmin), 0.0f, 15.0f) : 0;
+  const float S = d * (float)sc, M = dmin * (float)mn;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; b++) v |= (uint32_t)q2e_code(x[4 * q + b], S, M) << (8 * b);
+    codes[lb][4 * j + q] = v;
+  }
+  ((uint8_t*)sbytes[lb])[j] = (uint8_t)(sc | (mn << 4));
+  __syncthreads();
+  // qs dword j = bytes 4j .. 4j+3 of the 64 code bytes: byte B = 32h + l
+  // holds the codes of values 128h + 32s + l in bit pairs s
+  uint32_t out = 0;
+  const uint8_t* cb = (const uint8_t*)codes[lb];
+#pragma unroll
+  for (int b = 0; b < 4; b++) {
+    const int B = 4 * j + b, h = B >> 5, l = B & 31;
+    uint32_t byte = 0;
+#pragma unroll
+    for (int sh = 0; sh < 4; sh++) byte |= (uint32_t)cb[128 * h + 32 * sh + l] << (2 * sh);
+    out |= byte << (8 * b);
+  }
+  if (live) {
+    uint32_t* o = (uint32_t*)(a.dst + blk * 84);
+    o[4 + j] = out;
+    if (j < 4) o[j] = sbytes[lb][j];
+    if (j == 4) o[20] = (uint32_t)dh | ((uint32_t)mh << 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// IQ2_XXS
+// ---------------------------------------------------------------------------
+__device__ inline int iq2e_level(float v) { return v < 16.5f ? 0 : v < 34.0f ? 1 : 2; }
+
+// grid index for the 8 targets t (weights w) at scale S > 0; gl = the grid
+// in LDS (256 x 8 bytes)
+__device__ inline int iq2e_pick(const float* t, const float* w, float S, const uint8_t* gl,
+                                const uint8_t* __restrict__ map) {
+#pragma clang fp contract(off)
+  int key = 0, p = 1;
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    key += iq2e_level(t[k] / S) * p;
+    p *= 3;
+  }
+  const int n = ((const uint16_t*)map)[key];
+  const uint8_t* list = map + 2 * kIq2Keys + 256 * key;
+  int best = list[0];
+  if (n == 1) return best;
+  float be = __builtin_inff();
+  for (int jj = 0; jj < n; jj++) {
+    const int i = list[jj];
+    const uint2 ge = *(const uint2*)(gl + 8 * i);
+    float e = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const uint32_t gw = k < 4 ? ge.x : ge.y;
+      float r = S * (float)((gw >> (8 * (k & 3))) & 0xFF);
+      r = t[k] - r;
+      e = e + w[k] * (r * r);
+    }
+    if (e < be) {
+      be = e;
+      best = i;
+    }
+  }
+  return best;
+}
+
+__device__ inline float iq2e_g(const uint8_t* gl, int id, int k) { return (float)gl[8 * id + k]; }
+
+// 8 lanes per block (lane g: group g), 32 blocks per workgroup.
+__global__ __launch_bounds__(kEncThreads) void k_encode_iq2(EncArgs a) {
+#pragma clang fp contract(off)
+  __shared__ __align__(16) uint8_t gl[256 * 8];
+  const int tid = threadIdx.x, g = tid & 7;
+  ((uint2*)gl)[tid] = ((const uint2*)a.grid)[tid];  // 256 threads x 8 bytes
+  const int64_t blk0 = (int64_t)blockIdx.x * (kEncThreads / 8) + (tid >> 3);
+  const bool live = blk0 < a.n_blocks;
+  const int64_t blk = live ? blk0 : 0;
+  float t[32], w[32];
+  const float4* xp = (const float4*)(a.src + blk * 256 + 32 * g);
+  const float4* wp = (const float4*)(enc_imp_row(a, blk) + 32 * g);
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    const float4 v = xp[q], u = wp[q];
+    t[4 * q] = v.x;
+    t[4 * q + 1] = v.y;
+    t[4 * q + 2] = v.z;
+    t[4 * q + 3] = v.w;
+    w[4 * q] = u.x;
+    w[4 * q + 1] = u.y;
+    w[4 * q + 2] = u.z;
+    w[4 * q + 3] = u.w;
+  }
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 32; i++) bad |= enc_bad_value(t[i]) || enc_bad_weight(w[i]);
+  if (bad && live) raise_fault(a.status, DS4MOE_FAULT_BAD_INPUT);
+  __syncthreads();  // grid in LDS
+
+  // signs (even number of negatives per tuple), targets t = sign * x
+  uint32_t signs = 0;
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    int neg = 0, n = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+      if (t[8 * u + k] < 0.0f) {
+        neg |= 1 << k;
+        n++;
+      }
+    if (n & 1) {
+      int kmin = 0;
+      float emin = w[8 * u] * (t[8 * u] * t[8 * u]);
+#pragma unroll
+      for (int k = 1; k < 8; k++) {
+        const float e = w[8 * u + k] * (t[8 * u + k] * t[8 * u + k]);
+        if (e < emin) {
+          emin = e;
+          kmin = k;
+        }
+      }
+      neg ^= 1 << kmin;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+      if ((neg >> k) & 1) t[8 * u + k] = -t[8 * u + k];
+    signs |= (uint32_t)(neg & 0x7F) << (7 * u);
+  }
+
+  // group scale
+  float tmax = t[0];
+#pragma unroll
+  for (int k = 1; k < 32; k++) tmax = fmaxf(tmax, t[k]);
+  float Sg = 0.0f;
+  if (tmax > 0.0f) {
+    float be = __builtin_inff();
+    for (int c = 0; c < 16; c++) {
+      float S = tmax / (float)(24 + 2 * c);
+      int id[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) id[u] = iq2e_pick(t + 8 * u, w + 8 * u, S, gl, a.map);
+      float num = 0.0f, den = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 32; k++) {
+        const float gv = iq2e_g(gl, id[k >> 3], k & 7);
+        num = num + (w[k] * t[k]) * gv;
+        den = den + (w[k] * gv) * gv;
+      }
+      if (num > 0.0f && den > 0.0f) S = num / den;
+      float e = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 32; k++) {
+        float r = S * iq2e_g(gl, id[k >> 3], k & 7);
+        r = t[k] - r;
+        e = e + w[k] * (r * r);
+      }
+      if (e < be) {
+        be = e;
+        Sg = S;
+      }
+    }
+  }
+  float smax = enc_group_max<8>(Sg);
+  if (!(smax > 0.0f)) smax = 0.0f;
+  const uint16_t dh = enc_f16_bits((smax * 8.0f) / 31.0f);
+  const float d = enc_f16_float(dh);
+  const int s = d > 0.0f ? (int)enc_clamp(__builtin_rintf(((Sg * 8.0f) / d - 1.0f) / 2.0f), 0.0f, 15.0f) : 0;
+  const float S = (d * (float)(2 * s + 1)) / 8.0f;
+  uint32_t ids = 0;
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int id = S > 0.0f ? iq2e_pick(t + 8 * u, w + 8 * u, S, gl, a.map) : a.map[2 * kIq2Keys];
+    ids |= (uint32_t)id << (8 * u);
+  }
+  const uint32_t word = signs | ((uint32_t)s << 28);
+  if (live) {
+    uint16_t* o = (uint16_t*)(a.dst + blk * 66);  // 66-byte blocks: 2-byte aligned
+    if (g == 0) o[0] = dh;
+    uint16_t* og = o + 1 + 4 * g;
+    og[0] = (uint16_t)ids;
+    og[1] = (uint16_t)(ids >> 16);
+    og[2] = (uint16_t)word;
+    og[3] = (uint16_t)(word >> 16);
+  }
+}
+
+// Neighbour map of a grid: one wave per key (lane L holds entries 4L..4L+3).
+// The list: the lowest on-grid index, or every entry within the two smallest
+// squared level distances, ascending.
+__global__ __launch_bounds__(kEncThreads) void k_iq2_map(const uint8_t* __restrict__ grid,
+                                                         uint8_t* __restrict__ map,
+                                                         uint32_t* status) {
+  const int lane = threadIdx.x & 63;
+  const int key = blockIdx.x * (kEncThreads / 64) + (threadIdx.x >> 6);
+  if (key >= kIq2Keys) return;  // whole waves
+  int lv[8], k2 = key;
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    lv[k] = k2 % 3;
+    k2 /= 3;
+  }
+  int dist[4];
+  bool bad = false;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const uint2 ge = ((const uint2*)grid)[4 * lane + q];
+    int dd = 0;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const uint32_t v = ((k < 4 ? ge.x : ge.y) >> (8 * (k & 3))) & 0xFF;
+      const int gl = v == 8 ? 0 : v == 25 ? 1 : v == 43 ? 2 : -100;
+      bad |= gl < 0;
+      const int tdiff = lv[k] - gl;
+      dd += tdiff * tdiff;
+    }
+    dist[q] = dd;
+  }
+  if (bad && key == 0) raise_fault(status, DS4MOE_FAULT_BAD_INPUT);
+  // the two smallest distinct distances over the wave
+  int d1 = min(min(dist[0], dist[1]), min(dist[2], dist[3]));
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) d1 = min(d1, __shfl_xor(d1, o, 64));
+  int d2 = 1 << 30;
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+    if (dist[q] > d1) d2 = min(d2, dist[q]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) d2 = min(d2, __shfl_xor(d2, o, 64));
+  if (d2 == (1 << 30)) d2 = d1;
+  const int lim = d1 == 0 ? -1 : d2;
+  int mine = 0;
+#pragma unroll
+  for (int q = 0; q < 4; q++) mine += dist[q] <= lim;
+  // exclusive prefix over lanes (ascending index order: lane, then q)
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  const int total = __shfl(incl, 63, 64);
+  uint8_t* list = map + 2 * kIq2Keys + 256 * key;
+  if (d1 == 0) {
+    // lowest on-grid index
+    int first = 1 << 30;
+#pragma unroll
+    for (int q = 3; q >= 0; q--)
+      if (dist[q] == 0) first = 4 * lane + q;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) first = min(first, __shfl_xor(first, o, 64));
+    if (lane == 0) {
+      list[0] = (uint8_t)first;
+      ((uint16_t*)map)[key] = 1;
+    }
+  } else {
+    int pos = incl - mine;
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+      if (dist[q] <= lim) list[pos++] = (uint8_t)(4 * lane + q);
+    if (lane == 0) ((uint16_t*)map)[key] = (uint16_t)total;
+  }
+}
+
+// Column energy sum_r W[r][c]^2 (fp32 accumulation in row order) of n_mats
+// matrices: one thread per (matrix, column); reads stride over rows, the
+// threads of a wave covering consecutive columns.
+__global__ __launch_bounds__(kEncThreads) void k_column_energy(const float* __restrict__ src,
+                                                               int64_t n_mats, int64_t rows,
+                                                               int64_t cols, float* out) {
+  const int64_t i = (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
+  if (i >= n_mats * cols) return;
+  const int64_t m = i / cols, c = i - m * cols;
+  const float* p = src + m * rows * cols + c;
+  float e = 0.0f;
+  for (int64_t r = 0; r < rows; r++) {
+    const float v = p[r * cols];
+    e = fmaf(v, v, e);
+  }
+  out[i] = e;
+}
+
+}  // namespace ds4

@@ -212,6 +212,9 @@ ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_layer_desc* d
 #define DS4MOE_FAULT_BAD_TABLE 0x4u    /* tid2eid row out of range / repeated   */
 #define DS4MOE_FAULT_UNCERTIFIED 0x8u  /* routing not certifiable (see route)   */
 #define DS4MOE_FAULT_F16_RANGE 0x10u   /* an intermediate exceeded binary16     */
+#define DS4MOE_FAULT_BAD_INPUT 0x20u   /* encoder: non-finite value, negative or
+                                          non-finite importance, grid value not
+                                          8, 25 or 43                            */
 
 /* Kernel classes for ds4moe_profile_events(). */
 #define DS4MOE_K_ROUTE 0     /* router scoring + selection, or hash lookup  */
@@ -230,6 +233,69 @@ ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_layer_desc* d
  * thread.  Returns DS4MOE_EINVAL for an unknown class.
  */
 ds4moe_status ds4moe_profile_events(int32_t cls, hipEvent_t begin, hipEvent_t end);
+
+/* ------------------------------------------------------------------ */
+/* Block encoders: fp32 matrices -> Q2_K / IQ2_XXS blocks               */
+/* ------------------------------------------------------------------ */
+/*
+ * Defined by DS4C2 (qiita.com/yoshiyakato/items/4678be0e7860ddb444ec)
+ * sec. 3 (Q2_K: a scale and a min per 16 values, 2-bit codes; with an
+ * importance vector the weighted variant, whose per-column importance
+ * weighs the quantisation error), sec. 4 (IQ2_XXS: requires importance;
+ * tuples off the 256-entry grid are searched in a two-shell neighbour list),
+ * sec. 5, 7, 8 (importance = sum of squared activations per column, one
+ * vector per expert; fallback = column energy of the weights).  The pages
+ * print no search procedure: the library carries out a fixed one (least-
+ * squares refits for Q2_K, 16 candidate group scales for IQ2_XXS) with every
+ * decision in binary32 in a stated order; the exact steps are written at the
+ * kernels (encode.hip).  Outputs are deterministic: the same input gives the
+ * same bytes on every call and launch configuration.
+ */
+
+/* Bytes of an IQ2_XXS neighbour map: uint16 count[6561], then uint8
+ * idx[6561][256] (6561 = 3^8 tuples of the levels 8, 25, 43). */
+size_t ds4moe_iq2_map_bytes(void);
+
+/*
+ * Builds the neighbour map of an IQ2_XXS grid.  grid: device, 256 x 8 bytes,
+ * 8-byte aligned, every byte 8, 25 or 43.  map: device, ds4moe_iq2_map_bytes()
+ * bytes, caller-owned.  For the tuple of levels with key sum_k level_k 3^k
+ * the list holds the lowest grid index equal to it, or, off the grid, every
+ * index whose squared level distance is at most the second-smallest distance
+ * over the grid, ascending.  ws: a zero-filled workspace of >= 256 bytes (its
+ * status word; any workspace of this library serves); a grid byte outside
+ * {8, 25, 43} sets DS4MOE_FAULT_BAD_INPUT.  Asynchronous on `stream`.
+ */
+ds4moe_status ds4moe_iq2_map_build(const uint8_t* grid, void* map, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/*
+ * Encodes n_mats row-major fp32 matrices [rows][cols] (stacked, device,
+ * 16-byte aligned, cols % 256 == 0) into blocks tiling each row: dst gets
+ * n_mats*rows*cols/256 blocks of 84 (Q2_K, dst 4-byte aligned) or 66 bytes
+ * (IQ2_XXS, 2-byte aligned), in the layouts the expert kernels read.
+ * importance: device, nullable for Q2_K (every weight 1: the plain encoder),
+ * required for IQ2_XXS; matrix m's weights are importance[m * imp_stride + c]
+ * for column c (imp_stride 0: one vector for every matrix; otherwise a
+ * multiple of 4, normally cols: the n_expert x n_columns packing), 16-byte
+ * aligned.  grid and iq2_map (IQ2_XXS only): the grid as for
+ * ds4moe_iq2_map_build and the map built from it.  Non-finite values or
+ * weights, and negative weights, set DS4MOE_FAULT_BAD_INPUT in the status
+ * word of ws (>= 256 bytes); the blocks are then unspecified.  Returns
+ * DS4MOE_EINVAL for a bad type, pointer, alignment or shape.  Asynchronous.
+ */
+ds4moe_status ds4moe_quantize(int32_t qtype, const float* src, int64_t n_mats, int64_t rows,
+                              int64_t cols, const float* importance, int64_t imp_stride,
+                              const uint8_t* grid, const void* iq2_map, void* dst, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Fallback importance (DS4C2 sec. 8): out[m][c] = sum_r src[m][r][c]^2 for
+ * n_mats fp32 matrices [rows][cols] (device), accumulated in fp32 in row
+ * order with fused multiply-adds.  out: device, n_mats * cols floats.
+ */
+ds4moe_status ds4moe_column_energy(const float* src, int64_t n_mats, int64_t rows, int64_t cols,
+                                   float* out, hipStream_t stream);
 
 /*
  * Waits for `stream`, reads and clears the workspace status word.  Returns

@@ -103,3 +103,36 @@ def test_layer_and_permute_reject_bad_arguments(lib):
         ds4.permute(s, FAKE, 6000, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40)
     assert e.value.status == ds4.EUNSUPPORTED
     assert ds4.status_string(ds4.EDATA) == "device-detected data fault"
+
+
+def test_encoder_entry_points_reject_bad_arguments(lib):
+    assert ds4.iq2_map_bytes() == 6561 * 2 + 6561 * 256
+    bad = [
+        (7, FAKE, 1, 1, 256, None, 0, None, None, FAKE),            # type
+        (ds4.Q8_0, FAKE, 1, 1, 256, None, 0, None, None, FAKE),     # no Q8_0 encoder
+        (ds4.Q2_K, FAKE, 1, 1, 200, None, 0, None, None, FAKE),     # not whole blocks
+        (ds4.Q2_K, FAKE + 4, 1, 1, 256, None, 0, None, None, FAKE), # src alignment
+        (ds4.Q2_K, FAKE, 1, 1, 256, None, 0, None, None, FAKE + 2), # Q2_K dst alignment
+        (ds4.Q2_K, FAKE, 1, 1, 256, FAKE, 6, None, None, FAKE),     # importance stride
+        (ds4.IQ2_XXS, FAKE, 1, 1, 256, None, 0, FAKE, FAKE, FAKE),  # importance required
+        (ds4.IQ2_XXS, FAKE, 1, 1, 256, FAKE, 0, None, FAKE, FAKE),  # grid required
+        (ds4.IQ2_XXS, FAKE, 1, 1, 256, FAKE, 0, FAKE, None, FAKE),  # map required
+        (ds4.IQ2_XXS, FAKE, 1, 1, 256, FAKE, 0, FAKE + 4, FAKE, FAKE),  # grid alignment
+        (ds4.Q2_K, FAKE, -1, 1, 256, None, 0, None, None, FAKE),    # negative size
+    ]
+    for args in bad:
+        with pytest.raises(ds4.Ds4moeError) as e:
+            ds4.quantize(*args, FAKE, 256)
+        assert e.value.status == ds4.EINVAL, args
+    with pytest.raises(ds4.Ds4moeError) as e:
+        ds4.quantize(ds4.Q2_K, FAKE, 1, 1, 256, None, 0, None, None, FAKE, FAKE, 255)
+    assert e.value.status == ds4.EINVAL                              # workspace too small
+    with pytest.raises(ds4.Ds4moeError) as e:
+        ds4.iq2_map_build(FAKE + 1, FAKE, FAKE, 256)
+    assert e.value.status == ds4.EINVAL
+    with pytest.raises(ds4.Ds4moeError) as e:
+        ds4.column_energy(None, 1, 1, 256, FAKE)
+    assert e.value.status == ds4.EINVAL
+    # empty inputs are valid and launch nothing
+    ds4.quantize(ds4.Q2_K, FAKE, 0, 4, 256, None, 0, None, None, FAKE, FAKE, 256)
+    ds4.column_energy(FAKE, 0, 4, 256, FAKE)
