@@ -13,7 +13,7 @@ Other workloads (--workload): decode-b8 (8 correlated tokens + Q8_0 shared
 expert), prefill-512 (Zipf-routed 512-token chunk), stack-43 (43-layer
 decode stack, hash routing in layers 0-2), stack-43-q4k (the same stack with
 Q4_K routed experts in layers 37-42), decode-sweep (the decode-b8 layer at 1
-to 64 tokens per call).
+to 64 tokens per call), encode (fp32 experts to IQ2_XXS / Q2_K blocks).
 """
 import argparse
 import json
@@ -600,6 +600,143 @@ def bench_sweep(args):
     }
 
 
+# fp32 operations the encoder definitions perform per unit, list searches of
+# the IQ2_XXS neighbour map excluded (their length depends on the data), a
+# division counted as one operation.  IQ2_XXS group of 32 values: 16
+# candidates x (32 level divisions + 96 refit-numerator + 96 refit-denominator
+# + 160 error operations) + the final 32 level divisions.  Q2_K sub-block of
+# 16 values: start error 128, four refits of 16 codes x 2 + 16 sums x 9 + 10
+# + error 128, final codes 32.
+ENC_OPS_IQ2_GROUP = 16 * (32 + 96 + 96 + 160) + 32
+ENC_OPS_Q2K_SUB = 128 + 4 * (32 + 144 + 10 + 128) + 32
+# unpacked fp32 VALU operations per second: 256 CUs x 4 SIMDs x 16 lanes x
+# 2.4 GHz (the published 157.3 TFLOP/s counts a fused multiply-add as two and
+# packed-fp32 pairs twice)
+PEAK_FP32_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def bench_encode(args):
+    """Block encoders: one step quantises n experts of the V4-Flash shape from
+    fp32 resident in HBM, gate and up [2048][4096] to IQ2_XXS and down
+    [4096][2048] to Q2_K, each weighted by a per-expert importance vector
+    (n_expert x n_columns)."""
+    import numpy as np
+    import torch
+
+    import bit_quantized_expert_ds4moe_amd as ds4
+    import ds4gen as g
+
+    n, I, H = args.encode_experts, 2048, 4096
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    log("generating %d experts of fp32 weights on the device" % n)
+    gate = torch.randn((n, I, H), generator=gen, device="cuda") * 0.02
+    up = torch.randn((n, I, H), generator=gen, device="cuda") * 0.02
+    down = torch.randn((n, H, I), generator=gen, device="cuda") * 0.02
+    imp_gu = torch.randn((n, H), generator=gen, device="cuda") ** 2
+    imp_dn = torch.randn((n, I), generator=gen, device="cuda") ** 2
+    grid = torch.from_numpy(g.grid(1)).cuda()
+    qmap = torch.zeros(ds4.iq2_map_bytes(), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    ds4.iq2_map_build(grid.data_ptr(), qmap.data_ptr(), ws.data_ptr(), 256, st)
+    out_g = torch.empty(n * I * H // 256 * 66, dtype=torch.uint8, device="cuda")
+    out_u = torch.empty_like(out_g)
+    out_d = torch.empty(n * H * I // 256 * 84, dtype=torch.uint8, device="cuda")
+
+    def enc(kind):
+        if kind == "gate" or kind == "up":
+            src, out = (gate, out_g) if kind == "gate" else (up, out_u)
+            ds4.quantize(ds4.IQ2_XXS, src.data_ptr(), n, I, H, imp_gu.data_ptr(), H,
+                         grid.data_ptr(), qmap.data_ptr(), out.data_ptr(), ws.data_ptr(), 256, st)
+        else:
+            ds4.quantize(ds4.Q2_K, down.data_ptr(), n, H, I, imp_dn.data_ptr(), I, None, None,
+                         out_d.data_ptr(), ws.data_ptr(), 256, st)
+
+    def step():
+        for k in ("gate", "up", "down"):
+            enc(k)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert ds4.check(ws.data_ptr(), st) == 0
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert ds4.check(ws.data_ptr(), st) == 0
+    # per-kernel durations: events around each launch on the launch stream
+    kev = {k: [] for k in ("gate", "up", "down")}
+    for _ in range(max(2, args.steps // 2)):
+        for k in kev:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            enc(k)
+            b.record()
+            kev[k].append((a, b))
+    torch.cuda.synchronize()
+    k_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in kev.items()}
+    log("kernel averages (ms):", k_ms)
+    vals = 3 * n * I * H
+    groups = n * I * H // 32                       # per IQ2_XXS matrix
+    iq2_ops = groups * ENC_OPS_IQ2_GROUP
+    q2_ops = (n * H * I // 16) * ENC_OPS_Q2K_SUB
+    iq2_ms = (k_ms["gate"] + k_ms["up"]) / 2
+    ach = iq2_ops / (iq2_ms * 1e-3)
+    res = {
+        "metric": "block encoder throughput (fp32 expert weights to IQ2_XXS / Q2_K blocks, "
+                  "importance-weighted)",
+        "value": round(vals / (ms * 1e-3 / args.steps) / 1e9, 4), "unit": "Gvalues/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "v4flash-expert-encode", "experts_per_step": n, "hidden": H,
+                   "inter": I, "gate_up": "IQ2_XXS", "down": "Q2_K",
+                   "importance": "per expert and column"},
+        "experts_per_s": round(n / (ms * 1e-3 / args.steps), 2),
+        "kernels_ms": {k: round(v, 4) for k, v in k_ms.items()},
+        "q2k_tops": round(q2_ops / (k_ms["down"] * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "alu", "kernel": "k_encode_iq2", "achieved": round(ach / 1e12, 3),
+                     "peak": round(PEAK_FP32_OPS / 1e12, 2), "unit": "Tops/s (fp32)",
+                     "frac": round(ach / PEAK_FP32_OPS, 4), "traffic": None,
+                     "ops_per_launch": iq2_ops},
+    }
+    if args.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_encode(args.cpu_sample)
+    return res
+
+
+def cpu_baseline_encode(n_rows):
+    """The oracle encoders on a bounded sample: n_rows rows of each matrix of
+    one expert (gate and up rows of 4096 values to IQ2_XXS, down rows of 2048
+    to Q2_K), scaled to values per second."""
+    import numpy as np
+
+    import ds4gen as g
+    import oracle
+
+    grid = g.grid(1)
+    m = oracle.iq2_map(grid)[2]
+    gu = g.normal(5, 50, 2 * n_rows * 4096, 0.0, 0.02, "f32").reshape(2, n_rows, 4096)
+    dn = g.normal(5, 51, n_rows * 2 * 2048, 0.0, 0.02, "f32").reshape(1, 2 * n_rows, 2048)
+    igu = (g.normal(5, 52, 4096, 0.0, 1.0, "f32") ** 2).astype(np.float32)
+    idn = (g.normal(5, 53, 2048, 0.0, 1.0, "f32") ** 2).astype(np.float32)
+    t0 = time.perf_counter()
+    oracle.quantize(oracle.IQ2_XXS, gu, igu, grid, map_raw=m)
+    oracle.quantize(oracle.Q2_K, dn, idn)
+    dt = time.perf_counter() - t0
+    vals = gu.size + dn.size
+    return {"value": round(vals / dt / 1e9, 6), "unit": "Gvalues/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "%d rows each of one expert's gate and up (IQ2_XXS) and %d rows of its down "
+                      "(Q2_K), with the workload's proportions of values" % (n_rows, 2 * n_rows)}
+
+
 def cpu_baseline_stack(w, n_layers):
     """The oracle on one decode step through a sample of n_layers layers
     (normalisation, routing, experts, residual), scaled to 43 layers: the
@@ -688,7 +825,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode-b1",
                     choices=["decode-b1", "stack-43", "stack-43-q4k", "decode-b8", "prefill-512",
-                             "decode-sweep"])
+                             "decode-sweep", "encode"])
+    ap.add_argument("--encode-experts", type=int, default=8,
+                    help="encode: experts quantised per step")
     ap.add_argument("--layer-copies", type=int, default=1,
                     help="rotate over this many independently seeded layers")
     ap.add_argument("--cpu-sample", type=int, default=None,
@@ -709,12 +848,15 @@ def main():
         sys.exit(2)
     stack = args.workload in ("stack-43", "stack-43-q4k")
     batched = args.workload in ("decode-b8", "prefill-512")
+    if args.workload == "encode":
+        args.steps = 10 if args.steps is None else args.steps
+        args.warmup = 2 if args.warmup is None else args.warmup
     if args.steps is None:
         args.steps = 256 if stack else 200 if batched else 50 if args.workload == "decode-sweep" else 2000
     if args.warmup is None:
         args.warmup = 8 if stack else 20 if batched else 5 if args.workload == "decode-sweep" else 200
     if args.cpu_sample is None:
-        args.cpu_sample = 6 if stack else 3
+        args.cpu_sample = 6 if stack else 8192 if args.workload == "encode" else 3
     import torch
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -734,6 +876,8 @@ def main():
         res = bench_batched(args, args.workload)
     elif args.workload == "decode-sweep":
         res = bench_sweep(args)
+    elif args.workload == "encode":
+        res = bench_encode(args)
     else:
         res = bench_decode_b1(args)
     print(json.dumps(res), flush=True)
