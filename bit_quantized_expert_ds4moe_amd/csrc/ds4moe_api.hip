@@ -455,14 +455,19 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     {
       ProfScope prof(DS4MOE_K_GATEUP, st, !b1);
       const bool iq2 = iq2_grouped_fast(g);
+      const bool q4k = q4k_grouped_gu(g);
       const bool q80 = sh && q80_shared_fast(g);
-      if (iq2 && !b1) {  // x in binary16; small items (at most one per expert) and the rest
+      if ((iq2 || q4k) && !b1) {  // x in binary16
         const size_t n8 = (size_t)T * g.H / 8;
         launch_k(k_x_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, g.x, n8,
                  at<uint16_t>(ws, L.x16), status);
+      }
+      if (iq2 && !b1) {  // small items (at most one per expert) and the rest
         launch_k(k_grouped_gateup_iq2_small, dim3(g.I / kGNF, E < TK ? E : TK), dim3(kGW * 64), 0, st, g);
         launch_k(k_grouped_gateup_iq2<4>, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
       }
+      if (q4k && !b1)
+        launch_k(k_grouped_gateup_q4k, dim3((g.I + kNT - 1) / kNT, mi), dim3(256), 0, st, g);
       if (q80) {
         launch_k(k_grouped_gateup_q80, dim3(g.sh_I / kGNF, mi, g.ksplit_g), dim3(kGW * 64), 0, st, g);
         if (g.ksplit_g > 1)
@@ -470,7 +475,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       } else {
         g.ksplit_g = 1;
       }
-      if ((!iq2 && !b1) || (sh && !q80))
+      if ((!iq2 && !q4k && !b1) || (sh && !q80))
         launch_k(k_grouped_gateup, dim3((imax + kNT - 1) / kNT, mi), dim3(256), 0, st, g);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;

@@ -287,6 +287,44 @@ __host__ __device__ inline bool q80_shared_fast(const GroupArgs& a) {
   return a.sh_qt_g == DS4MOE_Q8_0 && a.sh_qt_u == DS4MOE_Q8_0 && a.sh_I % kGNF == 0 && a.H % 64 == 0;
 }
 
+// ---------------------------------------------------------------------------
+// Q4_K experts (the mixed stacks' Q4 layers) on the grouped path.  Block:
+// fp16 d, fp16 dmin, twelve bytes of 6-bit scales sc_j and mins m_j of the
+// eight 32-column groups, 128 code bytes (byte 16 + 32c + l: column 64c + l
+// in the low nibble, 64c + 32 + l in the high one); value = d sc_j q -
+// dmin m_j.  A lane quarter q takes the 8 columns 32j + 8q .. +7 of group j:
+// 8 consecutive code bytes, each in the low (even j) or high (odd j) nibble.
+// Masked in place inside 16-bit lanes they are the binary16 subnormals
+// q 2^-24 (low) or 16 q 2^-24 (high), exact, and form the f16 B fragment; the
+// group factor d sc_j 2^24 (/16) multiplies that MFMA's result.  The mins
+// need the sum of A over each group: gate/up take it from one more MFMA
+// against a fragment of ones, down from the per-16-feature sums of h.
+// ---------------------------------------------------------------------------
+__device__ inline void q4k_scale_min(const uint4& hd, int j, int& sc, int& mn) {
+  if (j < 4) {
+    sc = (int)((hd.y >> (8 * j)) & 63u);
+    mn = (int)((hd.z >> (8 * j)) & 63u);
+  } else {
+    const int k = 8 * (j - 4);
+    sc = (int)(((hd.w >> k) & 15u) | (((hd.y >> (k + 6)) & 3u) << 4));
+    mn = (int)(((hd.w >> (k + 4)) & 15u) | (((hd.z >> (k + 6)) & 3u) << 4));
+  }
+}
+
+// the lane's 8 code bytes as four 16-bit-lane pairs (bytes 0,1 | 2,3 | 4,5 | 6,7)
+__device__ inline uint4 q4k_pairs(uint2 c) {
+  return make_uint4(vperm(0u, c.x, 0x0C010C00u), vperm(0u, c.x, 0x0C030C02u),
+                    vperm(0u, c.y, 0x0C010C00u), vperm(0u, c.y, 0x0C030C02u));
+}
+__device__ inline f16x8_t q4k_frag(const uint4& p, bool high) {
+  const uint32_t M = high ? 0x00F000F0u : 0x000F000Fu;
+  return __builtin_bit_cast(f16x8_t, make_uint4(p.x & M, p.y & M, p.z & M, p.w & M));
+}
+
+__host__ __device__ inline bool q4k_grouped_gu(const GroupArgs& a) {
+  return a.qt_g == DS4MOE_Q4_K && a.qt_u == DS4MOE_Q4_K;
+}
+
 // gate/up + SwiGLU for one work item and 64 intermediate features.
 // Grid (ceil(Imax/64), max_items), 256 threads; wave w owns features
 // n0 + 16w .. +15 (gate and up).  x tile staged in LDS per 128 columns with
@@ -303,7 +341,7 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
   const bool sh = e == a.E;
   // routed items with IQ2_XXS gate and up run in k_grouped_gateup_iq2, a
   // Q8_0 shared expert in k_grouped_gateup_q80
-  if (!sh && iq2_grouped_fast(a)) return;
+  if (!sh && (iq2_grouped_fast(a) || q4k_grouped_gu(a))) return;
   if (sh && q80_shared_fast(a)) return;
   const int I = sh ? a.sh_I : a.I;
   const int n0 = blockIdx.x * kNT;
@@ -1013,6 +1051,48 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
         t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, sh_lo[m * 4 + q]), bm, t, 0, 0, 0);
         acc[mt] -= mmult * t;
       }
+    } else if (qd == DS4MOE_Q4_K) {
+      // Q4_K: group j = 2c (low nibbles) and 2c + 1 (high) of code chunk c
+      const uint4 hd = *(const uint4*)blk;
+      const float d = f16_bits_to_f32(hd.x & 0xFFFFu), dmin = f16_bits_to_f32(hd.x >> 16);
+#pragma unroll 1
+      for (int c = 0; c < 4; c++) {
+        const uint4 pc = q4k_pairs(*(const uint2*)(blk + 16 + 32 * c + 8 * q));
+#pragma unroll
+        for (int hi = 0; hi < 2; hi++) {
+          const int j = 2 * c + hi;
+          int sc, mn;
+          q4k_scale_min(hd, j, sc, mn);
+          const float mult = d * (float)sc * (hi ? 1048576.0f : 16777216.0f);
+          const f16x8_t bf = q4k_frag(pc, hi);
+#pragma unroll
+          for (int mt = 0; mt < 4; mt++) {
+            if (mt >= mtiles) break;
+            const int m = 16 * mt + (lane & 15);
+            const f16x8_t fh = __builtin_bit_cast(f16x8_t, ah[m * 32 + ((4 * j + q) ^ (m & 15))]);
+            const f16x8_t fl = __builtin_bit_cast(f16x8_t, al[m * 32 + ((4 * j + q) ^ (m & 15))]);
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_f16(fh, bf, z, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_16x16x32_f16(fl, bf, t, 0, 0, 0);
+            acc[mt] += mult * t;
+          }
+        }
+      }
+      // mins: the 16-feature sums j' = 4q .. 4q+3 belong to groups 2q, 2q+1
+      int sc0, m0, m1;
+      q4k_scale_min(hd, 2 * q, sc0, m0);
+      q4k_scale_min(hd, 2 * q + 1, sc0, m1);
+      const uint32_t f0 = f32_to_f16_bits((float)m0), f1 = f32_to_f16_bits((float)m1);
+      const f16x4_t bm = __builtin_bit_cast(f16x4_t, make_uint2(f0 | (f0 << 16), f1 | (f1 << 16)));
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) {
+        if (mt >= mtiles) break;
+        const int m = 16 * mt + (lane & 15);
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, sh_hi[m * 4 + q]), bm, z, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, sh_lo[m * 4 + q]), bm, t, 0, 0, 0);
+        acc[mt] -= dmin * t;
+      }
     } else {
       // Q8_0 (shared expert): 32-value blocks, f16 MFMA 16x16x32
 #pragma unroll 1
@@ -1340,12 +1420,94 @@ __global__ __launch_bounds__(256) void k_imatrix(ImxArgs a) {
 // The grouped kernels need bf16 x, 256-multiple shapes and formats they know
 // (any token count: at one token they run the shared expert after the
 // streaming matvec kernels).
+// gate/up + SwiGLU for routed items with Q4_K gate and up.  Grid
+// (I / 64, items), 256 threads; wave w owns features n0 + 16w .. +15.  K
+// runs in 128-column stages (half a block, four groups); a stage's weights
+// (the block header and the code bytes of its two chunk pairs) are requested
+// before its x tile (binary16, staged in LDS with the swizzle of
+// k_grouped_gateup) is written, so the two loads overlap.
+__global__ __launch_bounds__(256) void k_grouped_gateup_q4k(GroupArgs a) {
+  __shared__ uint4 xt[kMC * 16];
+  __shared__ int tok[kMC];
+  const int item = blockIdx.y;
+  if (item >= *a.n_items) return;
+  const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
+  if (e == a.E) return;  // the shared expert runs in its own kernels
+  const int n0 = blockIdx.x * kNT;
+  if (n0 >= a.I) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = lane >> 4;
+  const int n = n0 + 16 * w + (lane & 15);
+  const int nb = a.H / 256;
+  if (tid < kMC) tok[tid] = tid < nrows ? row_token(a, row0 + tid) : -1;
+  const size_t rowg = (size_t)e * a.I + n;
+  const uint8_t* G = a.gate + rowg * nb * kQ4kBytes;
+  const uint8_t* U = a.up + rowg * nb * kQ4kBytes;
+  const int mtiles = (nrows + 15) >> 4;
+  f32x4_t accg[4], accu[4];
+  for (int mt = 0; mt < 4; mt++) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const f16x8_t ones = __builtin_bit_cast(f16x8_t, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
+  __syncthreads();
+  for (int kh = 0; kh < 2 * nb; kh++) {
+    const int kb = kh >> 1, hf = kh & 1;
+    const uint8_t* bg = G + kb * kQ4kBytes;
+    const uint8_t* bu = U + kb * kQ4kBytes;
+    const uint4 hg = *(const uint4*)bg, hu = *(const uint4*)bu;
+    uint2 cg[2], cu[2];
+#pragma unroll
+    for (int c = 0; c < 2; c++) {  // code chunk 2hf + c: groups 4hf + 2c (low), + 1 (high)
+      cg[c] = *(const uint2*)(bg + 16 + 32 * (2 * hf + c) + 8 * q);
+      cu[c] = *(const uint2*)(bu + 16 + 32 * (2 * hf + c) + 8 * q);
+    }
+    for (int c = tid; c < kMC * 16; c += 256) {
+      const int m = c >> 4, ch = c & 15;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (m < nrows) v = ((const uint4*)(a.x16 + (size_t)tok[m] * a.H + 128 * kh))[ch];
+      xt[m * 16 + (ch ^ (m & 15))] = v;
+    }
+    __syncthreads();
+    const float dg = f16_bits_to_f32(hg.x & 0xFFFFu), mg = f16_bits_to_f32(hg.x >> 16);
+    const float du = f16_bits_to_f32(hu.x & 0xFFFFu), mu = f16_bits_to_f32(hu.x >> 16);
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      const uint4 pg = q4k_pairs(cg[c]), pu = q4k_pairs(cu[c]);
+#pragma unroll
+      for (int hi = 0; hi < 2; hi++) {
+        const int gi = 2 * c + hi, j = 4 * hf + gi;
+        int scg, mng, scu, mnu;
+        q4k_scale_min(hg, j, scg, mng);
+        q4k_scale_min(hu, j, scu, mnu);
+        const float unit = hi ? 1048576.0f : 16777216.0f;  // 2^24 / 16^hi
+        const float sgm = dg * (float)scg * unit, sgn = mg * (float)mng;
+        const float sum = du * (float)scu * unit, sun = mu * (float)mnu;
+        const f16x8_t fg = q4k_frag(pg, hi), fu = q4k_frag(pu, hi);
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+          if (mt >= mtiles) break;
+          const int m = 16 * mt + (lane & 15);
+          const f16x8_t af = __builtin_bit_cast(f16x8_t, xt[m * 16 + ((4 * gi + q) ^ (m & 15))]);
+          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+          const f32x4_t tg = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fg, z, 0, 0, 0);
+          const f32x4_t tu = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fu, z, 0, 0, 0);
+          const f32x4_t t1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, ones, z, 0, 0, 0);
+          accg[mt] += sgm * tg - sgn * t1;
+          accu[mt] += sum * tu - sun * t1;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu);
+}
+
 inline bool grouped_eligible(const ds4moe_shape& s, const ds4moe_experts& ex,
                              const ds4moe_experts* sh, const void* x, int32_t x_dt, int32_t T) {
   auto gu_ok = [](int qt) { return qt == DS4MOE_IQ2_XXS || qt == DS4MOE_Q8_0; };
-  auto dn_ok = [](int qt) { return qt == DS4MOE_Q2_K || qt == DS4MOE_Q8_0; };
+  auto dn_ok = [](int qt) { return qt == DS4MOE_Q2_K || qt == DS4MOE_Q8_0 || qt == DS4MOE_Q4_K; };
   if (x_dt != DS4MOE_BF16 || ((uintptr_t)x % 16) != 0 || s.hidden % 256 || ex.inter % 256) return false;
-  if (!gu_ok(ex.gate_qtype) || !gu_ok(ex.up_qtype) || !dn_ok(ex.down_qtype)) return false;
+  // routed gate/up: IQ2_XXS or Q8_0 each, or both Q4_K
+  const bool gu_q4k = ex.gate_qtype == DS4MOE_Q4_K && ex.up_qtype == DS4MOE_Q4_K;
+  if ((!gu_q4k && (!gu_ok(ex.gate_qtype) || !gu_ok(ex.up_qtype))) || !dn_ok(ex.down_qtype))
+    return false;
   if (((uintptr_t)ex.gate | (uintptr_t)ex.up | (uintptr_t)ex.down) % 16) return false;
   if (sh) {
     if (!gu_ok(sh->gate_qtype) || !gu_ok(sh->up_qtype) || !dn_ok(sh->down_qtype)) return false;

@@ -534,18 +534,24 @@ def test_imatrix_grouped_path():
 # --------------------------------------------------------------------------
 # Q4_K experts (generic kernels)
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("T", [1, 5])
+@pytest.mark.parametrize("T", [1, 5, 40, 512])
 def test_ffn_q4k_experts(T):
-    # V4-Flash expert shape with gate/up/down all in Q4_K, learned routing;
-    # and the mixed form of the q2/Q4 stacks (IQ2_XXS gate/up, Q4_K down)
+    # V4-Flash expert shape with gate/up/down all in Q4_K, and the mixed form
+    # (IQ2_XXS gate/up, Q4_K down): the matvec kernels at 1 and 5 tokens
+    # (learned routing), the grouped MFMA kernels at 40 (learned routing) and
+    # 512 (Zipf-routed prefill, outputs of the first and last tokens and of
+    # tokens on the most and least loaded experts)
     for qts in ((g.Q4_K, g.Q4_K, g.Q4_K), (g.IQ2_XXS, g.IQ2_XXS, g.Q4_K)):
         w = g.Workload("q4k", 31, T, 4096, 2048, 256, 6, *qts, "bf16", "f16")
         say("ffn q4k", qts, "T", T)
         from ds4gen.device import make_layer, host_experts
         lt = make_layer(w, 0)
         x = g.activations(w, n_tok=T)
-        ids, wts, _, _ = oracle.route(x, x_fmt(w), g.router_weight(w, 0), w.router_fmt,
-                                      g.router_bias(w, 0), w.K)
+        if T == 512:
+            ids, wts = g.zipf_routing(31, T, w.E, w.K)
+        else:
+            ids, wts, _, _ = oracle.route(x, x_fmt(w), g.router_weight(w, 0), w.router_fmt,
+                                          g.router_bias(w, 0), w.K)
         shp = shape_of(w)
         ws, nb = workspace(shp, T)
         out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
@@ -553,7 +559,14 @@ def test_ffn_q4k_experts(T):
         ds4.expert_ffn(shp, experts_of(lt, w), None, ptr(xd), x_dtype(w), T, ptr(idd), ptr(wd),
                        ptr(out), None, ptr(ws), nb, stream())
         check_clean(ws)
-        toks = np.arange(min(T, 2))
+        if T <= 5:
+            toks = np.arange(min(T, 2))
+        else:
+            counts = np.bincount(ids.ravel(), minlength=w.E)
+            heavy = int(np.argmax(counts))
+            light = [e for e in np.argsort(counts) if counts[e] > 0][0]
+            toks = np.unique([0, T - 1, int(np.where((ids == heavy).any(1))[0][0]),
+                              int(np.where((ids == light).any(1))[0][0])])
         want = oracle.moe_ffn(x, "bf16", ids, wts, host_experts(w, 0, np.unique(ids[toks])), qts,
                               w.H, w.I, w.E, grid=g.grid(w.seed), tokens=toks)
         err = max_rel_err(out.cpu().numpy()[toks], want)
