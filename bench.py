@@ -13,7 +13,8 @@ Other workloads (--workload): decode-b8 (8 correlated tokens + Q8_0 shared
 expert), prefill-512 (Zipf-routed 512-token chunk), stack-43 (43-layer
 decode stack, hash routing in layers 0-2), stack-43-q4k (the same stack with
 Q4_K routed experts in layers 37-42), decode-sweep (the decode-b8 layer at 1
-to 64 tokens per call), encode (fp32 experts to IQ2_XXS / Q2_K blocks).
+to 64 tokens per call), prefill-512-q4k (the prefill chunk through a layer
+with Q4_K experts), encode (fp32 experts to IQ2_XXS / Q2_K blocks).
 """
 import argparse
 import json
@@ -366,8 +367,11 @@ def bench_batched(args, which):
     import ds4gen as g
     from ds4gen.device import make_layer, to_dev
 
-    prefill = which == "prefill-512"
+    prefill = which.startswith("prefill-512")
     w = g.WORKLOADS[3 if prefill else 2]
+    if which == "prefill-512-q4k":  # a Q4 layer of the mixed stacks
+        from dataclasses import replace
+        w = replace(w, name=w.name + "-q4k", gate_qt=g.Q4_K, up_qt=g.Q4_K, down_qt=g.Q4_K)
     T = w.T
     log("building layer tensors (%s)" % w.name)
     lt = make_layer(w, 0)
@@ -490,7 +494,10 @@ def bench_batched(args, which):
         "mfma_tflops": round(flops / sec / 1e12, 2),
         "mfma_frac": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
-        "roofline": {"bound": "hbm", "kernel": ("grouped IQ2_XXS gate/up: k_x_to_f16 + k_grouped_gateup_iq2_small + k_grouped_gateup_iq2<4>" if prefill else "k_gateup_b1"),
+        "roofline": {"bound": "hbm", "kernel": (("grouped Q4_K gate/up: k_x_to_f16 + k_grouped_gateup_q4k"
+                                                 if w.gate_qt == g.Q4_K else
+                                                 "grouped IQ2_XXS gate/up: k_x_to_f16 + k_grouped_gateup_iq2_small + k_grouped_gateup_iq2<4>")
+                                                if prefill else "k_gateup_b1"),
                      "achieved": round(gu_bytes / gu_s / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gu_bytes / gu_s / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": None, "bytes_per_launch": int(gu_bytes),
@@ -825,7 +832,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode-b1",
                     choices=["decode-b1", "stack-43", "stack-43-q4k", "decode-b8", "prefill-512",
-                             "decode-sweep", "encode"])
+                             "prefill-512-q4k", "decode-sweep", "encode"])
     ap.add_argument("--encode-experts", type=int, default=8,
                     help="encode: experts quantised per step")
     ap.add_argument("--layer-copies", type=int, default=1,
@@ -847,7 +854,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     stack = args.workload in ("stack-43", "stack-43-q4k")
-    batched = args.workload in ("decode-b8", "prefill-512")
+    batched = args.workload in ("decode-b8", "prefill-512", "prefill-512-q4k")
     if args.workload == "encode":
         args.steps = 10 if args.steps is None else args.steps
         args.warmup = 2 if args.warmup is None else args.warmup
@@ -872,7 +879,7 @@ def main():
         del src, dst
     if stack:
         res = bench_stack(args, mixed=args.workload == "stack-43-q4k")
-    elif args.workload in ("decode-b8", "prefill-512"):
+    elif batched:
         res = bench_batched(args, args.workload)
     elif args.workload == "decode-sweep":
         res = bench_sweep(args)
