@@ -971,6 +971,16 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
   // K share (shared-expert split, a.ksplit_d blocks along z)
   const int ks = shr ? a.ksplit_d : 1, nbs = nb / ks, kb0 = blockIdx.z * nbs;
   for (int kb = kb0; kb < kb0 + nbs; kb++) {
+    // Q4_K: the block's header and the lane's code bytes are requested before
+    // the h tile is staged, so that the two loads overlap
+    uint4 q4h = make_uint4(0, 0, 0, 0);
+    uint2 q4c[4] = {};
+    if (qd == DS4MOE_Q4_K) {
+      const uint8_t* qb = D + (rowd * nb + kb) * bbd;
+      q4h = *(const uint4*)qb;
+#pragma unroll
+      for (int c = 0; c < 4; c++) q4c[c] = *(const uint2*)(qb + 16 + 32 * c + 8 * q);
+    }
     // stage: thread -> (row m, 16-column sub-block j): 16 values, high and low parts
     for (int c = tid; c < kMC * 16; c += 256) {
       const int m = c >> 4, j = c & 15;
@@ -1053,11 +1063,11 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
       }
     } else if (qd == DS4MOE_Q4_K) {
       // Q4_K: group j = 2c (low nibbles) and 2c + 1 (high) of code chunk c
-      const uint4 hd = *(const uint4*)blk;
+      const uint4 hd = q4h;
       const float d = f16_bits_to_f32(hd.x & 0xFFFFu), dmin = f16_bits_to_f32(hd.x >> 16);
-#pragma unroll 1
+#pragma unroll
       for (int c = 0; c < 4; c++) {
-        const uint4 pc = q4k_pairs(*(const uint2*)(blk + 16 + 32 * c + 8 * q));
+        const uint4 pc = q4k_pairs(q4c[c]);
 #pragma unroll
         for (int hi = 0; hi < 2; hi++) {
           const int j = 2 * c + hi;
