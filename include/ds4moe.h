@@ -154,8 +154,10 @@ ds4moe_status ds4moe_permute(const ds4moe_shape* shape, const int32_t* expert_id
  *   out[t] = sum_k weights[t][k] * E_{expert_ids[t][k]}(x[t])  + shared(x[t])
  * x: [n_tok][hidden] BF16 or F32; out: fp32 [n_tok][hidden].  `shared` may
  * be NULL.  Accumulation is fp32: dot products of exact products (decode
- * paths, up to 13 tokens with the V4-Flash shape and formats) or MFMAs on
- * exact binary16/bf16 operands (grouped path, more tokens).  The permutation
+ * paths, up to 13 tokens with the V4-Flash shape and formats: IQ2_XXS or
+ * Q4_K gate/up, Q2_K or Q4_K down) or MFMAs on exact binary16/bf16 operands
+ * (grouped path, more tokens; gate/up IQ2_XXS, Q8_0 or both Q4_K, down Q2_K,
+ * Q8_0 or Q4_K); other combinations run on scalar kernels.  The permutation
  * used for n_tok > 1 may be captured: perm_dbg (nullable) receives
  * offsets[n_expert+1], perm[n_tok*top_k], inv[n_tok*top_k] (int32).
  */
