@@ -23,6 +23,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Few-token calls use the streaming matvec kernels: each token reads its six
 // experts, which beats the grouped kernels' one read per distinct expert up to
 // about 13 tokens of correlated decode (measured crossover 12..16 tokens).
+constexpr int kFuseSelMaxTokens = 4;  // layer calls: selection fused into gate/up up to here
 constexpr int kB1MaxTokens = 13;
 constexpr int kSharedSplitG = 16;  // K shares of a shared expert's gate/up in calls of few tokens (<= kMaxSplit)
 constexpr int kSharedSplitD = 4;   // and of its down
@@ -282,9 +283,9 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
     ProfScope prof(DS4MOE_K_GATEUP, st);
     const bool q4 = ex.gate_qtype == DS4MOE_Q4_K;
     if (kbuf && q4)
-      launch_k(k_gateup_q4k_b1<true>, dim3(kGuBlocks, 1), dim3(kGuWaves * 64), 0, st, g);
+      launch_k(k_gateup_q4k_b1<true>, dim3(kGuBlocks, T), dim3(kGuWaves * 64), 0, st, g);
     else if (kbuf)
-      launch_k(k_gateup_b1<true>, dim3(kGuBlocks, 1), dim3(kGuWaves * 64), 0, st, g);
+      launch_k(k_gateup_b1<true>, dim3(kGuBlocks, T), dim3(kGuWaves * 64), 0, st, g);
     else if (q4)
       launch_k(k_gateup_q4k_b1<false>, dim3(kGuBlocks, T), dim3(kGuWaves * 64), 0, st, g);
     else
@@ -295,7 +296,7 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   {
     ProfScope prof(DS4MOE_K_DOWN, st);
     launch_k(ex.down_qtype == DS4MOE_Q4_K ? k_down_q4k_b1 : k_down_q2k_b1,
-             dim3(kH / kDnBlockRows, kbuf ? 1 : T), dim3(kDnThreads), 0, st, h,
+             dim3(kH / kDnBlockRows, T), dim3(kDnThreads), 0, st, h,
              (const uint8_t*)ex.down, kbuf ? ids : ids_in, wts, s.n_expert, out, residual, status);
   }
   return launched();
@@ -369,11 +370,16 @@ ds4moe_status launch_imatrix(const ds4moe_shape& s, const ImxOut& o, const void*
 ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_experts* sh,
                      const void* x, int32_t x_dt, int32_t T, const int32_t* ids, const float* wts,
                      float* out, float* residual, int32_t* perm_dbg, void* ws, const Layout& L,
-                     hipStream_t st, const ImxOut* imx = nullptr) {
+                     hipStream_t st, const ImxOut* imx = nullptr, const float4* kbuf_sel = nullptr) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   const bool b1 = fast_b1(s, ex, x, x_dt, T) && (!sh || grouped_eligible(s, ex, sh, x, x_dt, T));
   if (b1) {
-    ds4moe_status rc = launch_b1(s, ex, x, T, ids, nullptr, nullptr, wts, out, residual, ws, L, st);
+    // kbuf_sel: the top-K selection runs inside the gate/up kernel, which
+    // writes ids and wts (workspace buffers then)
+    ds4moe_status rc =
+        kbuf_sel ? launch_b1(s, ex, x, T, nullptr, kbuf_sel, const_cast<int32_t*>(ids), wts, out,
+                             residual, ws, L, st)
+                 : launch_b1(s, ex, x, T, ids, nullptr, nullptr, wts, out, residual, ws, L, st);
     if (rc == DS4MOE_OK && perm_dbg)  // the few-token path needs no permutation: make it for the caller
       rc = permute_dbg(s, T, ids, perm_dbg, ws, L, st);
     // h: fp32 [T][6][I] by pair; the shared expert's rows below reuse its memory
@@ -703,20 +709,20 @@ DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_la
   }
   const void* fx = norm ? (const void*)xn : x;
   int32_t fdt = norm ? (int32_t)DS4MOE_BF16 : x_dtype;
-  // batch-1 fast path with a learned router: the top-6 selection runs inside
-  // the gate/up kernel (one kernel boundary fewer)
-  const bool fuse = !r.tid2eid && !sh && n_tok == 1 &&
-                    fast_b1(*shape, desc->routed, norm ? (const void*)xn : x, fdt, n_tok);
+  // few-token path with a learned router, up to kFuseSelMaxTokens tokens: the
+  // top-6 selection of each token runs inside the gate/up kernel (one kernel
+  // boundary fewer; with more tokens every round of gate/up blocks would pay
+  // the selection's latency, which costs what the boundary saves)
+  const bool fuse = !r.tid2eid && n_tok <= kFuseSelMaxTokens &&
+                    fast_b1(*shape, desc->routed, fx, fdt, n_tok) &&
+                    (!sh || grouped_eligible(*shape, desc->routed, sh, fx, fdt, n_tok));
   rc = do_route(*shape, r, x, x_dtype, norm ? residual : nullptr, norm ? desc->norm_w : nullptr,
                 desc->norm_eps, norm ? xn : nullptr, n_tok, token_ids, ids, wts, ws, L, stream,
                 !fuse);
   if (rc != DS4MOE_OK) return rc;
-  if (fuse)
-    rc = launch_b1(*shape, desc->routed, fx, 1, nullptr, at<float4>(ws, L.kbuf), ids, wts,
-                   norm ? nullptr : out, norm ? residual : nullptr, ws, L, stream);
-  else
-    rc = do_ffn(*shape, desc->routed, sh, fx, fdt, n_tok, ids, wts, norm ? nullptr : out,
-                norm ? residual : nullptr, nullptr, ws, L, stream);
+  rc = do_ffn(*shape, desc->routed, sh, fx, fdt, n_tok, ids, wts, norm ? nullptr : out,
+              norm ? residual : nullptr, nullptr, ws, L, stream, nullptr,
+              fuse ? at<float4>(ws, L.kbuf) : nullptr);
   if (rc != DS4MOE_OK) return rc;
   if (ids_dbg &&
       hipMemcpyAsync(ids_dbg, ids, sizeof(int32_t) * n_tok * shape->top_k, hipMemcpyDeviceToDevice,

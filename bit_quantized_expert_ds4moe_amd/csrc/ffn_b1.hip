@@ -280,13 +280,13 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
   if (SEL && w == 0) {
     int e;
     float g;
-    const bool first = blockIdx.x == 0 && blockIdx.y == 0;
-    select_wave(a.kbuf, a.E, 6, a.scale, a.status, first, e, g);
+    const bool first = blockIdx.x == 0;  // one reporter per token
+    select_wave(a.kbuf + (size_t)blockIdx.y * a.E, a.E, 6, a.scale, a.status, first, e, g);
     if (lane < 6) {
       sel_e[lane] = e;
       if (first) {
-        a.ids_out[lane] = e;
-        a.wts_out[lane] = g;
+        a.ids_out[6 * blockIdx.y + lane] = e;
+        a.wts_out[6 * blockIdx.y + lane] = g;
       }
     }
   } else if (t >= 0 && t < 256) {

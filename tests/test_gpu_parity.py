@@ -284,14 +284,29 @@ MIXED_LAYER = g.Workload("v4flash-layer-iq2-q4k-down", 34, 1, 4096, 2048, 256, 6
                          g.IQ2_XXS, g.Q4_K, "bf16", "f16")
 
 
-@pytest.mark.parametrize("widx", [0, 1, "q4k", "mixed"])
+def _layer_workload(widx):
+    from dataclasses import replace
+    if widx == "q4k":
+        return Q4_LAYER
+    if widx == "mixed":
+        return MIXED_LAYER
+    if widx == "q4k-t3":
+        return replace(Q4_LAYER, T=3)
+    if isinstance(widx, str) and widx.startswith("b8-t"):
+        return replace(g.WORKLOADS[2], T=int(widx[4:]))
+    return g.WORKLOADS[widx]
+
+
+@pytest.mark.parametrize("widx", [0, 1, "q4k", "mixed", "q4k-t3", 2, "b8-t2", "b8-t13", "b8-t14"])
 def test_layer_route_and_ffn(widx):
-    # configs 0 and 1; the config-1 layer with Q4_K experts (the fast path's
-    # Q4_K kernels, selection fused into gate/up) and with IQ2_XXS gate/up and
-    # Q4_K down
-    from ds4gen.device import make_layer, host_experts
-    w = {"q4k": Q4_LAYER, "mixed": MIXED_LAYER}.get(widx) or g.WORKLOADS[widx]
-    say("layer", w.name)
+    # configs 0, 1 and 2; the config-1 layer with Q4_K experts (1 and 3
+    # tokens) and with IQ2_XXS gate/up and Q4_K down; config 2 (Q8_0 shared
+    # expert) at 2 tokens (few-token kernels, the top-6 selection of each
+    # token fused into gate/up), 8 and 13 (few-token kernels, selection
+    # kernel) and 14 (grouped kernels)
+    from ds4gen.device import make_layer, host_experts, host_shared
+    w = _layer_workload(widx)
+    say("layer", w.name, "T", w.T)
     T = w.T
     lt = make_layer(w, 0)
     x = g.activations(w, n_tok=T)
@@ -299,7 +314,7 @@ def test_layer_route_and_ffn(widx):
     ws, nb = workspace(shp, T)
     wdt = ds4.F32 if w.router_fmt == "f32" else ds4.F16
     d = ds4.layer_desc(ds4.router(w=ptr(lt.router_w), w_dtype=wdt, bias=ptr(lt.bias)),
-                       experts_of(lt, w))
+                       experts_of(lt, w), shared=shared_of(lt, w))
     out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
     ids = torch.empty((T, w.K), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, w.K), dtype=torch.float32, device="cuda")
@@ -310,8 +325,10 @@ def test_layer_route_and_ffn(widx):
     oids, owts, _, _ = oracle.route(x, x_fmt(w), g.router_weight(w, 0), w.router_fmt,
                                     g.router_bias(w, 0), w.K)
     np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    np.testing.assert_allclose(wts.cpu().numpy(), owts, rtol=2e-6)
     want = oracle.moe_ffn(x, x_fmt(w), oids, owts, host_experts(w, 0, np.unique(oids)),
-                          (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed))
+                          (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed),
+                          shared=host_shared(w, 0) if w.shared else None, sh_I=w.I)
     err = max_rel_err(out.cpu().numpy(), want)
     say("  max|err|/rms =", err)
     assert err <= TOL_FP32
