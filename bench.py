@@ -38,22 +38,20 @@ GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "eccfd29fc254cbdd4edd47399d496d5fe3cbfd392ee8d2bb341caa851d1c7f91",
-    "bytes": 26272900,
+    "sha256": "af69b5bb30d55ba6d0fa81f635f975e135fdf840db156fd0ae5d7f4455e5f30e",
+    "bytes": 26273738,
 }
 
 
-# The same for the Q4_K gate/up kernel of the mixed stack (summary in
-# profiles/stack43_q4k_hbm_traffic.txt): FETCH_SIZE 27,769.61 KiB x 1.99975
-# (the 256 MiB copy reads 131,088.44 KiB by that counter) + WRITE_SIZE
-# 53.26 KiB, per dispatch.
+# The same for the Q4_K gate/up kernel of the mixed stack (summary, with the
+# raw counters and the copy calibration, in profiles/stack43_q4k_hbm_traffic.txt).
 Q4K_GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_q4k.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "511c7290af6e9f08246069c74ecd3eb6f3e2507811157cd97bbb304f9994b085",
-    "bytes": 56919567,
+    "sha256": "1e9e597f49a1aba6133e49fa1c06968595395d9a88351d815608563d515e1cd1",
+    "bytes": 56915609,
 }
 
 
