@@ -8,6 +8,7 @@
 #include "route.hip"
 #include "ffn_b1.hip"
 #include "ffn_q4k.hip"
+#include "ffn_shared.hip"
 #include "ffn_generic.hip"
 #include "grouped.hip"
 #include "encode.hip"
@@ -23,6 +24,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Few-token calls use the streaming matvec kernels: each token reads its six
 // experts, which beats the grouped kernels' one read per distinct expert up to
 // about 13 tokens of correlated decode (measured crossover 12..16 tokens).
+constexpr int kSharedB1MaxTokens = 4;  // shared expert by per-token matvecs up to here
 constexpr int kFuseSelMaxTokens = 4;  // layer calls: selection fused into gate/up up to here
 constexpr int kB1MaxTokens = 13;
 constexpr int kSharedSplitG = 16;  // K shares of a shared expert's gate/up in calls of few tokens (<= kMaxSplit)
@@ -387,6 +389,22 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       rc = launch_imatrix(s, *imx, x, x_dt, T, ids, wts, at<float>(ws, L.h), s.inter, nullptr,
                           nullptr, false, ws, L, st);
     if (rc != DS4MOE_OK || !sh) return rc;
+    if (T <= kSharedB1MaxTokens && shared_b1_ok(s, *sh, x, x_dt)) {
+      // the shared expert as per-token matvecs (beyond a few tokens its
+      // weights are better read once by the grouped kernels)
+      ProfScope shared_only(DS4MOE_K_OTHER, st);
+      SharedB1Args sa{};
+      sa.x = (const uint16_t*)x;
+      sa.gate = (const uint8_t*)sh->gate;
+      sa.up = (const uint8_t*)sh->up;
+      sa.down = (const uint8_t*)sh->down;
+      sa.h = at<float>(ws, L.h) + (size_t)T * s.top_k * s.inter;  // after the routed rows
+      sa.out = residual ? residual : out;
+      sa.status = status;
+      launch_k(k_shared_gateup_q80_b1, dim3(kI / 8, T), dim3(256), 0, st, sa);
+      launch_k(k_shared_down_q80_b1, dim3(kH / 16, T), dim3(256), 0, st, sa);
+      return launched();
+    }
   }
   if (b1 || (T > 1 && grouped_eligible(s, ex, sh, x, x_dt, T))) {
     // after the few-token path, the shared expert's kernels time as one class

@@ -1,0 +1,155 @@
+// ffn_shared.hip -- the shared expert (Q8_0 gate, up and down with the
+// V4-Flash expert shape) in few-token calls: per-token matvecs that follow
+// the routed batch-1 kernels, one grid row per token.
+//
+// Method: FLOW = qiita.com/sukimaengineer/items/cd76fec76d49a098abed, section
+// "MoE FFN 部の中身" (an always-on shared expert whose output is added to
+// the routed weighted sum, unscaled).  Format: Q8_0, 34 bytes per 32 values
+// (fp16 d, then 32 int8 codes; y = d c), FLOW quantisation table.
+//
+// A lane covers 64 consecutive values of a row: two Q8_0 blocks, i.e. the 68
+// bytes at byte 68L of the row (4-byte aligned), read as 17 dwords.  Its
+// activations are held as 16-bit fixed point with one scale (q4k_fix: the
+// 16-bit pairs (4k, 4k+2) and (4k+1, 4k+3) of each half), and a code dword
+// XOR 0x80808080 holds the codes plus 128 as unsigned bytes, so the masks
+// 0x00FF00FF on it and on it shifted by 8 put them into 16-bit lanes in the
+// same pairs: v_dot2_i32_i16 multiplies them exactly, and 128 times the
+// half's fixed-point sum is taken off again.  Each block's d is applied once.
+#include "dev_common.h"
+
+namespace ds4 {
+
+constexpr int kShRowGu = kH / 32 * kQ80Bytes;  // 4352 bytes per gate/up row
+constexpr int kShRowDn = kI / 32 * kQ80Bytes;  // 2176 bytes per down row
+
+struct SharedB1Args {
+  const uint16_t* x;                 // [T][4096] bf16
+  const uint8_t *gate, *up, *down;   // Q8_0: [2048][4352 B], [2048][4352 B], [4096][2176 B]
+  float* h;                          // [T][2048] fp32 SwiGLU rows (workspace)
+  float* out;                        // [T][4096]: out (or the residual) += shared output
+  uint32_t* status;
+};
+
+__device__ inline void q80_pair_load(const uint8_t* p, uint32_t (&D)[17]) {
+  const uint32_t* q = (const uint32_t*)p;
+#pragma unroll
+  for (int j = 0; j < 17; j++) D[j] = q[j];
+}
+
+// Partial dot product of a lane's 64 values with its fixed-point activations
+// (before the lane's scale).  Block 0: d in bytes 0-1, codes in 2..33 (each
+// code dword straddles two loaded dwords); block 1: d in bytes 34-35, codes
+// in 36..67 (dwords 9..16).
+__device__ inline float q80_dot64(const uint32_t (&D)[17], const uint32_t* xl, const uint32_t* xh,
+                                  int sl, int sh) {
+  int a0 = 0, a1 = 0;  // |a| < 32 * 255 * 32767 < 2^31
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const uint32_t w0 = align_bytes(D[k + 1], D[k], 2) ^ 0x80808080u;
+    const uint32_t w1 = D[9 + k] ^ 0x80808080u;
+    a0 = sdot2(w0 & 0x00FF00FFu, xl[2 * k], a0);
+    a0 = sdot2((w0 >> 8) & 0x00FF00FFu, xl[2 * k + 1], a0);
+    a1 = sdot2(w1 & 0x00FF00FFu, xh[2 * k], a1);
+    a1 = sdot2((w1 >> 8) & 0x00FF00FFu, xh[2 * k + 1], a1);
+  }
+  const float d0 = f16_bits_to_f32(D[0] & 0xFFFFu), d1 = f16_bits_to_f32(D[8] >> 16);
+  return d0 * (float)(a0 - 128 * sl) + d1 * (float)(a1 - 128 * sh);
+}
+
+// gate/up + SwiGLU of the shared expert.  Grid (2048 / 8, T), 256 threads:
+// wave w of block b handles features 8b + 2w and 8b + 2w + 1 (their gate and
+// up rows) for token blockIdx.y.  The weights are requested right behind the
+// token's activations, before the fixed-point conversion.
+__global__ __launch_bounds__(256) void k_shared_gateup_q80_b1(SharedB1Args a) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = blockIdx.y;
+  const int f0 = 8 * blockIdx.x + 2 * w;
+  const uint4* xp = (const uint4*)(a.x + (size_t)t * kH + 64 * lane);
+  uint4 xq[8];
+#pragma unroll
+  for (int q = 0; q < 8; q++) xq[q] = xp[q];
+  uint32_t D[4][17];  // gate f0, gate f0+1, up f0, up f0+1
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const uint8_t* base = (r < 2 ? a.gate : a.up) + (size_t)(f0 + (r & 1)) * kShRowGu;
+    q80_pair_load(base + 68 * lane, D[r]);
+  }
+  auto xval = [&](int i) {
+    const uint4 q = xq[i >> 3];
+    const uint32_t ww = (i & 6) == 0 ? q.x : (i & 6) == 2 ? q.y : (i & 6) == 4 ? q.z : q.w;
+    return bf16_bits_to_f32((i & 1) ? (ww >> 16) : (ww & 0xFFFFu));
+  };
+  uint32_t xl[16], xh[16];
+  int sl, sh;
+  const float S = q4k_fix(xval, xl, xh, sl, sh);
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) v[r] = wave_sum(S * q80_dot64(D[r], xl, xh, sl, sh));
+  if (lane < 2) {
+    const float g = lane ? v[1] : v[0], u = lane ? v[3] : v[2];
+    a.h[(size_t)t * kI + f0 + lane] = silu(g) * u;
+  }
+}
+
+// down of the shared expert, added to the output.  Grid (4096 / 16, T), 256
+// threads: wave w of block b handles rows 16b + 4w .. +3, two at a time (wave
+// half u takes rows +u and +2+u); lane L of a half covers columns 64L .. +63.
+__global__ __launch_bounds__(256) void k_shared_down_q80_b1(SharedB1Args a) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int u = lane >> 5, L = lane & 31;
+  const int t = blockIdx.y;
+  const int r0 = 16 * blockIdx.x + 4 * w;
+  const float4* hp = (const float4*)(a.h + (size_t)t * kI + 64 * L);
+  float4 hv[16];
+#pragma unroll
+  for (int q = 0; q < 16; q++) hv[q] = hp[q];
+  uint32_t D0[17], D1[17];
+  q80_pair_load(a.down + (size_t)(r0 + u) * kShRowDn + 68 * L, D0);
+  q80_pair_load(a.down + (size_t)(r0 + 2 + u) * kShRowDn + 68 * L, D1);
+  float mx = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; q++)
+    mx = fmaxf(fmaxf(fmaxf(mx, fabsf(hv[q].x)), fmaxf(fabsf(hv[q].y), fabsf(hv[q].z))), fabsf(hv[q].w));
+  const bool h_bad = !(mx <= 3.0e38f);
+  auto hval = [&](int i) {
+    const float4 q = hv[i >> 2];
+    return (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
+  };
+  uint32_t xl[16], xh[16];
+  int sl, sh;
+  const float S = q4k_fix(hval, xl, xh, sl, sh);
+  float p0 = S * q80_dot64(D0, xl, xh, sl, sh), p1 = S * q80_dot64(D1, xl, xh, sl, sh);
+  // sums over each wave half: DPP inside rows of 16, then rows 0 + 1 and 2 + 3
+  p0 += dpp_f32<0xB1>(p0);
+  p0 += dpp_f32<0x4E>(p0);
+  p0 += dpp_f32<0x141>(p0);
+  p0 += dpp_f32<0x140>(p0);
+  p1 += dpp_f32<0xB1>(p1);
+  p1 += dpp_f32<0x4E>(p1);
+  p1 += dpp_f32<0x141>(p1);
+  p1 += dpp_f32<0x140>(p1);
+  auto rl = [](float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+  };
+  const float t0 = rl(p0, 0) + rl(p0, 16), t1 = rl(p0, 32) + rl(p0, 48);  // rows r0, r0 + 1
+  const float t2 = rl(p1, 0) + rl(p1, 16), t3 = rl(p1, 32) + rl(p1, 48);  // rows r0 + 2, r0 + 3
+  if (lane < 4) {
+    const float tot = lane == 0 ? t0 : lane == 1 ? t1 : lane == 2 ? t2 : t3;
+    a.out[(size_t)t * kH + r0 + lane] += tot;
+  }
+  if (h_bad && lane == 0) raise_fault(a.status, DS4MOE_FAULT_F16_RANGE);
+}
+
+// The few-token shared-expert kernels apply: Q8_0 gate, up and down of the
+// V4-Flash shape, bf16 activations, 4-byte-aligned weights.
+inline bool shared_b1_ok(const ds4moe_shape& s, const ds4moe_experts& sh, const void* x,
+                         int32_t x_dt) {
+  return sh.gate_qtype == DS4MOE_Q8_0 && sh.up_qtype == DS4MOE_Q8_0 &&
+         sh.down_qtype == DS4MOE_Q8_0 && sh.inter == kI && s.hidden == kH &&
+         x_dt == DS4MOE_BF16 && ((uintptr_t)x % 16) == 0 &&
+         (((uintptr_t)sh.gate | (uintptr_t)sh.up | (uintptr_t)sh.down) % 4) == 0;
+}
+
+}  // namespace ds4
