@@ -266,13 +266,48 @@ def test_ffn_v4_decode_b8_shared_q8():
     assert ffn_case(2, 8) <= TOL_FP32
 
 
-@pytest.mark.parametrize("T", [1, 17, 64])
+@pytest.mark.parametrize("T", [1, 4, 5, 17, 64])
 def test_ffn_v4_decode_batch_shared_split(T):
-    # one token (matvec kernels, then the shared expert alone through the
-    # grouped kernels) and just past the few-token path (routed experts
-    # through the grouped kernels too); the Q8_0 shared expert's single item
-    # is split along K (16 and 4 shares) and added after the routed part
+    # the Q8_0 shared expert as per-token matvecs after the routed matvec
+    # kernels (1 and 4 tokens), alone through the grouped kernels after them
+    # (5 tokens: its single item split along K, 16 and 4 shares), and just
+    # past the few-token path (routed experts through the grouped kernels too)
     assert ffn_case(2, T, tokens_for_oracle=sorted({0, T // 2, T - 1})) <= TOL_FP32
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_layer_norm_residual_with_shared_expert(T):
+    # a stack-style layer call (RMSNorm of the fp32 residual stream, learned
+    # routing, residual += output) with the Q8_0 shared expert: the shared
+    # matvec kernels add into the residual
+    from ds4gen.device import make_layer, host_experts, host_shared, step_inputs
+    from dataclasses import replace
+    w = replace(g.WORKLOADS[2], T=T)
+    say("layer norm + residual + shared T", T)
+    lt = make_layer(w, 0, norm=True)
+    h0, _ = step_inputs(w, T)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, T)
+    d = ds4.layer_desc(ds4.router(w=ptr(lt.router_w), w_dtype=ds4.F16, bias=ptr(lt.bias)),
+                       experts_of(lt, w), shared=shared_of(lt, w), norm_w=ptr(lt.norm_w),
+                       norm_eps=1e-6)
+    resid = dev(h0)
+    ids = torch.empty((T, w.K), dtype=torch.int32, device="cuda")
+    xn = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
+    ds4.layer(shp, d, None, ds4.BF16, ptr(resid), None, None, T, ptr(ids), None, ptr(xn), ptr(ws),
+              nb, stream())
+    check_clean(ws)
+    xo = oracle.rmsnorm_bf16(h0, g.norm_weight(w, 0), 1e-6)
+    np.testing.assert_array_equal(xn.cpu().numpy().view(np.uint16), xo)
+    oids, owts, _, _ = oracle.route(xo, "bf16", g.router_weight(w, 0), "f16", g.router_bias(w, 0),
+                                    w.K)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    y = oracle.moe_ffn(xo, "bf16", oids, owts, host_experts(w, 0, np.unique(oids)),
+                       (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed),
+                       shared=host_shared(w, 0), sh_I=w.I)
+    err = max_rel_err(resid.cpu().numpy() - h0, y)
+    say("  max|err|/rms = %g" % err)
+    assert err <= TOL_FP32
 
 
 # --------------------------------------------------------------------------
