@@ -75,6 +75,9 @@ __global__ __launch_bounds__(256) void k_shared_gateup_q80_b1(SharedB1Args a) {
     const uint8_t* base = (r < 2 ? a.gate : a.up) + (size_t)(f0 + (r & 1)) * kShRowGu;
     q80_pair_load(base + 68 * lane, D[r]);
   }
+  // keep every load ahead of the conversion (the scheduler would otherwise
+  // issue the weights only after the activations have returned)
+  __builtin_amdgcn_sched_barrier(0);
   auto xval = [&](int i) {
     const uint4 q = xq[i >> 3];
     const uint32_t ww = (i & 6) == 0 ? q.x : (i & 6) == 2 ? q.y : (i & 6) == 4 ? q.z : q.w;
@@ -108,6 +111,7 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_b1(SharedB1Args a) {
   uint32_t D0[17], D1[17];
   q80_pair_load(a.down + (size_t)(r0 + u) * kShRowDn + 68 * L, D0);
   q80_pair_load(a.down + (size_t)(r0 + 2 + u) * kShRowDn + 68 * L, D1);
+  __builtin_amdgcn_sched_barrier(0);  // all loads ahead of the conversion
   float mx = 0.0f;
 #pragma unroll
   for (int q = 0; q < 16; q++)
