@@ -12,7 +12,8 @@ region.  Prints one JSON line.
 Other workloads (--workload): decode-b8 (8 correlated tokens + Q8_0 shared
 expert), prefill-512 (Zipf-routed 512-token chunk), stack-43 (43-layer
 decode stack, hash routing in layers 0-2), stack-43-q4k (the same stack with
-Q4_K routed experts in layers 37-42), decode-sweep (the decode-b8 layer at 1
+Q4_K routed experts in layers 37-42), stack-43-shared (with the Q8_0 shared
+expert of every layer), decode-sweep (the decode-b8 layer at 1
 to 64 tokens per call), prefill-512-q4k (the prefill chunk through a layer
 with Q4_K experts), encode (fp32 experts to IQ2_XXS / Q2_K blocks).
 """
@@ -205,14 +206,19 @@ def stack_descs(ds4, w, layers):
             rt = ds4.router(tid2eid=lt.tid2eid.data_ptr(), vocab=w.vocab)
         else:
             rt = ds4.router(w=lt.router_w.data_ptr(), w_dtype=ds4.F16, bias=lt.bias.data_ptr())
-        descs.append(ds4.layer_desc(rt, ex, norm_w=lt.norm_w.data_ptr(), norm_eps=1e-6))
+        sh = None
+        if lt.shared is not None:
+            sh = ds4.experts(lt.shared[0].data_ptr(), lt.shared[1].data_ptr(),
+                             lt.shared[2].data_ptr(), w.I, (ds4.Q8_0, ds4.Q8_0, ds4.Q8_0))
+        descs.append(ds4.layer_desc(rt, ex, shared=sh, norm_w=lt.norm_w.data_ptr(), norm_eps=1e-6))
     return descs
 
 
-def bench_stack(args, mixed=False):
+def bench_stack(args, mixed=False, shared=False):
     """43-layer routed-expert stack at batch-1 decode: one step = one token
     through every layer (RMSNorm -> routing -> experts -> residual add).
-    mixed: the routed experts of layers 37-42 are Q4_K (gate, up and down)."""
+    mixed: the routed experts of layers 37-42 are Q4_K (gate, up and down);
+    shared: every layer also has its Q8_0 shared expert."""
     import numpy as np
     import torch
 
@@ -221,6 +227,9 @@ def bench_stack(args, mixed=False):
     from ds4gen.device import make_stack, step_inputs, to_dev
 
     w = g.WORKLOADS[5 if mixed else 4]
+    if shared:
+        from dataclasses import replace
+        w = replace(w, name=w.name + "-shared-q8", shared=True)
     log("generating %d layers x %d experts on the device" % (w.n_layers, w.E))
     t0 = time.perf_counter()
     layers = make_stack(w, log)
@@ -288,7 +297,7 @@ def bench_stack(args, mixed=False):
         torch.index_select(tok_all, 0, idx, out=tokbuf)
         for l, d in enumerate(descs):
             for c, k in classes.items():
-                if c == "other" and l >= w.n_hash:
+                if c == "other" and l >= w.n_hash and not w.shared:
                     ds4.profile_events(k, None, None)
                     continue
                 ds4.profile_events(k, handles[c][used[c]][0], handles[c][used[c]][1])
@@ -312,6 +321,8 @@ def bench_stack(args, mixed=False):
 
     # 1,826,095,104 per token (all q2); 2,080,899,072 with layers 37-42 in Q4_K
     expert_bytes = w.token_expert_bytes()
+    if w.shared:  # the Q8_0 shared expert of every layer
+        expert_bytes += w.n_layers * 3 * w.I * w.H // 32 * g.BLOCK_BYTES[g.Q8_0]
     gateup_bytes = w.K * 2 * w.blocks_per_expert["gate"] * g.BLOCK_BYTES[w.gate_qt]
     tok_s = args.steps / (ms * 1e-3)
     gbs = expert_bytes * tok_s / 1e9
@@ -323,7 +334,7 @@ def bench_stack(args, mixed=False):
         "data": "synthetic",
         "config": {"workload": w.name, "layers": w.n_layers, "hash_layers": w.n_hash,
                    "hidden": w.H, "inter": w.I, "experts": w.E, "top_k": w.K,
-                   "q4k_layers": list(w.q4_layers),
+                   "q4k_layers": list(w.q4_layers), "shared_q8_0": bool(w.shared),
                    "resident_expert_bytes": w.stack_expert_bytes(),
                    "timing": "hip-graph replay of one 43-layer step per token"},
         "expert_gbs": round(gbs, 1), "expert_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -749,7 +760,7 @@ def cpu_baseline_stack(w, n_layers):
     and then the first Q4_K layers, each kind scaled by its own layer count."""
     import ds4gen as g
     import oracle
-    from ds4gen.device import host_experts, step_inputs
+    from ds4gen.device import host_experts, host_shared, step_inputs
 
     h0, tok = step_inputs(w, 1)
     resid = h0.copy()
@@ -777,8 +788,9 @@ def cpu_baseline_stack(w, n_layers):
         t_total += time.perf_counter() - t0
         mats = host_experts(w, l, ids[0])
         t0 = time.perf_counter()
+        shm = host_shared(w, l) if w.shared else None
         y = oracle.moe_ffn(xn, "bf16", ids, wts, mats, (wl.gate_qt, wl.up_qt, wl.down_qt), w.H,
-                           w.I, w.E, grid=grid)
+                           w.I, w.E, grid=grid, shared=shm, sh_I=w.I)
         resid = oracle.residual_add(resid, y)
         t_total += time.perf_counter() - t0
         t_kind.setdefault(l in w.q4_layers, []).append(t_total)
@@ -829,7 +841,8 @@ def main():
                     help="timed steps (default 2000 tokens for decode-b1, 256 for stack-43)")
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode-b1",
-                    choices=["decode-b1", "stack-43", "stack-43-q4k", "decode-b8", "prefill-512",
+                    choices=["decode-b1", "stack-43", "stack-43-q4k", "stack-43-shared", "decode-b8",
+                             "prefill-512",
                              "prefill-512-q4k", "decode-sweep", "encode"])
     ap.add_argument("--encode-experts", type=int, default=8,
                     help="encode: experts quantised per step")
@@ -851,7 +864,7 @@ def main():
               "intermediate rows across GPUs but no multi-GPU run is implemented (--gpus 1).",
               file=sys.stderr)
         sys.exit(2)
-    stack = args.workload in ("stack-43", "stack-43-q4k")
+    stack = args.workload in ("stack-43", "stack-43-q4k", "stack-43-shared")
     batched = args.workload in ("decode-b8", "prefill-512", "prefill-512-q4k")
     if args.workload == "encode":
         args.steps = 10 if args.steps is None else args.steps
@@ -876,7 +889,8 @@ def main():
         log("copy calibration: %d bytes read, %d written" % (n, n))
         del src, dst
     if stack:
-        res = bench_stack(args, mixed=args.workload == "stack-43-q4k")
+        res = bench_stack(args, mixed=args.workload == "stack-43-q4k",
+                          shared=args.workload == "stack-43-shared")
     elif batched:
         res = bench_batched(args, args.workload)
     elif args.workload == "decode-sweep":
