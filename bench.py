@@ -39,7 +39,7 @@ GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "af69b5bb30d55ba6d0fa81f635f975e135fdf840db156fd0ae5d7f4455e5f30e",
+    "sha256": "5ddf38c1fb193aba661a6deaff254006c0cf926dfd0f69a67cc5617bd9a27135",
     "bytes": 26273738,
 }
 
@@ -51,7 +51,7 @@ Q4K_GATEUP_TRAFFIC = {
                 "bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "1e9e597f49a1aba6133e49fa1c06968595395d9a88351d815608563d515e1cd1",
+    "sha256": "578c30b5459941dbaab52e108f857136f3264322425426d0008b4df7a9ac9b34",
     "bytes": 56915609,
 }
 

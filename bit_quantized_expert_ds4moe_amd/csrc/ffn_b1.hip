@@ -214,13 +214,14 @@ __device__ inline void store_copies(uint8_t* tab, int entry, uint4 v) {
     *(uint4*)(tab + (entry << 8) + (((j + entry) & 15) << 4)) = v;
 }
 
-// gate/up + SwiGLU for one token.  Grid 256 workgroups of 16 waves; wave w of
-// workgroup g handles flattened rows 3u .. 3u+2, u = 16g + w, of the six
-// routed slots (row r of slot k is flattened row 2048k + r), gate and up.
-// With SEL the workgroup first picks the top-6 experts from the router's key
-// intervals (wave 0, while the other waves build the tables and stage x);
-// workgroup 0 publishes ids and gates for the down kernel.  Without SEL the
-// weight loads are issued before the tables are built.
+// gate/up + SwiGLU, one grid row of 256 workgroups of 16 waves per token
+// (blockIdx.y); wave w of workgroup g handles flattened rows 3u .. 3u+2,
+// u = 16g + w, of the six routed slots (row r of slot k is flattened row
+// 2048k + r), gate and up.  With SEL the workgroup first picks the token's
+// top-6 experts from the router's key intervals (wave 0, while the other
+// waves build the tables and stage x); workgroup 0 of each row publishes the
+// token's ids and gates for the down kernel.  Without SEL the weight loads
+// are issued before the tables are built.
 template <bool SEL>
 __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
   // one static array so that the table offsets are compile-time constants
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in scalar registers
   const int row0 = (blockIdx.x * kGuWaves + w) * kGuRows;  // flattened
-  // token t = blockIdx.y (several tokens: one grid row each; selection only at T = 1)
+  // token t = blockIdx.y (one grid row per token)
   const int tok = blockIdx.y;
   const uint16_t* xtok = a.x + (size_t)tok * kH;
   const int32_t* idtok = a.ids + 6 * tok;

@@ -1427,9 +1427,6 @@ __global__ __launch_bounds__(256) void k_imatrix(ImxArgs a) {
   }
 }
 
-// The grouped kernels need bf16 x, 256-multiple shapes and formats they know
-// (any token count: at one token they run the shared expert after the
-// streaming matvec kernels).
 // gate/up + SwiGLU for routed items with Q4_K gate and up.  Grid
 // (I / 64, items), 256 threads; wave w owns features n0 + 16w .. +15.  K
 // runs in 128-column stages (half a block, four groups); a stage's weights
@@ -1509,6 +1506,9 @@ __global__ __launch_bounds__(256) void k_grouped_gateup_q4k(GroupArgs a) {
   swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu);
 }
 
+// The grouped kernels need bf16 x, 256-multiple shapes and formats they know
+// (any token count; after the few-token matvec kernels they also run a shared
+// expert the per-token shared kernels do not take).
 inline bool grouped_eligible(const ds4moe_shape& s, const ds4moe_experts& ex,
                              const ds4moe_experts* sh, const void* x, int32_t x_dt, int32_t T) {
   auto gu_ok = [](int qt) { return qt == DS4MOE_IQ2_XXS || qt == DS4MOE_Q8_0; };
