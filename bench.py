@@ -39,7 +39,7 @@ GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "5ddf38c1fb193aba661a6deaff254006c0cf926dfd0f69a67cc5617bd9a27135",
+    "sha256": "792ca20d54e1b097a3d09c33f453b17e5ebab395869035dc1b7164601fab8c12",
     "bytes": 26273738,
 }
 
@@ -51,7 +51,7 @@ Q4K_GATEUP_TRAFFIC = {
                 "bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "578c30b5459941dbaab52e108f857136f3264322425426d0008b4df7a9ac9b34",
+    "sha256": "0486a8600abfc2d4e2fccb46ef39296fb9cc9ef89837192438c98732c2a71ca2",
     "bytes": 56915609,
 }
 

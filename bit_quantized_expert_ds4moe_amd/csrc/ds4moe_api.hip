@@ -265,7 +265,7 @@ bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x, int
 ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x,
                         int32_t T, const int32_t* ids_in, const float4* kbuf, int32_t* ids,
                         const float* wts, float* out, float* residual, void* ws, const Layout& L,
-                        hipStream_t st) {
+                        hipStream_t st, const SharedB1Args* shb = nullptr) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   float* h = at<float>(ws, L.h);
   GateUpB1Args g{};
@@ -295,13 +295,33 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   }
   ds4moe_status rc = launched();
   if (rc != DS4MOE_OK) return rc;
+  if (shb) {  // the shared expert's gate/up; its down rides along with the routed one
+    ProfScope prof(DS4MOE_K_OTHER, st);
+    launch_k(k_shared_gateup_q80_b1, dim3(kI / 8, T), dim3(256), 0, st, *shb);
+    if ((rc = launched()) != DS4MOE_OK) return rc;
+  }
+  const int32_t* dids = kbuf ? ids : ids_in;
+  const uint8_t* down = (const uint8_t*)ex.down;
+  const dim3 dgrid(kH / kDnBlockRows, T);
   {
     ProfScope prof(DS4MOE_K_DOWN, st);
-    launch_k(ex.down_qtype == DS4MOE_Q4_K ? k_down_q4k_b1 : k_down_q2k_b1,
-             dim3(kH / kDnBlockRows, T), dim3(kDnThreads), 0, st, h,
-             (const uint8_t*)ex.down, kbuf ? ids : ids_in, wts, s.n_expert, out, residual, status);
+    if (ex.down_qtype == DS4MOE_Q4_K)
+      launch_k(k_down_q4k_b1, dgrid, dim3(kDnThreads), 0, st, h, down, dids, wts, s.n_expert, out,
+               residual, status);
+    else if (shb)
+      launch_k(k_down_q2k_b1<true>, dgrid, dim3(kDnThreadsSh), 0, st, h, down, dids, wts,
+               s.n_expert, out, residual, status, (const float*)shb->h, shb->down);
+    else
+      launch_k(k_down_q2k_b1<false>, dgrid, dim3(kDnThreads), 0, st, h, down, dids, wts,
+               s.n_expert, out, residual, status, (const float*)nullptr, (const uint8_t*)nullptr);
   }
-  return launched();
+  if ((rc = launched()) != DS4MOE_OK) return rc;
+  if (shb && ex.down_qtype == DS4MOE_Q4_K) {  // Q4_K routed down: the shared down on its own
+    ProfScope prof(DS4MOE_K_OTHER, st);
+    launch_k(k_shared_down_q80_b1, dim3(kH / 16, T), dim3(256), 0, st, *shb);
+    rc = launched();
+  }
+  return rc;
 }
 
 // Permutation for the caller's debug buffer (offsets[E+1], perm, inv).
@@ -376,24 +396,12 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
   uint32_t* status = at<uint32_t>(ws, L.status);
   const bool b1 = fast_b1(s, ex, x, x_dt, T) && (!sh || grouped_eligible(s, ex, sh, x, x_dt, T));
   if (b1) {
-    // kbuf_sel: the top-K selection runs inside the gate/up kernel, which
-    // writes ids and wts (workspace buffers then)
-    ds4moe_status rc =
-        kbuf_sel ? launch_b1(s, ex, x, T, nullptr, kbuf_sel, const_cast<int32_t*>(ids), wts, out,
-                             residual, ws, L, st)
-                 : launch_b1(s, ex, x, T, ids, nullptr, nullptr, wts, out, residual, ws, L, st);
-    if (rc == DS4MOE_OK && perm_dbg)  // the few-token path needs no permutation: make it for the caller
-      rc = permute_dbg(s, T, ids, perm_dbg, ws, L, st);
-    // h: fp32 [T][6][I] by pair; the shared expert's rows below reuse its memory
-    if (rc == DS4MOE_OK && imx)
-      rc = launch_imatrix(s, *imx, x, x_dt, T, ids, wts, at<float>(ws, L.h), s.inter, nullptr,
-                          nullptr, false, ws, L, st);
-    if (rc != DS4MOE_OK || !sh) return rc;
-    if (T <= kSharedB1MaxTokens && shared_b1_ok(s, *sh, x, x_dt)) {
-      // the shared expert as per-token matvecs (beyond a few tokens its
-      // weights are better read once by the grouped kernels)
-      ProfScope shared_only(DS4MOE_K_OTHER, st);
-      SharedB1Args sa{};
+    // a Q8_0 shared expert at up to kSharedB1MaxTokens tokens runs as
+    // per-token matvecs inside launch_b1 (beyond that its weights are better
+    // read once by the grouped kernels below)
+    const bool shb1 = sh && T <= kSharedB1MaxTokens && shared_b1_ok(s, *sh, x, x_dt);
+    SharedB1Args sa{};
+    if (shb1) {
       sa.x = (const uint16_t*)x;
       sa.gate = (const uint8_t*)sh->gate;
       sa.up = (const uint8_t*)sh->up;
@@ -401,10 +409,22 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       sa.h = at<float>(ws, L.h) + (size_t)T * s.top_k * s.inter;  // after the routed rows
       sa.out = residual ? residual : out;
       sa.status = status;
-      launch_k(k_shared_gateup_q80_b1, dim3(kI / 8, T), dim3(256), 0, st, sa);
-      launch_k(k_shared_down_q80_b1, dim3(kH / 16, T), dim3(256), 0, st, sa);
-      return launched();
     }
+    // kbuf_sel: the top-K selection runs inside the gate/up kernel, which
+    // writes ids and wts (workspace buffers then)
+    ds4moe_status rc =
+        kbuf_sel ? launch_b1(s, ex, x, T, nullptr, kbuf_sel, const_cast<int32_t*>(ids), wts, out,
+                             residual, ws, L, st, shb1 ? &sa : nullptr)
+                 : launch_b1(s, ex, x, T, ids, nullptr, nullptr, wts, out, residual, ws, L, st,
+                             shb1 ? &sa : nullptr);
+    if (rc == DS4MOE_OK && perm_dbg)  // the few-token path needs no permutation: make it for the caller
+      rc = permute_dbg(s, T, ids, perm_dbg, ws, L, st);
+    // h: fp32 [T][6][I] by pair; the shared expert's rows below reuse its memory
+    if (rc == DS4MOE_OK && imx)
+      rc = launch_imatrix(s, *imx, x, x_dt, T, ids, wts, at<float>(ws, L.h), s.inter, nullptr,
+                          nullptr, false, ws, L, st);
+    if (rc != DS4MOE_OK || !sh) return rc;
+    if (shb1) return DS4MOE_OK;  // the shared expert ran inside launch_b1
   }
   if (b1 || (T > 1 && grouped_eligible(s, ex, sh, x, x_dt, T))) {
     // after the few-token path, the shared expert's kernels time as one class

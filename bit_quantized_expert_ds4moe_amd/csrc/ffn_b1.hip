@@ -370,6 +370,14 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
 // that the 16 lanes one 16-byte LDS read serves hit 16 distinct bank groups.
 constexpr int kDnBlockRows = 2 * kDnRows;  // 16 output rows per workgroup
 constexpr int kDnThreads = 12 * 64;
+constexpr int kDnThreadsSh = 14 * 64;      // with the shared expert as a seventh slot
+
+// The workgroup's 16 rows of a Q8_0 shared expert's down, as the seventh slot
+// (two more waves): partial sums of rows row0 + 2m + u, m < 4, in pr (the
+// reduce4x2 layout), from the shared SwiGLU row staged in LDS at hsl.
+// Defined with the shared-expert kernels (ffn_shared.hip).
+__device__ void shared_down_slot(const float4* hsl, const uint8_t* sh_down, int row0, int lane,
+                                 float* pr, bool& h_bad);
 
 __device__ inline int dn_chunk(int G) {
   return G ^ ((G >> 6) & 3) ^ (((G >> 5) & 1) << 3);
@@ -399,38 +407,46 @@ __device__ inline float reduce4x2(const float* v) {
   return z;
 }
 
-__global__ __launch_bounds__(kDnThreads) void k_down_q2k_b1(const float* __restrict__ h,
-                                                            const uint8_t* __restrict__ down,
-                                                            const int32_t* __restrict__ ids,
-                                                            const float* __restrict__ wts, int E,
-                                                            float* __restrict__ out,
-                                                            float* __restrict__ residual,
-                                                            uint32_t* status) {
+// SH: a Q8_0 shared expert rides along as a seventh slot (waves 12 and 13,
+// its SwiGLU row sh_h staged with the routed ones), added unscaled.
+template <bool SH>
+__global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
+    const float* __restrict__ h, const uint8_t* __restrict__ down,
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int E,
+    float* __restrict__ out, float* __restrict__ residual, uint32_t* status,
+    const float* __restrict__ sh_h, const uint8_t* __restrict__ sh_down) {
   constexpr int R = kDnRows;
-  constexpr int kChunks = 6 * kI / 4;  // 16-byte chunks of h
+  constexpr int NT = SH ? kDnThreadsSh : kDnThreads;
+  constexpr int kSlots = SH ? 7 : 6;
+  constexpr int kChunks = kSlots * kI / 4;  // 16-byte chunks of h
   static_assert(R == 8, "four steps of two rows per wave");
-  __shared__ float4 hs[kChunks];  // 48 KB
-  __shared__ float part[6][kDnBlockRows];
+  __shared__ float4 hs[kChunks];  // 48 KB (56 KB with the shared slot)
+  __shared__ float part[kSlots][kDnBlockRows];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int k = w >> 1, rh = w & 1;
+  const bool shw = SH && k == 6;  // a shared-slot wave
   const int u = lane >> 5, L = lane & 31, b = L >> 2, hq = (L >> 1) & 1, p = L & 1;
   // token t = blockIdx.y
   const int tok = blockIdx.y;
   h += (size_t)tok * 6 * kI;
+  if (SH) sh_h += (size_t)tok * kI;
   ids += 6 * tok;
   wts += 6 * tok;
   if (out) out += (size_t)tok * kH;
   if (residual) residual += (size_t)tok * kH;
   // the expert id and gate first: the weight addresses wait for the id
-  int e = load_scalar_i32(ids, k);
-  const float wk = __int_as_float(load_scalar_i32((const int32_t*)wts, k));
-  // 1. h into LDS
-  static_assert(kChunks == 4 * kDnThreads, "four h chunks per thread");
-  const float4* hg = (const float4*)h + tid;
-  const float4 hc0 = hg[0], hc1 = hg[kDnThreads], hc2 = hg[2 * kDnThreads], hc3 = hg[3 * kDnThreads];
+  int e = shw ? 0 : load_scalar_i32(ids, k);
+  const float wk = shw ? 1.0f : __int_as_float(load_scalar_i32((const int32_t*)wts, k));
+  // 1. h into LDS (slot 6: the shared row)
+  static_assert(kChunks == 4 * NT, "four h chunks per thread");
+  auto src = [&](int q) {
+    const int G = tid + NT * q;
+    return (SH && G >= 6 * kI / 4) ? ((const float4*)sh_h)[G - 6 * kI / 4] : ((const float4*)h)[G];
+  };
+  const float4 hc0 = src(0), hc1 = src(1), hc2 = src(2), hc3 = src(3);
   auto put = [&](int q, float4 v) {
-    const int G = tid + kDnThreads * q;
+    const int G = tid + NT * q;
     hs[(G & ~511) | dn_chunk(G & 511)] = v;
   };
   put(0, hc0);
@@ -438,9 +454,14 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q2k_b1(const float* __restr
   put(2, hc2);
   put(3, hc3);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  float pr[R / 2];
+  bool h_range = false, bad_id = false;
+  if (shw) {
+    shared_down_slot(hs + 6 * 512, sh_down, blockIdx.x * kDnBlockRows + rh * R, lane, pr, h_range);
+  } else {
   // 2. this wave's weights, requested only once the whole workgroup has its
   // h: in the other order the h lines queue behind weight traffic
-  const bool bad_id = e < 0 || e >= E;
+  bad_id = e < 0 || e >= E;
   e = bad_id ? 0 : e;
   const int row0 = blockIdx.x * kDnBlockRows + rh * R;  // output rows of token tok
   const uint8_t* base = down + ((size_t)e * kH + row0 + u) * kRowQ2k + b * kQ2kBytes;
@@ -472,7 +493,6 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q2k_b1(const float* __restr
   uint32_t nr[32];
   int xn[4];
   float S;
-  bool h_range;
   {
     float mx = 0.0f;
 #pragma unroll
@@ -496,7 +516,6 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q2k_b1(const float* __restr
   const float wS = wk * S;
   const uint32_t ssel = (uint32_t)p | ((uint32_t)(p + 2) << 8) | ((uint32_t)(p + 4) << 16) |
                         ((uint32_t)(p + 6) << 24);
-  float pr[R / 2];
 #pragma unroll
   for (int m = 0; m < R / 2; m++) {
     // the code bytes l = 2q, 2q + 1 in the two 16-bit halves
@@ -521,6 +540,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q2k_b1(const float* __restr
     const float d = f16_bits_to_f32(dd[m] & 0xFFFFu), dmin = f16_bits_to_f32(dd[m] >> 16);
     pr[m] = wS * fmaf(-dmin, (float)B, d * (float)A);
   }
+  }  // routed slot
   const float tot = reduce4x2(pr);
   if ((lane & 7) == 0) {
     const int rho = lane >> 4, up8 = (lane >> 3) & 1;
@@ -531,6 +551,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q2k_b1(const float* __restr
   if (tid < kDnBlockRows) {
     float acc = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) +
                 (part[4][tid] + part[5][tid]);
+    if (SH) acc += part[kSlots - 1][tid];
     const int row = blockIdx.x * kDnBlockRows + tid;
     if (residual) residual[row] += acc;
     else out[row] = acc;

@@ -146,6 +146,40 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_b1(SharedB1Args a) {
   if (h_bad && lane == 0) raise_fault(a.status, DS4MOE_FAULT_F16_RANGE);
 }
 
+// The shared expert's down as the seventh slot of k_down_q2k_b1<true>: rows
+// row0 + 2m + u (m < 4) of the wave, lane L of half u covering columns
+// 64L .. +63 (two Q8_0 blocks); the first two steps' weights are requested
+// before the activations are converted, the last two right after.
+__device__ void shared_down_slot(const float4* hsl, const uint8_t* sh_down, int row0, int lane,
+                                 float* pr, bool& h_bad) {
+  const int u = lane >> 5, L = lane & 31;
+  uint32_t D0[17], D1[17];
+  q80_pair_load(sh_down + (size_t)(row0 + u) * kShRowDn + 68 * L, D0);
+  q80_pair_load(sh_down + (size_t)(row0 + 2 + u) * kShRowDn + 68 * L, D1);
+  float4 hv[16];
+#pragma unroll
+  for (int q = 0; q < 16; q++) hv[q] = hsl[dn_chunk(16 * L + q)];
+  float mx = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; q++)
+    mx = fmaxf(fmaxf(fmaxf(mx, fabsf(hv[q].x)), fmaxf(fabsf(hv[q].y), fabsf(hv[q].z))), fabsf(hv[q].w));
+  h_bad = !(mx <= 3.0e38f);
+  auto hval = [&](int i) {
+    const float4 q = hv[i >> 2];
+    return (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
+  };
+  uint32_t xl[16], xh[16];
+  int sl, sh;
+  const float S = q4k_fix(hval, xl, xh, sl, sh);
+  uint32_t D2[17], D3[17];
+  q80_pair_load(sh_down + (size_t)(row0 + 4 + u) * kShRowDn + 68 * L, D2);
+  q80_pair_load(sh_down + (size_t)(row0 + 6 + u) * kShRowDn + 68 * L, D3);
+  pr[0] = S * q80_dot64(D0, xl, xh, sl, sh);
+  pr[1] = S * q80_dot64(D1, xl, xh, sl, sh);
+  pr[2] = S * q80_dot64(D2, xl, xh, sl, sh);
+  pr[3] = S * q80_dot64(D3, xl, xh, sl, sh);
+}
+
 // The few-token shared-expert kernels apply: Q8_0 gate, up and down of the
 // V4-Flash shape, bf16 activations, 4-byte-aligned weights.
 inline bool shared_b1_ok(const ds4moe_shape& s, const ds4moe_experts& sh, const void* x,

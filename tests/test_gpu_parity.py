@@ -327,12 +327,15 @@ def _layer_workload(widx):
         return MIXED_LAYER
     if widx == "q4k-t3":
         return replace(Q4_LAYER, T=3)
+    if widx == "q4k-shared-t2":
+        return replace(Q4_LAYER, T=2, shared=True)
     if isinstance(widx, str) and widx.startswith("b8-t"):
         return replace(g.WORKLOADS[2], T=int(widx[4:]))
     return g.WORKLOADS[widx]
 
 
-@pytest.mark.parametrize("widx", [0, 1, "q4k", "mixed", "q4k-t3", 2, "b8-t2", "b8-t13", "b8-t14"])
+@pytest.mark.parametrize("widx", [0, 1, "q4k", "mixed", "q4k-t3", "q4k-shared-t2", 2, "b8-t2",
+                                  "b8-t13", "b8-t14"])
 def test_layer_route_and_ffn(widx):
     # configs 0, 1 and 2; the config-1 layer with Q4_K experts (1 and 3
     # tokens) and with IQ2_XXS gate/up and Q4_K down; config 2 (Q8_0 shared
