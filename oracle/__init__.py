@@ -274,8 +274,8 @@ def quantize(qt, src, importance=None, grid=None, imp_stride=None, map_raw=None)
     g = None if grid is None else _c(grid, np.uint8)
     if qt == IQ2_XXS and map_raw is None and g is not None:
         map_raw = iq2_map(g)[2]
-    bb = {Q2_K: 84, IQ2_XXS: 66}[qt]
-    out = np.zeros(n_mats * rows * cols // 256 * bb, np.uint8)
+    bb = {Q2_K: 84, IQ2_XXS: 66, Q4_K: 144, Q8_0: 34}[qt]
+    out = np.zeros(n_mats * rows * cols // (32 if qt == Q8_0 else 256) * bb, np.uint8)
     rc = lib().en_quantize(qt, _p(x), n_mats, rows, cols, None if imp is None else _p(imp),
                            imp_stride, None if g is None else _p(g),
                            None if map_raw is None else _p(map_raw), _p(out))

@@ -18,6 +18,11 @@
  *   sec. 5, 7, 8  importance[column] = sum of squared activations; one
  *           vector per expert (n_expert x n_columns); without measured
  *           statistics the fallback is the column energy of the weights.
+ * The Q4 files of the mixed stacks (DS4C2 sec. 10) and the Q8_0 shared
+ * experts (FLOW quantisation table) come from the same tool; their encoders
+ * here are the plain readings: Q4_K = the Q2_K procedure on 32-value
+ * sub-blocks with 4-bit codes and 6-bit scale/min nibbles; Q8_0 = d =
+ * max|x| / 127 per 32 values, nearest codes.
  * The pages print no search procedure.  The one below is a plain reading
  * (every choice is written at the function): a fixed number of weighted
  * least-squares refits for Q2_K, a fixed set of candidate group scales for
@@ -39,7 +44,7 @@
 
 #define EXPORT __attribute__((visibility("default")))
 
-enum { EN_Q2_K = 0, EN_IQ2_XXS = 1 };
+enum { EN_Q2_K = 0, EN_IQ2_XXS = 1, EN_Q8_0 = 2, EN_Q4_K = 3 };
 enum { EN_OK = 0, EN_EINVAL = -1 };
 
 /* binary32 -> binary16 bits, round to nearest even (subnormals kept,
@@ -78,45 +83,48 @@ static float clampf(float v, float lo, float hi) { return fminf(fmaxf(v, lo), hi
 /* Q2_K                                                                */
 /* ------------------------------------------------------------------ */
 
-/* Code of x for scale s and min m: nearest of s*q - m, q in 0..3. */
-static int q2_code(float x, float s, float m) {
+/* Code of x for scale s and min m: nearest of s*q - m, q in 0..qmax. */
+static int af_code(float x, float s, float m, float qmax) {
   if (!(s > 0.0f)) return 0;
-  return (int)clampf(rintf((x + m) / s), 0.0f, 3.0f);
+  return (int)clampf(rintf((x + m) / s), 0.0f, qmax);
 }
 
-/* Weighted squared error of the 16 values of a sub-block for (s, m). */
-static float q2_err(const float* x, const float* w, float s, float m) {
+/* Weighted squared error of the n values of a sub-block for (s, m). */
+static float af_err(const float* x, const float* w, int n, float s, float m, float qmax) {
   float e = 0.0f;
-  for (int i = 0; i < 16; i++) {
-    float t = s * (float)q2_code(x[i], s, m);
+  for (int i = 0; i < n; i++) {
+    float t = s * (float)af_code(x[i], s, m, qmax);
     t = t - m;
     float r = t - x[i];
     e = e + w[i] * (r * r);
   }
   return e;
 }
+static int q2_code(float x, float s, float m) { return af_code(x, s, m, 3.0f); }
 
 /*
- * Scale s >= 0 and min m >= 0 of one 16-value sub-block for x ~ s*q - m.
- * Start: the range, m = -min(0, min x), s = (max x + m) / 3 (a sub-block whose
+ * Scale s >= 0 and min m >= 0 of one sub-block of n values for x ~ s*q - m,
+ * q in 0..qmax (Q2_K: 16 values, qmax 3; Q4_K: 32 values, qmax 15).
+ * Start: the range, m = -min(0, min x), s = (max x + m) / qmax (a sub-block whose
  * values are all equal and not positive is exact with s = 0).  Then four
  * rounds of: codes for the current (s, m), weighted least-squares (s, m) for
  * those codes (m clamped at 0, then s at 0), keeping the pair with the lowest
  * weighted error (strictly lower replaces; the start wins ties).
  */
-static void q2_fit(const float* x, const float* w, float* s_out, float* m_out) {
+static void af_fit(const float* x, const float* w, int n, float qmax, float* s_out,
+                   float* m_out) {
   float lo = 0.0f, hi = x[0];
-  for (int i = 0; i < 16; i++) {
+  for (int i = 0; i < n; i++) {
     lo = fminf(lo, x[i]);
     hi = fmaxf(hi, x[i]);
   }
-  float s = (hi - lo) / 3.0f, m = -lo;
+  float s = (hi - lo) / qmax, m = -lo;
   if (!(s > 0.0f)) s = 0.0f;
-  float bs = s, bm = m, be = q2_err(x, w, s, m);
+  float bs = s, bm = m, be = af_err(x, w, n, s, m, qmax);
   for (int it = 0; it < 4; it++) {
     float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f, T0 = 0.0f, T1 = 0.0f;
-    for (int i = 0; i < 16; i++) {
-      float q = (float)q2_code(x[i], s, m);
+    for (int i = 0; i < n; i++) {
+      float q = (float)af_code(x[i], s, m, qmax);
       float wq = w[i] * q;
       S0 = S0 + w[i];
       S1 = S1 + wq;
@@ -137,7 +145,7 @@ static void q2_fit(const float* x, const float* w, float* s_out, float* m_out) {
       nm = S0 > 0.0f ? -T0 / S0 : 0.0f;
       if (nm < 0.0f) nm = 0.0f;
     }
-    float e = q2_err(x, w, ns, nm);
+    float e = af_err(x, w, n, ns, nm, qmax);
     if (e < be) {
       be = e;
       bs = ns;
@@ -160,7 +168,7 @@ static void q2k_encode_block(const float* x, const float* w, uint8_t* b) {
   float s[16], m[16];
   float smax = 0.0f, mmax = 0.0f;
   for (int j = 0; j < 16; j++) {
-    q2_fit(x + 16 * j, w + 16 * j, &s[j], &m[j]);
+    af_fit(x + 16 * j, w + 16 * j, 16, 3.0f, &s[j], &m[j]);
     smax = fmaxf(smax, s[j]);
     mmax = fmaxf(mmax, m[j]);
   }
@@ -185,6 +193,71 @@ static void q2k_encode_block(const float* x, const float* w, uint8_t* b) {
   b[81] = (uint8_t)(dh >> 8);
   b[82] = (uint8_t)mh;
   b[83] = (uint8_t)(mh >> 8);
+}
+
+/* ------------------------------------------------------------------ */
+/* Q4_K and Q8_0                                                       */
+/* ------------------------------------------------------------------ */
+
+/*
+ * One 144-byte Q4_K block (layout of the decoder in ds4_oracle.c) from 256
+ * values x and weights w: the Q2_K procedure with 32-value sub-blocks and
+ * codes 0..15 (af_fit), d = max s_j / 63 and dmin = max m_j / 63 in fp16,
+ * 6-bit nibbles sc_j = rint(s_j / d), m_j = rint(m_j / dmin) in 0..63, codes
+ * nearest for the stored pair.
+ */
+static void q4k_encode_block(const float* x, const float* w, uint8_t* b) {
+  float s[8], m[8];
+  float smax = 0.0f, mmax = 0.0f;
+  for (int j = 0; j < 8; j++) {
+    af_fit(x + 32 * j, w + 32 * j, 32, 15.0f, &s[j], &m[j]);
+    smax = fmaxf(smax, s[j]);
+    mmax = fmaxf(mmax, m[j]);
+  }
+  if (!(smax > 0.0f)) smax = 0.0f;
+  if (!(mmax > 0.0f)) mmax = 0.0f;
+  uint16_t dh = en_f16_bits(smax / 63.0f), mh = en_f16_bits(mmax / 63.0f);
+  float d = f16_float(dh), dmin = f16_float(mh);
+  memset(b, 0, 144);
+  b[0] = (uint8_t)dh;
+  b[1] = (uint8_t)(dh >> 8);
+  b[2] = (uint8_t)mh;
+  b[3] = (uint8_t)(mh >> 8);
+  uint8_t* S = b + 4;
+  for (int j = 0; j < 8; j++) {
+    int sc = d > 0.0f ? (int)clampf(rintf(s[j] / d), 0.0f, 63.0f) : 0;
+    int mn = dmin > 0.0f ? (int)clampf(rintf(m[j] / dmin), 0.0f, 63.0f) : 0;
+    if (j < 4) {
+      S[j] = (uint8_t)sc;
+      S[j + 4] = (uint8_t)mn;
+    } else {
+      S[j + 4] = (uint8_t)((sc & 15) | ((mn & 15) << 4));
+      S[j - 4] |= (uint8_t)((sc >> 4) << 6);
+      S[j] |= (uint8_t)((mn >> 4) << 6);
+    }
+    float Sc = d * (float)sc, M = dmin * (float)mn;
+    for (int l = 0; l < 32; l++) {
+      int i = 32 * j + l;
+      int q = af_code(x[i], Sc, M, 15.0f);
+      int c = i / 64, hi = (i % 64) / 32;
+      b[16 + 32 * c + l] |= (uint8_t)(hi ? q << 4 : q);
+    }
+  }
+}
+
+/* One 34-byte Q8_0 block from 32 values: d = max|x| / 127 in fp16, codes
+ * rint(x / d) clamped to -127..127 (all zero when d is 0). */
+static void q80_encode_block(const float* x, uint8_t* b) {
+  float amax = 0.0f;
+  for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(x[i]));
+  uint16_t dh = en_f16_bits(amax / 127.0f);
+  float d = f16_float(dh);
+  b[0] = (uint8_t)dh;
+  b[1] = (uint8_t)(dh >> 8);
+  for (int i = 0; i < 32; i++) {
+    int q = d > 0.0f ? (int)clampf(rintf(x[i] / d), -127.0f, 127.0f) : 0;
+    b[2 + i] = (uint8_t)(int8_t)q;
+  }
 }
 
 /* ------------------------------------------------------------------ */
@@ -393,8 +466,8 @@ static void iq2_encode_block(const float* x, const float* w, const uint8_t* grid
 
 /*
  * Encode n_mats matrices [rows][cols] of src (row-major, stacked) into blocks
- * tiling each row (cols % 256 == 0).  importance: NULL (every weight 1; Q2_K
- * only) or n_mats vectors of cols values, matrix m's at importance +
+ * tiling each row (cols % 256 == 0).  importance: NULL (every weight 1; Q2_K,
+ * Q4_K and Q8_0, which uses none) or n_mats vectors of cols values, matrix m's at importance +
  * m * imp_stride (0: one vector for all); the weight of a value is its
  * column's importance.  IQ2_XXS needs the grid (256 x 8 bytes of 8, 25, 43)
  * and its map (en_iq2_map_build).  Values must be finite and weights finite
@@ -403,8 +476,8 @@ static void iq2_encode_block(const float* x, const float* w, const uint8_t* grid
 EXPORT int en_quantize(int qt, const float* src, int64_t n_mats, int64_t rows, int64_t cols,
                        const float* importance, int64_t imp_stride, const uint8_t* grid,
                        const uint8_t* map, uint8_t* dst) {
-  if ((qt != EN_Q2_K && qt != EN_IQ2_XXS) || n_mats < 0 || rows < 0 || cols < 0 ||
-      cols % 256 != 0 || imp_stride < 0)
+  if (qt < EN_Q2_K || qt > EN_Q4_K || n_mats < 0 || rows < 0 || cols < 0 || cols % 256 != 0 ||
+      imp_stride < 0)
     return EN_EINVAL;
   if (qt == EN_IQ2_XXS && (!importance || !grid || !map)) return EN_EINVAL;
   int64_t n = n_mats * rows * cols;
@@ -418,7 +491,7 @@ EXPORT int en_quantize(int qt, const float* src, int64_t n_mats, int64_t rows, i
         if (!isfinite(x) || x < 0.0f) return EN_EINVAL;
       }
   }
-  const int bb = qt == EN_Q2_K ? 84 : 66;
+  const int bb = qt == EN_Q2_K ? 84 : qt == EN_IQ2_XXS ? 66 : qt == EN_Q4_K ? 144 : 8 * 34;
   const int64_t bpr = cols / 256;
   float unit[256];
   for (int i = 0; i < 256; i++) unit[i] = 1.0f;
@@ -431,6 +504,9 @@ EXPORT int en_quantize(int qt, const float* src, int64_t n_mats, int64_t rows, i
       const float* w = imp ? imp + 256 * blk : unit;
       uint8_t* b = dst + (r * bpr + blk) * bb;
       if (qt == EN_Q2_K) q2k_encode_block(x, w, b);
+      else if (qt == EN_Q4_K) q4k_encode_block(x, w, b);
+      else if (qt == EN_Q8_0)
+        for (int g = 0; g < 8; g++) q80_encode_block(x + 32 * g, b + 34 * g);  /* 8 blocks per 256 */
       else iq2_encode_block(x, w, grid, map, b);
     }
   }

@@ -398,3 +398,115 @@ def test_encoder_argument_errors():
     g2[5] = 9
     with pytest.raises(ValueError):
         oracle.iq2_map(g2)
+
+
+# --------------------------------------------------------------------------
+# Q4_K and Q8_0 (the mixed stacks' Q4 layers and the shared expert)
+# --------------------------------------------------------------------------
+Q4_K, Q8_0 = oracle.Q4_K, oracle.Q8_0
+
+
+def q4k_pack_scales(sc, mn):
+    """The 12 scale bytes of the Q4_K layout (the decoder's reading)."""
+    S = np.zeros(12, np.uint8)
+    for j in range(8):
+        if j < 4:
+            S[j] |= sc[j]
+            S[j + 4] |= mn[j]
+        else:
+            S[j + 4] = (sc[j] & 15) | ((mn[j] & 15) << 4)
+            S[j - 4] |= (sc[j] >> 4) << 6
+            S[j] |= (mn[j] >> 4) << 6
+    return S
+
+
+def q4k_representable(seed, n_blocks):
+    """Q4_K blocks the encoder must reproduce exactly: codes 0 and 15 in every
+    32-value sub-block, 6-bit scales 1..63 and mins 0..63 with a 63 of each,
+    d and dmin within a factor 3 (decoded values exact in binary32)."""
+    r = rng(seed)
+    out = np.zeros((n_blocks, 144), np.uint8)
+    for b in range(n_blocks):
+        sc = r.integers(1, 64, 8)
+        mn = r.integers(0, 64, 8)
+        sc[r.integers(8)] = 63
+        mn[r.integers(8)] = 63
+        out[b, 4:16] = q4k_pack_scales(sc, mn)
+        codes = r.integers(0, 16, 256)
+        for j in range(8):
+            p = r.permutation(32)[:2]
+            codes[32 * j + p[0]] = 0
+            codes[32 * j + p[1]] = 15
+        for i in range(256):
+            c, hi, l = i // 64, (i % 64) // 32, i % 32
+            out[b, 16 + 32 * c + l] |= codes[i] << (4 * hi)
+        d = np.float16(r.uniform(1e-4, 1e-3))
+        dmin = np.float16(float(d) * r.uniform(0.3, 3.0))
+        out[b, 0:2] = np.array([d]).view(np.uint8)
+        out[b, 2:4] = np.array([dmin]).view(np.uint8)
+    return out
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_q4k_round_trip_of_representable_blocks(weighted):
+    blocks = q4k_representable(41, 16)
+    x64 = oracle.dequant(Q4_K, blocks)
+    x = x64.astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), x64)
+    x = x.reshape(4, 1024)
+    imp = rng(42).uniform(0.1, 10.0, 1024).astype(np.float32) if weighted else None
+    np.testing.assert_array_equal(oracle.quantize(Q4_K, x, imp).reshape(16, 144), blocks)
+
+
+def set_q4k_code(block, i, q):
+    b = block.copy()
+    c, hi, l = i // 64, (i % 64) // 32, i % 32
+    byte = 16 + 32 * c + l
+    keep = 0x0F if hi else 0xF0
+    b[byte] = (int(b[byte]) & keep) | (q << (4 * hi))
+    return b
+
+
+def test_q4k_codes_are_nearest_for_the_stored_scales():
+    r = rng(43)
+    x = (r.standard_normal((1, 256)) * 0.05).astype(np.float32)
+    blk = oracle.quantize(Q4_K, x)
+    base = oracle.dequant(Q4_K, blk)
+    for i in range(0, 256, 5):
+        errs = [abs(float(x[0, i]) - oracle.dequant(Q4_K, set_q4k_code(blk, i, q))[i])
+                for q in range(16)]
+        assert abs(float(x[0, i]) - base[i]) <= min(errs) + 1e-12
+
+
+def test_q4k_importance_lowers_the_weighted_error():
+    r = rng(44)
+    x = (r.standard_normal((32, 1024)) * 0.05).astype(np.float32)
+    imp = np.ones(1024, np.float32)
+    imp[r.permutation(1024)[:256]] = 50.0
+    yw = oracle.dequant(Q4_K, oracle.quantize(Q4_K, x, imp)).reshape(x.shape)
+    yp = oracle.dequant(Q4_K, oracle.quantize(Q4_K, x)).reshape(x.shape)
+    assert weighted_err(x, yw, imp) < 0.9 * weighted_err(x, yp, imp)
+    assert weighted_err(x, yp, 1.0) < weighted_err(x, yw, 1.0)
+    # 4-bit codes: well below the 2-bit error
+    y2 = oracle.dequant(Q2_K, oracle.quantize(Q2_K, x)).reshape(x.shape)
+    assert weighted_err(x, yp, 1.0) < 0.2 * weighted_err(x, y2, 1.0)
+
+
+def test_q80_closed_form():
+    # x = d c with |c| = 127 present: exact round trip; otherwise every value
+    # within half a step d/2 of its code, d = fp16(max|x| / 127)
+    r = rng(45)
+    d = np.float16(3e-4)
+    c = r.integers(-127, 128, (2, 256))
+    c[:, ::32] = 127
+    x = (np.float32(d) * c.astype(np.float32)).astype(np.float32)
+    blk = oracle.quantize(Q8_0, x).reshape(16, 34)
+    assert (blk[:, 0:2].copy().view(np.float16).ravel() == d).all()
+    np.testing.assert_array_equal(blk[:, 2:].view(np.int8).reshape(2, 256), c)
+    y = (r.standard_normal((2, 256)) * 0.05).astype(np.float32)
+    b2 = oracle.quantize(Q8_0, y).reshape(16, 34)
+    dd = b2[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
+    amax = np.abs(y.reshape(16, 32)).max(1)
+    np.testing.assert_array_equal(dd, (amax / np.float32(127)).astype(np.float32).astype(np.float16))
+    dec = oracle.dequant(Q8_0, b2).reshape(16, 32)
+    assert np.all(np.abs(dec - y.reshape(16, 32)) <= dd[:, None] / 2 * (1 + 1e-6) + 1e-12)
