@@ -803,7 +803,7 @@ DS4_EXPORT ds4moe_status ds4moe_quantize(int32_t qtype, const float* src, int64_
                                          int64_t imp_stride, const uint8_t* grid,
                                          const void* iq2_map, void* dst, void* ws,
                                          size_t ws_bytes, hipStream_t stream) {
-  if ((qtype != DS4MOE_Q2_K && qtype != DS4MOE_IQ2_XXS) || !src || !dst || !ws ||
+  if (!qtype_ok(qtype) || !src || !dst || !ws ||
       ws_bytes < 256 || n_mats < 0 || rows < 0 || cols < 0 || cols % 256 || imp_stride < 0 ||
       imp_stride % 4 || ((uintptr_t)src & 15) || ((uintptr_t)importance & 15))
     return DS4MOE_EINVAL;
@@ -812,7 +812,10 @@ DS4_EXPORT ds4moe_status ds4moe_quantize(int32_t qtype, const float* src, int64_
        ((uintptr_t)dst & 1)))
     return DS4MOE_EINVAL;
   if (qtype == DS4MOE_Q2_K && ((uintptr_t)dst & 3)) return DS4MOE_EINVAL;
-  const int64_t n_blocks = n_mats * rows * (cols / 256);
+  if (qtype == DS4MOE_Q4_K && ((uintptr_t)dst & 15)) return DS4MOE_EINVAL;
+  if (qtype == DS4MOE_Q8_0 && ((uintptr_t)dst & 1)) return DS4MOE_EINVAL;
+  // blocks of 256 values (Q8_0: of 32)
+  const int64_t n_blocks = n_mats * rows * (cols / (qtype == DS4MOE_Q8_0 ? 32 : 256));
   if (n_blocks == 0) return DS4MOE_OK;
   EncArgs a;
   a.src = src;
@@ -826,11 +829,17 @@ DS4_EXPORT ds4moe_status ds4moe_quantize(int32_t qtype, const float* src, int64_
   a.rows = rows;
   a.imp_stride = imp_stride;
   ProfScope prof(DS4MOE_K_OTHER, stream);
-  const int per = qtype == DS4MOE_Q2_K ? kEncThreads / 16 : kEncThreads / 8;
+  const int per = qtype == DS4MOE_Q2_K ? kEncThreads / 16
+                  : qtype == DS4MOE_Q8_0 ? kEncThreads
+                                         : kEncThreads / 8;
   const int64_t wgs = (n_blocks + per - 1) / per;
   if (wgs > 0x7FFFFFFF) return DS4MOE_EUNSUPPORTED;
   if (qtype == DS4MOE_Q2_K)
     launch_k(k_encode_q2k, dim3((uint32_t)wgs), dim3(kEncThreads), 0, stream, a);
+  else if (qtype == DS4MOE_Q4_K)
+    launch_k(k_encode_q4k, dim3((uint32_t)wgs), dim3(kEncThreads), 0, stream, a);
+  else if (qtype == DS4MOE_Q8_0)
+    launch_k(k_encode_q80, dim3((uint32_t)wgs), dim3(kEncThreads), 0, stream, a);
   else
     launch_k(k_encode_iq2, dim3((uint32_t)wgs), dim3(kEncThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;

@@ -1,6 +1,6 @@
-// encode.hip -- block encoders on gfx950: fp32 matrices to Q2_K and IQ2_XXS
-// blocks, plain or weighted by per-column importance, the IQ2_XXS neighbour
-// map of a grid, and the column-energy fallback importance.
+// encode.hip -- block encoders on gfx950: fp32 matrices to Q2_K, IQ2_XXS and
+// Q4_K blocks, plain or weighted by per-column importance, and to Q8_0; the
+// IQ2_XXS neighbour map of a grid, and the column-energy fallback importance.
 //
 // Pages: DS4C2 = qiita.com/yoshiyakato/items/4678be0e7860ddb444ec, sec. 3
 // (Q2_K: scale and min per 16 values, 2-bit codes, four per byte; with an
@@ -25,6 +25,9 @@
 //     that key's list, the scale is refitted (sum w t g / sum w g^2) and
 //     scored by sum w (t - S g)^2; d = 8 max S / 31 in fp16, nibble
 //     rint((8 S / d - 1) / 2), tuples assigned again at d (2s + 1) / 8.
+//   Q4_K: the Q2_K procedure on 32-value sub-blocks, codes 0..15, d = max s /
+//     63, dmin = max m / 63 (6-bit nibbles).  Q8_0: d = max|x| / 127 per 32
+//     values in fp16, nearest codes in -127..127.
 // Every integer decision is taken in binary32 in that order: sums run over
 // the values in index order with one rounding per operation (contraction is
 // switched off in each function), divisions are IEEE divisions, rint rounds
@@ -60,18 +63,23 @@ __device__ inline bool enc_bad_weight(float w) { return !(w >= 0.0f && w <= 3.40
 // ---------------------------------------------------------------------------
 // Q2_K
 // ---------------------------------------------------------------------------
-__device__ inline int q2e_code(float x, float s, float m) {
+// The affine fit of a sub-block of N values, codes 0..QMAX (Q2_K: 16 values,
+// 3; Q4_K: 32 values, 15).
+template <int QMAX>
+__device__ inline int afe_code(float x, float s, float m) {
 #pragma clang fp contract(off)
   if (!(s > 0.0f)) return 0;
-  return (int)enc_clamp(__builtin_rintf((x + m) / s), 0.0f, 3.0f);
+  return (int)enc_clamp(__builtin_rintf((x + m) / s), 0.0f, (float)QMAX);
 }
+__device__ inline int q2e_code(float x, float s, float m) { return afe_code<3>(x, s, m); }
 
-__device__ inline float q2e_err(const float* x, const float* w, float s, float m) {
+template <int N, int QMAX>
+__device__ inline float afe_err(const float* x, const float* w, float s, float m) {
 #pragma clang fp contract(off)
   float e = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    float t = s * (float)q2e_code(x[i], s, m);
+  for (int i = 0; i < N; i++) {
+    float t = s * (float)afe_code<QMAX>(x[i], s, m);
     t = t - m;
     const float r = t - x[i];
     e = e + w[i] * (r * r);
@@ -79,22 +87,23 @@ __device__ inline float q2e_err(const float* x, const float* w, float s, float m
   return e;
 }
 
-__device__ inline void q2e_fit(const float* x, const float* w, float& s_out, float& m_out) {
+template <int N, int QMAX>
+__device__ inline void afe_fit(const float* x, const float* w, float& s_out, float& m_out) {
 #pragma clang fp contract(off)
   float lo = 0.0f, hi = x[0];
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
+  for (int i = 0; i < N; i++) {
     lo = fminf(lo, x[i]);
     hi = fmaxf(hi, x[i]);
   }
-  float s = (hi - lo) / 3.0f, m = -lo;
+  float s = (hi - lo) / (float)QMAX, m = -lo;
   if (!(s > 0.0f)) s = 0.0f;
-  float bs = s, bm = m, be = q2e_err(x, w, s, m);
+  float bs = s, bm = m, be = afe_err<N, QMAX>(x, w, s, m);
   for (int it = 0; it < 4; it++) {
     float S0 = 0.0f, S1 = 0.0f, S2 = 0.0f, T0 = 0.0f, T1 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const float q = (float)q2e_code(x[i], s, m);
+    for (int i = 0; i < N; i++) {
+      const float q = (float)afe_code<QMAX>(x[i], s, m);
       const float wq = w[i] * q;
       S0 = S0 + w[i];
       S1 = S1 + wq;
@@ -115,7 +124,7 @@ __device__ inline void q2e_fit(const float* x, const float* w, float& s_out, flo
       nm = S0 > 0.0f ? -T0 / S0 : 0.0f;
       if (nm < 0.0f) nm = 0.0f;
     }
-    const float e = q2e_err(x, w, ns, nm);
+    const float e = afe_err<N, QMAX>(x, w, ns, nm);
     if (e < be) {
       be = e;
       bs = ns;
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_q2k(EncArgs a) {
   if (bad && live) raise_fault(a.status, DS4MOE_FAULT_BAD_INPUT);
 
   float s, m;
-  q2e_fit(x, w, s, m);
+  afe_fit<16, 3>(x, w, s, m);
   float smax = enc_group_max<16>(s), mmax = enc_group_max<16>(m);
   if (!(smax > 0.0f)) smax = 0.0f;
   if (!(mmax > 0.0f)) mmax = 0.0f;
@@ -223,6 +232,138 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_q2k(EncArgs a) {
     o[4 + j] = out;
     if (j < 4) o[j] = sbytes[lb][j];
     if (j == 4) o[20] = (uint32_t)dh | ((uint32_t)mh << 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Q4_K and Q8_0
+// ---------------------------------------------------------------------------
+// Q4_K: the Q2_K procedure on 32-value sub-blocks with codes 0..15 and 6-bit
+// nibbles (d = max s / 63, dmin = max m / 63).  8 lanes per block (lane j:
+// sub-block j), 32 blocks per workgroup.  Each header byte has one writer:
+// lane j < 4 writes bytes 4 + j and 8 + j (6-bit scale and min with the top
+// bits of sub-block j + 4, taken from lane j ^ 4), lane j >= 4 byte 8 + j (the
+// low nibbles); the even lane of a pair writes the 32 code bytes of its
+// chunk, its codes in the low nibbles and its partner's in the high ones.
+__global__ __launch_bounds__(kEncThreads) void k_encode_q4k(EncArgs a) {
+#pragma clang fp contract(off)
+  __shared__ uint32_t hdr[kEncThreads / 8][4];
+  const int tid = threadIdx.x, j = tid & 7, lb = tid >> 3;
+  const int64_t blk0 = (int64_t)blockIdx.x * (kEncThreads / 8) + lb;
+  const bool live = blk0 < a.n_blocks;
+  const int64_t blk = live ? blk0 : 0;
+  float x[32], w[32];
+  const float4* xp = (const float4*)(a.src + blk * 256 + 32 * j);
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    const float4 v = xp[q];
+    x[4 * q] = v.x;
+    x[4 * q + 1] = v.y;
+    x[4 * q + 2] = v.z;
+    x[4 * q + 3] = v.w;
+  }
+  if (a.imp) {
+    const float4* wp = (const float4*)(enc_imp_row(a, blk) + 32 * j);
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      const float4 v = wp[q];
+      w[4 * q] = v.x;
+      w[4 * q + 1] = v.y;
+      w[4 * q + 2] = v.z;
+      w[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; i++) w[i] = 1.0f;
+  }
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 32; i++) bad |= enc_bad_value(x[i]) || enc_bad_weight(w[i]);
+  if (bad && live) raise_fault(a.status, DS4MOE_FAULT_BAD_INPUT);
+
+  float s, m;
+  afe_fit<32, 15>(x, w, s, m);
+  float smax = enc_group_max<8>(s), mmax = enc_group_max<8>(m);
+  if (!(smax > 0.0f)) smax = 0.0f;
+  if (!(mmax > 0.0f)) mmax = 0.0f;
+  const uint16_t dh = enc_f16_bits(smax / 63.0f), mh = enc_f16_bits(mmax / 63.0f);
+  const float d = enc_f16_float(dh), dmin = enc_f16_float(mh);
+  const int sc = d > 0.0f ? (int)enc_clamp(__builtin_rintf(s / d), 0.0f, 63.0f) : 0;
+  const int mn = dmin > 0.0f ? (int)enc_clamp(__builtin_rintf(m / dmin), 0.0f, 63.0f) : 0;
+  const int sc4 = __shfl_xor(sc, 4, 64), mn4 = __shfl_xor(mn, 4, 64);
+  uint8_t* H = (uint8_t*)hdr[lb];
+  if (j == 0) {
+    H[0] = (uint8_t)dh;
+    H[1] = (uint8_t)(dh >> 8);
+    H[2] = (uint8_t)mh;
+    H[3] = (uint8_t)(mh >> 8);
+  }
+  if (j < 4) {
+    H[4 + j] = (uint8_t)(sc | ((sc4 >> 4) << 6));
+    H[8 + j] = (uint8_t)(mn | ((mn4 >> 4) << 6));
+  } else {
+    H[8 + j] = (uint8_t)((sc & 15) | ((mn & 15) << 4));
+  }
+  const float Sc = d * (float)sc, M = dmin * (float)mn;
+  uint32_t cw[8];  // byte l of the sub-block: its code
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; b++) v |= (uint32_t)afe_code<15>(x[4 * k + b], Sc, M) << (8 * b);
+    cw[k] = v;
+  }
+  uint32_t pw[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) pw[k] = __shfl_xor(cw[k], 1, 64);
+  __syncthreads();
+  if (live) {
+    uint8_t* o = a.dst + blk * kQ4kBytes;  // 144-byte blocks: 16-byte aligned
+    if (j < 4) ((uint32_t*)o)[j] = hdr[lb][j];
+    if ((j & 1) == 0) {
+      uint4* oc = (uint4*)(o + 16 + 32 * (j >> 1));
+      oc[0] = make_uint4(cw[0] | (pw[0] << 4), cw[1] | (pw[1] << 4), cw[2] | (pw[2] << 4),
+                         cw[3] | (pw[3] << 4));
+      oc[1] = make_uint4(cw[4] | (pw[4] << 4), cw[5] | (pw[5] << 4), cw[6] | (pw[6] << 4),
+                         cw[7] | (pw[7] << 4));
+    }
+  }
+}
+
+// Q8_0: one lane per 32-value block: d = max|x| / 127 in fp16, codes
+// rint(x / d) clamped to -127..127 (zero when d is 0); the 34 bytes leave as
+// 17 halfwords (2-byte aligned blocks).  n_blocks counts 32-value blocks.
+__global__ __launch_bounds__(kEncThreads) void k_encode_q80(EncArgs a) {
+#pragma clang fp contract(off)
+  const int64_t i = (int64_t)blockIdx.x * kEncThreads + threadIdx.x;
+  if (i >= a.n_blocks) return;
+  float x[32];
+  const float4* xp = (const float4*)(a.src + i * 32);
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    const float4 v = xp[q];
+    x[4 * q] = v.x;
+    x[4 * q + 1] = v.y;
+    x[4 * q + 2] = v.z;
+    x[4 * q + 3] = v.w;
+  }
+  bool bad = false;
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 32; k++) {
+    bad |= enc_bad_value(x[k]);
+    amax = fmaxf(amax, fabsf(x[k]));
+  }
+  if (bad) raise_fault(a.status, DS4MOE_FAULT_BAD_INPUT);
+  const uint16_t dh = enc_f16_bits(amax / 127.0f);
+  const float d = enc_f16_float(dh);
+  uint16_t* o = (uint16_t*)(a.dst + i * kQ80Bytes);
+  o[0] = dh;
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    const int q0 = d > 0.0f ? (int)enc_clamp(__builtin_rintf(x[2 * k] / d), -127.0f, 127.0f) : 0;
+    const int q1 = d > 0.0f ? (int)enc_clamp(__builtin_rintf(x[2 * k + 1] / d), -127.0f, 127.0f) : 0;
+    o[1 + k] = (uint16_t)((q0 & 0xFF) | ((q1 & 0xFF) << 8));
   }
 }
 

@@ -273,11 +273,15 @@ ds4moe_status ds4moe_iq2_map_build(const uint8_t* grid, void* map, void* ws, siz
 
 /*
  * Encodes n_mats row-major fp32 matrices [rows][cols] (stacked, device,
- * 16-byte aligned, cols % 256 == 0) into blocks tiling each row: dst gets
- * n_mats*rows*cols/256 blocks of 84 (Q2_K, dst 4-byte aligned) or 66 bytes
- * (IQ2_XXS, 2-byte aligned), in the layouts the expert kernels read.
- * importance: device, nullable for Q2_K (every weight 1: the plain encoder),
- * required for IQ2_XXS; matrix m's weights are importance[m * imp_stride + c]
+ * 16-byte aligned, cols % 256 == 0) into blocks tiling each row, in the
+ * layouts the expert kernels read: dst gets n_mats*rows*cols/256 blocks of
+ * 84 (Q2_K, dst 4-byte aligned), 66 (IQ2_XXS, 2-byte aligned) or 144 bytes
+ * (Q4_K, 16-byte aligned), or n_mats*rows*cols/32 blocks of 34 bytes (Q8_0,
+ * 2-byte aligned; d = max|x|/127 per 32 values, importance unused).  Q4_K
+ * is the Q2_K procedure on 32-value sub-blocks with 4-bit codes and 6-bit
+ * scale/min nibbles (the Q4 layers of the mixed stacks, DS4C2 sec. 10).
+ * importance: device, nullable for Q2_K and Q4_K (every weight 1: the plain
+ * encoder), required for IQ2_XXS; matrix m's weights are importance[m * imp_stride + c]
  * for column c (imp_stride 0: one vector for every matrix; otherwise a
  * multiple of 4, normally cols: the n_expert x n_columns packing), 16-byte
  * aligned.  grid and iq2_map (IQ2_XXS only): the grid as for

@@ -109,7 +109,7 @@ def test_encoder_entry_points_reject_bad_arguments(lib):
     assert ds4.iq2_map_bytes() == 6561 * 2 + 6561 * 256
     bad = [
         (7, FAKE, 1, 1, 256, None, 0, None, None, FAKE),            # type
-        (ds4.Q8_0, FAKE, 1, 1, 256, None, 0, None, None, FAKE),     # no Q8_0 encoder
+        (ds4.Q4_K, FAKE, 1, 1, 256, None, 0, None, None, FAKE + 8), # Q4_K dst alignment
         (ds4.Q2_K, FAKE, 1, 1, 200, None, 0, None, None, FAKE),     # not whole blocks
         (ds4.Q2_K, FAKE + 4, 1, 1, 256, None, 0, None, None, FAKE), # src alignment
         (ds4.Q2_K, FAKE, 1, 1, 256, None, 0, None, None, FAKE + 2), # Q2_K dst alignment

@@ -58,10 +58,11 @@ def edge_rows(x):
 
 def gpu_quantize(qt, x, imp=None, imp_stride=0, grid_d=None, map_d=None):
     n_mats, rows, cols = x.shape
-    bb = 84 if qt == ds4.Q2_K else 66
+    bb = {ds4.Q2_K: 84, ds4.IQ2_XXS: 66, ds4.Q4_K: 144, ds4.Q8_0: 34}[qt]
+    per = 32 if qt == ds4.Q8_0 else 256
     xd = dev(x)
     impd = None if imp is None else dev(imp)
-    out = torch.zeros(n_mats * rows * cols // 256 * bb, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(n_mats * rows * cols // per * bb, dtype=torch.uint8, device="cuda")
     w = ws()
     ds4.quantize(qt, ptr(xd), n_mats, rows, cols, ptr(impd), imp_stride, ptr(grid_d), ptr(map_d),
                  ptr(out), ptr(w), WS_BYTES, stream())
@@ -195,3 +196,40 @@ def test_column_energy():
     # fp32 sum of 2048 non-negative terms with fused multiply-adds: relative
     # error below 2048 * 2^-24
     np.testing.assert_array_less(np.abs(got - want), want * 2048 * 2.0 ** -24 + 1e-30)
+
+
+# --------------------------------------------------------------------------
+# Q4_K and Q8_0
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["plain", "per-matrix-importance"])
+def test_q4k_and_q80_ragged_stack(mode):
+    x = edge_rows(weights(51, 3, 37, 512))
+    imp, stride = (None, 0) if mode == "plain" else (importance(52, 3, 512), 512)
+    say("q4k", mode, x.shape)
+    got, faults = gpu_quantize(ds4.Q4_K, x, imp, stride)
+    assert faults == 0
+    want = oracle.quantize(oracle.Q4_K, x, imp, imp_stride=stride if imp is not None else None)
+    np.testing.assert_array_equal(got, want)
+    if mode == "plain":
+        say("q80", x.shape)
+        got, faults = gpu_quantize(ds4.Q8_0, x)
+        assert faults == 0
+        np.testing.assert_array_equal(got, oracle.quantize(oracle.Q8_0, x))
+
+
+def test_q4k_representable_and_full_matrix():
+    from test_encode_pins import q4k_representable
+    say("q4k representable + full expert matrix")
+    qb = q4k_representable(53, 32)
+    x = oracle.dequant(oracle.Q4_K, qb).astype(np.float32).reshape(1, 4, 2048)
+    got, faults = gpu_quantize(ds4.Q4_K, x)
+    assert faults == 0
+    np.testing.assert_array_equal(got.reshape(32, 144), qb)
+    x = weights(54, 1, 2048, 4096)
+    imp = importance(55, 1, 4096)[0]
+    got, faults = gpu_quantize(ds4.Q4_K, x, imp, 0)
+    assert faults == 0
+    np.testing.assert_array_equal(got, oracle.quantize(oracle.Q4_K, x, imp))
+    got, faults = gpu_quantize(ds4.Q8_0, x)
+    assert faults == 0
+    np.testing.assert_array_equal(got, oracle.quantize(oracle.Q8_0, x))
