@@ -40,7 +40,7 @@ GATEUP_TRAFFIC = {
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
     "sha256": "792ca20d54e1b097a3d09c33f453b17e5ebab395869035dc1b7164601fab8c12",
-    "bytes": 26273738,
+    "bytes": 26279104,
 }
 
 
@@ -52,7 +52,7 @@ Q4K_GATEUP_TRAFFIC = {
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
     "sha256": "0486a8600abfc2d4e2fccb46ef39296fb9cc9ef89837192438c98732c2a71ca2",
-    "bytes": 56915609,
+    "bytes": 56933204,
 }
 
 
