@@ -186,7 +186,7 @@ def bench_decode_b1(args):
         "expert_gbs": round(gbs, 1), "expert_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
         "kernel_timing": "HIP events recorded by the library around each launch, %d eager steps" % n_prof,
-        "roofline": {"bound": "hbm", "kernel": "k_gateup_iq2_b1", "achieved": round(ach, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_gateup_b1<true>", "achieved": round(ach, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(GATEUP_TRAFFIC),
                      "bytes_per_launch": gateup_bytes},
@@ -339,7 +339,7 @@ def bench_stack(args, mixed=False, shared=False):
                    "timing": "hip-graph replay of one 43-layer step per token"},
         "expert_gbs": round(gbs, 1), "expert_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
-        "roofline": {"bound": "hbm", "kernel": "k_gateup_iq2_b1", "achieved": round(ach, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_gateup_b1<true>", "achieved": round(ach, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(GATEUP_TRAFFIC),
                      "bytes_per_launch": gateup_bytes},
@@ -353,7 +353,7 @@ def bench_stack(args, mixed=False, shared=False):
         n4 = len(w.q4_layers)
         assert kern_us["gateup"] * (w.n_layers - n4) > kern_us_q4["gateup"] * n4
         res["kernels_us_q4k_layers"] = {k: round(v, 3) for k, v in kern_us_q4.items()}
-        res["roofline_q4k"] = {"bound": "hbm", "kernel": "k_gateup_q4k_b1", "achieved": round(a4, 1),
+        res["roofline_q4k"] = {"bound": "hbm", "kernel": "k_gateup_q4k_b1<true>", "achieved": round(a4, 1),
                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": round(a4 / PEAK_HBM_GBS, 4),
                                "traffic": measured_traffic(Q4K_GATEUP_TRAFFIC),
