@@ -39,7 +39,7 @@ GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "792ca20d54e1b097a3d09c33f453b17e5ebab395869035dc1b7164601fab8c12",
+    "sha256": "f945821f09fe5e16ab29aee314f26992237e024680ed0e1d6b27b72d7786ae7f",
     "bytes": 26279104,
 }
 
@@ -51,7 +51,7 @@ Q4K_GATEUP_TRAFFIC = {
                 "bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "0486a8600abfc2d4e2fccb46ef39296fb9cc9ef89837192438c98732c2a71ca2",
+    "sha256": "7c5d97aa84024b5894448ad37220430d245e934887a517bc41cd12af0c57674b",
     "bytes": 56933204,
 }
 

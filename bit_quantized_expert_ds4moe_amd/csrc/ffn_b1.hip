@@ -18,8 +18,9 @@
 //    the bf16 activation.  Grid values (< 128) are exact in bf16, so the
 //    products are exact and only the fp32 accumulation rounds.  The group
 //    scale d*(2s+1)/8 multiplies each 32-value partial sum once.
-//  * The SwiGLU output leaves gate/up as 16-bit fixed point with one scale per
-//    32 values, grouped exactly as the down matvec's lanes consume it.
+//  * The SwiGLU output leaves gate/up in fp32; each down lane turns the 64
+//    values it consumes into 16-bit fixed point with one scale (their
+//    largest magnitude).
 //  * down: a Q2_K code is masked in place inside a 16-bit lane (value 4^s q),
 //    v_dot2_i32_i16 multiplies it with the fixed-point h exactly, the 4^s is
 //    shifted out of the 8-value sum, and the sub-block scale and min are
