@@ -39,8 +39,8 @@ GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "f945821f09fe5e16ab29aee314f26992237e024680ed0e1d6b27b72d7786ae7f",
-    "bytes": 26279104,
+    "sha256": "f2f280e00b1f65ab2ed30de3dbc17e93ce50e825c187ca94a4fa08ca06d9438e",
+    "bytes": 26274150,
 }
 
 
@@ -51,7 +51,7 @@ Q4K_GATEUP_TRAFFIC = {
                 "bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "7c5d97aa84024b5894448ad37220430d245e934887a517bc41cd12af0c57674b",
+    "sha256": "4b150a33c8e8298fd1b8363f13d053c8a6790c2690cff931a667e2427849d8af",
     "bytes": 56933204,
 }
 

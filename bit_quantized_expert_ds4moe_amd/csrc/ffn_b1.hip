@@ -421,7 +421,9 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
   constexpr int kSlots = SH ? 7 : 6;
   constexpr int kChunks = kSlots * kI / 4;  // 16-byte chunks of h
   static_assert(R == 8, "four steps of two rows per wave");
-  __shared__ float4 hs[kChunks];  // 48 KB (56 KB with the shared slot)
+  // with the shared slot the SwiGLU rows are staged in LDS (56 KB); without
+  // it each routed wave reads its own slot's values straight into registers
+  __shared__ float4 hs[SH ? kChunks : 1];
   __shared__ float part[kSlots][kDnBlockRows];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -439,29 +441,50 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
   // the expert id and gate first: the weight addresses wait for the id
   int e = shw ? 0 : load_scalar_i32(ids, k);
   const float wk = shw ? 1.0f : __int_as_float(load_scalar_i32((const int32_t*)wts, k));
-  // 1. h into LDS (slot 6: the shared row)
-  static_assert(kChunks == 4 * NT, "four h chunks per thread");
-  auto src = [&](int q) {
-    const int G = tid + NT * q;
-    return (SH && G >= 6 * kI / 4) ? ((const float4*)sh_h)[G - 6 * kI / 4] : ((const float4*)h)[G];
+  // Lane chunk order of the 64 values a lane consumes: chunk G0 + 8s + m4 of
+  // its slot (16 bytes each) holds values 16s + 4m4 .. +3.
+  const int G0 = 64 * b + 32 * hq + 4 * p;
+  float hv[64];
+  auto take = [&](int s, int m4, float4 q) {
+    hv[16 * s + 4 * m4 + 0] = q.x;
+    hv[16 * s + 4 * m4 + 1] = q.y;
+    hv[16 * s + 4 * m4 + 2] = q.z;
+    hv[16 * s + 4 * m4 + 3] = q.w;
   };
-  const float4 hc0 = src(0), hc1 = src(1), hc2 = src(2), hc3 = src(3);
-  auto put = [&](int q, float4 v) {
-    const int G = tid + NT * q;
-    hs[(G & ~511) | dn_chunk(G & 511)] = v;
-  };
-  put(0, hc0);
-  put(1, hc1);
-  put(2, hc2);
-  put(3, hc3);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (SH) {
+    // 1. h into LDS (slot 6: the shared row)
+    static_assert(kChunks == 4 * NT, "four h chunks per thread");
+    auto src = [&](int q) {
+      const int G = tid + NT * q;
+      return G >= 6 * kI / 4 ? ((const float4*)sh_h)[G - 6 * kI / 4] : ((const float4*)h)[G];
+    };
+    const float4 hc0 = src(0), hc1 = src(1), hc2 = src(2), hc3 = src(3);
+    auto put = [&](int q, float4 v) {
+      const int G = tid + NT * q;
+      hs[(G & ~511) | dn_chunk(G & 511)] = v;
+    };
+    put(0, hc0);
+    put(1, hc1);
+    put(2, hc2);
+    put(3, hc3);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+    // 1. this lane's 64 values of slot k, requested ahead of the weights (the
+    // two wave halves read the same columns)
+    const float4* hk = (const float4*)h + 512 * k;
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+      for (int m4 = 0; m4 < 4; m4++) take(s, m4, hk[G0 + 8 * s + m4]);
+  }
   float pr[R / 2];
   bool h_range = false, bad_id = false;
   if (shw) {
     shared_down_slot(hs + 6 * 512, sh_down, blockIdx.x * kDnBlockRows + rh * R, lane, pr, h_range);
   } else {
-  // 2. this wave's weights, requested only once the whole workgroup has its
-  // h: in the other order the h lines queue behind weight traffic
+  // 2. this wave's weights, requested behind its h (with the shared slot, only
+  // once the whole workgroup has staged h: in the other order the h lines
+  // queue behind weight traffic)
   bad_id = e < 0 || e >= E;
   e = bad_id ? 0 : e;
   const int row0 = blockIdx.x * kDnBlockRows + rh * R;  // output rows of token tok
@@ -476,20 +499,13 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
     sc[m] = *(const uint2*)(blk + 8 * hq);
     dd[m] = *(const uint32_t*)(blk + 80);
   }
+  if constexpr (!SH) __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
   // 3. this lane's 64 values of slot k, as 16-bit fixed point
-  float hv[64];
-  {
-    const int G0 = 64 * b + 32 * hq + 4 * p;  // chunk of s = 0
+  if constexpr (SH) {
 #pragma unroll
     for (int s = 0; s < 4; s++)
 #pragma unroll
-      for (int m4 = 0; m4 < 4; m4++) {
-        const float4 q = hs[512 * k + dn_chunk(G0 + 8 * s + m4)];
-        hv[16 * s + 4 * m4 + 0] = q.x;
-        hv[16 * s + 4 * m4 + 1] = q.y;
-        hv[16 * s + 4 * m4 + 2] = q.z;
-        hv[16 * s + 4 * m4 + 3] = q.w;
-      }
+      for (int m4 = 0; m4 < 4; m4++) take(s, m4, hs[512 * k + dn_chunk(G0 + 8 * s + m4)]);
   }
   uint32_t nr[32];
   int xn[4];
