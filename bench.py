@@ -39,7 +39,7 @@ GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "f2f280e00b1f65ab2ed30de3dbc17e93ce50e825c187ca94a4fa08ca06d9438e",
+    "sha256": "c373c7c8412b55a32e51cbc16cf8a5e1da82c0839c365822fcee649aaa2e3ec2",
     "bytes": 26274150,
 }
 
@@ -51,7 +51,7 @@ Q4K_GATEUP_TRAFFIC = {
                 "bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "4b150a33c8e8298fd1b8363f13d053c8a6790c2690cff931a667e2427849d8af",
+    "sha256": "a6bbb99d253b10709443f5c37263049cb6582361c82b14fbebebf309a1a96b6e",
     "bytes": 56933204,
 }
 

@@ -26,6 +26,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // about 13 tokens of correlated decode (measured crossover 12..16 tokens).
 constexpr int kSharedB1MaxTokens = 4;  // shared expert by per-token matvecs up to here
 constexpr int kFuseSelMaxTokens = 4;  // layer calls: selection fused into gate/up up to here
+// Above this many tokens the batch-1 down stages the SwiGLU vectors in LDS.
+constexpr int kDnStageMinTokens = 4;
 constexpr int kB1MaxTokens = 13;
 constexpr int kSharedSplitG = 16;  // K shares of a shared expert's gate/up in calls of few tokens (<= kMaxSplit)
 constexpr int kSharedSplitD = 4;   // and of its down
@@ -309,10 +311,13 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
       launch_k(k_down_q4k_b1, dgrid, dim3(kDnThreads), 0, st, h, down, dids, wts, s.n_expert, out,
                residual, status);
     else if (shb)
-      launch_k(k_down_q2k_b1<true>, dgrid, dim3(kDnThreadsSh), 0, st, h, down, dids, wts,
+      launch_k(k_down_q2k_b1<true, false>, dgrid, dim3(kDnThreadsSh), 0, st, h, down, dids, wts,
                s.n_expert, out, residual, status, (const float*)shb->h, shb->down);
+    else if (T > kDnStageMinTokens)
+      launch_k(k_down_q2k_b1<false, true>, dgrid, dim3(kDnThreads), 0, st, h, down, dids, wts,
+               s.n_expert, out, residual, status, (const float*)nullptr, (const uint8_t*)nullptr);
     else
-      launch_k(k_down_q2k_b1<false>, dgrid, dim3(kDnThreads), 0, st, h, down, dids, wts,
+      launch_k(k_down_q2k_b1<false, false>, dgrid, dim3(kDnThreads), 0, st, h, down, dids, wts,
                s.n_expert, out, residual, status, (const float*)nullptr, (const uint8_t*)nullptr);
   }
   if ((rc = launched()) != DS4MOE_OK) return rc;

@@ -377,7 +377,7 @@ constexpr int kDnThreadsSh = 14 * 64;      // with the shared expert as a sevent
 // (two more waves): partial sums of rows row0 + 2m + u, m < 4, in pr (the
 // reduce4x2 layout), from the shared SwiGLU row staged in LDS at hsl.
 // Defined with the shared-expert kernels (ffn_shared.hip).
-__device__ void shared_down_slot(const float4* hsl, const uint8_t* sh_down, int row0, int lane,
+__device__ void shared_down_slot(const float4* sh_h, const uint8_t* sh_down, int row0, int lane,
                                  float* pr, bool& h_bad);
 
 __device__ inline int dn_chunk(int G) {
@@ -410,20 +410,15 @@ __device__ inline float reduce4x2(const float* v) {
 
 // SH: a Q8_0 shared expert rides along as a seventh slot (waves 12 and 13,
 // its SwiGLU row sh_h staged with the routed ones), added unscaled.
-template <bool SH>
+template <bool SH, bool STAGE>
 __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
     const float* __restrict__ h, const uint8_t* __restrict__ down,
     const int32_t* __restrict__ ids, const float* __restrict__ wts, int E,
     float* __restrict__ out, float* __restrict__ residual, uint32_t* status,
     const float* __restrict__ sh_h, const uint8_t* __restrict__ sh_down) {
   constexpr int R = kDnRows;
-  constexpr int NT = SH ? kDnThreadsSh : kDnThreads;
   constexpr int kSlots = SH ? 7 : 6;
-  constexpr int kChunks = kSlots * kI / 4;  // 16-byte chunks of h
   static_assert(R == 8, "four steps of two rows per wave");
-  // with the shared slot the SwiGLU rows are staged in LDS (56 KB); without
-  // it each routed wave reads its own slot's values straight into registers
-  __shared__ float4 hs[SH ? kChunks : 1];
   __shared__ float part[kSlots][kDnBlockRows];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -451,24 +446,24 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
     hv[16 * s + 4 * m4 + 2] = q.z;
     hv[16 * s + 4 * m4 + 3] = q.w;
   };
-  if constexpr (SH) {
-    // 1. h into LDS (slot 6: the shared row)
-    static_assert(kChunks == 4 * NT, "four h chunks per thread");
-    auto src = [&](int q) {
-      const int G = tid + NT * q;
-      return G >= 6 * kI / 4 ? ((const float4*)sh_h)[G - 6 * kI / 4] : ((const float4*)h)[G];
-    };
-    const float4 hc0 = src(0), hc1 = src(1), hc2 = src(2), hc3 = src(3);
-    auto put = [&](int q, float4 v) {
-      const int G = tid + NT * q;
-      hs[(G & ~511) | dn_chunk(G & 511)] = v;
-    };
-    put(0, hc0);
-    put(1, hc1);
-    put(2, hc2);
-    put(3, hc3);
+  static_assert(!(SH && STAGE), "the shared slot reads its row directly");
+  // STAGE (many tokens): the six SwiGLU vectors are copied into LDS once per
+  // workgroup and the weights requested after that barrier; at 8 and 12
+  // tokens that took about 1-2% less time than per-wave reads, which read h
+  // twice as often from L2.
+  __shared__ float4 hs[STAGE ? 6 * kI / 4 : 1];
+  if constexpr (STAGE) {
+    static_assert(6 * kI / 4 == 4 * kDnThreads, "four h chunks per thread");
+    float4 hc[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) hc[q] = ((const float4*)h)[tid + kDnThreads * q];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int G = tid + kDnThreads * q;
+      hs[(G & ~511) | dn_chunk(G & 511)] = hc[q];
+    }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  } else {
+  } else if (!shw) {
     // 1. this lane's 64 values of slot k, requested ahead of the weights (the
     // two wave halves read the same columns)
     const float4* hk = (const float4*)h + 512 * k;
@@ -480,11 +475,10 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
   float pr[R / 2];
   bool h_range = false, bad_id = false;
   if (shw) {
-    shared_down_slot(hs + 6 * 512, sh_down, blockIdx.x * kDnBlockRows + rh * R, lane, pr, h_range);
+    shared_down_slot((const float4*)sh_h, sh_down, blockIdx.x * kDnBlockRows + rh * R, lane, pr,
+                     h_range);
   } else {
-  // 2. this wave's weights, requested behind its h (with the shared slot, only
-  // once the whole workgroup has staged h: in the other order the h lines
-  // queue behind weight traffic)
+  // 2. this wave's weights, requested behind its h
   bad_id = e < 0 || e >= E;
   e = bad_id ? 0 : e;
   const int row0 = blockIdx.x * kDnBlockRows + rh * R;  // output rows of token tok
@@ -499,9 +493,9 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
     sc[m] = *(const uint2*)(blk + 8 * hq);
     dd[m] = *(const uint32_t*)(blk + 80);
   }
-  if constexpr (!SH) __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
+  if constexpr (!STAGE) __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
   // 3. this lane's 64 values of slot k, as 16-bit fixed point
-  if constexpr (SH) {
+  if constexpr (STAGE) {
 #pragma unroll
     for (int s = 0; s < 4; s++)
 #pragma unroll

@@ -146,19 +146,20 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_b1(SharedB1Args a) {
   if (h_bad && lane == 0) raise_fault(a.status, DS4MOE_FAULT_F16_RANGE);
 }
 
-// The shared expert's down as the seventh slot of k_down_q2k_b1<true>: rows
+// The shared expert's down as the seventh slot of k_down_q2k_b1<true, false>: rows
 // row0 + 2m + u (m < 4) of the wave, lane L of half u covering columns
-// 64L .. +63 (two Q8_0 blocks); the first two steps' weights are requested
-// before the activations are converted, the last two right after.
-__device__ void shared_down_slot(const float4* hsl, const uint8_t* sh_down, int row0, int lane,
+// 64L .. +63 (two Q8_0 blocks) of the shared SwiGLU row sh_h (global memory);
+// the row's values and the first two steps' weights are requested before the
+// values are converted, the last two steps' weights right after.
+__device__ void shared_down_slot(const float4* sh_h, const uint8_t* sh_down, int row0, int lane,
                                  float* pr, bool& h_bad) {
   const int u = lane >> 5, L = lane & 31;
+  float4 hv[16];
+#pragma unroll
+  for (int q = 0; q < 16; q++) hv[q] = sh_h[16 * L + q];
   uint32_t D0[17], D1[17];
   q80_pair_load(sh_down + (size_t)(row0 + u) * kShRowDn + 68 * L, D0);
   q80_pair_load(sh_down + (size_t)(row0 + 2 + u) * kShRowDn + 68 * L, D1);
-  float4 hv[16];
-#pragma unroll
-  for (int q = 0; q < 16; q++) hv[q] = hsl[dn_chunk(16 * L + q)];
   float mx = 0.0f;
 #pragma unroll
   for (int q = 0; q < 16; q++)
