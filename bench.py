@@ -40,7 +40,7 @@ GATEUP_TRAFFIC = {
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
     "sha256": "c373c7c8412b55a32e51cbc16cf8a5e1da82c0839c365822fcee649aaa2e3ec2",
-    "bytes": 26274150,
+    "bytes": 26271479,
 }
 
 
