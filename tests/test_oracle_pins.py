@@ -451,6 +451,98 @@ def test_rmsnorm_constant_and_scale_invariance():
     np.testing.assert_array_equal(a, b)
 
 
+def rn_bf16_bits(fr):
+    """Bits of the bfloat16 nearest to a Fraction in the normal range, ties to
+    even (Python rounds Fractions half to even)."""
+    if fr == 0:
+        return 0
+    sign = 0x8000 if fr < 0 else 0
+    a = abs(Fraction(fr))
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    n = round(a / Fraction(2) ** (e - 7))   # 128 <= n <= 256
+    if n == 256:
+        n, e = 128, e + 1
+    assert 128 <= n < 256 and -126 <= e <= 127
+    return sign | ((e + 127) << 7) | (n - 128)
+
+
+def frac_sqrt_inv(fr, digits=60):
+    """1/sqrt(fr) to `digits` significant digits, as a Fraction."""
+    getcontext().prec = digits
+    d = Decimal(fr.numerator) / Decimal(fr.denominator)
+    return Fraction(1 / d.sqrt())
+
+
+def test_rmsnorm_hand_values_weight_mean_and_eps():
+    # FLOW § "1 トークンの旅: 全体フロー": each layer normalises the residual
+    # stream before the MoE block.  xn = h * (mean h^2 + eps)^(-1/2) * w, per
+    # element, rounded once to bfloat16.  Hand cases, chosen so that dropping
+    # w, summing h^2 instead of averaging it, moving eps outside the root or
+    # ignoring it each give different bits.
+    # h = (3, 4, 0, 0), w = (2, 1/2, 1, 1), eps = 0: mean h^2 = 25/4, factor
+    # 2/5, xn = (12/5, 4/5, 0, 0) -> bf16 2.40625 and 0.80078125
+    h = np.array([[3.0, 4.0, 0.0, 0.0]], np.float32)
+    w = np.array([2.0, 0.5, 1.0, 1.0], np.float32)
+    xn = oracle.rmsnorm_bf16(h, w, 0.0)
+    assert rn_bf16_bits(Fraction(12, 5)) == 0x401A and rn_bf16_bits(Fraction(4, 5)) == 0x3F4D
+    assert xn.tolist() == [[0x401A, 0x3F4D, 0, 0]]
+    # without w: (6/5, 8/5); with sum instead of mean: (6/5, 2/5)
+    assert rn_bf16_bits(Fraction(6, 5)) != 0x401A and rn_bf16_bits(Fraction(2, 5)) != 0x3F4D
+    # eps inside the root: h = (1, 1), eps = 3 -> (1 + 3)^(-1/2) = 1/2 exactly
+    # (eps outside the root would give 1/4, no eps 1)
+    xn = oracle.rmsnorm_bf16(np.ones((1, 2), np.float32), np.ones(2, np.float32), 3.0)
+    assert xn.tolist() == [[0x3F00, 0x3F00]]
+    # h = (1, 2, 2), eps = 1: mean h^2 = 3, (3 + 1)^(-1/2) = 1/2 -> (1/2, 1, 1)
+    xn = oracle.rmsnorm_bf16(np.array([[1.0, 2.0, 2.0]], np.float32), np.ones(3, np.float32), 1.0)
+    assert xn.tolist() == [[0x3F00, 0x3F80, 0x3F80]]
+    # the layer's eps = 1e-6 moves a small constant row: h = 2^-10 everywhere,
+    # xn = 2^-10 / sqrt(2^-20 + 1e-6) ~= 0.6987 (not 1)
+    c = Fraction(1, 1024)
+    want = rn_bf16_bits(c * frac_sqrt_inv(c * c + Fraction(1e-6)))
+    assert want == 0x3F33
+    xn = oracle.rmsnorm_bf16(np.full((2, 8), 2.0 ** -10, np.float32), np.ones(8, np.float32), 1e-6)
+    assert np.all(xn == want)
+
+
+def test_rmsnorm_rows_and_columns_independent():
+    # each token is normalised by its own mean; each column takes its own
+    # weight: token 1 = 4 x token 0 gives the same xn (eps = 0), and swapping
+    # two columns of h and w swaps the outputs
+    h0 = np.array([1.0, -2.0, 0.5, 3.0, 0.25, -1.5, 2.0, 1.0], np.float32)
+    w = np.array([1.5, 0.75, 2.0, 0.5, 1.0, 3.0, 0.25, 1.25], np.float32)
+    xn = oracle.rmsnorm_bf16(np.stack([h0, 4 * h0]), w, 0.0)
+    np.testing.assert_array_equal(xn[0], xn[1])
+    ms = sum(Fraction(float(v)) ** 2 for v in h0) / 8
+    inv = frac_sqrt_inv(ms)
+    assert xn[0].tolist() == [rn_bf16_bits(Fraction(float(a)) * inv * Fraction(float(b)))
+                              for a, b in zip(h0, w)]
+    p = [1, 0, 2, 3, 4, 5, 7, 6]
+    xp = oracle.rmsnorm_bf16(h0[p][None, :], w[p], 0.0)
+    np.testing.assert_array_equal(xp[0], xn[0][p])
+
+
+def test_residual_add_binary32():
+    # FLOW token flow: the block's output is added to the residual stream,
+    # held in binary32 here, so the sum is rounded once to binary32.
+    r = oracle.residual_add(np.array([1.0, 2.0, -3.0], np.float32),
+                            np.array([10.0, -5.0, 1.0], np.float32))
+    assert r.tolist() == [11.0, -3.0, -2.0]
+    one = np.float32(1.0)
+    r = oracle.residual_add(np.array([1.0, 1.0, 2.0 ** 24, 0.5], np.float32),
+                            np.array([2.0 ** -24, 3 * 2.0 ** -24, 1.0, 0.25], np.float32))
+    # 1 + 2^-24: a tie, to even (1); 1 + 3 * 2^-24: a tie, to even (1 + 2^-22);
+    # 2^24 + 1: a tie, to even (2^24); 0.5 + 0.25 exact
+    assert r[0] == one and r[1] == np.float32(1.0 + 2.0 ** -22)
+    assert r[2] == np.float32(2.0 ** 24) and r[3] == np.float32(0.75)
+    # the second operand is not modified and the first is returned updated
+    out = np.array([2.0, 3.0], np.float32)
+    res = np.array([1.0, 1.0], np.float32)
+    assert oracle.residual_add(res, out).tolist() == [3.0, 4.0]
+    assert out.tolist() == [2.0, 3.0]
+
+
 # --------------------------------------------------------------------------
 # size arithmetic printed on the pages (FLOW config table and decode reads)
 # --------------------------------------------------------------------------
