@@ -145,6 +145,30 @@ __device__ inline double wave_sum_f64(double v) {
   return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
+// ---- largest magnitude with a non-finite check --------------------------------
+// A lane's largest |v| over many values, and whether any of them is NaN or
+// infinite, from their bit patterns alone: the signed maximum of the
+// patterns is the largest positive value (with NaN and +Inf above every
+// finite one), the unsigned maximum the negative value of largest magnitude
+// (NaN and -Inf above every finite one); each stands for the other sign's
+// extreme when no value of its own sign is present.  Two max3 operations per
+// three values.
+struct AbsMax {
+  int smax = (int)0x80000000;  // -0.0
+  uint32_t umax = 0u;          // +0.0
+  __device__ inline void add(float v) {
+    const uint32_t b = __float_as_uint(v);
+    smax = max(smax, (int)b);
+    umax = max(umax, b);
+  }
+  // max |v|; `bad` is set when some value was NaN or infinite
+  __device__ inline float value(bool& bad) const {
+    const uint32_t sp = (uint32_t)smax & 0x7FFFFFFFu, up = umax & 0x7FFFFFFFu;
+    bad = sp >= 0x7F800000u || up >= 0x7F800000u;
+    return fmaxf(__uint_as_float(sp), __uint_as_float(up));
+  }
+};
+
 // ---- device fault word -------------------------------------------------------
 __device__ inline void raise_fault(uint32_t* status, uint32_t bit) { atomicOr(status, bit); }
 

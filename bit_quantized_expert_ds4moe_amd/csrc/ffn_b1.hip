@@ -378,7 +378,7 @@ constexpr int kDnThreadsSh = 14 * 64;      // with the shared expert as a sevent
 // reduce4x2 layout), from the shared SwiGLU row staged in LDS at hsl.
 // Defined with the shared-expert kernels (ffn_shared.hip).
 __device__ void shared_down_slot(const float4* sh_h, const uint8_t* sh_down, int row0, int lane,
-                                 float* pr, bool& h_bad);
+                                 float* pr);
 
 __device__ inline int dn_chunk(int G) {
   return G ^ ((G >> 6) & 3) ^ (((G >> 5) & 1) << 3);
@@ -473,10 +473,9 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
       for (int m4 = 0; m4 < 4; m4++) take(s, m4, hk[G0 + 8 * s + m4]);
   }
   float pr[R / 2];
-  bool h_range = false, bad_id = false;
+  bool bad_id = false;
   if (shw) {
-    shared_down_slot((const float4*)sh_h, sh_down, blockIdx.x * kDnBlockRows + rh * R, lane, pr,
-                     h_range);
+    shared_down_slot((const float4*)sh_h, sh_down, blockIdx.x * kDnBlockRows + rh * R, lane, pr);
   } else {
   // 2. this wave's weights, requested behind its h
   bad_id = e < 0 || e >= E;
@@ -505,10 +504,11 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
   int xn[4];
   float S;
   {
-    float mx = 0.0f;
+    AbsMax am;
 #pragma unroll
-    for (int i = 0; i < 64; i++) mx = fmaxf(mx, fabsf(hv[i]));
-    h_range = !(mx <= 3.0e38f);
+    for (int i = 0; i < 64; i++) am.add(hv[i]);
+    bool nonfinite;
+    const float mx = am.value(nonfinite);
     const float inv = mx > 0.0f ? 1.0f / mx : 0.0f;
 #pragma unroll
     for (int q = 0; q < 32; q++)
@@ -521,7 +521,9 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
       for (int q = 0; q < 8; q++) t = sdot2(nr[8 * s + q], 0x00010001u, t);
       xn[s] = t;
     }
-    S = mx * (1.0f / 32767.0f);
+    // a NaN or infinite SwiGLU value makes every row of the slot NaN, as
+    // the exact products would (the fixed point cannot carry it)
+    S = nonfinite ? __builtin_nanf("") : mx * (1.0f / 32767.0f);
   }
   // 4. the rows
   const float wS = wk * S;
@@ -568,7 +570,6 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
     else out[row] = acc;
   }
   if (bad_id && lane == 0 && blockIdx.x == 0 && rh == 0) raise_fault(status, DS4MOE_FAULT_BAD_ID);
-  if (h_range) raise_fault(status, DS4MOE_FAULT_F16_RANGE);
 }
 
 }  // namespace ds4

@@ -55,11 +55,15 @@ __device__ inline uint32_t q4k_hdr(uint32_t hw) {
 // 32 + ..; sl, sh = sums of the low and high halves; returns the scale S.
 // val(i) gives value i (read twice: for the maximum, then for the packing,
 // so that the 64 values need not be held at once).
+// A NaN or infinite value makes S NaN, so that every product of the lane is
+// NaN, as the exact products would be (the fixed point cannot carry it).
 template <class V>
 __device__ inline float q4k_fix(V val, uint32_t* xl, uint32_t* xh, int& sl, int& sh) {
-  float mx = 0.0f;
+  AbsMax am;
 #pragma unroll
-  for (int i = 0; i < 64; i++) mx = fmaxf(mx, fabsf(val(i)));
+  for (int i = 0; i < 64; i++) am.add(val(i));
+  bool nonfinite;
+  const float mx = am.value(nonfinite);
   const float inv = mx > 0.0f ? 1.0f / mx : 0.0f;
   auto pk = [&](int i, int j) {
     return (uint32_t)__builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_i16(val(i) * inv, val(j) * inv));
@@ -79,7 +83,7 @@ __device__ inline float q4k_fix(V val, uint32_t* xl, uint32_t* xh, int& sl, int&
   }
   sl = a;
   sh = b;
-  return mx * (1.0f / 32767.0f);
+  return nonfinite ? __builtin_nanf("") : mx * (1.0f / 32767.0f);
 }
 
 // Partial dot product of a lane's 64 values of one row with the fixed-point
@@ -259,7 +263,6 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4k_b1(const float* __restr
   uint32_t xl[16], xh[16];
   int sl, sh;
   float S;
-  bool h_range;
   {
     float hv[64];
     const int G0 = 64 * b + 16 * c;  // chunk of value 256b + 64c
@@ -271,10 +274,6 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4k_b1(const float* __restr
       hv[4 * q + 2] = f.z;
       hv[4 * q + 3] = f.w;
     }
-    float mx = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 64; i++) mx = fmaxf(mx, fabsf(hv[i]));
-    h_range = !(mx <= 3.0e38f);
     S = q4k_fix([&](int i) { return hv[i]; }, xl, xh, sl, sh);
   }
   const float wS = wk * S;
@@ -296,7 +295,6 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4k_b1(const float* __restr
     else out[row] = acc;
   }
   if (bad_id && lane == 0 && blockIdx.x == 0 && rh == 0) raise_fault(status, DS4MOE_FAULT_BAD_ID);
-  if (h_range) raise_fault(status, DS4MOE_FAULT_F16_RANGE);
 }
 
 }  // namespace ds4

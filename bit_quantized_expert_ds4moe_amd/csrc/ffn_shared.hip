@@ -112,11 +112,6 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_b1(SharedB1Args a) {
   q80_pair_load(a.down + (size_t)(r0 + u) * kShRowDn + 68 * L, D0);
   q80_pair_load(a.down + (size_t)(r0 + 2 + u) * kShRowDn + 68 * L, D1);
   __builtin_amdgcn_sched_barrier(0);  // all loads ahead of the conversion
-  float mx = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 16; q++)
-    mx = fmaxf(fmaxf(fmaxf(mx, fabsf(hv[q].x)), fmaxf(fabsf(hv[q].y), fabsf(hv[q].z))), fabsf(hv[q].w));
-  const bool h_bad = !(mx <= 3.0e38f);
   auto hval = [&](int i) {
     const float4 q = hv[i >> 2];
     return (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
@@ -143,7 +138,6 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_b1(SharedB1Args a) {
     const float tot = lane == 0 ? t0 : lane == 1 ? t1 : lane == 2 ? t2 : t3;
     a.out[(size_t)t * kH + r0 + lane] += tot;
   }
-  if (h_bad && lane == 0) raise_fault(a.status, DS4MOE_FAULT_F16_RANGE);
 }
 
 // The shared expert's down as the seventh slot of k_down_q2k_b1<true, false>: rows
@@ -152,7 +146,7 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_b1(SharedB1Args a) {
 // the row's values and the first two steps' weights are requested before the
 // values are converted, the last two steps' weights right after.
 __device__ void shared_down_slot(const float4* sh_h, const uint8_t* sh_down, int row0, int lane,
-                                 float* pr, bool& h_bad) {
+                                 float* pr) {
   const int u = lane >> 5, L = lane & 31;
   float4 hv[16];
 #pragma unroll
@@ -160,11 +154,6 @@ __device__ void shared_down_slot(const float4* sh_h, const uint8_t* sh_down, int
   uint32_t D0[17], D1[17];
   q80_pair_load(sh_down + (size_t)(row0 + u) * kShRowDn + 68 * L, D0);
   q80_pair_load(sh_down + (size_t)(row0 + 2 + u) * kShRowDn + 68 * L, D1);
-  float mx = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 16; q++)
-    mx = fmaxf(fmaxf(fmaxf(mx, fabsf(hv[q].x)), fmaxf(fabsf(hv[q].y), fabsf(hv[q].z))), fabsf(hv[q].w));
-  h_bad = !(mx <= 3.0e38f);
   auto hval = [&](int i) {
     const float4 q = hv[i >> 2];
     return (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;

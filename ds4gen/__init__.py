@@ -19,8 +19,11 @@ ROUTER_W, ROUTER_B, GATE, UP, DOWN, SH_GATE, SH_UP, SH_DOWN, GRID, X, TID2EID, N
     ROUTE, GATES, COMMON, TOKID, RANKPERM = range(1, 18)
 
 Q2_K, IQ2_XXS, Q8_0, Q4_K = 0, 1, 2, 3
-BLOCK_BYTES = {Q2_K: 84, IQ2_XXS: 66, Q8_0: 34, Q4_K: 144}
-BLOCK_VALUES = {Q2_K: 256, IQ2_XXS: 256, Q8_0: 32, Q4_K: 256}
+# generator-only: Q2_K bytes drawn so that the decoded weights are zero-mean
+# (dmin ~ U[3e-3, 1.35e-2] instead of the configs' U[0, 5e-3])
+Q2_K_ZM = 4
+BLOCK_BYTES = {Q2_K: 84, IQ2_XXS: 66, Q8_0: 34, Q4_K: 144, Q2_K_ZM: 84}
+BLOCK_VALUES = {Q2_K: 256, IQ2_XXS: 256, Q8_0: 32, Q4_K: 256, Q2_K_ZM: 256}
 
 _host = None
 _dev = None
@@ -156,6 +159,7 @@ class Workload:
     routing: str = "router"   # "router" | "given-zipf"
     corr: float = 0.0         # token correlation (alpha) for batched decode
     q4_layers: tuple = ()     # layers whose routed experts are all Q4_K
+    q2k_zero_mean: bool = False  # Q2_K blocks drawn zero-mean (a named variant)
 
     def at_layer(self, layer):
         """The description of one layer of a stack: the same workload, with
@@ -182,6 +186,12 @@ class Workload:
         return {"gate": self.gate_qt, "up": self.up_qt, "down": self.down_qt,
                 "sh_gate": Q8_0, "sh_up": Q8_0, "sh_down": Q8_0}[which]
 
+    def gen_qtype(self, which):
+        """The generator's block kind for a tensor: its format, with Q2_K drawn
+        zero-mean in the zero-mean variant."""
+        qt = self.qtype(which)
+        return Q2_K_ZM if (qt == Q2_K and self.q2k_zero_mean) else qt
+
     def expert_bytes(self):
         b = self.blocks_per_expert
         return (b["gate"] * BLOCK_BYTES[self.gate_qt] + b["up"] * BLOCK_BYTES[self.up_qt]
@@ -202,6 +212,10 @@ WORKLOADS = [
     Workload("v4flash-43-layer-stack-decode-b1-q4k-37-42", 5, 1, 4096, 2048, 256, 6, IQ2_XXS,
              IQ2_XXS, Q2_K, "bf16", "f16", n_layers=43, n_hash=3, steps=256,
              q4_layers=(37, 38, 39, 40, 41, 42)),
+    # the 2-bit stack with zero-mean Q2_K down blocks (a departure from the
+    # stated dmin range, kept as a named variant)
+    Workload("v4flash-43-layer-stack-decode-b1-zero-mean-q2k", 6, 1, 4096, 2048, 256, 6, IQ2_XXS,
+             IQ2_XXS, Q2_K, "bf16", "f16", n_layers=43, n_hash=3, steps=256, q2k_zero_mean=True),
 ]
 
 KIND = {"gate": GATE, "up": UP, "down": DOWN, "sh_gate": SH_GATE, "sh_up": SH_UP,
@@ -211,7 +225,7 @@ KIND = {"gate": GATE, "up": UP, "down": DOWN, "sh_gate": SH_GATE, "sh_up": SH_UP
 def expert_tensor_blocks(w, layer, which, first_expert, n_experts):
     """Host bytes of experts [first, first+n) of one stacked tensor."""
     w = w.at_layer(layer)
-    qt = w.qtype(which)
+    qt = w.gen_qtype(which)
     bpe = w.blocks_per_expert[which] if not which.startswith("sh_") else w.I * w.H // 32
     return blocks(qt, w.seed, stream(layer, KIND[which]), first_expert * bpe, n_experts * bpe)
 

@@ -20,7 +20,7 @@ def _stream():
 def expert_tensor(w, layer, which, n_experts=None):
     """All experts of one stacked tensor, filled on the device."""
     w = w.at_layer(layer)
-    qt = w.qtype(which)
+    qt = w.gen_qtype(which)
     if which.startswith("sh_"):
         n_experts = 1
         bpe = w.I * w.H // g.BLOCK_VALUES[qt]

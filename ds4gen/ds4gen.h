@@ -59,8 +59,11 @@ enum {
   DS4GEN_RANKPERM = 17  /* expert popularity rank permutation           */
 };
 
-/* Block formats the generator can emit (byte sizes per block). */
-enum { DS4GEN_Q2_K = 0, DS4GEN_IQ2_XXS = 1, DS4GEN_Q8_0 = 2, DS4GEN_Q4_K = 3 };
+/* Block formats the generator can emit (byte sizes per block).  Q2_K_ZM is
+ * not a format of its own: Q2_K bytes drawn with a larger dmin range, so that
+ * the decoded weights are zero-mean (a named stack variant; the configs state
+ * dmin in [0, 5e-3]). */
+enum { DS4GEN_Q2_K = 0, DS4GEN_IQ2_XXS = 1, DS4GEN_Q8_0 = 2, DS4GEN_Q4_K = 3, DS4GEN_Q2_K_ZM = 4 };
 #define DS4GEN_Q2K_BYTES 84
 #define DS4GEN_IQ2_BYTES 66
 #define DS4GEN_Q80_BYTES 34
@@ -154,17 +157,19 @@ GEN_HD void gen_put_u16(uint8_t* p, uint16_t v) {
 /*
  * Q2_K-format block number `blk` of a tensor stream (84 bytes):
  * bytes 0..15 scale|min nibbles, 16..79 two-bit codes (all uniform random),
- * 80..81 fp16 d ~ U[1e-3,1e-2], 82..83 fp16 dmin ~ U[3e-3,1.35e-2].
- * E[dmin] = 1.5 E[d] = E[d] E[code] makes E[dmin*min] = E[d*scale*code]
- * (scale and min nibbles share a distribution): the decoded weights are
- * zero-mean, as a quantised weight matrix is, with RMS about 0.09.
- * Draw indices 12*blk + 0..11.
+ * 80..81 fp16 d ~ U[1e-3,1e-2], 82..83 fp16 dmin ~ U[dmin_lo, dmin_hi].
+ * The configs state dmin in [0, 5e-3]; the decoded weights then have mean
+ * about 0.043 and RMS about 0.09.  The zero-mean variant draws dmin from
+ * [3e-3, 1.35e-2]: E[dmin] = 1.5 E[d] = E[d] E[code] makes E[dmin*min] =
+ * E[d*scale*code] (scale and min nibbles share a distribution), RMS about
+ * 0.09.  Draw indices 12*blk + 0..11.
  */
-GEN_HD void gen_q2k_block(uint64_t key, uint64_t blk, uint8_t* out) {
+GEN_HD void gen_q2k_block(uint64_t key, uint64_t blk, uint8_t* out, double dmin_lo,
+                          double dmin_hi) {
   uint64_t base = blk * 12ULL;
   for (int j = 0; j < 10; j++) gen_put_u64(out + 8 * j, gen_draw(key, base + j));
   gen_put_u16(out + 80, gen_f16(gen_uniform(gen_draw(key, base + 10), 1e-3, 1e-2)));
-  gen_put_u16(out + 82, gen_f16(gen_uniform(gen_draw(key, base + 11), 3e-3, 1.35e-2)));
+  gen_put_u16(out + 82, gen_f16(gen_uniform(gen_draw(key, base + 11), dmin_lo, dmin_hi)));
 }
 
 /*
@@ -211,7 +216,7 @@ GEN_HD void gen_q4k_block(uint64_t key, uint64_t blk, uint8_t* out) {
 }
 
 GEN_HD int gen_block_bytes(int qtype) {
-  return qtype == DS4GEN_Q2_K ? DS4GEN_Q2K_BYTES
+  return (qtype == DS4GEN_Q2_K || qtype == DS4GEN_Q2_K_ZM) ? DS4GEN_Q2K_BYTES
        : qtype == DS4GEN_IQ2_XXS ? DS4GEN_IQ2_BYTES
        : qtype == DS4GEN_Q4_K ? DS4GEN_Q4K_BYTES
        : DS4GEN_Q80_BYTES;
@@ -220,7 +225,8 @@ GEN_HD int gen_block_bytes(int qtype) {
 GEN_HD int gen_block_values(int qtype) { return qtype == DS4GEN_Q8_0 ? 32 : 256; }
 
 GEN_HD void gen_block(int qtype, uint64_t key, uint64_t blk, uint8_t* out) {
-  if (qtype == DS4GEN_Q2_K) gen_q2k_block(key, blk, out);
+  if (qtype == DS4GEN_Q2_K) gen_q2k_block(key, blk, out, 0.0, 5e-3);
+  else if (qtype == DS4GEN_Q2_K_ZM) gen_q2k_block(key, blk, out, 3e-3, 1.35e-2);
   else if (qtype == DS4GEN_IQ2_XXS) gen_iq2_block(key, blk, out);
   else if (qtype == DS4GEN_Q4_K) gen_q4k_block(key, blk, out);
   else gen_q80_block(key, blk, out);

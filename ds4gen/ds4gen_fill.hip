@@ -48,6 +48,9 @@ extern "C" __attribute__((visibility("default"))) int ds4gen_dev_blocks(
   if (qtype == DS4GEN_Q2_K)
     hipLaunchKernelGGL((gen_fill_kernel<DS4GEN_Q2_K, DS4GEN_Q2K_BYTES>), dim3((unsigned)grid),
                        dim3(FILL_THREADS), 0, st, key, first, n, o);
+  else if (qtype == DS4GEN_Q2_K_ZM)
+    hipLaunchKernelGGL((gen_fill_kernel<DS4GEN_Q2_K_ZM, DS4GEN_Q2K_BYTES>), dim3((unsigned)grid),
+                       dim3(FILL_THREADS), 0, st, key, first, n, o);
   else if (qtype == DS4GEN_IQ2_XXS)
     hipLaunchKernelGGL((gen_fill_kernel<DS4GEN_IQ2_XXS, DS4GEN_IQ2_BYTES>), dim3((unsigned)grid),
                        dim3(FILL_THREADS), 0, st, key, first, n, o);

@@ -198,6 +198,8 @@ EXPORT int or_dequant(int qt, const uint8_t* blocks, int64_t n_blocks, const uin
                       double* out) {
   if (qt < 0 || qt > 3 || (qt == OR_IQ2_XXS && !grid)) return OR_EINVAL;
   int bb = block_bytes(qt), bv = block_vals(qt);
+  /* blocks are independent: threads split them, results do not change */
+#pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n_blocks; i++) {
     const uint8_t* b = blocks + i * bb;
     double* y = out + i * bv;

@@ -37,6 +37,23 @@ def check_clean(ws):
     assert f == 0, "device fault bits 0x%x" % f
 
 
+def covering_tokens(ids, extra=()):
+    """Tokens whose routes together touch every expert that any token uses
+    (greedy set cover), plus `extra`: checking their whole outputs checks
+    every touched expert's gate, up and down at least once."""
+    ids = np.asarray(ids)
+    left = set(np.unique(ids).tolist())
+    rows = [set(r.tolist()) for r in ids]
+    toks = set(int(t) for t in extra)
+    for t in toks:
+        left -= rows[t]
+    while left:
+        best = max(range(len(rows)), key=lambda t: len(left & rows[t]))
+        toks.add(best)
+        left -= rows[best]
+    return np.array(sorted(toks))
+
+
 def max_rel_err(got, want):
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)

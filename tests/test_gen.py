@@ -6,7 +6,7 @@ import oracle
 
 
 def test_blocks_are_random_access_and_deterministic():
-    for qt in (ds4gen.Q2_K, ds4gen.IQ2_XXS, ds4gen.Q8_0, ds4gen.Q4_K):
+    for qt in (ds4gen.Q2_K, ds4gen.IQ2_XXS, ds4gen.Q8_0, ds4gen.Q4_K, ds4gen.Q2_K_ZM):
         a = ds4gen.blocks(qt, 7, 3, 100, 20)
         b = ds4gen.blocks(qt, 7, 3, 110, 5)
         bb = ds4gen.BLOCK_BYTES[qt]
@@ -15,10 +15,19 @@ def test_blocks_are_random_access_and_deterministic():
 
 
 def test_block_field_ranges():
+    # Q2_K as the configs state it: d in [1e-3, 1e-2], dmin in [0, 5e-3]
     q = ds4gen.blocks(ds4gen.Q2_K, 1, 5, 0, 2000).reshape(2000, 84)
     d = q[:, 80:82].copy().view(np.float16).astype(np.float64).ravel()
     dmin = q[:, 82:84].copy().view(np.float16).astype(np.float64).ravel()
     assert d.min() >= 1e-3 * (1 - 2 ** -10) and d.max() <= 1e-2 * (1 + 2 ** -10)
+    assert dmin.min() >= 0.0 and dmin.max() <= 5e-3 * (1 + 2 ** -10)
+    assert dmin.min() < 1e-5 and dmin.max() > 4.9e-3      # spans the range
+    nib = np.concatenate([q[:, :16] & 15, q[:, :16] >> 4])
+    assert nib.min() == 0 and nib.max() == 15
+    # the zero-mean variant: same bytes but for dmin in [3e-3, 1.35e-2]
+    qz = ds4gen.blocks(ds4gen.Q2_K_ZM, 1, 5, 0, 2000).reshape(2000, 84)
+    np.testing.assert_array_equal(qz[:, :82], q[:, :82])
+    dmin = qz[:, 82:84].copy().view(np.float16).astype(np.float64).ravel()
     assert dmin.min() >= 3e-3 * (1 - 2 ** -10) and dmin.max() <= 1.35e-2 * (1 + 2 ** -10)
     iq = ds4gen.blocks(ds4gen.IQ2_XXS, 1, 3, 0, 2000).reshape(2000, 66)
     d = iq[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
@@ -37,16 +46,20 @@ def test_block_field_ranges():
     assert set(np.unique(g).tolist()) == {8, 25, 43}
 
 
-def test_decoded_weights_are_zero_mean():
-    # every weight format decodes to a zero-mean matrix of RMS 0.07-0.1, so
-    # that a deep stack keeps its residual stream free of a common direction
+def test_decoded_weight_statistics():
+    # IQ2_XXS (sign-symmetric), Q4_K (dmin drawn so that E[dmin*m] =
+    # E[d*sc*q]) and the zero-mean Q2_K variant decode to zero-mean matrices of
+    # RMS 0.07-0.1; Q2_K as the configs state it (dmin in [0, 5e-3]) has RMS
+    # about 0.09 and mean
+    # E[d] E[sc] E[q] - E[dmin] E[m] = 5.5e-3 * 7.5 * 1.5 - 2.5e-3 * 7.5 ~= 0.043
     grid = ds4gen.grid(1)
-    for qt, lo, hi in ((ds4gen.Q2_K, 0.085, 0.1), (ds4gen.IQ2_XXS, 0.07, 0.09),
-                       (ds4gen.Q4_K, 0.065, 0.085)):
-        v = oracle.dequant(qt, ds4gen.blocks(qt, 1, 9, 0, 4000), grid=grid)
+    for qt, lo, hi, mean in ((ds4gen.Q2_K, 0.085, 0.1, 0.0431), (ds4gen.Q2_K_ZM, 0.085, 0.1, 0.0),
+                             (ds4gen.IQ2_XXS, 0.07, 0.09, 0.0), (ds4gen.Q4_K, 0.065, 0.085, 0.0)):
+        dq = ds4gen.Q2_K if qt == ds4gen.Q2_K_ZM else qt
+        v = oracle.dequant(dq, ds4gen.blocks(qt, 1, 9, 0, 4000), grid=grid)
         rms = np.sqrt(np.mean(v * v))
         assert lo < rms < hi, (qt, rms)
-        assert abs(v.mean()) < 0.02 * rms, (qt, v.mean(), rms)
+        assert abs(v.mean() - mean) < 0.02 * rms, (qt, v.mean(), rms)
 
 
 def test_rounding_matches_independent_conversions():

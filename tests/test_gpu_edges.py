@@ -8,8 +8,8 @@ import torch
 import bit_quantized_expert_ds4moe_amd as ds4
 import ds4gen as g
 import oracle
-from gpu_util import (TOL_FP32, check_clean, experts_of, max_rel_err, ptr, say, shape_of, stream,
-                      workspace)
+from gpu_util import (TOL_FP32, check_clean, covering_tokens, experts_of, max_rel_err, ptr, say,
+                      shape_of, stream, workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,7 +74,9 @@ def test_max_tokens():
     counts = np.bincount(ids.ravel(), minlength=w.E)
     heavy = int(np.argmax(counts))
     t_heavy = int(np.where((ids == heavy).any(1))[0][-1])
-    toks = np.array([0, T // 2, t_heavy, T - 1])
+    # every touched expert through at least one checked token, and the last
+    # pair of the heaviest expert
+    toks = covering_tokens(ids, extra=(0, T // 2, t_heavy, T - 1))
     want = oracle.moe_ffn(x, "bf16", ids, wts, host_experts(w, 0, np.unique(ids[toks])),
                           (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed),
                           tokens=toks)

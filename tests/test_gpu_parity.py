@@ -8,8 +8,8 @@ import torch
 import bit_quantized_expert_ds4moe_amd as ds4
 import ds4gen as g
 import oracle
-from gpu_util import (TOL_FP32, check_clean, experts_of, max_rel_err, ptr, say, shape_of,
-                      shared_of, stream, workspace, x_dtype, x_fmt)
+from gpu_util import (TOL_FP32, check_clean, covering_tokens, experts_of, max_rel_err, ptr, say,
+                      shape_of, shared_of, stream, workspace, x_dtype, x_fmt)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def dev(a):
 # --------------------------------------------------------------------------
 # generator: device fill == host bytes
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("qt", [g.Q2_K, g.IQ2_XXS, g.Q8_0, g.Q4_K])
+@pytest.mark.parametrize("qt", [g.Q2_K, g.IQ2_XXS, g.Q8_0, g.Q4_K, g.Q2_K_ZM])
 def test_device_fill_matches_host(qt):
     say("device fill qt", qt)
     n, first = 1000 + 37, 12345
@@ -241,6 +241,13 @@ def test_ffn_v4_decode_b1():
     assert ffn_case(1, 1) <= TOL_FP32
 
 
+@pytest.mark.parametrize("T", [2, 3, 4, 5])
+def test_ffn_v4_decode_few_tokens(T):
+    # the matvec kernels with one grid row per token: the down kernel's
+    # per-wave SwiGLU reads up to 4 tokens, LDS staging from 5; every output
+    assert ffn_case(1, T) <= TOL_FP32
+
+
 @pytest.mark.parametrize("tok", [1, 2, 3])
 def test_ffn_v4_decode_b1_more_tokens(tok):
     from ds4gen.device import make_layer, host_experts
@@ -372,6 +379,44 @@ def test_layer_route_and_ffn(widx):
     assert err <= TOL_FP32
 
 
+@pytest.mark.parametrize("widx", [1, "q4k-t3", "b8-t2"])
+def test_ffn_nonfinite_activation_propagates(widx):
+    # a NaN (token 1) or an infinity (token 2) in x makes that token's whole
+    # output NaN, as the exact products would (every down row sums over every
+    # SwiGLU value); the other tokens are unaffected and no fault bit is set.
+    # Paths: IQ2_XXS/Q2_K matvecs (3 tokens), Q4_K matvecs (3 tokens), and the
+    # Q8_0 shared expert's matvecs (2 tokens)
+    from dataclasses import replace
+    from ds4gen.device import make_layer, host_experts, host_shared
+    w = _layer_workload(widx)
+    if widx == 1:
+        w = replace(w, T=3)
+    T = w.T
+    say("non-finite x", w.name, "T", T)
+    lt = make_layer(w, 0)
+    x = g.activations(w, n_tok=T)
+    ids, wts, _, _ = oracle.route(x, "bf16", g.router_weight(w, 0), "f16", g.router_bias(w, 0), w.K)
+    bad = x.copy()
+    bad[1, 100] = 0x7FC0            # bf16 quiet NaN
+    if T > 2:
+        bad[2, 3000] = 0xFF80       # bf16 -Inf
+    shp = shape_of(w)
+    ws, nb = workspace(shp, T)
+    out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    xd, idd, wd = dev(bad), dev(ids), dev(wts)
+    ds4.expert_ffn(shp, experts_of(lt, w), shared_of(lt, w), ptr(xd), ds4.BF16, T, ptr(idd),
+                   ptr(wd), ptr(out), None, ptr(ws), nb, stream())
+    check_clean(ws)
+    got = out.cpu().numpy()
+    assert np.isnan(got[1:]).all()
+    want = oracle.moe_ffn(x, "bf16", ids, wts, host_experts(w, 0, np.unique(ids[0])),
+                          (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed),
+                          tokens=[0], shared=host_shared(w, 0) if w.shared else None, sh_I=w.I)
+    err = max_rel_err(got[:1], want)
+    say("  clean token max|err|/rms =", err)
+    assert err <= TOL_FP32
+
+
 def test_layer_graph_replays_match_eager():
     """Captured layer calls replayed several times, with eager work and
     synchronisations in between, must reproduce the eager results bit for bit."""
@@ -451,19 +496,15 @@ def test_grouped_ragged_items_all_outputs():
     grouped_case(w, ids, wts)
 
 
-def test_grouped_prefill_512_zipf_sampled():
-    # the prefill workload: 512 tokens, 256 experts, Zipf(1.1) routing; outputs of
-    # tokens that hit the most and the least loaded experts are checked
+def test_grouped_prefill_512_zipf_every_expert():
+    # the prefill workload: 512 tokens, 256 experts, Zipf(1.1) routing; every
+    # output of a set of tokens whose routes cover all touched experts (about
+    # 108 tokens for the 246 experts) and of the first and last token
     w = g.WORKLOADS[3]
-    say("prefill 512")
     ids, wts = g.zipf_routing(w.seed, w.T, w.E, w.K)
-    counts = np.bincount(ids.ravel(), minlength=w.E)
-    heavy = int(np.argmax(counts))
-    light = [e for e in np.argsort(counts) if counts[e] > 0][0]
-    t_heavy = int(np.where((ids == heavy).any(1))[0][0])
-    t_light = int(np.where((ids == light).any(1))[0][0])
-    grouped_case(w, ids, wts, tokens_for_oracle=[0, t_heavy, t_light, w.T - 1],
-                 tol=TOL_FP32)
+    toks = covering_tokens(ids, extra=(0, w.T - 1))
+    say("prefill 512: %d tokens cover %d experts" % (toks.size, np.unique(ids).size))
+    grouped_case(w, ids, wts, tokens_for_oracle=toks, tol=TOL_FP32)
 
 
 def _grouped_fast_case(zero_d):
@@ -594,8 +635,8 @@ def test_ffn_q4k_experts(T):
     # V4-Flash expert shape with gate/up/down all in Q4_K, and the mixed form
     # (IQ2_XXS gate/up, Q4_K down): the matvec kernels at 1 and 5 tokens
     # (learned routing), the grouped MFMA kernels at 40 (learned routing) and
-    # 512 (Zipf-routed prefill, outputs of the first and last tokens and of
-    # tokens on the most and least loaded experts)
+    # 512 (Zipf-routed prefill); above 5 tokens every output of tokens that
+    # together cover every touched expert
     for qts in ((g.Q4_K, g.Q4_K, g.Q4_K), (g.IQ2_XXS, g.IQ2_XXS, g.Q4_K)):
         w = g.Workload("q4k", 31, T, 4096, 2048, 256, 6, *qts, "bf16", "f16")
         say("ffn q4k", qts, "T", T)
@@ -616,12 +657,8 @@ def test_ffn_q4k_experts(T):
         check_clean(ws)
         if T <= 5:
             toks = np.arange(min(T, 2))
-        else:
-            counts = np.bincount(ids.ravel(), minlength=w.E)
-            heavy = int(np.argmax(counts))
-            light = [e for e in np.argsort(counts) if counts[e] > 0][0]
-            toks = np.unique([0, T - 1, int(np.where((ids == heavy).any(1))[0][0]),
-                              int(np.where((ids == light).any(1))[0][0])])
+        else:  # every touched expert through at least one checked token
+            toks = covering_tokens(ids, extra=(0, T - 1))
         want = oracle.moe_ffn(x, "bf16", ids, wts, host_experts(w, 0, np.unique(ids[toks])), qts,
                               w.H, w.I, w.E, grid=g.grid(w.seed), tokens=toks)
         err = max_rel_err(out.cpu().numpy()[toks], want)
