@@ -267,7 +267,8 @@ bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x, int
 ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x,
                         int32_t T, const int32_t* ids_in, const float4* kbuf, int32_t* ids,
                         const float* wts, float* out, float* residual, void* ws, const Layout& L,
-                        hipStream_t st, const SharedB1Args* shb = nullptr) {
+                        hipStream_t st, const SharedB1Args* shb = nullptr,
+                        const ds4moe_router* rt = nullptr) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   float* h = at<float>(ws, L.h);
   GateUpB1Args g{};
@@ -280,6 +281,11 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   g.scale = s.routed_scale;
   g.ids_out = ids;
   g.wts_out = const_cast<float*>(wts);
+  if (rt) {
+    g.rw = rt->w;
+    g.rw_dt = rt->w_dtype;
+    g.rbias = rt->bias;
+  }
   g.E = s.n_expert;
   g.h = h;
   g.status = status;
@@ -397,7 +403,8 @@ ds4moe_status launch_imatrix(const ds4moe_shape& s, const ImxOut& o, const void*
 ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_experts* sh,
                      const void* x, int32_t x_dt, int32_t T, const int32_t* ids, const float* wts,
                      float* out, float* residual, int32_t* perm_dbg, void* ws, const Layout& L,
-                     hipStream_t st, const ImxOut* imx = nullptr, const float4* kbuf_sel = nullptr) {
+                     hipStream_t st, const ImxOut* imx = nullptr, const float4* kbuf_sel = nullptr,
+                     const ds4moe_router* rt = nullptr) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   const bool b1 = fast_b1(s, ex, x, x_dt, T) && (!sh || grouped_eligible(s, ex, sh, x, x_dt, T));
   if (b1) {
@@ -419,7 +426,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     // writes ids and wts (workspace buffers then)
     ds4moe_status rc =
         kbuf_sel ? launch_b1(s, ex, x, T, nullptr, kbuf_sel, const_cast<int32_t*>(ids), wts, out,
-                             residual, ws, L, st, shb1 ? &sa : nullptr)
+                             residual, ws, L, st, shb1 ? &sa : nullptr, rt)
                  : launch_b1(s, ex, x, T, ids, nullptr, nullptr, wts, out, residual, ws, L, st,
                              shb1 ? &sa : nullptr);
     if (rc == DS4MOE_OK && perm_dbg)  // the few-token path needs no permutation: make it for the caller
@@ -763,9 +770,11 @@ DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_la
                 desc->norm_eps, norm ? xn : nullptr, n_tok, token_ids, ids, wts, ws, L, stream,
                 !fuse);
   if (rc != DS4MOE_OK) return rc;
+  // the fused selection reads the router input fx (the normalised row when
+  // norm: the scoring wrote it to the workspace) for exact recomputations
   rc = do_ffn(*shape, desc->routed, sh, fx, fdt, n_tok, ids, wts, norm ? nullptr : out,
               norm ? residual : nullptr, nullptr, ws, L, stream, nullptr,
-              fuse ? at<float4>(ws, L.kbuf) : nullptr);
+              fuse ? at<float4>(ws, L.kbuf) : nullptr, fuse ? &r : nullptr);
   if (rc != DS4MOE_OK) return rc;
   if (ids_dbg &&
       hipMemcpyAsync(ids_dbg, ids, sizeof(int32_t) * n_tok * shape->top_k, hipMemcpyDeviceToDevice,

@@ -188,6 +188,9 @@ struct GateUpB1Args {
   float scale;
   int32_t* ids_out;        // [6] (selection)
   float* wts_out;          // [6] (selection)
+  const void* rw;          // router weights [E][4096] and their dtype, and the
+  int rw_dt;               // selection bias [E] (selection: for the exact
+  const float* rbias;      // recomputation of keys the intervals leave open)
   int E;
   float* h;                // [6][2048] SwiGLU output
   uint32_t* status;
@@ -283,7 +286,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
     int e;
     float g;
     const bool first = blockIdx.x == 0;  // one reporter per token
-    select_wave(a.kbuf + (size_t)blockIdx.y * a.E, a.E, 6, a.scale, a.status, first, e, g);
+    const RouteSrc src{xtok, DS4MOE_BF16, a.rw, a.rw_dt, a.rbias, kH};
+    select_wave(a.kbuf + (size_t)blockIdx.y * a.E, a.E, 6, a.scale, a.status, first, src, e, g);
     if (lane < 6) {
       sel_e[lane] = e;
       if (first) {

@@ -154,7 +154,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_q4k_b1(GateUpB1Args a)
       int e;
       float g;
       const bool first = blockIdx.x == 0;  // one reporter per token
-      select_wave(a.kbuf + (size_t)blockIdx.y * a.E, a.E, 6, a.scale, a.status, first, e, g);
+      const RouteSrc src{xtok, DS4MOE_BF16, a.rw, a.rw_dt, a.rbias, kH};
+      select_wave(a.kbuf + (size_t)blockIdx.y * a.E, a.E, 6, a.scale, a.status, first, src, e, g);
       if (lane < 6) {
         sel_e[lane] = e;
         if (first) {

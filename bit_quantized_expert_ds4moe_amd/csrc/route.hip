@@ -15,9 +15,15 @@
 // relative error far below 2^-44, giving an interval for the score, and the
 // key interval follows because rounding is monotone.  The selection is
 // accepted when every interval is a single binary32 value, or when the chosen
-// order holds for every value in the intervals; otherwise the status bit
-// DS4MOE_FAULT_UNCERTIFIED is raised.  Scoring and selection are two kernels:
-// the kernel boundary publishes the scores without any in-kernel fence.
+// order holds for every value in the intervals.  Otherwise (rare: a logit or
+// score within the error bound of a binary32 rounding point, next to the
+// selection's cut) the selecting wave recomputes the keys of every expert
+// that could still be selected exactly: the logit as an integer-limb sum of
+// the exact products (integer additions are associative, so any summation
+// order gives the same bits), rounded once; the score in double-double
+// arithmetic with its rounding decided against an error bound of 2^-90.
+// Scoring and selection are two kernels: the kernel boundary publishes the
+// scores without any in-kernel fence.
 #include "dev_common.h"
 #include "ssp64.h"
 
@@ -104,6 +110,136 @@ __device__ inline float readlane_f32(float v, int lane) {
 }
 
 constexpr int kMaxRouteK = 16;
+
+// Where the router input and weights of one token live, for the exact
+// recomputation of a logit by the selecting wave.
+struct RouteSrc {
+  const void* x;      // the token's router input row: bf16 bits or fp32
+  int x_dt;
+  const void* W;      // [E][H] f16 bits or fp32
+  int w_dt;
+  const float* bias;  // [E]
+  int H;
+};
+
+// ---- exact logit --------------------------------------------------------
+// Every product of a router input and a router weight is a product of two
+// binary32 values (bf16 and f16 values are binary32 values): an integer
+// m < 2^48 times 2^e, e >= -298.  A wave adds the products into a fixed-point
+// accumulator of kXLimbs limbs of 32 bits (limb j weighs 2^(32j - 298)), held
+// in int64 so that carries wait until the end (4096 products of < 2^32 per
+// limb stay below 2^44), sums the lanes' limbs, propagates the carries and
+// rounds the total once to binary32 (nearest, ties to even).
+constexpr int kXLimbs = 18;   // bits 0 .. 575: products reach bit 554, sums 12 more
+constexpr int kXBase = 298;
+
+// binary32 bit pattern -> m * 2^e with m < 2^24; false for NaN / infinity
+__device__ inline bool f32_parts(uint32_t u, uint32_t& m, int& e) {
+  const uint32_t ex = (u >> 23) & 0xFFu, fr = u & 0x7FFFFFu;
+  m = ex ? (fr | 0x800000u) : fr;
+  e = ex ? (int)ex - 150 : -149;
+  return ex != 0xFFu;
+}
+
+// limb j of a (static) limb array, for a run-time j (out of range: 0)
+__device__ inline int64_t limb_at(const int64_t (&L)[kXLimbs], int j) {
+  int64_t v = 0;
+#pragma unroll
+  for (int i = 0; i < kXLimbs; i++) v = (i == j) ? L[i] : v;
+  return v;
+}
+
+__device__ inline void limbs_carry(int64_t (&L)[kXLimbs]) {
+#pragma unroll
+  for (int i = 0; i < kXLimbs - 1; i++) {
+    const int64_t c = L[i] >> 32;  // arithmetic: floor division by 2^32
+    L[i] -= c * 4294967296LL;
+    L[i + 1] += c;
+  }
+}
+
+// RN_f32 of sum_c x[c] * W[e][c], computed by one wave (the result in every
+// lane).  ok is false if an input is NaN or infinite.
+__device__ __noinline__ float exact_logit_wave(RouteSrc src, int e, bool& ok) {
+  const int lane = threadIdx.x & 63;
+  int64_t L[kXLimbs];
+#pragma unroll
+  for (int i = 0; i < kXLimbs; i++) L[i] = 0;
+  bool finite = true;
+  for (int c = lane; c < src.H; c += 64) {
+    const uint32_t xu = src.x_dt == DS4MOE_F32
+                            ? ((const uint32_t*)src.x)[c]
+                            : (uint32_t)((const uint16_t*)src.x)[c] << 16;
+    const size_t wi = (size_t)e * src.H + c;
+    const uint32_t wu = src.w_dt == DS4MOE_F32
+                            ? ((const uint32_t*)src.W)[wi]
+                            : __float_as_uint(f16_bits_to_f32(((const uint16_t*)src.W)[wi]));
+    uint32_t mx, mw;
+    int ex, ew;
+    const bool fx = f32_parts(xu, mx, ex), fw = f32_parts(wu, mw, ew);
+    finite = finite && fx && fw;
+    const uint64_t P = (uint64_t)mx * mw;
+    if (P == 0) continue;
+    const int o = ex + ew + kXBase;  // >= 0
+    const int j = o >> 5, sft = o & 31;
+    const uint64_t t0 = (uint64_t)(uint32_t)P << sft;
+    const uint64_t t1 = ((P >> 32) << sft) + (t0 >> 32);
+    const int64_t p0 = (int64_t)(uint32_t)t0, p1 = (int64_t)(uint32_t)t1, p2 = (int64_t)(t1 >> 32);
+    const bool neg = ((xu ^ wu) >> 31) != 0;
+#pragma unroll
+    for (int i = 0; i < kXLimbs; i++) {
+      const int64_t add = i == j ? p0 : i == j + 1 ? p1 : i == j + 2 ? p2 : 0;
+      L[i] += neg ? -add : add;
+    }
+  }
+  ok = !__any(!finite);
+  // the lanes' sums (exact integer additions, any order)
+#pragma unroll
+  for (int i = 0; i < kXLimbs; i++) {
+    int64_t v = L[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    L[i] = v;
+  }
+  limbs_carry(L);
+  const bool negative = L[kXLimbs - 1] < 0;
+  if (negative) {
+#pragma unroll
+    for (int i = 0; i < kXLimbs; i++) L[i] = -L[i];
+    limbs_carry(L);
+  }
+  // the magnitude N = sum L[i] 2^(32 i), every limb now in [0, 2^32)
+  int top = -1;
+#pragma unroll
+  for (int i = 0; i < kXLimbs; i++)
+    if (L[i] != 0) top = 32 * i + 31 - __builtin_clz((uint32_t)L[i]);
+  if (top < 0) return 0.0f;
+  int q = max(top - 23, 149);  // the unit of the last kept bit (2^-149: subnormals)
+  auto bits_at = [&](int b) -> uint64_t {  // N >> b, low 64 bits
+    const int j = b >> 5, sft = b & 31;
+    const uint64_t w0 = (uint64_t)limb_at(L, j), w1 = (uint64_t)limb_at(L, j + 1),
+                   w2 = (uint64_t)limb_at(L, j + 2);
+    const uint64_t lo = w0 | (w1 << 32);
+    return sft ? ((lo >> sft) | (w2 << (64 - sft))) : lo;
+  };
+  uint32_t M = (uint32_t)bits_at(q);  // < 2^24
+  const uint32_t rbit = (uint32_t)bits_at(q - 1) & 1u;
+  bool sticky = false;
+  const int sb = q - 1;  // bits below sb
+#pragma unroll
+  for (int i = 0; i < kXLimbs; i++) {
+    const int lo = 32 * i;
+    const uint32_t mask = sb >= lo + 32 ? 0xFFFFFFFFu : sb <= lo ? 0u : ((1u << (sb - lo)) - 1u);
+    sticky |= ((uint32_t)L[i] & mask) != 0u;
+  }
+  if (rbit && (sticky || (M & 1u))) M++;
+  if (M == (1u << 24)) {
+    M >>= 1;
+    q++;
+  }
+  float r = q - kXBase > 104 ? __builtin_huge_valf() : ldexpf((float)M, q - kXBase);
+  return negative ? -r : r;
+}
 
 // Scoring.  Grid (E, T), 256 threads: block (e, t) computes the logit, score
 // and key interval of expert e for token t.  VEC (hidden % 2048 == 0, fp16
@@ -257,30 +393,13 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   return max((uint32_t)q[0], (uint32_t)q[1]);
 }
 
-// Top-K selection for one token by one wave, from the E <= 256 key intervals
-// of k_route_score: K rounds of "largest key, lowest expert index among
-// equal keys" (a wave maximum of the key codes, then the first expert whose
-// code equals it).  Lane k < K records the k-th expert; the winners' scores
-// and intervals are read back afterwards (one load per lane, from lines the
-// wave has just read), so a round carries no per-winner lookups.  On return
-// lane k < K holds slot k: expert id in e_out and gate in w_out.  When report
-// is set, an uncertified order raises the fault bit.  Deterministic: every
-// wave that runs it on the same keys gets the same answer.
-__device__ inline void select_wave(const float4* kb, int E, int K, float scale, uint32_t* status,
-                                   bool report, int& e_out, float& w_out) {
+// K rounds of "largest key, lowest expert index among equal keys" over the
+// key codes ko (expert lane + 64 j in slot j; 0 = out of the running): a
+// wave maximum of the codes, then the first expert whose code equals it.
+// Lane k < K returns the k-th winner; the winners' codes are cleared.
+__device__ inline int select_rounds(uint32_t (&ko)[4], int K) {
   const int lane = threadIdx.x & 63;
-  uint32_t ko[4];
-  float kh[4];
-  bool wide = false;
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int ee = lane + 64 * j;
-    const float4 v = ee < E ? kb[ee] : make_float4(0, 0, 0, 0);
-    ko[j] = ee < E ? key_order(v.x) : 0u;
-    kh[j] = v.z;
-    wide |= ee < E && (v.y != v.z);
-  }
-  int e_sel = 0;  // lane k: the k-th winner
+  int e_sel = 0;
   for (int k = 0; k < K; k++) {
     const uint32_t m = wave_max_u32(max(max(ko[0], ko[1]), max(ko[2], ko[3])));
     int be = 0;
@@ -294,7 +413,90 @@ __device__ inline void select_wave(const float4* kb, int E, int K, float scale, 
       if (lane + 64 * j == be) ko[j] = 0u;
     if (lane == k) e_sel = be;
   }
+  return e_sel;
+}
+
+// Exact selection among the experts that the key intervals cannot rule out
+// (upper end at or above `floor`, the lowest lower end among the approximate
+// winners: every other expert lies below K of them for sure).  Each
+// candidate's key is recomputed exactly (exact logit, double-double score);
+// K rounds over the exact keys give the winners.  Lane k < K returns the
+// k-th winner in e_sel and its score in s_sel.  A score too close to a
+// rounding point for double-double (never seen; the oracle stops there too)
+// raises DS4MOE_FAULT_UNCERTIFIED when report is set.
+__device__ __noinline__ void select_exact(const float4* kb, int E, int K, float floor,
+                                          RouteSrc src, uint32_t* status, bool report, int& e_sel,
+                                          float& s_sel) {
+  const int lane = threadIdx.x & 63;
+  uint32_t ko[4];
+  float sc[4];
+  unsigned long long cand[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int ee = lane + 64 * j;
+    cand[j] = __ballot(ee < E && kb[ee < E ? ee : 0].z >= floor);
+    ko[j] = 0u;
+    sc[j] = 0.0f;
+  }
+  bool fault = false;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    unsigned long long m = cand[j];
+    while (m) {
+      const int l = __ffsll((long long)m) - 1;
+      m &= m - 1;
+      const int e = 64 * j + l;
+      bool fin;
+      const float z = exact_logit_wave(src, e, fin);
+      bool dec = true;
+      float s = fin ? dd_round_f32(ssp_dd(z), 0x1p-90, dec) : __builtin_nanf("");
+      fault |= !dec;
+      float key = s + src.bias[e];
+      if (key != key) key = -__builtin_huge_valf();  // NaN never wins
+      if (lane == l) {
+        ko[j] = key_order(key);
+        sc[j] = s;
+      }
+    }
+  }
+  if (fault && lane == 0 && report) raise_fault(status, DS4MOE_FAULT_UNCERTIFIED);
+  e_sel = select_rounds(ko, K);
+  // the winner's score from the lane that holds it
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const float v = __shfl(sc[j], e_sel & 63);
+    s = (e_sel >> 6) == j ? v : s;
+  }
+  s_sel = s;
+}
+
+// Top-K selection for one token by one wave, from the E <= 256 key intervals
+// of k_route_score (select_rounds on the approximate keys).  Lane k < K
+// records the k-th expert; the winners' scores and intervals are read back
+// afterwards (one load per lane, from lines the wave has just read), so a
+// round carries no per-winner lookups.  When an interval is wider than one
+// binary32 value and the order cannot be certified from the intervals, the
+// selection is redone on exact keys (select_exact).  On return lane k < K
+// holds slot k: expert id in e_out and gate in w_out.  Deterministic: every
+// wave that runs it on the same inputs gets the same answer.
+__device__ inline void select_wave(const float4* kb, int E, int K, float scale, uint32_t* status,
+                                   bool report, const RouteSrc& src, int& e_out, float& w_out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t ko[4];
+  float kh[4];
+  bool wide = false;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int ee = lane + 64 * j;
+    const float4 v = ee < E ? kb[ee] : make_float4(0, 0, 0, 0);
+    ko[j] = ee < E ? key_order(v.x) : 0u;
+    kh[j] = v.z;
+    wide |= ee < E && (v.y != v.z);
+  }
+  int e_sel = select_rounds(ko, K);  // lane k: the k-th winner
   const float4 win = lane < K ? kb[e_sel] : make_float4(0, 0, 0, 0);  // key, lo, hi, score
+  float s_win = win.w;
   if (__any(wide)) {
     bool ok = true;
     // consecutive winners: the interval of winner k-1 lies above that of k
@@ -310,12 +512,17 @@ __device__ inline void select_wave(const float4* kb, int E, int K, float scale, 
       if (ee < E && ko[j] != 0u && !(last_lo > kh[j] || (last_lo == kh[j] && last_e < ee)))
         ok = false;
     }
-    if (__any(!ok) && lane == 0 && report) raise_fault(status, DS4MOE_FAULT_UNCERTIFIED);
+    if (__any(!ok)) {
+      float floor = lane < K ? win.y : __builtin_huge_valf();
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) floor = fminf(floor, __shfl_xor(floor, off));
+      select_exact(kb, E, K, floor, src, status, report, e_sel, s_win);
+    }
   }
   double ssum = 0.0;
-  for (int k = 0; k < K; k++) ssum += (double)readlane_f32(win.w, k);
+  for (int k = 0; k < K; k++) ssum += (double)readlane_f32(s_win, k);
   e_out = lane < K ? e_sel : 0;
-  w_out = lane < K ? (float)((double)scale * (double)win.w / ssum) : 0.0f;
+  w_out = lane < K ? (float)((double)scale * (double)s_win / ssum) : 0.0f;
 }
 
 // Selection kernel.  Grid T, one wave per token: reads the key intervals
@@ -325,7 +532,20 @@ __global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
   const int t = blockIdx.x, lane = threadIdx.x;
   int e;
   float w;
-  select_wave(a.kbuf + (size_t)t * a.E, a.E, a.K, a.scale, a.status, true, e, w);
+  // the router input of token t: the normalised row when the scoring wrote it
+  RouteSrc src;
+  if (a.norm_w) {
+    src.x = a.xn_out + (size_t)t * a.H;
+    src.x_dt = DS4MOE_BF16;
+  } else {
+    src.x = (const char*)a.x + (size_t)t * a.H * (a.x_dt == DS4MOE_F32 ? 4 : 2);
+    src.x_dt = a.x_dt;
+  }
+  src.W = a.W;
+  src.w_dt = a.w_dt;
+  src.bias = a.bias;
+  src.H = a.H;
+  select_wave(a.kbuf + (size_t)t * a.E, a.E, a.K, a.scale, a.status, true, src, e, w);
   if (lane < a.K) {
     a.ids[(size_t)t * a.K + lane] = e;
     a.wts[(size_t)t * a.K + lane] = w;

@@ -23,7 +23,7 @@
  *    negative status means nothing was enqueued.
  *  - Faults in the data that only the device can see (an expert id out of
  *    range in caller-given routing, a bad hash-table row, a token id out of
- *    range, a routing decision that could not be certified) set bits of a
+ *    range) set bits of a
  *    status word in the workspace; ds4moe_check() reports them.  Such data
  *    never causes an out-of-bounds access: offending ids are replaced by
  *    valid ones before use.
@@ -124,10 +124,15 @@ size_t ds4moe_workspace_size(const ds4moe_shape* shape, int32_t n_tok);
  * expert ids (int32 [n_tok][top_k], slots ordered by key descending, ties to
  * the lower expert index) and gate weights (fp32 [n_tok][top_k], summing to
  * routed_scale).  x: [n_tok][hidden] of x_dtype (BF16 or F32).
- * Learned router: logits are the exact dot products rounded once to fp32
- * (accumulated in fp64 and certified against an error bound), scores are
- * sqrtsoftplus rounded to fp32, keys are fp32 score + bias.  A selection that
- * the bounds cannot certify sets the status bit DS4MOE_FAULT_UNCERTIFIED.
+ * Learned router: logits are the exact dot products rounded once to fp32,
+ * scores are sqrtsoftplus rounded to fp32 (correctly rounded), keys are fp32
+ * score + bias.  The device accumulates logits in fp64 and evaluates scores
+ * in fp64, each with an error bound; where the bounds leave the selection
+ * open, the keys that could still be selected are recomputed exactly
+ * (integer-limb logit, double-double score with a 2^-90 error bound).  Only a
+ * score within 2^-90 (relative) of a binary32 rounding point, where even the
+ * double-double evaluation cannot decide, would set DS4MOE_FAULT_UNCERTIFIED
+ * (the selection then uses the nearer rounding); none is known.
  * Hash layer: token_ids (int32 [n_tok], required) index tid2eid; token ids
  * outside [0, vocab) or table rows with ids out of range or repeated set a
  * fault bit and route that token to experts 0..top_k-1.
@@ -212,7 +217,8 @@ ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_layer_desc* d
 #define DS4MOE_FAULT_BAD_ID 0x1u       /* caller-given expert id out of range   */
 #define DS4MOE_FAULT_BAD_TOKEN 0x2u    /* token id outside [0, vocab)           */
 #define DS4MOE_FAULT_BAD_TABLE 0x4u    /* tid2eid row out of range / repeated   */
-#define DS4MOE_FAULT_UNCERTIFIED 0x8u  /* routing not certifiable (see route)   */
+#define DS4MOE_FAULT_UNCERTIFIED 0x8u  /* a score undecidable even in double-
+                                          double arithmetic (see route)       */
 #define DS4MOE_FAULT_F16_RANGE 0x10u   /* an intermediate exceeded binary16     */
 #define DS4MOE_FAULT_BAD_INPUT 0x20u   /* encoder: non-finite value, negative or
                                           non-finite importance, grid value not
