@@ -19,7 +19,8 @@ FAULT_BAD_ID, FAULT_BAD_TOKEN, FAULT_BAD_TABLE, FAULT_UNCERTIFIED, FAULT_F16_RAN
 FAULT_BAD_INPUT = 32
 
 EXPORTED = ("ds4moe_workspace_size", "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn",
-            "ds4moe_expert_ffn_imatrix", "ds4moe_layer", "ds4moe_profile_events", "ds4moe_check",
+            "ds4moe_expert_ffn_imatrix", "ds4moe_layer", "ds4moe_layer_noalloc",
+            "ds4moe_profile_events", "ds4moe_check",
             "ds4moe_status_string", "ds4moe_iq2_map_bytes", "ds4moe_iq2_map_build",
             "ds4moe_quantize", "ds4moe_column_energy")
 K_ROUTE, K_GATEUP, K_DOWN, K_PERMUTE, K_OTHER = range(5)
@@ -82,6 +83,9 @@ def lib():
         L.ds4moe_layer.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(LayerDesc), vp, i32, vp,
                                    vp, vp, i32, vp, vp, vp, vp, sz, vp]
         L.ds4moe_layer.restype = i32
+        L.ds4moe_layer_noalloc.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(LayerDesc), vp,
+                                           i32, vp, vp, vp, i32, vp, vp, vp, vp, vp]
+        L.ds4moe_layer_noalloc.restype = i32
         L.ds4moe_profile_events.argtypes = [i32, vp, vp]
         L.ds4moe_profile_events.restype = i32
         L.ds4moe_check.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
@@ -168,6 +172,15 @@ def layer(shp, desc, x, x_dtype, residual, out, token_ids, n_tok, ids_dbg, w_dbg
     _ok(lib().ds4moe_layer(ctypes.byref(shp), ctypes.byref(desc), x, x_dtype, residual, out,
                            token_ids, n_tok, ids_dbg, w_dbg, xn_dbg, ws, ws_bytes, stream),
         "ds4moe_layer")
+
+
+def layer_noalloc(shp, desc, x, x_dtype, residual, out, token_ids, n_tok, ids_dbg, w_dbg, xn_dbg,
+                  faults, stream=0):
+    """ds4moe_layer on the library's static workspace (no allocation); faults:
+    device pointer to one uint32 receiving the call's fault bits, or None."""
+    _ok(lib().ds4moe_layer_noalloc(ctypes.byref(shp), ctypes.byref(desc), x, x_dtype, residual,
+                                   out, token_ids, n_tok, ids_dbg, w_dbg, xn_dbg, faults, stream),
+        "ds4moe_layer_noalloc")
 
 
 def profile_events(cls, begin, end):

@@ -4,6 +4,8 @@
 #include <hip/hip_ext.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dev_common.h"
 #include "route.hip"
 #include "ffn_b1.hip"
@@ -719,12 +721,13 @@ DS4_EXPORT ds4moe_status ds4moe_expert_ffn_imatrix(const ds4moe_shape* shape,
                 nullptr, ws, L, stream, &imx);
 }
 
-DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_layer_desc* desc,
-                                      const void* x, int32_t x_dtype, float* residual, float* out,
-                                      const int32_t* token_ids, int32_t n_tok, int32_t* ids_dbg,
-                                      float* w_dbg, uint16_t* xn_dbg, void* ws, size_t ws_bytes,
-                                      hipStream_t stream) {
-  if (!shape_ok(shape) || !desc || !experts_ok(&desc->routed, shape->hidden) || !ws || n_tok < 0)
+namespace {
+
+// Argument checks of ds4moe_layer (all but the workspace).
+ds4moe_status layer_args(const ds4moe_shape* shape, const ds4moe_layer_desc* desc, const void* x,
+                         int32_t x_dtype, float* residual, float* out, const int32_t* token_ids,
+                         int32_t n_tok) {
+  if (!shape_ok(shape) || !desc || !experts_ok(&desc->routed, shape->hidden) || n_tok < 0)
     return DS4MOE_EINVAL;
   if (desc->routed.inter != shape->inter) return DS4MOE_EINVAL;
   const ds4moe_experts* sh = desc->shared;
@@ -737,16 +740,23 @@ DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_la
   } else if (shape->top_k > kMaxRouteK) {
     return DS4MOE_EUNSUPPORTED;
   }
-  const bool norm = desc->norm_w != nullptr;
-  if (norm) {
+  if (desc->norm_w) {
     if (!residual) return DS4MOE_EINVAL;
   } else {
     if (!x || !x_dtype_ok(x_dtype) || !out) return DS4MOE_EINVAL;
   }
-  if (n_tok == 0) return DS4MOE_OK;
   if ((int64_t)n_tok * shape->top_k > 32768) return DS4MOE_EUNSUPPORTED;
-  Layout L = layout_for(*shape, n_tok);
-  if (ws_bytes < L.total) return DS4MOE_EWORKSPACE;
+  return DS4MOE_OK;
+}
+
+// The layer on a workspace of layout L (arguments checked, n_tok > 0).
+ds4moe_status layer_run(const ds4moe_shape* shape, const ds4moe_layer_desc* desc, const void* x,
+                        int32_t x_dtype, float* residual, float* out, const int32_t* token_ids,
+                        int32_t n_tok, int32_t* ids_dbg, float* w_dbg, uint16_t* xn_dbg, void* ws,
+                        const Layout& L, hipStream_t stream) {
+  const ds4moe_experts* sh = desc->shared;
+  const ds4moe_router& r = desc->router;
+  const bool norm = desc->norm_w != nullptr;
   int32_t* ids = at<int32_t>(ws, L.ids);
   float* wts = at<float>(ws, L.wts);
   uint16_t* xn = at<uint16_t>(ws, L.xn);
@@ -788,6 +798,83 @@ DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_la
                      hipMemcpyDeviceToDevice, stream) != hipSuccess)
     return DS4MOE_EDEVICE;
   return DS4MOE_OK;
+}
+
+}  // namespace
+
+DS4_EXPORT ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_layer_desc* desc,
+                                      const void* x, int32_t x_dtype, float* residual, float* out,
+                                      const int32_t* token_ids, int32_t n_tok, int32_t* ids_dbg,
+                                      float* w_dbg, uint16_t* xn_dbg, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  if (!ws) return DS4MOE_EINVAL;
+  ds4moe_status rc = layer_args(shape, desc, x, x_dtype, residual, out, token_ids, n_tok);
+  if (rc != DS4MOE_OK || n_tok == 0) return rc;
+  const Layout L = layout_for(*shape, n_tok);
+  if (ws_bytes < L.total) return DS4MOE_EWORKSPACE;
+  return layer_run(shape, desc, x, x_dtype, residual, out, token_ids, n_tok, ids_dbg, w_dbg,
+                   xn_dbg, ws, L, stream);
+}
+
+// ---- allocation-free layer call -------------------------------------------------
+// The workspace of ds4moe_layer_noalloc: one static device array per GPU,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever passed to kernels.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kScratchMaxDevices] = {};
+
+// The current device's address of `scratch` (nullptr if it cannot be had).
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_dev[dev] = p;
+  }
+  return g_scratch_dev[dev];
+}
+
+// Clears the status region at the start of the scratch workspace (a kernel,
+// not a memset, so that the call can be captured into a graph).
+__global__ void k_scratch_clear(uint32_t* status) { status[threadIdx.x] = 0u; }
+
+__global__ void k_scratch_faults(const uint32_t* status, uint32_t* faults) { *faults = *status; }
+
+}  // namespace
+
+DS4_EXPORT ds4moe_status ds4moe_layer_noalloc(const ds4moe_shape* shape,
+                                              const ds4moe_layer_desc* desc, const void* x,
+                                              int32_t x_dtype, float* residual, float* out,
+                                              const int32_t* token_ids, int32_t n_tok,
+                                              int32_t* ids_dbg, float* w_dbg, uint16_t* xn_dbg,
+                                              uint32_t* faults, hipStream_t stream) {
+  ds4moe_status rc = layer_args(shape, desc, x, x_dtype, residual, out, token_ids, n_tok);
+  if (rc != DS4MOE_OK || n_tok == 0) return rc;
+  const Layout L = layout_for(*shape, n_tok);
+  if (L.total > kScratchBytes) return DS4MOE_EWORKSPACE;
+  void* ws = scratch_for_current_device();
+  if (!ws) return DS4MOE_EDEVICE;
+  {
+    ProfScope prof(DS4MOE_K_OTHER, stream);
+    launch_k(k_scratch_clear, dim3(1), dim3(64), 0, stream, static_cast<uint32_t*>(ws));
+  }
+  if ((rc = launched()) != DS4MOE_OK) return rc;
+  rc = layer_run(shape, desc, x, x_dtype, residual, out, token_ids, n_tok, ids_dbg, w_dbg, xn_dbg,
+                 ws, L, stream);
+  if (rc != DS4MOE_OK || !faults) return rc;
+  ProfScope prof(DS4MOE_K_OTHER, stream);
+  launch_k(k_scratch_faults, dim3(1), dim3(1), 0, stream, static_cast<const uint32_t*>(ws), faults);
+  return launched();
 }
 
 DS4_EXPORT ds4moe_status ds4moe_profile_events(int32_t cls, hipEvent_t begin, hipEvent_t end) {

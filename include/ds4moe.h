@@ -213,6 +213,28 @@ ds4moe_status ds4moe_layer(const ds4moe_shape* shape, const ds4moe_layer_desc* d
                            const int32_t* token_ids, int32_t n_tok, int32_t* ids_dbg, float* w_dbg,
                            uint16_t* xn_dbg, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * ds4moe_layer for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and results as ds4moe_layer, without the
+ * workspace arguments.  Its workspace is a static device array of 8 MiB per
+ * GPU (part of the library's device code, present on every GPU the library
+ * runs on until the process ends); the call itself allocates nothing.  n_tok must satisfy
+ * ds4moe_workspace_size(shape, n_tok) <= 8 MiB (up to 17 tokens with the
+ * V4-Flash shape: hidden 4096, inter 2048, 256 experts, top-6), otherwise
+ * DS4MOE_EWORKSPACE is returned before anything is enqueued.  faults
+ * (device, nullable): one uint32 that receives this call's fault bits (the
+ * bits ds4moe_check reports; 0 when clean) when the call's work completes.
+ * Every call on a GPU uses that GPU's one array (its status word is cleared
+ * at the start of each call): calls that overlap on one GPU (two streams or
+ * host threads without ordering) race and must be ordered on one stream.
+ */
+ds4moe_status ds4moe_layer_noalloc(const ds4moe_shape* shape, const ds4moe_layer_desc* desc,
+                                   const void* x, int32_t x_dtype, float* residual, float* out,
+                                   const int32_t* token_ids, int32_t n_tok, int32_t* ids_dbg,
+                                   float* w_dbg, uint16_t* xn_dbg, uint32_t* faults,
+                                   hipStream_t stream);
+
 /* Status-word bits reported by ds4moe_check(). */
 #define DS4MOE_FAULT_BAD_ID 0x1u       /* caller-given expert id out of range   */
 #define DS4MOE_FAULT_BAD_TOKEN 0x2u    /* token id outside [0, vocab)           */
