@@ -76,6 +76,73 @@ def event_handle(ev):
     return ev.cuda_event
 
 
+def time_replays(replay, n):
+    """Times n passes of replay() (each a whole timed region: a graph replay
+    or a sequence of them), each bracketed by device synchronisations, with
+    events on the current stream.  Returns the milliseconds of each pass."""
+    import torch
+    out = []
+    for _ in range(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return out
+
+
+def replay_summary(ms_list):
+    import numpy as np
+    return {"passes": len(ms_list), "median_ms": round(float(np.median(ms_list)), 5),
+            "min_ms": round(float(np.min(ms_list)), 5), "max_ms": round(float(np.max(ms_list)), 5)}
+
+
+def read_bandwidth(nbytes=2 << 30, reps=11):
+    """The box's streaming-read bandwidth: the library's read probe (a plain
+    16-byte-load streaming kernel) over nbytes, median of reps launches timed
+    with events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import bit_quantized_expert_ds4moe_amd as ds4
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    ds4.read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), st)
+    ms = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ds4.read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), st)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    med = float(np.median(ms))
+    del buf
+    torch.cuda.empty_cache()
+    gbs = nbytes / (med * 1e-3) / 1e9
+    log("read probe: %d bytes in %.1f us (median of %d) = %.0f GB/s" % (nbytes, med * 1e3, reps, gbs))
+    return {"kernel": "k_read_probe (ds4moe_read_probe)", "bytes": nbytes, "median_us": round(med * 1e3, 2),
+            "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def add_stream_fracs(res, stream):
+    """Every bandwidth of a result line also as a fraction of the measured
+    streaming-read bandwidth."""
+    res["hbm_stream"] = stream
+    if "expert_gbs" in res:
+        res["expert_stream_frac"] = round(res["expert_gbs"] / stream["gbs"], 4)
+    for key in ("roofline", "roofline_q4k"):
+        r = res.get(key)
+        if r and r.get("unit") == "GB/s":
+            r["frac_of_stream"] = round(r["achieved"] / stream["gbs"], 4)
+    return res
+
+
 def bench_decode_b1(args):
     import numpy as np
     import torch
@@ -126,18 +193,12 @@ def bench_decode_b1(args):
     g_main = capture(args.warmup, args.steps)
     g_warm.replay()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record()
-    g_main.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1)
+    # the timed region: the K steps, replayed `replays` times; the median pass
+    passes = time_replays(g_main.replay, args.replays)
+    ms = float(np.median(passes))
     assert ds4.check(ws.data_ptr(), st) == 0
-    log("timed %d steps: %.3f ms (wall %.3f ms)" % (args.steps, ms, wall * 1e3))
+    log("timed %d steps x %d passes: median %.3f ms (min %.3f, max %.3f)"
+        % (args.steps, len(passes), ms, min(passes), max(passes)))
 
     # second pass: per-kernel HIP events around each launch, recorded by the
     # library on the launch stream.  The GPU first spins in a sleep kernel so
@@ -182,7 +243,10 @@ def bench_decode_b1(args):
         "config": {"workload": w.name, "hidden": w.H, "inter": w.I, "experts": w.E,
                    "top_k": w.K, "tokens_per_step": 1, "gate_up": "IQ2_XXS", "down": "Q2_K",
                    "router": "f16", "activations": "bf16", "layer_copies": args.layer_copies,
-                   "timing": "hip-graph replay, distinct token per step"},
+                   "timing": "hip-graph replay, distinct token per step, step i on layer copy "
+                             "i mod copies (cold: %.0f GB of experts cycled); median of %d passes"
+                             % (args.layer_copies * 256 * w.expert_bytes() / 1e9, args.replays)},
+        "timed_passes": replay_summary(passes),
         "expert_gbs": round(gbs, 1), "expert_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
         "kernel_timing": "HIP events recorded by the library around each launch, %d eager steps" % n_prof,
@@ -192,7 +256,7 @@ def bench_decode_b1(args):
                      "bytes_per_launch": gateup_bytes},
     }
     if args.cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_decode(w, args.cpu_sample)
+        res["cpu_baseline"] = with_single_thread(cpu_baseline_decode, (w, args.cpu_sample), (w, 1))
     return res
 
 
@@ -266,16 +330,19 @@ def bench_stack(args, mixed=False, shared=False):
     for _ in range(args.warmup):
         gr.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        gr.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
+
+    def timed_steps():  # the K steps after the warm-up, on their own inputs
+        for _ in range(args.steps):
+            gr.replay()
+
+    passes = []
+    for _ in range(args.replays):
+        idx.fill_(args.warmup)  # untimed: the pass starts at step `warmup`
+        passes += time_replays(timed_steps, 1)
+    ms = float(np.median(passes))
     assert ds4.check(ws.data_ptr(), st) == 0
-    log("timed %d steps: %.3f ms" % (args.steps, ms))
+    log("timed %d steps x %d passes: median %.3f ms (min %.3f, max %.3f)"
+        % (args.steps, len(passes), ms, min(passes), max(passes)))
 
     # per-kernel events over a few eager steps behind a GPU sleep
     classes = {"route": ds4.K_ROUTE, "gateup": ds4.K_GATEUP, "down": ds4.K_DOWN, "other": ds4.K_OTHER}
@@ -336,7 +403,9 @@ def bench_stack(args, mixed=False, shared=False):
                    "hidden": w.H, "inter": w.I, "experts": w.E, "top_k": w.K,
                    "q4k_layers": list(w.q4_layers), "shared_q8_0": bool(w.shared),
                    "resident_expert_bytes": w.stack_expert_bytes(),
-                   "timing": "hip-graph replay of one 43-layer step per token"},
+                   "timing": "hip-graph replay of one 43-layer step per token; median of %d "
+                             "passes of the timed steps" % args.replays},
+        "timed_passes": replay_summary(passes),
         "expert_gbs": round(gbs, 1), "expert_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
         "roofline": {"bound": "hbm", "kernel": "k_gateup_b1<true>", "achieved": round(ach, 1),
@@ -359,7 +428,8 @@ def bench_stack(args, mixed=False, shared=False):
                                "traffic": measured_traffic(Q4K_GATEUP_TRAFFIC),
                                "bytes_per_launch": b4}
     if args.cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_stack(w, args.cpu_sample)
+        res["cpu_baseline"] = with_single_thread(cpu_baseline_stack, (w, args.cpu_sample),
+                                                 (w, 2))
     return res
 
 
@@ -439,15 +509,10 @@ def bench_batched(args, which):
     g_main = capture(args.warmup, args.steps)
     g_warm.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g_main.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
+    passes = time_replays(g_main.replay, args.replays)
+    ms = float(np.median(passes))
     assert ds4.check(ws.data_ptr(), st) == 0
-    log("timed %d steps: %.3f ms" % (args.steps, ms))
+    log("timed %d steps x %d passes: median %.3f ms" % (args.steps, len(passes), ms))
     if not prefill:  # experts touched per step, from untimed calls
         for i in range(args.warmup, n_batches):
             step(i, st, ids_d[i].data_ptr())
@@ -497,7 +562,9 @@ def bench_batched(args, which):
                    "experts": w.E, "top_k": w.K, "shared_q8_0": bool(w.shared),
                    "experts_touched_per_step": touched,
                    "routing": "given Zipf(1.1)" if prefill else "learned router",
-                   "imatrix": bool(prefill and args.imatrix)},
+                   "imatrix": bool(prefill and args.imatrix),
+                   "timing": "hip-graph replay; median of %d passes" % args.replays},
+        "timed_passes": replay_summary(passes),
         "expert_gbs": round(step_bytes / sec / 1e9, 1),
         "expert_hbm_frac": round(step_bytes / sec / 1e9 / PEAK_HBM_GBS, 4),
         "mfma_tflops": round(flops / sec / 1e12, 2),
@@ -723,7 +790,24 @@ def bench_encode(args):
                      "ops_per_launch": iq2_ops},
     }
     if args.cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_encode(args.cpu_sample)
+        res["cpu_baseline"] = with_single_thread(cpu_baseline_encode, (args.cpu_sample,),
+                                                 (max(64, args.cpu_sample // 16),))
+    return res
+
+
+def with_single_thread(fn, args_all, args_one):
+    """The oracle baseline at all host threads (the reported value) and, on a
+    smaller sample of the same workload, at one thread."""
+    import oracle
+    res = fn(*args_all)
+    n = oracle.max_threads()
+    oracle.set_threads(1)
+    try:
+        one = fn(*args_one)
+    finally:
+        oracle.set_threads(n)
+    res["single_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1,
+                            "sample": one["sample"]}
     return res
 
 
@@ -846,8 +930,14 @@ def main():
                              "prefill-512-q4k", "decode-sweep", "encode"])
     ap.add_argument("--encode-experts", type=int, default=8,
                     help="encode: experts quantised per step")
-    ap.add_argument("--layer-copies", type=int, default=1,
-                    help="rotate over this many independently seeded layers")
+    ap.add_argument("--layer-copies", type=int, default=48,
+                    help="decode-b1: step i runs on layer copy i mod this many independently "
+                         "seeded layers (48 copies cycle 87 GB of experts and 96 MB of router "
+                         "weights, so no step finds its weights in the 256 MB last-level cache)")
+    ap.add_argument("--replays", type=int, default=21,
+                    help="timed passes over the K steps; the median pass gives the value")
+    ap.add_argument("--no-stream-probe", dest="stream_probe", action="store_false",
+                    help="skip the 2 GiB streaming-read measurement")
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="oracle sample: tokens (decode-b1, default 3) or layers (stack-43, default 6)")
     ap.add_argument("--sleep-cycles", type=int, default=200_000_000,
@@ -899,6 +989,8 @@ def main():
         res = bench_encode(args)
     else:
         res = bench_decode_b1(args)
+    if args.stream_probe:
+        res = add_stream_fracs(res, read_bandwidth())
     print(json.dumps(res), flush=True)
 
 

@@ -20,7 +20,7 @@ FAULT_BAD_INPUT = 32
 
 EXPORTED = ("ds4moe_workspace_size", "ds4moe_route", "ds4moe_permute", "ds4moe_expert_ffn",
             "ds4moe_expert_ffn_imatrix", "ds4moe_layer", "ds4moe_layer_noalloc",
-            "ds4moe_profile_events", "ds4moe_check",
+            "ds4moe_profile_events", "ds4moe_read_probe", "ds4moe_check",
             "ds4moe_status_string", "ds4moe_iq2_map_bytes", "ds4moe_iq2_map_build",
             "ds4moe_quantize", "ds4moe_column_energy")
 K_ROUTE, K_GATEUP, K_DOWN, K_PERMUTE, K_OTHER = range(5)
@@ -88,6 +88,8 @@ def lib():
         L.ds4moe_layer_noalloc.restype = i32
         L.ds4moe_profile_events.argtypes = [i32, vp, vp]
         L.ds4moe_profile_events.restype = i32
+        L.ds4moe_read_probe.argtypes = [vp, sz, vp, vp]
+        L.ds4moe_read_probe.restype = i32
         L.ds4moe_check.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
         L.ds4moe_check.restype = i32
         L.ds4moe_status_string.argtypes = [i32]
@@ -186,6 +188,11 @@ def layer_noalloc(shp, desc, x, x_dtype, residual, out, token_ids, n_tok, ids_db
 def profile_events(cls, begin, end):
     """begin/end: HIP event handles (int) or None to stop."""
     _ok(lib().ds4moe_profile_events(cls, begin, end), "ds4moe_profile_events")
+
+
+def read_probe(src, nbytes, sink, stream=0):
+    """Streaming read of nbytes at src (measurement only); checksum to sink."""
+    _ok(lib().ds4moe_read_probe(src, nbytes, sink, stream), "ds4moe_read_probe")
 
 
 def iq2_map_bytes():

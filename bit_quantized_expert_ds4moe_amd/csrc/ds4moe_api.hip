@@ -877,6 +877,48 @@ DS4_EXPORT ds4moe_status ds4moe_layer_noalloc(const ds4moe_shape* shape,
   return launched();
 }
 
+namespace {
+
+// Streaming-read probe: workgroup b reads the b-th contiguous chunk of the
+// buffer, each thread keeping eight 16-byte loads in flight; the data are
+// folded into a checksum so that no load can be dropped.
+constexpr int kProbeGroups = 4096, kProbeThreads = 256, kProbeUnroll = 8;
+
+__global__ __launch_bounds__(kProbeThreads) void k_read_probe(const uint4* __restrict__ src,
+                                                             size_t n16, uint32_t* sink) {
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t b = (size_t)blockIdx.x * per, e = b + per < n16 ? b + per : n16;
+  uint32_t acc = 0;
+  for (size_t i = b + threadIdx.x; i < e; i += (size_t)kProbeThreads * kProbeUnroll) {
+    uint4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; u++) {
+      const size_t j = i + (size_t)u * kProbeThreads;
+      v[u] = j < e ? src[j] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  // one writer per workgroup, in a fixed slot: the checksum is the same on
+  // every run (the XOR of the workgroups' values)
+  acc = __reduce_xor_sync(0xFFFFFFFFFFFFFFFFull, acc);
+  __shared__ uint32_t wv[kProbeThreads / 64];
+  if ((threadIdx.x & 63) == 0) wv[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicXor(sink, wv[0] ^ wv[1] ^ wv[2] ^ wv[3]);
+}
+
+}  // namespace
+
+DS4_EXPORT ds4moe_status ds4moe_read_probe(const void* src, size_t bytes, uint32_t* sink,
+                                           hipStream_t stream) {
+  if (!src || !sink || ((uintptr_t)src & 15) || (bytes & 15)) return DS4MOE_EINVAL;
+  if (bytes == 0) return DS4MOE_OK;
+  launch_k(k_read_probe, dim3(kProbeGroups), dim3(kProbeThreads), 0, stream,
+           static_cast<const uint4*>(src), bytes / 16, sink);
+  return launched();
+}
+
 DS4_EXPORT ds4moe_status ds4moe_profile_events(int32_t cls, hipEvent_t begin, hipEvent_t end) {
   if (cls < 0 || cls >= DS4MOE_K_CLASSES) return DS4MOE_EINVAL;
   g_prof[cls][0] = begin;

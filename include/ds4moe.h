@@ -264,6 +264,18 @@ ds4moe_status ds4moe_layer_noalloc(const ds4moe_shape* shape, const ds4moe_layer
  */
 ds4moe_status ds4moe_profile_events(int32_t cls, hipEvent_t begin, hipEvent_t end);
 
+/*
+ * Streaming-read probe (measurement only, not part of the method): reads
+ * `bytes` bytes at `src` (device, 16-byte aligned, bytes a multiple of 16)
+ * once with 16-byte vector loads, as a plain streaming kernel that does no
+ * other work (4096 workgroups of 256 threads, each reading one contiguous
+ * chunk, eight loads in flight per thread), and writes a checksum of the
+ * data to *sink (device).  Timing it gives the read bandwidth the memory
+ * system delivers to a kernel on this device, against which the expert
+ * kernels' bandwidth is quoted.  Asynchronous on `stream`.
+ */
+ds4moe_status ds4moe_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* ------------------------------------------------------------------ */
 /* Block encoders: fp32 matrices -> Q2_K / IQ2_XXS blocks               */
 /* ------------------------------------------------------------------ */
