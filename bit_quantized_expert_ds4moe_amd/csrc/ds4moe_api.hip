@@ -37,7 +37,7 @@ constexpr int kSharedSplitMaxT = 64;  // "few": one work item of shared rows
 
 // Byte offsets of the workspace regions for (shape, n_tok).
 struct Layout {
-  size_t status, kbuf, ids, wts, xn, x16, perm, h, y, hb, part, total;
+  size_t status, kbuf, ids, wts, xn, x16, perm, h, y, hb, part, xexp, hexp, total;
 };
 
 Layout layout_for(const ds4moe_shape& s, int32_t T) {
@@ -63,6 +63,11 @@ Layout layout_for(const ds4moe_shape& s, int32_t T) {
   L.hb = take(np * I * 2);
   // K shares of a shared expert in few-token calls
   L.part = take(t <= (size_t)kSharedSplitMaxT ? (size_t)kSharedSplitG * t * (2 * I > H ? 2 * I : H) * 4 : 0);
+  // binary16 exponents of the grouped path: x's per sorted row (the token's;
+  // 64 rows of padding read by the last tiles), the SwiGLU rows' per row and
+  // 64-feature range
+  L.xexp = take((t * K + 64) * 4);
+  L.hexp = take(np * ((I + 63) / 64));
   L.total = o;
   return L;
 }
@@ -390,6 +395,7 @@ ds4moe_status launch_imatrix(const ds4moe_shape& s, const ImxOut& o, const void*
   a.h_stride = h_stride;
   a.hh = hh;
   a.hl = hl;
+  a.hexp = at<int8_t>(ws, L.hexp);
   a.gu = o.gu;
   a.dn = o.dn;
   const int cmax = s.hidden > s.inter ? s.hidden : s.inter;
@@ -501,6 +507,8 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       g.hsh = sbase;
       g.hsl = sbase + np * (size_t)(g.I / 16);
     }
+    g.xrexp = at<int8_t>(ws, L.xexp);
+    g.hexp = at<int8_t>(ws, L.hexp);
     g.y = at<float>(ws, L.y);
     g.ksplit_g = g.ksplit_d = 1;
     g.part = at<float>(ws, L.part);
@@ -515,11 +523,9 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       const bool iq2 = iq2_grouped_fast(g);
       const bool q4k = q4k_grouped_gu(g);
       const bool q80 = sh && q80_shared_fast(g);
-      if ((iq2 || q4k) && !b1) {  // x in binary16
-        const size_t n8 = (size_t)T * g.H / 8;
-        launch_k(k_x_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, g.x, n8,
-                 at<uint16_t>(ws, L.x16), status);
-      }
+      if ((iq2 || q4k) && !b1)  // x in binary16, one power-of-two scale per token
+        launch_k(k_x_to_f16, dim3(T), dim3(256), 0, st, g.x, g.H, g.K, (const int32_t*)inv,
+                 at<uint16_t>(ws, L.x16), at<int8_t>(ws, L.xexp));
       if (iq2 && !b1) {  // small items (at most one per expert) and the rest
         launch_k(k_grouped_gateup_iq2_small, dim3(g.I / kGNF, E < TK ? E : TK), dim3(kGW * 64), 0, st, g);
         launch_k(k_grouped_gateup_iq2<4>, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);

@@ -151,10 +151,13 @@ struct GroupArgs {
   const uint8_t *sh_gate, *sh_up, *sh_down;
   int sh_qt_g, sh_qt_u, sh_qt_d, sh_I;
   const uint8_t* grid;
-  uint16_t* hh;             // [T*K + T][I] SwiGLU rows, binary16 high part
+  int8_t* xrexp;            // [T*K + 64][4] x16 = x * 2^e per token: word j packs e of sorted
+                            // rows j .. j + 3 (byte r: row j + r), one aligned load per lane
+  uint16_t* hh;             // [T*K + T][I] SwiGLU rows times 2^hexp, binary16 high part
   uint16_t* hl;             // [T*K + T][I] binary16 low part (h - hi, rounded)
   uint16_t* hsh;            // [T*K + T][I/16] sums of 16 consecutive features, high part
   uint16_t* hsl;            // [T*K + T][I/16] low part
+  int8_t* hexp;             // [T*K + T][I/64] the exponent of each row's 64-feature range
   float* y;                 // [T*K + T][H] fp32
   uint32_t* status;
   // K split of the shared expert's kernels (few-token calls): partial sums
@@ -167,43 +170,123 @@ __device__ inline int row_token(const GroupArgs& a, int row) {
   return row < a.T * a.K ? a.perm[row] / a.K : row - a.T * a.K;
 }
 
+// The power-of-two exponent e that brings a largest magnitude M into
+// [2^top, 2^(top+1)); 0 for M = 0 and for NaN or infinite values (they then
+// propagate as they are).  |e| <= 120.
+__device__ inline int pow2_exponent(float M, bool bad, int top) {
+  if (bad || !(M > 0.0f)) return 0;
+  int k;
+  (void)frexpf(M, &k);  // M = f 2^k, 1/2 <= f < 1
+  return min(max(top - k + 1, -120), 120);
+}
+
+// AbsMax over the lanes of a wave (every lane receives the result).
+__device__ inline AbsMax wave_absmax(AbsMax v) {
+  AbsMax r;
+  r.smax = (int)(wave_max_u32((uint32_t)v.smax ^ 0x80000000u) ^ 0x80000000u);
+  r.umax = wave_max_u32(v.umax);
+  return r;
+}
+
 // SwiGLU epilogue of the grouped gate/up kernels.  Lane (column n = lane%16,
 // quarter q) holds rows 4q + r of each 16-row tile.  The down kernels take h
 // as binary16 high + low parts (relative error < 2^-21) and, for the Q2_K
 // min term, the sum of each 16 consecutive features (a wave's tile) split
 // the same way; the sum runs over the 16 lanes of a DPP row in a fixed order.
+// So that any magnitude fits binary16, the stored values are h * 2^e with
+// one exponent per work item and feature tile (features n0 .. n0 + nf - 1):
+// 0 while the largest |h| of the tile, over every wave of the block, stays
+// below 2^11 (the sums of 16 then stay below 2^15), else the exponent that
+// brings it into [2^10, 2^11); scaling by a power of two is exact.  Each
+// wave stores its rows with e = 0 at once and, in the rare case e != 0,
+// again once the block has agreed on e; e is written for each row and
+// 64-feature range of the tile.  xe (binary16 x): the accumulators of rows
+// 16 mt + 4q + r are in units of 2^xe[mt][r], the x exponent of the row's
+// token (loaded by the caller ahead of its main loop), undone first;
+// nullptr otherwise.  red: 32 words of the caller's LDS that no wave touches
+// once the caller's last barrier has passed (its staging buffers, free after
+// the main loop: a block-wide array of its own here would push the iq2
+// kernels past 80 KB and halve their occupancy).  Every thread of the block
+// must call it.
 template <int MT = 4>
 __device__ inline void swiglu_store(const GroupArgs& a, int row0, int nrows, int mtiles, int n,
-                                    int q, const f32x4_t* accg, const f32x4_t* accu) {
-  bool ok = true;
+                                    int q, const f32x4_t* accg, const f32x4_t* accu, int n0,
+                                    int nf, const uint32_t* xe, uint32_t* red) {
+  float v[MT][4];
+  AbsMax am;
+  auto store = [&](int e) {
 #pragma unroll
-  for (int mt = 0; mt < MT; mt++) {
-    if (mt >= mtiles) break;
+    for (int mt = 0; mt < MT; mt++) {
+      if (mt >= mtiles) break;
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int m = 16 * mt + 4 * q + r;
-      const float v = m < nrows ? silu(accg[mt][r]) * accu[mt][r] : 0.0f;
-      ok &= fabsf(v) <= 65504.0f;
-      const uint32_t hi = f32_to_f16_bits(v);
-      const uint32_t lo = f32_to_f16_bits(v - f16_bits_to_f32(hi));
-      float sum = v;
-      sum += dpp_f32<0xB1>(sum);
-      sum += dpp_f32<0x4E>(sum);
-      sum += dpp_f32<0x141>(sum);
-      sum += dpp_f32<0x140>(sum);
-      if (m < nrows) {
-        const size_t row = (size_t)(row0 + m);
-        a.hh[row * a.I + n] = (uint16_t)hi;
-        a.hl[row * a.I + n] = (uint16_t)lo;
-        if ((n & 15) == 0) {
-          const uint32_t shi = f32_to_f16_bits(sum);
-          a.hsh[row * (a.I / 16) + n / 16] = (uint16_t)shi;
-          a.hsl[row * (a.I / 16) + n / 16] = (uint16_t)f32_to_f16_bits(sum - f16_bits_to_f32(shi));
+      for (int r = 0; r < 4; r++) {
+        const int m = 16 * mt + 4 * q + r;
+        const float vs = ldexpf(v[mt][r], e);
+        const uint32_t hi = f32_to_f16_bits(vs);
+        const uint32_t lo = f32_to_f16_bits(vs - f16_bits_to_f32(hi));
+        float sum = vs;
+        sum += dpp_f32<0xB1>(sum);
+        sum += dpp_f32<0x4E>(sum);
+        sum += dpp_f32<0x141>(sum);
+        sum += dpp_f32<0x140>(sum);
+        if (m < nrows) {
+          const size_t row = (size_t)(row0 + m);
+          a.hh[row * a.I + n] = (uint16_t)hi;
+          a.hl[row * a.I + n] = (uint16_t)lo;
+          if ((n & 15) == 0) {
+            const uint32_t shi = f32_to_f16_bits(sum);
+            a.hsh[row * (a.I / 16) + n / 16] = (uint16_t)shi;
+            a.hsl[row * (a.I / 16) + n / 16] = (uint16_t)f32_to_f16_bits(sum - f16_bits_to_f32(shi));
+          }
         }
       }
     }
+  };
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int m = 16 * mt + 4 * q + r;
+      const bool live = mt < mtiles && m < nrows;
+      float g = accg[mt][r], u = accu[mt][r];
+      if (xe) {
+        const int ex = (int8_t)(xe[mt] >> (8 * r));
+        g = ldexpf(g, -ex);
+        u = ldexpf(u, -ex);
+      }
+      v[mt][r] = live ? silu(g) * u : 0.0f;
+      if (live) am.add(v[mt][r]);
+    }
+  store(0);
+  am = wave_absmax(am);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (lane == 0) {
+    red[w] = (uint32_t)am.smax;
+    red[16 + w] = am.umax;
   }
-  if (!ok) raise_fault(a.status, DS4MOE_FAULT_F16_RANGE);
+  __syncthreads();
+  AbsMax bm;
+  for (int i = 0; i < nw; i++) {
+    bm.smax = max(bm.smax, (int)red[i]);
+    bm.umax = max(bm.umax, red[16 + i]);
+  }
+  bool bad;
+  const float M = bm.value(bad);
+  const int e = M < 2048.0f ? 0 : pow2_exponent(M, bad, 10);
+  if ((int)threadIdx.x < nrows * (nf / 64)) {
+    const int m = threadIdx.x / (nf / 64), rg = threadIdx.x % (nf / 64);
+    a.hexp[(size_t)(row0 + m) * (a.I / 64) + n0 / 64 + rg] = (int8_t)e;
+  }
+  if (e != 0) store(e);  // the same lanes rewrite the same addresses
+}
+
+// The x exponents of rows row0 + 16 mt + 4q .. +3 (mt < MT), for
+// swiglu_store; rows past the item read padding and are never used.
+template <int MT>
+__device__ inline void load_row_xexp(const GroupArgs& a, int row0, int q, uint32_t* xe) {
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+    xe[mt] = *(const uint32_t*)(a.xrexp + 4 * (size_t)(row0 + 16 * mt + 4 * q));
 }
 
 // 8 bytes at a 2-byte-aligned address (Q8_0 codes).
@@ -279,8 +362,12 @@ __host__ __device__ inline bool iq2_grouped_fast(const GroupArgs& a) {
          (uintptr_t)a.grid % 8 == 0;
 }
 
+// The pipelined Q2_K down takes its rows from the pipelined IQ2_XXS gate/up,
+// whose 128-feature tiles match its 128-column stages (one binary16 exponent
+// per work item and stage).
 __host__ __device__ inline bool q2k_grouped_fast(const GroupArgs& a) {
-  return a.qt_d == DS4MOE_Q2_K && a.H % kDNF == 0 && a.I % 512 == 0;
+  return a.qt_d == DS4MOE_Q2_K && a.H % kDNF == 0 && a.I % 512 == 0 && a.I <= 8192 &&
+         iq2_grouped_fast(a);
 }
 
 __host__ __device__ inline bool q80_shared_fast(const GroupArgs& a) {
@@ -396,7 +483,7 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
     }
     __syncthreads();
   }
-  swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu);
+  swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu, n0, kNT, nullptr, (uint32_t*)xt);
 }
 
 // ---------------------------------------------------------------------------
@@ -642,7 +729,11 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
     accg[mt] *= dgp * 0.125f;
     accu[mt] *= dup * 0.125f;
   }
-  swiglu_store<MT>(a, row0, nrows, mtiles, n, q, accg, accu);
+  // the rows' x exponents, loaded only now: held through the main loop they
+  // would take the registers of a second block per CU
+  uint32_t xe[MT];
+  load_row_xexp<MT>(a, row0, q, xe);
+  swiglu_store<MT>(a, row0, nrows, mtiles, n, q, accg, accu, n0, kGNF, xe, (uint32_t*)xt[0]);
 }
 
 // Small items (at most 16 rows, listed first): as k_grouped_gateup_iq2 with
@@ -665,6 +756,8 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2_small(GroupArgs
   const int n0 = blockIdx.x * kGNF;
   if (n0 >= a.I) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = lane >> 4;
+  uint32_t xe[1];  // the rows' x exponents, for the epilogue (requested first)
+  load_row_xexp<1>(a, row0, q, xe);
   const int n = n0 + 16 * w + (lane & 15);
   const uint32_t rep16 = (uint32_t)(lane & 7) << 4;
   const int rowbytes = (a.H / 256) * kIq2Bytes;
@@ -749,27 +842,83 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2_small(GroupArgs
     stage(s0 + 3, std::integral_constant<int, 3>{});
   }
   f32x4_t ag[1] = {accg * (dgp * 0.125f)}, au[1] = {accu * (dup * 0.125f)};
-  swiglu_store<1>(a, row0, nrows, 1, n, q, ag, au);
+  swiglu_store<1>(a, row0, nrows, 1, n, q, ag, au, n0, kGNF, xe, (uint32_t*)xr[0]);
 }
 
-// x (bf16) -> binary16 for k_grouped_gateup_iq2; magnitudes beyond the
-// binary16 range raise DS4MOE_FAULT_F16_RANGE.
-__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, size_t n8,
-                                                 uint16_t* __restrict__ x16, uint32_t* status) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const uint4 v = ((const uint4*)x)[i];
-  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-  uint32_t o[4];
-  bool ok = true;
+// x (bf16) -> binary16 for the grouped IQ2_XXS and Q4_K gate/up kernels,
+// one block per token: the token's values are scaled by the power of two
+// 2^e that brings their largest magnitude into [2^13, 2^14), exact for bf16
+// values (8 significant bits) down to 2^-14 of binary16's normal range; e
+// goes to byte r of word j - r of xrexp for each of the token's K sorted
+// rows j = inv[t*K + k] (r = 0..3, j - r >= 0).  NaN or
+// infinite values propagate (e = 0).  hidden is a multiple of 8; up to 8192
+// columns a thread's chunks stay in registers between the two passes.
+constexpr int kXRegChunks = 4;
+__global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, int H, int K,
+                                                 const int32_t* __restrict__ inv,
+                                                 uint16_t* __restrict__ x16,
+                                                 int8_t* __restrict__ xrexp) {
+  __shared__ uint32_t s_max[2][4];
+  const int t = blockIdx.x, tid = threadIdx.x, n8 = H / 8;
+  const uint4* xt = (const uint4*)(x + (size_t)t * H);
+  const bool regs = n8 <= 256 * kXRegChunks;
+  uint4 xv[kXRegChunks];
+  AbsMax am;
+  auto take = [&](uint4 v) {
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int k = 0; k < 4; k++) {
-    const float lo = __uint_as_float(in[k] << 16), hi = __uint_as_float(in[k] & 0xFFFF0000u);
-    ok &= fabsf(lo) <= 65504.0f && fabsf(hi) <= 65504.0f;
-    o[k] = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+    for (int k = 0; k < 4; k++) {
+      am.add(__uint_as_float(in[k] << 16));
+      am.add(__uint_as_float(in[k] & 0xFFFF0000u));
+    }
+  };
+  if (regs) {
+#pragma unroll
+    for (int j = 0; j < kXRegChunks; j++) {
+      const int i = tid + 256 * j;
+      xv[j] = i < n8 ? xt[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kXRegChunks; j++) take(xv[j]);
+  } else {
+    for (int i = tid; i < n8; i += 256) take(xt[i]);
   }
-  ((uint4*)x16)[i] = make_uint4(o[0], o[1], o[2], o[3]);
-  if (!ok) raise_fault(status, DS4MOE_FAULT_F16_RANGE);
+  am = wave_absmax(am);
+  if ((tid & 63) == 0) {
+    s_max[0][tid >> 6] = (uint32_t)am.smax;
+    s_max[1][tid >> 6] = am.umax;
+  }
+  __syncthreads();
+  AbsMax bm;
+  for (int i = 0; i < 4; i++) {
+    bm.smax = max(bm.smax, (int)s_max[0][i]);
+    bm.umax = max(bm.umax, s_max[1][i]);
+  }
+  bool bad;
+  const float M = bm.value(bad);
+  const int e = pow2_exponent(M, bad, 13);
+  for (int i = tid; i < 4 * K; i += 256) {
+    const int j = inv[t * K + (i >> 2)], r = i & 3;
+    if (j >= r) xrexp[4 * (size_t)(j - r) + r] = (int8_t)e;
+  }
+  auto put = [&](int i, uint4 v) {
+    const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const float lo = ldexpf(__uint_as_float(in[k] << 16), e);
+      const float hi = ldexpf(__uint_as_float(in[k] & 0xFFFF0000u), e);
+      o[k] = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+    }
+    ((uint4*)(x16 + (size_t)t * H))[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  };
+  if (regs) {
+#pragma unroll
+    for (int j = 0; j < kXRegChunks; j++)
+      if (tid + 256 * j < n8) put(tid + 256 * j, xv[j]);
+  } else {
+    for (int i = tid; i < n8; i += 256) put(i, xt[i]);  // the second read hits the cache
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -879,7 +1028,7 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_q80(GroupArgs a) {
     __syncthreads();
   }
   if (a.ksplit_g == 1) {
-    swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu);
+    swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu, n0, kGNF, nullptr, (uint32_t*)xt[0]);
     return;
   }
   // partial sums of this K share: part[z][row - T*K][f] (gate), [.. + I] (up)
@@ -922,7 +1071,16 @@ __global__ __launch_bounds__(256) void k_swiglu_finish(GroupArgs a) {
     g += gp[z];
     u += up[z];
   }
-  const float v = live ? silu(g) * u : 0.0f;
+  const float v0 = live ? silu(g) * u : 0.0f;
+  // one exponent per 64-feature range of the row (a wave: I is a multiple of
+  // 64, so no range straddles two rows), chosen as in swiglu_store
+  AbsMax am;
+  if (live) am.add(v0);
+  am = wave_absmax(am);
+  bool bad;
+  const float M = am.value(bad);
+  const int e = M < 2048.0f ? 0 : pow2_exponent(M, bad, 10);
+  const float v = ldexpf(v0, e);
   float sum = v;
   sum += dpp_f32<0xB1>(sum);
   sum += dpp_f32<0x4E>(sum);
@@ -938,7 +1096,7 @@ __global__ __launch_bounds__(256) void k_swiglu_finish(GroupArgs a) {
     a.hsh[row * (a.I / 16) + f / 16] = (uint16_t)shi;
     a.hsl[row * (a.I / 16) + f / 16] = (uint16_t)f32_to_f16_bits(sum - f16_bits_to_f32(shi));
   }
-  if (!(fabsf(v) <= 65504.0f)) raise_fault(a.status, DS4MOE_FAULT_F16_RANGE);
+  if ((f & 63) == 0) a.hexp[row * (a.I / 64) + f / 64] = (int8_t)e;
 }
 
 // down for one work item and 64 output features.  Grid (H/64, max_items).
@@ -949,6 +1107,7 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
   __shared__ uint4 al[kMC * 32];
   __shared__ uint2 sh_hi[kMC * 4];  // [m][4 x (4 f16)] sub-block sums, hi part
   __shared__ uint2 sh_lo[kMC * 4];
+  __shared__ int s_eb[kMC];         // row m's binary16 exponent in the staged block
   const int item = blockIdx.y;
   if (item >= *a.n_items) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
@@ -967,6 +1126,9 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
   const int mtiles = (nrows + 15) >> 4;
   f32x4_t acc[4];
   for (int mt = 0; mt < 4; mt++) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the accumulators of row 16 mt + 4 q + r are in units of 2^eb[mt][r], the
+  // exponent of that row's current block
+  int eb[4][4] = {};
   const size_t rowd = (size_t)ee * a.H + n;
   // K share (shared-expert split, a.ksplit_d blocks along z)
   const int ks = shr ? a.ksplit_d : 1, nbs = nb / ks, kb0 = blockIdx.z * nbs;
@@ -981,7 +1143,9 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; c++) q4c[c] = *(const uint2*)(qb + 16 + 32 * c + 8 * q);
     }
-    // stage: thread -> (row m, 16-column sub-block j): 16 values, high and low parts
+    // stage: thread -> (row m, 16-column sub-block j): 16 values, high and low
+    // parts, brought to the block's largest exponent (the smallest e of its
+    // four 64-feature ranges) when its range has another one
     for (int c = tid; c < kMC * 16; c += 256) {
       const int m = c >> 4, j = c & 15;
       uint4 h0 = make_uint4(0, 0, 0, 0), h1 = h0, l0 = h0, l1 = h0;
@@ -996,6 +1160,33 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
         l1 = lp[1];
         sh16 = a.hsh[row * (a.I / 16) + 16 * kb + j];
         sl16 = a.hsl[row * (a.I / 16) + 16 * kb + j];
+        const uint32_t ew = *(const uint32_t*)(a.hexp + row * (a.I / 64) + 4 * kb);
+        const int e0 = (int8_t)(ew & 0xFF), e1 = (int8_t)((ew >> 8) & 0xFF),
+                  e2 = (int8_t)((ew >> 16) & 0xFF), e3 = (int8_t)(ew >> 24);
+        const int emin = min(min(e0, e1), min(e2, e3));
+        const int er = (int8_t)((ew >> (8 * (j >> 2))) & 0xFF);
+        if (er != emin) {  // rescale the pair (hi, lo) exactly, then split again
+          const int de = emin - er;
+          auto fix = [&](uint32_t& hw, uint32_t& lw) {
+            const float v0 = ldexpf(f16_bits_to_f32(hw & 0xFFFFu) + f16_bits_to_f32(lw & 0xFFFFu), de);
+            const float v1 = ldexpf(f16_bits_to_f32(hw >> 16) + f16_bits_to_f32(lw >> 16), de);
+            const uint32_t a0 = f32_to_f16_bits(v0), a1 = f32_to_f16_bits(v1);
+            hw = a0 | (a1 << 16);
+            lw = f32_to_f16_bits(v0 - f16_bits_to_f32(a0)) | (f32_to_f16_bits(v1 - f16_bits_to_f32(a1)) << 16);
+          };
+          fix(h0.x, l0.x);
+          fix(h0.y, l0.y);
+          fix(h0.z, l0.z);
+          fix(h0.w, l0.w);
+          fix(h1.x, l1.x);
+          fix(h1.y, l1.y);
+          fix(h1.z, l1.z);
+          fix(h1.w, l1.w);
+          const float sv = ldexpf(f16_bits_to_f32(sh16) + f16_bits_to_f32(sl16), de);
+          sh16 = (uint16_t)f32_to_f16_bits(sv);
+          sl16 = (uint16_t)f32_to_f16_bits(sv - f16_bits_to_f32(sh16));
+        }
+        if (j == 0) s_eb[m] = emin;
       }
       // two 16-byte chunks (8 values each) per sub-block
       const int c0 = 2 * j, c1 = 2 * j + 1;
@@ -1007,6 +1198,16 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
       ((uint16_t*)sh_lo)[m * 16 + j] = sl16;
     }
     __syncthreads();
+    // the accumulators follow their rows' exponents (exact rescaling)
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int m = 16 * mt + 4 * q + r;
+        const int en = m < nrows ? s_eb[m] : 0;
+        acc[mt][r] = ldexpf(acc[mt][r], en - eb[mt][r]);
+        eb[mt][r] = en;
+      }
     const uint8_t* blk = D + (rowd * nb + kb) * bbd;
     if (qd == DS4MOE_Q2_K) {
       // lane: output row n, k = 4q + j inside each 16-value sub-block
@@ -1136,8 +1337,9 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
       if (mt >= mtiles) break;
       const int m = 16 * mt + 4 * q + r;
       if (m < nrows) {
-        if (ks == 1) a.y[(size_t)(row0 + m) * a.H + n] = acc[mt][r];
-        else a.part[((size_t)blockIdx.z * a.T + (row0 + m - a.T * a.K)) * a.H + n] = acc[mt][r];
+        const float y = ldexpf(acc[mt][r], -eb[mt][r]);
+        if (ks == 1) a.y[(size_t)(row0 + m) * a.H + n] = y;
+        else a.part[((size_t)blockIdx.z * a.T + (row0 + m - a.T * a.K)) * a.H + n] = y;
       }
     }
 }
@@ -1244,6 +1446,13 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float dp = 1.0f;  // d of the current block
+  // the stored rows are h * 2^e(stage), e the same for every row of the item
+  // (byte 2s of the item's first row): the accumulators hold the sum in
+  // units of the current stage's 2^e too.  Read through the scalar cache,
+  // four stages ahead, so that no wait for them waits for vector loads.
+  const int32_t* ex32 = (const int32_t*)(a.hexp + (size_t)row0 * (a.I / 64));
+  int ecur0 = load_scalar_i32(ex32, 0), ecur1 = load_scalar_i32(ex32, 1);
+  int ep = (int8_t)(ecur0 & 0xFF);
   auto stage = [&](int s, auto Rc) {
     constexpr int R = decltype(Rc)::value;
     if constexpr ((R & 1) == 0) H0 = h_load(min(s + 2, nst - 1));
@@ -1255,11 +1464,17 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
     const float dv = f16_bits_to_f32(cw.dd & 0xFFFFu);
     const float d = dv != 0.0f ? dv : 1.0f;
     const float rd = __builtin_amdgcn_rcpf(d);  // within 1 ulp
+    const int es = (int8_t)(((R < 2 ? ecur0 : ecur1) >> (16 * (R & 1))) & 0xFF), de = es - ep;
+    ep = es;
     if constexpr ((R & 1) == 0) {  // a block starts: sums in units of its d
-      const float r = dp * rd;
+      const float r = ldexpf(dp * rd, de);
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) acc[mt] *= r;
       dp = d;
+    } else if (de != 0) {
+      const float r = ldexpf(1.0f, de);
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) acc[mt] *= r;
     }
     // scale bytes 2j + (q >> 1) of the half (sub-block 8hf + 2j + (q >> 1))
     const uint32_t s4 = vperm(cw.s1, cw.s0, (q >> 1) ? 0x07050301u : 0x06040200u);
@@ -1314,12 +1529,16 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
     __syncthreads();
   };
   for (int s0 = 0; s0 < nst; s0 += 4) {
+    const int sn = s0 + 4 < nst ? s0 + 4 : s0;
+    const int enext0 = load_scalar_i32(ex32, sn / 2), enext1 = load_scalar_i32(ex32, sn / 2 + 1);
     stage(s0, std::integral_constant<int, 0>{});
     stage(s0 + 1, std::integral_constant<int, 1>{});
     stage(s0 + 2, std::integral_constant<int, 2>{});
     stage(s0 + 3, std::integral_constant<int, 3>{});
+    ecur0 = enext0;
+    ecur1 = enext1;
   }
-  const float fin = dp * 16777216.0f;
+  const float fin = ldexpf(dp * 16777216.0f, -ep);
 #pragma unroll
   for (int mt = 0; mt < MT; mt++)
 #pragma unroll
@@ -1365,6 +1584,7 @@ struct ImxArgs {
   int h_stride;
   const uint16_t* hh;
   const uint16_t* hl;
+  const int8_t* hexp;   // with hh/hl: the exponent of each row's 64-feature range
   float* gu;
   float* dn;
 };
@@ -1400,8 +1620,9 @@ __global__ __launch_bounds__(256) void k_imatrix(ImxArgs a) {
       else xv[u] = bf16_bits_to_f32(((const uint16_t*)a.x)[xi]);
       if constexpr (HF16) {
         const size_t hi = (size_t)r * a.I + cdc;
-        hv[u] = f16_bits_to_f32(a.hh[hi]);
-        lv[u] = f16_bits_to_f32(a.hl[hi]);
+        const int ex = a.hexp[(size_t)r * (a.I / 64) + cdc / 64];
+        hv[u] = ldexpf(f16_bits_to_f32(a.hh[hi]), -ex);
+        lv[u] = ldexpf(f16_bits_to_f32(a.hl[hi]), -ex);
       } else {
         hv[u] = a.h32[(size_t)p * a.h_stride + cdc];
         lv[u] = 0.0f;
@@ -1443,6 +1664,8 @@ __global__ __launch_bounds__(256) void k_grouped_gateup_q4k(GroupArgs a) {
   const int n0 = blockIdx.x * kNT;
   if (n0 >= a.I) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = lane >> 4;
+  uint32_t xe[4];  // the rows' x exponents, for the epilogue (requested first)
+  load_row_xexp<4>(a, row0, q, xe);
   const int n = n0 + 16 * w + (lane & 15);
   const int nb = a.H / 256;
   if (tid < kMC) tok[tid] = tid < nrows ? row_token(a, row0 + tid) : -1;
@@ -1503,7 +1726,7 @@ __global__ __launch_bounds__(256) void k_grouped_gateup_q4k(GroupArgs a) {
     }
     __syncthreads();
   }
-  swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu);
+  swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu, n0, kNT, xe, (uint32_t*)xt);
 }
 
 // The grouped kernels need bf16 x, 256-multiple shapes and formats they know

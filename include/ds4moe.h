@@ -241,7 +241,8 @@ ds4moe_status ds4moe_layer_noalloc(const ds4moe_shape* shape, const ds4moe_layer
 #define DS4MOE_FAULT_BAD_TABLE 0x4u    /* tid2eid row out of range / repeated   */
 #define DS4MOE_FAULT_UNCERTIFIED 0x8u  /* a score undecidable even in double-
                                           double arithmetic (see route)       */
-#define DS4MOE_FAULT_F16_RANGE 0x10u   /* an intermediate exceeded binary16     */
+#define DS4MOE_FAULT_F16_RANGE 0x10u   /* reserved: not raised (binary16
+                                          operands are scaled by powers of two) */
 #define DS4MOE_FAULT_BAD_INPUT 0x20u   /* encoder: non-finite value, negative or
                                           non-finite importance, grid value not
                                           8, 25 or 43                            */

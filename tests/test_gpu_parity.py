@@ -664,3 +664,50 @@ def test_ffn_q4k_experts(T):
         err = max_rel_err(out.cpu().numpy()[toks], want)
         say("  max|err|/rms = %g" % err)
         assert err <= TOL_FP32
+
+
+# --------------------------------------------------------------------------
+# activation outliers
+# --------------------------------------------------------------------------
+def outlier_x(w, T, mag, seed=7):
+    """bf16 activations N(0,1) with eight channels of every token set to
+    +-mag (as hidden states with a few large channels have)."""
+    x = g.activations(w, n_tok=T).copy()
+    rng = np.random.default_rng(seed)
+    ch = rng.choice(w.H, 8, replace=False)
+    sign = rng.choice([-1.0, 1.0], (T, 8))
+    vals = (sign * mag).astype(np.float32)
+    x[:, ch] = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    return x
+
+
+@pytest.mark.parametrize("mag", [200.0, 3000.0])
+@pytest.mark.parametrize("T", [1, 8, 40, 512])
+def test_ffn_activation_outliers(T, mag):
+    # matvec kernels (1, 8 tokens) and grouped MFMA kernels (40, 512 tokens):
+    # every output of tokens covering all touched experts within 2e-3 * RMS,
+    # no fault bit
+    from ds4gen.device import make_layer, host_experts
+    w = g.WORKLOADS[1]
+    say("outliers +-%g T %d" % (mag, T))
+    lt = make_layer(w, 0)
+    x = outlier_x(w, T, mag)
+    if T == 512:
+        ids, wts = g.zipf_routing(w.seed, T, w.E, w.K)
+    else:
+        ids, wts, _, _ = oracle.route(x, "bf16", g.router_weight(w, 0), "f16", g.router_bias(w, 0),
+                                      w.K)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, T)
+    out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    xd, idd, wd = dev(x), dev(ids), dev(wts)
+    ds4.expert_ffn(shp, experts_of(lt, w), None, ptr(xd), ds4.BF16, T, ptr(idd), ptr(wd),
+                   ptr(out), None, ptr(ws), nb, stream())
+    check_clean(ws)
+    toks = covering_tokens(ids, extra=(0, T - 1))
+    want = oracle.moe_ffn(x, "bf16", ids, wts, host_experts(w, 0, np.unique(ids[toks])),
+                          (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed),
+                          tokens=toks)
+    err = max_rel_err(out.cpu().numpy()[toks], want)
+    say("  max|err|/rms = %g (rms %g)" % (err, np.sqrt(np.mean(want.astype(np.float64) ** 2))))
+    assert err <= TOL_FP32
