@@ -39,8 +39,8 @@ GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "c373c7c8412b55a32e51cbc16cf8a5e1da82c0839c365822fcee649aaa2e3ec2",
-    "bytes": 26271479,
+    "sha256": "6b59230eb804c079daa441ffe55c53d49e519d84fb9bf03e94409f799bcac8aa",
+    "bytes": 26421106,
 }
 
 
