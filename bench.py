@@ -585,7 +585,7 @@ def bench_batched(args, which):
 def bench_sweep(args):
     """Decode batch sweep: the config-2 layer (learned router, Q8_0 shared
     expert, correlated tokens) at T = 1 .. 64 tokens per call, one
-    ds4moe_layer call per step.  Up to 13 tokens the routed experts run
+    ds4moe_layer call per step.  Up to 8 tokens the routed experts run
     through the streaming matvec kernels (one grid row per token), above that
     through the grouped MFMA kernels; the sweep shows where the union of
     experts makes the grouped form pay.  Each T: hip-graph replay of `steps` calls on distinct
@@ -598,7 +598,7 @@ def bench_sweep(args):
     from ds4gen.device import make_layer, to_dev
 
     w = g.WORKLOADS[2]
-    sizes = [1, 2, 4, 8, 12, 13, 14, 16, 24, 32, 48, 64]
+    sizes = [1, 2, 4, 8, 9, 12, 13, 14, 16, 24, 32, 48, 64]
     tmax = max(sizes)
     log("building layer tensors (%s)" % w.name)
     lt = make_layer(w, 0)

@@ -25,12 +25,15 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Few-token calls use the streaming matvec kernels: each token reads its six
 // experts, which beats the grouped kernels' one read per distinct expert up to
-// about 13 tokens of correlated decode (measured crossover 12..16 tokens).
+// kB1MaxTokensIq2 tokens of correlated decode with IQ2_XXS gate/up and Q2_K
+// down (measured: 8 tokens 145 vs 149 us per call, 9 tokens 158 vs 151) and
+// up to kB1MaxTokens with the other fast-path formats (Q4_K, not re-measured).
 constexpr int kSharedB1MaxTokens = 4;  // shared expert by per-token matvecs up to here
 constexpr int kFuseSelMaxTokens = 4;  // layer calls: selection fused into gate/up up to here
 // Above this many tokens the batch-1 down stages the SwiGLU vectors in LDS.
 constexpr int kDnStageMinTokens = 4;
 constexpr int kB1MaxTokens = 13;
+constexpr int kB1MaxTokensIq2 = 8;
 constexpr int kSharedSplitG = 16;  // K shares of a shared expert's gate/up in calls of few tokens (<= kMaxSplit)
 constexpr int kSharedSplitD = 4;   // and of its down
 constexpr int kSharedSplitMaxT = 64;  // "few": one work item of shared rows
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, con
 }
 
 // ---- expert FFN dispatch ----------------------------------------------------
-// Few tokens (up to kB1MaxTokens) with the V4-Flash expert shape and formats:
+// Few tokens (up to kB1MaxTokensIq2 or kB1MaxTokens) with the V4-Flash expert shape and formats:
 // the streaming matvec kernels, one grid row per token (the routed experts;
 // a shared expert then runs through the grouped path, split along K).
 bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x, int32_t x_dt,
@@ -264,7 +267,9 @@ bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x, int
   const bool gu = (ex.gate_qtype == DS4MOE_IQ2_XXS && ex.up_qtype == DS4MOE_IQ2_XXS) ||
                   (ex.gate_qtype == DS4MOE_Q4_K && ex.up_qtype == DS4MOE_Q4_K);
   const bool dn = ex.down_qtype == DS4MOE_Q2_K || ex.down_qtype == DS4MOE_Q4_K;
-  return T >= 1 && T <= kB1MaxTokens && x_dt == DS4MOE_BF16 && s.hidden == kH && s.inter == kI && ex.inter == kI &&
+  const bool iq2_q2k = ex.gate_qtype == DS4MOE_IQ2_XXS && ex.down_qtype == DS4MOE_Q2_K;
+  return T >= 1 && T <= (iq2_q2k ? kB1MaxTokensIq2 : kB1MaxTokens) && x_dt == DS4MOE_BF16 &&
+         s.hidden == kH && s.inter == kI && ex.inter == kI &&
          s.top_k == 6 && gu && dn && aligned(x, 16) && aligned(ex.gate, 16) &&
          aligned(ex.up, 16) && aligned(ex.down, 16) && aligned(ex.grid, 8);
 }
@@ -517,6 +522,14 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       if ((g.sh_I / 256) % kSharedSplitD == 0) g.ksplit_d = kSharedSplitD;
     }
     g.status = status;
+    g.sh_tail = 0;
+    // at most 16 tokens: at most 16 rows per expert, so no 64-row items
+    const bool large = T > 16;
+    // kernels that see only the shared expert's rows: grid rows over its
+    // work items, the last ns of the list
+    const int ns = (T + kMC - 1) / kMC;
+    GroupArgs gs = g;
+    gs.sh_tail = ns;
     const int imax = g.I > g.sh_I ? g.I : g.sh_I;
     {
       ProfScope prof(DS4MOE_K_GATEUP, st, !b1);
@@ -528,19 +541,21 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
                  at<uint16_t>(ws, L.x16), at<int8_t>(ws, L.xexp));
       if (iq2 && !b1) {  // small items (at most one per expert) and the rest
         launch_k(k_grouped_gateup_iq2_small, dim3(g.I / kGNF, E < TK ? E : TK), dim3(kGW * 64), 0, st, g);
-        launch_k(k_grouped_gateup_iq2<4>, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
+        if (large) launch_k(k_grouped_gateup_iq2<4>, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
       }
       if (q4k && !b1)
         launch_k(k_grouped_gateup_q4k, dim3((g.I + kNT - 1) / kNT, mi), dim3(256), 0, st, g);
       if (q80) {
-        launch_k(k_grouped_gateup_q80, dim3(g.sh_I / kGNF, mi, g.ksplit_g), dim3(kGW * 64), 0, st, g);
+        launch_k(k_grouped_gateup_q80, dim3(g.sh_I / kGNF, ns, g.ksplit_g), dim3(kGW * 64), 0, st, gs);
         if (g.ksplit_g > 1)
           launch_k(k_swiglu_finish, dim3((T * g.sh_I + 255) / 256), dim3(256), 0, st, g);
       } else {
-        g.ksplit_g = 1;
+        g.ksplit_g = gs.ksplit_g = 1;
       }
-      if ((!iq2 && !q4k && !b1) || (sh && !q80))
+      if (!iq2 && !q4k && !b1)  // every item
         launch_k(k_grouped_gateup, dim3((imax + kNT - 1) / kNT, mi), dim3(256), 0, st, g);
+      else if (sh && !q80)  // the shared expert's items
+        launch_k(k_grouped_gateup, dim3((imax + kNT - 1) / kNT, ns), dim3(256), 0, st, gs);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     {
@@ -548,10 +563,12 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       const bool q2k = q2k_grouped_fast(g);
       if (q2k && !b1) {  // small items and the rest
         launch_k(k_grouped_down_q2k<1>, dim3(g.H / kDNF, E < TK ? E : TK), dim3(kDW * 64), 0, st, g);
-        launch_k(k_grouped_down_q2k<4>, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
+        if (large) launch_k(k_grouped_down_q2k<4>, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
       }
-      if (!q2k || sh)
+      if (!q2k && !b1)  // every item
         launch_k(k_grouped_down, dim3(s.hidden / kNT, mi, g.ksplit_d), dim3(256), 0, st, g);
+      else if (sh)  // the shared expert's items
+        launch_k(k_grouped_down, dim3(s.hidden / kNT, ns, g.ksplit_d), dim3(256), 0, st, gs);
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;
     if (imx && !b1 &&
@@ -561,13 +578,13 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     {
       ProfScope prof(DS4MOE_K_OTHER, st, !b1);
       const size_t n = (size_t)T * s.hidden;
-      // the shared expert's output: y rows T*K.. (one share) or the K shares
-      // in part, added by k_add_shared after the routed combine
-      const bool add_sh = sh && (b1 || g.ksplit_d > 1);
+      // the shared expert's output: y rows T*K.. (one share) or its K shares
+      // in part; after the per-token matvecs k_add_shared adds it to their output
+      const bool add_sh = sh && b1;
       if (!b1)
         launch_k(k_grouped_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                 (const float*)g.y, (const int32_t*)inv, wts, T, K, s.hidden,
-                 (sh && !add_sh) ? 1 : 0, out, residual);
+                 (const float*)g.y, (const int32_t*)inv, wts, T, K, s.hidden, sh ? 1 : 0, out,
+                 residual, (const float*)g.part, g.ksplit_d);
       if (add_sh)
         launch_k(k_add_shared, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                  (const float*)g.y, (const float*)g.part, g.ksplit_d, TK, T, s.hidden,

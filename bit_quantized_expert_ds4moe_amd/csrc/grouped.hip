@@ -164,7 +164,15 @@ struct GroupArgs {
   // [split][T][2*I] (gate, up) then [split][T][H] (down), reduced in a fixed order
   int ksplit_g, ksplit_d;
   float* part;
+  // > 0: the grid rows cover only the shared expert's work items, the last
+  // sh_tail of the list (launches of kernels that see shared rows only)
+  int sh_tail;
 };
+
+// The work item of grid row blockIdx.y.
+__device__ inline int grid_item(const GroupArgs& a) {
+  return a.sh_tail > 0 ? a.n_items[0] - a.sh_tail + (int)blockIdx.y : (int)blockIdx.y;
+}
 
 __device__ inline int row_token(const GroupArgs& a, int row) {
   return row < a.T * a.K ? a.perm[row] / a.K : row - a.T * a.K;
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(256) void k_grouped_gateup(GroupArgs a) {
   __shared__ uint4 gt8[256 * 8];
   __shared__ uint4 mt8[128 * 8];
   __shared__ int tok[kMC];
-  const int item = blockIdx.y;
+  const int item = grid_item(a);
   if (item >= *a.n_items) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   const bool sh = e == a.E;
@@ -961,7 +969,7 @@ __device__ inline bf16x8_t q80_stage_frag(const Q80Stage& st, int i, float& scal
 __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_q80(GroupArgs a) {
   __shared__ uint4 xt[2][kMC * 8];  // 2 x 8 KB: row m, 16-byte chunk c at m*8 + (c ^ ((m >> 1) & 7))
   __shared__ int tok[kMC];
-  const int item = blockIdx.y;
+  const int item = grid_item(a);
   if (item >= *a.n_items) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   if (e != a.E) return;  // the shared expert only
@@ -1108,7 +1116,7 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
   __shared__ uint2 sh_hi[kMC * 4];  // [m][4 x (4 f16)] sub-block sums, hi part
   __shared__ uint2 sh_lo[kMC * 4];
   __shared__ int s_eb[kMC];         // row m's binary16 exponent in the staged block
-  const int item = blockIdx.y;
+  const int item = grid_item(a);
   if (item >= *a.n_items) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   const bool shr = e == a.E;
@@ -1549,15 +1557,26 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
     }
 }
 
-// out[t] = sum_k w[t][k] y[inv[t*K+k]] (+ y[T*K + t]) (+ residual), fixed order.
+// out[t] = sum_k w[t][k] y[inv[t*K+k]] (+ the shared row) (+ residual), fixed
+// order.  The shared row (with_shared) is y[T*K + t], or with ksplit > 1 the
+// sum of its K shares in part ([ksplit][T][H]) in share order.
 __global__ void k_grouped_combine(const float* y, const int32_t* inv, const float* wts, int T, int K,
-                                  int H, int with_shared, float* out, float* residual) {
+                                  int H, int with_shared, float* out, float* residual,
+                                  const float* part, int ksplit) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (size_t)T * H) return;
   const int t = (int)(idx / H), c = (int)(idx % H);
+  float sh = 0.0f;
+  if (with_shared) {
+    if (ksplit == 1) {
+      sh = y[((size_t)T * K + t) * H + c];
+    } else {
+      for (int z = 0; z < ksplit; z++) sh += part[(size_t)z * T * H + idx];
+    }
+  }
   float acc = 0.0f;
   for (int k = 0; k < K; k++) acc = fmaf(wts[t * K + k], y[(size_t)inv[t * K + k] * H + c], acc);
-  if (with_shared) acc += y[((size_t)T * K + t) * H + c];
+  if (with_shared) acc += sh;
   if (residual) residual[idx] += acc;
   else out[idx] = acc;
 }
@@ -1657,7 +1676,7 @@ __global__ __launch_bounds__(256) void k_imatrix(ImxArgs a) {
 __global__ __launch_bounds__(256) void k_grouped_gateup_q4k(GroupArgs a) {
   __shared__ uint4 xt[kMC * 16];
   __shared__ int tok[kMC];
-  const int item = blockIdx.y;
+  const int item = grid_item(a);
   if (item >= *a.n_items) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   if (e == a.E) return;  // the shared expert runs in its own kernels

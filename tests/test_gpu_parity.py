@@ -347,8 +347,9 @@ def test_layer_route_and_ffn(widx):
     # configs 0, 1 and 2; the config-1 layer with Q4_K experts (1 and 3
     # tokens) and with IQ2_XXS gate/up and Q4_K down; config 2 (Q8_0 shared
     # expert) at 2 tokens (few-token kernels, the top-6 selection of each
-    # token fused into gate/up), 8 and 13 (few-token kernels, selection
-    # kernel) and 14 (grouped kernels)
+    # token fused into gate/up), 8 (few-token kernels, selection kernel), 13
+    # and 14 (grouped kernels: at most 16 rows per item, so the small-item
+    # kernels alone)
     from ds4gen.device import make_layer, host_experts, host_shared
     w = _layer_workload(widx)
     say("layer", w.name, "T", w.T)
