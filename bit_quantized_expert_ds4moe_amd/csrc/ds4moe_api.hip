@@ -28,7 +28,11 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // kB1MaxTokensIq2 tokens of correlated decode with IQ2_XXS gate/up and Q2_K
 // down (measured: 8 tokens 145 vs 149 us per call, 9 tokens 158 vs 151) and
 // up to kB1MaxTokens with the other fast-path formats (Q4_K, not re-measured).
-constexpr int kSharedB1MaxTokens = 4;  // shared expert by per-token matvecs up to here
+constexpr int kSharedB1MaxTokens = 4;  // shared expert by per-token matvecs up to here,
+// then up to kSharedFewMaxTokens (on the matvec path) by matvecs that read its
+// weights once for every token; beyond, by the grouped kernels
+constexpr int kSharedFewMaxTokens = 8;
+static_assert(kSharedFewMaxTokens <= kShFewMaxT, "the few-token shared kernels hold kShFewMaxT tokens");
 constexpr int kFuseSelMaxTokens = 4;  // layer calls: selection fused into gate/up up to here
 // Above this many tokens the batch-1 down stages the SwiGLU vectors in LDS.
 constexpr int kDnStageMinTokens = 4;
@@ -281,6 +285,9 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
                         const float* wts, float* out, float* residual, void* ws, const Layout& L,
                         hipStream_t st, const SharedB1Args* shb = nullptr,
                         const ds4moe_router* rt = nullptr) {
+  // one weight read for all tokens, measured faster than the grouped Q8_0
+  // kernels from 5 to 8 tokens (5: 98.9 vs 108.3 us per layer call, 8: equal)
+  const bool sh_few = shb && T > kSharedB1MaxTokens && T <= kSharedFewMaxTokens;
   uint32_t* status = at<uint32_t>(ws, L.status);
   float* h = at<float>(ws, L.h);
   GateUpB1Args g{};
@@ -317,7 +324,8 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   if (rc != DS4MOE_OK) return rc;
   if (shb) {  // the shared expert's gate/up; its down rides along with the routed one
     ProfScope prof(DS4MOE_K_OTHER, st);
-    launch_k(k_shared_gateup_q80_b1, dim3(kI / 8, T), dim3(256), 0, st, *shb);
+    if (sh_few) launch_k(k_shared_gateup_q80_few, dim3(kI / 8), dim3(256), 0, st, *shb, T);
+    else launch_k(k_shared_gateup_q80_b1, dim3(kI / 8, T), dim3(256), 0, st, *shb);
     if ((rc = launched()) != DS4MOE_OK) return rc;
   }
   const int32_t* dids = kbuf ? ids : ids_in;
@@ -328,7 +336,7 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
     if (ex.down_qtype == DS4MOE_Q4_K)
       launch_k(k_down_q4k_b1, dgrid, dim3(kDnThreads), 0, st, h, down, dids, wts, s.n_expert, out,
                residual, status);
-    else if (shb)
+    else if (shb && !sh_few)
       launch_k(k_down_q2k_b1<true, false>, dgrid, dim3(kDnThreadsSh), 0, st, h, down, dids, wts,
                s.n_expert, out, residual, status, (const float*)shb->h, shb->down);
     else if (T > kDnStageMinTokens)
@@ -339,9 +347,10 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
                s.n_expert, out, residual, status, (const float*)nullptr, (const uint8_t*)nullptr);
   }
   if ((rc = launched()) != DS4MOE_OK) return rc;
-  if (shb && ex.down_qtype == DS4MOE_Q4_K) {  // Q4_K routed down: the shared down on its own
+  if (shb && (sh_few || ex.down_qtype == DS4MOE_Q4_K)) {  // the shared down on its own
     ProfScope prof(DS4MOE_K_OTHER, st);
-    launch_k(k_shared_down_q80_b1, dim3(kH / 16, T), dim3(256), 0, st, *shb);
+    if (sh_few) launch_k(k_shared_down_q80_few, dim3(kH / 16), dim3(256), 0, st, *shb, T);
+    else launch_k(k_shared_down_q80_b1, dim3(kH / 16, T), dim3(256), 0, st, *shb);
     rc = launched();
   }
   return rc;
@@ -421,10 +430,10 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
   uint32_t* status = at<uint32_t>(ws, L.status);
   const bool b1 = fast_b1(s, ex, x, x_dt, T) && (!sh || grouped_eligible(s, ex, sh, x, x_dt, T));
   if (b1) {
-    // a Q8_0 shared expert at up to kSharedB1MaxTokens tokens runs as
-    // per-token matvecs inside launch_b1 (beyond that its weights are better
-    // read once by the grouped kernels below)
-    const bool shb1 = sh && T <= kSharedB1MaxTokens && shared_b1_ok(s, *sh, x, x_dt);
+    // a Q8_0 shared expert runs inside launch_b1 as matvecs: per token up
+    // to kSharedB1MaxTokens tokens, then one weight read for all tokens up to
+    // kSharedFewMaxTokens; beyond, the grouped kernels below take it
+    const bool shb1 = sh && T <= kSharedFewMaxTokens && shared_b1_ok(s, *sh, x, x_dt);
     SharedB1Args sa{};
     if (shb1) {
       sa.x = (const uint16_t*)x;

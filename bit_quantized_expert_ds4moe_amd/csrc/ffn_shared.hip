@@ -140,6 +140,106 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_b1(SharedB1Args a) {
   }
 }
 
+// The same two matvecs for a few tokens at once (T <= kShFewMaxT): every
+// wave requests its weight rows once, the workgroup then stages the
+// activations of all T tokens in LDS (16-byte chunk c of a token at
+// c + (c >> 4), one spare chunk per 16, so that the 16 lanes one read
+// serves hit 16 distinct bank groups) and the wave runs through the tokens.
+constexpr int kShFewMaxT = 13;
+constexpr int kShXc = kH / 8;                  // 16-byte chunks of a token's x (bf16)
+constexpr int kShXs = kShXc + kShXc / 16;      // and its LDS slots
+constexpr int kShHc = kI / 4;                  // 16-byte chunks of a token's h (fp32)
+constexpr int kShHs = kShHc + kShHc / 16;
+
+// gate/up: grid (2048 / 8), 256 threads, rows as in k_shared_gateup_q80_b1.
+__global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, int T) {
+  __shared__ uint4 xs[kShFewMaxT * kShXs];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int f0 = 8 * blockIdx.x + 2 * w;
+  uint32_t D[4][17];  // gate f0, gate f0+1, up f0, up f0+1
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const uint8_t* base = (r < 2 ? a.gate : a.up) + (size_t)(f0 + (r & 1)) * kShRowGu;
+    q80_pair_load(base + 68 * lane, D[r]);
+  }
+  for (int c = tid; c < T * kShXc; c += 256) {
+    const int t = c / kShXc, k = c % kShXc;
+    xs[t * kShXs + k + (k >> 4)] = ((const uint4*)(a.x + (size_t)t * kH))[k];
+  }
+  __syncthreads();
+  const uint4* xl0 = xs + 8 * lane + (lane >> 1);  // chunk 8 lane
+  for (int t = 0; t < T; t++) {
+    uint4 xq[8];
+#pragma unroll
+    for (int q = 0; q < 8; q++) xq[q] = xl0[t * kShXs + q];
+    auto xval = [&](int i) {
+      const uint4 q = xq[i >> 3];
+      const uint32_t ww = (i & 6) == 0 ? q.x : (i & 6) == 2 ? q.y : (i & 6) == 4 ? q.z : q.w;
+      return bf16_bits_to_f32((i & 1) ? (ww >> 16) : (ww & 0xFFFFu));
+    };
+    uint32_t xl[16], xh[16];
+    int sl, sh;
+    const float S = q4k_fix(xval, xl, xh, sl, sh);
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) v[r] = wave_sum(S * q80_dot64(D[r], xl, xh, sl, sh));
+    if (lane < 2) {
+      const float g = lane ? v[1] : v[0], u = lane ? v[3] : v[2];
+      a.h[(size_t)t * kI + f0 + lane] = silu(g) * u;
+    }
+  }
+}
+
+// down: grid (4096 / 16), 256 threads, rows as in k_shared_down_q80_b1;
+// out[t] (or the residual) += the shared output.
+__global__ __launch_bounds__(256) void k_shared_down_q80_few(SharedB1Args a, int T) {
+  __shared__ float4 hs[kShFewMaxT * kShHs];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int u = lane >> 5, L = lane & 31;
+  const int r0 = 16 * blockIdx.x + 4 * w;
+  uint32_t D0[17], D1[17];
+  q80_pair_load(a.down + (size_t)(r0 + u) * kShRowDn + 68 * L, D0);
+  q80_pair_load(a.down + (size_t)(r0 + 2 + u) * kShRowDn + 68 * L, D1);
+  for (int c = tid; c < T * kShHc; c += 256) {
+    const int t = c / kShHc, k = c % kShHc;
+    hs[t * kShHs + k + (k >> 4)] = ((const float4*)(a.h + (size_t)t * kI))[k];
+  }
+  __syncthreads();
+  const float4* hl0 = hs + 16 * L + L;  // chunk 16 L
+  auto rl = [](float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+  };
+  for (int t = 0; t < T; t++) {
+    float4 hv[16];
+#pragma unroll
+    for (int q = 0; q < 16; q++) hv[q] = hl0[t * kShHs + q];
+    auto hval = [&](int i) {
+      const float4 q = hv[i >> 2];
+      return (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
+    };
+    uint32_t xl[16], xh[16];
+    int sl, sh;
+    const float S = q4k_fix(hval, xl, xh, sl, sh);
+    float p0 = S * q80_dot64(D0, xl, xh, sl, sh), p1 = S * q80_dot64(D1, xl, xh, sl, sh);
+    p0 += dpp_f32<0xB1>(p0);
+    p0 += dpp_f32<0x4E>(p0);
+    p0 += dpp_f32<0x141>(p0);
+    p0 += dpp_f32<0x140>(p0);
+    p1 += dpp_f32<0xB1>(p1);
+    p1 += dpp_f32<0x4E>(p1);
+    p1 += dpp_f32<0x141>(p1);
+    p1 += dpp_f32<0x140>(p1);
+    const float t0 = rl(p0, 0) + rl(p0, 16), t1 = rl(p0, 32) + rl(p0, 48);
+    const float t2 = rl(p1, 0) + rl(p1, 16), t3 = rl(p1, 32) + rl(p1, 48);
+    if (lane < 4) {
+      const float tot = lane == 0 ? t0 : lane == 1 ? t1 : lane == 2 ? t2 : t3;
+      a.out[(size_t)t * kH + r0 + lane] += tot;
+    }
+  }
+}
+
 // The shared expert's down as the seventh slot of k_down_q2k_b1<true, false>: rows
 // row0 + 2m + u (m < 4) of the wave, lane L of half u covering columns
 // 64L .. +63 (two Q8_0 blocks) of the shared SwiGLU row sh_h (global memory);

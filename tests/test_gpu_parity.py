@@ -336,20 +336,23 @@ def _layer_workload(widx):
         return replace(Q4_LAYER, T=3)
     if widx == "q4k-shared-t2":
         return replace(Q4_LAYER, T=2, shared=True)
+    if widx == "q4k-shared-t6":
+        return replace(Q4_LAYER, T=6, shared=True)
     if isinstance(widx, str) and widx.startswith("b8-t"):
         return replace(g.WORKLOADS[2], T=int(widx[4:]))
     return g.WORKLOADS[widx]
 
 
-@pytest.mark.parametrize("widx", [0, 1, "q4k", "mixed", "q4k-t3", "q4k-shared-t2", 2, "b8-t2",
-                                  "b8-t13", "b8-t14"])
+@pytest.mark.parametrize("widx", [0, 1, "q4k", "mixed", "q4k-t3", "q4k-shared-t2", "q4k-shared-t6", 2,
+                                  "b8-t2", "b8-t5", "b8-t7", "b8-t13", "b8-t14"])
 def test_layer_route_and_ffn(widx):
     # configs 0, 1 and 2; the config-1 layer with Q4_K experts (1 and 3
-    # tokens) and with IQ2_XXS gate/up and Q4_K down; config 2 (Q8_0 shared
-    # expert) at 2 tokens (few-token kernels, the top-6 selection of each
-    # token fused into gate/up), 8 (few-token kernels, selection kernel), 13
-    # and 14 (grouped kernels: at most 16 rows per item, so the small-item
-    # kernels alone)
+    # tokens, and 2 and 6 with a Q8_0 shared expert) and with IQ2_XXS gate/up
+    # and Q4_K down; config 2 (Q8_0 shared expert) at 2 tokens (few-token
+    # kernels, the top-6 selection of each token fused into gate/up, shared
+    # expert per token), 5, 7 and 8 (few-token kernels, selection kernel,
+    # shared expert read once for all tokens), 13 and 14 (grouped kernels: at
+    # most 16 rows per item, so the small-item kernels alone)
     from ds4gen.device import make_layer, host_experts, host_shared
     w = _layer_workload(widx)
     say("layer", w.name, "T", w.T)
