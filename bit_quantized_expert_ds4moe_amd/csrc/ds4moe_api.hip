@@ -32,7 +32,6 @@ constexpr int kSharedB1MaxTokens = 4;  // shared expert by per-token matvecs up 
 // then up to kSharedFewMaxTokens (on the matvec path) by matvecs that read its
 // weights once for every token; beyond, by the grouped kernels
 constexpr int kSharedFewMaxTokens = 8;
-static_assert(kSharedFewMaxTokens <= kShFewMaxT, "the few-token shared kernels hold kShFewMaxT tokens");
 constexpr int kFuseSelMaxTokens = 4;  // layer calls: selection fused into gate/up up to here
 // Above this many tokens the batch-1 down stages the SwiGLU vectors in LDS.
 constexpr int kDnStageMinTokens = 4;
@@ -230,24 +229,24 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, con
     const double ns = 1.0 / sqrt(ss / (double)H + (double)eps);
     // results outside the normal bfloat16 range (rare) take the general
     // rounding in a separate pass, so the common loop has no call in it
-    uint32_t r[kRegCols];
+    uint32_t bb[kRegCols];
     bool all_ok = true;
 #pragma unroll
     for (int j = 0; j < kRegCols; j++) {
       bool ok;
-      r[j] = f64_to_bf16_bits_fast((double)v[j] * ns * (double)wv[j], ok);
+      bb[j] = f64_to_bf16_bits_fast((double)v[j] * ns * (double)wv[j], ok);
       all_ok &= ok;
     }
     if (!all_ok)
       for (int j = 0; j < kRegCols; j++) {
         bool ok;
         (void)f64_to_bf16_bits_fast((double)v[j] * ns * (double)wv[j], ok);
-        if (!ok) r[j] = f64_to_bf16_bits_general((double)v[j] * ns * (double)wv[j]);
+        if (!ok) bb[j] = f64_to_bf16_bits_general((double)v[j] * ns * (double)wv[j]);
       }
 #pragma unroll
     for (int j = 0; j < kRegCols; j++) {
       const int c = tid + 256 * j;
-      if (c < H) xn[(size_t)t * H + c] = (uint16_t)r[j];
+      if (c < H) xn[(size_t)t * H + c] = (uint16_t)bb[j];
     }
     return;
   }
@@ -324,7 +323,9 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   if (rc != DS4MOE_OK) return rc;
   if (shb) {  // the shared expert's gate/up; its down rides along with the routed one
     ProfScope prof(DS4MOE_K_OTHER, st);
-    if (sh_few) launch_k(k_shared_gateup_q80_few, dim3(kI / 8), dim3(256), 0, st, *shb, T);
+    if (sh_few)
+      launch_k(k_shared_gateup_q80_few, dim3(kI / 8, (T + kShFewTok - 1) / kShFewTok), dim3(256), 0,
+               st, *shb, T);
     else launch_k(k_shared_gateup_q80_b1, dim3(kI / 8, T), dim3(256), 0, st, *shb);
     if ((rc = launched()) != DS4MOE_OK) return rc;
   }
@@ -349,7 +350,9 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   if ((rc = launched()) != DS4MOE_OK) return rc;
   if (shb && (sh_few || ex.down_qtype == DS4MOE_Q4_K)) {  // the shared down on its own
     ProfScope prof(DS4MOE_K_OTHER, st);
-    if (sh_few) launch_k(k_shared_down_q80_few, dim3(kH / 16), dim3(256), 0, st, *shb, T);
+    if (sh_few)
+      launch_k(k_shared_down_q80_few, dim3(kH / 16, (T + kShFewTok - 1) / kShFewTok), dim3(256), 0,
+               st, *shb, T);
     else launch_k(k_shared_down_q80_b1, dim3(kH / 16, T), dim3(256), 0, st, *shb);
     rc = launched();
   }

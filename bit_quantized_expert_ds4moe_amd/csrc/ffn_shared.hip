@@ -140,20 +140,23 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_b1(SharedB1Args a) {
   }
 }
 
-// The same two matvecs for a few tokens at once (T <= kShFewMaxT): every
-// wave requests its weight rows once, the workgroup then stages the
-// activations of all T tokens in LDS (16-byte chunk c of a token at
-// c + (c >> 4), one spare chunk per 16, so that the 16 lanes one read
-// serves hit 16 distinct bank groups) and the wave runs through the tokens.
-constexpr int kShFewMaxT = 13;
+// The same two matvecs for a few tokens at once: grid row y takes tokens
+// kShFewTok y .. +kShFewTok-1 (of T); every wave requests its weight rows
+// once, the workgroup then stages those tokens' activations in LDS (16-byte
+// chunk c of a token at c + (c >> 4), one spare chunk per 16, so that the 16
+// lanes one read serves hit 16 distinct bank groups) and the wave runs
+// through the tokens.
+constexpr int kShFewTok = 4;
 constexpr int kShXc = kH / 8;                  // 16-byte chunks of a token's x (bf16)
 constexpr int kShXs = kShXc + kShXc / 16;      // and its LDS slots
 constexpr int kShHc = kI / 4;                  // 16-byte chunks of a token's h (fp32)
 constexpr int kShHs = kShHc + kShHc / 16;
 
-// gate/up: grid (2048 / 8), 256 threads, rows as in k_shared_gateup_q80_b1.
+// gate/up: grid (2048 / 8, rows of kShFewTok tokens), 256 threads, rows as in
+// k_shared_gateup_q80_b1.
 __global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, int T) {
-  __shared__ uint4 xs[kShFewMaxT * kShXs];
+  __shared__ uint4 xs[kShFewTok * kShXs];
+  const int t0 = kShFewTok * blockIdx.y, nt = min(kShFewTok, T - t0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int f0 = 8 * blockIdx.x + 2 * w;
@@ -163,13 +166,13 @@ __global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, i
     const uint8_t* base = (r < 2 ? a.gate : a.up) + (size_t)(f0 + (r & 1)) * kShRowGu;
     q80_pair_load(base + 68 * lane, D[r]);
   }
-  for (int c = tid; c < T * kShXc; c += 256) {
+  for (int c = tid; c < nt * kShXc; c += 256) {
     const int t = c / kShXc, k = c % kShXc;
-    xs[t * kShXs + k + (k >> 4)] = ((const uint4*)(a.x + (size_t)t * kH))[k];
+    xs[t * kShXs + k + (k >> 4)] = ((const uint4*)(a.x + (size_t)(t0 + t) * kH))[k];
   }
   __syncthreads();
   const uint4* xl0 = xs + 8 * lane + (lane >> 1);  // chunk 8 lane
-  for (int t = 0; t < T; t++) {
+  for (int t = 0; t < nt; t++) {
     uint4 xq[8];
 #pragma unroll
     for (int q = 0; q < 8; q++) xq[q] = xl0[t * kShXs + q];
@@ -186,15 +189,16 @@ __global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, i
     for (int r = 0; r < 4; r++) v[r] = wave_sum(S * q80_dot64(D[r], xl, xh, sl, sh));
     if (lane < 2) {
       const float g = lane ? v[1] : v[0], u = lane ? v[3] : v[2];
-      a.h[(size_t)t * kI + f0 + lane] = silu(g) * u;
+      a.h[(size_t)(t0 + t) * kI + f0 + lane] = silu(g) * u;
     }
   }
 }
 
-// down: grid (4096 / 16), 256 threads, rows as in k_shared_down_q80_b1;
+// down: grid (4096 / 16, rows of kShFewTok tokens), 256 threads, rows as in k_shared_down_q80_b1;
 // out[t] (or the residual) += the shared output.
 __global__ __launch_bounds__(256) void k_shared_down_q80_few(SharedB1Args a, int T) {
-  __shared__ float4 hs[kShFewMaxT * kShHs];
+  __shared__ float4 hs[kShFewTok * kShHs];
+  const int t0 = kShFewTok * blockIdx.y, nt = min(kShFewTok, T - t0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int u = lane >> 5, L = lane & 31;
@@ -202,16 +206,16 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_few(SharedB1Args a, int
   uint32_t D0[17], D1[17];
   q80_pair_load(a.down + (size_t)(r0 + u) * kShRowDn + 68 * L, D0);
   q80_pair_load(a.down + (size_t)(r0 + 2 + u) * kShRowDn + 68 * L, D1);
-  for (int c = tid; c < T * kShHc; c += 256) {
+  for (int c = tid; c < nt * kShHc; c += 256) {
     const int t = c / kShHc, k = c % kShHc;
-    hs[t * kShHs + k + (k >> 4)] = ((const float4*)(a.h + (size_t)t * kI))[k];
+    hs[t * kShHs + k + (k >> 4)] = ((const float4*)(a.h + (size_t)(t0 + t) * kI))[k];
   }
   __syncthreads();
   const float4* hl0 = hs + 16 * L + L;  // chunk 16 L
   auto rl = [](float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
   };
-  for (int t = 0; t < T; t++) {
+  for (int t = 0; t < nt; t++) {
     float4 hv[16];
 #pragma unroll
     for (int q = 0; q < 16; q++) hv[q] = hl0[t * kShHs + q];
@@ -231,11 +235,11 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_few(SharedB1Args a, int
     p1 += dpp_f32<0x4E>(p1);
     p1 += dpp_f32<0x141>(p1);
     p1 += dpp_f32<0x140>(p1);
-    const float t0 = rl(p0, 0) + rl(p0, 16), t1 = rl(p0, 32) + rl(p0, 48);
-    const float t2 = rl(p1, 0) + rl(p1, 16), t3 = rl(p1, 32) + rl(p1, 48);
+    const float s0 = rl(p0, 0) + rl(p0, 16), s1 = rl(p0, 32) + rl(p0, 48);  // rows r0, r0 + 1
+    const float s2 = rl(p1, 0) + rl(p1, 16), s3 = rl(p1, 32) + rl(p1, 48);  // rows r0 + 2, r0 + 3
     if (lane < 4) {
-      const float tot = lane == 0 ? t0 : lane == 1 ? t1 : lane == 2 ? t2 : t3;
-      a.out[(size_t)t * kH + r0 + lane] += tot;
+      const float tot = lane == 0 ? s0 : lane == 1 ? s1 : lane == 2 ? s2 : s3;
+      a.out[(size_t)(t0 + t) * kH + r0 + lane] += tot;
     }
   }
 }
