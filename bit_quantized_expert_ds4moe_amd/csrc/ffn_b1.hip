@@ -356,9 +356,12 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
 // Grid (H / kDnBlockRows, T), 12 waves: wave w handles routed slot k = w / 2
 // for kDnRows rows (w odd: the second half of the workgroup's 16 rows), two
 // rows per step: lanes 0-31 take the even row, lanes 32-63 the odd one.
-// The token's six SwiGLU vectors (48 KB) are read once per workgroup into
-// LDS before any weight is requested (the vector memory path of a compute
-// unit returns data in request order, so h must not queue behind weights).
+// Each lane requests its slot's SwiGLU values before the weights (the vector
+// memory path of a compute unit returns data in request order, so h must not
+// queue behind weights): straight from global memory (up to 4 tokens, and
+// whenever a shared expert rides along as the seventh slot), or with STAGE
+// (more than 4 tokens, no seventh slot) from LDS, where the workgroup copies
+// the token's six vectors (48 KB) before the weights are requested.
 // Lane 32u + L (L < 32), b = L >> 2, hq = (L >> 1) & 1, p = L & 1, covers
 // the 64 columns i = 256b + 128hq + 32s + 16p + l (s < 4, l < 16) of its
 // row: their 2-bit codes are exactly the 16 bytes qs[32hq + 16p .. +15] of
@@ -379,7 +382,8 @@ constexpr int kDnThreadsSh = 14 * 64;      // with the shared expert as a sevent
 
 // The workgroup's 16 rows of a Q8_0 shared expert's down, as the seventh slot
 // (two more waves): partial sums of rows row0 + 2m + u, m < 4, in pr (the
-// reduce4x2 layout), from the shared SwiGLU row staged in LDS at hsl.
+// reduce4x2 layout), from the token's shared SwiGLU row sh_h, read from
+// global memory by each lane (64 values) ahead of its weights.
 // Defined with the shared-expert kernels (ffn_shared.hip).
 __device__ void shared_down_slot(const float4* sh_h, const uint8_t* sh_down, int row0, int lane,
                                  float* pr);
@@ -413,7 +417,8 @@ __device__ inline float reduce4x2(const float* v) {
 }
 
 // SH: a Q8_0 shared expert rides along as a seventh slot (waves 12 and 13,
-// its SwiGLU row sh_h staged with the routed ones), added unscaled.
+// reading its SwiGLU row sh_h from global memory; only without STAGE),
+// added unscaled.
 template <bool SH, bool STAGE>
 __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
     const float* __restrict__ h, const uint8_t* __restrict__ down,
