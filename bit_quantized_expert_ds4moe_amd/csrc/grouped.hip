@@ -1674,7 +1674,7 @@ __global__ __launch_bounds__(256) void k_imatrix(ImxArgs a) {
 // before its x tile (binary16, staged in LDS with the swizzle of
 // k_grouped_gateup) is written, so the two loads overlap.
 __global__ __launch_bounds__(256) void k_grouped_gateup_q4k(GroupArgs a) {
-  __shared__ uint4 xt[kMC * 16];
+  __shared__ uint4 xt[2][kMC * 16];  // x of stages s (read) and s + 1 (written)
   __shared__ int tok[kMC];
   const int item = grid_item(a);
   if (item >= *a.n_items) return;
@@ -1686,7 +1686,7 @@ __global__ __launch_bounds__(256) void k_grouped_gateup_q4k(GroupArgs a) {
   uint32_t xe[4];  // the rows' x exponents, for the epilogue (requested first)
   load_row_xexp<4>(a, row0, q, xe);
   const int n = n0 + 16 * w + (lane & 15);
-  const int nb = a.H / 256;
+  const int nb = a.H / 256, nst = 2 * nb;
   if (tid < kMC) tok[tid] = tid < nrows ? row_token(a, row0 + tid) : -1;
   const size_t rowg = (size_t)e * a.I + n;
   const uint8_t* G = a.gate + rowg * nb * kQ4kBytes;
@@ -1695,36 +1695,65 @@ __global__ __launch_bounds__(256) void k_grouped_gateup_q4k(GroupArgs a) {
   f32x4_t accg[4], accu[4];
   for (int mt = 0; mt < 4; mt++) accg[mt] = accu[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const f16x8_t ones = __builtin_bit_cast(f16x8_t, make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
-  __syncthreads();
-  for (int kh = 0; kh < 2 * nb; kh++) {
+  // A stage is half a block (128 columns): the block header (d, dmin, scales)
+  // and the lane's two code chunks, for gate and up.  Stage s + 1's weights
+  // and x are requested while stage s is multiplied; x alternates between
+  // the two LDS buffers, one barrier per stage.
+  struct Q4kW {
+    uint4 hg, hu;
+    uint2 cg[2], cu[2];
+  };
+  auto wload = [&](int kh, Q4kW& W) {
     const int kb = kh >> 1, hf = kh & 1;
     const uint8_t* bg = G + kb * kQ4kBytes;
     const uint8_t* bu = U + kb * kQ4kBytes;
-    const uint4 hg = *(const uint4*)bg, hu = *(const uint4*)bu;
-    uint2 cg[2], cu[2];
+    W.hg = *(const uint4*)bg;
+    W.hu = *(const uint4*)bu;
 #pragma unroll
     for (int c = 0; c < 2; c++) {  // code chunk 2hf + c: groups 4hf + 2c (low), + 1 (high)
-      cg[c] = *(const uint2*)(bg + 16 + 32 * (2 * hf + c) + 8 * q);
-      cu[c] = *(const uint2*)(bu + 16 + 32 * (2 * hf + c) + 8 * q);
+      W.cg[c] = *(const uint2*)(bg + 16 + 32 * (2 * hf + c) + 8 * q);
+      W.cu[c] = *(const uint2*)(bu + 16 + 32 * (2 * hf + c) + 8 * q);
     }
-    for (int c = tid; c < kMC * 16; c += 256) {
-      const int m = c >> 4, ch = c & 15;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < nrows) v = ((const uint4*)(a.x16 + (size_t)tok[m] * a.H + 128 * kh))[ch];
-      xt[m * 16 + (ch ^ (m & 15))] = v;
+  };
+  // x chunk c = tid + 256 i (i < 4): row c >> 4, 16-byte column chunk c & 15;
+  // rows past the item load nothing and store zeros
+  auto xload = [&](int kh, uint4 (&xv)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int c = tid + 256 * i, m = c >> 4, ch = c & 15;
+      xv[i] = m < nrows ? ((const uint4*)(a.x16 + (size_t)tok[m] * a.H + 128 * kh))[ch]
+                        : make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
-    const float dg = f16_bits_to_f32(hg.x & 0xFFFFu), mg = f16_bits_to_f32(hg.x >> 16);
-    const float du = f16_bits_to_f32(hu.x & 0xFFFFu), mu = f16_bits_to_f32(hu.x >> 16);
+  };
+  auto xstore = [&](int buf, const uint4 (&xv)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int c = tid + 256 * i, m = c >> 4, ch = c & 15;
+      xt[buf][m * 16 + (ch ^ (m & 15))] = xv[i];
+    }
+  };
+  // stage kh = 2 kb + HF (HF a constant, so the sub-block of every scale and
+  // min is known at compile time); Wc holds its weights, Wn receives the next
+  auto stage = [&](int kh, auto HFc, const Q4kW& Wc, Q4kW& Wn) {
+    constexpr int hf = decltype(HFc)::value;
+    const bool more = kh + 1 < nst;
+    uint4 xn[4];
+    if (more) {
+      xload(kh + 1, xn);
+      wload(kh + 1, Wn);
+    }
+    const uint4* xb = xt[hf];
+    const float dg = f16_bits_to_f32(Wc.hg.x & 0xFFFFu), mg = f16_bits_to_f32(Wc.hg.x >> 16);
+    const float du = f16_bits_to_f32(Wc.hu.x & 0xFFFFu), mu = f16_bits_to_f32(Wc.hu.x >> 16);
 #pragma unroll
     for (int c = 0; c < 2; c++) {
-      const uint4 pg = q4k_pairs(cg[c]), pu = q4k_pairs(cu[c]);
+      const uint4 pg = q4k_pairs(Wc.cg[c]), pu = q4k_pairs(Wc.cu[c]);
 #pragma unroll
       for (int hi = 0; hi < 2; hi++) {
         const int gi = 2 * c + hi, j = 4 * hf + gi;
         int scg, mng, scu, mnu;
-        q4k_scale_min(hg, j, scg, mng);
-        q4k_scale_min(hu, j, scu, mnu);
+        q4k_scale_min(Wc.hg, j, scg, mng);
+        q4k_scale_min(Wc.hu, j, scu, mnu);
         const float unit = hi ? 1048576.0f : 16777216.0f;  // 2^24 / 16^hi
         const float sgm = dg * (float)scg * unit, sgn = mg * (float)mng;
         const float sum = du * (float)scu * unit, sun = mu * (float)mnu;
@@ -1733,7 +1762,7 @@ __global__ __launch_bounds__(256) void k_grouped_gateup_q4k(GroupArgs a) {
         for (int mt = 0; mt < 4; mt++) {
           if (mt >= mtiles) break;
           const int m = 16 * mt + (lane & 15);
-          const f16x8_t af = __builtin_bit_cast(f16x8_t, xt[m * 16 + ((4 * gi + q) ^ (m & 15))]);
+          const f16x8_t af = __builtin_bit_cast(f16x8_t, xb[m * 16 + ((4 * gi + q) ^ (m & 15))]);
           const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
           const f32x4_t tg = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fg, z, 0, 0, 0);
           const f32x4_t tu = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, fu, z, 0, 0, 0);
@@ -1743,9 +1772,23 @@ __global__ __launch_bounds__(256) void k_grouped_gateup_q4k(GroupArgs a) {
         }
       }
     }
+    if (more) xstore(hf ^ 1, xn);
     __syncthreads();
+  };
+  Q4kW WA, WB;
+  wload(0, WA);
+  __syncthreads();  // tok
+  {
+    uint4 xv[4];
+    xload(0, xv);
+    xstore(0, xv);
   }
-  swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu, n0, kNT, xe, (uint32_t*)xt);
+  __syncthreads();
+  for (int kh = 0; kh < nst; kh += 2) {  // nst is even
+    stage(kh, std::integral_constant<int, 0>{}, WA, WB);
+    stage(kh + 1, std::integral_constant<int, 1>{}, WB, WA);
+  }
+  swiglu_store(a, row0, nrows, mtiles, n, q, accg, accu, n0, kNT, xe, (uint32_t*)xt[0]);
 }
 
 // The grouped kernels need bf16 x, 256-multiple shapes and formats they know
