@@ -808,7 +808,22 @@ def with_single_thread(fn, args_all, args_one):
         oracle.set_threads(n)
     res["single_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1,
                             "sample": one["sample"]}
+    res["host"] = host_cpu()
     return res
+
+
+def host_cpu():
+    """The host's CPU model and logical CPU count (the oracle's machine)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cpus": os.cpu_count()}
 
 
 def cpu_baseline_encode(n_rows):
