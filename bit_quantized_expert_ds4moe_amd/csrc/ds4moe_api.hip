@@ -37,6 +37,9 @@ constexpr int kFuseSelMaxTokens = 4;  // layer calls: selection fused into gate/
 constexpr int kDnStageMinTokens = 4;
 constexpr int kB1MaxTokens = 13;
 constexpr int kB1MaxTokensIq2 = 8;
+// Layer calls from this many tokens (selection kernel, no fused selection)
+// read each distinct IQ2_XXS expert once in gate/up (k_gateup_few).
+constexpr int kFewMinT = 2;
 constexpr int kSharedSplitG = 16;  // K shares of a shared expert's gate/up in calls of few tokens (<= kMaxSplit)
 constexpr int kSharedSplitD = 4;   // and of its down
 constexpr int kSharedSplitMaxT = 64;  // "few": one work item of shared rows
@@ -153,11 +156,29 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// Permutation and work-item arrays in the workspace (the grouped path's, also
+// built by the selection kernel for the few-token distinct-expert gate/up).
+struct PermPtrs {
+  int32_t *counts, *offsets, *perm, *inv, *items, *n_items;
+};
+PermPtrs perm_ptrs(const ds4moe_shape& s, int32_t T, void* ws, const Layout& L) {
+  const int E = s.n_expert, TK = T * s.top_k;
+  PermPtrs p;
+  p.counts = at<int32_t>(ws, L.perm);
+  p.offsets = p.counts + E;
+  p.perm = p.offsets + E + 1;
+  p.inv = p.perm + TK;
+  p.items = p.inv + TK;
+  p.n_items = p.items + 3 * max_items(E, TK, T, true);
+  return p;
+}
+
 // ---- routing ---------------------------------------------------------------
 ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void* x, int32_t x_dt,
                        const float* residual, const float* norm_w, float eps, uint16_t* xn_out,
                        int32_t T, const int32_t* tok, int32_t* ids, float* wts, void* ws,
-                       const Layout& L, hipStream_t st, bool select = true) {
+                       const Layout& L, hipStream_t st, bool select = true,
+                       bool few_items = false) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   ProfScope prof(DS4MOE_K_ROUTE, st);
   if (r.tid2eid) {
@@ -184,6 +205,13 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
   a.ids = ids;
   a.wts = wts;
   a.status = status;
+  if (few_items && T * s.top_k <= kSelItemsMax) {  // the selection kernel also lists the items
+    const PermPtrs pp = perm_ptrs(s, T, ws, L);
+    a.done = status + 16;  // inside the zero-initialised status region
+    a.perm = pp.perm;
+    a.items = pp.items;
+    a.n_items = pp.n_items;
+  }
   const bool vec = s.hidden % 2048 == 0 && s.hidden <= 4096 && r.w_dtype == DS4MOE_F16 &&
                    (norm_w || x_dt == DS4MOE_BF16) && ((uintptr_t)r.w % 16 == 0) &&
                    (norm_w ? ((uintptr_t)residual % 16 == 0 && (uintptr_t)norm_w % 16 == 0 &&
@@ -283,12 +311,32 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
                         int32_t T, const int32_t* ids_in, const float4* kbuf, int32_t* ids,
                         const float* wts, float* out, float* residual, void* ws, const Layout& L,
                         hipStream_t st, const SharedB1Args* shb = nullptr,
-                        const ds4moe_router* rt = nullptr) {
+                        const ds4moe_router* rt = nullptr, bool few_items = false) {
   // one weight read for all tokens, measured faster than the grouped Q8_0
   // kernels from 5 to 8 tokens (5: 98.9 vs 108.3 us per layer call, 8: equal)
   const bool sh_few = shb && T > kSharedB1MaxTokens && T <= kSharedFewMaxTokens;
   uint32_t* status = at<uint32_t>(ws, L.status);
   float* h = at<float>(ws, L.h);
+  // the selection kernel listed one work item per distinct expert: the
+  // IQ2_XXS gate/up reads each of them once for all its tokens
+  const bool few = few_items && !kbuf && ids_in && ex.gate_qtype == DS4MOE_IQ2_XXS &&
+                   ex.up_qtype == DS4MOE_IQ2_XXS;
+  if (few) {
+    const PermPtrs pp = perm_ptrs(s, T, ws, L);
+    GateUpFewArgs f{};
+    f.x = (const uint16_t*)x;
+    f.gate = (const uint8_t*)ex.gate;
+    f.up = (const uint8_t*)ex.up;
+    f.grid = ex.grid;
+    f.items = pp.items;
+    f.n_items = pp.n_items;
+    f.perm = pp.perm;
+    f.h = h;
+    const int TK = T * s.top_k;
+    ProfScope prof(DS4MOE_K_GATEUP, st);
+    launch_k(k_gateup_few, dim3(kI / kFewFeat, s.n_expert < TK ? s.n_expert : TK),
+             dim3(kFewWaves * 64), 0, st, f);
+  }
   GateUpB1Args g{};
   g.x = (const uint16_t*)x;
   g.gate = (const uint8_t*)ex.gate;
@@ -307,7 +355,7 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   g.E = s.n_expert;
   g.h = h;
   g.status = status;
-  {
+  if (!few) {
     ProfScope prof(DS4MOE_K_GATEUP, st);
     const bool q4 = ex.gate_qtype == DS4MOE_Q4_K;
     if (kbuf && q4)
@@ -429,7 +477,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
                      const void* x, int32_t x_dt, int32_t T, const int32_t* ids, const float* wts,
                      float* out, float* residual, int32_t* perm_dbg, void* ws, const Layout& L,
                      hipStream_t st, const ImxOut* imx = nullptr, const float4* kbuf_sel = nullptr,
-                     const ds4moe_router* rt = nullptr) {
+                     const ds4moe_router* rt = nullptr, bool few_items = false) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   const bool b1 = fast_b1(s, ex, x, x_dt, T) && (!sh || grouped_eligible(s, ex, sh, x, x_dt, T));
   if (b1) {
@@ -453,7 +501,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
         kbuf_sel ? launch_b1(s, ex, x, T, nullptr, kbuf_sel, const_cast<int32_t*>(ids), wts, out,
                              residual, ws, L, st, shb1 ? &sa : nullptr, rt)
                  : launch_b1(s, ex, x, T, ids, nullptr, nullptr, wts, out, residual, ws, L, st,
-                             shb1 ? &sa : nullptr);
+                             shb1 ? &sa : nullptr, nullptr, few_items);
     if (rc == DS4MOE_OK && perm_dbg)  // the few-token path needs no permutation: make it for the caller
       rc = permute_dbg(s, T, ids, perm_dbg, ws, L, st);
     // h: fp32 [T][6][I] by pair; the shared expert's rows below reuse its memory
@@ -811,15 +859,22 @@ ds4moe_status layer_run(const ds4moe_shape* shape, const ds4moe_layer_desc* desc
   const bool fuse = !r.tid2eid && n_tok <= kFuseSelMaxTokens &&
                     fast_b1(*shape, desc->routed, fx, fdt, n_tok) &&
                     (!sh || grouped_eligible(*shape, desc->routed, sh, fx, fdt, n_tok));
+  // selection kernel before the few-token matvecs: it also lists the
+  // distinct experts for the IQ2_XXS gate/up that reads each once
+  const bool few_items = !fuse && !r.tid2eid && n_tok >= kFewMinT &&
+                         n_tok * shape->top_k <= kSelItemsMax &&
+                         desc->routed.gate_qtype == DS4MOE_IQ2_XXS &&
+                         fast_b1(*shape, desc->routed, fx, fdt, n_tok) &&
+                         (!sh || grouped_eligible(*shape, desc->routed, sh, fx, fdt, n_tok));
   rc = do_route(*shape, r, x, x_dtype, norm ? residual : nullptr, norm ? desc->norm_w : nullptr,
                 desc->norm_eps, norm ? xn : nullptr, n_tok, token_ids, ids, wts, ws, L, stream,
-                !fuse);
+                !fuse, few_items);
   if (rc != DS4MOE_OK) return rc;
   // the fused selection reads the router input fx (the normalised row when
   // norm: the scoring wrote it to the workspace) for exact recomputations
   rc = do_ffn(*shape, desc->routed, sh, fx, fdt, n_tok, ids, wts, norm ? nullptr : out,
               norm ? residual : nullptr, nullptr, ws, L, stream, nullptr,
-              fuse ? at<float4>(ws, L.kbuf) : nullptr, fuse ? &r : nullptr);
+              fuse ? at<float4>(ws, L.kbuf) : nullptr, fuse ? &r : nullptr, few_items);
   if (rc != DS4MOE_OK) return rc;
   if (ids_dbg &&
       hipMemcpyAsync(ids_dbg, ids, sizeof(int32_t) * n_tok * shape->top_k, hipMemcpyDeviceToDevice,

@@ -352,6 +352,175 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
   }
 }
 
+// gate/up + SwiGLU for a few tokens, each distinct routed expert read once.
+// Grid (kI / kFewFeat, items): work item u is one expert e and the nrows
+// (at most 16) sorted pairs that chose it, rows row0 .. row0 + nrows - 1 of
+// the permutation (pair p = perm[row] = 6t + k).  Wave w of workgroup b
+// takes features f0 = kFewFeat b + 2w and f0 + 1 of expert e, gate and up:
+// it requests those four rows before anything else (lane layout of the
+// batch-1 kernel: 64 columns per lane), then decodes each 8-value group once
+// and multiplies it with the x of every token of the item, kFewTok tokens
+// per pass.  The pass's x sits in LDS, 16-byte chunk c of a token at
+// c + (c >> 4) (one spare chunk per 16): lane l reads chunks 8l + i (i < 8),
+// at 8l + (l >> 1) + i, so the 16 lanes one read serves hit 16 distinct bank
+// groups and every address is the lane's base plus an immediate.  The pairs are
+// read through the scalar cache, so no wait for them queues behind weights.
+// Output: h[p][f] = SiLU(gate) * up in fp32, the batch-1 layout [T][6][kI].
+constexpr int kFewWaves = 16;
+constexpr int kFewFeat = 2 * kFewWaves;  // features per workgroup
+constexpr int kFewTok = 4;               // tokens per pass
+constexpr int kXsTok = kH / 8;           // 16-byte chunks of one token's x
+constexpr int kXsStride = kXsTok + kXsTok / 16;  // and their LDS slots
+
+struct GateUpFewArgs {
+  const uint16_t* x;       // [T][4096] bf16
+  const uint8_t* gate;     // [E][2048][1056 B]
+  const uint8_t* up;
+  const uint8_t* grid;     // [256][8]
+  const int32_t* items;    // [n][3]: expert, first sorted row, rows (one item per expert)
+  const int32_t* n_items;  // n_items[0]: the number of items
+  const int32_t* perm;     // sorted row -> pair 6t + k
+  float* h;                // [T*6][2048] by pair
+};
+
+// iq2_dot16 for the x of tokens 0 .. nt-1 (xl: the lane's first slot in
+// the pass's x, kXsStride slots per token): acc[j] = the lane's partial dot
+// product of its 64 columns of the row with token j's x.
+template <int NT>
+__device__ __attribute__((always_inline)) inline void iq2_dot16_multi(const Iq2Seg& sg, uint32_t sh, const uint4* xl,
+                                       const uint8_t* gtab, const uint8_t* stab, uint32_t rep16,
+                                       int nt, float (&acc)[NT]) {
+  const float d = f16_bits_to_f32(sh ? (sg.dw & 0xFFFFu) : (sg.dw >> 16));
+  uint32_t g[4];
+  g[0] = align_bytes(sg.w1, sg.w0, sh);
+  g[1] = align_bytes(sg.w2, sg.w1, sh);
+  g[2] = align_bytes(sg.w3, sg.w2, sh);
+  g[3] = align_bytes(sg.w4, sg.w3, sh);
+  float a2[NT];
+#pragma unroll
+  for (int j = 0; j < NT; j++) a2[j] = 0.0f;
+#pragma unroll
+  for (int grp = 0; grp < 2; grp++) {
+    const uint32_t idxw = g[2 * grp], sw = g[2 * grp + 1];
+    uint4 gv[4], mv[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+      const uint32_t ga = vperm(idxw, rep16, 0x0C0C0000u | ((4u + kk) << 8));
+      const uint32_t sa = (((sw >> (7 * kk)) & 0x7Fu) << 8) | rep16;
+      gv[kk] = *(const uint4*)(gtab + ga);
+      mv[kk] = *(const uint4*)(stab + sa);
+    }
+    // the group's 32 values as bf16 pairs, decoded once for every token
+    uint32_t wv[16];
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++) {
+      wv[4 * kk] = gv[kk].x ^ mv[kk].x;
+      wv[4 * kk + 1] = gv[kk].y ^ mv[kk].y;
+      wv[4 * kk + 2] = gv[kk].z ^ mv[kk].z;
+      wv[4 * kk + 3] = gv[kk].w ^ mv[kk].w;
+    }
+    const float sc = (float)(((sw & 0xF0000000u) | 0x08000000u) >> 24);  // 16s + 8
+#pragma unroll
+    for (int j = 0; j < NT; j++) {
+      if (j < nt) {  // wave-uniform
+        float ga0 = 0.0f, ga1 = 0.0f;  // two chains
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+          const uint4 xv = xl[j * kXsStride + 4 * grp + kk];
+          float& ac = (kk & 1) ? ga1 : ga0;
+          ac = dot2_bf16(wv[4 * kk], xv.x, ac);
+          ac = dot2_bf16(wv[4 * kk + 1], xv.y, ac);
+          ac = dot2_bf16(wv[4 * kk + 2], xv.z, ac);
+          ac = dot2_bf16(wv[4 * kk + 3], xv.w, ac);
+        }
+        a2[j] = fmaf(sc, ga0 + ga1, a2[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NT; j++) acc[j] = a2[j] * (d * 0.015625f);
+}
+
+__global__ __launch_bounds__(kFewWaves * 64) void k_gateup_few(GateUpFewArgs a) {
+  __shared__ uint4 lds4[(kSignTab + kGridTab) / 16 + kFewTok * kXsStride];
+  uint8_t* stab = (uint8_t*)lds4;                  // 32 KB
+  uint8_t* gtab = stab + kSignTab;                 // 64 KB
+  uint4* xs = lds4 + (kSignTab + kGridTab) / 16;  // 34 KB
+  const int item = (int)blockIdx.y;
+  if (item >= a.n_items[0]) return;
+  const int e = load_scalar_i32(a.items, 3 * item);
+  const int row0 = load_scalar_i32(a.items, 3 * item + 1);
+  const int nrows = load_scalar_i32(a.items, 3 * item + 2);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int f0 = blockIdx.x * kFewFeat + 2 * w;
+  // grid bytes (table build), then the wave's four rows
+  uint2 gb = make_uint2(0, 0);
+  if (tid < 256) gb = *(const uint2*)(a.grid + 8 * tid);
+  const Iq2Off off = iq2_offsets(lane);
+  Iq2Seg sg[2], su[2];
+#pragma unroll
+  for (int r = 0; r < 2; r++) {
+    const size_t rowi = (size_t)e * kI + f0 + r;
+    iq2_load((const uint32_t*)(a.gate + rowi * kRowIq2), 0, off, sg[r]);
+    iq2_load((const uint32_t*)(a.up + rowi * kRowIq2), 0, off, su[r]);
+  }
+  if (tid < 256) store_copies(gtab, tid, grid_pairs(gb));
+  else if (tid < 384) store_copies(stab, tid - 256, sign_masks(tid - 256));
+  const uint32_t sh = ((lane >> 2) & 1) ? 0u : 2u;
+  const uint32_t rep16 = (uint32_t)(lane & 15) << 4;
+  const uint4* xl = xs + 8 * lane + (lane >> 1);  // chunk 8 lane
+  for (int j0 = 0; j0 < nrows; j0 += kFewTok) {
+    const int nt = min(kFewTok, nrows - j0);
+    // an empty asm that "changes" the weight words, so that the decode's
+    // table addresses (functions of them alone) are not hoisted out of the
+    // pass loop: kept live across it they would not fit the registers
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+      asm volatile("" : "+v"(sg[r].w0), "+v"(sg[r].w1), "+v"(sg[r].w2), "+v"(sg[r].w3),
+                   "+v"(sg[r].w4), "+v"(sg[r].dw));
+      asm volatile("" : "+v"(su[r].w0), "+v"(su[r].w1), "+v"(su[r].w2), "+v"(su[r].w3),
+                   "+v"(su[r].w4), "+v"(su[r].dw));
+    }
+    if (j0 > 0) __syncthreads();  // every wave is done with the last pass's x
+    // x of the pass's tokens: chunk q = tid + 1024 i of the kFewTok tokens'
+    // chunks, token jj = q / kXsTok (wave-uniform)
+#pragma unroll
+    for (int i = 0; i < kFewTok * kXsTok / (kFewWaves * 64); i++) {
+      const int q = tid + kFewWaves * 64 * i, jj = q / kXsTok, c = q % kXsTok;
+      if (jj < nt) {
+        const int tok = load_scalar_i32(a.perm, row0 + j0 + jj) / 6;
+        xs[jj * kXsStride + c + (c >> 4)] = ((const uint4*)(a.x + (size_t)tok * kH))[c];
+      }
+    }
+    __syncthreads();
+    float acc[4][kFewTok];  // rows: gate f0, gate f0+1, up f0, up f0+1
+    iq2_dot16_multi<kFewTok>(sg[0], sh, xl, gtab, stab, rep16, nt, acc[0]);
+    iq2_dot16_multi<kFewTok>(sg[1], sh, xl, gtab, stab, rep16, nt, acc[1]);
+    iq2_dot16_multi<kFewTok>(su[0], sh, xl, gtab, stab, rep16, nt, acc[2]);
+    iq2_dot16_multi<kFewTok>(su[1], sh, xl, gtab, stab, rep16, nt, acc[3]);
+    // two tokens per reduction: v = gate (f0, j), (f0+1, j), (f0, j+1),
+    // (f0+1, j+1), then the same four up totals; lane 16 rho holds the gate
+    // total of v[c[rho]] (c = {0, 2, 1, 3}), its up total 8 lanes further on
+#pragma unroll
+    for (int jp = 0; jp < kFewTok; jp += 2) {
+      if (jp >= nt) continue;
+      float v[8] = {acc[0][jp], acc[1][jp], acc[0][jp + 1], acc[1][jp + 1],
+                    acc[2][jp], acc[3][jp], acc[2][jp + 1], acc[3][jp + 1]};
+      if (jp + 1 >= nt) v[2] = v[3] = v[6] = v[7] = 0.0f;
+      const float tot = reduce8(v);
+      const float upv = dpp_f32<0x128>(tot);
+      const int rho = lane >> 4;
+      const int ci = (rho == 1) ? 2 : (rho == 2) ? 1 : rho;
+      const int jj = jp + (ci >> 1);
+      if ((lane & 15) == 0 && jj < nt) {
+        const int pair = a.perm[row0 + j0 + jj];
+        a.h[(size_t)pair * kI + f0 + (ci & 1)] = silu(tot) * upv;
+      }
+    }
+  }
+}
+
 // down + weighted combine (+ residual) for one token.
 // Grid (H / kDnBlockRows, T), 12 waves: wave w handles routed slot k = w / 2
 // for kDnRows rows (w odd: the second half of the workgroup's 16 rows), two

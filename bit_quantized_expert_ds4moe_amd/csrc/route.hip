@@ -45,7 +45,16 @@ struct RouteArgs {
   int32_t* ids;           // [T][K]
   float* wts;             // [T][K]
   uint32_t* status;
+  // Few-token layer calls (T*K <= kSelItemsMax; nullable: not built): the
+  // last selecting workgroup also sorts the pairs p = tK + k by (expert, p)
+  // and lists one work item per expert, as the grouped path's permutation
+  // and item list do.
+  uint32_t* done;         // arrival counter, zero between calls
+  int32_t* perm;          // [T*K] sorted position -> pair
+  int32_t* items;         // [n][3]: expert, first sorted position, pairs
+  int32_t* n_items;       // [2]: items, items of at most 16 pairs
 };
+constexpr int kSelItemsMax = 128;
 
 __device__ inline double load_x64(const RouteArgs& a, int t, int c, double nscale) {
   if (a.norm_w) {
@@ -549,6 +558,56 @@ __global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
   if (lane < a.K) {
     a.ids[(size_t)t * a.K + lane] = e;
     a.wts[(size_t)t * a.K + lane] = w;
+  }
+  if (!a.items) return;
+  // the workgroup's ids visible device-wide before it counts itself in; the
+  // last one to arrive (after the matching acquire) sees every token's ids
+  __threadfence();
+  uint32_t old = 0;
+  if (lane == 0) old = atomicAdd(a.done, 1u);
+  old = (uint32_t)__shfl((int)old, 0);
+  if (old != (uint32_t)gridDim.x - 1) return;
+  __threadfence();
+  __shared__ int s_e[kSelItemsMax], s_sorted[kSelItemsMax];
+  const int n = a.T * a.K;
+  for (int p = lane; p < n; p += 64) s_e[p] = __hip_atomic_load(a.ids + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  // rank of pair p in the order (expert, p)
+  for (int p = lane; p < n; p += 64) {
+    const int ep = s_e[p];
+    int r = 0;
+    for (int q = 0; q < n; q++) r += (s_e[q] < ep || (s_e[q] == ep && q < p)) ? 1 : 0;
+    a.perm[r] = p;
+    s_sorted[r] = ep;
+  }
+  __syncthreads();
+  // an item starts wherever the expert changes; its index counts the starts before it
+  bool st[kSelItemsMax / 64];
+  uint64_t m[kSelItemsMax / 64];
+#pragma unroll
+  for (int h = 0; h < kSelItemsMax / 64; h++) {
+    const int i = 64 * h + lane;
+    st[h] = i < n && (i == 0 || s_sorted[i] != s_sorted[i - 1]);
+    m[h] = __ballot(st[h]);
+  }
+  int before = 0;
+#pragma unroll
+  for (int h = 0; h < kSelItemsMax / 64; h++) {
+    const int i = 64 * h + lane;
+    const int u = before + __popcll(m[h] & ((1ull << lane) - 1ull));
+    if (st[h]) {
+      int c = 1;
+      while (i + c < n && s_sorted[i + c] == s_sorted[i]) c++;
+      a.items[3 * u] = s_sorted[i];
+      a.items[3 * u + 1] = i;
+      a.items[3 * u + 2] = c;
+    }
+    before += __popcll(m[h]);
+  }
+  if (lane == 0) {
+    a.n_items[0] = before;
+    a.n_items[1] = before;
+    *a.done = 0u;  // ready for the next call
   }
 }
 
