@@ -141,21 +141,43 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_b1(SharedB1Args a) {
 }
 
 // The same two matvecs for a few tokens at once: grid row y takes tokens
-// kShFewTok y .. +kShFewTok-1 (of T); every wave requests its weight rows
-// once, the workgroup then stages those tokens' activations in LDS (16-byte
-// chunk c of a token at c + (c >> 4), one spare chunk per 16, so that the 16
-// lanes one read serves hit 16 distinct bank groups) and the wave runs
-// through the tokens.
-constexpr int kShFewTok = 4;
-constexpr int kShXc = kH / 8;                  // 16-byte chunks of a token's x (bf16)
-constexpr int kShXs = kShXc + kShXc / 16;      // and its LDS slots
-constexpr int kShHc = kI / 4;                  // 16-byte chunks of a token's h (fp32)
-constexpr int kShHs = kShHc + kShHc / 16;
+// kShFewTok y .. +kShFewTok-1 (of T).  Every wave requests its weight rows
+// once; then wave w turns token w's activations into the lanes' 16-bit
+// fixed-point form (q4k_fix: the same for every wave, since lane L covers
+// the same 64 columns in each) and leaves it in LDS, and every wave runs
+// through the tokens' dot products from there.  A lane's record is 36 words
+// (xl[16], xh[16], sl, sh, S, one spare): at that stride the 16 lanes one
+// 16-byte read serves hit 16 distinct bank groups.
+constexpr int kShFewTok = 4;   // tokens per grid row: one per wave
+constexpr int kShFx = 36;      // words of a lane's fixed-point record
+
+__device__ inline void fx_store(uint32_t* r, const uint32_t* xl, const uint32_t* xh, int sl, int sh,
+                                float S) {
+#pragma unroll
+  for (int q = 0; q < 16; q += 4) {
+    *(uint4*)(r + q) = make_uint4(xl[q], xl[q + 1], xl[q + 2], xl[q + 3]);
+    *(uint4*)(r + 16 + q) = make_uint4(xh[q], xh[q + 1], xh[q + 2], xh[q + 3]);
+  }
+  *(uint4*)(r + 32) = make_uint4((uint32_t)sl, (uint32_t)sh, __float_as_uint(S), 0u);
+}
+
+__device__ inline float fx_load(const uint32_t* r, uint32_t* xl, uint32_t* xh, int& sl, int& sh) {
+#pragma unroll
+  for (int q = 0; q < 16; q += 4) {
+    const uint4 a = *(const uint4*)(r + q), b = *(const uint4*)(r + 16 + q);
+    xl[q] = a.x; xl[q + 1] = a.y; xl[q + 2] = a.z; xl[q + 3] = a.w;
+    xh[q] = b.x; xh[q + 1] = b.y; xh[q + 2] = b.z; xh[q + 3] = b.w;
+  }
+  const uint4 c = *(const uint4*)(r + 32);
+  sl = (int)c.x;
+  sh = (int)c.y;
+  return __uint_as_float(c.z);
+}
 
 // gate/up: grid (2048 / 8, rows of kShFewTok tokens), 256 threads, rows as in
 // k_shared_gateup_q80_b1.
 __global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, int T) {
-  __shared__ uint4 xs[kShFewTok * kShXs];
+  __shared__ uint32_t fx[kShFewTok * 64 * kShFx];
   const int t0 = kShFewTok * blockIdx.y, nt = min(kShFewTok, T - t0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -166,16 +188,11 @@ __global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, i
     const uint8_t* base = (r < 2 ? a.gate : a.up) + (size_t)(f0 + (r & 1)) * kShRowGu;
     q80_pair_load(base + 68 * lane, D[r]);
   }
-  for (int c = tid; c < nt * kShXc; c += 256) {
-    const int t = c / kShXc, k = c % kShXc;
-    xs[t * kShXs + k + (k >> 4)] = ((const uint4*)(a.x + (size_t)(t0 + t) * kH))[k];
-  }
-  __syncthreads();
-  const uint4* xl0 = xs + 8 * lane + (lane >> 1);  // chunk 8 lane
-  for (int t = 0; t < nt; t++) {
+  if (w < nt) {  // wave w converts token t0 + w
+    const uint4* xp = (const uint4*)(a.x + (size_t)(t0 + w) * kH + 64 * lane);
     uint4 xq[8];
 #pragma unroll
-    for (int q = 0; q < 8; q++) xq[q] = xl0[t * kShXs + q];
+    for (int q = 0; q < 8; q++) xq[q] = xp[q];
     auto xval = [&](int i) {
       const uint4 q = xq[i >> 3];
       const uint32_t ww = (i & 6) == 0 ? q.x : (i & 6) == 2 ? q.y : (i & 6) == 4 ? q.z : q.w;
@@ -184,6 +201,13 @@ __global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, i
     uint32_t xl[16], xh[16];
     int sl, sh;
     const float S = q4k_fix(xval, xl, xh, sl, sh);
+    fx_store(fx + (w * 64 + lane) * kShFx, xl, xh, sl, sh, S);
+  }
+  __syncthreads();
+  for (int t = 0; t < nt; t++) {
+    uint32_t xl[16], xh[16];
+    int sl, sh;
+    const float S = fx_load(fx + (t * 64 + lane) * kShFx, xl, xh, sl, sh);
     float v[4];
 #pragma unroll
     for (int r = 0; r < 4; r++) v[r] = wave_sum(S * q80_dot64(D[r], xl, xh, sl, sh));
@@ -194,10 +218,11 @@ __global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, i
   }
 }
 
-// down: grid (4096 / 16, rows of kShFewTok tokens), 256 threads, rows as in k_shared_down_q80_b1;
-// out[t] (or the residual) += the shared output.
+// down: grid (4096 / 16, rows of kShFewTok tokens), 256 threads, rows as in
+// k_shared_down_q80_b1 (both wave halves cover the same 64 columns per lane,
+// so the lower half converts); out[t] (or the residual) += the shared output.
 __global__ __launch_bounds__(256) void k_shared_down_q80_few(SharedB1Args a, int T) {
-  __shared__ float4 hs[kShFewTok * kShHs];
+  __shared__ uint32_t fx[kShFewTok * 32 * kShFx];
   const int t0 = kShFewTok * blockIdx.y, nt = min(kShFewTok, T - t0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -206,19 +231,11 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_few(SharedB1Args a, int
   uint32_t D0[17], D1[17];
   q80_pair_load(a.down + (size_t)(r0 + u) * kShRowDn + 68 * L, D0);
   q80_pair_load(a.down + (size_t)(r0 + 2 + u) * kShRowDn + 68 * L, D1);
-  for (int c = tid; c < nt * kShHc; c += 256) {
-    const int t = c / kShHc, k = c % kShHc;
-    hs[t * kShHs + k + (k >> 4)] = ((const float4*)(a.h + (size_t)(t0 + t) * kI))[k];
-  }
-  __syncthreads();
-  const float4* hl0 = hs + 16 * L + L;  // chunk 16 L
-  auto rl = [](float x, int l) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
-  };
-  for (int t = 0; t < nt; t++) {
+  if (w < nt) {  // wave w converts token t0 + w
+    const float4* hp = (const float4*)(a.h + (size_t)(t0 + w) * kI + 64 * L);
     float4 hv[16];
 #pragma unroll
-    for (int q = 0; q < 16; q++) hv[q] = hl0[t * kShHs + q];
+    for (int q = 0; q < 16; q++) hv[q] = hp[q];
     auto hval = [&](int i) {
       const float4 q = hv[i >> 2];
       return (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
@@ -226,6 +243,16 @@ __global__ __launch_bounds__(256) void k_shared_down_q80_few(SharedB1Args a, int
     uint32_t xl[16], xh[16];
     int sl, sh;
     const float S = q4k_fix(hval, xl, xh, sl, sh);
+    if (u == 0) fx_store(fx + (w * 32 + L) * kShFx, xl, xh, sl, sh, S);
+  }
+  __syncthreads();
+  auto rl = [](float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+  };
+  for (int t = 0; t < nt; t++) {
+    uint32_t xl[16], xh[16];
+    int sl, sh;
+    const float S = fx_load(fx + (t * 32 + L) * kShFx, xl, xh, sl, sh);
     float p0 = S * q80_dot64(D0, xl, xh, sl, sh), p1 = S * q80_dot64(D1, xl, xh, sl, sh);
     p0 += dpp_f32<0xB1>(p0);
     p0 += dpp_f32<0x4E>(p0);
