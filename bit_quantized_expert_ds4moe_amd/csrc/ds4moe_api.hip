@@ -23,20 +23,24 @@ using namespace ds4;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Few-token calls use the streaming matvec kernels: each token reads its six
-// experts, which beats the grouped kernels' one read per distinct expert up to
-// kB1MaxTokensIq2 tokens of correlated decode with IQ2_XXS gate/up and Q2_K
-// down (measured: 8 tokens 145 vs 149 us per call, 9 tokens 158 vs 151) and
-// up to kB1MaxTokens with the other fast-path formats (Q4_K, not re-measured).
-constexpr int kSharedB1MaxTokens = 4;  // shared expert by per-token matvecs up to here,
+// Few-token calls use the streaming matvec kernels (in layer calls with the
+// IQ2_XXS gate/up reading each distinct expert once, otherwise one grid row
+// per token), which beat the grouped kernels up to kB1MaxTokensIq2 tokens of
+// correlated decode with IQ2_XXS gate/up and Q2_K down (config-2 layer call,
+// us: 9 tokens 132 vs 152, 10 tokens 143 vs 155, 11 tokens equal) and up to
+// kB1MaxTokens with the other fast-path formats (Q4_K, not re-measured).
+constexpr int kSharedB1MaxTokens = 2;  // shared expert by per-token matvecs up to here,
 // then up to kSharedFewMaxTokens (on the matvec path) by matvecs that read its
-// weights once for every token; beyond, by the grouped kernels
-constexpr int kSharedFewMaxTokens = 8;
+// weights once for every token (3 tokens: 66.2 vs 67.3 us per layer call,
+// 4: 80.5 vs 83.4; 2: 50.6 vs 50.0); beyond, by the grouped kernels
+constexpr int kSharedFewMaxTokens = 10;
 constexpr int kFuseSelMaxTokens = 4;  // layer calls: selection fused into gate/up up to here
 // Above this many tokens the batch-1 down stages the SwiGLU vectors in LDS.
 constexpr int kDnStageMinTokens = 4;
 constexpr int kB1MaxTokens = 13;
-constexpr int kB1MaxTokensIq2 = 8;
+constexpr int kB1MaxTokensIq2 = 10;
+constexpr int kB1MaxTokensIq2Ids = 8;  // the same with caller-given ids (one grid row per token:
+// 8 tokens 145 vs 149 us per call, 9 tokens 158 vs 151)
 // Layer calls from this many tokens (selection kernel, no fused selection)
 // read each distinct IQ2_XXS expert once in gate/up (k_gateup_few).
 constexpr int kFewMinT = 2;
@@ -293,13 +297,14 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, con
 // the streaming matvec kernels, one grid row per token (the routed experts;
 // a shared expert then runs through the grouped path, split along K).
 bool fast_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const void* x, int32_t x_dt,
-             int32_t T) {
+             int32_t T, bool few_items = false) {
   // gate/up: both IQ2_XXS or both Q4_K; down: Q2_K or Q4_K
   const bool gu = (ex.gate_qtype == DS4MOE_IQ2_XXS && ex.up_qtype == DS4MOE_IQ2_XXS) ||
                   (ex.gate_qtype == DS4MOE_Q4_K && ex.up_qtype == DS4MOE_Q4_K);
   const bool dn = ex.down_qtype == DS4MOE_Q2_K || ex.down_qtype == DS4MOE_Q4_K;
   const bool iq2_q2k = ex.gate_qtype == DS4MOE_IQ2_XXS && ex.down_qtype == DS4MOE_Q2_K;
-  return T >= 1 && T <= (iq2_q2k ? kB1MaxTokensIq2 : kB1MaxTokens) && x_dt == DS4MOE_BF16 &&
+  const int tmax = iq2_q2k ? (few_items ? kB1MaxTokensIq2 : kB1MaxTokensIq2Ids) : kB1MaxTokens;
+  return T >= 1 && T <= tmax && x_dt == DS4MOE_BF16 &&
          s.hidden == kH && s.inter == kI && ex.inter == kI &&
          s.top_k == 6 && gu && dn && aligned(x, 16) && aligned(ex.gate, 16) &&
          aligned(ex.up, 16) && aligned(ex.down, 16) && aligned(ex.grid, 8);
@@ -312,8 +317,7 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
                         const float* wts, float* out, float* residual, void* ws, const Layout& L,
                         hipStream_t st, const SharedB1Args* shb = nullptr,
                         const ds4moe_router* rt = nullptr, bool few_items = false) {
-  // one weight read for all tokens, measured faster than the grouped Q8_0
-  // kernels from 5 to 8 tokens (5: 98.9 vs 108.3 us per layer call, 8: equal)
+  // one weight read for all tokens (kSharedB1MaxTokens < T <= kSharedFewMaxTokens)
   const bool sh_few = shb && T > kSharedB1MaxTokens && T <= kSharedFewMaxTokens;
   uint32_t* status = at<uint32_t>(ws, L.status);
   float* h = at<float>(ws, L.h);
@@ -479,7 +483,8 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
                      hipStream_t st, const ImxOut* imx = nullptr, const float4* kbuf_sel = nullptr,
                      const ds4moe_router* rt = nullptr, bool few_items = false) {
   uint32_t* status = at<uint32_t>(ws, L.status);
-  const bool b1 = fast_b1(s, ex, x, x_dt, T) && (!sh || grouped_eligible(s, ex, sh, x, x_dt, T));
+  const bool b1 = fast_b1(s, ex, x, x_dt, T, few_items && !kbuf_sel) &&
+                  (!sh || grouped_eligible(s, ex, sh, x, x_dt, T));
   if (b1) {
     // a Q8_0 shared expert runs inside launch_b1 as matvecs: per token up
     // to kSharedB1MaxTokens tokens, then one weight read for all tokens up to
@@ -864,7 +869,7 @@ ds4moe_status layer_run(const ds4moe_shape* shape, const ds4moe_layer_desc* desc
   const bool few_items = !fuse && !r.tid2eid && n_tok >= kFewMinT &&
                          n_tok * shape->top_k <= kSelItemsMax &&
                          desc->routed.gate_qtype == DS4MOE_IQ2_XXS &&
-                         fast_b1(*shape, desc->routed, fx, fdt, n_tok) &&
+                         fast_b1(*shape, desc->routed, fx, fdt, n_tok, true) &&
                          (!sh || grouped_eligible(*shape, desc->routed, sh, fx, fdt, n_tok));
   rc = do_route(*shape, r, x, x_dtype, norm ? residual : nullptr, norm ? desc->norm_w : nullptr,
                 desc->norm_eps, norm ? xn : nullptr, n_tok, token_ids, ids, wts, ws, L, stream,

@@ -160,7 +160,8 @@ ds4moe_status ds4moe_permute(const ds4moe_shape* shape, const int32_t* expert_id
  * x: [n_tok][hidden] BF16 or F32; out: fp32 [n_tok][hidden].  `shared` may
  * be NULL.  Accumulation is fp32: dot products of exact products (decode
  * paths with the V4-Flash shape and formats: up to 8 tokens with IQ2_XXS
- * gate/up and Q2_K down, up to 13 with Q4_K gate/up or down) or MFMAs on
+ * gate/up and Q2_K down (10 in ds4moe_layer calls, whose selection lists
+ * the distinct experts), up to 13 with Q4_K gate/up or down) or MFMAs on
  * exact binary16/bf16 operands
  * (grouped path, more tokens; gate/up IQ2_XXS, Q8_0 or both Q4_K, down Q2_K,
  * Q8_0 or Q4_K); other combinations run on scalar kernels.  The permutation
