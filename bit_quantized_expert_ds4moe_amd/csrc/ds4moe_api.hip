@@ -209,9 +209,9 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
   a.ids = ids;
   a.wts = wts;
   a.status = status;
-  if (few_items && T * s.top_k <= kSelItemsMax) {  // the selection kernel also lists the items
+  // the selection kernel also lists the items (one workgroup, a wave per token)
+  if (few_items && T * s.top_k <= kSelItemsMax && T <= 16) {
     const PermPtrs pp = perm_ptrs(s, T, ws, L);
-    a.done = status + 16;  // inside the zero-initialised status region
     a.perm = pp.perm;
     a.items = pp.items;
     a.n_items = pp.n_items;
@@ -232,7 +232,8 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
     launch_k(k_route_score<false, false>, grid, dim3(256), 0, st, a);
   ds4moe_status rc = launched();
   if (rc != DS4MOE_OK || !select) return rc;
-  launch_k(k_route_select, dim3(T), dim3(64), 0, st, a);
+  if (a.items) launch_k(k_route_select, dim3(1), dim3(64 * T), 0, st, a);
+  else launch_k(k_route_select, dim3(T), dim3(64), 0, st, a);
   return launched();
 }
 
@@ -867,7 +868,7 @@ ds4moe_status layer_run(const ds4moe_shape* shape, const ds4moe_layer_desc* desc
   // selection kernel before the few-token matvecs: it also lists the
   // distinct experts for the IQ2_XXS gate/up that reads each once
   const bool few_items = !fuse && !r.tid2eid && n_tok >= kFewMinT &&
-                         n_tok * shape->top_k <= kSelItemsMax &&
+                         n_tok * shape->top_k <= kSelItemsMax && n_tok <= 16 &&
                          desc->routed.gate_qtype == DS4MOE_IQ2_XXS &&
                          fast_b1(*shape, desc->routed, fx, fdt, n_tok, true) &&
                          (!sh || grouped_eligible(*shape, desc->routed, sh, fx, fdt, n_tok));

@@ -46,10 +46,9 @@ struct RouteArgs {
   float* wts;             // [T][K]
   uint32_t* status;
   // Few-token layer calls (T*K <= kSelItemsMax; nullable: not built): the
-  // last selecting workgroup also sorts the pairs p = tK + k by (expert, p)
-  // and lists one work item per expert, as the grouped path's permutation
-  // and item list do.
-  uint32_t* done;         // arrival counter, zero between calls
+  // selection runs as one workgroup, wave t selecting token t, which then
+  // also sorts the pairs p = tK + k by (expert, p) and lists one work item
+  // per expert, as the grouped path's permutation and item list do.
   int32_t* perm;          // [T*K] sorted position -> pair
   int32_t* items;         // [n][3]: expert, first sorted position, pairs
   int32_t* n_items;       // [2]: items, items of at most 16 pairs
@@ -537,8 +536,12 @@ __device__ inline void select_wave(const float4* kb, int E, int K, float scale, 
 // Selection kernel.  Grid T, one wave per token: reads the key intervals
 // written by k_route_score (visible at the kernel boundary), picks the top K
 // and writes ids and gates.
-__global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
-  const int t = blockIdx.x, lane = threadIdx.x;
+// Grid (T) of one wave each; with a.items one workgroup of T waves (wave t:
+// token t), whose ids meet in LDS for the item list.
+__global__ __launch_bounds__(1024) void k_route_select(RouteArgs a) {
+  __shared__ int s_e[kSelItemsMax], s_sorted[kSelItemsMax];
+  const int lane = threadIdx.x & 63;
+  const int t = a.items ? (int)(threadIdx.x >> 6) : (int)blockIdx.x;
   int e;
   float w;
   // the router input of token t: the normalised row when the scoring wrote it
@@ -558,22 +561,13 @@ __global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
   if (lane < a.K) {
     a.ids[(size_t)t * a.K + lane] = e;
     a.wts[(size_t)t * a.K + lane] = w;
+    if (a.items) s_e[t * a.K + lane] = e;
   }
   if (!a.items) return;
-  // the workgroup's ids visible device-wide before it counts itself in; the
-  // last one to arrive (after the matching acquire) sees every token's ids
-  __threadfence();
-  uint32_t old = 0;
-  if (lane == 0) old = atomicAdd(a.done, 1u);
-  old = (uint32_t)__shfl((int)old, 0);
-  if (old != (uint32_t)gridDim.x - 1) return;
-  __threadfence();
-  __shared__ int s_e[kSelItemsMax], s_sorted[kSelItemsMax];
-  const int n = a.T * a.K;
-  for (int p = lane; p < n; p += 64) s_e[p] = __hip_atomic_load(a.ids + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  // rank of pair p in the order (expert, p)
-  for (int p = lane; p < n; p += 64) {
+  const int n = a.T * a.K;
+  // rank of pair p in the order (expert, p), one thread per pair
+  for (int p = threadIdx.x; p < n; p += blockDim.x) {
     const int ep = s_e[p];
     int r = 0;
     for (int q = 0; q < n; q++) r += (s_e[q] < ep || (s_e[q] == ep && q < p)) ? 1 : 0;
@@ -581,6 +575,7 @@ __global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
     s_sorted[r] = ep;
   }
   __syncthreads();
+  if (threadIdx.x >= 64) return;
   // an item starts wherever the expert changes; its index counts the starts before it
   bool st[kSelItemsMax / 64];
   uint64_t m[kSelItemsMax / 64];
@@ -607,7 +602,6 @@ __global__ __launch_bounds__(64) void k_route_select(RouteArgs a) {
   if (lane == 0) {
     a.n_items[0] = before;
     a.n_items[1] = before;
-    *a.done = 0u;  // ready for the next call
   }
 }
 
