@@ -385,6 +385,42 @@ def test_layer_route_and_ffn(widx):
     assert err <= TOL_FP32
 
 
+@pytest.mark.parametrize("T", [9, 10])
+def test_layer_identical_tokens(T):
+    # config 2's layer with every token equal: all T tokens pick the same six
+    # experts, so each distinct-expert item holds T pairs (the gate/up passes
+    # of 4, 4 and 1 or 2 tokens) and the shared expert runs three grid rows
+    from ds4gen.device import make_layer, host_experts, host_shared
+    from dataclasses import replace
+    w = replace(g.WORKLOADS[2], T=T)
+    say("layer, identical tokens, T", T)
+    lt = make_layer(w, 0)
+    x = np.repeat(g.activations(w, n_tok=1), T, axis=0)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, T)
+    d = ds4.layer_desc(ds4.router(w=ptr(lt.router_w), w_dtype=ds4.F16, bias=ptr(lt.bias)),
+                       experts_of(lt, w), shared=shared_of(lt, w))
+    out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, w.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, w.K), dtype=torch.float32, device="cuda")
+    xd = dev(x)
+    ds4.layer(shp, d, ptr(xd), ds4.BF16, None, ptr(out), None, T, ptr(ids), ptr(wts), None,
+              ptr(ws), nb, stream())
+    check_clean(ws)
+    oids, owts, _, _ = oracle.route(x, "bf16", g.router_weight(w, 0), "f16", g.router_bias(w, 0), w.K)
+    assert np.unique(oids).size == w.K
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    want = oracle.moe_ffn(x[:1], "bf16", oids[:1], owts[:1], host_experts(w, 0, np.unique(oids)),
+                          (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed),
+                          shared=host_shared(w, 0), sh_I=w.I)
+    got = out.cpu().numpy()
+    for t in range(T):
+        err = max_rel_err(got[t:t + 1], want)
+        assert err <= TOL_FP32, (t, err)
+    # every token's row is computed from the same values in the same order
+    assert (got == got[:1]).all()
+
+
 @pytest.mark.parametrize("widx", [1, "q4k-t3", "b8-t2"])
 def test_ffn_nonfinite_activation_propagates(widx):
     # a NaN (token 1) or an infinity (token 2) in x makes that token's whole
