@@ -149,9 +149,12 @@ void launch_k(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shm, hipStre
 
 inline ds4moe_status launch_permute(const int32_t* ids, int n, int E, int32_t* counts,
                                     int32_t* offsets, int32_t* perm, int32_t* inv,
-                                    uint32_t* status, hipStream_t st) {
+                                    uint32_t* status, hipStream_t st, int T = 0,
+                                    int with_shared = 0, int32_t* items = nullptr,
+                                    int32_t* n_items = nullptr) {
   if (n > kPermMax) return DS4MOE_EUNSUPPORTED;
-  launch_k(k_permute, dim3(1), dim3(1024), 0, st, ids, n, E, counts, offsets, perm, inv, status);
+  launch_k(k_permute, dim3(1), dim3(1024), 0, st, ids, n, E, counts, offsets, perm, inv, status,
+           T, with_shared, items, n_items);
   return hipGetLastError() == hipSuccess ? DS4MOE_OK : DS4MOE_EDEVICE;
 }
 
@@ -535,10 +538,9 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       if (b1) {  // the routed experts are done: the shared expert's rows only
         launch_k(k_make_shared_items, dim3(1), dim3(64), 0, st, E, TK, T, items, n_items);
       } else {
-        rc = launch_permute(ids, TK, E, counts, offsets, perm, inv, status, st);
+        rc = launch_permute(ids, TK, E, counts, offsets, perm, inv, status, st, T, sh ? 1 : 0,
+                            items, n_items);
         if (rc != DS4MOE_OK) return rc;
-        launch_k(k_make_items, dim3(1), dim3(64), 0, st, counts, offsets, E, TK, T,
-                 sh ? 1 : 0, items, n_items);
       }
     }
     if ((rc = launched()) != DS4MOE_OK) return rc;

@@ -46,7 +46,8 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(1024) void k_permute(const int32_t* ids, int n, int E, int32_t* counts,
                                                   int32_t* offsets, int32_t* perm, int32_t* inv,
-                                                  uint32_t* status);
+                                                  uint32_t* status, int T, int with_shared,
+                                                  int32_t* items, int32_t* n_items);
 
 // Work list: items (e, row0, nrows) for every expert with pairs (64-row
 // pieces), then the shared expert's rows (e == E).  Items of at most 16 rows
@@ -65,10 +66,11 @@ __device__ inline int wave_prefix_excl(int v, int& total) {
   return incl - v;
 }
 
-__global__ __launch_bounds__(64) void k_make_items(const int32_t* counts, const int32_t* offsets,
-                                                   int E, int TK, int T, int with_shared,
-                                                   int32_t* items, int32_t* n_items) {
-  const int lane = threadIdx.x;
+// The work list by one wave (lane = threadIdx.x mod 64), built inside
+// k_permute from its LDS copies of the counts and offsets.
+__device__ void make_items_wave(const int32_t* counts, const int32_t* offsets, int E, int TK, int T,
+                                int with_shared, int32_t* items, int32_t* n_items) {
+  const int lane = threadIdx.x & 63;
   int cnt[4], nsm = 0, nlg = 0;
 #pragma unroll
   for (int j = 0; j < 4; j++) {

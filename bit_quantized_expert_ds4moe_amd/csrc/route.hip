@@ -643,12 +643,20 @@ __global__ void k_route_hash(const int32_t* tok, const int32_t* table, int vocab
 constexpr int kPermChunks = 64;
 constexpr int kPermMax = 32768;
 
+__device__ void make_items_wave(const int32_t* counts, const int32_t* offsets, int E, int TK, int T,
+                                int with_shared, int32_t* items, int32_t* n_items);
+
+// Counting sort of the pairs by expert (stable: pair order within an
+// expert), one workgroup.  With items (nullable) the work list of the
+// grouped kernels is built too (make_items_wave, wave 1, from the counts and
+// offsets in LDS while wave 0 scatters).
 __global__ __launch_bounds__(1024) void k_permute(const int32_t* ids, int n, int E, int32_t* counts,
                                                   int32_t* offsets, int32_t* perm, int32_t* inv,
-                                                  uint32_t* status) {
+                                                  uint32_t* status, int T, int with_shared,
+                                                  int32_t* items, int32_t* n_items) {
   __shared__ int tab[kPermChunks * 256];  // [chunk][expert]: counts, then first positions
   __shared__ uint8_t eid[kPermMax];
-  __shared__ int base[257];
+  __shared__ int base[257], s_cnt[256];
   const int tid = threadIdx.x;
   for (int i = tid; i < kPermChunks * 256; i += 1024) tab[i] = 0;
   bool bad = false;
@@ -678,16 +686,33 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* ids, int n, int
     base[tid] = run;
   }
   __syncthreads();
-  if (tid == 0) {  // exclusive scan over experts
-    int run = 0;
-    for (int e = 0; e < E; e++) {
-      const int c = base[e];
-      counts[e] = c;
-      offsets[e] = run;
-      base[e] = run;
-      run += c;
+  if (tid < 64) {  // exclusive scan over the experts: four per lane, then over the lanes
+    int c[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int e = 4 * tid + j;
+      c[j] = e < E ? base[e] : 0;
+      sum += c[j];
     }
-    offsets[E] = run;
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(incl, d);
+      if (tid >= d) incl += u;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int e = 4 * tid + j;
+      if (e < E) {
+        counts[e] = c[j];
+        offsets[e] = run;
+        s_cnt[e] = c[j];
+        base[e] = run;
+      }
+      run += c[j];
+    }
+    if (tid == 63) offsets[E] = run;
   }
   __syncthreads();
   if (tid < kPermChunks) {
@@ -698,6 +723,8 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* ids, int n, int
       perm[pos] = i;
       inv[i] = pos;
     }
+  } else if (items && tid < 2 * 64) {
+    make_items_wave(s_cnt, base, E, n, T, with_shared, items, n_items);
   }
 }
 
