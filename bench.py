@@ -39,8 +39,8 @@ GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "6b59230eb804c079daa441ffe55c53d49e519d84fb9bf03e94409f799bcac8aa",
-    "bytes": 26421106,
+    "sha256": "e9dbb7d9037dfdf749c5dd5ff0a883bad1514ef272208c06f855ce4e0df314c2",
+    "bytes": 26480029,
 }
 
 
@@ -51,8 +51,8 @@ Q4K_GATEUP_TRAFFIC = {
                 "bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "a6bbb99d253b10709443f5c37263049cb6582361c82b14fbebebf309a1a96b6e",
-    "bytes": 56933204,
+    "sha256": "0117109e4f443b140f8e6673de4827887288433af93dd4975b23dafd25286dc0",
+    "bytes": 57050723,
 }
 
 
