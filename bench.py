@@ -76,6 +76,20 @@ def event_handle(ev):
     return ev.cuda_event
 
 
+def mean_event_us(pairs):
+    """Mean span in microseconds of the recorded (start, stop) event pairs;
+    None when no launch of the class recorded them (a one-token layer call
+    scores inside its gate/up kernel, so no scoring kernel runs)."""
+    import numpy as np
+    t = []
+    for a, b in pairs:
+        try:
+            t.append(a.elapsed_time(b))
+        except RuntimeError:
+            continue
+    return float(np.mean(t)) * 1e3 if t else None
+
+
 def time_replays(replay, n):
     """Times n passes of replay() (each a whole timed region: a graph replay
     or a sequence of them), each bracketed by device synchronisations, with
@@ -226,7 +240,8 @@ def bench_decode_b1(args):
     sleep_ms = s0.elapsed_time(s1)
     if sleep_ms < host_ms:
         log("warning: GPU sleep %.2f ms shorter than host enqueue %.2f ms" % (sleep_ms, host_ms))
-    kern_us = {c: float(np.mean([a.elapsed_time(b) for a, b in evs[c]]) * 1e3) for c in classes}
+    kern_us = {c: mean_event_us(evs[c]) for c in classes}
+    kern_us = {c: v for c, v in kern_us.items() if v is not None}
     log("kernel averages (us):", kern_us, "sleep %.2f ms, enqueue %.2f ms" % (sleep_ms, host_ms))
     assert ds4.check(ws.data_ptr(), st) == 0
 
@@ -377,10 +392,10 @@ def bench_stack(args, mixed=False, shared=False):
         ds4.profile_events(k, None, None)
     torch.cuda.synchronize()
     def mean_us(c, q4):
-        t = [a.elapsed_time(b) for (a, b), f in zip(evs[c][:used[c]], ev_q4[c]) if f == q4]
-        return float(np.mean(t)) * 1e3 if t else None
+        return mean_event_us([ab for ab, f in zip(evs[c][:used[c]], ev_q4[c]) if f == q4])
 
     kern_us = {c: mean_us(c, False) for c in classes if used[c]}
+    kern_us = {c: v for c, v in kern_us.items() if v is not None}
     log("kernel averages (us):", kern_us)
     kern_us_q4 = {c: mean_us(c, True) for c in ("gateup", "down")} if w.q4_layers else None
     if kern_us_q4:
@@ -538,7 +553,8 @@ def bench_batched(args, which):
     for k in classes.values():
         ds4.profile_events(k, None, None)
     torch.cuda.synchronize()
-    kern_us = {c: float(np.mean([a.elapsed_time(b) for a, b in evs[c]]) * 1e3) for c in classes}
+    kern_us = {c: mean_event_us(evs[c]) for c in classes}
+    kern_us = {c: v for c, v in kern_us.items() if v is not None}
     log("kernel averages (us):", kern_us)
 
     per_expert = w.expert_bytes()

@@ -536,10 +536,12 @@ __global__ __launch_bounds__(kFewWaves * 64) void k_gateup_few(GateUpFewArgs a) 
 // row: their 2-bit codes are exactly the 16 bytes qs[32hq + 16p .. +15] of
 // block b (one 16-byte load), their sub-blocks are j = 8hq + 2s + p (scale
 // bytes 8hq + p + 2s, inside the 8 bytes at 8hq), and d, dmin sit at byte 80:
-// three loads per lane serve two rows.  The lane first turns its 64 SwiGLU
-// values into 16-bit fixed point with one scale, h_i ~= S n_i,
+// three loads per lane serve two rows.  The lane's 64 SwiGLU values become
+// 16-bit fixed point with one scale, h_i ~= S n_i,
 // n_i = round(32767 h_i / max|h|) (relative error below 2^-16 of the chunk
-// maximum; every later product is exact):
+// maximum; every later product is exact); lanes L and L + 32 need the same
+// values, so each reads and converts 32 of them and the pair swaps the
+// results (and their partial maxima) with v_permlane32_swap:
 //   nr[8s + q] = (n[16s + 2q], n[16s + 2q + 1]) as int16 pairs,
 //   xn[s] = sum_l n[16s + l]   (for the min term).
 // The h vectors sit in LDS as 16-byte chunks; chunk G of a slot (G = f / 4
@@ -617,7 +619,7 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
   // Lane chunk order of the 64 values a lane consumes: chunk G0 + 8s + m4 of
   // its slot (16 bytes each) holds values 16s + 4m4 .. +3.
   const int G0 = 64 * b + 32 * hq + 4 * p;
-  float hv[64];
+  float hv[32];
   auto take = [&](int s, int m4, float4 q) {
     hv[16 * s + 4 * m4 + 0] = q.x;
     hv[16 * s + 4 * m4 + 1] = q.y;
@@ -642,13 +644,15 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   } else if (!shw) {
-    // 1. this lane's 64 values of slot k, requested ahead of the weights (the
-    // two wave halves read the same columns)
+    // 1. half of this lane's 64 values of slot k, requested ahead of the
+    // weights: the two wave halves cover the same columns, so the lower half
+    // reads and converts values 0-31 (s = 0, 1) and the upper half 32-63
+    // (s = 2, 3), and they exchange the fixed-point results
     const float4* hk = (const float4*)h + 512 * k;
 #pragma unroll
-    for (int s = 0; s < 4; s++)
+    for (int s2 = 0; s2 < 2; s2++)
 #pragma unroll
-      for (int m4 = 0; m4 < 4; m4++) take(s, m4, hk[G0 + 8 * s + m4]);
+      for (int m4 = 0; m4 < 4; m4++) take(s2, m4, hk[G0 + 8 * (2 * u + s2) + m4]);
   }
   float pr[R / 2];
   bool bad_id = false;
@@ -671,27 +675,46 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
     dd[m] = *(const uint32_t*)(blk + 80);
   }
   if constexpr (!STAGE) __builtin_amdgcn_sched_barrier(0);  // every load ahead of the arithmetic
-  // 3. this lane's 64 values of slot k, as 16-bit fixed point
+  // 3. this lane's 64 values of slot k, as 16-bit fixed point (each wave
+  // half takes 32 of them, as above)
   if constexpr (STAGE) {
 #pragma unroll
-    for (int s = 0; s < 4; s++)
+    for (int s2 = 0; s2 < 2; s2++)
 #pragma unroll
-      for (int m4 = 0; m4 < 4; m4++) take(s, m4, hs[512 * k + dn_chunk(G0 + 8 * s + m4)]);
+      for (int m4 = 0; m4 < 4; m4++)
+        take(s2, m4, hs[512 * k + dn_chunk(G0 + 8 * (2 * u + s2) + m4)]);
   }
   uint32_t nr[32];
   int xn[4];
   float S;
   {
+    // the half's 32 values: the largest magnitude over both halves (the
+    // pair of lanes L and L + 32 swap their partial maxima), then the
+    // fixed point of the half's values and of its two sub-block sums, which
+    // the lane pair swaps so that both hold all 64
     AbsMax am;
 #pragma unroll
-    for (int i = 0; i < 64; i++) am.add(hv[i]);
+    for (int i = 0; i < 32; i++) am.add(hv[i]);
+    {
+      const auto rs = __builtin_amdgcn_permlane32_swap((uint32_t)am.smax, (uint32_t)am.smax, false, false);
+      const auto ru = __builtin_amdgcn_permlane32_swap(am.umax, am.umax, false, false);
+      am.smax = max((int)rs[0], (int)rs[1]);
+      am.umax = max((uint32_t)ru[0], (uint32_t)ru[1]);
+    }
     bool nonfinite;
     const float mx = am.value(nonfinite);
     const float inv = mx > 0.0f ? 1.0f / mx : 0.0f;
+    uint32_t own[16];
 #pragma unroll
-    for (int q = 0; q < 32; q++)
-      nr[q] = (uint32_t)__builtin_bit_cast(
+    for (int q = 0; q < 16; q++)
+      own[q] = (uint32_t)__builtin_bit_cast(
           int, __builtin_amdgcn_cvt_pknorm_i16(hv[2 * q] * inv, hv[2 * q + 1] * inv));
+#pragma unroll
+    for (int q = 0; q < 16; q++) {  // lower half's values (s = 0, 1), then the upper half's
+      const auto r = __builtin_amdgcn_permlane32_swap(own[q], own[q], false, false);
+      nr[q] = (uint32_t)r[0];
+      nr[16 + q] = (uint32_t)r[1];
+    }
 #pragma unroll
     for (int s = 0; s < 4; s++) {
       int t = 0;

@@ -459,6 +459,42 @@ def test_ffn_nonfinite_activation_propagates(widx):
     assert err <= TOL_FP32
 
 
+def test_layer_one_token_calls_in_sequence():
+    """Consecutive one-token layer calls on one workspace (scoring kernel,
+    selection fused into gate/up, down), each with its own token, must each
+    select exactly the oracle's experts and gates: nothing a call leaves in
+    the workspace may leak into the next."""
+    from ds4gen.device import make_layer, host_experts
+    w = g.WORKLOADS[1]
+    say("one-token calls in sequence")
+    lt = make_layer(w, 0)
+    T = 8
+    xh = g.activations(w, n_tok=T)
+    x = dev(xh)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, 1)
+    d = ds4.layer_desc(ds4.router(w=ptr(lt.router_w), w_dtype=ds4.F16, bias=ptr(lt.bias)),
+                       experts_of(lt, w))
+    out = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, w.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, w.K), dtype=torch.float32, device="cuda")
+    for i in range(T):
+        ds4.layer(shp, d, x.data_ptr() + i * w.H * 2, ds4.BF16, None, out.data_ptr() + i * w.H * 4,
+                  None, 1, ids.data_ptr() + i * w.K * 4, wts.data_ptr() + i * w.K * 4, None,
+                  ptr(ws), nb, stream())
+    check_clean(ws)
+    oids, owts, _, _ = oracle.route(xh, "bf16", g.router_weight(w, 0), "f16", g.router_bias(w, 0), w.K)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    np.testing.assert_allclose(wts.cpu().numpy(), owts, rtol=2e-6, atol=0)
+    toks = np.array([0, T - 1])
+    want = oracle.moe_ffn(xh, "bf16", oids, owts, host_experts(w, 0, np.unique(oids[toks])),
+                          (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed),
+                          tokens=toks)
+    err = max_rel_err(out.cpu().numpy()[toks], want)
+    say("  max|err|/rms = %g" % err)
+    assert err <= TOL_FP32
+
+
 def test_layer_graph_replays_match_eager():
     """Captured layer calls replayed several times, with eager work and
     synchronisations in between, must reproduce the eager results bit for bit."""

@@ -9,8 +9,8 @@ keys exactly (integer-limb logit, double-double score) and agree with the
 oracle bit for bit, with no fault bit.  FLOW (qiita.com/sukimaengineer/items/
 cd76fec76d49a098abed) § "MoE FFN 部の中身".
 
-Paths: ds4moe_route (selection kernel), ds4moe_layer with the selection fused
-into the batch-1 gate/up kernel (2 tokens), the same after an RMSNorm of the
+Paths: ds4moe_route (selection kernel), ds4moe_layer with the selection
+fused into the batch-1 gate/up kernel (1 and 2 tokens), the same after an RMSNorm of the
 residual stream (the router input then comes from the workspace), and a
 5-token layer call (selection kernel, then the few-token matvecs).  The
 constructed token sits at a non-zero row so that the per-token offsets of
@@ -89,7 +89,7 @@ def test_route_call_exact(cases, ci):
     assert oids[row, 5] == min(case.A, case.B)
 
 
-@pytest.mark.parametrize("T,row", [(2, 1), (5, 4)], ids=["fused-2", "selkernel-5"])
+@pytest.mark.parametrize("T,row", [(1, 0), (2, 1), (5, 4)], ids=["fused-1", "fused-2", "selkernel-5"])
 @pytest.mark.parametrize("ci", range(4), ids=["logit-up", "logit-down", "score-a", "score-b"])
 def test_layer_call_exact(layer, cases, ci, T, row):
     case = cases[ci]
