@@ -185,7 +185,7 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
                        const float* residual, const float* norm_w, float eps, uint16_t* xn_out,
                        int32_t T, const int32_t* tok, int32_t* ids, float* wts, void* ws,
                        const Layout& L, hipStream_t st, bool select = true,
-                       bool few_items = false) {
+                       bool few_items = false, const SharedB1Args* shu = nullptr) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   ProfScope prof(DS4MOE_K_ROUTE, st);
   if (r.tid2eid) {
@@ -225,7 +225,14 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
                               (uintptr_t)xn_out % 16 == 0)
                            : (uintptr_t)x % 16 == 0);
   const dim3 grid(s.n_expert, T);
-  if (vec && norm_w)
+  if (shu && !norm_w) {  // with the shared expert's gate/up (independent of the routing)
+    const dim3 ug(s.n_expert + kI / 8, T);
+    const bool few = T > kSharedB1MaxTokens;
+    if (vec && few) launch_k(k_route_score_shared<true, true>, ug, dim3(256), 0, st, a, *shu, T);
+    else if (vec) launch_k(k_route_score_shared<true, false>, ug, dim3(256), 0, st, a, *shu, T);
+    else if (few) launch_k(k_route_score_shared<false, true>, ug, dim3(256), 0, st, a, *shu, T);
+    else launch_k(k_route_score_shared<false, false>, ug, dim3(256), 0, st, a, *shu, T);
+  } else if (vec && norm_w)
     launch_k(k_route_score<true, true>, grid, dim3(256), 0, st, a);
   else if (vec)
     launch_k(k_route_score<false, true>, grid, dim3(256), 0, st, a);
@@ -320,7 +327,8 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
                         int32_t T, const int32_t* ids_in, const float4* kbuf, int32_t* ids,
                         const float* wts, float* out, float* residual, void* ws, const Layout& L,
                         hipStream_t st, const SharedB1Args* shb = nullptr,
-                        const ds4moe_router* rt = nullptr, bool few_items = false) {
+                        const ds4moe_router* rt = nullptr, bool few_items = false,
+                        bool sh_gu_done = false) {
   // one weight read for all tokens (kSharedB1MaxTokens < T <= kSharedFewMaxTokens)
   const bool sh_few = shb && T > kSharedB1MaxTokens && T <= kSharedFewMaxTokens;
   uint32_t* status = at<uint32_t>(ws, L.status);
@@ -377,7 +385,7 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
   }
   ds4moe_status rc = launched();
   if (rc != DS4MOE_OK) return rc;
-  if (shb) {  // the shared expert's gate/up; its down rides along with the routed one
+  if (shb && !sh_gu_done) {  // the shared expert's gate/up; its down rides along with the routed one
     ProfScope prof(DS4MOE_K_OTHER, st);
     if (sh_few)
       launch_k(k_shared_gateup_q80_few, dim3(kI / 8, (T + kShFewTok - 1) / kShFewTok), dim3(256), 0,
@@ -481,11 +489,36 @@ ds4moe_status launch_imatrix(const ds4moe_shape& s, const ImxOut& o, const void*
   return launched();
 }
 
+// Arguments of the shared expert's matvec kernels (its SwiGLU rows follow the
+// routed rows in the workspace; its output is added to out or the residual).
+SharedB1Args shared_args(const ds4moe_shape& s, const ds4moe_experts& sh, const void* x, int32_t T,
+                         float* out, float* residual, void* ws, const Layout& L) {
+  SharedB1Args sa{};
+  sa.x = (const uint16_t*)x;
+  sa.gate = (const uint8_t*)sh.gate;
+  sa.up = (const uint8_t*)sh.up;
+  sa.down = (const uint8_t*)sh.down;
+  sa.h = at<float>(ws, L.h) + (size_t)T * s.top_k * s.inter;  // after the routed rows
+  sa.out = residual ? residual : out;
+  sa.status = at<uint32_t>(ws, L.status);
+  return sa;
+}
+
+// do_ffn takes the few-token matvec path and runs the shared expert there by
+// matvecs (the same tests as in do_ffn).
+bool shared_by_matvecs(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_experts* sh,
+                       const void* x, int32_t x_dt, int32_t T, bool few_items_only) {
+  return sh && fast_b1(s, ex, x, x_dt, T, few_items_only) &&
+         grouped_eligible(s, ex, sh, x, x_dt, T) && T <= kSharedFewMaxTokens &&
+         shared_b1_ok(s, *sh, x, x_dt);
+}
+
 ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4moe_experts* sh,
                      const void* x, int32_t x_dt, int32_t T, const int32_t* ids, const float* wts,
                      float* out, float* residual, int32_t* perm_dbg, void* ws, const Layout& L,
                      hipStream_t st, const ImxOut* imx = nullptr, const float4* kbuf_sel = nullptr,
-                     const ds4moe_router* rt = nullptr, bool few_items = false) {
+                     const ds4moe_router* rt = nullptr, bool few_items = false,
+                     bool sh_gu_done = false) {
   uint32_t* status = at<uint32_t>(ws, L.status);
   const bool b1 = fast_b1(s, ex, x, x_dt, T, few_items && !kbuf_sel) &&
                   (!sh || grouped_eligible(s, ex, sh, x, x_dt, T));
@@ -494,23 +527,14 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     // to kSharedB1MaxTokens tokens, then one weight read for all tokens up to
     // kSharedFewMaxTokens; beyond, the grouped kernels below take it
     const bool shb1 = sh && T <= kSharedFewMaxTokens && shared_b1_ok(s, *sh, x, x_dt);
-    SharedB1Args sa{};
-    if (shb1) {
-      sa.x = (const uint16_t*)x;
-      sa.gate = (const uint8_t*)sh->gate;
-      sa.up = (const uint8_t*)sh->up;
-      sa.down = (const uint8_t*)sh->down;
-      sa.h = at<float>(ws, L.h) + (size_t)T * s.top_k * s.inter;  // after the routed rows
-      sa.out = residual ? residual : out;
-      sa.status = status;
-    }
+    const SharedB1Args sa = shb1 ? shared_args(s, *sh, x, T, out, residual, ws, L) : SharedB1Args{};
     // kbuf_sel: the top-K selection runs inside the gate/up kernel, which
     // writes ids and wts (workspace buffers then)
     ds4moe_status rc =
         kbuf_sel ? launch_b1(s, ex, x, T, nullptr, kbuf_sel, const_cast<int32_t*>(ids), wts, out,
-                             residual, ws, L, st, shb1 ? &sa : nullptr, rt)
+                             residual, ws, L, st, shb1 ? &sa : nullptr, rt, false, sh_gu_done)
                  : launch_b1(s, ex, x, T, ids, nullptr, nullptr, wts, out, residual, ws, L, st,
-                             shb1 ? &sa : nullptr, nullptr, few_items);
+                             shb1 ? &sa : nullptr, nullptr, few_items, sh_gu_done);
     if (rc == DS4MOE_OK && perm_dbg)  // the few-token path needs no permutation: make it for the caller
       rc = permute_dbg(s, T, ids, perm_dbg, ws, L, st);
     // h: fp32 [T][6][I] by pair; the shared expert's rows below reuse its memory
@@ -874,15 +898,21 @@ ds4moe_status layer_run(const ds4moe_shape* shape, const ds4moe_layer_desc* desc
                          desc->routed.gate_qtype == DS4MOE_IQ2_XXS &&
                          fast_b1(*shape, desc->routed, fx, fdt, n_tok, true) &&
                          (!sh || grouped_eligible(*shape, desc->routed, sh, fx, fdt, n_tok));
+  // the shared expert's gate/up runs in the scoring launch when the input is
+  // given (no RMSNorm to wait for) and the shared expert goes by matvecs
+  const bool sh_union = sh && !norm && !r.tid2eid &&
+                        shared_by_matvecs(*shape, desc->routed, sh, fx, fdt, n_tok, few_items && !fuse);
+  const SharedB1Args shu =
+      sh_union ? shared_args(*shape, *sh, fx, n_tok, out, residual, ws, L) : SharedB1Args{};
   rc = do_route(*shape, r, x, x_dtype, norm ? residual : nullptr, norm ? desc->norm_w : nullptr,
                 desc->norm_eps, norm ? xn : nullptr, n_tok, token_ids, ids, wts, ws, L, stream,
-                !fuse, few_items);
+                !fuse, few_items, sh_union ? &shu : nullptr);
   if (rc != DS4MOE_OK) return rc;
   // the fused selection reads the router input fx (the normalised row when
   // norm: the scoring wrote it to the workspace) for exact recomputations
   rc = do_ffn(*shape, desc->routed, sh, fx, fdt, n_tok, ids, wts, norm ? nullptr : out,
               norm ? residual : nullptr, nullptr, ws, L, stream, nullptr,
-              fuse ? at<float4>(ws, L.kbuf) : nullptr, fuse ? &r : nullptr, few_items);
+              fuse ? at<float4>(ws, L.kbuf) : nullptr, fuse ? &r : nullptr, few_items, sh_union);
   if (rc != DS4MOE_OK) return rc;
   if (ids_dbg &&
       hipMemcpyAsync(ids_dbg, ids, sizeof(int32_t) * n_tok * shape->top_k, hipMemcpyDeviceToDevice,

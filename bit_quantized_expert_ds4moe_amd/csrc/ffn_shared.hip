@@ -60,11 +60,10 @@ __device__ inline float q80_dot64(const uint32_t (&D)[17], const uint32_t* xl, c
 // wave w of block b handles features 8b + 2w and 8b + 2w + 1 (their gate and
 // up rows) for token blockIdx.y.  The weights are requested right behind the
 // token's activations, before the fixed-point conversion.
-__global__ __launch_bounds__(256) void k_shared_gateup_q80_b1(SharedB1Args a) {
+__device__ inline void shared_gateup_b1_block(const SharedB1Args& a, int bx, int t) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t = blockIdx.y;
-  const int f0 = 8 * blockIdx.x + 2 * w;
+  const int f0 = 8 * bx + 2 * w;
   const uint4* xp = (const uint4*)(a.x + (size_t)t * kH + 64 * lane);
   uint4 xq[8];
 #pragma unroll
@@ -93,6 +92,9 @@ __global__ __launch_bounds__(256) void k_shared_gateup_q80_b1(SharedB1Args a) {
     const float g = lane ? v[1] : v[0], u = lane ? v[3] : v[2];
     a.h[(size_t)t * kI + f0 + lane] = silu(g) * u;
   }
+}
+__global__ __launch_bounds__(256) void k_shared_gateup_q80_b1(SharedB1Args a) {
+  shared_gateup_b1_block(a, blockIdx.x, blockIdx.y);
 }
 
 // down of the shared expert, added to the output.  Grid (4096 / 16, T), 256
@@ -176,12 +178,12 @@ __device__ inline float fx_load(const uint32_t* r, uint32_t* xl, uint32_t* xh, i
 
 // gate/up: grid (2048 / 8, rows of kShFewTok tokens), 256 threads, rows as in
 // k_shared_gateup_q80_b1.
-__global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, int T) {
+__device__ inline void shared_gateup_few_block(const SharedB1Args& a, int T, int bx, int by) {
   __shared__ uint32_t fx[kShFewTok * 64 * kShFx];
-  const int t0 = kShFewTok * blockIdx.y, nt = min(kShFewTok, T - t0);
+  const int t0 = kShFewTok * by, nt = min(kShFewTok, T - t0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int f0 = 8 * blockIdx.x + 2 * w;
+  const int f0 = 8 * bx + 2 * w;
   uint32_t D[4][17];  // gate f0, gate f0+1, up f0, up f0+1
 #pragma unroll
   for (int r = 0; r < 4; r++) {
@@ -215,6 +217,26 @@ __global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, i
       const float g = lane ? v[1] : v[0], u = lane ? v[3] : v[2];
       a.h[(size_t)(t0 + t) * kI + f0 + lane] = silu(g) * u;
     }
+  }
+}
+__global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, int T) {
+  shared_gateup_few_block(a, T, blockIdx.x, blockIdx.y);
+}
+
+// The router's scoring and the shared expert's gate/up in one launch: the
+// shared expert does not depend on the routing, so its weight stream runs
+// beside the scoring, whose blocks wait mostly on memory latency.  Grid
+// (E + 2048 / 8, T), 256 threads: blocks x < E score expert x for token y
+// (k_route_score<false, VEC>); the others are the shared gate/up blocks
+// x - E (per token, or FEW: for the tokens of grid row y of kShFewTok).
+template <bool VEC, bool FEW>
+__global__ __launch_bounds__(256) void k_route_score_shared(RouteArgs r, SharedB1Args s, int T) {
+  if ((int)blockIdx.x < r.E) {
+    route_score_block<false, VEC>(r, blockIdx.x, blockIdx.y);
+  } else if (FEW) {
+    if ((int)blockIdx.y * kShFewTok < T) shared_gateup_few_block(s, T, blockIdx.x - r.E, blockIdx.y);
+  } else {
+    shared_gateup_b1_block(s, blockIdx.x - r.E, blockIdx.y);
   }
 }
 

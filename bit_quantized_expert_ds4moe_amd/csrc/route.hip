@@ -258,9 +258,9 @@ __device__ __noinline__ float exact_logit_wave(RouteSrc src, int e, bool& ok) {
 // specialised so that the batch-1 variant carries no unused code: its blocks
 // run through their code once, and instruction fetch is on the critical path.
 template <bool NORM, bool VEC>
-__global__ __launch_bounds__(256) void k_route_score(RouteArgs a) {
+__device__ inline void route_score_block(const RouteArgs& a, int e, int t) {
   __shared__ double sh[8];
-  const int e = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   constexpr int kMaxSlab = 2;  // VEC: hidden <= 4096
 
   uint4 wv[kMaxSlab];
@@ -380,6 +380,11 @@ __global__ __launch_bounds__(256) void k_route_score(RouteArgs a) {
     if (key != key) key = klo = khi = -__builtin_huge_valf();  // NaN never wins
     a.kbuf[(size_t)t * a.E + e] = make_float4(key, klo, khi, sp);
   }
+}
+
+template <bool NORM, bool VEC>
+__global__ __launch_bounds__(256) void k_route_score(RouteArgs a) {
+  route_score_block<NORM, VEC>(a, blockIdx.x, blockIdx.y);
 }
 
 // Order-preserving map of a binary32 key to uint32 (larger key, larger code;

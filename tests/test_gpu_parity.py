@@ -344,11 +344,13 @@ def _layer_workload(widx):
 
 
 @pytest.mark.parametrize("widx", [0, 1, "q4k", "mixed", "q4k-t3", "q4k-shared-t2", "q4k-shared-t6", 2,
-                                  "b8-t2", "b8-t3", "b8-t5", "b8-t7", "b8-t10", "b8-t13", "b8-t14"])
+                                  "b8-t1", "b8-t2", "b8-t3", "b8-t5", "b8-t7", "b8-t10", "b8-t13",
+                                  "b8-t14"])
 def test_layer_route_and_ffn(widx):
     # configs 0, 1 and 2; the config-1 layer with Q4_K experts (1 and 3
     # tokens, and 2 and 6 with a Q8_0 shared expert) and with IQ2_XXS gate/up
-    # and Q4_K down; config 2 (Q8_0 shared expert) at 2 tokens (few-token
+    # and Q4_K down; with a shared expert up to 10 tokens its gate/up runs in
+    # the scoring launch; config 2 (Q8_0 shared expert) at 1 and 2 tokens (few-token
     # kernels, the top-6 selection of each token fused into gate/up, shared
     # expert per token), 3 (the same, shared expert read once for all
     # tokens), 5, 7, 8 and 10 (selection kernel listing the distinct experts,
