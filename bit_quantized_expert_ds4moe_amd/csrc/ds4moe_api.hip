@@ -181,6 +181,17 @@ PermPtrs perm_ptrs(const ds4moe_shape& s, int32_t T, void* ws, const Layout& L) 
 }
 
 // ---- routing ---------------------------------------------------------------
+// The scoring kernel's 16-byte column layout applies (hidden a multiple of
+// 2048 up to 4096, f16 router, bf16 or normalised input, aligned rows).
+bool route_vec(const ds4moe_shape& s, const ds4moe_router& r, const void* x, int32_t x_dt,
+               const float* residual, const float* norm_w, const uint16_t* xn_out) {
+  return s.hidden % 2048 == 0 && s.hidden <= 4096 && r.w_dtype == DS4MOE_F16 &&
+         (norm_w || x_dt == DS4MOE_BF16) && ((uintptr_t)r.w % 16 == 0) &&
+         (norm_w ? ((uintptr_t)residual % 16 == 0 && (uintptr_t)norm_w % 16 == 0 &&
+                    (uintptr_t)xn_out % 16 == 0)
+                 : (uintptr_t)x % 16 == 0);
+}
+
 ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void* x, int32_t x_dt,
                        const float* residual, const float* norm_w, float eps, uint16_t* xn_out,
                        int32_t T, const int32_t* tok, int32_t* ids, float* wts, void* ws,
@@ -219,19 +230,17 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
     a.items = pp.items;
     a.n_items = pp.n_items;
   }
-  const bool vec = s.hidden % 2048 == 0 && s.hidden <= 4096 && r.w_dtype == DS4MOE_F16 &&
-                   (norm_w || x_dt == DS4MOE_BF16) && ((uintptr_t)r.w % 16 == 0) &&
-                   (norm_w ? ((uintptr_t)residual % 16 == 0 && (uintptr_t)norm_w % 16 == 0 &&
-                              (uintptr_t)xn_out % 16 == 0)
-                           : (uintptr_t)x % 16 == 0);
+  const bool vec = route_vec(s, r, x, x_dt, residual, norm_w, xn_out);
   const dim3 grid(s.n_expert, T);
-  if (shu && !norm_w) {  // with the shared expert's gate/up (independent of the routing)
+  if (shu) {  // with the shared expert's gate/up (independent of the routing)
     const dim3 ug(s.n_expert + kI / 8, T);
     const bool few = T > kSharedB1MaxTokens;
-    if (vec && few) launch_k(k_route_score_shared<true, true>, ug, dim3(256), 0, st, a, *shu, T);
-    else if (vec) launch_k(k_route_score_shared<true, false>, ug, dim3(256), 0, st, a, *shu, T);
-    else if (few) launch_k(k_route_score_shared<false, true>, ug, dim3(256), 0, st, a, *shu, T);
-    else launch_k(k_route_score_shared<false, false>, ug, dim3(256), 0, st, a, *shu, T);
+    // (with norm_w the caller has checked vec and T <= kSharedB1MaxTokens)
+    if (norm_w) launch_k(k_route_score_shared<true, false, true>, ug, dim3(256), 0, st, a, *shu, T);
+    else if (vec && few) launch_k(k_route_score_shared<true, true, false>, ug, dim3(256), 0, st, a, *shu, T);
+    else if (vec) launch_k(k_route_score_shared<true, false, false>, ug, dim3(256), 0, st, a, *shu, T);
+    else if (few) launch_k(k_route_score_shared<false, true, false>, ug, dim3(256), 0, st, a, *shu, T);
+    else launch_k(k_route_score_shared<false, false, false>, ug, dim3(256), 0, st, a, *shu, T);
   } else if (vec && norm_w)
     launch_k(k_route_score<true, true>, grid, dim3(256), 0, st, a);
   else if (vec)
@@ -898,10 +907,14 @@ ds4moe_status layer_run(const ds4moe_shape* shape, const ds4moe_layer_desc* desc
                          desc->routed.gate_qtype == DS4MOE_IQ2_XXS &&
                          fast_b1(*shape, desc->routed, fx, fdt, n_tok, true) &&
                          (!sh || grouped_eligible(*shape, desc->routed, sh, fx, fdt, n_tok));
-  // the shared expert's gate/up runs in the scoring launch when the input is
-  // given (no RMSNorm to wait for) and the shared expert goes by matvecs
-  const bool sh_union = sh && !norm && !r.tid2eid &&
-                        shared_by_matvecs(*shape, desc->routed, sh, fx, fdt, n_tok, few_items && !fuse);
+  // the shared expert's gate/up runs in the scoring launch when it goes by
+  // matvecs (with an RMSNorm, per-token kernels whose blocks normalise the
+  // input themselves)
+  const bool sh_union =
+      sh && !r.tid2eid &&
+      shared_by_matvecs(*shape, desc->routed, sh, fx, fdt, n_tok, few_items && !fuse) &&
+      (!norm || (n_tok <= kSharedB1MaxTokens &&
+                 route_vec(*shape, r, x, x_dtype, residual, desc->norm_w, xn)));
   const SharedB1Args shu =
       sh_union ? shared_args(*shape, *sh, fx, n_tok, out, residual, ws, L) : SharedB1Args{};
   rc = do_route(*shape, r, x, x_dtype, norm ? residual : nullptr, norm ? desc->norm_w : nullptr,

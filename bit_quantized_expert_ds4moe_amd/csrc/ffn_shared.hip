@@ -60,11 +60,13 @@ __device__ inline float q80_dot64(const uint32_t (&D)[17], const uint32_t* xl, c
 // wave w of block b handles features 8b + 2w and 8b + 2w + 1 (their gate and
 // up rows) for token blockIdx.y.  The weights are requested right behind the
 // token's activations, before the fixed-point conversion.
-__device__ inline void shared_gateup_b1_block(const SharedB1Args& a, int bx, int t) {
+// xrow: the token's input row (a.x + t * 4096, or a copy in LDS)
+__device__ inline void shared_gateup_b1_block(const SharedB1Args& a, int bx, int t,
+                                              const uint16_t* xrow) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int f0 = 8 * bx + 2 * w;
-  const uint4* xp = (const uint4*)(a.x + (size_t)t * kH + 64 * lane);
+  const uint4* xp = (const uint4*)(xrow + 64 * lane);
   uint4 xq[8];
 #pragma unroll
   for (int q = 0; q < 8; q++) xq[q] = xp[q];
@@ -94,7 +96,7 @@ __device__ inline void shared_gateup_b1_block(const SharedB1Args& a, int bx, int
   }
 }
 __global__ __launch_bounds__(256) void k_shared_gateup_q80_b1(SharedB1Args a) {
-  shared_gateup_b1_block(a, blockIdx.x, blockIdx.y);
+  shared_gateup_b1_block(a, blockIdx.x, blockIdx.y, a.x + (size_t)blockIdx.y * kH);
 }
 
 // down of the shared expert, added to the output.  Grid (4096 / 16, T), 256
@@ -227,16 +229,35 @@ __global__ __launch_bounds__(256) void k_shared_gateup_q80_few(SharedB1Args a, i
 // shared expert does not depend on the routing, so its weight stream runs
 // beside the scoring, whose blocks wait mostly on memory latency.  Grid
 // (E + 2048 / 8, T), 256 threads: blocks x < E score expert x for token y
-// (k_route_score<false, VEC>); the others are the shared gate/up blocks
+// (k_route_score<NORM, VEC>); the others are the shared gate/up blocks
 // x - E (per token, or FEW: for the tokens of grid row y of kShFewTok).
-template <bool VEC, bool FEW>
+// NORM (VEC, per token): the input is RMSNorm(residual), which the scoring
+// blocks compute and block 0 stores; a shared block cannot wait for that
+// store, so it computes the normalised row itself with the scoring's own
+// code and order of operations (the same bits) into LDS.
+template <bool VEC, bool FEW, bool NORM>
 __global__ __launch_bounds__(256) void k_route_score_shared(RouteArgs r, SharedB1Args s, int T) {
+  static_assert(!NORM || (VEC && !FEW), "normalised input: per-token shared blocks only");
   if ((int)blockIdx.x < r.E) {
-    route_score_block<false, VEC>(r, blockIdx.x, blockIdx.y);
+    route_score_block<NORM, VEC>(r, blockIdx.x, blockIdx.y);
+  } else if (NORM) {
+    __shared__ double shd[8];
+    __shared__ uint4 xs4[kH / 8];
+    uint16_t* xs = (uint16_t*)xs4;
+    float rr[2][8], nw[2][8];
+    const double ns = rms_scale_vec(r, blockIdx.y, shd, rr, nw);
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int u = 0; u < 8; u++)
+        xs[2048 * j + 8 * threadIdx.x + u] =
+            (uint16_t)f64_to_bf16_bits((double)rr[j][u] * ns * (double)nw[j][u]);
+    __syncthreads();
+    shared_gateup_b1_block(s, blockIdx.x - r.E, blockIdx.y, xs);
   } else if (FEW) {
     if ((int)blockIdx.y * kShFewTok < T) shared_gateup_few_block(s, T, blockIdx.x - r.E, blockIdx.y);
   } else {
-    shared_gateup_b1_block(s, blockIdx.x - r.E, blockIdx.y);
+    shared_gateup_b1_block(s, blockIdx.x - r.E, blockIdx.y, s.x + (size_t)blockIdx.y * kH);
   }
 }
 

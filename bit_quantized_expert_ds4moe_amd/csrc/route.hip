@@ -249,6 +249,36 @@ __device__ __noinline__ float exact_logit_wave(RouteSrc src, int e, bool& ok) {
   return negative ? -r : r;
 }
 
+// RMSNorm scale of token t for hidden % 2048 == 0, up to 4096, with 256
+// threads: thread tid loads the residual and norm weight of columns
+// 2048 j + 8 tid .. +7 (into rr, nw) and the block sums the squares along a
+// fixed tree in binary64; returns 1 / sqrt(mean + eps).  Every block that
+// calls it for a token gets the same bits.
+__device__ inline double rms_scale_vec(const RouteArgs& a, int t, double* sh, float (&rr)[2][8],
+                                       float (&nw)[2][8]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    if (j >= a.H / 2048) break;
+    const float4* rp = (const float4*)(a.residual + (size_t)t * a.H) + 512 * j + 2 * tid;
+    const float4* np = (const float4*)a.norm_w + 512 * j + 2 * tid;
+    const float4 r0 = rp[0], r1 = rp[1], n0 = np[0], n1 = np[1];
+    rr[j][0] = r0.x; rr[j][1] = r0.y; rr[j][2] = r0.z; rr[j][3] = r0.w;
+    rr[j][4] = r1.x; rr[j][5] = r1.y; rr[j][6] = r1.z; rr[j][7] = r1.w;
+    nw[j][0] = n0.x; nw[j][1] = n0.y; nw[j][2] = n0.z; nw[j][3] = n0.w;
+    nw[j][4] = n1.x; nw[j][5] = n1.y; nw[j][6] = n1.z; nw[j][7] = n1.w;
+  }
+  double ss = 0.0, dummy = 0.0;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    if (j >= a.H / 2048) break;
+#pragma unroll
+    for (int u = 0; u < 8; u++) ss = fma((double)rr[j][u], (double)rr[j][u], ss);
+  }
+  block_sum2(ss, dummy, sh);
+  return 1.0 / sqrt(ss / (double)a.H + (double)a.eps);
+}
+
 // Scoring.  Grid (E, T), 256 threads: block (e, t) computes the logit, score
 // and key interval of expert e for token t.  VEC (hidden % 2048 == 0, fp16
 // router, bf16 or normalised input): thread t owns columns 8t..8t+7 of every
@@ -276,26 +306,7 @@ __device__ inline void route_score_block(const RouteArgs& a, int e, int t) {
   float rr[kMaxSlab][8], nw[kMaxSlab][8];
   double nscale = 1.0;
   if (NORM && VEC) {
-#pragma unroll
-    for (int j = 0; j < kMaxSlab; j++) {
-      if (j >= a.H / 2048) break;
-      const float4* rp = (const float4*)(a.residual + (size_t)t * a.H) + 512 * j + 2 * tid;
-      const float4* np = (const float4*)a.norm_w + 512 * j + 2 * tid;
-      const float4 r0 = rp[0], r1 = rp[1], n0 = np[0], n1 = np[1];
-      rr[j][0] = r0.x; rr[j][1] = r0.y; rr[j][2] = r0.z; rr[j][3] = r0.w;
-      rr[j][4] = r1.x; rr[j][5] = r1.y; rr[j][6] = r1.z; rr[j][7] = r1.w;
-      nw[j][0] = n0.x; nw[j][1] = n0.y; nw[j][2] = n0.z; nw[j][3] = n0.w;
-      nw[j][4] = n1.x; nw[j][5] = n1.y; nw[j][6] = n1.z; nw[j][7] = n1.w;
-    }
-    double ss = 0.0, dummy = 0.0;
-#pragma unroll
-    for (int j = 0; j < kMaxSlab; j++) {
-      if (j >= a.H / 2048) break;
-#pragma unroll
-      for (int u = 0; u < 8; u++) ss = fma((double)rr[j][u], (double)rr[j][u], ss);
-    }
-    block_sum2(ss, dummy, sh);
-    nscale = 1.0 / sqrt(ss / (double)a.H + (double)a.eps);
+    nscale = rms_scale_vec(a, t, sh, rr, nw);
   } else if (NORM) {  // generic shapes: strided columns
     double ss = 0.0, dummy = 0.0;
     for (int c = tid; c < a.H; c += 256) {
