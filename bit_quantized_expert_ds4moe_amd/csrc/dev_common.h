@@ -169,6 +169,12 @@ struct AbsMax {
   }
 };
 
+// A wave-uniform int32 read through the scalar cache (the data must not be
+// written while the kernel runs).
+__device__ inline int load_scalar_i32(const int32_t* p, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 // ---- device fault word -------------------------------------------------------
 __device__ inline void raise_fault(uint32_t* status, uint32_t bit) { atomicOr(status, bit); }
 

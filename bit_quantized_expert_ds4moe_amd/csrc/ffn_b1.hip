@@ -203,11 +203,6 @@ constexpr int kGuBlocks = 6 * kI / (kGuWaves * kGuRows);      // 256
 static_assert(kGuBlocks * kGuWaves * kGuRows == 6 * kI, "gate/up rows must tile the 6 slots");
 static_assert(384 + kH / 8 <= kGuWaves * 64 - 64, "x staging needs one helper per 16-byte chunk");
 
-// A wave-uniform int32 read through the scalar cache (the data must not be
-// written while the kernel runs).
-__device__ inline int load_scalar_i32(const int32_t* p, int i) {
-  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
-}
 
 // Table build, conflict-free: a thread owns one entry and writes its 16
 // copies in the order p = (j + entry) % 16, so the 16 lanes a store serves in

@@ -257,11 +257,12 @@ __device__ __noinline__ float exact_logit_wave(RouteSrc src, int e, bool& ok) {
 __device__ inline double rms_scale_vec(const RouteArgs& a, int t, double* sh, float (&rr)[2][8],
                                        float (&nw)[2][8]) {
   const int tid = threadIdx.x;
+  const int nslab = a.H / 2048;  // 1 or 2; the loads are unconditional (see route_score_block)
 #pragma unroll
   for (int j = 0; j < 2; j++) {
-    if (j >= a.H / 2048) break;
-    const float4* rp = (const float4*)(a.residual + (size_t)t * a.H) + 512 * j + 2 * tid;
-    const float4* np = (const float4*)a.norm_w + 512 * j + 2 * tid;
+    const int js = min(j, nslab - 1);
+    const float4* rp = (const float4*)(a.residual + (size_t)t * a.H) + 512 * js + 2 * tid;
+    const float4* np = (const float4*)a.norm_w + 512 * js + 2 * tid;
     const float4 r0 = rp[0], r1 = rp[1], n0 = np[0], n1 = np[1];
     rr[j][0] = r0.x; rr[j][1] = r0.y; rr[j][2] = r0.z; rr[j][3] = r0.w;
     rr[j][4] = r1.x; rr[j][5] = r1.y; rr[j][6] = r1.z; rr[j][7] = r1.w;
@@ -293,12 +294,28 @@ __device__ inline void route_score_block(const RouteArgs& a, int e, int t) {
   const int tid = threadIdx.x;
   constexpr int kMaxSlab = 2;  // VEC: hidden <= 4096
 
-  uint4 wv[kMaxSlab];
-  if (VEC) {  // router-weight loads first: their latency overlaps the input
+  // VEC: every load up front and unconditional (with one slab, the second
+  // load repeats the first and is not used), so that all of them are in
+  // flight together: loads issued inside the slab loop went out one round
+  // trip after another
+  const int nslab = VEC ? a.H / 2048 : 0;  // 1 or 2
+  // the expert's bias, requested now through the scalar cache (read at the
+  // end, it was a round trip of its own)
+  const float bias_e = __int_as_float(load_scalar_i32((const int32_t*)a.bias, e));
+  uint4 wv[kMaxSlab], xv[kMaxSlab];
+  if (VEC) {  // router weights first, then the input
     const uint4* wp = (const uint4*)((const uint16_t*)a.W + (size_t)e * a.H);
 #pragma unroll
-    for (int j = 0; j < kMaxSlab; j++)
-      if (j < a.H / 2048) wv[j] = wp[256 * j + tid];
+    for (int j = 0; j < kMaxSlab; j++) wv[j] = wp[256 * min(j, nslab - 1) + tid];
+    if (!NORM) {
+      const uint4* xp = (const uint4*)((const uint16_t*)a.x + (size_t)t * a.H);
+#pragma unroll
+      for (int j = 0; j < kMaxSlab; j++) xv[j] = xp[256 * min(j, nslab - 1) + tid];
+      // an empty asm that reads one word of every load, so that the
+      // compiler neither sinks the second slab's loads into the branch that
+      // uses them nor issues them after the first slab's wait
+      asm volatile("" ::"v"(wv[0].x), "v"(wv[1].x), "v"(xv[0].x), "v"(xv[1].x), "s"(bias_e));
+    }
   }
   // Normalised input: the residual and norm weight of the thread's own
   // columns are loaded once, up front; the columns of all threads cover the
@@ -328,8 +345,7 @@ __device__ inline void route_score_block(const RouteArgs& a, int e, int t) {
       if (j >= a.H / 2048) break;
       uint32_t xx[4];
       if (!NORM) {
-        const uint4 xv = ((const uint4*)((const uint16_t*)a.x + (size_t)t * a.H))[256 * j + tid];
-        xx[0] = xv.x; xx[1] = xv.y; xx[2] = xv.z; xx[3] = xv.w;
+        xx[0] = xv[j].x; xx[1] = xv[j].y; xx[2] = xv[j].z; xx[3] = xv[j].w;
       } else {
         // rare results outside the normal bfloat16 range take the general
         // rounding in a separate pass (no call in the common path)
@@ -386,7 +402,7 @@ __device__ inline void route_score_block(const RouteArgs& a, int e, int t) {
     const double rel = 0x1p-40;  // far above the error of ssp64
     float sp = (float)s64;
     float slo = (float)(sl64 * (1.0 - rel)), shi = (float)(sh64 * (1.0 + rel));
-    float b = a.bias[e];
+    const float b = bias_e;
     float key = sp + b, klo = slo + b, khi = shi + b;
     if (key != key) key = klo = khi = -__builtin_huge_valf();  // NaN never wins
     a.kbuf[(size_t)t * a.E + e] = make_float4(key, klo, khi, sp);
