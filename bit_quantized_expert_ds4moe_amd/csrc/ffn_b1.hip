@@ -277,19 +277,12 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
     load_row(1);
   }
 
+  SelIds sel{0, 0.0f, false};
+  const float4* kbt = a.kbuf + (size_t)blockIdx.y * a.E;
   if (SEL && w == 0) {
-    int e;
-    float g;
-    const bool first = blockIdx.x == 0;  // one reporter per token
     const RouteSrc src{xtok, DS4MOE_BF16, a.rw, a.rw_dt, a.rbias, kH};
-    select_wave(a.kbuf + (size_t)blockIdx.y * a.E, a.E, 6, a.scale, a.status, first, src, e, g);
-    if (lane < 6) {
-      sel_e[lane] = e;
-      if (first) {
-        a.ids_out[6 * blockIdx.y + lane] = e;
-        a.wts_out[6 * blockIdx.y + lane] = g;
-      }
-    }
+    sel = select_ids(kbt, a.E, 6, a.status, blockIdx.x == 0, src);
+    if (lane < 6) sel_e[lane] = sel.e;
   } else if (t >= 0 && t < 256) {
     store_copies(gtab, t, grid_pairs(gb));
   } else if (t >= 256 && t < 384) {
@@ -306,6 +299,15 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_b1(GateUpB1Args a) {
     load_row(0);
     load_row(1);
     load_row(2);
+    // the gates, off the path to the first weight request; workgroup 0 of
+    // each row publishes the token's ids and gates
+    if (w == 0 && blockIdx.x == 0) {
+      const float g = select_gate(kbt, 6, a.scale, sel);
+      if (lane < 6) {
+        a.ids_out[6 * blockIdx.y + lane] = sel.e;
+        a.wts_out[6 * blockIdx.y + lane] = g;
+      }
+    }
   } else {
     load_row(2);
   }

@@ -145,24 +145,17 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_q4k_b1(GateUpB1Args a)
   uint32_t xl[16], xh[16];
   int sl, sh;
   float S;
+  SelIds sel{0, 0.0f, false};
+  const float4* kbt = a.kbuf + (size_t)blockIdx.y * a.E;
   {
     const uint4* xp = (const uint4*)(xtok + 256 * b + 64 * c);
     uint4 xq[8];
 #pragma unroll
     for (int q = 0; q < 8; q++) xq[q] = xp[q];
     if (SEL && w == 0) {
-      int e;
-      float g;
-      const bool first = blockIdx.x == 0;  // one reporter per token
       const RouteSrc src{xtok, DS4MOE_BF16, a.rw, a.rw_dt, a.rbias, kH};
-      select_wave(a.kbuf + (size_t)blockIdx.y * a.E, a.E, 6, a.scale, a.status, first, src, e, g);
-      if (lane < 6) {
-        sel_e[lane] = e;
-        if (first) {
-          a.ids_out[6 * blockIdx.y + lane] = e;
-          a.wts_out[6 * blockIdx.y + lane] = g;
-        }
-      }
+      sel = select_ids(kbt, a.E, 6, a.status, blockIdx.x == 0, src);
+      if (lane < 6) sel_e[lane] = sel.e;
     }
     auto xval = [&](int i) {  // value i of the lane's 64 (bf16 pairs in xq)
       const uint4 q = xq[i >> 3];
@@ -190,6 +183,15 @@ __global__ __launch_bounds__(kGuWaves * 64) void k_gateup_q4k_b1(GateUpB1Args a)
     const size_t rowi = (size_t)e * kI + ((row0 + r) & (kI - 1));
     q4k_load(a.gate + rowi * kRowQ4kGu, b, c, sg[r]);
     q4k_load(a.up + rowi * kRowQ4kGu, b, c, su[r]);
+  }
+  // the gates, off the path to the first weight request; workgroup 0 of each
+  // row publishes the token's ids and gates
+  if (SEL && w == 0 && blockIdx.x == 0) {
+    const float g = select_gate(kbt, 6, a.scale, sel);
+    if (lane < 6) {
+      a.ids_out[6 * blockIdx.y + lane] = sel.e;
+      a.wts_out[6 * blockIdx.y + lane] = g;
+    }
   }
   float v[8];
 #pragma unroll

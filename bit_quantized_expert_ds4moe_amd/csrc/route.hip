@@ -249,6 +249,7 @@ __device__ __noinline__ float exact_logit_wave(RouteSrc src, int e, bool& ok) {
   return negative ? -r : r;
 }
 
+
 // RMSNorm scale of token t for hidden % 2048 == 0, up to 4096, with 256
 // threads: thread tid loads the residual and norm weight of columns
 // 2048 j + 8 tid .. +7 (into rr, nw) and the block sums the squares along a
@@ -456,6 +457,56 @@ __device__ inline int select_rounds(uint32_t (&ko)[4], int K) {
   return e_sel;
 }
 
+// Descending sorting network on four values (five compare-exchanges).
+__device__ inline void sort4_desc(uint32_t (&c)[4]) {
+  auto cx = [](uint32_t& a, uint32_t& b) {
+    const uint32_t hi = max(a, b), lo = min(a, b);
+    a = hi;
+    b = lo;
+  };
+  cx(c[0], c[1]);
+  cx(c[2], c[3]);
+  cx(c[0], c[2]);
+  cx(c[1], c[3]);
+  cx(c[1], c[2]);
+}
+
+// The same K rounds on packed codes: the upper 24 bits of the key code and
+// 255 - expert in the low byte, so that every code is unique and carries its
+// expert.  Each lane keeps its four codes sorted, so a round is one wave
+// maximum over the lanes' heads and a pop in the winning lane (no ballots,
+// no scalar search).  The packed order is the exact one unless two codes that
+// decide the result share their upper 24 bits: two winners, or the last
+// winner and an expert left out.  Then the function returns false and the
+// caller reruns select_rounds on the full codes.  Otherwise lane k < K
+// returns the k-th winner in e_sel.
+__device__ inline bool select_rounds_packed(const uint32_t (&ko)[4], int K, int& e_sel) {
+  const int lane = threadIdx.x & 63;
+  uint32_t c[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+    c[j] = ko[j] ? ((ko[j] & 0xFFFFFF00u) | (uint32_t)(255 - (lane + 64 * j))) : 0u;
+  sort4_desc(c);
+  uint32_t mine = 0u, m = 0u, prev = 0u;
+  bool clash = false;
+  for (int k = 0; k < K; k++) {
+    m = wave_max_u32(c[0]);
+    clash |= k > 0 && (m >> 8) == (prev >> 8);
+    prev = m;
+    const bool pop = c[0] == m;
+    c[0] = pop ? c[1] : c[0];
+    c[1] = pop ? c[2] : c[1];
+    c[2] = pop ? c[3] : c[2];
+    c[3] = pop ? 0u : c[3];
+    if (lane == k) mine = m;
+  }
+  // a head left behind with the last winner's upper bits (packed codes are
+  // never 0 for a real expert, so 0 never matches)
+  clash |= c[0] != 0u && (c[0] >> 8) == (m >> 8);
+  e_sel = 255 - (int)(mine & 0xFFu);
+  return !__any(clash);
+}
+
 // Exact selection among the experts that the key intervals cannot rule out
 // (upper end at or above `floor`, the lowest lower end among the approximate
 // winners: every other expert lies below K of them for sure).  Each
@@ -465,8 +516,8 @@ __device__ inline int select_rounds(uint32_t (&ko)[4], int K) {
 // rounding point for double-double (never seen; the oracle stops there too)
 // raises DS4MOE_FAULT_UNCERTIFIED when report is set.
 __device__ __noinline__ void select_exact(const float4* kb, int E, int K, float floor,
-                                          RouteSrc src, uint32_t* status, bool report, int& e_sel,
-                                          float& s_sel) {
+                                          RouteSrc src, uint32_t* status, bool report, int& e_out,
+                                          float& s_out) {
   const int lane = threadIdx.x & 63;
   uint32_t ko[4];
   float sc[4];
@@ -500,7 +551,7 @@ __device__ __noinline__ void select_exact(const float4* kb, int E, int K, float 
     }
   }
   if (fault && lane == 0 && report) raise_fault(status, DS4MOE_FAULT_UNCERTIFIED);
-  e_sel = select_rounds(ko, K);
+  const int e_sel = select_rounds(ko, K);
   // the winner's score from the lane that holds it
   float s = 0.0f;
 #pragma unroll
@@ -508,61 +559,93 @@ __device__ __noinline__ void select_exact(const float4* kb, int E, int K, float 
     const float v = __shfl(sc[j], e_sel & 63);
     s = (e_sel >> 6) == j ? v : s;
   }
-  s_sel = s;
+  e_out = e_sel;
+  s_out = s;
 }
 
 // Top-K selection for one token by one wave, from the E <= 256 key intervals
-// of k_route_score (select_rounds on the approximate keys).  Lane k < K
-// records the k-th expert; the winners' scores and intervals are read back
-// afterwards (one load per lane, from lines the wave has just read), so a
-// round carries no per-winner lookups.  When an interval is wider than one
-// binary32 value and the order cannot be certified from the intervals, the
-// selection is redone on exact keys (select_exact).  On return lane k < K
-// holds slot k: expert id in e_out and gate in w_out.  Deterministic: every
-// wave that runs it on the same inputs gets the same answer.
-__device__ inline void select_wave(const float4* kb, int E, int K, float scale, uint32_t* status,
-                                   bool report, const RouteSrc& src, int& e_out, float& w_out) {
+// of k_route_score, in two parts so that a caller can request expert weights
+// between them.  select_ids: the rounds on the approximate keys
+// (select_rounds_packed, or select_rounds on the full codes when packed codes
+// clash); when an interval is wider than one binary32 value, the winners'
+// intervals are read back and the order is certified, else the selection is
+// redone on exact keys (select_exact).  Lane k < K holds the k-th expert.
+// select_gate: lane k < K gets the gate of its expert, from the score the
+// exact pass computed or else the one k_route_score stored (read back from
+// lines the wave has just read).  Deterministic: every wave that runs them on
+// the same inputs gets the same answer.
+struct SelIds {
+  int e;       // lane k < K: the k-th expert
+  float s;     // its score when `exact`
+  bool exact;  // wave-uniform: the exact pass ran
+};
+
+__device__ inline SelIds select_ids(const float4* kb, int E, int K, uint32_t* status, bool report,
+                                    const RouteSrc& src) {
   const int lane = threadIdx.x & 63;
   uint32_t ko[4];
   float kh[4];
   bool wide = false;
+  // four unconditional loads (indices past E read entry E - 1 and are then
+  // masked), so that they go out together: loads in branches of their own
+  // were each preceded by a wait for the one before
+  float4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) v[j] = kb[min(lane + 64 * j, E - 1)];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int ee = lane + 64 * j;
-    const float4 v = ee < E ? kb[ee] : make_float4(0, 0, 0, 0);
-    ko[j] = ee < E ? key_order(v.x) : 0u;
-    kh[j] = v.z;
-    wide |= ee < E && (v.y != v.z);
+    ko[j] = ee < E ? key_order(v[j].x) : 0u;
+    kh[j] = v[j].z;
+    wide |= ee < E && (v[j].y != v[j].z);
   }
-  int e_sel = select_rounds(ko, K);  // lane k: the k-th winner
-  const float4 win = lane < K ? kb[e_sel] : make_float4(0, 0, 0, 0);  // key, lo, hi, score
-  float s_win = win.w;
+  SelIds r{0, 0.0f, false};
+  if (!select_rounds_packed(ko, K, r.e)) r.e = select_rounds(ko, K);
   if (__any(wide)) {
+    const float4 win = lane < K ? kb[r.e] : make_float4(0, 0, 0, 0);  // key, lo, hi, score
     bool ok = true;
     // consecutive winners: the interval of winner k-1 lies above that of k
     const float plo = __shfl_up(win.y, 1);
-    const int pe = __shfl_up(e_sel, 1);
-    if (lane >= 1 && lane < K && !(plo > win.z || (plo == win.z && pe < e_sel))) ok = false;
-    // the last winner precedes every unselected expert
+    const int pe = __shfl_up(r.e, 1);
+    if (lane >= 1 && lane < K && !(plo > win.z || (plo == win.z && pe < r.e))) ok = false;
+    // the last winner precedes every unselected expert (the winners are
+    // taken out first: the packed rounds leave ko as it was)
     const float last_lo = readlane_f32(win.y, K - 1);
-    const int last_e = __builtin_amdgcn_readlane(e_sel, K - 1);
+    const int last_e = __builtin_amdgcn_readlane(r.e, K - 1);
+    bool out[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) out[j] = ko[j] != 0u;
+    for (int k = 0; k < K; k++) {
+      const int ew = __builtin_amdgcn_readlane(r.e, k);
+#pragma unroll
+      for (int j = 0; j < 4; j++) out[j] = out[j] && lane + 64 * j != ew;
+    }
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int ee = lane + 64 * j;
-      if (ee < E && ko[j] != 0u && !(last_lo > kh[j] || (last_lo == kh[j] && last_e < ee)))
-        ok = false;
+      if (ee < E && out[j] && !(last_lo > kh[j] || (last_lo == kh[j] && last_e < ee))) ok = false;
     }
     if (__any(!ok)) {
       float floor = lane < K ? win.y : __builtin_huge_valf();
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) floor = fminf(floor, __shfl_xor(floor, off));
-      select_exact(kb, E, K, floor, src, status, report, e_sel, s_win);
+      // outputs of their own, live only on this path (the common path then
+      // keeps nothing in the stack slots the call needs)
+      int ex;
+      float sx;
+      select_exact(kb, E, K, floor, src, status, report, ex, sx);
+      r = SelIds{ex, sx, true};
     }
   }
+  return r;
+}
+
+__device__ inline float select_gate(const float4* kb, int K, float scale, const SelIds& r) {
+  const int lane = threadIdx.x & 63;
+  const float s = r.exact ? r.s : (lane < K ? kb[r.e].w : 0.0f);
   double ssum = 0.0;
-  for (int k = 0; k < K; k++) ssum += (double)readlane_f32(s_win, k);
-  e_out = lane < K ? e_sel : 0;
-  w_out = lane < K ? (float)((double)scale * (double)s_win / ssum) : 0.0f;
+  for (int k = 0; k < K; k++) ssum += (double)readlane_f32(s, k);
+  return lane < K ? (float)((double)scale * (double)s / ssum) : 0.0f;
 }
 
 // Selection kernel.  Grid T, one wave per token: reads the key intervals
@@ -589,7 +672,9 @@ __global__ __launch_bounds__(1024) void k_route_select(RouteArgs a) {
   src.w_dt = a.w_dt;
   src.bias = a.bias;
   src.H = a.H;
-  select_wave(a.kbuf + (size_t)t * a.E, a.E, a.K, a.scale, a.status, true, src, e, w);
+  const SelIds sel = select_ids(a.kbuf + (size_t)t * a.E, a.E, a.K, a.status, true, src);
+  e = lane < a.K ? sel.e : 0;
+  w = select_gate(a.kbuf + (size_t)t * a.E, a.K, a.scale, sel);
   if (lane < a.K) {
     a.ids[(size_t)t * a.K + lane] = e;
     a.wts[(size_t)t * a.K + lane] = w;

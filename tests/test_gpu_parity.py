@@ -88,38 +88,49 @@ def test_route_ties_and_bias():
     np.testing.assert_allclose(wts, owts, rtol=2e-6)
 
 
-def tied_router(w):
+def tied_router(w, near=False):
     """Router with experts 10, 74 (same lane slot set), 138 and 200 given
     identical keys that beat all others but expert 77: the order must be
-    77, 10, 74, 138, 200 (equal keys go to the lower index)."""
+    77, 10, 74, 138, 200 (equal keys go to the lower index).  With near, the
+    four biases step up by two units in the last place of 30 (2^-18) with the
+    expert index, so the keys differ only in their lowest bits and the order
+    must be 77, 200, 138, 74, 10."""
     W = g.router_weight(w, 0).copy()
     b = g.router_bias(w, 0).copy()
     for e in (74, 138, 200):
         W[e] = W[10]
     b[[10, 74, 138, 200]] = 30.0
+    if near:
+        b[[10, 74, 138, 200]] += np.float32(2.0 ** -18) * np.arange(4, dtype=np.float32)
     b[77] = 50.0
     return W, b
 
 
-def test_route_many_ties():
+NEAR_TIE_ORDER = [77, 200, 138, 74, 10]
+
+
+@pytest.mark.parametrize("near", [False, True], ids=["equal", "near"])
+def test_route_many_ties(near):
     w = g.WORKLOADS[1]
     T = 4
     x = g.activations(w, n_tok=T)
-    W, b = tied_router(w)
+    W, b = tied_router(w, near)
     ids, wts = run_route(w, dev(x), dev(W), dev(b), T)
     oids, owts, _, _ = oracle.route(x, "bf16", W, "f16", b, w.K)
     np.testing.assert_array_equal(ids, oids)
-    assert np.all(ids[:, :5] == [77, 10, 74, 138, 200])
+    assert np.all(ids[:, :5] == (NEAR_TIE_ORDER if near else [77, 10, 74, 138, 200]))
     np.testing.assert_allclose(wts, owts, rtol=2e-6)
 
 
-def test_layer_fused_selection_ties():
-    """Batch-1 layer call (selection fused into the gate/up kernel) on tied keys."""
+@pytest.mark.parametrize("near", [False, True], ids=["equal", "near"])
+def test_layer_fused_selection_ties(near):
+    """Batch-1 layer call (selection fused into the gate/up kernel) on tied
+    keys, and on keys that differ only in their lowest bits."""
     from ds4gen.device import make_layer, host_experts
     w = g.WORKLOADS[1]
-    say("layer fused selection ties")
+    say("layer fused selection ties", "near" if near else "equal")
     lt = make_layer(w, 0)
-    W, b = tied_router(w)
+    W, b = tied_router(w, near)
     x = g.activations(w, n_tok=1)
     shp = shape_of(w)
     ws, nb = workspace(shp, 1)
@@ -134,7 +145,7 @@ def test_layer_fused_selection_ties():
     check_clean(ws)
     oids, owts, _, _ = oracle.route(x, "bf16", W, "f16", b, w.K)
     np.testing.assert_array_equal(ids.cpu().numpy(), oids)
-    assert list(oids[0, :5]) == [77, 10, 74, 138, 200]
+    assert list(oids[0, :5]) == (NEAR_TIE_ORDER if near else [77, 10, 74, 138, 200])
     np.testing.assert_allclose(wts.cpu().numpy(), owts, rtol=2e-6)
     want = oracle.moe_ffn(x, "bf16", oids, owts, host_experts(w, 0, np.unique(oids)),
                           (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed))
