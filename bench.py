@@ -32,15 +32,16 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
 METRIC = "MoE layer tokens/s + expert-weight HBM GB/s (% of peak), batch-1 decode"
 
 # HBM bytes per dispatch of the gate/up kernel from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE passes, scaled against a plain device copy of known size (the
-# summary sits in profiles/decode_b1_hbm_traffic.txt).  Reported only while
+# WRITE_SIZE passes, FETCH_SIZE scaled by what it reads for the 2 GiB read
+# probe (a 256 MiB device copy agrees; the summary sits in
+# profiles/decode_b1_hbm_traffic.txt).  Reported only while
 # the kernel source still hashes to what was measured.
 GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "e9dbb7d9037dfdf749c5dd5ff0a883bad1514ef272208c06f855ce4e0df314c2",
-    "bytes": 26480029,
+    "sha256": "d27256305c2738a7a231627ba4ac43fe830359c7dcbce68ed41b49b4121b568c",
+    "bytes": 26302994,
 }
 
 
@@ -51,8 +52,8 @@ Q4K_GATEUP_TRAFFIC = {
                 "bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "0117109e4f443b140f8e6673de4827887288433af93dd4975b23dafd25286dc0",
-    "bytes": 57050723,
+    "sha256": "dea1a1cad2fb6b936c38032853da0926072dabbf4da4f2882cffa68d64b05d41",
+    "bytes": 56945783,
 }
 
 
