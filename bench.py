@@ -57,6 +57,15 @@ Q4K_GATEUP_TRAFFIC = {
 }
 
 
+def batched_gateup_kernel(w, T):
+    """The routed gate/up kernel that a layer call of T decode tokens runs
+    (the library's token thresholds, learned router)."""
+    import ds4gen as g
+    if w.gate_qt == g.Q4_K:
+        return "k_gateup_q4k_b1<true>" if T <= 4 else "k_gateup_q4k_b1<false>" if T <= 13 else "grouped gate/up"
+    return "k_gateup_b1<true>" if T <= 4 else "k_gateup_few" if T <= 10 else "grouped gate/up"
+
+
 def measured_traffic(rec):
     import hashlib
     h = hashlib.sha256()
@@ -590,7 +599,7 @@ def bench_batched(args, which):
         "roofline": {"bound": "hbm", "kernel": (("grouped Q4_K gate/up: k_x_to_f16 + k_grouped_gateup_q4k"
                                                  if w.gate_qt == g.Q4_K else
                                                  "grouped IQ2_XXS gate/up: k_x_to_f16 + k_grouped_gateup_iq2_small + k_grouped_gateup_iq2<4>")
-                                                if prefill else "k_gateup_b1"),
+                                                if prefill else batched_gateup_kernel(w, T)),
                      "achieved": round(gu_bytes / gu_s / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gu_bytes / gu_s / 1e9 / PEAK_HBM_GBS, 4),
                      "traffic": None, "bytes_per_launch": int(gu_bytes),
