@@ -340,6 +340,12 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
                         bool sh_gu_done = false) {
   // one weight read for all tokens (kSharedB1MaxTokens < T <= kSharedFewMaxTokens)
   const bool sh_few = shb && T > kSharedB1MaxTokens && T <= kSharedFewMaxTokens;
+  // the shared down as a seventh slot of the routed Q2_K down up to
+  // kDnStageMinTokens tokens, also after the read-once gate/up (config-2 layer
+  // call, 4 tokens: 75.3 / 74.0 -> 71.9 / 71.9 us); with more tokens, where
+  // the routed down stages its rows in LDS, the read-once kernel of its own
+  // (8 tokens: a seventh slot there took the down from 34.4 to 53.8 us)
+  const bool sh_slot = shb && T <= kDnStageMinTokens && ex.down_qtype != DS4MOE_Q4_K;
   uint32_t* status = at<uint32_t>(ws, L.status);
   float* h = at<float>(ws, L.h);
   // the selection kernel listed one work item per distinct expert: the
@@ -410,7 +416,7 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
     if (ex.down_qtype == DS4MOE_Q4_K)
       launch_k(k_down_q4k_b1, dgrid, dim3(kDnThreads), 0, st, h, down, dids, wts, s.n_expert, out,
                residual, status);
-    else if (shb && !sh_few)
+    else if (sh_slot)
       launch_k(k_down_q2k_b1<true, false>, dgrid, dim3(kDnThreadsSh), 0, st, h, down, dids, wts,
                s.n_expert, out, residual, status, (const float*)shb->h, shb->down);
     else if (T > kDnStageMinTokens)
@@ -421,7 +427,7 @@ ds4moe_status launch_b1(const ds4moe_shape& s, const ds4moe_experts& ex, const v
                s.n_expert, out, residual, status, (const float*)nullptr, (const uint8_t*)nullptr);
   }
   if ((rc = launched()) != DS4MOE_OK) return rc;
-  if (shb && (sh_few || ex.down_qtype == DS4MOE_Q4_K)) {  // the shared down on its own
+  if (shb && !sh_slot) {  // the shared down on its own
     ProfScope prof(DS4MOE_K_OTHER, st);
     if (sh_few)
       launch_k(k_shared_down_q80_few, dim3(kH / 16, (T + kShFewTok - 1) / kShFewTok), dim3(256), 0,

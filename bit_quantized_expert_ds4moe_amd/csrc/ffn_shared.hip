@@ -3,8 +3,8 @@
 // per token) and read-once variants for a few tokens per grid row.  In layer
 // calls of up to ten tokens the gate/up blocks run inside the router's
 // scoring launch (k_route_score_shared); otherwise they follow the routed
-// kernels.  With per-token matvecs (one or two tokens) the down runs as a
-// seventh slot of the routed batch-1 down, else as a kernel of its own.
+// kernels.  Up to four tokens (Q2_K routed down) the down runs as a seventh
+// slot of the routed batch-1 down, else as a kernel of its own.
 //
 // Method: FLOW = qiita.com/sukimaengineer/items/cd76fec76d49a098abed, section
 // "MoE FFN 部の中身" (an always-on shared expert whose output is added to
