@@ -331,39 +331,44 @@ def bench_stack(args, mixed=False, shared=False):
     resid = torch.empty((1, w.H), dtype=torch.float32, device="cuda")
     tokbuf = torch.empty(1, dtype=torch.int32, device="cuda")
     idx = torch.zeros(1, dtype=torch.int64, device="cuda")
-    out_all = torch.zeros((n_steps, w.H), dtype=torch.float32, device="cuda")
     shp = ds4.shape(w.H, w.I, w.E, w.K, 1.5)
     nb = ds4.workspace_size(shp, 1)
     ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
 
-    def step(st):
-        torch.index_select(h0_all, 0, idx, out=resid)
-        torch.index_select(tok_all, 0, idx, out=tokbuf)
+    # each step runs the 43 layers on its own residual row (reset from the
+    # step inputs before every pass, outside the timed region) and reads its
+    # own token id, so the graph holds the library's launches only
+    resid_all = torch.empty((n_steps, w.H), dtype=torch.float32, device="cuda")
+
+    def step(j, st):
+        rp = resid_all.data_ptr() + j * w.H * 4
+        tp = tok_all.data_ptr() + j * 4
         for d in descs:
-            ds4.layer(shp, d, None, ds4.BF16, resid.data_ptr(), None, tokbuf.data_ptr(), 1, None,
-                      None, None, ws.data_ptr(), nb, st)
-        out_all.index_copy_(0, idx, resid)
-        idx.add_(1)
+            ds4.layer(shp, d, None, ds4.BF16, rp, None, tp, 1, None, None, None, ws.data_ptr(), nb, st)
+
+    def capture(first, count):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            cs = torch.cuda.current_stream().cuda_stream
+            for j in range(count):
+                step(first + j, cs)
+        return gr
 
     st = torch.cuda.current_stream().cuda_stream
-    step(st)
+    resid_all.copy_(h0_all)
+    step(0, st)
     assert ds4.check(ws.data_ptr(), st) == 0
-    idx.zero_()
-    gr = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gr):
-        step(torch.cuda.current_stream().cuda_stream)
-    for _ in range(args.warmup):
-        gr.replay()
+    log("capturing graphs")
+    g_warm = capture(0, args.warmup)
+    g_main = capture(args.warmup, args.steps)
+    resid_all.copy_(h0_all)
+    g_warm.replay()
     torch.cuda.synchronize()
-
-    def timed_steps():  # the K steps after the warm-up, on their own inputs
-        for _ in range(args.steps):
-            gr.replay()
 
     passes = []
     for _ in range(args.replays):
-        idx.fill_(args.warmup)  # untimed: the pass starts at step `warmup`
-        passes += time_replays(timed_steps, 1)
+        resid_all.copy_(h0_all)  # untimed: every pass starts from the step inputs
+        passes += time_replays(g_main.replay, 1)
     ms = float(np.median(passes))
     assert ds4.check(ws.data_ptr(), st) == 0
     log("timed %d steps x %d passes: median %.3f ms (min %.3f, max %.3f)"
@@ -378,10 +383,8 @@ def bench_stack(args, mixed=False, shared=False):
     handles = {c: [(event_handle(a), event_handle(b)) for a, b in evs[c]] for c in classes}
     used = {c: 0 for c in classes}
     ev_q4 = {c: [] for c in classes}     # whether each recorded launch is in a Q4_K layer
-    # the replays above advanced the step index to n_steps: start over so the
-    # eager steps read rows 0 .. n_prof-1 of the step inputs
+    # the eager steps read rows 0 .. n_prof-1 of the step inputs
     assert n_prof <= n_steps
-    idx.zero_()
     torch.cuda.synchronize()
     torch.cuda._sleep(args.sleep_cycles)
     for j in range(n_prof):
@@ -428,8 +431,8 @@ def bench_stack(args, mixed=False, shared=False):
                    "hidden": w.H, "inter": w.I, "experts": w.E, "top_k": w.K,
                    "q4k_layers": list(w.q4_layers), "shared_q8_0": bool(w.shared),
                    "resident_expert_bytes": w.stack_expert_bytes(),
-                   "timing": "hip-graph replay of one 43-layer step per token; median of %d "
-                             "passes of the timed steps" % args.replays},
+                   "timing": "hip-graph replay of the timed steps (43 layers per token, each step "
+                             "on its own residual row); median of %d passes" % args.replays},
         "timed_passes": replay_summary(passes),
         "expert_gbs": round(gbs, 1), "expert_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
