@@ -257,14 +257,32 @@ ds4moe_status do_route(const ds4moe_shape& s, const ds4moe_router& r, const void
 }
 
 // RMSNorm only (hash layers): one block per token writes xn.
+// Hash routing done beside the RMSNorm (one launch for both in hash-routed
+// layers): the arguments of route_hash_token, table == nullptr for none.
+struct HashArgs {
+  const int32_t* tok;
+  const int32_t* table;
+  int vocab, E, K;
+  float scale;
+  int32_t* ids;
+  float* wts;
+  uint32_t* status;
+};
+
 // RMSNorm of the residual stream to bf16 (used where routing does not fold it
 // in, i.e. hash-routed layers).  One block per token; up to 4096 columns the
-// loads of a thread are all issued before the first use.
+// loads of a thread are all issued before the first use.  With hs.table the
+// block's last lane also routes its token by the table (the two do not depend
+// on each other; the lookup's loads overlap the norm's).
 __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, const float* w,
-                                                     float eps, int H, uint16_t* xn) {
+                                                     float eps, int H, uint16_t* xn, HashArgs hs) {
   __shared__ double sh[8];
   constexpr int kRegCols = 16;
   const int t = blockIdx.x, tid = threadIdx.x;
+  auto route = [&]() {
+    if (hs.table && tid == 255)
+      route_hash_token(t, hs.tok, hs.table, hs.vocab, hs.E, hs.K, hs.scale, hs.ids, hs.wts, hs.status);
+  };
   const float* r = residual + (size_t)t * H;
   double ss = 0.0, dummy = 0.0;
   if (H <= 256 * kRegCols) {
@@ -275,6 +293,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, con
       v[j] = c < H ? r[c] : 0.0f;
       wv[j] = c < H ? w[c] : 0.0f;
     }
+    route();  // behind the norm's loads, which it waits for first
 #pragma unroll
     for (int j = 0; j < kRegCols; j++) ss = fma((double)v[j], (double)v[j], ss);
     block_sum2(ss, dummy, sh);
@@ -302,6 +321,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* residual, con
     }
     return;
   }
+  route();
   for (int c = tid; c < H; c += 256) {
     double v = (double)r[c];
     ss = fma(v, v, ss);
@@ -891,10 +911,14 @@ ds4moe_status layer_run(const ds4moe_shape* shape, const ds4moe_layer_desc* desc
   float* wts = at<float>(ws, L.wts);
   uint16_t* xn = at<uint16_t>(ws, L.xn);
   ds4moe_status rc;
-  if (norm && r.tid2eid) {
+  // hash-routed layers with an RMSNorm: one launch normalises and routes
+  const bool norm_hash = norm && r.tid2eid;
+  if (norm_hash) {
     ProfScope prof(DS4MOE_K_OTHER, stream);
+    const HashArgs hs{token_ids, r.tid2eid, r.vocab, shape->n_expert, shape->top_k,
+                      shape->routed_scale, ids, wts, at<uint32_t>(ws, L.status)};
     launch_k(k_rmsnorm_bf16, dim3(n_tok), dim3(256), 0, stream, residual, desc->norm_w,
-                       desc->norm_eps, shape->hidden, xn);
+                       desc->norm_eps, shape->hidden, xn, hs);
     if ((rc = launched()) != DS4MOE_OK) return rc;
   }
   const void* fx = norm ? (const void*)xn : x;
@@ -923,10 +947,12 @@ ds4moe_status layer_run(const ds4moe_shape* shape, const ds4moe_layer_desc* desc
                  route_vec(*shape, r, x, x_dtype, residual, desc->norm_w, xn)));
   const SharedB1Args shu =
       sh_union ? shared_args(*shape, *sh, fx, n_tok, out, residual, ws, L) : SharedB1Args{};
-  rc = do_route(*shape, r, x, x_dtype, norm ? residual : nullptr, norm ? desc->norm_w : nullptr,
-                desc->norm_eps, norm ? xn : nullptr, n_tok, token_ids, ids, wts, ws, L, stream,
-                !fuse, few_items, sh_union ? &shu : nullptr);
-  if (rc != DS4MOE_OK) return rc;
+  if (!norm_hash) {
+    rc = do_route(*shape, r, x, x_dtype, norm ? residual : nullptr, norm ? desc->norm_w : nullptr,
+                  desc->norm_eps, norm ? xn : nullptr, n_tok, token_ids, ids, wts, ws, L, stream,
+                  !fuse, few_items, sh_union ? &shu : nullptr);
+    if (rc != DS4MOE_OK) return rc;
+  }
   // the fused selection reads the router input fx (the normalised row when
   // norm: the scoring wrote it to the workspace) for exact recomputations
   rc = do_ffn(*shape, desc->routed, sh, fx, fdt, n_tok, ids, wts, norm ? nullptr : out,

@@ -722,13 +722,12 @@ __global__ __launch_bounds__(1024) void k_route_select(RouteArgs a) {
   }
 }
 
-// Hash routing: one thread per token.  Invalid token ids or table rows
-// raise a fault bit and route to experts 0..K-1 so that later kernels stay
-// in bounds.
-__global__ void k_route_hash(const int32_t* tok, const int32_t* table, int vocab, int E, int K, int T,
-                             float scale, int32_t* ids, float* wts, uint32_t* status) {
-  int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
+// Hash routing of token t: its row of the table.  An invalid token id or
+// table row raises a fault bit and routes to experts 0..K-1 so that later
+// kernels stay in bounds.
+__device__ inline void route_hash_token(int t, const int32_t* tok, const int32_t* table, int vocab,
+                                        int E, int K, float scale, int32_t* ids, float* wts,
+                                        uint32_t* status) {
   int id = tok[t];
   bool good = id >= 0 && id < vocab;
   if (!good) raise_fault(status, DS4MOE_FAULT_BAD_TOKEN);
@@ -748,6 +747,14 @@ __global__ void k_route_hash(const int32_t* tok, const int32_t* table, int vocab
     ids[(size_t)t * K + k] = row_ok ? table[(size_t)id * K + k] : k;
     wts[(size_t)t * K + k] = w;
   }
+}
+
+// Hash routing: one thread per token.
+__global__ void k_route_hash(const int32_t* tok, const int32_t* table, int vocab, int E, int K, int T,
+                             float scale, int32_t* ids, float* wts, uint32_t* status) {
+  int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  route_hash_token(t, tok, table, vocab, E, K, scale, ids, wts, status);
 }
 
 // Permutation by a stable counting sort in one workgroup of 1024 threads

@@ -179,6 +179,56 @@ def test_hash_route_is_table_lookup():
     np.testing.assert_array_equal(ids.cpu().numpy()[:2], [list(range(6))] * 2)
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_layer_norm_hash_one_launch(T):
+    """Hash-routed layer with an RMSNorm: one launch normalises the residual and
+    routes by the table.  ids and the normalised row are bit-exact against
+    the oracle, the output within tolerance; a bad token id in the same
+    launch raises BAD_TOKEN and routes to experts 0..5."""
+    from ds4gen.device import make_layer, host_experts, step_inputs, to_dev
+    w = g.WORKLOADS[4]
+    say("layer norm + hash", "T", T)
+    lt = make_layer(w, 0, hashed=True, norm=True)
+    h0, tok = step_inputs(w, T, first_step=11)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, T)
+    d = ds4.layer_desc(ds4.router(tid2eid=ptr(lt.tid2eid), vocab=w.vocab), experts_of(lt, w),
+                       norm_w=ptr(lt.norm_w), norm_eps=1e-6)
+    resid = to_dev(h0)
+    tokd = to_dev(tok)
+    ids = torch.empty((T, w.K), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, w.K), dtype=torch.float32, device="cuda")
+    xn = torch.empty((T, w.H), dtype=torch.int16, device="cuda")
+    ds4.layer(shp, d, None, ds4.BF16, ptr(resid), None, ptr(tokd), T, ptr(ids), ptr(wts), ptr(xn),
+              ptr(ws), nb, stream())
+    check_clean(ws)
+    table = lt.tid2eid.cpu().numpy()
+    oids, owts = oracle.route_hash(tok, table, w.E, w.K)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    np.testing.assert_array_equal(wts.cpu().numpy(), owts)
+    nw = lt.norm_w.cpu().numpy()
+    oxn = oracle.rmsnorm_bf16(h0, nw, 1e-6)
+    np.testing.assert_array_equal(xn.cpu().numpy().view(np.uint16), oxn)
+    y = oracle.moe_ffn(oxn, "bf16", oids, owts, host_experts(w, 0, np.unique(oids)),
+                       (w.gate_qt, w.up_qt, w.down_qt), w.H, w.I, w.E, grid=g.grid(w.seed))
+    want = oracle.residual_add(h0, y)
+    err = max_rel_err(resid.cpu().numpy() - h0, want - h0)
+    say("  max|err|/rms =", err)
+    assert err <= TOL_FP32
+    # a token id out of range: reported, routed to experts 0..5, nothing else breaks
+    bad = tok.copy()
+    bad[0] = w.vocab + 5
+    tokd = to_dev(bad)
+    resid = to_dev(h0)
+    ds4.layer(shp, d, None, ds4.BF16, ptr(resid), None, ptr(tokd), T, ptr(ids), ptr(wts), None,
+              ptr(ws), nb, stream())
+    f = ds4.check(ptr(ws), stream())
+    assert f & ds4.FAULT_BAD_TOKEN
+    np.testing.assert_array_equal(ids.cpu().numpy()[0], list(range(6)))
+    if T > 1:
+        np.testing.assert_array_equal(ids.cpu().numpy()[1:], oids[1:])
+
+
 # --------------------------------------------------------------------------
 # permutation
 # --------------------------------------------------------------------------
