@@ -63,10 +63,23 @@ __device__ inline float q80_dot64(const uint32_t (&D)[17], const uint32_t* xl, c
 // gate/up + SwiGLU of the shared expert.  Grid (2048 / 8, T), 256 threads:
 // wave w of block b handles features 8b + 2w and 8b + 2w + 1 (their gate and
 // up rows) for token blockIdx.y.  The weights are requested right behind the
-// token's activations, before the fixed-point conversion.
+// token's activations, before the fixed-point conversion (or, with the
+// normalised input, right behind the RMSNorm's loads: shared_gateup_b1_rows
+// first, shared_gateup_b1_block on the rows afterwards).
 // xrow: the token's input row (a.x + t * 4096, or a copy in LDS)
+__device__ inline void shared_gateup_b1_rows(const SharedB1Args& a, int bx, uint32_t (&D)[4][17]) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int f0 = 8 * bx + 2 * w;
+#pragma unroll
+  for (int r = 0; r < 4; r++) {  // gate f0, gate f0+1, up f0, up f0+1
+    const uint8_t* base = (r < 2 ? a.gate : a.up) + (size_t)(f0 + (r & 1)) * kShRowGu;
+    q80_pair_load(base + 68 * lane, D[r]);
+  }
+}
+template <bool ROWS_GIVEN = false>
 __device__ inline void shared_gateup_b1_block(const SharedB1Args& a, int bx, int t,
-                                              const uint16_t* xrow) {
+                                              const uint16_t* xrow, uint32_t (*Dg)[17] = nullptr) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int f0 = 8 * bx + 2 * w;
@@ -74,12 +87,9 @@ __device__ inline void shared_gateup_b1_block(const SharedB1Args& a, int bx, int
   uint4 xq[8];
 #pragma unroll
   for (int q = 0; q < 8; q++) xq[q] = xp[q];
-  uint32_t D[4][17];  // gate f0, gate f0+1, up f0, up f0+1
-#pragma unroll
-  for (int r = 0; r < 4; r++) {
-    const uint8_t* base = (r < 2 ? a.gate : a.up) + (size_t)(f0 + (r & 1)) * kShRowGu;
-    q80_pair_load(base + 68 * lane, D[r]);
-  }
+  uint32_t Dl[4][17];
+  if constexpr (!ROWS_GIVEN) shared_gateup_b1_rows(a, bx, Dl);
+  uint32_t (*D)[17] = ROWS_GIVEN ? Dg : Dl;
   // keep every load ahead of the conversion (the scheduler would otherwise
   // issue the weights only after the activations have returned)
   __builtin_amdgcn_sched_barrier(0);
@@ -248,8 +258,14 @@ __global__ __launch_bounds__(256) void k_route_score_shared(RouteArgs r, SharedB
     __shared__ double shd[8];
     __shared__ uint4 xs4[kH / 8];
     uint16_t* xs = (uint16_t*)xs4;
+    // the RMSNorm's loads, then the weight rows, then the norm: its waits
+    // (the vector memory counter retires in order) do not wait for weights
     float rr[2][8], nw[2][8];
-    const double ns = rms_scale_vec(r, blockIdx.y, shd, rr, nw);
+    rms_load_vec(r, blockIdx.y, rr, nw);
+    uint32_t D[4][17];
+    shared_gateup_b1_rows(s, blockIdx.x - r.E, D);
+    __builtin_amdgcn_sched_barrier(0);
+    const double ns = rms_scale_of(r, shd, rr);
 #pragma unroll
     for (int j = 0; j < 2; j++)
 #pragma unroll
@@ -257,7 +273,7 @@ __global__ __launch_bounds__(256) void k_route_score_shared(RouteArgs r, SharedB
         xs[2048 * j + 8 * threadIdx.x + u] =
             (uint16_t)f64_to_bf16_bits((double)rr[j][u] * ns * (double)nw[j][u]);
     __syncthreads();
-    shared_gateup_b1_block(s, blockIdx.x - r.E, blockIdx.y, xs);
+    shared_gateup_b1_block<true>(s, blockIdx.x - r.E, blockIdx.y, xs, D);
   } else if (FEW) {
     if ((int)blockIdx.y * kShFewTok < T) shared_gateup_few_block(s, T, blockIdx.x - r.E, blockIdx.y);
   } else {

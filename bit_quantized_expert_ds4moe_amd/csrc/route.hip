@@ -252,11 +252,11 @@ __device__ __noinline__ float exact_logit_wave(RouteSrc src, int e, bool& ok) {
 
 // RMSNorm scale of token t for hidden % 2048 == 0, up to 4096, with 256
 // threads: thread tid loads the residual and norm weight of columns
-// 2048 j + 8 tid .. +7 (into rr, nw) and the block sums the squares along a
-// fixed tree in binary64; returns 1 / sqrt(mean + eps).  Every block that
-// calls it for a token gets the same bits.
-__device__ inline double rms_scale_vec(const RouteArgs& a, int t, double* sh, float (&rr)[2][8],
-                                       float (&nw)[2][8]) {
+// 2048 j + 8 tid .. +7 (into rr, nw; rms_load_vec) and the block sums the
+// squares along a fixed tree in binary64 (rms_scale_of); returns
+// 1 / sqrt(mean + eps).  Every block that calls it for a token gets the same
+// bits.  The two halves let a caller request other data between them.
+__device__ inline void rms_load_vec(const RouteArgs& a, int t, float (&rr)[2][8], float (&nw)[2][8]) {
   const int tid = threadIdx.x;
   const int nslab = a.H / 2048;  // 1 or 2; the loads are unconditional (see route_score_block)
 #pragma unroll
@@ -270,6 +270,8 @@ __device__ inline double rms_scale_vec(const RouteArgs& a, int t, double* sh, fl
     nw[j][0] = n0.x; nw[j][1] = n0.y; nw[j][2] = n0.z; nw[j][3] = n0.w;
     nw[j][4] = n1.x; nw[j][5] = n1.y; nw[j][6] = n1.z; nw[j][7] = n1.w;
   }
+}
+__device__ inline double rms_scale_of(const RouteArgs& a, double* sh, const float (&rr)[2][8]) {
   double ss = 0.0, dummy = 0.0;
 #pragma unroll
   for (int j = 0; j < 2; j++) {
@@ -279,6 +281,11 @@ __device__ inline double rms_scale_vec(const RouteArgs& a, int t, double* sh, fl
   }
   block_sum2(ss, dummy, sh);
   return 1.0 / sqrt(ss / (double)a.H + (double)a.eps);
+}
+__device__ inline double rms_scale_vec(const RouteArgs& a, int t, double* sh, float (&rr)[2][8],
+                                       float (&nw)[2][8]) {
+  rms_load_vec(a, t, rr, nw);
+  return rms_scale_of(a, sh, rr);
 }
 
 // Scoring.  Grid (E, T), 256 threads: block (e, t) computes the logit, score
