@@ -254,8 +254,8 @@ __device__ __noinline__ float exact_logit_wave(RouteSrc src, int e, bool& ok) {
 // threads: thread tid loads the residual and norm weight of columns
 // 2048 j + 8 tid .. +7 (into rr, nw; rms_load_vec) and the block sums the
 // squares along a fixed tree in binary64 (rms_scale_of); returns
-// 1 / sqrt(mean + eps).  Every block that calls it for a token gets the same
-// bits.  The two halves let a caller request other data between them.
+// 1 / sqrt(mean + eps).  Every block that calls them for a token gets the
+// same bits.  Callers request other data between the two.
 __device__ inline void rms_load_vec(const RouteArgs& a, int t, float (&rr)[2][8], float (&nw)[2][8]) {
   const int tid = threadIdx.x;
   const int nslab = a.H / 2048;  // 1 or 2; the loads are unconditional (see route_score_block)
@@ -282,11 +282,6 @@ __device__ inline double rms_scale_of(const RouteArgs& a, double* sh, const floa
   block_sum2(ss, dummy, sh);
   return 1.0 / sqrt(ss / (double)a.H + (double)a.eps);
 }
-__device__ inline double rms_scale_vec(const RouteArgs& a, int t, double* sh, float (&rr)[2][8],
-                                       float (&nw)[2][8]) {
-  rms_load_vec(a, t, rr, nw);
-  return rms_scale_of(a, sh, rr);
-}
 
 // Scoring.  Grid (E, T), 256 threads: block (e, t) computes the logit, score
 // and key interval of expert e for token t.  VEC (hidden % 2048 == 0, fp16
@@ -310,8 +305,15 @@ __device__ inline void route_score_block(const RouteArgs& a, int e, int t) {
   // the expert's bias, requested now through the scalar cache (read at the
   // end, it was a round trip of its own)
   const float bias_e = __int_as_float(load_scalar_i32((const int32_t*)a.bias, e));
+  // Normalised input: the residual and norm weight of the thread's own
+  // columns, requested before the router weights so that the norm's wait
+  // (the vector memory counter retires in order) does not wait for them; the
+  // columns of all threads cover the row exactly once, so the sum of squares
+  // comes from the same registers.
+  float rr[kMaxSlab][8], nw[kMaxSlab][8];
+  if (NORM && VEC) rms_load_vec(a, t, rr, nw);
   uint4 wv[kMaxSlab], xv[kMaxSlab];
-  if (VEC) {  // router weights first, then the input
+  if (VEC) {  // router weights, then (not normalised) the input
     const uint4* wp = (const uint4*)((const uint16_t*)a.W + (size_t)e * a.H);
 #pragma unroll
     for (int j = 0; j < kMaxSlab; j++) wv[j] = wp[256 * min(j, nslab - 1) + tid];
@@ -325,13 +327,9 @@ __device__ inline void route_score_block(const RouteArgs& a, int e, int t) {
       asm volatile("" ::"v"(wv[0].x), "v"(wv[1].x), "v"(xv[0].x), "v"(xv[1].x), "s"(bias_e));
     }
   }
-  // Normalised input: the residual and norm weight of the thread's own
-  // columns are loaded once, up front; the columns of all threads cover the
-  // row exactly once, so the sum of squares comes from the same registers.
-  float rr[kMaxSlab][8], nw[kMaxSlab][8];
   double nscale = 1.0;
   if (NORM && VEC) {
-    nscale = rms_scale_vec(a, t, sh, rr, nw);
+    nscale = rms_scale_of(a, sh, rr);
   } else if (NORM) {  // generic shapes: strided columns
     double ss = 0.0, dummy = 0.0;
     for (int c = tid; c < a.H; c += 256) {
