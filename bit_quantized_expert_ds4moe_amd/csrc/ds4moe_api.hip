@@ -688,11 +688,16 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     {
       ProfScope prof(DS4MOE_K_DOWN, st, !b1);
       const bool q2k = q2k_grouped_fast(g);
+      const bool q4d = !q2k && q4k_grouped_dn(g);
       if (q2k && !b1) {  // small items and the rest
         launch_k(k_grouped_down_q2k<1>, dim3(g.H / kDNF, E < TK ? E : TK), dim3(kDW * 64), 0, st, g);
         if (large) launch_k(k_grouped_down_q2k<4>, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
       }
-      if (!q2k && !b1)  // every item
+      if (q4d && !b1) {
+        launch_k(k_grouped_down_q4k<1>, dim3(g.H / kDNF, E < TK ? E : TK), dim3(kDW * 64), 0, st, g);
+        if (large) launch_k(k_grouped_down_q4k<4>, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
+      }
+      if (!q2k && !q4d && !b1)  // every item
         launch_k(k_grouped_down, dim3(s.hidden / kNT, mi, g.ksplit_d), dim3(256), 0, st, g);
       else if (sh)  // the shared expert's items
         launch_k(k_grouped_down, dim3(s.hidden / kNT, ns, g.ksplit_d), dim3(256), 0, st, gs);

@@ -380,6 +380,12 @@ __host__ __device__ inline bool q2k_grouped_fast(const GroupArgs& a) {
          iq2_grouped_fast(a);
 }
 
+// The pipelined Q4_K down follows each 64-column chunk's binary16 exponent,
+// so it takes the rows of any grouped gate/up kernel.
+__host__ __device__ inline bool q4k_grouped_dn(const GroupArgs& a) {
+  return a.qt_d == DS4MOE_Q4_K && a.H % kDNF == 0 && a.I % 512 == 0 && a.I <= 8192;
+}
+
 __host__ __device__ inline bool q80_shared_fast(const GroupArgs& a) {
   return a.sh_qt_g == DS4MOE_Q8_0 && a.sh_qt_u == DS4MOE_Q8_0 && a.sh_I % kGNF == 0 && a.H % 64 == 0;
 }
@@ -1122,9 +1128,9 @@ __global__ __launch_bounds__(256) void k_grouped_down(GroupArgs a) {
   if (item >= *a.n_items) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   const bool shr = e == a.E;
-  // routed Q2_K items run in k_grouped_down_q2k; only the shared expert is
-  // split along K (grid z)
-  if (!shr && (q2k_grouped_fast(a) || blockIdx.z > 0)) return;
+  // routed Q2_K and Q4_K items run in k_grouped_down_q2k / _q4k; only the
+  // shared expert is split along K (grid z)
+  if (!shr && (q2k_grouped_fast(a) || q4k_grouped_dn(a) || blockIdx.z > 0)) return;
   const int I = shr ? a.sh_I : a.I;
   const int qd = shr ? a.sh_qt_d : a.qt_d;
   const uint8_t* D = shr ? a.sh_down : a.down;
@@ -1531,6 +1537,226 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q2k(GroupArgs a) {
         f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, shi), bm, z, 0, 0, 0);
         t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, slo), bm, t, 0, 0, 0);
         acc[mt] -= fmin * t;
+      }
+    }
+    // h of stage s + 1 into the other buffers (after the last stage: unused)
+    if constexpr ((R & 1) == 0) h_store(1, H1);
+    else h_store(0, H0);
+    __syncthreads();
+  };
+  for (int s0 = 0; s0 < nst; s0 += 4) {
+    const int sn = s0 + 4 < nst ? s0 + 4 : s0;
+    const int enext0 = load_scalar_i32(ex32, sn / 2), enext1 = load_scalar_i32(ex32, sn / 2 + 1);
+    stage(s0, std::integral_constant<int, 0>{});
+    stage(s0 + 1, std::integral_constant<int, 1>{});
+    stage(s0 + 2, std::integral_constant<int, 2>{});
+    stage(s0 + 3, std::integral_constant<int, 3>{});
+    ecur0 = enext0;
+    ecur1 = enext1;
+  }
+  const float fin = ldexpf(dp * 16777216.0f, -ep);
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      if (mt >= mtiles) break;
+      const int m = 16 * mt + 4 * q + r;
+      if (m < nrows) a.y[(size_t)(row0 + m) * a.H + n] = acc[mt][r] * fin;
+    }
+}
+
+// down for routed items with Q4_K down weights: software-pipelined like
+// k_grouped_down_q2k (same grid, h staging, weight ring and barriers).  A
+// Q4_K block (fp16 d and dmin, twelve bytes of the 6-bit scales sc_j and mins
+// m_j of its eight 32-column groups, 128 code bytes) spans two 128-column
+// stages: stage half hf holds code chunks 2hf and 2hf + 1, and byte l of
+// chunk c carries column 64c + l in its low nibble (group 2c) and column
+// 64c + 32 + l in its high nibble (group 2c + 1).  Lane quarter q takes bytes
+// 8q .. 8q+7 of each chunk: for each of the stage's four groups the B
+// fragment of one f16 16x16x32 MFMA step (columns 32j + 8q .. +7 of the
+// stage), with the group's scale folded in:
+//   B = q * sc as a binary16 subnormal (q * sc <= 945: q sc 2^-24, exact),
+//   A = the SwiGLU rows as binary16 high and low parts (two MFMAs).
+// The accumulators hold the sum in units of the current block's d and of
+// 2^-e, e the binary16 exponent of the current 64-column chunk (the grouped
+// gate/up kernels store one per row and 64-feature range, the same for all
+// rows of an item): a new block rescales them by the ratio of the d, a new
+// exponent by a power of two (exact).  The mins, per chunk: one f16 16x16x16
+// MFMA pair (hi, lo) of the stage's eight 16-feature sums of h against the
+// chunk's mins (m_j as binary16 subnormals, in quarter c only: its K slots
+// hold the chunk's four sums), scaled by dmin / d.
+struct Q4kSub {
+  uint4 hd;                // the block header: d | dmin << 16, scale and min bytes
+  uint32_t c0, c1, c2, c3;  // the lane's code bytes of chunks 2hf and 2hf + 1
+};
+
+__device__ inline void q4k_sub_load(const uint8_t* __restrict__ row, int s, int q, Q4kSub& o) {
+  const uint8_t* blk = row + kQ4kBytes * (s >> 1);
+  const int hf = s & 1;
+  o.hd = *(const uint4*)blk;
+  const uint2 a = *(const uint2*)(blk + 16 + 64 * hf + 8 * q);
+  const uint2 b = *(const uint2*)(blk + 16 + 64 * hf + 32 + 8 * q);
+  o.c0 = a.x;
+  o.c1 = a.y;
+  o.c2 = b.x;
+  o.c3 = b.y;
+}
+
+// MT = 1: the small items (at most 16 rows, listed first); MT = 4: the rest.
+template <int MT>
+__global__ __launch_bounds__(kDW * 64) void k_grouped_down_q4k(GroupArgs a) {
+  constexpr int kRows = 16 * MT;
+  constexpr int kHC = kRows * 32;                          // h chunks of a stage (hi, lo)
+  constexpr int kHJ = (kHC + kDW * 64 - 1) / (kDW * 64);  // per thread
+  constexpr int kSC = kRows * 2;                           // sum chunks (hi, lo)
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ u32x4_t ht[2][kHC];  // row m: [hi 16 chunks][lo 16 chunks], chunk c at c ^ (m & 15)
+  __shared__ u32x4_t st[2][kSC];  // row m: [8 sums hi][8 sums lo]
+  const int n_small = a.n_items[1];
+  const int item = (MT == 1 ? 0 : n_small) + (int)blockIdx.y;
+  if (item >= (MT == 1 ? n_small : a.n_items[0])) return;
+  const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
+  if (e >= a.E) return;  // shared-expert items run in k_grouped_down
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = lane >> 4;
+  const int n = blockIdx.x * kDNF + 16 * w + (lane & 15);
+  const int rowbytes = (a.I / 256) * kQ4kBytes;
+  const uint8_t* drow = a.down + ((size_t)e * a.H + n) * rowbytes;
+  const int nst = a.I / 128;  // a multiple of 4
+  const int mtiles = (nrows + 15) >> 4;
+  // h tile loads as in k_grouped_down_q2k: chunk c = tid + 512 j -> row
+  // c >> 5, part (c >> 4) & 1, chunk c & 15; sum chunk cs = tid mod 2 kRows.
+  // Rows past the item repeat row 0 (never stored).
+  struct HV {
+    u32x4_t v[kHJ];
+    u32x4_t sm;
+  };
+  const uint16_t* hsrc[kHJ];
+#pragma unroll
+  for (int j = 0; j < kHJ; j++) {
+    const int c = (tid + kDW * 64 * j) & (kHC - 1), m = c >> 5;
+    const size_t r = (size_t)(row0 + (m < nrows ? m : 0));
+    hsrc[j] = ((c >> 4) & 1 ? a.hl : a.hh) + r * a.I + 8 * (c & 15);
+  }
+  const int cs = tid & (kSC - 1), ms = cs >> 1;
+  const uint16_t* ssrc = ((cs & 1) ? a.hsl : a.hsh) + (size_t)(row0 + (ms < nrows ? ms : 0)) * (a.I / 16);
+  auto h_load = [&](int s) {
+    HV r;
+#pragma unroll
+    for (int j = 0; j < kHJ; j++) r.v[j] = *(const u32x4_t*)(hsrc[j] + 128 * s);
+    r.sm = *(const u32x4_t*)(ssrc + 8 * s);
+    return r;
+  };
+  auto h_store = [&](int buf, const HV& h) {
+#pragma unroll
+    for (int j = 0; j < kHJ; j++) {
+      const int c = (tid + kDW * 64 * j) & (kHC - 1), m = c >> 5;
+      ht[buf][m * 32 + (c & 16) + ((c & 15) ^ (m & 15))] = h.v[j];
+    }
+    st[buf][cs] = h.sm;
+  };
+  // in-order returns: weights of stages 0 and 1, h of stages 0 and 1, then
+  // the weights of stage 2
+  Q4kSub W[4];
+  q4k_sub_load(drow, 0, q, W[0]);
+  q4k_sub_load(drow, 1, q, W[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  HV H0 = h_load(0), H1 = h_load(1);
+  __builtin_amdgcn_sched_barrier(0);
+  q4k_sub_load(drow, 2, q, W[2]);
+  __builtin_amdgcn_sched_barrier(0);
+  h_store(0, H0);
+  __syncthreads();
+
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float dp = 1.0f;  // d of the current block
+  // exponent bytes of the item's first row (64-feature range r at byte r),
+  // read through the scalar cache four stages ahead
+  const int32_t* ex32 = (const int32_t*)(a.hexp + (size_t)row0 * (a.I / 64));
+  int ecur0 = load_scalar_i32(ex32, 0), ecur1 = load_scalar_i32(ex32, 1);
+  int ep = (int8_t)(ecur0 & 0xFF);  // exponent the accumulators are in
+  auto stage = [&](int s, auto Rc) {
+    constexpr int R = decltype(Rc)::value;
+    constexpr int hf = R & 1;
+    if constexpr ((R & 1) == 0) H0 = h_load(min(s + 2, nst - 1));
+    else H1 = h_load(min(s + 2, nst - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    q4k_sub_load(drow, s + 3 < nst ? s + 3 : s - 1, q, W[(R + 3) & 3]);
+    __builtin_amdgcn_sched_barrier(0);
+    const Q4kSub& cw = W[R];
+    const float dv = f16_bits_to_f32(cw.hd.x & 0xFFFFu);
+    const float d = dv != 0.0f ? dv : 1.0f;
+    const float rd = __builtin_amdgcn_rcpf(d);  // within 1 ulp
+    const float fmin = f16_bits_to_f32(cw.hd.x >> 16) * rd;
+    if constexpr (hf == 0) {  // a block starts: sums in units of its d
+      const float r = dp * rd;
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) acc[mt] *= r;
+      dp = d;
+    }
+    const u32x4_t* hb = ht[R & 1];
+    const u32x4_t* sb = st[R & 1];
+    const uint32_t ew = R < 2 ? (uint32_t)ecur0 : (uint32_t)ecur1;
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      // the chunk's exponent: 64-feature range 2s + c
+      const int es = (int8_t)((ew >> (16 * (R & 1) + 8 * c)) & 0xFFu), de = es - ep;
+      ep = es;
+      if (de != 0) {
+        const float r = ldexpf(1.0f, de);
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) acc[mt] *= r;
+      }
+      // code bytes in 16-bit lanes: (b0, b1), (b2, b3), (b4, b5), (b6, b7)
+      const uint32_t cx = c ? cw.c2 : cw.c0, cy = c ? cw.c3 : cw.c1;
+      const uint32_t P[4] = {vperm(0u, cx, 0x0C010C00u), vperm(0u, cx, 0x0C030C02u),
+                             vperm(0u, cy, 0x0C010C00u), vperm(0u, cy, 0x0C030C02u)};
+#pragma unroll
+      for (int hi = 0; hi < 2; hi++) {
+        const int jl = 2 * c + hi;  // group of the stage, 4 hf + jl of the block
+        int sc, mn;
+        q4k_scale_min(cw.hd, 4 * hf + jl, sc, mn);
+        const uint32_t scm = dv != 0.0f ? (uint32_t)sc : 0u;
+        // low nibbles: q sc in each 16-bit lane; high nibbles: 16 q sc
+        // (below 2^14), shifted down by 4.  The unsigned 24-bit multiply:
+        // the masked high nibbles reach bit 23, a sign bit to the signed one
+        uint32_t bw[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          bw[i] = hi ? __umul24(P[i] & 0x00F000F0u, scm) >> 4 : __umul24(P[i] & 0x000F000Fu, scm);
+        const f16x8_t bf = __builtin_bit_cast(f16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+          if (MT > 1 && mt >= mtiles) break;
+          const int m = 16 * mt + (lane & 15);
+          const int ci = (4 * jl + q) ^ (m & 15);
+          const f16x8_t ahi = __builtin_bit_cast(f16x8_t, hb[m * 32 + ci]);
+          const f16x8_t alo = __builtin_bit_cast(f16x8_t, hb[m * 32 + 16 + ci]);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bf, acc[mt], 0, 0, 0);
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bf, acc[mt], 0, 0, 0);
+        }
+      }
+      // the chunk's mins: sums 4c .. 4c+3 of the stage (quarter c's K slots;
+      // sums 4c, 4c+1 in group 2c, 4c+2, 4c+3 in group 2c+1)
+      {
+        int scx, m0, m1;
+        q4k_scale_min(cw.hd, 4 * hf + 2 * c, scx, m0);
+        q4k_scale_min(cw.hd, 4 * hf + 2 * c + 1, scx, m1);
+        const uint32_t w0 = q == c ? (uint32_t)m0 * 0x00010001u : 0u;
+        const uint32_t w1 = q == c ? (uint32_t)m1 * 0x00010001u : 0u;
+        const f16x4_t bm = __builtin_bit_cast(f16x4_t, make_uint2(w0, w1));
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+          if (MT > 1 && mt >= mtiles) break;
+          const int m = 16 * mt + (lane & 15);
+          const uint2* sp = (const uint2*)&sb[2 * m];
+          const uint2 shi = sp[q & 1], slo = sp[2 + (q & 1)];
+          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, shi), bm, z, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, slo), bm, t, 0, 0, 0);
+          acc[mt] -= fmin * t;
+        }
       }
     }
     // h of stage s + 1 into the other buffers (after the last stage: unused)

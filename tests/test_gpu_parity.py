@@ -714,6 +714,41 @@ def test_grouped_pipelined_kernels_zero_scales():
     _grouped_fast_case(True)
 
 
+@pytest.mark.parametrize("mag", [0.0, 200.0])
+@pytest.mark.parametrize("gu", ["q4k", "iq2"])
+def test_grouped_q4k_down_all_outputs(gu, mag):
+    # the pipelined Q4_K down (hidden 512, inter 512: four 128-column stages,
+    # two Q4_K blocks per row) behind the Q4_K gate/up (one binary16 exponent
+    # per 64 features) and behind the pipelined IQ2_XXS gate/up (one per 128):
+    # 160 tokens x top-4 over 16 experts, Zipf(1.1) routing, so 64-row items,
+    # ragged pieces and small items; every output checked.  mag > 0: eight
+    # channels of every token at +-mag, which puts |h| of every 64-feature
+    # range above 2^11, at maxima between 2^12 and 2^16: the items' ranges
+    # take different power-of-two exponents and the accumulators follow them
+    # from chunk to chunk.
+    from ds4gen.device import make_layer, host_experts
+    qts = (g.Q4_K, g.Q4_K, g.Q4_K) if gu == "q4k" else (g.IQ2_XXS, g.IQ2_XXS, g.Q4_K)
+    w = g.Workload("grouped-q4k", 17, 160, 512, 512, 16, 4, *qts, "bf16", "f16")
+    say("grouped q4k down, gate/up %s, outliers %g" % (gu, mag))
+    lt = make_layer(w, 0)
+    ids, wts = g.zipf_routing(17, w.T, w.E, w.K)
+    counts = np.bincount(ids.ravel(), minlength=w.E)
+    assert (counts > 64).any() and ((counts > 0) & (counts <= 16)).any()
+    x = outlier_x(w, w.T, mag) if mag else g.activations(w, n_tok=w.T)
+    shp = shape_of(w)
+    ws, nb = workspace(shp, w.T)
+    out = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+    xd, idd, wd = dev(x), dev(ids), dev(wts)
+    ds4.expert_ffn(shp, experts_of(lt, w), None, ptr(xd), ds4.BF16, w.T, ptr(idd), ptr(wd),
+                   ptr(out), None, ptr(ws), nb, stream())
+    check_clean(ws)
+    want = oracle.moe_ffn(x, "bf16", ids, wts, host_experts(w, 0, np.unique(ids)), qts, w.H, w.I,
+                          w.E, grid=g.grid(w.seed), tokens=np.arange(w.T))
+    err = max_rel_err(out.cpu().numpy(), want)
+    say("  max|err|/rms = %g" % err)
+    assert err <= TOL_FP32
+
+
 # --------------------------------------------------------------------------
 # importance statistics (ds4moe_expert_ffn_imatrix)
 # --------------------------------------------------------------------------
