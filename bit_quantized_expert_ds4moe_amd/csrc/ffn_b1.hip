@@ -613,6 +613,10 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
   // the expert id and gate first: the weight addresses wait for the id
   int e = shw ? 0 : load_scalar_i32(ids, k);
   const float wk = shw ? 1.0f : __int_as_float(load_scalar_i32((const int32_t*)wts, k));
+  // the residual rows this workgroup adds to, requested before anything else:
+  // read at the end, their round trip came after all the arithmetic
+  float res_in = 0.0f;
+  if (residual && tid < kDnBlockRows) res_in = residual[blockIdx.x * kDnBlockRows + tid];
   // Lane chunk order of the 64 values a lane consumes: chunk G0 + 8s + m4 of
   // its slot (16 bytes each) holds values 16s + 4m4 .. +3.
   const int G0 = 64 * b + 32 * hq + 4 * p;
@@ -764,7 +768,7 @@ __global__ __launch_bounds__(SH ? kDnThreadsSh : kDnThreads) void k_down_q2k_b1(
                 (part[4][tid] + part[5][tid]);
     if (SH) acc += part[kSlots - 1][tid];
     const int row = blockIdx.x * kDnBlockRows + tid;
-    if (residual) residual[row] += acc;
+    if (residual) residual[row] = res_in + acc;
     else out[row] = acc;
   }
   if (bad_id && lane == 0 && blockIdx.x == 0 && rh == 0) raise_fault(status, DS4MOE_FAULT_BAD_ID);

@@ -243,6 +243,10 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4k_b1(const float* __restr
   if (residual) residual += (size_t)tok * kH;
   int e = load_scalar_i32(ids, k);
   const float wk = __int_as_float(load_scalar_i32((const int32_t*)wts, k));
+  // the residual rows this workgroup adds to, requested before anything else:
+  // read at the end, their round trip came after all the arithmetic
+  float res_in = 0.0f;
+  if (residual && tid < kDnBlockRows) res_in = residual[blockIdx.x * kDnBlockRows + tid];
   static_assert(kChunks == 4 * kDnThreads, "four h chunks per thread");
   const float4* hg = (const float4*)h + tid;
   const float4 hc0 = hg[0], hc1 = hg[kDnThreads], hc2 = hg[2 * kDnThreads], hc3 = hg[3 * kDnThreads];
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down_q4k_b1(const float* __restr
     float acc = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) +
                 (part[4][tid] + part[5][tid]);
     const int row = blockIdx.x * kDnBlockRows + tid;
-    if (residual) residual[row] += acc;
+    if (residual) residual[row] = res_in + acc;
     else out[row] = acc;
   }
   if (bad_id && lane == 0 && blockIdx.x == 0 && rh == 0) raise_fault(status, DS4MOE_FAULT_BAD_ID);
