@@ -40,8 +40,8 @@ GATEUP_TRAFFIC = {
     "sources": ("bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "d27256305c2738a7a231627ba4ac43fe830359c7dcbce68ed41b49b4121b568c",
-    "bytes": 26302994,
+    "sha256": "beb81eface1de7703d8cbbdac1963520f9b80627b9773c42318bf392d5e76e50",
+    "bytes": 26303165,
 }
 
 
@@ -52,8 +52,8 @@ Q4K_GATEUP_TRAFFIC = {
                 "bit_quantized_expert_ds4moe_amd/csrc/ffn_b1.hip",
                 "bit_quantized_expert_ds4moe_amd/csrc/dev_common.h",
                 "bit_quantized_expert_ds4moe_amd/csrc/route.hip"),
-    "sha256": "dea1a1cad2fb6b936c38032853da0926072dabbf4da4f2882cffa68d64b05d41",
-    "bytes": 56945783,
+    "sha256": "10e6891d6d42c10bcd30e9c298e3dd506169537d13253b637dc5db040c099603",
+    "bytes": 56954311,
 }
 
 
