@@ -714,9 +714,10 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       // in part; after the per-token matvecs k_add_shared adds it to their output
       const bool add_sh = sh && b1;
       if (!b1)
-        launch_k(k_grouped_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+        launch_k(k_grouped_combine, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, st,
                  (const float*)g.y, (const int32_t*)inv, wts, T, K, s.hidden, sh ? 1 : 0, out,
-                 residual, (const float*)g.part, g.ksplit_d);
+                 residual, (const float*)g.part, g.ksplit_d,
+                 (((uintptr_t)out | (uintptr_t)residual) & 15) == 0 ? 1 : 0);
       if (add_sh)
         launch_k(k_add_shared, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                  (const float*)g.y, (const float*)g.part, g.ksplit_d, TK, T, s.hidden,

@@ -1787,26 +1787,63 @@ __global__ __launch_bounds__(kDW * 64) void k_grouped_down_q4k(GroupArgs a) {
 
 // out[t] = sum_k w[t][k] y[inv[t*K+k]] (+ the shared row) (+ residual), fixed
 // order.  The shared row (with_shared) is y[T*K + t], or with ksplit > 1 the
-// sum of its K shares in part ([ksplit][T][H]) in share order.
+// sum of its K shares in part ([ksplit][T][H]) in share order.  Four
+// consecutive columns per thread (16-byte loads of y); H is a multiple of 256,
+// so a wave covers 256 columns of one token and reads the token's rows and
+// gates through the scalar cache.  vec_out: out and residual are 16-byte
+// aligned and take 16-byte accesses too.
 __global__ void k_grouped_combine(const float* y, const int32_t* inv, const float* wts, int T, int K,
                                   int H, int with_shared, float* out, float* residual,
-                                  const float* part, int ksplit) {
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)T * H) return;
-  const int t = (int)(idx / H), c = (int)(idx % H);
-  float sh = 0.0f;
+                                  const float* part, int ksplit, int vec_out) {
+  const size_t idx = 4 * ((size_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (idx >= (size_t)T * H) return;  // whole waves (T * H is a multiple of 256)
+  const int t = __builtin_amdgcn_readfirstlane((int)(idx / H)), c = (int)(idx % H);
+  float4 sh = make_float4(0.f, 0.f, 0.f, 0.f);
   if (with_shared) {
     if (ksplit == 1) {
-      sh = y[((size_t)T * K + t) * H + c];
+      sh = *(const float4*)(y + ((size_t)T * K + t) * H + c);
     } else {
-      for (int z = 0; z < ksplit; z++) sh += part[(size_t)z * T * H + idx];
+      for (int z = 0; z < ksplit; z++) {
+        const float4 v = *(const float4*)(part + (size_t)z * T * H + idx);
+        sh.x += v.x;
+        sh.y += v.y;
+        sh.z += v.z;
+        sh.w += v.w;
+      }
     }
   }
-  float acc = 0.0f;
-  for (int k = 0; k < K; k++) acc = fmaf(wts[t * K + k], y[(size_t)inv[t * K + k] * H + c], acc);
-  if (with_shared) acc += sh;
-  if (residual) residual[idx] += acc;
-  else out[idx] = acc;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < K; k++) {
+    const float wk = __int_as_float(load_scalar_i32((const int32_t*)wts, t * K + k));
+    const int r = load_scalar_i32(inv, t * K + k);
+    const float4 v = *(const float4*)(y + (size_t)r * H + c);
+    acc.x = fmaf(wk, v.x, acc.x);
+    acc.y = fmaf(wk, v.y, acc.y);
+    acc.z = fmaf(wk, v.z, acc.z);
+    acc.w = fmaf(wk, v.w, acc.w);
+  }
+  if (with_shared) {
+    acc.x += sh.x;
+    acc.y += sh.y;
+    acc.z += sh.z;
+    acc.w += sh.w;
+  }
+  float* dst = residual ? residual : out;
+  if (vec_out) {
+    float4 o = acc;
+    if (residual) {
+      const float4 r = *(const float4*)(residual + idx);
+      o = make_float4(r.x + acc.x, r.y + acc.y, r.z + acc.z, r.w + acc.w);
+    }
+    *(float4*)(dst + idx) = o;
+  } else {
+    const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      if (residual) residual[idx + u] += a4[u];
+      else out[idx + u] = a4[u];
+    }
+  }
 }
 
 // Importance statistics of the routed experts' inputs (DS4C2 =
