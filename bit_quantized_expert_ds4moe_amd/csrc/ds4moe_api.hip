@@ -70,7 +70,7 @@ Layout layout_for(const ds4moe_shape& s, int32_t T) {
   L.wts = take(t * K * 4);
   L.xn = take(t * H * 2);
   L.x16 = take(t * H * 2);
-  L.perm = take((E + (E + 1) + 2 * t * K + 3 * (size_t)max_items((int)E, (int)(t * K), (int)t, true) + 64) * 4);
+  L.perm = take((E + (E + 1) + 2 * t * K + 3 * (size_t)max_items_upto((int)E, (int)K, (int)t) + 64) * 4);
   L.h = take(np * I * 4);
   L.y = take(np * H * 4);
   L.hb = take(np * I * 2);
@@ -650,8 +650,8 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
     }
     g.status = status;
     g.sh_tail = 0;
-    // at most 16 tokens: at most 16 rows per expert, so no 64-row items
-    const bool large = T > 16;
+    // items of more than 16 rows only with 64-row pieces and more than 16 tokens
+    const bool large = item_rows(T) > 16 && T > 16;
     // kernels that see only the shared expert's rows: grid rows over its
     // work items, the last ns of the list
     const int ns = (T + kMC - 1) / kMC;
@@ -667,7 +667,7 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
         launch_k(k_x_to_f16, dim3(T), dim3(256), 0, st, g.x, g.H, g.K, (const int32_t*)inv,
                  at<uint16_t>(ws, L.x16), at<int8_t>(ws, L.xexp));
       if (iq2 && !b1) {  // small items (at most one per expert) and the rest
-        launch_k(k_grouped_gateup_iq2_small, dim3(g.I / kGNF, E < TK ? E : TK), dim3(kGW * 64), 0, st, g);
+        launch_k(k_grouped_gateup_iq2_small, dim3(g.I / kGNF, max_small_items(E, TK, T)), dim3(kGW * 64), 0, st, g);
         if (large) launch_k(k_grouped_gateup_iq2<4>, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
       }
       if (q4k && !b1)
@@ -690,11 +690,11 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
       const bool q2k = q2k_grouped_fast(g);
       const bool q4d = !q2k && q4k_grouped_dn(g);
       if (q2k && !b1) {  // small items and the rest
-        launch_k(k_grouped_down_q2k<1>, dim3(g.H / kDNF, E < TK ? E : TK), dim3(kDW * 64), 0, st, g);
+        launch_k(k_grouped_down_q2k<1>, dim3(g.H / kDNF, max_small_items(E, TK, T)), dim3(kDW * 64), 0, st, g);
         if (large) launch_k(k_grouped_down_q2k<4>, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
       }
       if (q4d && !b1) {
-        launch_k(k_grouped_down_q4k<1>, dim3(g.H / kDNF, E < TK ? E : TK), dim3(kDW * 64), 0, st, g);
+        launch_k(k_grouped_down_q4k<1>, dim3(g.H / kDNF, max_small_items(E, TK, T)), dim3(kDW * 64), 0, st, g);
         if (large) launch_k(k_grouped_down_q4k<4>, dim3(g.H / kDNF, mi), dim3(kDW * 64), 0, st, g);
       }
       if (!q2k && !q4d && !b1)  // every item

@@ -34,6 +34,13 @@
 namespace ds4 {
 
 constexpr int kMC = 64;   // rows (pairs) per work item
+// Routed work items of calls with at most kSmallPieceMaxT tokens are cut into
+// 16-row pieces, so that every item runs in the small-item kernels (one
+// 16-row tile, many workgroups per expert) instead of a few 64-row items
+// setting the pace; larger calls use 64-row pieces (each weight decoded once
+// per 64 rows).
+constexpr int kSmallPieceMaxT = 64;
+__host__ __device__ inline int item_rows(int T) { return T <= kSmallPieceMaxT ? 16 : kMC; }
 constexpr int kNT = 64;   // output features per block (16 per wave)
 constexpr int kGW = 8;             // pipelined IQ2_XXS gate/up: waves per block
 constexpr int kGNF = 16 * kGW;     // and features per block
@@ -49,12 +56,13 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* ids, int n, int
                                                   uint32_t* status, int T, int with_shared,
                                                   int32_t* items, int32_t* n_items);
 
-// Work list: items (e, row0, nrows) for every expert with pairs (64-row
-// pieces), then the shared expert's rows (e == E).  Items of at most 16 rows
-// (an expert's last piece) come first, in ascending expert order, so that a
-// kernel specialised for one 16-row tile can take them; n_items[0] is the
-// number of items, n_items[1] the number of those small ones.  One wave of 64
-// threads, four experts per lane, prefix sums over the lanes.
+// Work list: items (e, row0, nrows) for every expert with pairs (pieces of
+// item_rows(T) rows), then the shared expert's rows (e == E, 64-row pieces).
+// Items of at most 16 rows (with 64-row pieces an expert's last piece) come
+// first, in ascending expert order, so that a kernel specialised for one
+// 16-row tile can take them; n_items[0] is the number of items, n_items[1]
+// the number of those small ones.  One wave of 64 threads, four experts per
+// lane, prefix sums over the lanes.
 __device__ inline int wave_prefix_excl(int v, int& total) {
   int incl = v;
 #pragma unroll
@@ -71,14 +79,15 @@ __device__ inline int wave_prefix_excl(int v, int& total) {
 __device__ void make_items_wave(const int32_t* counts, const int32_t* offsets, int E, int TK, int T,
                                 int with_shared, int32_t* items, int32_t* n_items) {
   const int lane = threadIdx.x & 63;
+  const int P = item_rows(T);
   int cnt[4], nsm = 0, nlg = 0;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int e = 4 * lane + j;
     cnt[j] = e < E ? counts[e] : 0;
-    const int rem = cnt[j] % kMC;
-    nsm += (rem > 0 && rem <= 16) ? 1 : 0;
-    nlg += cnt[j] / kMC + (rem > 16 ? 1 : 0);
+    const int full = cnt[j] / P, rem = cnt[j] % P;
+    nsm += (P <= 16 ? full : 0) + ((rem > 0 && rem <= 16) ? 1 : 0);
+    nlg += (P > 16 ? full : 0) + (rem > 16 ? 1 : 0);
   }
   int small_total, large_total;
   int ps = wave_prefix_excl(nsm, small_total);
@@ -91,8 +100,8 @@ __device__ void make_items_wave(const int32_t* counts, const int32_t* offsets, i
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     const int e = 4 * lane + j;
-    for (int m0 = 0; m0 < cnt[j]; m0 += kMC) {
-      const int nr = min(kMC, cnt[j] - m0);
+    for (int m0 = 0; m0 < cnt[j]; m0 += P) {
+      const int nr = min(P, cnt[j] - m0);
       if (nr <= 16) put(ps++, e, offsets[e] + m0, nr);
       else put(pl++, e, offsets[e] + m0, nr);
     }
@@ -138,7 +147,22 @@ __global__ void k_add_shared(const float* y, const float* part, int ks, int TK, 
 }
 
 inline int max_items(int E, int TK, int T, bool shared) {
-  return E + (TK + kMC - 1) / kMC + (shared ? (T + kMC - 1) / kMC : 0);
+  const int P = item_rows(T);
+  return E + (TK + P - 1) / P + (shared ? (T + kMC - 1) / kMC : 0);
+}
+// The most work items a call of at most T tokens lists (16-row pieces can
+// list more items at 64 tokens than 64-row pieces at 65): the workspace size,
+// which so stays monotone in the token count.
+inline int max_items_upto(int E, int K, int T) {
+  const int t16 = T < kSmallPieceMaxT ? T : kSmallPieceMaxT;
+  const int m16 = max_items(E, t16 * K, t16, true), m = max_items(E, T * K, T, true);
+  return m16 > m ? m16 : m;
+}
+// Grid rows of the small-item kernels: at most one small item per expert
+// with 64-row pieces; with 16-row pieces every routed item is small.
+inline int max_small_items(int E, int TK, int T) {
+  const int m = item_rows(T) <= 16 ? E + (TK + 15) / 16 : E;
+  return m < TK ? m : TK;
 }
 
 struct GroupArgs {
