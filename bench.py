@@ -601,7 +601,7 @@ def bench_batched(args, which):
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
         "roofline": {"bound": "hbm", "kernel": (("grouped Q4_K gate/up: k_x_to_f16 + k_grouped_gateup_q4k"
                                                  if w.gate_qt == g.Q4_K else
-                                                 "grouped IQ2_XXS gate/up: k_x_to_f16 + k_grouped_gateup_iq2_small + k_grouped_gateup_iq2<4>")
+                                                 "grouped IQ2_XXS gate/up: k_x_to_f16 + k_grouped_gateup_iq2_all")
                                                 if prefill else batched_gateup_kernel(w, T)),
                      "achieved": round(gu_bytes / gu_s / 1e9, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gu_bytes / gu_s / 1e9 / PEAK_HBM_GBS, 4),

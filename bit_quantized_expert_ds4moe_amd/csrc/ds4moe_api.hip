@@ -667,8 +667,10 @@ ds4moe_status do_ffn(const ds4moe_shape& s, const ds4moe_experts& ex, const ds4m
         launch_k(k_x_to_f16, dim3(T), dim3(256), 0, st, g.x, g.H, g.K, (const int32_t*)inv,
                  at<uint16_t>(ws, L.x16), at<int8_t>(ws, L.xexp));
       if (iq2 && !b1) {  // small items (at most one per expert) and the rest
-        launch_k(k_grouped_gateup_iq2_small, dim3(g.I / kGNF, max_small_items(E, TK, T)), dim3(kGW * 64), 0, st, g);
-        if (large) launch_k(k_grouped_gateup_iq2<4>, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
+        if (large)  // 64-row items first, then the small ones, in one launch
+          launch_k(k_grouped_gateup_iq2_all, dim3(g.I / kGNF, mi), dim3(kGW * 64), 0, st, g);
+        else
+          launch_k(k_grouped_gateup_iq2_small, dim3(g.I / kGNF, max_small_items(E, TK, T)), dim3(kGW * 64), 0, st, g);
       }
       if (q4k && !b1)
         launch_k(k_grouped_gateup_q4k, dim3((g.I + kNT - 1) / kNT, mi), dim3(256), 0, st, g);

@@ -622,18 +622,23 @@ __device__ inline void build_tables8_f16(uint2 gb, uint4* gt8, uint4* mt8) {
   }
 }
 
-// MT = 1: the small items (at most 16 rows, listed first); MT = 4: the rest.
+// LDS of the IQ2_XXS gate/up bodies, 80 KB (two blocks per CU): the grid and
+// sign tables (32 + 16 KB) and 32 KB of x tiles.
+constexpr int kGuLds = (256 * 8 + 128 * 8) + 2048;  // uint4 units
+
+// The body for items of up to 16 MT rows (MT = 4: the 64-row items after the
+// small ones); item: its index in the work list, lds: kGuLds uint4.
 template <int MT>
-__global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
+__device__ __attribute__((always_inline)) inline void gateup_iq2_body(const GroupArgs& a, int item,
+                                                                     uint4* lds) {
   constexpr int kRows = 16 * MT;                           // x tile rows
   constexpr int kXC = kRows * 16;                          // 16-byte chunks of an x stage
   constexpr int kXJ = (kXC + kGW * 64 - 1) / (kGW * 64);  // chunks per thread
-  __shared__ uint4 xt[2][kXC];    // 2 x (MT x 4 KB)
-  __shared__ uint4 gt8[256 * 8];  // 32 KB
-  __shared__ uint4 mt8[128 * 8];  // 16 KB (MT = 4: 80 KB in all, two blocks per CU)
-  const int n_small = a.n_items[1];
-  const int item = (MT == 1 ? 0 : n_small) + (int)blockIdx.y;
-  if (item >= (MT == 1 ? n_small : a.n_items[0])) return;
+  static_assert(2 * kXC <= 2048, "x tiles fit the LDS area");
+  uint4* gt8 = lds;                                   // 32 KB
+  uint4* mt8 = lds + 256 * 8;                         // 16 KB
+  uint4 (*xt)[kXC] = (uint4 (*)[kXC])(lds + 256 * 8 + 128 * 8);  // 2 x (MT x 4 KB)
+  if (item >= a.n_items[0]) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   if (e >= a.E) return;  // shared-expert items run in k_grouped_gateup
   const int n0 = blockIdx.x * kGNF;
@@ -784,12 +789,12 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2(GroupArgs a) {
 // (read) and receives round r + 1's: stage s requests x of stage s + 5 and
 // stores x of stage s + 4 (requested one stage earlier) into the slot of
 // stage s - 4, which every wave finished before the last barrier.
-__global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2_small(GroupArgs a) {
+__device__ __attribute__((always_inline)) inline void gateup_iq2_small_body(const GroupArgs& a,
+                                                                           int item, uint4* lds) {
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  __shared__ uint4 gt8[256 * 8];       // 32 KB
-  __shared__ uint4 mt8[128 * 8];       // 16 KB
-  __shared__ u32x4_t xr[8][16 * 16];   // 32 KB: 80 KB in all, two blocks per CU
-  const int item = (int)blockIdx.y;
+  uint4* gt8 = lds;                                                   // 32 KB
+  uint4* mt8 = lds + 256 * 8;                                         // 16 KB
+  u32x4_t (*xr)[16 * 16] = (u32x4_t (*)[16 * 16])(lds + 256 * 8 + 128 * 8);  // 32 KB
   if (item >= a.n_items[1]) return;
   const int e = a.items[3 * item], row0 = a.items[3 * item + 1], nrows = a.items[3 * item + 2];
   if (e >= a.E) return;
@@ -883,6 +888,24 @@ __global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2_small(GroupArgs
   }
   f32x4_t ag[1] = {accg * (dgp * 0.125f)}, au[1] = {accu * (dup * 0.125f)};
   swiglu_store<1>(a, row0, nrows, 1, n, q, ag, au, n0, kGNF, xe, (uint32_t*)xr[0]);
+}
+
+__global__ __launch_bounds__(kGW * 64) void k_grouped_gateup_iq2_small(GroupArgs a) {
+  __shared__ uint4 lds[kGuLds];
+  gateup_iq2_small_body(a, (int)blockIdx.y, lds);
+}
+
+// Every routed IQ2_XXS gate/up item in one launch: grid rows first take the
+// items after the small ones (64-row pieces, the longest blocks, started
+// first), then the small items, so that the two kinds share the chip instead
+// of the 64-row items running alone after the small ones.  Four waves per
+// SIMD (two blocks per CU, as each body alone) bound the registers.
+__global__ __launch_bounds__(kGW * 64, 4) void k_grouped_gateup_iq2_all(GroupArgs a) {
+  __shared__ uint4 lds[kGuLds];
+  const int n_small = a.n_items[1], n_rest = a.n_items[0] - n_small;
+  const int y = (int)blockIdx.y;
+  if (y < n_rest) gateup_iq2_body<4>(a, n_small + y, lds);
+  else gateup_iq2_small_body(a, y - n_rest, lds);
 }
 
 // x (bf16) -> binary16 for the grouped IQ2_XXS and Q4_K gate/up kernels,
