@@ -1985,7 +1985,7 @@ __global__ __launch_bounds__(256) void k_imatrix(ImxArgs a) {
 // (the block header and the code bytes of its two chunk pairs) are requested
 // before its x tile (binary16, staged in LDS with the swizzle of
 // k_grouped_gateup) is written, so the two loads overlap.
-__global__ __launch_bounds__(256) void k_grouped_gateup_q4k(GroupArgs a) {
+__global__ __launch_bounds__(256, 3) void k_grouped_gateup_q4k(GroupArgs a) {
   __shared__ uint4 xt[2][kMC * 16];  // x of stages s (read) and s + 1 (written)
   __shared__ int tok[kMC];
   const int item = grid_item(a);
